@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for the gated delta-rule recurrence.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path. It shares no code with
+the HIP kernels.
+
+* ``recurrence`` -- the token-by-token recurrence in plain C (``kda_oracle.c``),
+  fp64, OpenMP over independent (sequence, head) pairs.
+* ``dense`` -- a second, independent formulation for tiny inputs: explicit
+  dense transition matrices and their products.
+"""
+from .recurrence import build, fwd, decode_step, fwd_heads, threads  # noqa: F401

@@ -1,0 +1,121 @@
+"""ctypes wrapper over the plain-C fp64 recurrence in ``kda_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).
+
+Inputs are the exact values handed to the GPU: bf16 or fp32 tensors are
+up-converted to fp64 here, so input quantisation is not charged to the kernel.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP); returns the library path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.kda_oracle_fwd.restype = ctypes.c_int
+        lib.kda_oracle_fwd.argtypes = [_dp] * 7 + [_dp] + [ctypes.c_int] * 5 + [_ip] + [ctypes.c_int] * 2
+        lib.kda_oracle_decode.restype = ctypes.c_int
+        lib.kda_oracle_decode.argtypes = [_dp] * 7 + [ctypes.c_int] * 5
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """Threads OpenMP will use (OMP_NUM_THREADS, else the process's CPU set)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env:
+        try:
+            return int(env)
+        except ValueError:
+            pass
+    return len(os.sched_getaffinity(0))
+
+
+def _f64(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().to(torch.float64).numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def fwd(q, k, v, gate, beta, S0=None, cu_seqlens=None, gate_kind: int = 0):
+    """Run the recurrence over whole sequences. Returns (o, S_T) as fp64 numpy.
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; gate: [B,T,H,dk] or [B,T,H]; beta [B,T,H];
+    S0: [nseq,H,dk,dv] or None; cu_seqlens: [nseq+1] int offsets (B must be 1).
+    """
+    lib = _load()
+    q, k, v, gate, beta = (_f64(t) for t in (q, k, v, gate, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    cu = None
+    nseq = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if isinstance(cu_seqlens, torch.Tensor)
+                                             else cu_seqlens), dtype=np.int32)
+        nseq = cu.size - 1
+    s0 = None if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((nseq, H, dk, dv))
+    rc = lib.kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                            None if s0 is None else _ptr(s0), _ptr(o), _ptr(ST),
+                            B, H, T, dk, dv, None if cu is None else cu.ctypes.data_as(_ip), nseq,
+                            int(gate_kind))
+    if rc != 0:
+        raise ValueError("kda_oracle_fwd rejected its arguments")
+    return o, ST
+
+
+def fwd_heads(q, k, v, gate, beta, heads, S0=None, cu_seqlens=None, gate_kind: int = 0):
+    """The recurrence restricted to a subset of heads (every head is
+    independent). Returns (o[..., heads, :], S_T[:, heads]) as fp64 numpy."""
+    idx = torch.as_tensor(list(heads), dtype=torch.long)
+    sel = lambda t: None if t is None else t.index_select(2, idx)  # noqa: E731
+    s0 = None if S0 is None else S0.index_select(1, idx)
+    return fwd(sel(q), sel(k), sel(v), sel(gate), beta.index_select(2, idx), s0, cu_seqlens, gate_kind)
+
+
+def decode_step(q, k, v, gate, beta, S: np.ndarray, gate_kind: int = 0) -> np.ndarray:
+    """One decode step; ``S`` (fp64 numpy [N,H,dk,dv]) is updated in place.
+    Returns o [N,H,dv] fp64."""
+    lib = _load()
+    q, k, v, gate, beta = (_f64(t) for t in (q, k, v, gate, beta))
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((N, H, dv))
+    rc = lib.kda_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S), _ptr(o),
+                               N, H, dk, dv, int(gate_kind))
+    if rc != 0:
+        raise ValueError("kda_oracle_decode rejected its arguments")
+    return o
