@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise gated delta-rule forward and the decode step
+on one MI355X, with roofline fractions and the fp64 CPU oracle as baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+A step is one kda_chunk_fwd call over the Complex KDA workload (B=2, H=16,
+T=8192, dk=dv=128, bf16 inputs, fp32 state, chunk 64): 16,384 tokens. Two
+seeded input sets alternate so the 256 MB last-level cache cannot hold the
+whole working set. The decode step (N=256 sequences, H=32, d=128, fp32 state
+of 512 MiB updated in place) is timed as one block of 128 consecutive steps.
+Timing uses HIP events recorded on the stream the kernels run on. Prints one
+JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s KDA chunk fwd (H=16,d=128,T=8192) + decode GB/s, % roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def fwd_bytes_per_head_token(dk: int, dv: int, scalar_gate: bool, in_bytes: int = 2) -> int:
+    """Compulsory HBM bytes per (token, head): q, k, v, gate, beta read once
+    in the input dtype, o written once in fp32."""
+    gate = 1 if scalar_gate else dk
+    return in_bytes * (2 * dk + dv + gate + 1) + 4 * dv
+
+
+def fwd_flops_per_head_token(dk: int, dv: int, C: int = 64) -> int:
+    """Algorithmic flops of the chunkwise form per (token, head) at chunk 64:
+    full CxC tiles for the gated Gram matrices A and P and for T(Gamma K),
+    T V and P U, plus the three state contractions."""
+    return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+
+
+def decode_bytes_per_head_step(dk: int, dv: int, in_bytes: int = 2) -> int:
+    return 8 * dk * dv + in_bytes * (3 * dk + dv + 1) + 4 * dv
+
+
+def time_region(fn, iters: int, stream):
+    import torch
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters   # ms per call
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the gated delta-rule path here is single-GPU "
+              "(independent (sequence, head) scans shard without communication; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from gated_delta_rule_46_amd import inputs, kda
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    kda.library()
+
+    # ---------------------------------------------------------------- forward
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    sets = []
+    for seed in (0, 1):
+        w = inputs.ckda_fwd(seed=seed)
+        sets.append(tuple(t.to(dev) for t in (w.q, w.k, w.v, w.gate, w.beta)))
+    B, H, T, dk, dv, C = w.B, w.H, w.T, w.dk, w.dv, w.chunk
+    tokens = B * T
+    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+    ST = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+    wsb = kda.workspace_bytes(B, H, T, dk, dv, C)
+    ws = torch.empty(wsb, device=dev, dtype=torch.uint8)
+
+    def fwd(i, stage=kda.STAGE_ALL):
+        q, k, v, g, b = sets[i % 2]
+        kda.chunk_fwd(q, k, v, g, b, chunk=C, gate_kind=0, out=o, S_T=ST, workspace=ws, stage=stage)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    ms = time_region(fwd, args.steps, stream)
+    print("[bench] forward %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    ms_prep = time_region(lambda i: fwd(i, kda.STAGE_PREP), args.steps, stream)
+    fwd(0, kda.STAGE_PREP)
+    ms_state = time_region(lambda i: fwd(0, kda.STAGE_STATE), args.steps, stream)
+    print("[bench] prep %.3f ms, state %.3f ms" % (ms_prep, ms_state), file=sys.stderr, flush=True)
+
+    head_tokens = tokens * H
+    alg_bytes = head_tokens * fwd_bytes_per_head_token(dk, dv, False) + B * H * dk * dv * 4
+    alg_flops = head_tokens * fwd_flops_per_head_token(dk, dv)
+    tok_s = tokens / (ms * 1e-3)
+    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved_gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "kernel": "kda_chunk_fwd: chunk_prep_kernel + chunk_state_kernel (one call)",
+        "bytes_per_launch": alg_bytes,
+        "launch_ms": round(ms, 4),
+        "mfma_frac_algorithmic": round(alg_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernels_ms": {"chunk_prep_kernel": round(ms_prep, 4), "chunk_state_kernel": round(ms_state, 4)},
+    }
+    del sets, ws, o
+
+    # ---------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        print("[bench] decode inputs", file=sys.stderr, flush=True)
+        dw = inputs.ckda_decode(n_steps=16)
+        S = dw.S.to(dev)
+        steps = [tuple(st[x].to(dev) for x in ("q", "k", "v", "gate", "beta")) for st in dw.steps]
+        od = torch.empty((dw.N, dw.H, dw.dv), device=dev, dtype=torch.float32)
+
+        def dec(i):
+            q, k, v, g, b = steps[i % len(steps)]
+            kda.decode_step(q, k, v, g, b, S, out=od, gate_kind=0)
+
+        for i in range(4):
+            dec(i)
+        n_dec = args.decode_steps
+        ms_block = time_region(lambda i: [dec(j) for j in range(n_dec)], 1, stream)
+        per = ms_block / n_dec
+        dbytes = dw.N * dw.H * decode_bytes_per_head_step(dw.dk, dw.dv)
+        gbs = dbytes / (per * 1e-3) / 1e9
+        decode = {
+            "workload": "ckda_decode_n256_h32_d128",
+            "steps_in_block": n_dec,
+            "ms_per_step": round(per, 4),
+            "tokens_per_s": round(dw.N / (per * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "decode_step_kernel", "bytes_per_launch": dbytes},
+        }
+        print("[bench] decode %.4f ms/step, %.1f GB/s" % (per, gbs), file=sys.stderr, flush=True)
+        del S, steps
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        w0 = inputs.ckda_fwd(seed=0)
+        t0 = time.time()
+        reps = 0
+        while True:
+            oracle.fwd(w0.q, w0.k, w0.v, w0.gate, w0.beta, None, None, 0)
+            reps += 1
+            if time.time() - t0 > 8.0:
+                break
+        dt = (time.time() - t0) / reps
+        cpu = {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": min(oracle.threads(), B * H),
+               "kind": "oracle",
+               "sample": "whole Complex KDA workload (B=2, H=16, T=8192, d=128), fp64 token recurrence, "
+                         "%d pass(es), %.2f s each" % (reps, dt)}
+        print("[bench] oracle %.2f s per pass" % dt, file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ckda_fwd_b2_h16_t8192_d128_chunk64", "B": B, "H": H, "T": T, "dk": dk, "dv": dv,
+                   "chunk": C, "tokens_per_step": tokens, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode": decode,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,121 @@
+// C ABI: argument validation (before any HIP call) and dispatch.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+bool size_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+bool aligned(const void* p, uintptr_t a = 16) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return KDA_OK;
+    g_last_hip = (int)e;
+    return KDA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char* kda_strerror(int status) {
+    switch (status) {
+        case KDA_OK: return "success";
+        case KDA_EINVAL: return "invalid argument";
+        case KDA_ENOTSUP: return "unsupported size, chunk, dtype or gate kind";
+        case KDA_EALIGN: return "pointer misaligned for its element type, or a 16-byte-aligned buffer is not";
+        case KDA_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int kda_last_hip_error(void) { return g_last_hip; }
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int N, int has_cu,
+                                     int dtype) {
+    if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (has_cu && (B != 1 || N <= 0)) return 0;
+    return kda::chunk_workspace_bytes(B, H, T, dk, chunk, has_cu != 0, has_cu ? N : B, dtype == KDA_BF16);
+}
+
+int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const void* gate,
+                        const void* beta, const float* S0, float* o, float* S_T, int B, int H, int T, int dk,
+                        int dv, int chunk, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (stage != KDA_STAGE_ALL && stage != KDA_STAGE_PREP && stage != KDA_STAGE_STATE) return KDA_EINVAL;
+    if (stage != KDA_STAGE_ALL && !workspace) return KDA_EINVAL;
+    if (B <= 0 || H <= 0 || T < 0) return KDA_EINVAL;
+    if (!size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return KDA_ENOTSUP;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ENOTSUP;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return KDA_ENOTSUP;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen) {
+        if (B != 1 || N <= 0) return KDA_EINVAL;
+    } else {
+        if (N != 0 && N != B) return KDA_EINVAL;
+        N = B;
+    }
+    const bool need_data = T > 0;
+    if (need_data && (!q || !k || !v || !gate || !beta || !o)) return KDA_EINVAL;
+    const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (need_data && (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(gate, es) ||
+                      !aligned(beta, es) || !aligned(o, 4)))
+        return KDA_EALIGN;
+    if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) || (workspace && !aligned(workspace))) return KDA_EALIGN;
+    if (varlen && !aligned(cu_seqlens, 4)) return KDA_EALIGN;
+    const size_t need = kda::chunk_workspace_bytes(B, H, T, dk, chunk, varlen, N, dtype == KDA_BF16);
+    if (workspace && workspace_bytes < need) return KDA_EINVAL;
+    if (!need_data && !S_T) return KDA_OK;
+    if (stage == KDA_STAGE_PREP && !need_data) return KDA_OK;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    bool owned = false;
+    if (!ws && need > 0) {
+        hipError_t e = hipMallocAsync(&ws, need, st);
+        if (e != hipSuccess) return hip_status(e);
+        owned = true;
+    }
+    kda::ChunkArgs a{q, k, v, gate, beta, S0, o, S_T, B, H, T, dk, dv, chunk, cu_seqlens, N,
+                     dtype == KDA_BF16, gate_kind == KDA_GATE_SCALAR, ws, st, stage};
+    hipError_t e = kda::launch_chunk_fwd(a);
+    if (owned) {
+        hipError_t f = hipFreeAsync(ws, st);
+        if (e == hipSuccess) e = f;
+    }
+    return hip_status(e);
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                  const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
+                  const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    return kda_chunk_fwd_stage(KDA_STAGE_ALL, q, k, v, gate, beta, S0, o, S_T, B, H, T, dk, dv, chunk, cu_seqlens,
+                               N, dtype, gate_kind, workspace, workspace_bytes, stream);
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                    float* S, float* o, int N, int H, int dk, int dv, int dtype, int gate_kind, void* stream) {
+    if (N <= 0 || H <= 0) return KDA_EINVAL;
+    if (!size_ok(dk) || !size_ok(dv)) return KDA_ENOTSUP;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ENOTSUP;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return KDA_ENOTSUP;
+    if (!q || !k || !v || !gate || !beta || !S || !o) return KDA_EINVAL;
+    const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(gate, es) || !aligned(beta, es) ||
+        !aligned(S) || !aligned(o))
+        return KDA_EALIGN;
+    kda::DecodeArgs a{q, k, v, gate, beta, S, o, N, H, dk, dv, dtype == KDA_BF16,
+                      gate_kind == KDA_GATE_SCALAR, reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(kda::launch_decode(a));
+}
+
+}  // extern "C"

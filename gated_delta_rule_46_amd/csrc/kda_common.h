@@ -1,0 +1,115 @@
+// Device-side building blocks shared by the gated delta-rule kernels (gfx950).
+//
+// MFMA fragment convention used throughout (16x16 output tiles, 32-deep K
+// steps, 64-lane wavefronts):
+//   lane l = 16*g + i   (g = l / 16 in 0..3, i = l % 16)
+//   A operand (16 rows x 32 K): lane holds row i, 8 values at K positions
+//       kpos(g, p), p = 0..7
+//   B operand (32 K x 16 cols): lane holds column i, the same 8 K positions
+//   C/D (16 x 16 fp32):          lane holds column i, rows 4g .. 4g+3
+// with kpos(g, p) = 4g + p for p < 4 and 16 + 4g + (p - 4) for p >= 4.
+// The K order inside a step does not change a product as long as A and B
+// agree, and this particular order makes two vertically stacked D tiles a
+// ready B operand: a state or update matrix held in accumulator registers
+// feeds the next contraction without an LDS round trip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+namespace kda {
+
+constexpr int WAVE = 64;
+constexpr int NXCD = 8;   // accelerator complex dies; consecutive workgroups round-robin over them
+
+__host__ __device__ constexpr int kpos(int g, int p) { return p < 4 ? 4 * g + p : 12 + 4 * g + p; }
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <class TIn> __device__ __forceinline__ float ld_in(const TIn* p);
+template <> __device__ __forceinline__ float ld_in<uint16_t>(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+template <> __device__ __forceinline__ float ld_in<float>(const float* p) { return *p; }
+
+// 2^-e such that |m| * scale lies in [0.5, 1); 1 for m == 0 or non-finite m.
+__device__ __forceinline__ float pow2_scale_for(float m) {
+    if (!(m > 0.f) || !(m < 3.0e38f)) return 1.f;
+    int e;
+    frexpf(m, &e);              // m = f * 2^e, f in [0.5, 1)
+    return ldexpf(1.f, -e);
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 operands: eight 16x16x4 steps; step m takes position m of every lane
+// group, which covers the 32 K positions once each.
+__device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[m], c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Split an fp32 value into bf16 hi + lo (hi + lo carries 16 mantissa bits).
+struct bf16pair { bf16x8 hi, lo; };
+__device__ __forceinline__ bf16pair split8(const f32x8& x) {
+    bf16pair r;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        __bf16 h = (__bf16)x[p];
+        r.hi[p] = h;
+        r.lo[p] = (__bf16)(x[p] - (float)h);
+    }
+    return r;
+}
+
+__device__ __forceinline__ f16x8 to_f16x8(const f32x8& x, float s) {
+    f16x8 r;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) r[p] = (_Float16)(x[p] * s);
+    return r;
+}
+
+// Two stacked D tiles (rows 0-15 and 16-31 of a 32-deep K step) as the 8
+// values of a B fragment, per the kpos order.
+__device__ __forceinline__ f32x8 dtiles_to_frag(const f32x4& top, const f32x4& bot) {
+    return f32x8{top[0], top[1], top[2], top[3], bot[0], bot[1], bot[2], bot[3]};
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
+    return v;
+}
+
+// ---------------------------------------------------------------- XCD-aware work order
+// Workgroup ids are dispatched round-robin over the XCDs. Renumber them so
+// that consecutive work items (e.g. the value-column slices of one head) land
+// on one XCD and share its L2. A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+    const int per = total / NXCD, rem = total % NXCD;
+    const int x = L % NXCD, j = L / NXCD;
+    return x * per + (x < rem ? x : rem) + j;
+}
+
+}  // namespace kda

@@ -1,0 +1,148 @@
+// Recurrent decode step of the gated delta rule, one token per sequence.
+//
+// For each (sequence n, head h) with fp32 state S in R^{dk x dv}:
+//   S'   = Diag(alpha) S                       (gate first; Complex KDA summary,
+//                                                background, diagonal-plus-rank-one)
+//   pred = S'^T k,  y = S'^T q                 (both reductions from one read of S)
+//   u    = beta (v - pred)
+//   S    = S' + k u^T                          (delta form, CyFA blog post 2.2)
+//   o    = S^T q = y + (k . q) u               (readout after the update)
+// The state is streamed once in and once out with 128-bit accesses; the step
+// is bound by HBM bandwidth (about 0.87 flop per byte at dk = dv = 128).
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <class TIn, int DK, int DV, bool SCALAR_GATE>
+__global__ void __launch_bounds__(256)
+decode_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+                   const TIn* __restrict__ gate, const TIn* __restrict__ beta,
+                   float* __restrict__ S, float* __restrict__ o, int NH) {
+    constexpr int CG = DV / 4;                                   // float4 columns per row
+    constexpr int NT = (DK * DV / 4) < 256 ? (DK * DV / 4) : 256;
+    constexpr int RG = NT / CG;                                  // row groups
+    constexpr int RPT = DK / RG;                                 // rows per thread
+    constexpr int NW = NT / WAVE;
+    static_assert(NT % WAVE == 0 && DK % RG == 0, "decode tiling");
+
+    __shared__ float s_a[DK], s_k[DK], s_q[DK], s_v[DV];
+    __shared__ float s_red[NW][2][DV];
+    __shared__ float s_kq[NW];
+
+    const int pair = blockIdx.x;            // n * H + h
+    if (pair >= NH) return;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    const int lane = t % WAVE, w = t / WAVE;
+
+    const size_t kb = (size_t)pair * DK, vb = (size_t)pair * DV;
+    float kq_part = 0.f;
+    if (t < DK) {
+        const float kv = ld_in(k + kb + t), qv = ld_in(q + kb + t);
+        s_k[t] = kv;
+        s_q[t] = qv;
+        s_a[t] = SCALAR_GATE ? ld_in(gate + pair) : ld_in(gate + kb + t);
+        kq_part = kv * qv;
+    }
+    if (t < DV) s_v[t] = ld_in(v + vb + t);
+    kq_part = wave_sum(kq_part);
+    if (lane == 0) s_kq[w] = kq_part;
+
+    f32x4* Sp = reinterpret_cast<f32x4*>(S + (size_t)pair * DK * DV);
+    f32x4 sv[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) sv[m] = __builtin_nontemporal_load(Sp + (size_t)(rg + RG * m) * CG + cg);
+    __syncthreads();
+
+    f32x4 pr = zero4(), yy = zero4();
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int r = rg + RG * m;
+        const float a = s_a[r], kr = s_k[r], qr = s_q[r];
+        sv[m] *= a;
+        pr += sv[m] * kr;
+        yy += sv[m] * qr;
+    }
+    // reduce over the row groups inside the wave (lanes that share cg)
+#pragma unroll
+    for (int off = CG; off < WAVE; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pr[j] += __shfl_xor(pr[j], off, WAVE);
+            yy[j] += __shfl_xor(yy[j], off, WAVE);
+        }
+    }
+    if (lane < CG) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s_red[w][0][4 * cg + j] = pr[j];
+            s_red[w][1][4 * cg + j] = yy[j];
+        }
+    }
+    __syncthreads();
+    float kqs = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) kqs += s_kq[ww];
+    const float bt = ld_in(beta + pair);
+    float u[4], yv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float p = 0.f, y = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) { p += s_red[ww][0][4 * cg + j]; y += s_red[ww][1][4 * cg + j]; }
+        u[j] = bt * (s_v[4 * cg + j] - p);
+        yv[j] = y;
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const float kr = s_k[rg + RG * m];
+        f32x4 nv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nv[j] = sv[m][j] + kr * u[j];
+        __builtin_nontemporal_store(nv, Sp + (size_t)(rg + RG * m) * CG + cg);
+    }
+    if (rg == 0) {
+        f32x4 ov;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[j] = yv[j] + kqs * u[j];
+        reinterpret_cast<f32x4*>(o + vb)[cg] = ov;
+    }
+}
+
+template <class TIn, int DK, int DV, bool SG>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+    constexpr int NT = (DK * DV / 4) < 256 ? (DK * DV / 4) : 256;
+    const int NH = a.N * a.H;
+    hipLaunchKernelGGL((decode_step_kernel<TIn, DK, DV, SG>), dim3(NH), dim3(NT), 0, a.stream,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.gate,
+                       (const TIn*)a.beta, a.S, a.o, NH);
+    return hipGetLastError();
+}
+
+template <class TIn, int DK, bool SG>
+static hipError_t launch_decode_dv(const DecodeArgs& a) {
+    switch (a.dv) {
+        case 16: return launch_decode_t<TIn, DK, 16, SG>(a);
+        case 32: return launch_decode_t<TIn, DK, 32, SG>(a);
+        case 64: return launch_decode_t<TIn, DK, 64, SG>(a);
+        default: return launch_decode_t<TIn, DK, 128, SG>(a);
+    }
+}
+
+template <class TIn, bool SG>
+static hipError_t launch_decode_dk(const DecodeArgs& a) {
+    switch (a.dk) {
+        case 16: return launch_decode_dv<TIn, 16, SG>(a);
+        case 32: return launch_decode_dv<TIn, 32, SG>(a);
+        case 64: return launch_decode_dv<TIn, 64, SG>(a);
+        default: return launch_decode_dv<TIn, 128, SG>(a);
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+    if (a.bf16) return a.scalar_gate ? launch_decode_dk<uint16_t, true>(a) : launch_decode_dk<uint16_t, false>(a);
+    return a.scalar_gate ? launch_decode_dk<float, true>(a) : launch_decode_dk<float, false>(a);
+}
+
+}  // namespace kda

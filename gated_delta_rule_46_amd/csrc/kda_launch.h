@@ -1,0 +1,43 @@
+// Host-side launch descriptors shared by the C-ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void *q, *k, *v, *gate, *beta;
+    float* S;
+    float* o;
+    int N, H, dk, dv;
+    bool bf16, scalar_gate;
+    hipStream_t stream;
+};
+
+struct ChunkArgs {
+    const void *q, *k, *v, *gate, *beta;
+    const float* S0;
+    float* o;
+    float* S_T;
+    int B, H, T, dk, dv, chunk;
+    const int32_t* cu_seqlens;  // device, N+1 entries, or null
+    int N;                      // number of sequences (B when cu_seqlens is null)
+    bool bf16, scalar_gate;
+    void* workspace;
+    hipStream_t stream;
+    int stages;                 // bit 0: index + prep kernels, bit 1: state kernel
+};
+
+// Bytes of intermediates one (chunk, head) pair occupies in the workspace.
+size_t chunk_block_bytes(int dk, int chunk, bool bf16);
+// Upper bound on the number of chunks over all sequences.
+long chunk_count_bound(int B, int T, int chunk, bool varlen, int N);
+// Total workspace bytes for one forward call.
+size_t chunk_workspace_bytes(int B, int H, int T, int dk, int chunk, bool varlen, int N, bool bf16);
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_chunk_fwd(const ChunkArgs& a);
+
+}  // namespace kda

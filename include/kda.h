@@ -1,0 +1,154 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) gated delta-rule library, libkda.so.
+ *
+ * The operator is the diagonal-plus-rank-one recurrence of Kimi Delta
+ * Attention and its extensions, as described in "Complex KDA: Understanding
+ * and Enhancing the Expressivity of Kimi Delta Attention" (summary page,
+ * background "diagonal-plus-rank-one transitions" and core method):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t
+ *
+ * per (sequence, head), with state S in R^{dk x dv} read on the key side
+ * (Dual DeltaNet abstract). KDA uses a per-channel gate alpha_t in R^{dk};
+ * GDN is the scalar-gate case (one alpha per token and head); Complex KDA
+ * allows alpha in [-1, 1] (negative and exactly zero gates) and beta in
+ * [0, 2]. The gate is applied first, then the rank-one delta term; there is
+ * no query scaling and no key normalisation inside the library.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent),
+ *    row-major and contiguous, aligned to their element size. The decode
+ *    state S and output o, and any workspace, must be 16-byte aligned.
+ *    The caller owns every buffer.
+ *  - Element type of q, k, v, gate and beta is selected by `dtype`:
+ *    KDA_BF16 (bfloat16 bits) or KDA_F32. States S0, S_T, S and outputs o
+ *    are always fp32.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    and the call returns without synchronising.
+ *  - Arguments are validated before any HIP call; nothing is enqueued when
+ *    validation fails. Device-side contents (cu_seqlens offsets, NaN/Inf in
+ *    inputs) are not checked: NaN/Inf propagate.
+ *  - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}.
+ *  - Calls are re-entrant; the library keeps no mutable global state. Two
+ *    calls may run concurrently on different streams if they do not share
+ *    output or workspace buffers.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KDA_OK 0
+#define KDA_EINVAL (-1)  /* null required pointer, non-positive size, inconsistent counts, short workspace */
+#define KDA_ENOTSUP (-2) /* dk, dv, chunk, dtype or gate_kind outside the supported set */
+#define KDA_EALIGN (-3)  /* a pointer violates the alignment rules above */
+#define KDA_EHIP (-4)    /* a HIP call failed; see kda_last_hip_error() */
+
+/* dtype */
+#define KDA_F32 0
+#define KDA_BF16 1
+
+/* gate_kind */
+#define KDA_GATE_CHANNEL 0 /* gate [.., dk]: one alpha per key channel (KDA, Complex KDA) */
+#define KDA_GATE_SCALAR 1  /* gate [..]: one alpha per token and head (GDN) */
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 when the
+ * arguments are invalid). For packed variable-length input pass the number
+ * of sequences N and has_cu_seqlens = 1; the bound then assumes the worst
+ * split of T over N sequences.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int N,
+                                     int has_cu_seqlens, int dtype);
+
+/*
+ * Chunkwise-parallel forward over whole sequences (the pages' chunkwise WY
+ * training form of this family; Complex KDA summary, background and core
+ * method; Gated DeltaNet-2 blurb). Produces exactly the token recurrence above
+ * up to floating-point rounding.
+ *
+ * Layouts (fixed-length batch; cu_seqlens == NULL):
+ *   q, k   [B, T, H, dk]      v    [B, T, H, dv]
+ *   gate   [B, T, H, dk] (KDA_GATE_CHANNEL) or [B, T, H] (KDA_GATE_SCALAR)
+ *   beta   [B, T, H]
+ *   o      [B, T, H, dv] fp32 (output; must not alias any input)
+ *   S0     [B, H, dk, dv] fp32 initial state, or NULL for zeros
+ *   S_T    [B, H, dk, dv] fp32 final state, or NULL; may alias S0
+ * Packed variable-length input (cu_seqlens != NULL): B must be 1; cu_seqlens
+ * is a DEVICE int32 array of N+1 non-decreasing offsets with cu_seqlens[0] = 0
+ * and cu_seqlens[N] = T; sequence s covers tokens [cu_seqlens[s],
+ * cu_seqlens[s+1]) and starts from S0[s] (or zeros); S0 and S_T are
+ * [N, H, dk, dv]. With cu_seqlens == NULL, N must equal B (or be 0).
+ *
+ * chunk (16, 32 or 64) sets the block size of the parallel form; results
+ * agree across chunk sizes up to rounding. T need not be a multiple of it.
+ *
+ * workspace: device memory of at least kda_chunk_fwd_workspace_bytes(...)
+ * bytes, owned by the caller and not read before it is written. If workspace
+ * is NULL the library takes it stream-ordered from the device's default memory
+ * pool (hipMallocAsync) and returns it the same way (hipFreeAsync).
+ *
+ * Returns KDA_OK or a negative status.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                  const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
+                  const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* stage for kda_chunk_fwd_stage */
+#define KDA_STAGE_PREP 1  /* in-chunk work: gate products, gated Gram, UT inverse -> workspace */
+#define KDA_STAGE_STATE 2 /* sequential state pass over the chunks: reads the workspace, writes o, S_T */
+#define KDA_STAGE_ALL 3   /* both, in order (what kda_chunk_fwd does) */
+
+/*
+ * kda_chunk_fwd split into its two launches, for callers that schedule or
+ * time them separately. Arguments as for kda_chunk_fwd. KDA_STAGE_STATE
+ * consumes a workspace that a KDA_STAGE_PREP call with identical arguments
+ * filled earlier on the same stream (or with ordering the caller provides);
+ * both partial stages require a caller-provided workspace (KDA_EINVAL when it
+ * is NULL). KDA_STAGE_PREP writes neither o nor S_T.
+ */
+int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const void* gate,
+                        const void* beta, const float* S0, float* o, float* S_T, int B, int H, int T, int dk,
+                        int dv, int chunk, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step for N sequences, state updated in place (the
+ * pages' recurrent inference form with constant memory per sequence; Gated
+ * DeltaNet-2 blurb; Complex KDA summary, background):
+ *   S' = Diag(alpha) S;  u = beta (v - S'^T k);  S <- S' + k u^T;  o = S^T q.
+ *
+ * Layouts: q, k [N, H, dk]; v [N, H, dv]; gate [N, H, dk] or [N, H];
+ * beta [N, H]; S [N, H, dk, dv] fp32 (read and written in place);
+ * o [N, H, dv] fp32 (must not alias S or the inputs).
+ * The state layout equals kda_chunk_fwd's S_T, so a forward's final state
+ * feeds decode directly.
+ *
+ * Returns KDA_OK or a negative status.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                    float* S, float* o, int N, int H, int dk, int dv, int dtype, int gate_kind,
+                    void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* kda_strerror(int status);
+
+/* hipError_t of the most recent KDA_EHIP on the calling thread (0 if none). */
+int kda_last_hip_error(void);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_46_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_46_amd import build
+        build.build()
+    return kda.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    assert lib.kda_version() == 100
+    for code in (0, -1, -2, -3, -4):
+        assert kda.strerror(code)
+    assert kda.strerror(-99) == "unknown status"
+    assert lib.kda_last_hip_error() == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, S0=None, o=FAKE, S_T=None, B=1, H=2, T=8,
+             dk=16, dv=16, chunk=16, cu=None, N=0, dtype=kda.KDA_BF16, gate_kind=0, ws=FAKE, wsb=0,
+             stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(*[a[x] for x in ("q", "k", "v", "gate", "beta", "S0", "o", "S_T", "B", "H",
+                                                 "T", "dk", "dv", "chunk", "cu", "N", "dtype",
+                                                 "gate_kind", "ws", "wsb", "stream")])
+
+
+def test_chunk_validation(lib):
+    assert chunk(lib, B=0) == kda.KDA_EINVAL
+    assert chunk(lib, H=-1) == kda.KDA_EINVAL
+    assert chunk(lib, dk=24) == kda.KDA_ENOTSUP
+    assert chunk(lib, dv=256) == kda.KDA_ENOTSUP
+    assert chunk(lib, chunk=128) == kda.KDA_ENOTSUP
+    assert chunk(lib, dtype=7) == kda.KDA_ENOTSUP
+    assert chunk(lib, gate_kind=2) == kda.KDA_ENOTSUP
+    assert chunk(lib, q=None) == kda.KDA_EINVAL
+    assert chunk(lib, o=None) == kda.KDA_EINVAL
+    assert chunk(lib, q=FAKE + 1) == kda.KDA_EALIGN                   # bf16 needs 2-byte alignment
+    assert chunk(lib, dtype=kda.KDA_F32, k=FAKE + 2) == kda.KDA_EALIGN
+    assert chunk(lib, ws=FAKE + 8) == kda.KDA_EALIGN
+    assert chunk(lib, wsb=1) == kda.KDA_EINVAL                        # workspace too small
+    assert chunk(lib, cu=FAKE, B=2, N=2) == kda.KDA_EINVAL            # varlen needs B == 1
+    assert chunk(lib, cu=FAKE, N=0) == kda.KDA_EINVAL
+    assert chunk(lib, N=3) == kda.KDA_EINVAL                          # N != B without offsets
+
+
+def test_decode_validation(lib):
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, S=FAKE, o=FAKE, N=2, H=2, dk=16, dv=16,
+                 dtype=kda.KDA_BF16, gate_kind=0, stream=None)
+        a.update(kw)
+        return lib.kda_decode_step(*a.values())
+    assert dec(N=0) == kda.KDA_EINVAL
+    assert dec(dk=48) == kda.KDA_ENOTSUP
+    assert dec(dtype=3) == kda.KDA_ENOTSUP
+    assert dec(gate_kind=-1) == kda.KDA_ENOTSUP
+    assert dec(S=None) == kda.KDA_EINVAL
+    assert dec(S=FAKE + 4) == kda.KDA_EALIGN                           # state needs 16 bytes
+    assert dec(o=FAKE + 8) == kda.KDA_EALIGN
+
+
+def test_workspace_bytes(lib):
+    f = kda.workspace_bytes
+    assert f(1, 2, 64, 24, 16, 16) == 0
+    a = f(1, 2, 64, 16, 16, 16)
+    assert a > 0 and a % 256 == 0
+    assert f(2, 2, 64, 16, 16, 16) == 2 * a
+    assert f(1, 2, 65, 16, 16, 16) > a                                # ragged tail adds a chunk
+    assert f(1, 16, 8192, 128, 128, 64) > f(1, 16, 8192, 128, 128, 64, dtype=None) * 0  # defined
+    v = f(1, 2, 100, 16, 16, 16, N=5, varlen=True)
+    assert v >= f(1, 2, 100, 16, 16, 16)
+    assert f(2, 2, 100, 16, 16, 16, N=5, varlen=True) == 0           # varlen needs B == 1
