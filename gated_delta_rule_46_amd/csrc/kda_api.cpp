@@ -43,7 +43,7 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
     if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     if (has_cu && (B != 1 || N <= 0)) return 0;
-    return kda::chunk_workspace_bytes(B, H, T, dk, chunk, has_cu != 0, has_cu ? N : B, dtype == KDA_BF16);
+    return kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, has_cu != 0, has_cu ? N : B, dtype == KDA_BF16);
 }
 
 int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const void* gate,
@@ -66,12 +66,12 @@ int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, 
     const bool need_data = T > 0;
     if (need_data && (!q || !k || !v || !gate || !beta || !o)) return KDA_EINVAL;
     const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
-    if (need_data && (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(gate, es) ||
-                      !aligned(beta, es) || !aligned(o, 4)))
+    if (need_data && (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(gate) || !aligned(beta, es) ||
+                      !aligned(o, 4)))
         return KDA_EALIGN;
     if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) || (workspace && !aligned(workspace))) return KDA_EALIGN;
     if (varlen && !aligned(cu_seqlens, 4)) return KDA_EALIGN;
-    const size_t need = kda::chunk_workspace_bytes(B, H, T, dk, chunk, varlen, N, dtype == KDA_BF16);
+    const size_t need = kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, N, dtype == KDA_BF16);
     if (workspace && workspace_bytes < need) return KDA_EINVAL;
     if (!need_data && !S_T) return KDA_OK;
     if (stage == KDA_STAGE_PREP && !need_data) return KDA_OK;

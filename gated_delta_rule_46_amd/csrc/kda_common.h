@@ -37,12 +37,27 @@ template <class TIn> __device__ __forceinline__ float ld_in(const TIn* p);
 template <> __device__ __forceinline__ float ld_in<uint16_t>(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 template <> __device__ __forceinline__ float ld_in<float>(const float* p) { return *p; }
 
-// 2^-e such that |m| * scale lies in [0.5, 1); 1 for m == 0 or non-finite m.
-__device__ __forceinline__ float pow2_scale_for(float m) {
-    if (!(m > 0.f) || !(m < 3.0e38f)) return 1.f;
-    int e;
-    frexpf(m, &e);              // m = f * 2^e, f in [0.5, 1)
-    return ldexpf(1.f, -e);
+// Power-of-two scale for a block of values whose largest magnitude is m >= 0:
+// m * scale lies in [0.5, 1). The exponent is clamped to [2^-62, 2^62] so that
+// products and inverses of two scales stay normal fp32 numbers; blocks with
+// m < 2^-63 are scaled up by 2^62 only, and m >= 2^78 is outside the range the
+// fp16 operand path represents. Read straight from the exponent bits.
+__device__ __forceinline__ int scale_exp(float m) {
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xffu);
+    return min(max(e, 64), 188);
+}
+__device__ __forceinline__ float pow2_scale_for(float m) { return __uint_as_float((uint32_t)(253 - scale_exp(m)) << 23); }
+__device__ __forceinline__ float pow2_inv_scale_for(float m) { return __uint_as_float((uint32_t)(scale_exp(m) + 1) << 23); }
+
+// Largest value over the four lanes that hold one column of a 16x16 D tile
+// (lanes i, i+16, i+32, i+48): two lane-swap steps, no LDS round trip.
+__device__ __forceinline__ float colmax4(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t u2 = __float_as_uint(m);
+    const auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // ---------------------------------------------------------------- MFMA
@@ -87,6 +102,14 @@ __device__ __forceinline__ f16x8 to_f16x8(const f32x8& x, float s) {
 // values of a B fragment, per the kpos order.
 __device__ __forceinline__ f32x8 dtiles_to_frag(const f32x4& top, const f32x4& bot) {
     return f32x8{top[0], top[1], top[2], top[3], bot[0], bot[1], bot[2], bot[3]};
+}
+
+// ---------------------------------------------------------------- buffer resources
+// A raw buffer descriptor (gfx9 family) over `bytes` bytes at `base`. Loads
+// and stores through it take a 32-bit per-lane offset plus scalar offsets,
+// and accesses past `bytes` are dropped by the hardware (stores) or return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // ---------------------------------------------------------------- wave reductions

@@ -31,11 +31,11 @@ struct ChunkArgs {
 };
 
 // Bytes of intermediates one (chunk, head) pair occupies in the workspace.
-size_t chunk_block_bytes(int dk, int chunk, bool bf16);
+size_t chunk_block_bytes(int dk, int dv, int chunk, bool bf16);
 // Upper bound on the number of chunks over all sequences.
 long chunk_count_bound(int B, int T, int chunk, bool varlen, int N);
 // Total workspace bytes for one forward call.
-size_t chunk_workspace_bytes(int B, int H, int T, int dk, int chunk, bool varlen, int N, bool bf16);
+size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, bool varlen, int N, bool bf16);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);

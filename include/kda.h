@@ -19,7 +19,8 @@
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent),
  *    row-major and contiguous, aligned to their element size. The decode
- *    state S and output o, and any workspace, must be 16-byte aligned.
+ *    state S and output o, the forward's q, k, v and gate, and any
+ *    workspace, must be 16-byte aligned.
  *    The caller owns every buffer.
  *  - Element type of q, k, v, gate and beta is selected by `dtype`:
  *    KDA_BF16 (bfloat16 bits) or KDA_F32. States S0, S_T, S and outputs o
