@@ -17,8 +17,8 @@
 //
 // Two kernels:
 //  * prep  -- one workgroup per (chunk, head), all chunks in parallel. Gate
-//    products, gated Gram matrices, the triangular inverse, and the operands
-//    W, Gamma o Q, K_end^T, T, P written to a workspace as MFMA fragments.
+//    products, gated Gram matrices, the triangular inverse, U~ = T V, and the
+//    operands W, Gamma o Q, K_end^T, P written to a workspace as MFMA fragments.
 //  * state -- one wavefront per 16 value columns of one (sequence, head),
 //    up to four per workgroup. Walks the chunks of its sequence in order with its
 //    slice of S in fp32 MFMA accumulator registers, while copy wavefronts of
@@ -37,18 +37,18 @@
 //
 // Precision. Inputs are exact in the operand formats. Matrix operands are
 // fp16 with a power-of-two scale per matrix (the scale is a property of the
-// data, chosen so the largest entry lies in [0.5, 1)), products accumulate in
-// fp32, and the state stays fp32. The one term that dominates an output --
-// the current token's own update, P_rr u_r -- is applied in fp32.
+// data, chosen so the largest entry lies in [0.5, 1)), value-side operands
+// with one such scale per column, products accumulate in fp32, and the state
+// stays fp32. The triangular inverse runs in fp32. The one term that dominates
+// an output -- the current token's own update, P_rr u_r -- is applied in fp32.
 // With fp32 inputs every contraction runs on fp32 MFMA instead.
+#include <mutex>
 #include <type_traits>
 
 #include "kda_common.h"
 #include "kda_launch.h"
 
 namespace kda {
-
-__device__ __forceinline__ __bf16 bf16_from_bits(uint16_t b) { return __builtin_bit_cast(__bf16, b); }
 
 // vmcnt(0) with lgkmcnt and expcnt left alone (gfx9 s_waitcnt encoding).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -59,6 +59,8 @@ __device__ __forceinline__ void wait_vm_upto() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
+// LDS writes of this wave are complete and visible to its own later reads.
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 // ------------------------------------------------------------------ one (chunk, head) block of the workspace
 
@@ -73,14 +75,20 @@ struct Lay {
     static constexpr size_t W_OFF = 0;                                      // W       [RB][KSD] A frags
     static constexpr size_t QG_OFF = W_OFF + (size_t)RB * KSD * FRAG;       // Gamma o Q [RB][KSD]
     static constexpr size_t KE_OFF = QG_OFF + (size_t)RB * KSD * FRAG;      // K_end^T [CB][KSC]
-    static constexpr size_t TT_OFF = KE_OFF + (size_t)CB * KSC * FRAG;      // T       [RB][KSC]
-    static constexpr size_t PS_OFF = TT_OFF + (size_t)RB * KSC * FRAG;      // strictly lower P [RB][KSC]
+    static constexpr size_t PS_OFF = KE_OFF + (size_t)CB * KSC * FRAG;      // strictly lower P [RB][KSC]
     static constexpr size_t PD_OFF = PS_OFF + (size_t)RB * KSC * FRAG;      // diagonal of P, fp32 [C]
     static constexpr size_t GN_OFF = PD_OFF + (size_t)C * 4;                // gamma_last, fp32 [DK]
-    static constexpr size_t SV_OFF = GN_OFF + (size_t)DK * 4;               // value column scales [128] + inverses [128]
-    static constexpr size_t SC_OFF = SV_OFF + 256 * 4;                      // matrix scales [8] + inverses [8]
+    static constexpr size_t SU_OFF = GN_OFF + (size_t)DK * 4;               // inverse scales of U~ columns [128]
+    static constexpr size_t SC_OFF = SU_OFF + 128 * 4;                      // matrix scales [8] + inverses [8]
     static constexpr size_t BYTES = (SC_OFF + 64 + 1023) / 1024 * 1024;     // shared part
-    static constexpr size_t VSL = (size_t)KSC * FRAG;                       // value B frags of one 16-column slice
+    // U~ = T V of one 16-column value slice in accumulator layout: lane l holds
+    // rows 16 rb + 4 (l / 16) + e of column l % 16. Stored [RB / UPR][64][UPR * 4]
+    // so that one lane reads UPR row blocks with one 8- or 16-byte load.
+    static constexpr int UPR = (!F32M && RB >= 2) ? 2 : 1;
+    static constexpr size_t USL = (size_t)C * 16 * sizeof(TM);
+    __host__ __device__ static constexpr size_t u_off(int rb, int lane) {
+        return (((size_t)(rb / UPR) * 64 + lane) * UPR + rb % UPR) * 4 * sizeof(TM);
+    }
 };
 
 // ------------------------------------------------------------------ fragments
@@ -92,47 +100,15 @@ template <> struct FragOf<float> { using type = f32x8; };
 template <class TM>
 __device__ __forceinline__ typename FragOf<TM>::type to_frag(const f32x8& x, float s) {
     if constexpr (std::is_same<TM, float>::value) {
-        return x;
+        return x;   // fp32 operands carry no scale
     } else {
         return to_f16x8(x, s);
     }
 }
 
-// Fragment from a row-major LDS array: row `row`, columns k0 + kpos(g, p),
-// zero where the column is >= KLIM.
-template <class TM, int KLIM>
-__device__ __forceinline__ typename FragOf<TM>::type lds_frag(const TM* base, int ld, int row, int k0, int g) {
-    using F = typename FragOf<TM>::type;
-    const TM* p = base + (size_t)row * ld + k0 + 4 * g;
-    F r;
-    if constexpr (KLIM % 32 == 0) {
-        if constexpr (std::is_same<TM, float>::value) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(p + 16);
-            r = F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        } else {
-            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-            const h4 a = *reinterpret_cast<const h4*>(p);
-            const h4 b = *reinterpret_cast<const h4*>(p + 16);
-            r = F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = (k0 + 4 * g + j < KLIM) ? p[j] : (TM)0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[4 + j] = (k0 + 16 + 4 * g + j < KLIM) ? p[16 + j] : (TM)0;
-    }
-    return r;
-}
-
 template <class TM>
 __device__ __forceinline__ void st_frag(unsigned char* base, int tile, int lane, const typename FragOf<TM>::type& f) {
     *reinterpret_cast<typename FragOf<TM>::type*>(base + ((size_t)tile * 64 + lane) * sizeof(f)) = f;
-}
-template <class TM>
-__device__ __forceinline__ typename FragOf<TM>::type ld_frag(const unsigned char* base, int tile, int lane) {
-    using F = typename FragOf<TM>::type;
-    return *reinterpret_cast<const F*>(base + ((size_t)tile * 64 + lane) * sizeof(F));
 }
 
 // 16-deep fp32 product on 16x16 tiles: step m takes K index 4g + m from lane group g.
@@ -142,13 +118,33 @@ __device__ __forceinline__ f32x4 mma16_f32(const f32x4& a, const f32x4& b, f32x4
     return c;
 }
 
+// Sum over the four lanes that hold one column of a 16x16 D tile (lanes i,
+// i+16, i+32, i+48). Every lane receives the same bits: each step adds the
+// same two operands in both lanes of a pair.
+__device__ __forceinline__ float colsum4(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t u2 = __float_as_uint(s);
+    const auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ------------------------------------------------------------------ chunk addressing
 
 struct ChunkMap {
     const int32_t* cu;      // null when every sequence has length T
     const int32_t* cstart;  // first chunk of each sequence (N+1), varlen only
     int T, N, NC;           // NC: chunks per sequence when not varlen
+    int c0, c1;             // not varlen: this launch covers chunks [c0, c1) of every sequence
 };
+
+// Workgroup-local chunk number -> global chunk index.
+__device__ __forceinline__ int launch_chunk(const ChunkMap& m, int li) {
+    if (m.cu != nullptr) return li;
+    const int ns = m.c1 - m.c0;
+    return (li / ns) * m.NC + m.c0 + li % ns;
+}
 
 // Chunk g -> first token (flattened over batch and time) and token count.
 __device__ __forceinline__ bool resolve_chunk(const ChunkMap& m, int g, int C, long& t0, int& n) {
@@ -203,36 +199,161 @@ __global__ void __launch_bounds__(256) chunk_index_kernel(const int32_t* __restr
 
 // ------------------------------------------------------------------ prep kernel
 
-template <int DK, int C, bool F32M>
-struct PrepSmem {
+// An operand staged in LDS as fragment tiles: tile (row / 16, k / 32); inside
+// a tile, lane group g owns a run of 16 slots (one per row i) holding the 8
+// values lane (i, g) reads for its fragment (row i, K positions kpos(g, p)).
+// Groups and tiles are padded (group stride = 16 slots + 16 or 32 bytes, tile
+// stride = 4 groups) so that a wave writing one row, two adjacent K
+// positions per lane, hits 4-byte banks that differ in both the group and
+// the K step, while each lane's row offset stays a constant: a lane computes
+// one base address and reaches every row with the instruction offset.
+template <class TM>
+struct Stg {
+    static constexpr int SLOT = 8 * (int)sizeof(TM);
+    static constexpr int GS = 17 * SLOT;   // 272 (fp16) or 544 (fp32) bytes
+    static constexpr int TS = 4 * GS;                                 // 1088 or 2176 bytes
+};
+template <class TM, int KS>
+__device__ __forceinline__ uint32_t stage_off(int row, int k) {
+    const int R = row >> 4, i = row & 15, s = k >> 5, q = k & 31;
+    const int g = (q & 15) >> 2, p = (q & 3) + ((q >> 4) << 2);
+    return (uint32_t)((R * KS + s) * Stg<TM>::TS + g * Stg<TM>::GS + i * Stg<TM>::SLOT + p * (int)sizeof(TM));
+}
+template <class TM, int KS>
+__device__ __forceinline__ uint32_t stage_frag_off(int R, int s, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    return (uint32_t)((R * KS + s) * Stg<TM>::TS + g * Stg<TM>::GS + i * Stg<TM>::SLOT);
+}
+
+template <class F>
+__device__ __forceinline__ F lds_ld(uint32_t off) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    return *reinterpret_cast<const F*>(smem + off);
+}
+template <class F>
+__device__ __forceinline__ void lds_st(uint32_t off, const F& v) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    *reinterpret_cast<F*>(smem + off) = v;
+}
+
+// n consecutive operand values (n = 1, 2 or 4) into LDS.
+template <class TM, int NV>
+__device__ __forceinline__ void st_vals(uint32_t off, const float* x) {
+    typedef TM v2 __attribute__((ext_vector_type(2)));
+    typedef TM v4 __attribute__((ext_vector_type(4)));
+    if constexpr (NV == 1) {
+        lds_st<TM>(off, (TM)x[0]);
+    } else if constexpr (NV == 2) {
+        lds_st<v2>(off, v2{(TM)x[0], (TM)x[1]});
+    } else {
+        lds_st<v4>(off, v4{(TM)x[0], (TM)x[1], (TM)x[2], (TM)x[3]});
+    }
+}
+
+// One lane's values of one input tensor over the 16 tokens of its block, for
+// its CPL channels; bf16 inputs stay packed (two channels per register).
+template <class TIn, int CPL>
+struct Gx {
+    float v[16][CPL];
+    __device__ __forceinline__ float get(int t, int j) const { return v[t][j]; }
+    __device__ __forceinline__ void load(const float* p, int t) {
+        if constexpr (CPL == 2) {
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            const f2 u = *reinterpret_cast<const f2*>(p);
+            v[t][0] = u[0];
+            v[t][1] = u[1];
+        } else {
+            v[t][0] = *p;
+        }
+    }
+    __device__ __forceinline__ void fill(int t, float x) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) v[t][j] = x;
+    }
+    __device__ __forceinline__ void fill_from(const float* p, int t) { fill(t, *p); }
+    __device__ __forceinline__ void opaque() {}
+};
+template <int CPL>
+struct Gx<uint16_t, CPL> {
+    uint32_t w[16];   // CPL == 2: channel 0 in the low half; CPL == 1: the low half
+    // Unpacked at each use, in place (volatile: not merged with, or hoisted
+    // ahead of, the same unpack in another phase, which would keep 96 fp32
+    // copies live next to the 48 packed words).
+    __device__ __forceinline__ float get(int t, int j) const {
+        uint32_t r;
+        if (CPL == 2 && j) asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w[t]));
+        else asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w[t]));
+        return __uint_as_float(r);
+    }
+    __device__ __forceinline__ void load(const uint16_t* p, int t) {
+        if constexpr (CPL == 2) w[t] = *reinterpret_cast<const uint32_t*>(p);
+        else w[t] = *p;
+    }
+    __device__ __forceinline__ void fill(int t, float x) {
+        const uint32_t b = __float_as_uint(x) >> 16;
+        w[t] = CPL == 2 ? (b | (b << 16)) : b;
+    }
+    __device__ __forceinline__ void fill_from(const uint16_t* p, int t) {
+        const uint32_t b = *p;
+        w[t] = CPL == 2 ? (b | (b << 16)) : b;
+    }
+    // Mark the packed words as rewritten (no instruction), so that unpacked
+    // copies are not kept live from one phase to the next.
+    __device__ __forceinline__ void opaque() {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) asm volatile("" : "+v"(w[t]));
+    }
+};
+
+template <int C, int KSC>
+__host__ __device__ constexpr int tf_count() {
+    int n = 0;
+    for (int rb = 0; rb < C / 16; ++rb) n += (rb / 2 < KSC - 1 ? rb / 2 : KSC - 1) + 1;
+    return n;
+}
+// Index of T fragment (rb, s), s <= rb / 2, in row-block order.
+template <int KSC>
+__host__ __device__ constexpr int tf_index(int rb, int s) {
+    int n = 0;
+    for (int r = 0; r < rb; ++r) n += (r / 2 < KSC - 1 ? r / 2 : KSC - 1) + 1;
+    return n + s;
+}
+
+template <class TIn, int DK, int C, bool F32M>
+struct PrepLds {
     using TM = typename Lay<DK, C, F32M>::TM;
-    static constexpr int NBK = C / 16;
-    static constexpr int LDM = DK + 8;   // [C][DK] arrays of TM
-    static constexpr int LDT = C + 4;    // [DK][C] arrays of TM
-    static constexpr int LDC = C + 4;    // [C][C] fp32
+    static constexpr int NBK = C / 16, KSD = (DK + 31) / 32, KSC = (C + 31) / 32, CB = DK / 16;
+    static constexpr int TILE = Stg<TM>::TS;                // staged operand tile
+    static constexpr int TFT = 64 * 8 * (int)sizeof(TM);    // T fragment tile (lane-ordered)
+    static constexpr int LDX = C + 4;   // row stride (floats) of the fp32 inverse arrays
+    static constexpr int NTF = tf_count<C, KSC>();
     static constexpr size_t al(size_t x) { return (x + 15) / 16 * 16; }
     static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-    static constexpr size_t GKT = 0;                                       // (Gamma o K)^T
-    static constexpr size_t BETA = al(GKT + (size_t)DK * LDT * sizeof(TM));
-    static constexpr size_t TOT = al(BETA + (size_t)C * 4);                // block gate totals [NBK][DK]
-    static constexpr size_t RED = al(TOT + (size_t)NBK * DK * 4);          // reductions [32]
-    static constexpr size_t ROUND = al(RED + 32 * 4);
-    // round A: Gamma o Q and K_end^T staging
-    static constexpr size_t QGS = ROUND;
-    static constexpr size_t KES = al(QGS + (size_t)C * LDM * sizeof(TM));
-    static constexpr size_t END_A = al(KES + (size_t)DK * LDT * sizeof(TM));
-    // one split level: K-side and Q-side scaled operands
-    static constexpr size_t XS = ROUND;
-    static constexpr size_t YS = al(XS + (size_t)C * LDM * sizeof(TM));
-    static constexpr size_t END_L = al(YS + (size_t)C * LDM * sizeof(TM));
-    // inverse
-    static constexpr size_t XI = ROUND;
-    static constexpr size_t AS = al(XI + (size_t)C * LDC * 4);
-    static constexpr size_t PSM = al(AS + (size_t)C * LDC * 4);
-    static constexpr size_t END_I = al(PSM + (size_t)C * LDC * 4);
-    // staged value rows (value width up to 128, rounded to whole 1 KiB copies)
-    static constexpr size_t END_V = ROUND + ((size_t)C * 128 * sizeof(TM) + 1023) / 1024 * 1024;
-    static constexpr size_t BYTES = mx(mx(mx(END_A, END_L), END_I), END_V);
+    static constexpr size_t BETA = 0;                                   // fp32 [C]
+    static constexpr size_t TOT = al(BETA + (size_t)C * 4);             // gate totals per token block [NBK][DK]
+    static constexpr size_t RED = al(TOT + (size_t)NBK * DK * 4);       // cross-wave maxima [32]
+    static constexpr size_t RGN = al(RED + 32 * 4);                     // reused region
+    // staged value rows (value width up to 128)
+    static constexpr size_t VST = RGN;
+    static constexpr size_t END_V = VST + ((size_t)C * 128 * sizeof(TIn) + 1023) / 1024 * 1024;
+    // Gamma o Q and K_end^T tiles
+    static constexpr size_t QGT = RGN;
+    static constexpr size_t KET = QGT + (size_t)NBK * KSD * TILE;
+    static constexpr size_t END_A = KET + (size_t)CB * KSC * TILE;
+    // one split level: K-side and Q-side tiles
+    static constexpr size_t XT = RGN;
+    static constexpr size_t YT = XT + (size_t)NBK * KSD * TILE;
+    static constexpr size_t END_L = YT + (size_t)NBK * KSD * TILE;
+    // inverse: A and X = (I + A)^{-1}, fp32 row-major
+    static constexpr size_t AM = RGN;
+    static constexpr size_t XM = al(AM + (size_t)C * LDX * 4);
+    static constexpr size_t END_I = al(XM + (size_t)C * LDX * 4);
+    // T fragments (over A), then (Gamma o K)^T tiles (over X)
+    static constexpr size_t TF = RGN;
+    static constexpr size_t GKT = TF + (size_t)NTF * TFT;
+    static constexpr size_t END_G = GKT + (size_t)CB * KSC * TILE;
+    static constexpr size_t BYTES = mx(mx(mx(END_A, END_L), mx(END_I, END_G)), END_V);
+    static_assert(TF + (size_t)NTF * TFT <= END_I, "T fragments fit the inverse area");
 };
 
 struct PrepParams {
@@ -251,61 +372,29 @@ __device__ __forceinline__ bool sep_at(int r, int j, int hh) {
     return (r / w == j / w) && (r % w >= hh) && (j % w < hh);
 }
 
-// Are 16-token blocks R (rows) and J (columns), R > J, separated at level hh >= 16?
-__host__ __device__ constexpr bool blocks_sep_at(int R, int J, int hh) {
-    return ((16 * R) / (2 * hh) == (16 * J) / (2 * hh)) && ((16 * R) % (2 * hh) >= hh) && ((16 * J) % (2 * hh) < hh);
-}
-
-// Two adjacent input elements (4- or 8-byte aligned) as floats.
-__device__ __forceinline__ void ld2(const uint16_t* p, float& a, float& b) {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-    a = bf16_bits_to_f32((uint16_t)(u & 0xffffu));
-    b = bf16_bits_to_f32((uint16_t)(u >> 16));
-}
-__device__ __forceinline__ void ld2(const float* p, float& a, float& b) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    const f2 u = *reinterpret_cast<const f2*>(p);
-    a = u[0];
-    b = u[1];
-}
-// Two adjacent operand elements into LDS.
-__device__ __forceinline__ void st2(_Float16* p, float a, float b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<h2*>(p) = h2{(_Float16)a, (_Float16)b};
-}
-__device__ __forceinline__ void st2(float* p, float a, float b) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<f2*>(p) = f2{a, b};
-}
-
 template <class TIn, int DK, int C, bool SG, bool F32M>
 __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
     using L = Lay<DK, C, F32M>;
-    using SM = PrepSmem<DK, C, F32M>;
+    using SM = PrepLds<TIn, DK, C, F32M>;
     using TM = typename L::TM;
+    using F = typename FragOf<TM>::type;
     constexpr int RB = L::RB, CB = L::CB, KSD = L::KSD, KSC = L::KSC;
     constexpr int NBK = C / 16;
-    constexpr int CPL = DK >= 64 ? DK / 64 : 1;   // channels per lane in the gate phase
-    constexpr int ACT = DK >= 64 ? 64 : DK;       // active lanes per wave in the gate phase
-    constexpr int NOFF = NBK * (NBK - 1);         // off-diagonal output blocks (A and P)
-    constexpr int OPW = NOFF > 0 ? (NOFF + 3) / 4 : 1;
+    constexpr int CPL = DK >= 64 ? DK / 64 : 1;   // channels per lane in the gate phases
+    constexpr int ACT = DK >= 64 ? 64 : DK;       // active lanes per wave in the gate phases
+    constexpr int LDX = SM::LDX;
+    constexpr int NBL = C == 64 ? 2 : (C == 32 ? 1 : 0);   // split levels between 16-token blocks
 
     extern __shared__ __align__(16) unsigned char smem[];
-    TM* s_gkt = reinterpret_cast<TM*>(smem + SM::GKT);
     float* s_beta = reinterpret_cast<float*>(smem + SM::BETA);
     float* s_tot = reinterpret_cast<float*>(smem + SM::TOT);
     float* s_red = reinterpret_cast<float*>(smem + SM::RED);
-    TM* s_qg = reinterpret_cast<TM*>(smem + SM::QGS);
-    TM* s_ke = reinterpret_cast<TM*>(smem + SM::KES);
-    TM* s_x = reinterpret_cast<TM*>(smem + SM::XS);
-    TM* s_y = reinterpret_cast<TM*>(smem + SM::YS);
-    float* s_xi = reinterpret_cast<float*>(smem + SM::XI);
-    float* s_a = reinterpret_cast<float*>(smem + SM::AS);
-    float* s_p = reinterpret_cast<float*>(smem + SM::PSM);
+    float* s_am = reinterpret_cast<float*>(smem + SM::AM);
+    float* s_xm = reinterpret_cast<float*>(smem + SM::XM);
 
     const int H = p.H, DV = p.DV;
     const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = item % H, gidx = item / H;
+    const int h = item % H, gidx = launch_chunk(p.map, item / H);
     long t0;
     int n;
     if (!resolve_chunk(p.map, gidx, C, t0, n)) return;   // uniform over the workgroup
@@ -320,43 +409,36 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
     const TIn* gg = (const TIn*)p.gate;
     const TIn* gb = (const TIn*)p.beta;
 
-    // ---- gate phase layout: wave b owns tokens 16b..16b+15, lane owns CPL channels
+    // ---- gate phases: wave b owns tokens 16b..16b+15, lane owns CPL channels
     const bool gate_lane = (w < NBK) && (lane < ACT);
-    const int blk_b = w;
+    const int b = w;
     const int c0 = lane * CPL;
-    float kk[16][CPL], qq[16][CPL], aa[16][CPL];
+    Gx<TIn, CPL> kk, qq, aa;
     float mk = 0.f, mq = 0.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-        const int tl = 16 * blk_b + t;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) { kk[t][j] = 0.f; qq[t][j] = 0.f; aa[t][j] = 1.f; }
+        const int tl = 16 * b + t;
         if (gate_lane && tl < n) {
             const size_t row = (size_t)(t0 + tl) * H + h;
-            if constexpr (CPL == 2) {
-                ld2(gk + row * DK + c0, kk[t][0], kk[t][1]);
-                ld2(gq + row * DK + c0, qq[t][0], qq[t][1]);
-                if constexpr (SG) {
-                    aa[t][0] = aa[t][1] = ld_in(gg + row);
-                } else {
-                    ld2(gg + row * DK + c0, aa[t][0], aa[t][1]);
-                }
-            } else {
-                kk[t][0] = ld_in(gk + row * DK + c0);
-                qq[t][0] = ld_in(gq + row * DK + c0);
-                aa[t][0] = SG ? ld_in(gg + row) : ld_in(gg + row * DK + c0);
-            }
+            kk.load(gk + row * DK + c0, t);
+            qq.load(gq + row * DK + c0, t);
+            if constexpr (SG) aa.fill_from(gg + row, t);
+            else aa.load(gg + row * DK + c0, t);
+        } else {
+            kk.fill(t, 0.f);
+            qq.fill(t, 0.f);
+            aa.fill(t, 1.f);
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            mk = fmaxf(mk, fabsf(kk[t][j]));
-            mq = fmaxf(mq, fabsf(qq[t][j]));
+            mk = fmaxf(mk, fabsf(kk.get(t, j)));
+            mq = fmaxf(mq, fabsf(qq.get(t, j)));
         }
     }
     if (tid < C) s_beta[tid] = tid < n ? ld_in(gb + (size_t)(t0 + tid) * H + h) : 0.f;
 
-    // ---- value rows of the chunk -> LDS, asynchronously; rows past the chunk
-    // end fall outside the descriptor and arrive as zeros
+    // value rows of the chunk -> LDS, asynchronously; rows past the chunk end
+    // fall outside the descriptor and arrive as zeros
     {
         const int rby = DV * (int)sizeof(TIn);            // bytes of one value row
         const int lpr = rby / 16, rpi = 64 / lpr;          // lanes per row, rows per instruction
@@ -366,7 +448,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
         for (int u = w; u < ni; u += 4) {
             const uint32_t voff = (uint32_t)(u * rpi + lane / lpr) * rowb + (uint32_t)(lane % lpr) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, (__attribute__((address_space(3))) void*)(smem + SM::ROUND + (size_t)u * 1024), 16, voff, 0, 0, 0);
+                rv, (__attribute__((address_space(3))) void*)(smem + SM::VST + (size_t)u * 1024), 16, voff, 0, 0, 0);
         }
     }
 
@@ -375,8 +457,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
         for (int j = 0; j < CPL; ++j) {
             float tot = 1.f;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) tot *= aa[t][j];
-            s_tot[blk_b * DK + c0 + j] = tot;
+            for (int t = 0; t < 16; ++t) tot *= aa.get(t, j);
+            s_tot[b * DK + c0 + j] = tot;
         }
     }
     mk = wave_max(mk);
@@ -393,13 +475,19 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
         sQ = pow2_scale_for(m2);
         iQ = pow2_inv_scale_for(m2);
     }
+    const float rQK = sQ * iK;   // Q-side over K-side scale (a power of two)
 
-    // ---- value fragments (B operand over tokens) from the staged rows, one
-    // 16-column slice per wave, scaled per column
+    // ---- value fragments (B operand over tokens), kept in registers until
+    // U~ = T V: wave w owns value slices w and w + 4, one scale per column
+    F vf[2][KSC];
+    float ivs[2];
     {
-        const TIn* vst = reinterpret_cast<const TIn*>(smem + SM::ROUND);
-        for (int sl = w; sl < DV / 16; sl += 4) {
-            f32x8 vf[KSC];
+        const TIn* vst = reinterpret_cast<const TIn*>(smem + SM::VST);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int sl = w + 4 * jj;
+            ivs[jj] = 1.f;
+            f32x8 x[KSC];
             float mv = 0.f;
             const int col = 16 * sl + li;
 #pragma unroll
@@ -407,305 +495,469 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int pp = 0; pp < 8; ++pp) {
                     const int t = 32 * ks + kpos(lg, pp);
-                    const float x = t < C ? ld_in(vst + t * DV + col) : 0.f;
-                    vf[ks][pp] = x;
-                    mv = fmaxf(mv, fabsf(x));
+                    const float v = (sl < DV / 16 && t < C) ? ld_in(vst + t * DV + col) : 0.f;
+                    x[ks][pp] = v;
+                    mv = fmaxf(mv, fabsf(v));
                 }
             float sv = 1.f;
             if constexpr (!F32M) {
                 mv = colmax4(mv);
                 sv = pow2_scale_for(mv);
-                if (lg == 0) {
-                    reinterpret_cast<float*>(blk + L::SV_OFF)[col] = sv;
-                    reinterpret_cast<float*>(blk + L::SV_OFF)[128 + col] = pow2_inv_scale_for(mv);
-                }
+                ivs[jj] = pow2_inv_scale_for(mv);
             }
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-                st_frag<TM>(blk + L::BYTES + (size_t)sl * L::VSL, ks, lane, to_frag<TM>(vf[ks], sv));
+            for (int ks = 0; ks < KSC; ++ks) vf[jj][ks] = to_frag<TM>(x[ks], sv);
         }
     }
     __syncthreads();
 
-    // ---- round A: Gamma o Q, K_end^T, (Gamma o K)^T, gamma_last
+    // ---- Gamma o Q (rows tokens), K_end^T (rows channels), gamma_last
+    kk.opaque();
+    qq.opaque();
+    aa.opaque();
     if (gate_lane) {
         float pre[CPL], suf[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            pre[j] = 1.f;
-            suf[j] = 1.f;
+            pre[j] = sQ;
+            suf[j] = sK;
+            float all = 1.f;
 #pragma unroll
-            for (int b = 0; b < NBK; ++b) {
-                const float tb = s_tot[b * DK + c0 + j];
-                if (b < blk_b) pre[j] *= tb;
-                if (b > blk_b) suf[j] *= tb;
+            for (int bb = 0; bb < NBK; ++bb) {
+                const float tb = s_tot[bb * DK + c0 + j];
+                if (bb < b) pre[j] *= tb;
+                if (bb > b) suf[j] *= tb;
+                all *= tb;
             }
+            if (b == 0) reinterpret_cast<float*>(blk + L::GN_OFF)[c0 + j] = all;
         }
-        float run[CPL], gkp[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) run[j] = pre[j];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const int tl = 16 * blk_b + t;
-            float qg[CPL];
+            float qg[2];
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                run[j] *= aa[t][j];
-                qg[j] = qq[t][j] * run[j] * sQ;
-                const float gk = kk[t][j] * run[j] * sK;
-                if (t & 1) st2(&s_gkt[(c0 + j) * SM::LDT + tl - 1], gkp[j], gk);
-                gkp[j] = gk;
+                pre[j] *= aa.get(t, j);
+                qg[j] = qq.get(t, j) * pre[j];
             }
-            if constexpr (CPL == 2) st2(&s_qg[tl * SM::LDM + c0], qg[0], qg[1]);
-            else s_qg[tl * SM::LDM + c0] = (TM)qg[0];
-        }
-        if (blk_b == NBK - 1) {
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) reinterpret_cast<float*>(blk + L::GN_OFF)[c0 + j] = run[j];
+            st_vals<TM, CPL>(SM::QGT + stage_off<TM, KSD>(16 * b + t, c0), qg);
+            if constexpr (DK == 16) {
+                const float z = 0.f;
+                st_vals<TM, 1>(SM::QGT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+            }
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            float r = suf[j], nxt = 0.f;
+            float ke[16];
+            float r = suf[j];
 #pragma unroll
             for (int t = 15; t >= 0; --t) {
-                const float ke = kk[t][j] * r * sK;
-                if (!(t & 1)) st2(&s_ke[(c0 + j) * SM::LDT + 16 * blk_b + t], ke, nxt);
-                nxt = ke;
-                r *= aa[t][j];
+                ke[t] = kk.get(t, j) * r;
+                r *= aa.get(t, j);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; u += 4) {
+                st_vals<TM, 4>(SM::KET + stage_off<TM, KSC>(c0 + j, 16 * b + u), ke + u);
+                if constexpr (C == 16) {
+                    const float z[4] = {0.f, 0.f, 0.f, 0.f};
+                    st_vals<TM, 4>(SM::KET + stage_off<TM, KSC>(c0 + j, 16 + u), z);
+                }
             }
         }
     }
     __syncthreads();
-    for (int tt = w; tt < RB * KSD; tt += 4) {
-        const int rb = tt / KSD, s = tt % KSD;
-        st_frag<TM>(blk + L::QG_OFF, tt, lane, lds_frag<TM, DK>(s_qg, SM::LDM, 16 * rb + li, 32 * s, lg));
-    }
-    for (int tt = w; tt < CB * KSC; tt += 4) {
-        const int cb = tt / KSC, s = tt % KSC;
-        st_frag<TM>(blk + L::KE_OFF, tt, lane, lds_frag<TM, C>(s_ke, SM::LDT, 16 * cb + li, 32 * s, lg));
-    }
+    for (int tt = w; tt < RB * KSD; tt += 4)
+        st_frag<TM>(blk + L::QG_OFF, tt, lane, lds_ld<F>(SM::QGT + stage_frag_off<TM, KSD>(tt / KSD, tt % KSD, lane)));
+    for (int tt = w; tt < CB * KSC; tt += 4)
+        st_frag<TM>(blk + L::KE_OFF, tt, lane, lds_ld<F>(SM::KET + stage_frag_off<TM, KSC>(tt / KSC, tt % KSC, lane)));
     __syncthreads();
 
-    // ---- gated Gram matrices, one split level per round
-    f32x4 accA = zero4(), accP = zero4();   // diagonal block (w, w)
-    f32x4 accO[OPW];                        // off-diagonal outputs o = w + 4 j
+    // ---- split levels between 16-token blocks. Each block pair (R > J) is
+    // separated at exactly one of them; the wave that takes the pair holds its
+    // A^T and P^T tiles (row j, column r) until they are written out.
+    f32x4 pa[NBL > 0 ? NBL : 1], pq[NBL > 0 ? NBL : 1];
+    int pR[NBL > 0 ? NBL : 1], pJ[NBL > 0 ? NBL : 1];
 #pragma unroll
-    for (int j = 0; j < OPW; ++j) accO[j] = zero4();
-
-    auto off_out = [](int o, int& R, int& J, bool& isP) {
-        isP = o >= NOFF / 2;
-        int idx = isP ? o - NOFF / 2 : o;
-        R = 1;
-        while (idx >= R) { idx -= R; ++R; }
-        J = idx;
-    };
-
-    constexpr int NLEV = (C == 64 ? 2 : (C == 32 ? 1 : 0)) + 5;
-#pragma unroll
-    for (int lev = 0; lev < NLEV; ++lev) {
-        // half widths: C/2, ..., 16 (between blocks), then 8, 4, 2, 1, 0 (inside blocks)
-        const int hh = lev < NLEV - 5 ? (C >> (lev + 1)) : (lev == NLEV - 1 ? 0 : (8 >> (lev - (NLEV - 5))));
+    for (int lev = 0; lev < NBL; ++lev) {
+        const int hb = (C >> (lev + 1)) / 16;   // half width in blocks
+        kk.opaque();
+        qq.opaque();
+        aa.opaque();
         if (gate_lane) {
-            float f[16][CPL];
+            const int gs = (b / (2 * hb)) * 2 * hb, midb = gs + hb;
+            const bool right = b >= midb;
+            float f[CPL];
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const int c = c0 + j;
-                if (hh >= 16) {
-                    const int hb = hh / 16;
-                    const int gs = (blk_b / (2 * hb)) * 2 * hb, midb = gs + hb;
-                    if (blk_b >= midb) {
-                        float run = 1.f;
-                        for (int b = midb; b < blk_b; ++b) run *= s_tot[b * DK + c];
-#pragma unroll
-                        for (int t = 0; t < 16; ++t) { run *= aa[t][j]; f[t][j] = run; }
-                    } else {
-                        float run = 1.f;
-                        for (int b = blk_b + 1; b < midb; ++b) run *= s_tot[b * DK + c];
-#pragma unroll
-                        for (int t = 15; t >= 0; --t) { f[t][j] = run; run *= aa[t][j]; }
-                    }
-                } else if (hh == 0) {
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) f[t][j] = 1.f;
+                f[j] = sK;
+                if (right) {
+                    for (int bb = midb; bb < b; ++bb) f[j] *= s_tot[bb * DK + c0 + j];
                 } else {
-#pragma unroll
-                    for (int g0 = 0; g0 < 16; g0 += 2 * hh) {
-                        float run = 1.f;
-#pragma unroll
-                        for (int t = g0 + hh; t < g0 + 2 * hh; ++t) { run *= aa[t][j]; f[t][j] = run; }
-                        run = 1.f;
-#pragma unroll
-                        for (int t = g0 + hh - 1; t >= g0; --t) { f[t][j] = run; run *= aa[t][j]; }
-                    }
+                    for (int bb = b + 1; bb < midb; ++bb) f[j] *= s_tot[bb * DK + c0 + j];
                 }
             }
+            if (right) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int tl = 16 * blk_b + t;
-                if constexpr (CPL == 2) {
-                    st2(&s_x[tl * SM::LDM + c0], kk[t][0] * f[t][0] * sK, kk[t][1] * f[t][1] * sK);
-                    st2(&s_y[tl * SM::LDM + c0], qq[t][0] * f[t][0] * sQ, qq[t][1] * f[t][1] * sQ);
-                } else {
-                    s_x[tl * SM::LDM + c0] = (TM)(kk[t][0] * f[t][0] * sK);
-                    s_y[tl * SM::LDM + c0] = (TM)(qq[t][0] * f[t][0] * sQ);
+                for (int t = 0; t < 16; ++t) {
+                    float x[2], y[2];
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        f[j] *= aa.get(t, j);
+                        x[j] = kk.get(t, j) * f[j];
+                        y[j] = qq.get(t, j) * (f[j] * rQK);
+                    }
+                    st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
+                    st_vals<TM, CPL>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0), y);
+                    if constexpr (DK == 16) {
+                        const float z = 0.f;
+                        st_vals<TM, 1>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                        st_vals<TM, 1>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 15; t >= 0; --t) {
+                    float x[2];
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        x[j] = kk.get(t, j) * f[j];
+                        f[j] *= aa.get(t, j);
+                    }
+                    st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
+                    if constexpr (DK == 16) {
+                        const float z = 0.f;
+                        st_vals<TM, 1>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                    }
                 }
             }
         }
         __syncthreads();
-        if (hh >= 16) {
-#pragma unroll
-            for (int j = 0; j < OPW; ++j) {
-                const int o = w + 4 * j;
-                if (o >= NOFF) continue;
-                int R, J;
-                bool isP;
-                off_out(o, R, J, isP);
-                if (!blocks_sep_at(R, J, hh)) continue;
-#pragma unroll
-                for (int s = 0; s < KSD; ++s) {
-                    const auto af = lds_frag<TM, DK>(isP ? s_y : s_x, SM::LDM, 16 * R + li, 32 * s, lg);
-                    const auto bf = lds_frag<TM, DK>(s_x, SM::LDM, 16 * J + li, 32 * s, lg);
-                    accO[j] = mma(af, bf, accO[j]);
-                }
-            }
-        } else if (w < NBK) {
+        const int npairs = (NBK / (2 * hb)) * hb * hb;
+        pR[lev] = -1;
+        pJ[lev] = 0;
+        pa[lev] = zero4();
+        pq[lev] = zero4();
+        if (w < npairs) {
+            const int gi = w / (hb * hb), rem = w % (hb * hb);
+            const int R = gi * 2 * hb + hb + rem / hb, J = gi * 2 * hb + rem % hb;
             f32x4 ta = zero4(), tp = zero4();
 #pragma unroll
             for (int s = 0; s < KSD; ++s) {
-                const auto xf = lds_frag<TM, DK>(s_x, SM::LDM, 16 * w + li, 32 * s, lg);
-                const auto yf = lds_frag<TM, DK>(s_y, SM::LDM, 16 * w + li, 32 * s, lg);
-                if (hh > 0) ta = mma(xf, xf, ta);
-                tp = mma(yf, xf, tp);
+                const F xj = lds_ld<F>(SM::XT + stage_frag_off<TM, KSD>(J, s, lane));
+                const F xr = lds_ld<F>(SM::XT + stage_frag_off<TM, KSD>(R, s, lane));
+                const F yr = lds_ld<F>(SM::YT + stage_frag_off<TM, KSD>(R, s, lane));
+                ta = mma(xj, xr, ta);
+                tp = mma(xj, yr, tp);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (sep_at(4 * lg + e, li, hh)) {
-                    accA[e] += ta[e];
-                    accP[e] += tp[e];
-                }
-            }
+            pa[lev] = ta;
+            pq[lev] = tp;
+            pR[lev] = R;
+            pJ[lev] = J;
         }
         __syncthreads();
     }
 
-    // ---- A = Diag(beta) A', P into LDS (upper blocks zero)
-    for (int x = tid; x < C * SM::LDC; x += 256) { s_xi[x] = 0.f; s_a[x] = 0.f; s_p[x] = 0.f; }
-    __syncthreads();
+    // ---- split levels inside each 16-token block (8, 4, 2, 1, then the
+    // diagonal): wave b stages and reads only its own block, no barriers.
+    f32x4 dA = zero4(), dP = zero4();   // A^T and P^T of diagonal block (b, b)
+    if (w < NBK) {
+#pragma unroll
+        for (int lev = 0; lev < 5; ++lev) {
+            const int hh = lev < 4 ? (8 >> lev) : 0;
+            kk.opaque();
+            qq.opaque();
+            aa.opaque();
+            if (lane < ACT) {
+                if (hh > 0) {
+#pragma unroll
+                    for (int g0 = 0; g0 < 16; g0 += 2 * hh) {
+                        float f[CPL];
+#pragma unroll
+                        for (int j = 0; j < CPL; ++j) f[j] = sK;
+#pragma unroll
+                        for (int t = g0 + hh; t < g0 + 2 * hh; ++t) {
+                            float x[2], y[2];
+#pragma unroll
+                            for (int j = 0; j < CPL; ++j) {
+                                f[j] *= aa.get(t, j);
+                                x[j] = kk.get(t, j) * f[j];
+                                y[j] = qq.get(t, j) * (f[j] * rQK);
+                            }
+                            st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
+                            st_vals<TM, CPL>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0), y);
+                            if constexpr (DK == 16) {
+                                const float z = 0.f;
+                                st_vals<TM, 1>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                                st_vals<TM, 1>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                            }
+                        }
+#pragma unroll
+                        for (int j = 0; j < CPL; ++j) f[j] = sK;
+#pragma unroll
+                        for (int t = g0 + hh - 1; t >= g0; --t) {
+                            float x[2];
+#pragma unroll
+                            for (int j = 0; j < CPL; ++j) {
+                                x[j] = kk.get(t, j) * f[j];
+                                f[j] *= aa.get(t, j);
+                            }
+                            st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
+                            if constexpr (DK == 16) {
+                                const float z = 0.f;
+                                st_vals<TM, 1>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        float x[2], y[2];
+#pragma unroll
+                        for (int j = 0; j < CPL; ++j) {
+                            x[j] = kk.get(t, j) * sK;
+                            y[j] = qq.get(t, j) * sQ;
+                        }
+                        st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
+                        st_vals<TM, CPL>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0), y);
+                        if constexpr (DK == 16) {
+                            const float z = 0.f;
+                            st_vals<TM, 1>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                            st_vals<TM, 1>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0 + 16), &z);
+                        }
+                    }
+                }
+            }
+            wave_lds_fence();
+            f32x4 ta = zero4(), tp = zero4();
+#pragma unroll
+            for (int s = 0; s < KSD; ++s) {
+                const F xb = lds_ld<F>(SM::XT + stage_frag_off<TM, KSD>(b, s, lane));
+                const F yb = lds_ld<F>(SM::YT + stage_frag_off<TM, KSD>(b, s, lane));
+                if (hh > 0) ta = mma(xb, xb, ta);
+                tp = mma(xb, yb, tp);
+            }
+            // lane (li, lg) holds entries (row j = 4 lg + e, column r = li)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool keep = sep_at(li, 4 * lg + e, hh);
+                if (hh > 0) dA[e] = keep ? dA[e] + ta[e] : dA[e];
+                dP[e] = keep ? dP[e] + tp[e] : dP[e];
+            }
+            wave_lds_fence();
+        }
+    }
+    __syncthreads();   // the inverse arrays overlay the level tiles
+
+    // ---- A = Diag(beta) A' into LDS (fp32, row-major); largest |P| below the diagonal
+    const float invKK = iK * iK, invQK = iQ * iK;
+    float mp = 0.f;
     {
-        const float invKK = iK * iK, invQK = iQ * iK;
+        auto put_a = [&](int R, int J, const f32x4& t) {
+            const int r = 16 * R + li;
+            const float sb = invKK * s_beta[r];
+            lds_st<f32x4>(SM::AM + (uint32_t)((r * LDX + 16 * J + 4 * lg) * 4), t * sb);
+        };
         if (w < NBK) {
+            put_a(b, b, dA);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * w + 4 * lg + e, c = 16 * w + li;
-                s_a[r * SM::LDC + c] = accA[e] * invKK * s_beta[r];
-                s_p[r * SM::LDC + c] = accP[e] * invQK;
-            }
+            for (int e = 0; e < 4; ++e)
+                if (4 * lg + e < li) mp = fmaxf(mp, fabsf(dP[e]));
         }
 #pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-            const int o = w + 4 * j;
-            if (o >= NOFF) continue;
-            int R, J;
-            bool isP;
-            off_out(o, R, J, isP);
+        for (int lev = 0; lev < NBL; ++lev) {
+            if (pR[lev] >= 0) {
+                put_a(pR[lev], pJ[lev], pa[lev]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * R + 4 * lg + e, c = 16 * J + li;
-                if (isP) s_p[r * SM::LDC + c] = accO[j][e] * invQK;
-                else s_a[r * SM::LDC + c] = accO[j][e] * invKK * s_beta[r];
+                for (int e = 0; e < 4; ++e) mp = fmaxf(mp, fabsf(pq[lev][e]));
             }
         }
     }
+    mp = wave_max(mp);
+    if (lane == 0) s_red[8 + w] = mp;
     __syncthreads();
 
-    // ---- inverses of the 16x16 unit-lower diagonal blocks of I + A
-    if (tid < RB * 16) {
-        const int b = tid / 16, jj = tid % 16;
-        const float* arow = s_a + (16 * b) * SM::LDC + 16 * b;
-        float x[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float v = rr == jj ? 1.f : 0.f;
-            if (rr > jj) {
-                float sacc = 0.f;
-#pragma unroll
-                for (int m = 0; m < rr; ++m)
-                    if (m >= jj) sacc += arow[rr * SM::LDC + m] * x[m];
-                v = -sacc;
-            }
-            x[rr] = v;
-            s_xi[(16 * b + rr) * SM::LDC + 16 * b + jj] = v;
-        }
-    }
-    __syncthreads();
-    // ---- off-diagonal blocks, X_RJ = -X_RR sum_{J<=M<R} A_RM X_MJ
-    for (int R = 1; R < RB; ++R) {
-        for (int J = w; J < R; J += 4) {
-            f32x4 tacc = zero4();
-            for (int M = J; M < R; ++M) {
-                f32x4 af, bf;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    af[m] = s_a[(16 * R + li) * SM::LDC + 16 * M + 4 * lg + m];
-                    bf[m] = s_xi[(16 * M + 4 * lg + m) * SM::LDC + 16 * J + li];
-                }
-                tacc = mma16_f32(af, bf, tacc);
-            }
-            f32x4 xf;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) xf[m] = s_xi[(16 * R + li) * SM::LDC + 16 * R + 4 * lg + m];
-            const f32x4 xr = mma16_f32(xf, tacc, zero4());
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s_xi[(16 * R + 4 * lg + e) * SM::LDC + 16 * J + li] = -xr[e];
-        }
-        __syncthreads();
-    }
-
-    // ---- T = X Diag(beta), strictly lower P, diagonal of P; their scales
-    auto t_frag = [&](int rb, int s) -> f32x8 {
-        f32x8 r;
-#pragma unroll
-        for (int pp = 0; pp < 8; ++pp) {
-            const int c = 32 * s + kpos(lg, pp);
-            r[pp] = c < C ? s_xi[(16 * rb + li) * SM::LDC + c] * s_beta[c] : 0.f;
-        }
-        return r;
-    };
-    auto p_frag = [&](int rb, int s) -> f32x8 {
-        f32x8 r;
-#pragma unroll
-        for (int pp = 0; pp < 8; ++pp) {
-            const int c = 32 * s + kpos(lg, pp);
-            const int row = 16 * rb + li;
-            r[pp] = (c < C && c < row) ? s_p[row * SM::LDC + c] : 0.f;
-        }
-        return r;
-    };
-    float sT = 1.f, sP = 1.f, iT = 1.f, iP = 1.f;
+    // ---- P: strictly lower part as scaled A fragments, diagonal in fp32
+    float sP = 1.f, iP = 1.f;
     if constexpr (!F32M) {
-        float mt = 0.f, mp = 0.f;
-        for (int x = tid; x < C * C; x += 256) {
-            const int r = x / C, c = x % C;
-            mt = fmaxf(mt, fabsf(s_xi[r * SM::LDC + c] * s_beta[c]));
-            if (c < r) mp = fmaxf(mp, fabsf(s_p[r * SM::LDC + c]));
+        const float m = fmaxf(fmaxf(s_red[8], s_red[9]), fmaxf(s_red[10], s_red[11])) * invQK;
+        sP = pow2_scale_for(m);
+        iP = pow2_inv_scale_for(m);
+    }
+    {
+        typedef TM v4 __attribute__((ext_vector_type(4)));
+        const float cP = invQK * sP;
+        // lane (li, lg) holds P[16R + li][16J + 4lg + e]: half J % 2 of fragment (R, J / 2)
+        auto put_p = [&](int R, int J, const f32x4& t, bool diag) {
+            v4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (TM)((!diag || 4 * lg + e < li) ? t[e] * cP : 0.f);
+            *reinterpret_cast<v4*>(blk + L::PS_OFF + ((size_t)(R * KSC + J / 2) * 64 + lane) * 8 * sizeof(TM) +
+                                   (J % 2) * 4 * sizeof(TM)) = x;
+        };
+        if (w < NBK) {
+            put_p(b, b, dP, true);
+            if (b % 2 == 0) put_p(b, b + 1, zero4(), false);   // upper half of the fragment
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * lg + e == li) reinterpret_cast<float*>(blk + L::PD_OFF)[16 * b + li] = dP[e] * invQK;
         }
-        mt = wave_max(mt);
-        mp = wave_max(mp);
-        if (lane == 0) { s_red[8 + w] = mt; s_red[12 + w] = mp; }
+#pragma unroll
+        for (int lev = 0; lev < NBL; ++lev)
+            if (pR[lev] >= 0) put_p(pR[lev], pJ[lev], pq[lev], false);
+    }
+
+    // ---- inverses of the 16x16 unit-lower diagonal blocks of I + A, one wave
+    // per block: lane (li, lg) keeps rows 4lg..4lg+3 of column li
+    if (w < NBK) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (4 * lg + e == li) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            const f32x4 a = lds_ld<f32x4>(SM::AM + (uint32_t)(((16 * b + r) * LDX + 16 * b + 4 * lg) * 4));
+            const float part = colsum4(a[0] * x[0] + a[1] * x[1] + a[2] * x[2] + a[3] * x[3]);
+            const float xr = r > li ? -part : (r == li ? 1.f : 0.f);
+            if (lg == r / 4) x[r % 4] = xr;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_xm[(16 * b + 4 * lg + e) * LDX + 16 * b + li] = x[e];
+    }
+    __syncthreads();
+    // ---- off-diagonal blocks by distance, X_RJ = -X_RR sum_{J<=M<R} A_RM X_MJ
+#pragma unroll
+    for (int d = 1; d < NBK; ++d) {
+        if (w < NBK - d) {
+            const int J = w, R = w + d;
+            f32x4 y = zero4();
+            for (int M = J; M < R; ++M) {
+                const f32x4 a = lds_ld<f32x4>(SM::AM + (uint32_t)(((16 * R + li) * LDX + 16 * M + 4 * lg) * 4));
+                f32x4 bx;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) bx[m] = s_xm[(16 * M + 4 * lg + m) * LDX + 16 * J + li];
+                y = mma16_f32(a, bx, y);
+            }
+            const f32x4 xr = lds_ld<f32x4>(SM::XM + (uint32_t)(((16 * R + li) * LDX + 16 * R + 4 * lg) * 4));
+            const f32x4 res = mma16_f32(xr, y, zero4());
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_xm[(16 * R + 4 * lg + e) * LDX + 16 * J + li] = -res[e];
+        }
         __syncthreads();
-        const float m1 = fmaxf(fmaxf(s_red[8], s_red[9]), fmaxf(s_red[10], s_red[11]));
-        const float m2 = fmaxf(fmaxf(s_red[12], s_red[13]), fmaxf(s_red[14], s_red[15]));
-        sT = pow2_scale_for(m1);
-        iT = pow2_inv_scale_for(m1);
-        sP = pow2_scale_for(m2);
-        iP = pow2_inv_scale_for(m2);
     }
-    for (int tt = w; tt < RB * KSC; tt += 4) {
-        const int rb = tt / KSC, s = tt % KSC;
-        st_frag<TM>(blk + L::TT_OFF, tt, lane, to_frag<TM>(t_frag(rb, s), sT));
-        st_frag<TM>(blk + L::PS_OFF, tt, lane, to_frag<TM>(p_frag(rb, s), sP));
+
+    // ---- T = X Diag(beta) as A fragments (rows r, K over tokens j <= r), one scale
+    constexpr int NTF = SM::NTF;
+    f32x8 tv[2];
+    float mt = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int f = w + 4 * jj;
+        tv[jj] = f32x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (f < NTF) {
+            int rb = 0, s = 0;
+            for (int r = 0, acc = 0; r < RB; ++r) {
+                const int ns = (r / 2 < KSC - 1 ? r / 2 : KSC - 1) + 1;
+                if (f < acc + ns) { rb = r; s = f - acc; break; }
+                acc += ns;
+            }
+            const int row = 16 * rb + li;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int c = 32 * s + 16 * half + 4 * lg;
+                if (c < C) {
+                    const f32x4 xv = lds_ld<f32x4>(SM::XM + (uint32_t)((row * LDX + c) * 4));
+                    const f32x4 bv = lds_ld<f32x4>(SM::BETA + (uint32_t)(c * 4));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = (c + e <= row) ? xv[e] * bv[e] : 0.f;
+                        tv[jj][4 * half + e] = v;
+                        mt = fmaxf(mt, fabsf(v));
+                    }
+                }
+            }
+        }
     }
-    if (tid < C) reinterpret_cast<float*>(blk + L::PD_OFF)[tid] = s_p[tid * SM::LDC + tid];
+    mt = wave_max(mt);
+    if (lane == 0) s_red[12 + w] = mt;
+    __syncthreads();
+    float sT = 1.f, iT = 1.f;
+    if constexpr (!F32M) {
+        const float m = fmaxf(fmaxf(s_red[12], s_red[13]), fmaxf(s_red[14], s_red[15]));
+        sT = pow2_scale_for(m);
+        iT = pow2_inv_scale_for(m);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int f = w + 4 * jj;
+        if (f < NTF) lds_st<F>(SM::TF + (uint32_t)((f * 64 + lane) * sizeof(F)), to_frag<TM>(tv[jj], sT));
+    }
+    __syncthreads();
+    auto tfrag = [&](int rb, int s) { return lds_ld<F>(SM::TF + (uint32_t)((tf_index<KSC>(rb, s) * 64 + lane) * sizeof(F))); };
+
+    // ---- (Gamma o K)^T tiles (rows channels, K over tokens) for W
+    kk.opaque();
+    aa.opaque();
+    if (gate_lane) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            float r = sK;
+            for (int bb = 0; bb < b; ++bb) r *= s_tot[bb * DK + c0 + j];
+            float gk[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                r *= aa.get(t, j);
+                gk[t] = kk.get(t, j) * r;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; u += 4) {
+                st_vals<TM, 4>(SM::GKT + stage_off<TM, KSC>(c0 + j, 16 * b + u), gk + u);
+                if constexpr (C == 16) {
+                    const float z[4] = {0.f, 0.f, 0.f, 0.f};
+                    st_vals<TM, 4>(SM::GKT + stage_off<TM, KSC>(c0 + j, 16 + u), z);
+                }
+            }
+        }
+    }
+
+    // ---- U~ = T V for this wave's value slices, one scale per column
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int sl = w + 4 * jj;
+        if (sl < DV / 16) {
+            f32x4 acc[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                acc[rb] = zero4();
+#pragma unroll
+                for (int s = 0; s < KSC; ++s)
+                    if (s <= rb / 2) acc[rb] = mma(tfrag(rb, s), vf[jj][s], acc[rb]);
+            }
+            const float cu = iT * ivs[jj];
+            float m = 0.f;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[rb][e] *= cu;
+                    m = fmaxf(m, fabsf(acc[rb][e]));
+                }
+            float sU = 1.f, iU = 1.f;
+            if constexpr (!F32M) {
+                m = colmax4(m);
+                sU = pow2_scale_for(m);
+                iU = pow2_inv_scale_for(m);
+            }
+            typedef TM v4 __attribute__((ext_vector_type(4)));
+            unsigned char* ub = blk + L::BYTES + (size_t)sl * L::USL;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                v4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (TM)(acc[rb][e] * sU);
+                *reinterpret_cast<v4*>(ub + L::u_off(rb, lane)) = x;
+            }
+            if (lg == 0) reinterpret_cast<float*>(blk + L::SU_OFF)[16 * sl + li] = iU;
+        }
+    }
+    __syncthreads();
 
     // ---- W = T (Gamma o K), computed as W^T = (Gamma o K)^T T^T: two stacked
     // 16x16 tiles of W^T (channel blocks 2s, 2s+1) are the A fragment of W for
@@ -724,12 +976,12 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
 #pragma unroll
         for (int s = 0; s < KSC; ++s) {
             if (s > rb / 2) continue;
-            const auto bf = to_frag<TM>(t_frag(rb, s), sT);
+            const F bf = tfrag(rb, s);
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int cb = 2 * s2 + half;
                 if (cb >= CB) continue;
-                const auto af = lds_frag<TM, C>(s_gkt, SM::LDT, 16 * cb + li, 32 * s, lg);
+                const F af = lds_ld<F>(SM::GKT + stage_frag_off<TM, KSC>(cb, s, lane));
                 wt[j][half] = mma(af, bf, wt[j][half]);
             }
         }
@@ -789,7 +1041,8 @@ template <int DK, int C, bool F32M, int NW, int SPW>
 struct StateSmem {
     using L = Lay<DK, C, F32M>;
     static constexpr int NSL = NW * SPW;   // slices per workgroup
-    static constexpr size_t BUF = L::BYTES + (size_t)NSL * L::VSL;
+    static constexpr size_t UBYTES = ((size_t)NSL * L::USL + 1023) / 1024 * 1024;   // whole 1 KiB copies
+    static constexpr size_t BUF = L::BYTES + UBYTES;
     static constexpr int NBUF = (2 * BUF <= 160 * 1024) ? 2 : 1;
     static constexpr size_t BYTES = NBUF * BUF;
 };
@@ -804,9 +1057,9 @@ __device__ __forceinline__ void stage_chunk(uint32_t lds_off, const unsigned cha
     using L = Lay<DK, C, F32M>;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int U0 = (int)(L::BYTES / 1024);
-    constexpr int UV = (int)(NSL * L::VSL / 1024);
+    constexpr int UV = (int)((NSL * L::USL + 1023) / 1024);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(gblk, (uint32_t)blk_bytes);
-    const int vbase = (int)(L::BYTES + (size_t)sg * NSL * L::VSL) - U0 * 1024;
+    const int vbase = (int)(L::BYTES + (size_t)sg * NSL * L::USL) - U0 * 1024;
 #pragma unroll
     for (int u = w; u < U0 + UV; u += NW) {
         const int soff = u < U0 ? u * 1024 : vbase + u * 1024;
@@ -824,7 +1077,7 @@ __device__ __forceinline__ void touch_chunk(uint32_t (&pf)[NPF], const unsigned 
     using L = Lay<DK, C, F32M>;
     constexpr int L0 = (int)(L::BYTES / 128);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(gblk, (uint32_t)blk_bytes);
-    const int vbase = (int)(L::BYTES + (size_t)sg * NSL * L::VSL) - L0 * 128;
+    const int vbase = (int)(L::BYTES + (size_t)sg * NSL * L::USL) - L0 * 128;
 #pragma unroll
     for (int k = 0; k < NPF; ++k) {
         const int line = (k * NW + w) * 64 + lane;
@@ -833,19 +1086,13 @@ __device__ __forceinline__ void touch_chunk(uint32_t (&pf)[NPF], const unsigned 
     }
 }
 
-template <class F>
-__device__ __forceinline__ F lds_ld(uint32_t off) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    return *reinterpret_cast<const F*>(smem + off);
-}
-
 template <int DK, int C, bool F32M, int NW, int SPW>
 __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
     using L = Lay<DK, C, F32M>;
     using SM = StateSmem<DK, C, F32M, NW, SPW>;
     using TM = typename L::TM;
     using F = typename FragOf<TM>::type;
-    constexpr int RB = L::RB, CB = L::CB, KSD = L::KSD, KSC = L::KSC;
+    constexpr int RB = L::RB, CB = L::CB, KSD = L::KSD, KSC = L::KSC, UPR = L::UPR;
     constexpr int NSL = SM::NSL;
     constexpr uint32_t FB = sizeof(F);   // bytes of one lane's fragment
 
@@ -868,10 +1115,10 @@ __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
     long bos, eos;
     int cs, ce;
     if (p.map.cu == nullptr) {
-        bos = (long)s * p.map.T;
-        eos = bos + p.map.T;
-        cs = s * p.map.NC;
-        ce = cs + p.map.NC;
+        bos = (long)s * p.map.T + (long)p.map.c0 * C;
+        eos = (long)(s + 1) * p.map.T;
+        cs = s * p.map.NC + p.map.c0;
+        ce = s * p.map.NC + p.map.c1;
     } else {
         bos = p.map.cu[s];
         eos = p.map.cu[s + 1];
@@ -964,14 +1211,14 @@ __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
             }
         }
 
-        // ---- U~ = T V ;  U = U~ - W S ;  O = (Gamma o Q) S
+        // ---- U = U~ - W S ;  O = (Gamma o Q) S
         f32x4 u[SPW][RB], ov[SPW][RB];
         {
-            f32x4 tv[SPW][RB], wsum[SPW][RB], osum[SPW][RB];
+            f32x4 wsum[SPW][RB], osum[SPW][RB];
 #pragma unroll
             for (int j = 0; j < SPW; ++j)
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) { tv[j][rb] = zero4(); wsum[j][rb] = zero4(); osum[j][rb] = zero4(); }
+                for (int rb = 0; rb < RB; ++rb) { wsum[j][rb] = zero4(); osum[j][rb] = zero4(); }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -984,30 +1231,25 @@ __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
                         osum[j][rb] = mma(qa, sf[j][ks], osum[j][rb]);
                     }
                 }
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) {
-                    if (ks > rb / 2) continue;
-                    const F ta = frag(L::TT_OFF, rb * KSC + ks);
-#pragma unroll
-                    for (int j = 0; j < SPW; ++j)
-                        tv[j][rb] = mma(ta, lds_ld<F>(bo + (uint32_t)L::BYTES + (uint32_t)((w * SPW + j) * L::VSL) +
-                                                      (uint32_t)ks * 64 * FB + lfr),
-                                        tv[j][rb]);
-                }
             }
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
-                float invTV = 1.f, invWS = 1.f, invQS = 1.f;
-                if constexpr (!F32M) {
-                    invTV = scl(SC_INV + SC_T) * lds_ld<float>(bo + (uint32_t)L::SV_OFF + 4 * (128 + col[j]));
-                    invWS = scl(SC_INV + SC_W) * iS[j];
-                    invQS = scl(SC_INV + SC_Q) * iS[j];
+                const uint32_t ub = bo + (uint32_t)L::BYTES + (uint32_t)((w * SPW + j) * L::USL);
+                const float iUc = lds_ld<float>(bo + (uint32_t)L::SU_OFF + 4 * (uint32_t)col[j]);
+                const float invWS = F32M ? 1.f : scl(SC_INV + SC_W) * iS[j];
+                const float invQS = F32M ? 1.f : scl(SC_INV + SC_Q) * iS[j];
+#pragma unroll
+                for (int rb = 0; rb < RB; rb += UPR) {
+                    typedef TM vu __attribute__((ext_vector_type(4 * UPR)));
+                    const vu ut = lds_ld<vu>(ub + (uint32_t)L::u_off(rb, lane));
+#pragma unroll
+                    for (int r2 = 0; r2 < UPR; ++r2)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            u[j][rb + r2][e] = (float)ut[4 * r2 + e] * iUc - wsum[j][rb + r2][e] * invWS;
                 }
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    u[j][rb] = tv[j][rb] * invTV - wsum[j][rb] * invWS;
-                    ov[j][rb] = osum[j][rb] * invQS;
-                }
+                for (int rb = 0; rb < RB; ++rb) ov[j][rb] = osum[j][rb] * invQS;
             }
         }
 
@@ -1110,12 +1352,254 @@ __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
     }
 }
 
+// ------------------------------------------------------------------ state kernel, two waves per slice
+//
+// For 64-token chunks with bf16 inputs, each 16-column slice is shared by a
+// pair of waves: wave hf of the pair keeps state rows (channels)
+// 64 hf .. 64 hf + 63 (for dk = 128) and produces the outputs of token rows
+// 32 hf .. 32 hf + 31. Per chunk the pair trades fp16 fragments through LDS:
+// the halves of S (B operand over channels) before W S and (Gamma o Q) S, and
+// the halves of U (B operand over tokens) before P U and K_end^T U. Each wave
+// then reads half of the W, Gamma o Q and K_end^T fragments, which halves the
+// LDS traffic per wave -- the limit of the one-wave form. Fragments keep one
+// power-of-two scale per column and per half; partial products over the two
+// halves go to separate accumulators and are combined in fp32.
+
+template <int DK, int C, int NP>
+struct PairSmem {
+    using L = Lay<DK, C, false>;
+    static constexpr int KH = L::KSD / 2;   // channel K steps per half
+    static constexpr size_t UBYTES = ((size_t)NP * L::USL + 1023) / 1024 * 1024;
+    static constexpr size_t BUF = L::BYTES + UBYTES;
+    // per-slice exchange area
+    static constexpr size_t X_S = 0;                                 // S halves [2][KH] fragment tiles
+    static constexpr size_t X_U = X_S + (size_t)2 * KH * 1024;       // U halves [2] fragment tiles
+    static constexpr size_t X_SI = X_U + 2 * 1024;                   // inverse S scales [2][16]
+    static constexpr size_t X_UI = X_SI + 2 * 16 * 4;                // inverse U scales [2][16]
+    static constexpr size_t X_F = X_UI + 2 * 16 * 4;                 // U-ready flags [2] (chunk index)
+    static constexpr size_t XSL = X_F + 16;
+    static constexpr size_t XCH = 2 * BUF;
+    static constexpr size_t BYTES = XCH + (size_t)NP * XSL;
+};
+
+template <int DK, int C, int NP>
+__global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams p) {
+    using L = Lay<DK, C, false>;
+    using SM = PairSmem<DK, C, NP>;
+    using F = f16x8;
+    static_assert(C == 64 && DK >= 64, "pair form: 64-token chunks, dk >= 64");
+    constexpr int KSD = L::KSD, KSC = L::KSC, KH = SM::KH;
+    constexpr int CH = L::CB / 2;          // 16-row state tiles per wave
+    constexpr int NCW = 2 * NP;            // compute waves
+
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int sg = item % p.NSG;
+    const int hs = item / p.NSG;
+    const int H = p.H, DV = p.DV;
+    const int h = hs % H, s = hs / H;
+    const int lane = threadIdx.x % 64;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);   // wave index, uniform
+    const bool copier = wv >= NCW;
+    const int w = copier ? wv - NCW : wv;
+    const int sl = w / 2, hf = w % 2;      // slice in the workgroup, half of the pair
+    const int li = lane % 16, lg = lane / 16;
+    const int col = 16 * (sg * NP + sl) + li;
+
+    long bos, eos;
+    int cs, ce;
+    if (p.map.cu == nullptr) {
+        bos = (long)s * p.map.T + (long)p.map.c0 * C;
+        eos = (long)(s + 1) * p.map.T;
+        cs = s * p.map.NC + p.map.c0;
+        ce = s * p.map.NC + p.map.c1;
+    } else {
+        bos = p.map.cu[s];
+        eos = p.map.cu[s + 1];
+        cs = p.map.cstart[s];
+        ce = p.map.cstart[s + 1];
+    }
+
+    const uint32_t xs = (uint32_t)(SM::XCH + (size_t)sl * SM::XSL);   // this slice's exchange area
+    const uint32_t lfr = (uint32_t)lane * 16;
+
+    // own state rows 16 (CH hf + c) + 4 lg + e of column col
+    f32x4 S[CH];
+    const size_t sbase = ((size_t)s * H + h) * DK * DV;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[c][e] = (p.S0 && !copier) ? p.S0[sbase + (size_t)(16 * (CH * hf + c) + 4 * lg + e) * DV + col] : 0.f;
+
+    // own half of S as fragments (channel steps KH hf + k), and its inverse scale
+    F sfo[KH];
+    float iSo = 1.f;
+    auto make_s_frags = [&]() {
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[c][e]));
+        m = colmax4(m);
+        const float sc = pow2_scale_for(m);
+        iSo = pow2_inv_scale_for(m);
+#pragma unroll
+        for (int k = 0; k < KH; ++k) {
+            sfo[k] = to_f16x8(dtiles_to_frag(S[2 * k], S[2 * k + 1]), sc);
+            lds_st<F>(xs + (uint32_t)(SM::X_S + (size_t)(hf * KH + k) * 1024) + lfr, sfo[k]);
+        }
+        if (lg == 0) lds_st<float>(xs + (uint32_t)SM::X_SI + 4 * (16 * hf + li), iSo);
+    };
+
+    auto gblock = [&](int cg) { return p.ws + ((size_t)cg * H + h) * p.blk_bytes; };
+    const uint32_t orow = (uint32_t)H * DV * 4;
+
+    if (copier) {
+        if (cs < ce) {
+            stage_chunk<DK, C, false, NP, NP>(0, gblock(cs), p.blk_bytes, sg, w, lane);
+            wait_vm_all();
+        }
+    } else {
+        make_s_frags();
+        if (lane == 0) lds_st<int>(xs + (uint32_t)SM::X_F + 4 * hf, -1);
+    }
+    __syncthreads();
+
+    for (int cg = cs; cg < ce; ++cg) {
+        if (copier) {
+            // chunk cg+1 into the free buffer; the copy has the whole
+            // iteration and must land before the barrier that ends it
+            if (cg + 1 < ce)
+                stage_chunk<DK, C, false, NP, NP>((uint32_t)(((cg + 1 - cs) % 2) * SM::BUF), gblock(cg + 1), p.blk_bytes,
+                                                  sg, w, lane);
+            wait_vm_all();
+            __syncthreads();
+            continue;
+        }
+        const long t0 = bos + (long)(cg - cs) * C;
+        const int n = (int)min((long)C, eos - t0);
+        const uint32_t bo = (uint32_t)(((cg - cs) % 2) * SM::BUF);
+        auto frag = [&](size_t off, int tile) { return lds_ld<F>(bo + (uint32_t)off + (uint32_t)tile * 1024 + lfr); };
+        auto scl = [&](int i) { return lds_ld<float>(bo + (uint32_t)L::SC_OFF + 4 * i); };
+        const float iW = scl(SC_INV + SC_W), iQ = scl(SC_INV + SC_Q), iK = scl(SC_INV + SC_K), iP = scl(SC_INV + SC_P);
+
+        // ---- the other half of S
+        F sfx[KH];
+#pragma unroll
+        for (int k = 0; k < KH; ++k) sfx[k] = lds_ld<F>(xs + (uint32_t)(SM::X_S + (size_t)((1 - hf) * KH + k) * 1024) + lfr);
+        const float iSx = lds_ld<float>(xs + (uint32_t)SM::X_SI + 4 * (16 * (1 - hf) + li));
+
+        // ---- own token rows rb = 2 hf + r:  U = U~ - W S,  O = (Gamma o Q) S
+        f32x4 u[2], ov[2];
+        {
+            const float iUc = lds_ld<float>(bo + (uint32_t)L::SU_OFF + 4 * (uint32_t)col);
+            const F ut = lds_ld<F>(bo + (uint32_t)L::BYTES + (uint32_t)(sl * L::USL) + (uint32_t)L::u_off(2 * hf, lane));
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int rb = 2 * hf + r;
+                f32x4 wo = zero4(), wx = zero4(), qo = zero4(), qx = zero4();
+#pragma unroll
+                for (int k = 0; k < KH; ++k) {
+                    const int ko = hf * KH + k, kx = (1 - hf) * KH + k;
+                    wo = mma(frag(L::W_OFF, rb * KSD + ko), sfo[k], wo);
+                    wx = mma(frag(L::W_OFF, rb * KSD + kx), sfx[k], wx);
+                    qo = mma(frag(L::QG_OFF, rb * KSD + ko), sfo[k], qo);
+                    qx = mma(frag(L::QG_OFF, rb * KSD + kx), sfx[k], qx);
+                }
+                const float a1 = iW * iSo, a2 = iW * iSx, b1 = iQ * iSo, b2 = iQ * iSx;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    u[r][e] = (float)ut[4 * r + e] * iUc - (wo[e] * a1 + wx[e] * a2);
+                    ov[r][e] = qo[e] * b1 + qx[e] * b2;
+                }
+            }
+        }
+
+        // ---- own half of U (token step hf) as a fragment; trade halves
+        F ufo;
+        float iUo;
+        {
+            float m = 0.f;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(u[r][e]));
+            m = colmax4(m);
+            const float sc = pow2_scale_for(m);
+            iUo = pow2_inv_scale_for(m);
+            ufo = to_f16x8(dtiles_to_frag(u[0], u[1]), sc);
+            lds_st<F>(xs + (uint32_t)(SM::X_U + (size_t)hf * 1024) + lfr, ufo);
+            if (lg == 0) lds_st<float>(xs + (uint32_t)SM::X_UI + 4 * (16 * hf + li), iUo);
+        }
+        // hand-off inside the pair: the LDS operations of one wave complete in
+        // order, so the flag lands after the fragment; the wait is bounded
+        // (both waves are resident, and the partner posts every chunk)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) lds_st<int>(xs + (uint32_t)SM::X_F + 4 * hf, cg);
+        {
+            extern __shared__ __align__(16) unsigned char smem[];
+            typedef __attribute__((address_space(3))) const volatile int lds_flag_t;
+            lds_flag_t* flag = (lds_flag_t*)(smem + xs + SM::X_F + 4 * (1 - hf));
+            for (int spin = 0; *flag != cg && spin < (1 << 24); ++spin) __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const F ufx = lds_ld<F>(xs + (uint32_t)(SM::X_U + (size_t)(1 - hf) * 1024) + lfr);
+        const float iUx = lds_ld<float>(xs + (uint32_t)SM::X_UI + 4 * (16 * (1 - hf) + li));
+
+        // ---- O += P U for own rows (strictly lower part on MFMA, diagonal in
+        // fp32); rows past the chunk end fall outside the store descriptor
+        {
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
+            const uint32_t ovoff = (uint32_t)(4 * lg) * orow + (uint32_t)col * 4;
+            const float po = iP * iUo, px = iP * iUx;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int rb = 2 * hf + r;
+                // token step hf is this wave's own U half; step 0 for hf = 1 is the other's
+                f32x4 pu_o = mma(frag(L::PS_OFF, rb * KSC + hf), ufo, zero4());
+                f32x4 pu_x = zero4();
+                if (hf == 1) pu_x = mma(frag(L::PS_OFF, rb * KSC + 0), ufx, pu_x);
+                const f32x4 pd4 = lds_ld<f32x4>(bo + (uint32_t)L::PD_OFF + 4 * (16 * rb + 4 * lg));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ovv = ov[r][e] + pu_o[e] * po + pu_x[e] * px + pd4[e] * u[r][e];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ovv), ro, ovoff, (16 * rb + e) * orow, 0);
+                }
+            }
+        }
+
+        // ---- own state rows: S <- Diag(gamma_last) S + K_end^T U
+        {
+            const float ko = iK * iUo, kx = iK * iUx;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int cb = CH * hf + c;
+                const f32x4 k_o = mma(frag(L::KE_OFF, cb * KSC + hf), ufo, zero4());
+                const f32x4 k_x = mma(frag(L::KE_OFF, cb * KSC + (1 - hf)), ufx, zero4());
+                const f32x4 g4 = lds_ld<f32x4>(bo + (uint32_t)L::GN_OFF + 4 * (16 * cb + 4 * lg));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[c][e] = S[c][e] * g4[e] + (k_o[e] * ko + k_x[e] * kx);
+            }
+        }
+        make_s_frags();
+        __syncthreads();
+    }
+
+    if (!copier && p.S_T) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.S_T[sbase + (size_t)(16 * (CH * hf + c) + 4 * lg + e) * DV + col] = S[c][e];
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 template <int DK, int C>
 static size_t block_bytes_t(int dv, bool bf16) {
-    return bf16 ? Lay<DK, C, false>::BYTES + (size_t)(dv / 16) * Lay<DK, C, false>::VSL
-                : Lay<DK, C, true>::BYTES + (size_t)(dv / 16) * Lay<DK, C, true>::VSL;
+    return bf16 ? Lay<DK, C, false>::BYTES + (size_t)(dv / 16) * Lay<DK, C, false>::USL
+                : Lay<DK, C, true>::BYTES + (size_t)(dv / 16) * Lay<DK, C, true>::USL;
 }
 
 template <int DK>
@@ -1143,9 +1627,55 @@ long chunk_count_bound(int B, int T, int chunk, bool varlen, int N) {
 
 static size_t index_bytes(bool varlen, int N) { return varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0; }
 
+// Chunks per time segment. Long equal-length sequences run as a series of
+// (prep, state) launches over consecutive chunk ranges, so that the state
+// kernel reads each segment's blocks while they are still in the last-level
+// cache; the state carries from one segment to the next through the
+// workspace.
+constexpr int MAX_SEG = 16;
+static int segment_chunks(int NC, bool varlen) {
+    if (varlen || NC < 32) return NC;
+    int seg = (NC + 7) / 8;                                // about eight segments (measured best of 1-16)
+    if (seg < 16) seg = 16;
+    if (seg < (NC + MAX_SEG - 1) / MAX_SEG) seg = (NC + MAX_SEG - 1) / MAX_SEG;
+    return seg;
+}
+
+// A second stream per device for the prep kernels of the segmented path, and
+// events to order it against the caller's stream (fork at the start of a
+// call, one event per segment). Created on first use, default priority.
+struct SegStreams {
+    hipStream_t aux = nullptr;
+    hipEvent_t fork = nullptr;
+    hipEvent_t seg[MAX_SEG] = {};
+};
+static hipError_t seg_streams(SegStreams*& out) {
+    static std::mutex mu;
+    static SegStreams per_dev[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    SegStreams& r = per_dev[dev];
+    if (r.aux == nullptr) {
+        hipStream_t st;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+        e = hipEventCreateWithFlags(&r.fork, hipEventDisableTiming);
+        for (int i = 0; i < MAX_SEG && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&r.seg[i], hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+        r.aux = st;
+    }
+    out = &r;
+    return hipSuccess;
+}
+
 size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, bool varlen, int N, bool bf16) {
+    const int NC = (T + chunk - 1) / chunk;
+    const size_t carry = segment_chunks(NC, varlen) < NC ? (size_t)B * H * dk * dv * 4 : 0;
     return index_bytes(varlen, N) +
-           (size_t)chunk_count_bound(B, T, chunk, varlen, N) * H * chunk_block_bytes(dk, dv, chunk, bf16);
+           (size_t)chunk_count_bound(B, T, chunk, varlen, N) * H * chunk_block_bytes(dk, dv, chunk, bf16) + carry;
 }
 
 template <class K>
@@ -1157,7 +1687,7 @@ static hipError_t allow_lds(K kern, size_t bytes) {
 template <class TIn, int DK, int C, bool SG>
 static hipError_t launch_prep_t(const ChunkArgs& a, const ChunkMap& map, unsigned char* blocks, long nchunks) {
     constexpr bool F32M = std::is_same<TIn, float>::value;
-    using SM = PrepSmem<DK, C, F32M>;
+    using SM = PrepLds<TIn, DK, C, F32M>;
     static_assert(SM::BYTES <= 160 * 1024, "prep LDS");
     auto kern = chunk_prep_kernel<TIn, DK, C, SG, F32M>;
     hipError_t e = allow_lds(kern, SM::BYTES);
@@ -1183,11 +1713,32 @@ static hipError_t launch_state_w(const ChunkArgs& a, const ChunkMap& map, const 
     return hipGetLastError();
 }
 
-// Slices per workgroup: four compute waves of one slice each when the value
-// width allows (more waves in flight shorten the sequential chunk loop more
-// than sharing fragment reads between slices of one wave does).
+template <int DK, int C, int NP>
+static hipError_t launch_state_pair(const ChunkArgs& a, const ChunkMap& map, const unsigned char* blocks) {
+    using SM = PairSmem<DK, C, NP>;
+    static_assert(SM::BYTES <= 160 * 1024, "pair state LDS");
+    auto kern = chunk_state_pair_kernel<DK, C, NP>;
+    hipError_t e = allow_lds(kern, SM::BYTES);
+    if (e != hipSuccess) return e;
+    const int nsg = a.dv / 16 / NP;
+    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(DK, a.dv, C, true), map, a.H, a.dv, nsg};
+    const long grid = (long)nsg * a.H * a.N;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(192 * NP), SM::BYTES, a.stream, sp);
+    return hipGetLastError();
+}
+
+// bf16 inputs, 64-token chunks, dk >= 64: two waves per slice, four slices
+// per workgroup. Otherwise one wave per slice: four compute waves of one
+// slice each when the value width allows (more waves in flight shorten the
+// sequential chunk loop more than sharing fragment reads between slices of
+// one wave does).
 template <class TIn, int DK, int C>
 static hipError_t launch_state_t(const ChunkArgs& a, const ChunkMap& map, const unsigned char* blocks) {
+    if constexpr (std::is_same<TIn, uint16_t>::value && C == 64 && DK >= 64) {
+        if (a.dv >= 64) return launch_state_pair<DK, C, 4>(a, map, blocks);
+        if (a.dv >= 32) return launch_state_pair<DK, C, 2>(a, map, blocks);
+        return launch_state_pair<DK, C, 1>(a, map, blocks);
+    }
     if (a.dv >= 64) return launch_state_w<TIn, DK, C, 4, 1>(a, map, blocks);
     if (a.dv >= 32) return launch_state_w<TIn, DK, C, 2, 1>(a, map, blocks);
     return launch_state_w<TIn, DK, C, 1, 1>(a, map, blocks);
@@ -1198,20 +1749,51 @@ static hipError_t launch_pair(const ChunkArgs& a) {
     const bool varlen = a.cu_seqlens != nullptr;
     unsigned char* ws = (unsigned char*)a.workspace;
     const size_t ib = index_bytes(varlen, a.N);
-    ChunkMap map{a.cu_seqlens, varlen ? (const int32_t*)ws : nullptr, a.T, a.N, (a.T + C - 1) / C};
+    const int NC = (a.T + C - 1) / C;
+    ChunkMap map{a.cu_seqlens, varlen ? (const int32_t*)ws : nullptr, a.T, a.N, NC, 0, NC};
     unsigned char* blocks = ws + ib;
+    auto prep = [&](const ChunkMap& m, long nch) -> hipError_t {
+        if (nch <= 0) return hipSuccess;
+        return a.scalar_gate ? launch_prep_t<TIn, DK, C, true>(a, m, blocks, nch)
+                             : launch_prep_t<TIn, DK, C, false>(a, m, blocks, nch);
+    };
+    const int seg = segment_chunks(NC, varlen);
+    if (a.stages == 3 && seg < NC) {
+        // prep of segment k+1 (second stream) overlaps the state walk of
+        // segment k (caller's stream)
+        SegStreams* ss = nullptr;
+        hipError_t e = seg_streams(ss);
+        if (e != hipSuccess) return e;
+        float* carry = reinterpret_cast<float*>(blocks + (size_t)chunk_count_bound(a.B, a.T, C, false, a.N) * a.H *
+                                                             chunk_block_bytes(DK, a.dv, C, !std::is_same<TIn, float>::value));
+        e = hipEventRecord(ss->fork, a.stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(ss->aux, ss->fork, 0);
+        ChunkArgs ap = a;
+        ap.stream = ss->aux;
+        for (int k = 0, c0 = 0; e == hipSuccess && c0 < NC; ++k, c0 += seg) {
+            ChunkMap m = map;
+            m.c0 = c0;
+            m.c1 = c0 + seg < NC ? c0 + seg : NC;
+            e = ap.scalar_gate ? launch_prep_t<TIn, DK, C, true>(ap, m, blocks, (long)a.N * (m.c1 - m.c0))
+                               : launch_prep_t<TIn, DK, C, false>(ap, m, blocks, (long)a.N * (m.c1 - m.c0));
+            if (e == hipSuccess) e = hipEventRecord(ss->seg[k], ss->aux);
+            if (e == hipSuccess) e = hipStreamWaitEvent(a.stream, ss->seg[k], 0);
+            if (e != hipSuccess) break;
+            ChunkArgs as = a;
+            as.S0 = c0 == 0 ? a.S0 : carry;
+            as.S_T = m.c1 == NC ? a.S_T : carry;
+            e = launch_state_t<TIn, DK, C>(as, m, blocks);
+        }
+        return e;
+    }
     if (a.stages & 1) {
         if (varlen) {
             hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, (int32_t*)ws, a.N, C);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        const long nch = chunk_count_bound(a.B, a.T, C, varlen, a.N);
-        if (nch > 0) {
-            hipError_t e = a.scalar_gate ? launch_prep_t<TIn, DK, C, true>(a, map, blocks, nch)
-                                         : launch_prep_t<TIn, DK, C, false>(a, map, blocks, nch);
-            if (e != hipSuccess) return e;
-        }
+        hipError_t e = prep(map, chunk_count_bound(a.B, a.T, C, varlen, a.N));
+        if (e != hipSuccess) return e;
     }
     if (a.stages & 2) return launch_state_t<TIn, DK, C>(a, map, blocks);
     return hipSuccess;

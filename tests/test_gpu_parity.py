@@ -261,6 +261,35 @@ def test_scalar_gate_equals_broadcast_channel_gate(kda):
     assert err(o2, o1.double().numpy()) < 1e-5 and err(S2, S1.double().numpy()) < 1e-5
 
 
+@pytest.mark.parametrize("dk,dv,T", [(128, 64, 300), (64, 128, 129), (128, 32, 65)])
+def test_pair_state_path(kda, dk, dv, T):
+    """64-token chunks with bf16 inputs and dk >= 64 take the two-waves-per-slice
+    state kernel; nonzero initial state, ragged tail, each value width."""
+    w = inputs.make_forward("pair", B=2, H=3, T=T, dk=dk, dv=dv, chunk=64, dtype=torch.bfloat16, gate="ckda",
+                            s0_std=0.2, seed=dk + dv + T)
+    check(kda, w)
+
+
+def test_segmented_equals_single_pass(kda):
+    """Long sequences run as time segments (prep on a second stream, state
+    carried between segments); the result equals the single prep + state pass
+    bit for bit, and the oracle within the bf16 bar."""
+    w = inputs.make_forward("seg", B=2, H=2, T=2100, dk=128, dv=128, chunk=64, dtype=torch.bfloat16, gate="ckda",
+                            s0_std=0.2, seed=21)
+    q, k, v, g, b, s0, _ = to_dev(w)
+    o1, S1 = kda.chunk_fwd(q, k, v, g, b, S0=s0, chunk=64)
+    wsb = kda.workspace_bytes(w.B, w.H, w.T, 128, 128, 64)
+    ws = torch.empty(wsb, device="cuda", dtype=torch.uint8)
+    o2 = torch.empty_like(o1)
+    S2 = torch.empty_like(S1)
+    kda.chunk_fwd(q, k, v, g, b, S0=s0, chunk=64, out=o2, S_T=S2, workspace=ws, stage=kda.STAGE_PREP)
+    kda.chunk_fwd(q, k, v, g, b, S0=s0, chunk=64, out=o2, S_T=S2, workspace=ws, stage=kda.STAGE_STATE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    ro, rS = ref_fwd(w)
+    assert err(o1, ro) <= 2e-2 and err(S1, rS) <= 2e-2
+
+
 def test_deterministic(kda):
     w = inputs.make_forward("det", B=1, H=4, T=257, dk=128, dv=128, dtype=torch.bfloat16, gate="ckda", seed=14)
     o1, S1 = gpu_fwd(kda, w)
