@@ -47,6 +47,27 @@ def decode_bytes_per_head_step(dk: int, dv: int, in_bytes: int = 2) -> int:
     return 8 * dk * dv + in_bytes * (3 * dk + dv + 1) + 4 * dv
 
 
+def measured_traffic():
+    """HBM bytes per forward call and per decode step from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None for each when the
+    kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_ckda_fwd_decode.txt")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    for rel, digest in rec.get("sources_sha256", {}).items():
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None, None
+        except OSError:
+            return None, None
+    return rec.get("forward_bytes_per_call"), rec.get("decode_bytes_per_step")
+
+
 def time_region(fn, iters: int, stream):
     import torch
     torch.cuda.synchronize()
@@ -112,6 +133,7 @@ def main(argv=None) -> int:
     ms_state = time_region(lambda i: fwd(0, kda.STAGE_STATE), args.steps, stream)
     print("[bench] prep %.3f ms, state %.3f ms" % (ms_prep, ms_state), file=sys.stderr, flush=True)
 
+    traffic_fwd, traffic_dec = measured_traffic()
     head_tokens = tokens * H
     alg_bytes = head_tokens * fwd_bytes_per_head_token(dk, dv, False) + B * H * dk * dv * 4
     alg_flops = head_tokens * fwd_flops_per_head_token(dk, dv)
@@ -123,8 +145,8 @@ def main(argv=None) -> int:
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-        "traffic": None,
-        "kernel": "kda_chunk_fwd: chunk_prep_kernel + chunk_state_kernel (one call)",
+        "traffic": traffic_fwd,
+        "kernel": "kda_chunk_fwd: chunk_prep_kernel + chunk_state_pair_kernel, 8 time segments on two streams (one call)",
         "bytes_per_launch": alg_bytes,
         "launch_ms": round(ms, 4),
         "mfma_frac_algorithmic": round(alg_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -158,7 +180,7 @@ def main(argv=None) -> int:
             "ms_per_step": round(per, 4),
             "tokens_per_s": round(dw.N / (per * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_dec,
                          "kernel": "decode_step_kernel", "bytes_per_launch": dbytes},
         }
         print("[bench] decode %.4f ms/step, %.1f GB/s" % (per, gbs), file=sys.stderr, flush=True)

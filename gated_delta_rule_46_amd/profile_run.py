@@ -1,0 +1,66 @@
+"""A short, fixed workload to run under rocprofv3.
+
+    python -m gated_delta_rule_46_amd.profile_run [--fwd 3] [--decode 8] [--copy-mib 256]
+
+Runs, on cuda:0 and with seeded synthetic inputs: --fwd forward calls on the
+Complex KDA workload (B=2, H=16, T=8192, d=128, bf16, chunk 64), --decode
+decode steps on the decode workload (N=256, H=32, d=128, fp32 state in place),
+and --copy-mib MiB of plain device-to-device copy (one read and one write of
+that many bytes per call, three calls), whose counter readings calibrate
+FETCH_SIZE and WRITE_SIZE against a known byte count.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--fwd", type=int, default=3)
+    ap.add_argument("--decode", type=int, default=8)
+    ap.add_argument("--copy-mib", type=int, default=256)
+    args = ap.parse_args(argv)
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import torch
+    from gated_delta_rule_46_amd import inputs, kda
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    kda.library()
+    if args.fwd > 0:
+        w = inputs.ckda_fwd(seed=0)
+        q, k, v, g, b = (t.to(dev) for t in (w.q, w.k, w.v, w.gate, w.beta))
+        ws = torch.empty(kda.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk), device=dev, dtype=torch.uint8)
+        o = torch.empty((w.B, w.T, w.H, w.dv), device=dev, dtype=torch.float32)
+        ST = torch.empty((w.B, w.H, w.dk, w.dv), device=dev, dtype=torch.float32)
+        for _ in range(args.fwd):
+            kda.chunk_fwd(q, k, v, g, b, chunk=w.chunk, gate_kind=0, out=o, S_T=ST, workspace=ws)
+        torch.cuda.synchronize()
+        print("forward calls: %d" % args.fwd, flush=True)
+        del q, k, v, g, b, ws, o, ST
+    if args.decode > 0:
+        dw = inputs.ckda_decode(n_steps=min(args.decode, 16))
+        S = dw.S.to(dev)
+        steps = [tuple(st[x].to(dev) for x in ("q", "k", "v", "gate", "beta")) for st in dw.steps]
+        od = torch.empty((dw.N, dw.H, dw.dv), device=dev, dtype=torch.float32)
+        for i in range(args.decode):
+            qd, kd, vd, gd, bd = steps[i % len(steps)]
+            kda.decode_step(qd, kd, vd, gd, bd, S, out=od, gate_kind=0)
+        torch.cuda.synchronize()
+        print("decode steps: %d" % args.decode, flush=True)
+        del S, steps, od
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 20, device=dev, dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy: 3 x %d MiB" % args.copy_mib, flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
