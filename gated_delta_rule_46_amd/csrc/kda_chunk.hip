@@ -271,19 +271,12 @@ struct Gx {
         for (int j = 0; j < CPL; ++j) v[t][j] = x;
     }
     __device__ __forceinline__ void fill_from(const float* p, int t) { fill(t, *p); }
-    __device__ __forceinline__ void opaque() {}
 };
 template <int CPL>
 struct Gx<uint16_t, CPL> {
     uint32_t w[16];   // CPL == 2: channel 0 in the low half; CPL == 1: the low half
-    // Unpacked at each use, in place (volatile: not merged with, or hoisted
-    // ahead of, the same unpack in another phase, which would keep 96 fp32
-    // copies live next to the 48 packed words).
     __device__ __forceinline__ float get(int t, int j) const {
-        uint32_t r;
-        if (CPL == 2 && j) asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w[t]));
-        else asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w[t]));
-        return __uint_as_float(r);
+        return __uint_as_float(j ? (w[t] & 0xffff0000u) : (w[t] << 16));
     }
     __device__ __forceinline__ void load(const uint16_t* p, int t) {
         if constexpr (CPL == 2) w[t] = *reinterpret_cast<const uint32_t*>(p);
@@ -297,11 +290,36 @@ struct Gx<uint16_t, CPL> {
         const uint32_t b = *p;
         w[t] = CPL == 2 ? (b | (b << 16)) : b;
     }
-    // Mark the packed words as rewritten (no instruction), so that unpacked
-    // copies are not kept live from one phase to the next.
+};
+
+// The same values once the operand scales are known: k * sK and q * sQ (and
+// alpha unscaled). bf16 inputs go to fp16 pairs -- exact, a bf16 value times a
+// power of two lands in fp16's normal range -- which mixed-precision FMAs
+// read directly; fp32 inputs stay fp32.
+template <class TIn, int CPL>
+struct Hx {
+    float v[16][CPL];
+    __device__ __forceinline__ float get(int t, int j) const { return v[t][j]; }
+    __device__ __forceinline__ float mul(int t, int j, float f) const { return v[t][j] * f; }
+    __device__ __forceinline__ void set(int t, int j, float x) { v[t][j] = x; }
+    __device__ __forceinline__ void opaque() {}
+};
+template <int CPL>
+struct Hx<uint16_t, CPL> {
+    typedef _Float16 hv __attribute__((ext_vector_type(2)));
+    hv v[16];   // CPL == 1 uses the first half
+    __device__ __forceinline__ float get(int t, int j) const { return (float)v[t][j]; }
+    // value * f in one mixed-precision FMA (the fp16 operand read in place);
+    // the +0 addend only changes the sign of a zero product, which no later
+    // sum or product here can see
+    __device__ __forceinline__ float mul(int t, int j, float f) const { return __builtin_fmaf((float)v[t][j], f, 0.f); }
+    __device__ __forceinline__ void set(int t, int j, float x) { v[t][j] = (_Float16)x; }
+    // Mark the pairs as rewritten (no instruction): conversions to fp32 are
+    // then redone inside each phase, folded into mixed FMAs, rather than
+    // kept live across phases.
     __device__ __forceinline__ void opaque() {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) asm volatile("" : "+v"(w[t]));
+        for (int t = 0; t < 16; ++t) asm volatile("" : "+v"(v[t]));
     }
 };
 
@@ -373,7 +391,7 @@ __device__ __forceinline__ bool sep_at(int r, int j, int hh) {
 }
 
 template <class TIn, int DK, int C, bool SG, bool F32M>
-__global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
+__global__ void __launch_bounds__(256, F32M ? 1 : 3) chunk_prep_kernel(PrepParams p) {
     using L = Lay<DK, C, F32M>;
     using SM = PrepLds<TIn, DK, C, F32M>;
     using TM = typename L::TM;
@@ -475,7 +493,16 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
         sQ = pow2_scale_for(m2);
         iQ = pow2_inv_scale_for(m2);
     }
-    const float rQK = sQ * iK;   // Q-side over K-side scale (a power of two)
+    // scaled operand values for every later phase: k * sK, q * sQ, alpha
+    Hx<TIn, CPL> hk, hq, ha;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            hk.set(t, j, kk.get(t, j) * sK);
+            hq.set(t, j, qq.get(t, j) * sQ);
+            ha.set(t, j, aa.get(t, j));
+        }
 
     // ---- value fragments (B operand over tokens), kept in registers until
     // U~ = T V: wave w owns value slices w and w + 4, one scale per column
@@ -512,15 +539,15 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
     __syncthreads();
 
     // ---- Gamma o Q (rows tokens), K_end^T (rows channels), gamma_last
-    kk.opaque();
-    qq.opaque();
-    aa.opaque();
+    hk.opaque();
+    hq.opaque();
+    ha.opaque();
     if (gate_lane) {
         float pre[CPL], suf[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            pre[j] = sQ;
-            suf[j] = sK;
+            pre[j] = 1.f;
+            suf[j] = 1.f;
             float all = 1.f;
 #pragma unroll
             for (int bb = 0; bb < NBK; ++bb) {
@@ -536,8 +563,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
             float qg[2];
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                pre[j] *= aa.get(t, j);
-                qg[j] = qq.get(t, j) * pre[j];
+                pre[j] = ha.mul(t, j, pre[j]);
+                qg[j] = hq.mul(t, j, pre[j]);
             }
             st_vals<TM, CPL>(SM::QGT + stage_off<TM, KSD>(16 * b + t, c0), qg);
             if constexpr (DK == 16) {
@@ -551,8 +578,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
             float r = suf[j];
 #pragma unroll
             for (int t = 15; t >= 0; --t) {
-                ke[t] = kk.get(t, j) * r;
-                r *= aa.get(t, j);
+                ke[t] = hk.mul(t, j, r);
+                r = ha.mul(t, j, r);
             }
 #pragma unroll
             for (int u = 0; u < 16; u += 4) {
@@ -579,16 +606,16 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
 #pragma unroll
     for (int lev = 0; lev < NBL; ++lev) {
         const int hb = (C >> (lev + 1)) / 16;   // half width in blocks
-        kk.opaque();
-        qq.opaque();
-        aa.opaque();
+        hk.opaque();
+        hq.opaque();
+        ha.opaque();
         if (gate_lane) {
             const int gs = (b / (2 * hb)) * 2 * hb, midb = gs + hb;
             const bool right = b >= midb;
             float f[CPL];
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                f[j] = sK;
+                f[j] = 1.f;
                 if (right) {
                     for (int bb = midb; bb < b; ++bb) f[j] *= s_tot[bb * DK + c0 + j];
                 } else {
@@ -601,9 +628,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
                     float x[2], y[2];
 #pragma unroll
                     for (int j = 0; j < CPL; ++j) {
-                        f[j] *= aa.get(t, j);
-                        x[j] = kk.get(t, j) * f[j];
-                        y[j] = qq.get(t, j) * (f[j] * rQK);
+                        f[j] = ha.mul(t, j, f[j]);
+                        x[j] = hk.mul(t, j, f[j]);
+                        y[j] = hq.mul(t, j, f[j]);
                     }
                     st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
                     st_vals<TM, CPL>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0), y);
@@ -619,8 +646,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
                     float x[2];
 #pragma unroll
                     for (int j = 0; j < CPL; ++j) {
-                        x[j] = kk.get(t, j) * f[j];
-                        f[j] *= aa.get(t, j);
+                        x[j] = hk.mul(t, j, f[j]);
+                        f[j] = ha.mul(t, j, f[j]);
                     }
                     st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
                     if constexpr (DK == 16) {
@@ -663,24 +690,24 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
 #pragma unroll
         for (int lev = 0; lev < 5; ++lev) {
             const int hh = lev < 4 ? (8 >> lev) : 0;
-            kk.opaque();
-            qq.opaque();
-            aa.opaque();
+            hk.opaque();
+            hq.opaque();
+            ha.opaque();
             if (lane < ACT) {
                 if (hh > 0) {
 #pragma unroll
                     for (int g0 = 0; g0 < 16; g0 += 2 * hh) {
                         float f[CPL];
 #pragma unroll
-                        for (int j = 0; j < CPL; ++j) f[j] = sK;
+                        for (int j = 0; j < CPL; ++j) f[j] = 1.f;
 #pragma unroll
                         for (int t = g0 + hh; t < g0 + 2 * hh; ++t) {
                             float x[2], y[2];
 #pragma unroll
                             for (int j = 0; j < CPL; ++j) {
-                                f[j] *= aa.get(t, j);
-                                x[j] = kk.get(t, j) * f[j];
-                                y[j] = qq.get(t, j) * (f[j] * rQK);
+                                f[j] = ha.mul(t, j, f[j]);
+                                x[j] = hk.mul(t, j, f[j]);
+                                y[j] = hq.mul(t, j, f[j]);
                             }
                             st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
                             st_vals<TM, CPL>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0), y);
@@ -691,14 +718,14 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
                             }
                         }
 #pragma unroll
-                        for (int j = 0; j < CPL; ++j) f[j] = sK;
+                        for (int j = 0; j < CPL; ++j) f[j] = 1.f;
 #pragma unroll
                         for (int t = g0 + hh - 1; t >= g0; --t) {
                             float x[2];
 #pragma unroll
                             for (int j = 0; j < CPL; ++j) {
-                                x[j] = kk.get(t, j) * f[j];
-                                f[j] *= aa.get(t, j);
+                                x[j] = hk.mul(t, j, f[j]);
+                                f[j] = ha.mul(t, j, f[j]);
                             }
                             st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
                             if constexpr (DK == 16) {
@@ -713,8 +740,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
                         float x[2], y[2];
 #pragma unroll
                         for (int j = 0; j < CPL; ++j) {
-                            x[j] = kk.get(t, j) * sK;
-                            y[j] = qq.get(t, j) * sQ;
+                            x[j] = hk.get(t, j);
+                            y[j] = hq.get(t, j);
                         }
                         st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
                         st_vals<TM, CPL>(SM::YT + stage_off<TM, KSD>(16 * b + t, c0), y);
@@ -893,18 +920,18 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrepParams p) {
     auto tfrag = [&](int rb, int s) { return lds_ld<F>(SM::TF + (uint32_t)((tf_index<KSC>(rb, s) * 64 + lane) * sizeof(F))); };
 
     // ---- (Gamma o K)^T tiles (rows channels, K over tokens) for W
-    kk.opaque();
-    aa.opaque();
+    hk.opaque();
+    ha.opaque();
     if (gate_lane) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            float r = sK;
+            float r = 1.f;
             for (int bb = 0; bb < b; ++bb) r *= s_tot[bb * DK + c0 + j];
             float gk[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                r *= aa.get(t, j);
-                gk[t] = kk.get(t, j) * r;
+                r = ha.mul(t, j, r);
+                gk[t] = hk.mul(t, j, r);
             }
 #pragma unroll
             for (int u = 0; u < 16; u += 4) {
@@ -1053,15 +1080,18 @@ struct StateSmem {
 // waves split the work.
 template <int DK, int C, bool F32M, int NW, int NSL>
 __device__ __forceinline__ void stage_chunk(uint32_t lds_off, const unsigned char* gblk, size_t blk_bytes, int sg, int w,
-                                            int lane) {
+                                            int lane, int rot = 0) {
     using L = Lay<DK, C, F32M>;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int U0 = (int)(L::BYTES / 1024);
     constexpr int UV = (int)((NSL * L::USL + 1023) / 1024);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(gblk, (uint32_t)blk_bytes);
     const int vbase = (int)(L::BYTES + (size_t)sg * NSL * L::USL) - U0 * 1024;
+    // rot: start the shared part at piece (rot * 16) mod U0 (issue order only)
+    const int r0 = (rot * 16) % U0;
 #pragma unroll
-    for (int u = w; u < U0 + UV; u += NW) {
+    for (int i = w; i < U0 + UV; i += NW) {
+        const int u = i < U0 ? (i + r0) % U0 : i;
         const int soff = u < U0 ? u * 1024 : vbase + u * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(smem + lds_off + u * 1024),
                                                  16, lane * 16, soff, 0, 0);
@@ -1594,6 +1624,249 @@ __global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams 
     }
 }
 
+// ------------------------------------------------------------------ state kernel, four waves per slice
+//
+// dk = 128, 64-token chunks, bf16 inputs: each 16-column slice is shared by
+// four waves. Wave q keeps state rows (channels) 32q .. 32q + 31 -- channel
+// step q of the B operand over channels -- and produces token rows
+// 16q .. 16q + 15. Per chunk the four waves trade, through LDS, their fp16
+// fragment of S (before W S and (Gamma o Q) S) and their rows of U in fp32
+// (before P U and K_end^T U; every wave then forms the same U fragments with
+// the same scales). Each wave reads a quarter of the W, Gamma o Q and K_end^T
+// fragments. Partial products over channel steps with different scales go to
+// separate accumulators and are combined in fp32.
+
+template <int NS>
+struct QuadSmem {
+    using L = Lay<128, 64, false>;
+    static constexpr size_t UBYTES = ((size_t)NS * L::USL + 1023) / 1024 * 1024;
+    static constexpr size_t BUF = L::BYTES + UBYTES;
+    // per-slice exchange area
+    static constexpr size_t X_S = 0;                     // S fragments [4 channel steps][64 lanes]
+    static constexpr size_t X_U = X_S + 4 * 1024;        // U rows, fp32 [4 token blocks][64 lanes][4]
+    static constexpr size_t X_SI = X_U + 4 * 1024;       // inverse S scales [4][16]
+    static constexpr size_t X_F = X_SI + 4 * 16 * 4;     // U-posted flags [4] (chunk index)
+    static constexpr size_t XSL = X_F + 16;
+    static constexpr size_t XCH = 2 * BUF;
+    static constexpr size_t BYTES = XCH + (size_t)NS * XSL;
+};
+
+template <int NS>
+__global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams p) {
+    constexpr int DK = 128, C = 64;
+    using L = Lay<DK, C, false>;
+    using SM = QuadSmem<NS>;
+    using F = f16x8;
+    constexpr int KSD = L::KSD, KSC = L::KSC;   // 4 channel steps, 2 token steps
+    constexpr int NCW = 4 * NS;                  // compute waves
+    constexpr int NCP = 2 * NS;                  // copy waves
+
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int sg = item % p.NSG;
+    const int hs = item / p.NSG;
+    const int H = p.H, DV = p.DV;
+    const int h = hs % H, s = hs / H;
+    const int lane = threadIdx.x % 64;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);   // wave index, uniform
+    const bool copier = wv >= NCW;
+    const int w = copier ? wv - NCW : wv;
+    const int sl = w / 4, q = w % 4;       // slice in the workgroup, quarter of the slice
+    const int li = lane % 16, lg = lane / 16;
+    const int col = 16 * (sg * NS + sl) + li;
+
+    long bos, eos;
+    int cs, ce;
+    if (p.map.cu == nullptr) {
+        bos = (long)s * p.map.T + (long)p.map.c0 * C;
+        eos = (long)(s + 1) * p.map.T;
+        cs = s * p.map.NC + p.map.c0;
+        ce = s * p.map.NC + p.map.c1;
+    } else {
+        bos = p.map.cu[s];
+        eos = p.map.cu[s + 1];
+        cs = p.map.cstart[s];
+        ce = p.map.cstart[s + 1];
+    }
+
+    const uint32_t xs = (uint32_t)(SM::XCH + (size_t)sl * SM::XSL);   // this slice's exchange area
+    const uint32_t lfr = (uint32_t)lane * 16;
+
+    // own state rows 16 (2q + c) + 4 lg + e of column col
+    f32x4 S[2];
+    const size_t sbase = ((size_t)s * H + h) * DK * DV;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[c][e] = (p.S0 && !copier) ? p.S0[sbase + (size_t)(16 * (2 * q + c) + 4 * lg + e) * DV + col] : 0.f;
+
+    // own channel step of S as a fragment, its inverse scale, both posted
+    F sfo;
+    float iSo = 1.f;
+    auto make_s_frag = [&]() {
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[c][e]));
+        m = colmax4(m);
+        const float sc = pow2_scale_for(m);
+        iSo = pow2_inv_scale_for(m);
+        sfo = to_f16x8(dtiles_to_frag(S[0], S[1]), sc);
+        lds_st<F>(xs + (uint32_t)(SM::X_S + (size_t)q * 1024) + lfr, sfo);
+        if (lg == 0) lds_st<float>(xs + (uint32_t)SM::X_SI + 4 * (16 * q + li), iSo);
+    };
+
+    auto gblock = [&](int cg) { return p.ws + ((size_t)cg * H + h) * p.blk_bytes; };
+    const uint32_t orow = (uint32_t)H * DV * 4;
+
+    if (copier) {
+        if (cs < ce) {
+            stage_chunk<DK, C, false, NCP, NS>(0, gblock(cs), p.blk_bytes, sg, w, lane, sg);
+            wait_vm_all();
+        }
+    } else {
+        make_s_frag();
+        if (lane == 0) lds_st<int>(xs + (uint32_t)SM::X_F + 4 * q, -1);
+    }
+    __syncthreads();
+
+    for (int cg = cs; cg < ce; ++cg) {
+        if (copier) {
+            // chunk cg+1 into the free buffer; the copy has the whole
+            // iteration and must land before the barrier that ends it. The
+            // workgroups of one (sequence, head) start at different pieces,
+            // so that one of them misses L2 on each line and the others hit.
+            if (cg + 1 < ce)
+                stage_chunk<DK, C, false, NCP, NS>((uint32_t)(((cg + 1 - cs) % 2) * SM::BUF), gblock(cg + 1), p.blk_bytes,
+                                                   sg, w, lane, sg);
+            wait_vm_all();
+            __syncthreads();
+            continue;
+        }
+        const long t0 = bos + (long)(cg - cs) * C;
+        const int n = (int)min((long)C, eos - t0);
+        const uint32_t bo = (uint32_t)(((cg - cs) % 2) * SM::BUF);
+        auto frag = [&](size_t off, int tile) { return lds_ld<F>(bo + (uint32_t)off + (uint32_t)tile * 1024 + lfr); };
+        auto scl = [&](int i) { return lds_ld<float>(bo + (uint32_t)L::SC_OFF + 4 * i); };
+        const float iW = scl(SC_INV + SC_W), iQ = scl(SC_INV + SC_Q), iK = scl(SC_INV + SC_K), iP = scl(SC_INV + SC_P);
+
+        // ---- S over all channel steps (the other three from LDS)
+        F sf[KSD];
+        float iS[KSD];
+#pragma unroll
+        for (int k = 0; k < KSD; ++k) {
+            if (k == q) continue;
+            sf[k] = lds_ld<F>(xs + (uint32_t)(SM::X_S + (size_t)k * 1024) + lfr);
+            iS[k] = lds_ld<float>(xs + (uint32_t)SM::X_SI + 4 * (16 * k + li));
+        }
+        // wave-uniform q: place the own step by selection (no dynamic register index)
+#pragma unroll
+        for (int k = 0; k < KSD; ++k)
+            if (k == q) { sf[k] = sfo; iS[k] = iSo; }
+
+        // ---- own token rows rb = q:  u = U~ - W S,  O = (Gamma o Q) S
+        f32x4 uq, ov = zero4();
+        {
+            f32x4 ws = zero4();
+#pragma unroll
+            for (int k = 0; k < KSD; ++k) {
+                const f32x4 wk = mma(frag(L::W_OFF, q * KSD + k), sf[k], zero4());
+                const f32x4 qk = mma(frag(L::QG_OFF, q * KSD + k), sf[k], zero4());
+                const float a = iW * iS[k], b = iQ * iS[k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ws[e] += wk[e] * a;
+                    ov[e] += qk[e] * b;
+                }
+            }
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            const float iUc = lds_ld<float>(bo + (uint32_t)L::SU_OFF + 4 * (uint32_t)col);
+            const h4 ut = lds_ld<h4>(bo + (uint32_t)L::BYTES + (uint32_t)(sl * L::USL) + (uint32_t)L::u_off(q, lane));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uq[e] = (float)ut[e] * iUc - ws[e];
+        }
+        // post own rows of U; the LDS operations of one wave complete in order,
+        // so the flag lands after the rows; waits are bounded (all four waves
+        // are resident and post every chunk)
+        lds_st<f32x4>(xs + (uint32_t)(SM::X_U + (size_t)q * 1024) + lfr, uq);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) lds_st<int>(xs + (uint32_t)SM::X_F + 4 * q, cg);
+        {
+            extern __shared__ __align__(16) unsigned char smem[];
+            typedef __attribute__((address_space(3))) const volatile int lds_flag_t;
+            lds_flag_t* flags = (lds_flag_t*)(smem + xs + SM::X_F);
+            for (int spin = 0; spin < (1 << 24); ++spin) {
+                if (flags[0] == cg && flags[1] == cg && flags[2] == cg && flags[3] == cg) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        f32x4 u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = r == q ? uq : lds_ld<f32x4>(xs + (uint32_t)(SM::X_U + (size_t)r * 1024) + lfr);
+
+        // ---- U over the two token steps, one scale per (step, column); every
+        // wave of the slice forms the same fragments
+        F uf[KSC];
+        float iU[KSC];
+#pragma unroll
+        for (int t = 0; t < KSC; ++t) {
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(u[2 * t][e]), fabsf(u[2 * t + 1][e])));
+            m = colmax4(m);
+            iU[t] = pow2_inv_scale_for(m);
+            uf[t] = to_f16x8(dtiles_to_frag(u[2 * t], u[2 * t + 1]), pow2_scale_for(m));
+        }
+
+        // ---- O += P U for token rows rb = q (strictly lower part on MFMA,
+        // diagonal in fp32); rows past the chunk end fall outside the store
+        // descriptor
+        {
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
+            const uint32_t ovoff = (uint32_t)(4 * lg) * orow + (uint32_t)col * 4;
+            f32x4 o4 = ov;
+#pragma unroll
+            for (int t = 0; t < KSC; ++t) {
+                if (t > q / 2) continue;
+                const f32x4 pu = mma(frag(L::PS_OFF, q * KSC + t), uf[t], zero4());
+                const float pc = iP * iU[t];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] += pu[e] * pc;
+            }
+            const f32x4 pd4 = lds_ld<f32x4>(bo + (uint32_t)L::PD_OFF + 4 * (16 * q + 4 * lg));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ovv = o4[e] + pd4[e] * uq[e];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ovv), ro, ovoff, (16 * q + e) * orow, 0);
+            }
+        }
+
+        // ---- own state rows: S <- Diag(gamma_last) S + K_end^T U
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int cb = 2 * q + c;
+            const f32x4 k0 = mma(frag(L::KE_OFF, cb * KSC + 0), uf[0], zero4());
+            const f32x4 k1 = mma(frag(L::KE_OFF, cb * KSC + 1), uf[1], zero4());
+            const float c0 = iK * iU[0], c1 = iK * iU[1];
+            const f32x4 g4 = lds_ld<f32x4>(bo + (uint32_t)L::GN_OFF + 4 * (16 * cb + 4 * lg));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[c][e] = S[c][e] * g4[e] + (k0[e] * c0 + k1[e] * c1);
+        }
+        make_s_frag();
+        __syncthreads();
+    }
+
+    if (!copier && p.S_T) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.S_T[sbase + (size_t)(16 * (2 * q + c) + 4 * lg + e) * DV + col] = S[c][e];
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 template <int DK, int C>
@@ -1634,8 +1907,12 @@ static size_t index_bytes(bool varlen, int N) { return varlen ? ((size_t)(N + 1)
 // workspace.
 constexpr int MAX_SEG = 16;
 static int segment_chunks(int NC, bool varlen) {
-    if (varlen || NC < 32) return NC;
-    int seg = (NC + 7) / 8;                                // about eight segments (measured best of 1-16)
+    // Off: with the current prep kernel the two launches run faster one after
+    // the other (0.447 ms) than overlapped in 2 to 16 segments (0.48-0.50 ms
+    // on the Complex KDA workload): prep workgroups spread over every CU and
+    // the state walk's workgroups, which need a whole CU's LDS, wait for them.
+    if (varlen || NC < 32 || NC > 0) return NC;
+    int seg = (NC + 7) / 8;
     if (seg < 16) seg = 16;
     if (seg < (NC + MAX_SEG - 1) / MAX_SEG) seg = (NC + MAX_SEG - 1) / MAX_SEG;
     return seg;
@@ -1727,13 +2004,32 @@ static hipError_t launch_state_pair(const ChunkArgs& a, const ChunkMap& map, con
     return hipGetLastError();
 }
 
-// bf16 inputs, 64-token chunks, dk >= 64: two waves per slice, four slices
-// per workgroup. Otherwise one wave per slice: four compute waves of one
+template <int NS>
+static hipError_t launch_state_quad(const ChunkArgs& a, const ChunkMap& map, const unsigned char* blocks) {
+    using SM = QuadSmem<NS>;
+    static_assert(SM::BYTES <= 160 * 1024, "quad state LDS");
+    auto kern = chunk_state_quad_kernel<NS>;
+    hipError_t e = allow_lds(kern, SM::BYTES);
+    if (e != hipSuccess) return e;
+    const int nsg = a.dv / 16 / NS;
+    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(128, a.dv, 64, true), map, a.H, a.dv, nsg};
+    const long grid = (long)nsg * a.H * a.N;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(384 * NS), SM::BYTES, a.stream, sp);
+    return hipGetLastError();
+}
+
+// bf16 inputs, 64-token chunks: dk = 128 takes four waves per slice (two
+// slices per workgroup), dk = 64 two waves per slice (four slices per
+// workgroup). Otherwise one wave per slice: four compute waves of one
 // slice each when the value width allows (more waves in flight shorten the
 // sequential chunk loop more than sharing fragment reads between slices of
 // one wave does).
 template <class TIn, int DK, int C>
 static hipError_t launch_state_t(const ChunkArgs& a, const ChunkMap& map, const unsigned char* blocks) {
+    if constexpr (std::is_same<TIn, uint16_t>::value && C == 64 && DK == 128) {
+        if (a.dv >= 32) return launch_state_quad<2>(a, map, blocks);
+        return launch_state_quad<1>(a, map, blocks);
+    }
     if constexpr (std::is_same<TIn, uint16_t>::value && C == 64 && DK >= 64) {
         if (a.dv >= 64) return launch_state_pair<DK, C, 4>(a, map, blocks);
         if (a.dv >= 32) return launch_state_pair<DK, C, 2>(a, map, blocks);
