@@ -1720,6 +1720,7 @@ __global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams 
     auto gblock = [&](int cg) { return p.ws + ((size_t)cg * H + h) * p.blk_bytes; };
     const uint32_t orow = (uint32_t)H * DV * 4;
 
+    uint32_t sink = 0;
     if (copier) {
         if (cs < ce) {
             stage_chunk<DK, C, false, NCP, NS>(0, gblock(cs), p.blk_bytes, sg, w, lane, sg);
@@ -1740,7 +1741,22 @@ __global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams 
             if (cg + 1 < ce)
                 stage_chunk<DK, C, false, NCP, NS>((uint32_t)(((cg + 1 - cs) % 2) * SM::BUF), gblock(cg + 1), p.blk_bytes,
                                                    sg, w, lane, sg);
-            wait_vm_all();
+            // Pull this workgroup's share (one part in NSG) of chunk cg+2's
+            // shared operands into L2 with one 4-byte load per 128-byte line:
+            // the misses are spread over the workgroups of the (sequence,
+            // head), and every workgroup's copy of chunk cg+2 then hits L2.
+            if (cg + 2 < ce) {
+                constexpr int L0 = (int)(L::BYTES / 128);
+                const int per = (L0 + p.NSG - 1) / p.NSG;
+                const int line = sg * per + w * 64 + lane;
+                const bool mine = w * 64 + lane < per && line < L0;
+                const __amdgpu_buffer_rsrc_t rt = make_rsrc(gblock(cg + 2), (uint32_t)L::BYTES);
+                // other lanes point past the descriptor: no access, value 0
+                sink ^= __builtin_amdgcn_raw_buffer_load_b32(rt, mine ? line * 128 : (int)L::BYTES, 0, 0);
+                wait_vm_upto<1>();
+            } else {
+                wait_vm_all();
+            }
             __syncthreads();
             continue;
         }
@@ -1859,7 +1875,11 @@ __global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams 
         __syncthreads();
     }
 
-    if (!copier && p.S_T) {
+    if (copier) {
+        // keep the L2 touches alive: a store that no real input triggers
+        // (H is positive for every launch)
+        if (sink == 0x9e3779b9u && p.H < 0) p.o[0] = 0.f;
+    } else if (p.S_T) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
