@@ -146,11 +146,11 @@ def main(argv=None) -> int:
         "unit": "GB/s",
         "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
         "traffic": traffic_fwd,
-        "kernel": "kda_chunk_fwd: chunk_prep_kernel + chunk_state_pair_kernel, 8 time segments on two streams (one call)",
+        "kernel": "kda_chunk_fwd: chunk_prep_kernel then chunk_state_slice_kernel (one call, one stream)",
         "bytes_per_launch": alg_bytes,
         "launch_ms": round(ms, 4),
         "mfma_frac_algorithmic": round(alg_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "kernels_ms": {"chunk_prep_kernel": round(ms_prep, 4), "chunk_state_kernel": round(ms_state, 4)},
+        "kernels_ms": {"chunk_prep_kernel": round(ms_prep, 4), "chunk_state_slice_kernel": round(ms_state, 4)},
     }
     del sets, ws, o
 

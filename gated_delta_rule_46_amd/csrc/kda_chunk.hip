@@ -390,8 +390,9 @@ __device__ __forceinline__ bool sep_at(int r, int j, int hh) {
     return (r / w == j / w) && (r % w >= hh) && (j % w < hh);
 }
 
+// One (chunk, head) item of the prep work on the four waves of a workgroup.
 template <class TIn, int DK, int C, bool SG, bool F32M>
-__global__ void __launch_bounds__(256, F32M ? 1 : 3) chunk_prep_kernel(PrepParams p) {
+__device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     using L = Lay<DK, C, F32M>;
     using SM = PrepLds<TIn, DK, C, F32M>;
     using TM = typename L::TM;
@@ -411,7 +412,6 @@ __global__ void __launch_bounds__(256, F32M ? 1 : 3) chunk_prep_kernel(PrepParam
     float* s_xm = reinterpret_cast<float*>(smem + SM::XM);
 
     const int H = p.H, DV = p.DV;
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
     const int h = item % H, gidx = launch_chunk(p.map, item / H);
     long t0;
     int n;
@@ -1050,6 +1050,11 @@ __global__ void __launch_bounds__(256, F32M ? 1 : 3) chunk_prep_kernel(PrepParam
     }
 }
 
+template <class TIn, int DK, int C, bool SG, bool F32M>
+__global__ void __launch_bounds__(256, F32M ? 1 : 3) chunk_prep_kernel(PrepParams p) {
+    prep_item<TIn, DK, C, SG, F32M>(p, xcd_remap(blockIdx.x, gridDim.x));
+}
+
 // ------------------------------------------------------------------ state kernel
 
 struct StateParams {
@@ -1652,7 +1657,7 @@ struct QuadSmem {
 };
 
 template <int NS>
-__global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams p) {
+__device__ __forceinline__ void quad_walk(const StateParams& p, int item) {
     constexpr int DK = 128, C = 64;
     using L = Lay<DK, C, false>;
     using SM = QuadSmem<NS>;
@@ -1661,7 +1666,6 @@ __global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams 
     constexpr int NCW = 4 * NS;                  // compute waves
     constexpr int NCP = 2 * NS;                  // copy waves
 
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
     const int sg = item % p.NSG;
     const int hs = item / p.NSG;
     const int H = p.H, DV = p.DV;
@@ -1887,6 +1891,303 @@ __global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams 
     }
 }
 
+template <int NS>
+__global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams p) {
+    quad_walk<NS>(p, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// ------------------------------------------------------------------ slice walker
+
+// One 16-column value slice of one (sequence, head) on one workgroup of four
+// waves, with the chunk operands loaded straight into registers one chunk
+// ahead (no LDS staging and no copy waves). Wave q keeps state rows 32q ..
+// 32q + 31 and produces token rows 16q .. 16q + 15, and needs only its own
+// quarter of W, Gamma o Q, K_end^T and P; the four waves trade their fp16
+// S fragment and their fp32 U rows through LDS, as in the two-slice walker,
+// whose arithmetic this repeats operation for operation. The eight slices of
+// a (sequence, head) are consecutive workgroups (one XCD), so a block fetched
+// from memory by one of them is served to the others by L2.
+struct SliceLds {
+    static constexpr size_t X_S = 0;                     // S fragments [4 channel steps][64 lanes]
+    static constexpr size_t X_U = X_S + 4 * 1024;        // U rows, fp32 [4 token blocks][64 lanes][4]
+    static constexpr size_t X_SI = X_U + 4 * 1024;       // inverse S scales [4][16]
+    static constexpr size_t X_F = X_SI + 4 * 16 * 4;     // U-posted flags [4] (chunk index)
+    static constexpr size_t BYTES = (X_F + 16 + 1023) / 1024 * 1024;
+};
+
+// A 16x32 fp16 fragment of a block: tile t, this lane's 16 bytes.
+__device__ __forceinline__ f16x8 ld_frag(__amdgpu_buffer_rsrc_t r, uint32_t off, int tile, int lane) {
+    return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + (uint32_t)tile * 1024 + (uint32_t)lane * 16), 0, 0));
+}
+__device__ __forceinline__ f32x4 ld_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float ld_f1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// The operands of one chunk that wave q reads, in the groups in which they
+// are reloaded for the next chunk: each group right after its last use in
+// this chunk, so that the loads spread over the chunk instead of stalling the
+// wave's instruction stream in one burst.
+struct SliceOps {
+    f16x8 w[4], qg[4];            // group 0: W, Gamma o Q (first used)
+    f32x4 isc;                    //          inverse scales W Q K T
+    float iP, iUc;                //          inverse scale of P, of this U~ column
+    _Float16 __attribute__((ext_vector_type(4))) ut;   // U~ rows
+    f16x8 ps[2];                  // group 1: strictly lower P
+    f32x4 pd;                     //          P diagonal rows
+    f16x8 ke[2][2];               // group 2: K_end^T
+    f32x4 g[2];                   //          gamma_last rows
+};
+
+struct SliceSrc {
+    __amdgpu_buffer_rsrc_t r;
+    int q, lane, col, slice;
+};
+
+__device__ __forceinline__ void slice_load0(SliceOps& o, const SliceSrc& x) {
+    using L = Lay<128, 64, false>;
+    constexpr int KSD = L::KSD;
+#pragma unroll
+    for (int k = 0; k < KSD; ++k) o.w[k] = ld_frag(x.r, (uint32_t)L::W_OFF, x.q * KSD + k, x.lane);
+#pragma unroll
+    for (int k = 0; k < KSD; ++k) o.qg[k] = ld_frag(x.r, (uint32_t)L::QG_OFF, x.q * KSD + k, x.lane);
+    o.isc = ld_f4(x.r, (uint32_t)L::SC_OFF + 4 * SC_INV);
+    o.iP = ld_f1(x.r, (uint32_t)L::SC_OFF + 4 * (SC_INV + SC_P));
+    o.iUc = ld_f1(x.r, (uint32_t)L::SU_OFF + 4 * (uint32_t)x.col);
+    const uint32_t uo = (uint32_t)(L::BYTES + (size_t)x.slice * L::USL + L::u_off(x.q, x.lane));
+    o.ut = __builtin_bit_cast(decltype(o.ut), __builtin_amdgcn_raw_buffer_load_b64(x.r, (int)uo, 0, 0));
+}
+
+__device__ __forceinline__ void slice_load1(SliceOps& o, const SliceSrc& x) {
+    using L = Lay<128, 64, false>;
+    constexpr int KSC = L::KSC;
+#pragma unroll
+    for (int t = 0; t < KSC; ++t)
+        if (t <= x.q / 2) o.ps[t] = ld_frag(x.r, (uint32_t)L::PS_OFF, x.q * KSC + t, x.lane);
+    o.pd = ld_f4(x.r, (uint32_t)L::PD_OFF + 4 * (16 * x.q + 4 * (x.lane / 16)));
+}
+
+__device__ __forceinline__ void slice_load2(SliceOps& o, const SliceSrc& x) {
+    using L = Lay<128, 64, false>;
+    constexpr int KSC = L::KSC;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int t = 0; t < KSC; ++t) o.ke[c][t] = ld_frag(x.r, (uint32_t)L::KE_OFF, (2 * x.q + c) * KSC + t, x.lane);
+        o.g[c] = ld_f4(x.r, (uint32_t)L::GN_OFF + 4 * (16 * (2 * x.q + c) + 4 * (x.lane / 16)));
+    }
+}
+
+__device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
+    constexpr int DK = 128, C = 64;
+    using L = Lay<DK, C, false>;
+    using SM = SliceLds;
+    using F = f16x8;
+    constexpr int KSD = L::KSD, KSC = L::KSC;   // 4 channel steps, 2 token steps
+
+    const int nsl = p.NSG;                       // slices per (sequence, head)
+    const int sl = item % nsl;
+    const int hs = item / nsl;
+    const int H = p.H, DV = p.DV;
+    const int h = hs % H, s = hs / H;
+    const int lane = threadIdx.x % 64;
+    const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);   // quarter, uniform
+    const int li = lane % 16, lg = lane / 16;
+    const int col = 16 * sl + li;
+
+    long bos, eos;
+    int cs, ce;
+    if (p.map.cu == nullptr) {
+        bos = (long)s * p.map.T + (long)p.map.c0 * C;
+        eos = (long)(s + 1) * p.map.T;
+        cs = s * p.map.NC + p.map.c0;
+        ce = s * p.map.NC + p.map.c1;
+    } else {
+        bos = p.map.cu[s];
+        eos = p.map.cu[s + 1];
+        cs = p.map.cstart[s];
+        ce = p.map.cstart[s + 1];
+    }
+    const uint32_t lfr = (uint32_t)lane * 16;
+
+    // own state rows 16 (2q + c) + 4 lg + e of column col
+    f32x4 S[2];
+    const size_t sbase = ((size_t)s * H + h) * DK * DV;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[c][e] = p.S0 ? p.S0[sbase + (size_t)(16 * (2 * q + c) + 4 * lg + e) * DV + col] : 0.f;
+
+    F sfo;
+    float iSo = 1.f;
+    auto make_s_frag = [&]() {
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[c][e]));
+        m = colmax4(m);
+        const float sc = pow2_scale_for(m);
+        iSo = pow2_inv_scale_for(m);
+        sfo = to_f16x8(dtiles_to_frag(S[0], S[1]), sc);
+        lds_st<F>((uint32_t)(SM::X_S + (size_t)q * 1024) + lfr, sfo);
+        if (lg == 0) lds_st<float>((uint32_t)SM::X_SI + 4 * (16 * q + li), iSo);
+    };
+
+    auto gblock = [&](int cg) { return p.ws + ((size_t)cg * H + h) * p.blk_bytes; };
+    const uint32_t orow = (uint32_t)H * DV * 4;
+
+    auto src = [&](int cg) { return SliceSrc{make_rsrc(gblock(cg), (uint32_t)p.blk_bytes), q, lane, col, sl}; };
+    SliceOps op;
+    if (cs < ce) {
+        const SliceSrc x = src(cs);
+        slice_load0(op, x);
+        slice_load1(op, x);
+        slice_load2(op, x);
+    }
+    make_s_frag();
+    if (lane == 0) lds_st<int>((uint32_t)SM::X_F + 4 * q, -1);
+    __syncthreads();
+
+    uint32_t sink = 0;
+    for (int cg = cs; cg < ce; ++cg) {
+        const long t0 = bos + (long)(cg - cs) * C;
+        const int n = (int)min((long)C, eos - t0);
+        // first touch of chunk cg+2's shared operands by this slice's share of
+        // the lines, so that the slices of the (sequence, head) find them in
+        // L2. Issued before the loads below and consumed at the end of the
+        // iteration: waiting for it then does not wait for them.
+        uint32_t tch;
+        {
+            constexpr int L0 = (int)(L::BYTES / 128);
+            const int per = (L0 + nsl - 1) / nsl;
+            const int line = sl * per + q * 64 + lane;
+            const bool mine = cg + 2 < ce && q * 64 + lane < per && line < L0;
+            const __amdgpu_buffer_rsrc_t rt = make_rsrc(gblock(cg + 2 < ce ? cg + 2 : cg), (uint32_t)L::BYTES);
+            // lanes without a line point past the descriptor: no access, value 0
+            tch = __builtin_amdgcn_raw_buffer_load_b32(rt, mine ? line * 128 : (int)L::BYTES, 0, 0);
+        }
+        // operands of the next chunk (the last chunk reloads its own: a valid
+        // block, never used)
+        const int cn = cg + 1 < ce ? cg + 1 : cg;
+        const SliceSrc xn = src(cn);
+        const float iW = op.isc[SC_W], iQ = op.isc[SC_Q], iK = op.isc[SC_K], iP = op.iP;
+
+        // ---- S over all channel steps (the other three from LDS)
+        F sf[KSD];
+        float iS[KSD];
+#pragma unroll
+        for (int k = 0; k < KSD; ++k) {
+            if (k == q) continue;
+            sf[k] = lds_ld<F>((uint32_t)(SM::X_S + (size_t)k * 1024) + lfr);
+            iS[k] = lds_ld<float>((uint32_t)SM::X_SI + 4 * (16 * k + li));
+        }
+#pragma unroll
+        for (int k = 0; k < KSD; ++k)
+            if (k == q) { sf[k] = sfo; iS[k] = iSo; }
+
+        // ---- own token rows rb = q:  u = U~ - W S,  O = (Gamma o Q) S
+        f32x4 uq, ov = zero4();
+        {
+            f32x4 ws = zero4();
+#pragma unroll
+            for (int k = 0; k < KSD; ++k) {
+                const f32x4 wk = mma(op.w[k], sf[k], zero4());
+                const f32x4 qk = mma(op.qg[k], sf[k], zero4());
+                const float a = iW * iS[k], b = iQ * iS[k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ws[e] += wk[e] * a;
+                    ov[e] += qk[e] * b;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uq[e] = (float)op.ut[e] * op.iUc - ws[e];
+        }
+        slice_load0(op, xn);
+        lds_st<f32x4>((uint32_t)(SM::X_U + (size_t)q * 1024) + lfr, uq);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) lds_st<int>((uint32_t)SM::X_F + 4 * q, cg);
+        {
+            extern __shared__ __align__(16) unsigned char smem[];
+            typedef __attribute__((address_space(3))) const volatile int lds_flag_t;
+            lds_flag_t* fl = (lds_flag_t*)(smem + SM::X_F);
+            for (int spin = 0; spin < (1 << 24); ++spin) {
+                if (fl[0] == cg && fl[1] == cg && fl[2] == cg && fl[3] == cg) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        f32x4 u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = r == q ? uq : lds_ld<f32x4>((uint32_t)(SM::X_U + (size_t)r * 1024) + lfr);
+
+        // ---- U over the two token steps, one scale per (step, column)
+        F uf[KSC];
+        float iU[KSC];
+#pragma unroll
+        for (int t = 0; t < KSC; ++t) {
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(u[2 * t][e]), fabsf(u[2 * t + 1][e])));
+            m = colmax4(m);
+            iU[t] = pow2_inv_scale_for(m);
+            uf[t] = to_f16x8(dtiles_to_frag(u[2 * t], u[2 * t + 1]), pow2_scale_for(m));
+        }
+
+        // ---- O += P U for token rows rb = q, diagonal in fp32
+        {
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
+            const uint32_t ovoff = (uint32_t)(4 * lg) * orow + (uint32_t)col * 4;
+            f32x4 o4 = ov;
+#pragma unroll
+            for (int t = 0; t < KSC; ++t) {
+                if (t > q / 2) continue;
+                const f32x4 pu = mma(op.ps[t], uf[t], zero4());
+                const float pc = iP * iU[t];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] += pu[e] * pc;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ovv = o4[e] + op.pd[e] * uq[e];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ovv), ro, ovoff, (16 * q + e) * orow, 0);
+            }
+        }
+        slice_load1(op, xn);
+
+        // ---- own state rows: S <- Diag(gamma_last) S + K_end^T U
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const f32x4 k0 = mma(op.ke[c][0], uf[0], zero4());
+            const f32x4 k1 = mma(op.ke[c][1], uf[1], zero4());
+            const float c0 = iK * iU[0], c1 = iK * iU[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[c][e] = S[c][e] * op.g[c][e] + (k0[e] * c0 + k1[e] * c1);
+        }
+        slice_load2(op, xn);
+        make_s_frag();
+        sink ^= tch;
+        __syncthreads();
+    }
+    // keep the L2 touches alive: a store that no real input triggers
+    if (sink == 0x9e3779b9u && p.H < 0) p.o[0] = 0.f;
+    if (p.S_T) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.S_T[sbase + (size_t)(16 * (2 * q + c) + 4 * lg + e) * DV + col] = S[c][e];
+    }
+}
+
+__global__ void __launch_bounds__(256) chunk_state_slice_kernel(StateParams p) {
+    slice_walk(p, xcd_remap(blockIdx.x, gridDim.x));
+}
+
 // ------------------------------------------------------------------ host side
 
 template <int DK, int C>
@@ -1920,59 +2221,22 @@ long chunk_count_bound(int B, int T, int chunk, bool varlen, int N) {
 
 static size_t index_bytes(bool varlen, int N) { return varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0; }
 
-// Chunks per time segment. Long equal-length sequences run as a series of
-// (prep, state) launches over consecutive chunk ranges, so that the state
-// kernel reads each segment's blocks while they are still in the last-level
-// cache; the state carries from one segment to the next through the
-// workspace.
-constexpr int MAX_SEG = 16;
-static int segment_chunks(int NC, bool varlen) {
-    // Off: with the current prep kernel the two launches run faster one after
-    // the other (0.447 ms) than overlapped in 2 to 16 segments (0.48-0.50 ms
-    // on the Complex KDA workload): prep workgroups spread over every CU and
-    // the state walk's workgroups, which need a whole CU's LDS, wait for them.
-    if (varlen || NC < 32 || NC > 0) return NC;
-    int seg = (NC + 7) / 8;
-    if (seg < 16) seg = 16;
-    if (seg < (NC + MAX_SEG - 1) / MAX_SEG) seg = (NC + MAX_SEG - 1) / MAX_SEG;
-    return seg;
-}
-
-// A second stream per device for the prep kernels of the segmented path, and
-// events to order it against the caller's stream (fork at the start of a
-// call, one event per segment). Created on first use, default priority.
-struct SegStreams {
-    hipStream_t aux = nullptr;
-    hipEvent_t fork = nullptr;
-    hipEvent_t seg[MAX_SEG] = {};
-};
-static hipError_t seg_streams(SegStreams*& out) {
-    static std::mutex mu;
-    static SegStreams per_dev[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    SegStreams& r = per_dev[dev];
-    if (r.aux == nullptr) {
-        hipStream_t st;
-        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
-        if (e != hipSuccess) return e;
-        e = hipEventCreateWithFlags(&r.fork, hipEventDisableTiming);
-        for (int i = 0; i < MAX_SEG && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&r.seg[i], hipEventDisableTiming);
-        if (e != hipSuccess) return e;
-        r.aux = st;
-    }
-    out = &r;
-    return hipSuccess;
-}
-
 size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, bool varlen, int N, bool bf16) {
-    const int NC = (T + chunk - 1) / chunk;
-    const size_t carry = segment_chunks(NC, varlen) < NC ? (size_t)B * H * dk * dv * 4 : 0;
-    return index_bytes(varlen, N) +
-           (size_t)chunk_count_bound(B, T, chunk, varlen, N) * H * chunk_block_bytes(dk, dv, chunk, bf16) + carry;
+    return index_bytes(varlen, N) + (size_t)chunk_count_bound(B, T, chunk, varlen, N) * H * chunk_block_bytes(dk, dv, chunk, bf16);
+}
+
+static int device_cus() {
+    static std::mutex mu;
+    static int per_dev[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (per_dev[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        per_dev[dev] = n;
+    }
+    return per_dev[dev];
 }
 
 template <class K>
@@ -2038,6 +2302,14 @@ static hipError_t launch_state_quad(const ChunkArgs& a, const ChunkMap& map, con
     return hipGetLastError();
 }
 
+static hipError_t launch_state_slice(const ChunkArgs& a, const ChunkMap& map, const unsigned char* blocks) {
+    const int nsl = a.dv / 16;
+    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(128, a.dv, 64, true), map, a.H, a.dv, nsl};
+    const long grid = (long)nsl * a.H * a.N;
+    hipLaunchKernelGGL(chunk_state_slice_kernel, dim3((unsigned)grid), dim3(256), SliceLds::BYTES, a.stream, sp);
+    return hipGetLastError();
+}
+
 // bf16 inputs, 64-token chunks: dk = 128 takes four waves per slice (two
 // slices per workgroup), dk = 64 two waves per slice (four slices per
 // workgroup). Otherwise one wave per slice: four compute waves of one
@@ -2047,6 +2319,10 @@ static hipError_t launch_state_quad(const ChunkArgs& a, const ChunkMap& map, con
 template <class TIn, int DK, int C>
 static hipError_t launch_state_t(const ChunkArgs& a, const ChunkMap& map, const unsigned char* blocks) {
     if constexpr (std::is_same<TIn, uint16_t>::value && C == 64 && DK == 128) {
+        // one-slice walkers while they fit one per CU (measured faster
+        // there); two-slice walkers when slices outnumber the CUs
+        const long slices = (long)a.N * a.H * (a.dv / 16);
+        if (slices <= device_cus()) return launch_state_slice(a, map, blocks);
         if (a.dv >= 32) return launch_state_quad<2>(a, map, blocks);
         return launch_state_quad<1>(a, map, blocks);
     }
@@ -2068,48 +2344,18 @@ static hipError_t launch_pair(const ChunkArgs& a) {
     const int NC = (a.T + C - 1) / C;
     ChunkMap map{a.cu_seqlens, varlen ? (const int32_t*)ws : nullptr, a.T, a.N, NC, 0, NC};
     unsigned char* blocks = ws + ib;
-    auto prep = [&](const ChunkMap& m, long nch) -> hipError_t {
-        if (nch <= 0) return hipSuccess;
-        return a.scalar_gate ? launch_prep_t<TIn, DK, C, true>(a, m, blocks, nch)
-                             : launch_prep_t<TIn, DK, C, false>(a, m, blocks, nch);
-    };
-    const int seg = segment_chunks(NC, varlen);
-    if (a.stages == 3 && seg < NC) {
-        // prep of segment k+1 (second stream) overlaps the state walk of
-        // segment k (caller's stream)
-        SegStreams* ss = nullptr;
-        hipError_t e = seg_streams(ss);
-        if (e != hipSuccess) return e;
-        float* carry = reinterpret_cast<float*>(blocks + (size_t)chunk_count_bound(a.B, a.T, C, false, a.N) * a.H *
-                                                             chunk_block_bytes(DK, a.dv, C, !std::is_same<TIn, float>::value));
-        e = hipEventRecord(ss->fork, a.stream);
-        if (e == hipSuccess) e = hipStreamWaitEvent(ss->aux, ss->fork, 0);
-        ChunkArgs ap = a;
-        ap.stream = ss->aux;
-        for (int k = 0, c0 = 0; e == hipSuccess && c0 < NC; ++k, c0 += seg) {
-            ChunkMap m = map;
-            m.c0 = c0;
-            m.c1 = c0 + seg < NC ? c0 + seg : NC;
-            e = ap.scalar_gate ? launch_prep_t<TIn, DK, C, true>(ap, m, blocks, (long)a.N * (m.c1 - m.c0))
-                               : launch_prep_t<TIn, DK, C, false>(ap, m, blocks, (long)a.N * (m.c1 - m.c0));
-            if (e == hipSuccess) e = hipEventRecord(ss->seg[k], ss->aux);
-            if (e == hipSuccess) e = hipStreamWaitEvent(a.stream, ss->seg[k], 0);
-            if (e != hipSuccess) break;
-            ChunkArgs as = a;
-            as.S0 = c0 == 0 ? a.S0 : carry;
-            as.S_T = m.c1 == NC ? a.S_T : carry;
-            e = launch_state_t<TIn, DK, C>(as, m, blocks);
-        }
-        return e;
-    }
+    const long nch = chunk_count_bound(a.B, a.T, C, varlen, a.N);
     if (a.stages & 1) {
         if (varlen) {
             hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, (int32_t*)ws, a.N, C);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        hipError_t e = prep(map, chunk_count_bound(a.B, a.T, C, varlen, a.N));
-        if (e != hipSuccess) return e;
+        if (nch > 0) {
+            hipError_t e = a.scalar_gate ? launch_prep_t<TIn, DK, C, true>(a, map, blocks, nch)
+                                         : launch_prep_t<TIn, DK, C, false>(a, map, blocks, nch);
+            if (e != hipSuccess) return e;
+        }
     }
     if (a.stages & 2) return launch_state_t<TIn, DK, C>(a, map, blocks);
     return hipSuccess;
