@@ -427,6 +427,22 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     const TIn* gg = (const TIn*)p.gate;
     const TIn* gb = (const TIn*)p.beta;
 
+    // value rows of the chunk -> LDS, asynchronously and first, so that their
+    // latency overlaps that of the gate loads; rows past the chunk end fall
+    // outside the descriptor and arrive as zeros
+    {
+        const int rby = DV * (int)sizeof(TIn);            // bytes of one value row
+        const int lpr = rby / 16, rpi = 64 / lpr;          // lanes per row, rows per instruction
+        const uint32_t rowb = (uint32_t)H * (uint32_t)rby;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(gv + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * rowb + (uint32_t)rby);
+        const int ni = (C * rby + 1023) / 1024;
+        for (int u = w; u < ni; u += 4) {
+            const uint32_t voff = (uint32_t)(u * rpi + lane / lpr) * rowb + (uint32_t)(lane % lpr) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (__attribute__((address_space(3))) void*)(smem + SM::VST + (size_t)u * 1024), 16, voff, 0, 0, 0);
+        }
+    }
+
     // ---- gate phases: wave b owns tokens 16b..16b+15, lane owns CPL channels
     const bool gate_lane = (w < NBK) && (lane < ACT);
     const int b = w;
@@ -454,21 +470,6 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
         }
     }
     if (tid < C) s_beta[tid] = tid < n ? ld_in(gb + (size_t)(t0 + tid) * H + h) : 0.f;
-
-    // value rows of the chunk -> LDS, asynchronously; rows past the chunk end
-    // fall outside the descriptor and arrive as zeros
-    {
-        const int rby = DV * (int)sizeof(TIn);            // bytes of one value row
-        const int lpr = rby / 16, rpi = 64 / lpr;          // lanes per row, rows per instruction
-        const uint32_t rowb = (uint32_t)H * (uint32_t)rby;
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(gv + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * rowb + (uint32_t)rby);
-        const int ni = (C * rby + 1023) / 1024;
-        for (int u = w; u < ni; u += 4) {
-            const uint32_t voff = (uint32_t)(u * rpi + lane / lpr) * rowb + (uint32_t)(lane % lpr) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, (__attribute__((address_space(3))) void*)(smem + SM::VST + (size_t)u * 1024), 16, voff, 0, 0, 0);
-        }
-    }
 
     if (gate_lane) {
 #pragma unroll
@@ -2056,19 +2057,22 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
     for (int cg = cs; cg < ce; ++cg) {
         const long t0 = bos + (long)(cg - cs) * C;
         const int n = (int)min((long)C, eos - t0);
-        // first touch of chunk cg+2's shared operands by this slice's share of
-        // the lines, so that the slices of the (sequence, head) find them in
-        // L2. Issued before the loads below and consumed at the end of the
-        // iteration: waiting for it then does not wait for them.
+        // first touch of chunk cg+2: this slice's share of the shared operands'
+        // lines (so that the slices of the (sequence, head) find them in L2)
+        // and its own U~ lines. Issued before the loads below and consumed at
+        // the end of the iteration: waiting for it then does not wait for them.
         uint32_t tch;
         {
-            constexpr int L0 = (int)(L::BYTES / 128);
+            constexpr int L0 = (int)(L::BYTES / 128), LU = (int)(L::USL / 128);
             const int per = (L0 + nsl - 1) / nsl;
-            const int line = sl * per + q * 64 + lane;
-            const bool mine = cg + 2 < ce && q * 64 + lane < per && line < L0;
-            const __amdgpu_buffer_rsrc_t rt = make_rsrc(gblock(cg + 2 < ce ? cg + 2 : cg), (uint32_t)L::BYTES);
-            // lanes without a line point past the descriptor: no access, value 0
-            tch = __builtin_amdgcn_raw_buffer_load_b32(rt, mine ? line * 128 : (int)L::BYTES, 0, 0);
+            const int i = q * 64 + lane;
+            int off = (int)p.blk_bytes;   // past the descriptor: no access, value 0
+            if (cg + 2 < ce) {
+                if (i < per && sl * per + i < L0) off = (sl * per + i) * 128;
+                else if (i >= per && i < per + LU) off = (int)(L::BYTES + (size_t)sl * L::USL) + (i - per) * 128;
+            }
+            const __amdgpu_buffer_rsrc_t rt = make_rsrc(gblock(cg + 2 < ce ? cg + 2 : cg), (uint32_t)p.blk_bytes);
+            tch = __builtin_amdgcn_raw_buffer_load_b32(rt, off, 0, 0);
         }
         // operands of the next chunk (the last chunk reloads its own: a valid
         // block, never used)
@@ -2107,10 +2111,12 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) uq[e] = (float)op.ut[e] * op.iUc - ws[e];
         }
-        slice_load0(op, xn);
         lds_st<f32x4>((uint32_t)(SM::X_U + (size_t)q * 1024) + lfr, uq);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         if (lane == 0) lds_st<int>((uint32_t)SM::X_F + 4 * q, cg);
+        // issuing loads stalls this wave for a while: do it only once U is
+        // posted, while the other waves post theirs
+        slice_load0(op, xn);
         {
             extern __shared__ __align__(16) unsigned char smem[];
             typedef __attribute__((address_space(3))) const volatile int lds_flag_t;
@@ -2158,7 +2164,6 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ovv), ro, ovoff, (16 * q + e) * orow, 0);
             }
         }
-        slice_load1(op, xn);
 
         // ---- own state rows: S <- Diag(gamma_last) S + K_end^T U
 #pragma unroll
@@ -2169,8 +2174,10 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[c][e] = S[c][e] * op.g[c][e] + (k0[e] * c0 + k1[e] * c1);
         }
-        slice_load2(op, xn);
         make_s_frag();
+        // the rest of the next chunk's operands, once this wave's S is posted
+        slice_load1(op, xn);
+        slice_load2(op, xn);
         sink ^= tch;
         __syncthreads();
     }
