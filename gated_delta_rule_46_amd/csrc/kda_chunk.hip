@@ -2121,9 +2121,11 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
             extern __shared__ __align__(16) unsigned char smem[];
             typedef __attribute__((address_space(3))) const volatile int lds_flag_t;
             lds_flag_t* fl = (lds_flag_t*)(smem + SM::X_F);
+            // all four flags read before one wait (not one round trip each);
+            // no sleep: the waits are short
             for (int spin = 0; spin < (1 << 24); ++spin) {
-                if (fl[0] == cg && fl[1] == cg && fl[2] == cg && fl[3] == cg) break;
-                __builtin_amdgcn_s_sleep(1);
+                const int f0 = fl[0], f1 = fl[1], f2 = fl[2], f3 = fl[3];
+                if ((f0 == cg) & (f1 == cg) & (f2 == cg) & (f3 == cg)) break;
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
