@@ -21,6 +21,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     # packed fp32 VALU forms stay off (the compiler must not emit v_pk_* f32 ops)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs (no accumulator-register copies in the state walk)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"),
 ]

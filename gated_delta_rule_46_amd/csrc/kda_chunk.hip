@@ -64,7 +64,7 @@ __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOM
 
 // ------------------------------------------------------------------ one (chunk, head) block of the workspace
 
-enum { SC_W = 0, SC_Q = 1, SC_K = 2, SC_T = 3, SC_P = 4, SC_INV = 8 };
+enum { SC_W = 0, SC_Q = 1, SC_K = 2, SC_P = 3, SC_T = 4, SC_INV = 8 };   // W Q K P inverses: one 16-byte read
 
 template <int DK, int C, bool F32M>
 struct Lay {
@@ -1933,8 +1933,8 @@ __device__ __forceinline__ float ld_f1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // wave's instruction stream in one burst.
 struct SliceOps {
     f16x8 w[4], qg[4];            // group 0: W, Gamma o Q (first used)
-    f32x4 isc;                    //          inverse scales W Q K T
-    float iP, iUc;                //          inverse scale of P, of this U~ column
+    f32x4 isc;                    //          inverse scales of W, Gamma o Q, K_end^T, P
+    float iUc;                    //          inverse scale of this U~ column
     _Float16 __attribute__((ext_vector_type(4))) ut;   // U~ rows
     f16x8 ps[2];                  // group 1: strictly lower P
     f32x4 pd;                     //          P diagonal rows
@@ -1955,7 +1955,6 @@ __device__ __forceinline__ void slice_load0(SliceOps& o, const SliceSrc& x) {
 #pragma unroll
     for (int k = 0; k < KSD; ++k) o.qg[k] = ld_frag(x.r, (uint32_t)L::QG_OFF, x.q * KSD + k, x.lane);
     o.isc = ld_f4(x.r, (uint32_t)L::SC_OFF + 4 * SC_INV);
-    o.iP = ld_f1(x.r, (uint32_t)L::SC_OFF + 4 * (SC_INV + SC_P));
     o.iUc = ld_f1(x.r, (uint32_t)L::SU_OFF + 4 * (uint32_t)x.col);
     const uint32_t uo = (uint32_t)(L::BYTES + (size_t)x.slice * L::USL + L::u_off(x.q, x.lane));
     o.ut = __builtin_bit_cast(decltype(o.ut), __builtin_amdgcn_raw_buffer_load_b64(x.r, (int)uo, 0, 0));
@@ -2061,8 +2060,8 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         // lines (so that the slices of the (sequence, head) find them in L2)
         // and its own U~ lines. Issued before the loads below and consumed at
         // the end of the iteration: waiting for it then does not wait for them.
-        uint32_t tch;
-        {
+        uint32_t tch = 0;
+        if (q * 64 < (int)((L::BYTES / 128 + nsl - 1) / nsl + L::USL / 128)) {   // waves with lines to touch
             constexpr int L0 = (int)(L::BYTES / 128), LU = (int)(L::USL / 128);
             const int per = (L0 + nsl - 1) / nsl;
             const int i = q * 64 + lane;
@@ -2078,7 +2077,7 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         // block, never used)
         const int cn = cg + 1 < ce ? cg + 1 : cg;
         const SliceSrc xn = src(cn);
-        const float iW = op.isc[SC_W], iQ = op.isc[SC_Q], iK = op.isc[SC_K], iP = op.iP;
+        const float iW = op.isc[SC_W], iQ = op.isc[SC_Q], iK = op.isc[SC_K], iP = op.isc[SC_P];
 
         // ---- S over all channel steps (the other three from LDS)
         F sf[KSD];
