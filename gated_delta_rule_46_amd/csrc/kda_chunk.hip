@@ -518,15 +518,41 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
             f32x8 x[KSC];
             float mv = 0.f;
             const int col = 16 * sl + li;
+            if constexpr (!F32M && C >= 32) {
+                // transposing LDS reads: within each group of 16 lanes, lane
+                // i receives element i % 4 of the 4-element pieces that lanes
+                // i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4 address. Lane s of
+                // group g addresses row 32 ks + 16 hf + 4 g + s / 4, columns
+                // 16 sl + 4 (s % 4) ..+3, so lane (li, g) gets the column li
+                // values of rows kpos(g, 4 hf + 0..3): one B fragment half.
+                typedef short v4s __attribute__((ext_vector_type(4)));
+                const bool ok = sl < DV / 16;
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
+                for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
-                for (int pp = 0; pp < 8; ++pp) {
-                    const int t = 32 * ks + kpos(lg, pp);
-                    const float v = (sl < DV / 16 && t < C) ? ld_in(vst + t * DV + col) : 0.f;
-                    x[ks][pp] = v;
-                    mv = fmaxf(mv, fabsf(v));
-                }
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int row = 32 * ks + 16 * hf + 4 * lg + li / 4;
+                        const int cc = ok ? 16 * sl + 4 * (li % 4) : 0;
+                        const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4s*)(smem + SM::VST + (size_t)(row * DV + cc) * sizeof(TIn)));
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float v = ok ? bf16_bits_to_f32((uint16_t)r[j]) : 0.f;
+                            x[ks][4 * hf + j] = v;
+                            mv = fmaxf(mv, fabsf(v));
+                        }
+                    }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+                    for (int pp = 0; pp < 8; ++pp) {
+                        const int t = 32 * ks + kpos(lg, pp);
+                        const float v = (sl < DV / 16 && t < C) ? ld_in(vst + t * DV + col) : 0.f;
+                        x[ks][pp] = v;
+                        mv = fmaxf(mv, fabsf(v));
+                    }
+            }
             float sv = 1.f;
             if constexpr (!F32M) {
                 mv = colmax4(mv);

@@ -114,10 +114,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // ---------------------------------------------------------------- wave reductions
 
+// v from lane CTRL's DPP source within each row of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the wave, in every lane: within each row of 16 lanes by DPP
+// (swap neighbours, swap pairs, mirror halves of 8, mirror the row), then
+// across the four rows with colmax4; no LDS round trips.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
-    return v;
+    v = fmaxf(v, dpp_row<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_row<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_row<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_row<0x140>(v));   // row_mirror
+    return colmax4(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
