@@ -19,11 +19,14 @@
 //  * prep  -- one workgroup per (chunk, head), all chunks in parallel. Gate
 //    products, gated Gram matrices, the triangular inverse, U~ = T V, and the
 //    operands W, Gamma o Q, K_end^T, P written to a workspace as MFMA fragments.
-//  * state -- one wavefront per 16 value columns of one (sequence, head),
-//    up to four per workgroup. Walks the chunks of its sequence in order with its
-//    slice of S in fp32 MFMA accumulator registers, while copy wavefronts of
-//    the same workgroup stream the next chunk's operands into the other half
-//    of a double-buffered LDS area.
+//  * state -- walks the chunks of each sequence in order, per 16 value
+//    columns ("slice") of one (sequence, head), with that slice of S in fp32
+//    registers. bf16, dk = 128, chunk 64: four waves per slice, each holding a
+//    quarter of the state rows and loading its quarter of the chunk operands
+//    into registers one chunk ahead (one slice per workgroup while the slices
+//    fit one per CU; otherwise two slices per workgroup, with copy waves that
+//    stage the chunk operands in LDS). dk = 64: two waves per slice. Other
+//    cases: one wave per slice with copy waves.
 //
 // Gated Gram without overflow, with exact signs and zeros: every pair
 // (r > j) inside a chunk is separated at exactly one level of the binary
