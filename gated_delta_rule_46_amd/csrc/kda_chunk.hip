@@ -1087,6 +1087,20 @@ __global__ void __launch_bounds__(256, F32M ? 1 : 3) chunk_prep_kernel(PrepParam
 
 // ------------------------------------------------------------------ state kernel
 
+// Workgroup -> walker item (hs * nsg + sg: (sequence, head) hs, its part sg).
+// The nsg workgroups of one (sequence, head) read the same blocks, so they go
+// to one XCD (shared L2); consecutive (sequence, head) pairs go to different
+// XCDs, so that sequences of different lengths spread over the XCDs instead
+// of one XCD taking all the heads of the longest sequence. Workgroups are
+// dispatched round-robin over the XCDs (L % NXCD); when the pair count is not
+// a multiple of NXCD the items are spread as xcd_remap does.
+__device__ __forceinline__ int walker_item(int L, int total, int nsg) {
+    const int nhs = total / nsg;
+    if (nhs % NXCD != 0) return xcd_remap(L, total);
+    const int x = L % NXCD, r = L / NXCD;
+    return (NXCD * (r / nsg) + x) * nsg + r % nsg;
+}
+
 struct StateParams {
     const float* S0;
     float* o;
@@ -1161,7 +1175,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
     constexpr int NSL = SM::NSL;
     constexpr uint32_t FB = sizeof(F);   // bytes of one lane's fragment
 
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int item = walker_item(blockIdx.x, gridDim.x, p.NSG);
     const int sg = item % p.NSG;
     const int hs = item / p.NSG;
     const int H = p.H, DV = p.DV;
@@ -1457,7 +1471,7 @@ __global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams 
     constexpr int CH = L::CB / 2;          // 16-row state tiles per wave
     constexpr int NCW = 2 * NP;            // compute waves
 
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int item = walker_item(blockIdx.x, gridDim.x, p.NSG);
     const int sg = item % p.NSG;
     const int hs = item / p.NSG;
     const int H = p.H, DV = p.DV;
@@ -1923,7 +1937,7 @@ __device__ __forceinline__ void quad_walk(const StateParams& p, int item) {
 
 template <int NS>
 __global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams p) {
-    quad_walk<NS>(p, xcd_remap(blockIdx.x, gridDim.x));
+    quad_walk<NS>(p, walker_item(blockIdx.x, gridDim.x, p.NSG));
 }
 
 // ------------------------------------------------------------------ slice walker
@@ -2222,7 +2236,7 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
 }
 
 __global__ void __launch_bounds__(256) chunk_state_slice_kernel(StateParams p) {
-    slice_walk(p, xcd_remap(blockIdx.x, gridDim.x));
+    slice_walk(p, walker_item(blockIdx.x, gridDim.x, p.NSG));
 }
 
 // ------------------------------------------------------------------ host side
