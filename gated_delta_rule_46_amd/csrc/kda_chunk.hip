@@ -2064,18 +2064,16 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         for (int e = 0; e < 4; ++e)
             S[c][e] = p.S0 ? p.S0[sbase + (size_t)(16 * (2 * q + c) + 4 * lg + e) * DV + col] : 0.f;
 
-    F sfo;
-    float iSo = 1.f;
+    // own channel step of S as an fp16 fragment and its inverse column
+    // scales, posted for all four waves
     auto make_s_frag = [&]() {
-        float m = 0.f;
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[c][e]));
+        float m = fmaxf(fmaxf(fabsf(S[0][0]), fabsf(S[0][1])), fabsf(S[0][2]));
+        m = fmaxf(fmaxf(m, fabsf(S[0][3])), fabsf(S[1][0]));
+        m = fmaxf(fmaxf(m, fabsf(S[1][1])), fabsf(S[1][2]));
+        m = fmaxf(m, fabsf(S[1][3]));
         m = colmax4(m);
-        const float sc = pow2_scale_for(m);
-        iSo = pow2_inv_scale_for(m);
-        sfo = to_f16x8(dtiles_to_frag(S[0], S[1]), sc);
+        const float iSo = pow2_inv_scale_for(m);
+        const F sfo = to_f16x8(dtiles_to_frag(S[0], S[1]), pow2_scale_for(m));
         lds_st<F>((uint32_t)(SM::X_S + (size_t)q * 1024) + lfr, sfo);
         if (lg == 0) lds_st<float>((uint32_t)SM::X_SI + 4 * (16 * q + li), iSo);
     };
@@ -2122,18 +2120,15 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         const SliceSrc xn = src(cn);
         const float iW = op.isc[SC_W], iQ = op.isc[SC_Q], iK = op.isc[SC_K], iP = op.isc[SC_P];
 
-        // ---- S over all channel steps (the other three from LDS)
+        // ---- S over all channel steps, read back from LDS (this wave's own
+        // step too: one more read in parallel costs less than selecting it)
         F sf[KSD];
         float iS[KSD];
 #pragma unroll
         for (int k = 0; k < KSD; ++k) {
-            if (k == q) continue;
             sf[k] = lds_ld<F>((uint32_t)(SM::X_S + (size_t)k * 1024) + lfr);
             iS[k] = lds_ld<float>((uint32_t)SM::X_SI + 4 * (16 * k + li));
         }
-#pragma unroll
-        for (int k = 0; k < KSD; ++k)
-            if (k == q) { sf[k] = sfo; iS[k] = iSo; }
 
         // ---- own token rows rb = q:  u = U~ - W S,  O = (Gamma o Q) S
         f32x4 uq, ov = zero4();
@@ -2173,16 +2168,18 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         f32x4 u[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = r == q ? uq : lds_ld<f32x4>((uint32_t)(SM::X_U + (size_t)r * 1024) + lfr);
+        for (int r = 0; r < 4; ++r) u[r] = lds_ld<f32x4>((uint32_t)(SM::X_U + (size_t)r * 1024) + lfr);
 
         // ---- U over the two token steps, one scale per (step, column)
         F uf[KSC];
         float iU[KSC];
 #pragma unroll
         for (int t = 0; t < KSC; ++t) {
-            float m = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(u[2 * t][e]), fabsf(u[2 * t + 1][e])));
+            const f32x4 a = u[2 * t], c = u[2 * t + 1];
+            float m = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fabsf(a[2]));
+            m = fmaxf(fmaxf(m, fabsf(a[3])), fabsf(c[0]));
+            m = fmaxf(fmaxf(m, fabsf(c[1])), fabsf(c[2]));
+            m = fmaxf(m, fabsf(c[3]));
             m = colmax4(m);
             iU[t] = pow2_inv_scale_for(m);
             uf[t] = to_f16x8(dtiles_to_frag(u[2 * t], u[2 * t + 1]), pow2_scale_for(m));
