@@ -2067,11 +2067,7 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
     // own channel step of S as an fp16 fragment and its inverse column
     // scales, posted for all four waves
     auto make_s_frag = [&]() {
-        float m = fmaxf(fmaxf(fabsf(S[0][0]), fabsf(S[0][1])), fabsf(S[0][2]));
-        m = fmaxf(fmaxf(m, fabsf(S[0][3])), fabsf(S[1][0]));
-        m = fmaxf(fmaxf(m, fabsf(S[1][1])), fabsf(S[1][2]));
-        m = fmaxf(m, fabsf(S[1][3]));
-        m = colmax4(m);
+        const float m = colmax4(absmax8(S[0], S[1]));
         const float iSo = pow2_inv_scale_for(m);
         const F sfo = to_f16x8(dtiles_to_frag(S[0], S[1]), pow2_scale_for(m));
         lds_st<F>((uint32_t)(SM::X_S + (size_t)q * 1024) + lfr, sfo);
@@ -2175,12 +2171,7 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         float iU[KSC];
 #pragma unroll
         for (int t = 0; t < KSC; ++t) {
-            const f32x4 a = u[2 * t], c = u[2 * t + 1];
-            float m = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fabsf(a[2]));
-            m = fmaxf(fmaxf(m, fabsf(a[3])), fabsf(c[0]));
-            m = fmaxf(fmaxf(m, fabsf(c[1])), fabsf(c[2]));
-            m = fmaxf(m, fabsf(c[3]));
-            m = colmax4(m);
+            const float m = colmax4(absmax8(u[2 * t], u[2 * t + 1]));
             iU[t] = pow2_inv_scale_for(m);
             uf[t] = to_f16x8(dtiles_to_frag(u[2 * t], u[2 * t + 1]), pow2_scale_for(m));
         }

@@ -49,15 +49,31 @@ __device__ __forceinline__ int scale_exp(float m) {
 __device__ __forceinline__ float pow2_scale_for(float m) { return __uint_as_float((uint32_t)(253 - scale_exp(m)) << 23); }
 __device__ __forceinline__ float pow2_inv_scale_for(float m) { return __uint_as_float((uint32_t)(scale_exp(m) + 1) << 23); }
 
+// max(|a|, |b|, |c|) in one instruction (the compiler does not always fuse
+// the chains itself)
+__device__ __forceinline__ float absmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// Largest |x| over the eight values of two D-tile quads.
+__device__ __forceinline__ float absmax8(const f32x4& a, const f32x4& b) {
+    float m = absmax3(a[0], a[1], a[2]);
+    m = absmax3(m, a[3], b[0]);
+    m = absmax3(m, b[1], b[2]);
+    return absmax3(m, b[3], b[3]);
+}
+
 // Largest value over the four lanes that hold one column of a 16x16 D tile
-// (lanes i, i+16, i+32, i+48): two lane-swap steps, no LDS round trip.
+// (lanes i, i+16, i+32, i+48): two lane-swap steps, no LDS round trip. For
+// v >= +0 (maxima of |x|, the only use): non-negative floats order as their
+// bit patterns, so integer maxima do it without float canonicalisation.
 __device__ __forceinline__ float colmax4(float v) {
     const uint32_t u = __float_as_uint(v);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const uint32_t u2 = __float_as_uint(m);
-    const auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    const uint32_t m = a[0] > a[1] ? a[0] : a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return __uint_as_float(b[0] > b[1] ? b[0] : b[1]);
 }
 
 // ---------------------------------------------------------------- MFMA
@@ -116,19 +132,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // v from lane CTRL's DPP source within each row of 16 lanes
 template <int CTRL>
-__device__ __forceinline__ float dpp_row(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_row(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// Maximum over the wave, in every lane: within each row of 16 lanes by DPP
-// (swap neighbours, swap pairs, mirror halves of 8, mirror the row), then
-// across the four rows with colmax4; no LDS round trips.
+// Maximum over the wave of v >= +0 (maxima of |x|), in every lane: within
+// each row of 16 lanes by DPP (swap neighbours, swap pairs, mirror halves of
+// 8, mirror the row), then across the four rows with colmax4; integer maxima
+// on the bit patterns, no LDS round trips.
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_row<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_row<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_row<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp_row<0x140>(v));   // row_mirror
-    return colmax4(v);
+    uint32_t u = __float_as_uint(v), t;
+    t = dpp_row<0xB1>(u);  u = u > t ? u : t;   // quad_perm [1,0,3,2]
+    t = dpp_row<0x4E>(u);  u = u > t ? u : t;   // quad_perm [2,3,0,1]
+    t = dpp_row<0x141>(u); u = u > t ? u : t;   // row_half_mirror
+    t = dpp_row<0x140>(u); u = u > t ? u : t;   // row_mirror
+    return colmax4(__uint_as_float(u));
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
