@@ -28,9 +28,16 @@ FLAGS = [
 ]
 
 
+# Per-source additions. The chunk kernels are bound by dependent chains and
+# schedule better for latency (3-6% faster on every forward configuration);
+# the streaming decode kernel loses 17% with that schedule, so it keeps the
+# default.
+EXTRA = {"kda_chunk.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
