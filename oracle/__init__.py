@@ -5,8 +5,9 @@ benchmark's CPU-baseline leg, never by the product path. It shares no code with
 the HIP kernels.
 
 * ``recurrence`` -- the token-by-token recurrence in plain C (``kda_oracle.c``),
-  fp64, OpenMP over independent (sequence, head) pairs.
+  fp64, OpenMP over independent (sequence, head) pairs, and its reverse-mode
+  gradient (``bwd``).
 * ``dense`` -- a second, independent formulation for tiny inputs: explicit
   dense transition matrices and their products.
 """
-from .recurrence import build, fwd, decode_step, fwd_heads, threads  # noqa: F401
+from .recurrence import build, bwd, fwd, decode_step, fwd_heads, threads  # noqa: F401
