@@ -102,6 +102,63 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate,
                                N, dtype, gate_kind, workspace, workspace_bytes, stream);
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int N, int has_cu) {
+    if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk) || !size_ok(dv)) return 0;
+    if (has_cu && (B != 1 || N <= 0)) return 0;
+    return kda::bwd_workspace_bytes(B, H, T, dk, dv, has_cu != 0, has_cu ? N : B);
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                  const float* S0, const float* dO, const float* dS_T, float* grad_q, float* grad_k,
+                  float* grad_v, float* grad_gate, float* grad_beta, float* grad_S0, int B, int H, int T,
+                  int dk, int dv, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (B <= 0 || H <= 0 || T < 0) return KDA_EINVAL;
+    if (!size_ok(dk) || !size_ok(dv)) return KDA_ENOTSUP;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ENOTSUP;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return KDA_ENOTSUP;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen) {
+        if (B != 1 || N <= 0) return KDA_EINVAL;
+    } else {
+        if (N != 0 && N != B) return KDA_EINVAL;
+        N = B;
+    }
+    const bool need_data = T > 0;
+    if (need_data && (!q || !k || !v || !gate || !beta || !dO || !grad_q || !grad_k || !grad_v || !grad_gate ||
+                      !grad_beta))
+        return KDA_EINVAL;
+    const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (need_data && (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(gate, es) ||
+                      !aligned(beta, es) || !aligned(dO) || !aligned(grad_q, 4) || !aligned(grad_k, 4) ||
+                      !aligned(grad_v) || !aligned(grad_gate, 4) || !aligned(grad_beta, 4)))
+        return KDA_EALIGN;
+    if ((S0 && !aligned(S0)) || (dS_T && !aligned(dS_T)) || (grad_S0 && !aligned(grad_S0)) ||
+        (workspace && !aligned(workspace)))
+        return KDA_EALIGN;
+    if (varlen && !aligned(cu_seqlens, 4)) return KDA_EALIGN;
+    const size_t need = kda::bwd_workspace_bytes(B, H, T, dk, dv, varlen, N);
+    if (workspace && workspace_bytes < need) return KDA_EINVAL;
+    if (!need_data && !grad_S0) return KDA_OK;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    bool owned = false;
+    if (!ws && need > 0) {
+        hipError_t e = hipMallocAsync(&ws, need, st);
+        if (e != hipSuccess) return hip_status(e);
+        owned = true;
+    }
+    kda::BwdArgs a{q, k, v, gate, beta, S0, dO, dS_T, grad_q, grad_k, grad_v, grad_gate, grad_beta, grad_S0,
+                   B, H, T, dk, dv, cu_seqlens, N, dtype == KDA_BF16, gate_kind == KDA_GATE_SCALAR, ws, st};
+    hipError_t e = kda::launch_chunk_bwd(a);
+    if (owned) {
+        hipError_t f = hipFreeAsync(ws, st);
+        if (e == hipSuccess) e = f;
+    }
+    return hip_status(e);
+}
+
 int kda_decode_step(const void* q, const void* k, const void* v, const void* gate, const void* beta,
                     float* S, float* o, int N, int H, int dk, int dv, int dtype, int gate_kind, void* stream) {
     if (N <= 0 || H <= 0) return KDA_EINVAL;

@@ -1,0 +1,544 @@
+// Gradient of the gated delta-rule forward over whole sequences.
+//
+// Forward, per (sequence, head), state S in R^{dk x dv} (Complex KDA summary,
+// background "diagonal-plus-rank-one transitions"; delta form of the CyFA blog
+// post, section 2.2, gate first):
+//   S' = Diag(alpha_t) S_{t-1};  pred = S'^T k_t;  u = beta_t (v_t - pred)
+//   S_t = S' + k_t u^T;          o_t = S_t^T q_t
+// With dS = dL/dS_t (dS_T, or zero, before the last token), the adjoint of
+// one token, last token first:
+//   dS += q dO^T                 dq = S_t dO
+//   du = dS^T k                  dk = dS u + S' dpred,   dpred = -beta du
+//   dbeta = du . (v - pred)      dv = beta du
+//   dS' = dS + k dpred^T         dalpha_i = sum_j dS'_ij S_{t-1,ij}
+//   dS  = Diag(alpha) dS'        (dL/dS_{t-1}; after the first token: dS0)
+// The pages measure forward-plus-backward throughput of this family (Complex
+// KDA summary, efficiency) without printing the backward; the lines above
+// are the chain rule applied to the forward, nothing more.
+//
+// Value columns of S never mix (the transition acts on the key side only),
+// so each wave owns COLS value columns and all dk rows of S and dS: lane l
+// holds rows l + 64 m. A column sum over the rows (pred, du) is then a
+// wave-wide sum (DPP inside rows of 16 lanes, lane swaps across rows), with
+// no barrier; only dq, dk and dalpha (sums over value columns) cross waves,
+// through LDS atomics, and workgroups, through per-workgroup partial sums
+// that a second kernel adds up.
+//
+// Pass A runs the forward from S0 and stores S at the start of every
+// SUB-token block (the checkpoints). Pass B walks the blocks backwards:
+// reload the checkpoint, replay the block forward keeping the SUB states
+// S_{t-1} in registers, then the adjoint over the block. Each block's
+// inputs are staged in LDS once, fetched one block ahead; one barrier per
+// block. All arithmetic is fp32 (inputs converted exactly).
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int BW_SUB = 8;   // tokens per checkpoint interval
+
+// Sum over the 64 lanes, the same bits in every lane: DPP add steps inside
+// each row of 16 lanes (swap neighbours, swap pairs, mirror halves of 8,
+// mirror the row), then the lane swaps across rows. Every step adds a value
+// to its partner's in both lanes, so all lanes round identically.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_allsum(float v) {
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    v = dpp_add<0x141>(v);
+    v = dpp_add<0x140>(v);
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t u2 = __float_as_uint(v);
+    const auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+struct BwdParams {
+    const void *q, *k, *v, *gate, *beta;
+    const float *S0, *dO, *dST;
+    float *dv_out, *dS0, *ckpt, *part;
+    const int32_t* cu;
+    int H, T, dv, ncg;
+    long nblk;   // checkpoint slots per (head, column group)
+    long rows;   // B * T * H
+};
+
+template <int DK, int NC, bool SG>
+struct BwdStage {
+    float k[BW_SUB][DK], q[BW_SUB][DK], a[BW_SUB][SG ? 1 : DK];
+    float v[BW_SUB][NC], dO[BW_SUB][NC], b[BW_SUB];
+};
+
+template <int DK, int NC, bool SG>
+struct BwdLds {
+    BwdStage<DK, NC, SG> st[2];
+    float acc[2][BW_SUB][3][DK];   // dq, dk, dalpha partial sums over this workgroup's columns
+    float accb[2][BW_SUB];         // dbeta partial sums
+};
+
+// One block's inputs, fetched into registers one block ahead, then written
+// to LDS. Element e = tid + NT i of the [SUB][DK] key-side arrays and of the
+// [SUB][NC] value-side arrays; entries past the sequence end are zero.
+template <class TIn, int DK, int NC, int NT, int RPL, int COLS, bool SG, bool BWD>
+struct BwdFetch {
+    static constexpr int KPT = (BW_SUB * DK + NT - 1) / NT;
+    static constexpr int VPT = (BW_SUB * NC + NT - 1) / NT;
+    float k[KPT], q[BWD ? KPT : 1], a[SG ? 1 : KPT], v[VPT], dO[BWD ? VPT : 1], b, ag;
+    f32x4 ck[BWD ? RPL * COLS / 4 : 1];   // this lane's part of the block's checkpoint
+
+    __device__ __forceinline__ void fetch(const BwdParams& p, int tid, int b0, int h, int ts, int te, int cw0,
+                                          const float* ckp) {
+        const TIn* K = (const TIn*)p.k;
+        const TIn* Q = (const TIn*)p.q;
+        const TIn* A = (const TIn*)p.gate;
+        const TIn* V = (const TIn*)p.v;
+        const TIn* Bt = (const TIn*)p.beta;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int e = tid + NT * i, j = e / DK, r = e % DK, t = ts + j;
+            const bool ok = e < BW_SUB * DK && t < te;
+            const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
+            k[i] = ok ? ld_in(K + row * DK + r) : 0.f;
+            if (BWD) q[i] = ok ? ld_in(Q + row * DK + r) : 0.f;
+            if (!SG) a[i] = ok ? ld_in(A + row * DK + r) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int e = tid + NT * i, j = e / NC, c = e % NC, t = ts + j;
+            const bool ok = e < BW_SUB * NC && t < te;
+            const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
+            v[i] = ok ? ld_in(V + row * p.dv + cw0 + c) : 0.f;
+            if (BWD) dO[i] = ok ? p.dO[row * p.dv + cw0 + c] : 0.f;
+        }
+        {
+            const int t = ts + tid;
+            const bool ok = tid < BW_SUB && t < te;
+            const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
+            b = ok ? ld_in(Bt + row) : 0.f;
+            ag = (SG && ok) ? ld_in(A + row) : 0.f;
+        }
+        if (BWD) {
+            const f32x4* c4 = reinterpret_cast<const f32x4*>(ckp);
+#pragma unroll
+            for (int m = 0; m < RPL * COLS / 4; ++m) ck[m] = c4[m];
+        }
+    }
+
+    __device__ __forceinline__ void store(BwdStage<DK, NC, SG>& s, int tid) const {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int e = tid + NT * i;
+            if (e < BW_SUB * DK) {
+                (&s.k[0][0])[e] = k[i];
+                if (BWD) (&s.q[0][0])[e] = q[i];
+                if (!SG) (&s.a[0][0])[e] = a[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int e = tid + NT * i;
+            if (e < BW_SUB * NC) {
+                (&s.v[0][0])[e] = v[i];
+                if (BWD) (&s.dO[0][0])[e] = dO[i];
+            }
+        }
+        if (tid < BW_SUB) {
+            s.b[tid] = b;
+            if (SG) s.a[tid][0] = ag;
+        }
+    }
+};
+
+template <class TIn, int DK, int NWV, int COLS, bool SG>
+__global__ void __launch_bounds__(NWV * WAVE)
+chunk_bwd_kernel(BwdParams p) {
+    constexpr int NT = NWV * WAVE, NC = NWV * COLS, SUB = BW_SUB;
+    constexpr int RPL = DK >= WAVE ? DK / WAVE : 1;        // state rows per lane
+    constexpr int CKF = NT * RPL * COLS;                    // floats per checkpoint slot
+    static_assert(COLS % 4 == 0, "float4 column groups");
+    __shared__ BwdLds<DK, NC, SG> L;
+
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int cg = blockIdx.x % p.ncg, pair = blockIdx.x / p.ncg;
+    const int s = pair / p.H, h = pair % p.H;
+    int t0, t1, b0;
+    long base;
+    if (p.cu) {
+        t0 = p.cu[s];
+        t1 = p.cu[s + 1];
+        b0 = 0;
+        base = t0 / SUB + s;
+    } else {
+        t0 = 0;
+        t1 = p.T;
+        b0 = s;
+        base = (long)s * ((p.T + SUB - 1) / SUB);
+    }
+    const int nb = (t1 - t0 + SUB - 1) / SUB;
+    const int cw0 = cg * NC, c0 = cw0 + w * COLS;          // first column of the workgroup / of this wave
+    float* ck = p.ckpt + ((size_t)(h * p.ncg + cg) * p.nblk + base) * CKF + (size_t)tid * RPL * COLS;
+    const size_t sbase = (size_t)(s * p.H + h) * DK * p.dv;
+
+    for (int e = tid; e < 2 * SUB * 3 * DK; e += NT) (&L.acc[0][0][0][0])[e] = 0.f;
+    if (tid < 2 * SUB) (&L.accb[0][0])[tid] = 0.f;
+
+    bool rv[RPL];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) rv[m] = lane + WAVE * m < DK;
+
+    float S[RPL][COLS];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        const int r = lane + WAVE * m;
+#pragma unroll
+        for (int c4 = 0; c4 < COLS / 4; ++c4) {
+            f32x4 x = zero4();
+            if (p.S0 && rv[m]) x = *reinterpret_cast<const f32x4*>(p.S0 + sbase + (size_t)r * p.dv + c0 + 4 * c4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) S[m][4 * c4 + c] = x[c];
+        }
+    }
+
+    // ------------------------------------------------ pass A: forward, checkpoints
+    {
+        BwdFetch<TIn, DK, NC, NT, RPL, COLS, SG, false> f;
+        if (nb > 0) f.fetch(p, tid, b0, h, t0, t1, cw0, nullptr);
+        for (int blk = 0; blk < nb; ++blk) {
+            BwdStage<DK, NC, SG>& st = L.st[blk & 1];
+            f.store(st, tid);
+            __syncthreads();
+            const int ts = t0 + blk * SUB;
+            if (blk + 1 < nb) f.fetch(p, tid, b0, h, ts + SUB, t1, cw0, nullptr);
+            f32x4* cp = reinterpret_cast<f32x4*>(ck + (size_t)blk * CKF);
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int c4 = 0; c4 < COLS / 4; ++c4)
+                    cp[m * (COLS / 4) + c4] = f32x4{S[m][4 * c4], S[m][4 * c4 + 1], S[m][4 * c4 + 2], S[m][4 * c4 + 3]};
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) {
+                if (ts + j < t1) {
+                    float kr[RPL], part[COLS];
+#pragma unroll
+                    for (int m = 0; m < RPL; ++m) {
+                        const int r = rv[m] ? lane + WAVE * m : 0;
+                        kr[m] = rv[m] ? st.k[j][r] : 0.f;
+                        const float a = SG ? st.a[j][0] : (rv[m] ? st.a[j][r] : 0.f);
+#pragma unroll
+                        for (int c = 0; c < COLS; ++c) S[m][c] *= a;
+                    }
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) {
+                        float x = 0.f;
+#pragma unroll
+                        for (int m = 0; m < RPL; ++m) x = fmaf(S[m][c], kr[m], x);
+                        part[c] = wave_allsum(x);
+                    }
+                    const float bt = st.b[j];
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) {
+                        const float u = bt * (st.v[j][w * COLS + c] - part[c]);
+#pragma unroll
+                        for (int m = 0; m < RPL; ++m) S[m][c] = fmaf(kr[m], u, S[m][c]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------ pass B: adjoint, blocks in reverse
+    float dS[RPL][COLS];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        const int r = lane + WAVE * m;
+#pragma unroll
+        for (int c4 = 0; c4 < COLS / 4; ++c4) {
+            f32x4 x = zero4();
+            if (p.dST && rv[m]) x = *reinterpret_cast<const f32x4*>(p.dST + sbase + (size_t)r * p.dv + c0 + 4 * c4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dS[m][4 * c4 + c] = x[c];
+        }
+    }
+    const size_t nrk = (size_t)p.rows * DK;
+    auto flush = [&](int fb) {   // partial sums of block fb (its accumulator half) to memory, then zero them
+        const int ts = t0 + fb * SUB;
+        float(*acc)[3][DK] = L.acc[fb & 1];
+        for (int e = tid; e < SUB * 3 * DK; e += NT) {
+            const int j = e / (3 * DK), rem = e % (3 * DK), qty = rem / DK, i = rem % DK, t = ts + j;
+            if (t < t1) {
+                const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
+                p.part[((size_t)cg * 3 + qty) * nrk + row * DK + i] = acc[j][qty][i];
+            }
+            acc[j][qty][i] = 0.f;
+        }
+        if (tid < SUB) {
+            const int t = ts + tid;
+            if (t < t1) {
+                const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
+                p.part[(size_t)p.ncg * 3 * nrk + (size_t)cg * p.rows + row] = L.accb[fb & 1][tid];
+            }
+            L.accb[fb & 1][tid] = 0.f;
+        }
+    };
+    {
+        BwdFetch<TIn, DK, NC, NT, RPL, COLS, SG, true> f;
+        if (nb > 0) f.fetch(p, tid, b0, h, t0 + (nb - 1) * SUB, t1, cw0, ck + (size_t)(nb - 1) * CKF);
+        for (int blk = nb - 1; blk >= 0; --blk) {
+            BwdStage<DK, NC, SG>& st = L.st[blk & 1];
+            f.store(st, tid);
+            float Sb[RPL][COLS];
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int c = 0; c < COLS; ++c) Sb[m][c] = f.ck[m * (COLS / 4) + c / 4][c % 4];
+            __syncthreads();
+            if (blk + 1 < nb) flush(blk + 1);
+            const int ts = t0 + blk * SUB;
+            if (blk > 0) f.fetch(p, tid, b0, h, ts - SUB, t1, cw0, ck + (size_t)(blk - 1) * CKF);
+
+            // replay the block forward, keeping S_{t-1} for every token
+            float Sh[SUB][RPL][COLS];
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) {
+#pragma unroll
+                for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) Sh[j][m][c] = Sb[m][c];
+                if (j + 1 < SUB && ts + j + 1 < t1) {
+                    float kr[RPL], part[COLS];
+#pragma unroll
+                    for (int m = 0; m < RPL; ++m) {
+                        const int r = rv[m] ? lane + WAVE * m : 0;
+                        kr[m] = rv[m] ? st.k[j][r] : 0.f;
+                        const float a = SG ? st.a[j][0] : (rv[m] ? st.a[j][r] : 0.f);
+#pragma unroll
+                        for (int c = 0; c < COLS; ++c) Sb[m][c] *= a;
+                    }
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) {
+                        float x = 0.f;
+#pragma unroll
+                        for (int m = 0; m < RPL; ++m) x = fmaf(Sb[m][c], kr[m], x);
+                        part[c] = wave_allsum(x);
+                    }
+                    const float bt = st.b[j];
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) {
+                        const float u = bt * (st.v[j][w * COLS + c] - part[c]);
+#pragma unroll
+                        for (int m = 0; m < RPL; ++m) Sb[m][c] = fmaf(kr[m], u, Sb[m][c]);
+                    }
+                }
+            }
+
+            float(*acc)[3][DK] = L.acc[blk & 1];
+#pragma unroll
+            for (int j = SUB - 1; j >= 0; --j) {
+                if (ts + j < t1) {
+                    float kr[RPL], qr[RPL], ar[RPL], oo[COLS], vv[COLS];
+#pragma unroll
+                    for (int m = 0; m < RPL; ++m) {
+                        const int r = rv[m] ? lane + WAVE * m : 0;
+                        kr[m] = rv[m] ? st.k[j][r] : 0.f;
+                        qr[m] = rv[m] ? st.q[j][r] : 0.f;
+                        ar[m] = SG ? st.a[j][0] : (rv[m] ? st.a[j][r] : 0.f);
+                    }
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) {
+                        oo[c] = st.dO[j][w * COLS + c];
+                        vv[c] = st.v[j][w * COLS + c];
+                    }
+                    const float bt = st.b[j];
+                    float Sp[RPL][COLS], pred[COLS], du[COLS];
+#pragma unroll
+                    for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                        for (int c = 0; c < COLS; ++c) {
+                            Sp[m][c] = ar[m] * Sh[j][m][c];
+                            dS[m][c] = fmaf(qr[m], oo[c], dS[m][c]);
+                        }
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) {
+                        float x = 0.f, y = 0.f;
+#pragma unroll
+                        for (int m = 0; m < RPL; ++m) {
+                            x = fmaf(Sp[m][c], kr[m], x);
+                            y = fmaf(dS[m][c], kr[m], y);
+                        }
+                        pred[c] = wave_allsum(x);
+                        du[c] = wave_allsum(y);
+                    }
+                    float u[COLS], dpred[COLS], dbt = 0.f;
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) {
+                        const float e = vv[c] - pred[c];
+                        u[c] = bt * e;
+                        dpred[c] = -bt * du[c];
+                        dbt = fmaf(du[c], e, dbt);
+                    }
+#pragma unroll
+                    for (int m = 0; m < RPL; ++m) {
+                        float gq = 0.f, gk = 0.f, ga = 0.f;
+#pragma unroll
+                        for (int c = 0; c < COLS; ++c) {
+                            gq = fmaf(fmaf(kr[m], u[c], Sp[m][c]), oo[c], gq);
+                            gk = fmaf(dS[m][c], u[c], gk);
+                            gk = fmaf(Sp[m][c], dpred[c], gk);
+                            const float dsp = fmaf(kr[m], dpred[c], dS[m][c]);
+                            ga = fmaf(dsp, Sh[j][m][c], ga);
+                            dS[m][c] = ar[m] * dsp;
+                        }
+                        if (rv[m]) {
+                            const int r = lane + WAVE * m;
+                            atomicAdd(&acc[j][0][r], gq);
+                            atomicAdd(&acc[j][1][r], gk);
+                            atomicAdd(&acc[j][2][r], ga);
+                        }
+                    }
+                    if (lane == 0) {
+                        atomicAdd(&L.accb[blk & 1][j], dbt);
+                        const size_t row = ((size_t)b0 * p.T + ts + j) * p.H + h;
+                        f32x4* dvp = reinterpret_cast<f32x4*>(p.dv_out + row * p.dv + c0);
+#pragma unroll
+                        for (int c4 = 0; c4 < COLS / 4; ++c4)
+                            dvp[c4] = f32x4{bt * du[4 * c4], bt * du[4 * c4 + 1], bt * du[4 * c4 + 2],
+                                            bt * du[4 * c4 + 3]};
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (nb > 0) flush(0);
+    if (p.dS0) {
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            if (!rv[m]) continue;
+            const int r = lane + WAVE * m;
+#pragma unroll
+            for (int c4 = 0; c4 < COLS / 4; ++c4)
+                *reinterpret_cast<f32x4*>(p.dS0 + sbase + (size_t)r * p.dv + c0 + 4 * c4) =
+                    f32x4{dS[m][4 * c4], dS[m][4 * c4 + 1], dS[m][4 * c4 + 2], dS[m][4 * c4 + 3]};
+        }
+    }
+}
+
+// Sums the per-workgroup partials: dq, dk, dalpha per (token, head, channel)
+// and dbeta per (token, head); the scalar gate's gradient also sums over
+// the channels.
+__global__ void __launch_bounds__(256)
+chunk_bwd_reduce_kernel(const float* __restrict__ part, long rows, int dk, int ncg, bool sg,
+                        float* __restrict__ dq, float* __restrict__ dkg, float* __restrict__ dg,
+                        float* __restrict__ db) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    const long n = rows * dk;
+    if (e < n) {
+        float a = 0.f, b = 0.f, c = 0.f;
+        for (int g = 0; g < ncg; ++g) {
+            a += part[(size_t)(3 * g) * n + e];
+            b += part[(size_t)(3 * g + 1) * n + e];
+            if (!sg) c += part[(size_t)(3 * g + 2) * n + e];
+        }
+        dq[e] = a;
+        dkg[e] = b;
+        if (!sg) dg[e] = c;
+    }
+    if (e < rows) {
+        float x = 0.f;
+        for (int g = 0; g < ncg; ++g) x += part[(size_t)3 * ncg * n + (size_t)g * rows + e];
+        db[e] = x;
+        if (sg) {
+            float y = 0.f;
+            for (int g = 0; g < ncg; ++g)
+                for (int i = 0; i < dk; ++i) y += part[(size_t)(3 * g + 2) * n + (size_t)e * dk + i];
+            dg[e] = y;
+        }
+    }
+}
+
+int bwd_waves(int dv) { return dv >= 32 ? 4 : 2; }
+constexpr int BW_COLS = 8;
+
+template <class TIn, int DK, int NWV, bool SG>
+hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p) {
+    hipLaunchKernelGGL((chunk_bwd_kernel<TIn, DK, NWV, BW_COLS, SG>), dim3(a.N * a.H * p.ncg), dim3(NWV * WAVE), 0,
+                       a.stream, p);
+    return hipGetLastError();
+}
+
+template <class TIn, int DK, bool SG>
+hipError_t launch_bwd_w(const BwdArgs& a, const BwdParams& p) {
+    return bwd_waves(a.dv) == 4 ? launch_bwd_t<TIn, DK, 4, SG>(a, p) : launch_bwd_t<TIn, DK, 2, SG>(a, p);
+}
+
+template <class TIn, bool SG>
+hipError_t launch_bwd_dk(const BwdArgs& a, const BwdParams& p) {
+    switch (a.dk) {
+        case 16: return launch_bwd_w<TIn, 16, SG>(a, p);
+        case 32: return launch_bwd_w<TIn, 32, SG>(a, p);
+        case 64: return launch_bwd_w<TIn, 64, SG>(a, p);
+        default: return launch_bwd_w<TIn, 128, SG>(a, p);
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+long bwd_slots(int B, int T, bool varlen, int N) {
+    return varlen ? (long)T / BW_SUB + N : (long)B * ((T + BW_SUB - 1) / BW_SUB);
+}
+
+size_t bwd_ckpt_bytes(int H, long slots, int dk, int dv) {
+    const int rpl = dk >= WAVE ? dk / WAVE : 1;
+    return align256((size_t)H * slots * dv * WAVE * rpl * sizeof(float));
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N) {
+    const int ncg = dv / (bwd_waves(dv) * BW_COLS);
+    const size_t rows = (size_t)B * T * H;
+    const size_t part = ((size_t)ncg * 3 * rows * dk + (size_t)ncg * rows) * sizeof(float);
+    return bwd_ckpt_bytes(H, bwd_slots(B, T, varlen, N), dk, dv) + align256(part);
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a) {
+    const bool varlen = a.cu_seqlens != nullptr;
+    BwdParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.gate = a.gate;
+    p.beta = a.beta;
+    p.S0 = a.S0;
+    p.dO = a.dO;
+    p.dST = a.dST;
+    p.dv_out = a.g_v;
+    p.dS0 = a.g_S0;
+    p.cu = a.cu_seqlens;
+    p.H = a.H;
+    p.T = a.T;
+    p.dv = a.dv;
+    p.ncg = a.dv / (bwd_waves(a.dv) * BW_COLS);
+    p.nblk = bwd_slots(a.B, a.T, varlen, a.N);
+    p.rows = (long)a.B * a.T * a.H;
+    char* ws = static_cast<char*>(a.workspace);
+    p.ckpt = reinterpret_cast<float*>(ws);
+    p.part = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv));
+    hipError_t e = a.bf16 ? (a.scalar_gate ? launch_bwd_dk<uint16_t, true>(a, p) : launch_bwd_dk<uint16_t, false>(a, p))
+                          : (a.scalar_gate ? launch_bwd_dk<float, true>(a, p) : launch_bwd_dk<float, false>(a, p));
+    if (e != hipSuccess || p.rows == 0) return e;
+    const long n = p.rows * a.dk;
+    hipLaunchKernelGGL(chunk_bwd_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, p.part,
+                       p.rows, a.dk, p.ncg, a.scalar_gate, a.g_q, a.g_k, a.g_gate, a.g_beta);
+    return hipGetLastError();
+}
+
+}  // namespace kda

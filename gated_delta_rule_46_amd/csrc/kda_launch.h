@@ -30,6 +30,18 @@ struct ChunkArgs {
     int stages;                 // bit 0: index + prep kernels, bit 1: state kernel
 };
 
+struct BwdArgs {
+    const void *q, *k, *v, *gate, *beta;
+    const float *S0, *dO, *dST;                            // dST may be null (zero)
+    float *g_q, *g_k, *g_v, *g_gate, *g_beta, *g_S0;       // gradients; g_S0 may be null
+    int B, H, T, dk, dv;
+    const int32_t* cu_seqlens;                             // device, N+1 entries, or null
+    int N;
+    bool bf16, scalar_gate;
+    void* workspace;
+    hipStream_t stream;
+};
+
 // Bytes of intermediates one (chunk, head) pair occupies in the workspace.
 size_t chunk_block_bytes(int dk, int dv, int chunk, bool bf16);
 // Upper bound on the number of chunks over all sequences.
@@ -37,7 +49,11 @@ long chunk_count_bound(int B, int T, int chunk, bool varlen, int N);
 // Total workspace bytes for one forward call.
 size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, bool varlen, int N, bool bf16);
 
+// Workspace bytes of one backward call (checkpoints and partial sums).
+size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N);
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 
 }  // namespace kda

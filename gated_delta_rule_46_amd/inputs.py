@@ -22,6 +22,9 @@ rounded once to the storage dtype with torch's round-to-nearest-even):
   their own seeded like the tensors.
 
 Draw order: q, k, v, gate variates, beta variates, masks, S0.
+
+Backward inputs (``cotangents``): dO ~ N(0, 1) and dS_T ~ N(0, 1), fp32, from a
+generator of their own seeded with seed + 7919.
 """
 from __future__ import annotations
 
@@ -145,6 +148,17 @@ def make_forward(name: str, *, B: int, H: int, T: int, dk: int, dv: int, chunk: 
         cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
     return Workload(name, _round(q, dtype), _round(k, dtype), _round(v, dtype), _round(g, dtype),
                     _round(beta, dtype), S0, cu, B, H, T, dk, dv, chunk, gate_kind)
+
+
+def cotangents(w: Workload, seed: int = 0, with_dS_T: bool = True):
+    """Output gradients for a backward call on ``w``: dO [B,T,H,dv] and dS_T
+    [N,H,dk,dv] (or None), fp32 CPU tensors."""
+    rng = np.random.default_rng(seed + 7919)
+    dO = torch.from_numpy(rng.standard_normal((w.B, w.T, w.H, w.dv))).float()
+    dST = None
+    if with_dS_T:
+        dST = torch.from_numpy(rng.standard_normal((w.n_seqs, w.H, w.dk, w.dv))).float()
+    return dO, dST
 
 
 def varlen_lengths(seed: int = 0, n: int = 8, lo: int = 4096, hi: int = 32768):

@@ -21,8 +21,8 @@ GATE_CHANNEL, GATE_SCALAR = 0, 1
 
 STAGE_PREP, STAGE_STATE, STAGE_ALL = 1, 2, 3
 
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_strerror",
-           "kda_last_hip_error", "kda_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd",
+           "kda_chunk_bwd_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error", "kda_version")
 
 
 class KDAError(RuntimeError):
@@ -51,6 +51,10 @@ def _lib():
         lib.kda_chunk_fwd_stage.argtypes = [i] + [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
         lib.kda_chunk_fwd_workspace_bytes.restype = sz
         lib.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 9
+        lib.kda_chunk_bwd.restype = i
+        lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
+        lib.kda_chunk_bwd_workspace_bytes.restype = sz
+        lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 7
         lib.kda_decode_step.restype = i
         lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.kda_strerror.restype = ctypes.c_char_p
@@ -150,6 +154,64 @@ def chunk_fwd(q, k, v, gate, beta, S0=None, cu_seqlens=None, chunk: int = 64, ga
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_fwd_stage")
     return out, S_T
+
+
+def bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, N: int = 0, varlen: bool = False) -> int:
+    return int(_lib().kda_chunk_bwd_workspace_bytes(B, H, T, dk, dv, N, int(varlen)))
+
+
+def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate_kind: Optional[int] = None,
+              want_dS0: bool = True, out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> dict:
+    """Gradient of chunk_fwd for L = sum(o * dO) + sum(S_T * dS_T). Inputs as
+    for chunk_fwd; dO fp32 [B,T,H,dv]; dS_T fp32 [N,H,dk,dv] or None. Returns
+    a dict of fp32 tensors dq, dk, dv, dgate, dbeta (input layouts) and dS0
+    ([N,H,dk,dv], or None when not wanted). ``out`` may supply that dict's
+    tensors to write into."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    device = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta), ("dO", dO)):
+        _check_dev(name, t, device)
+    if gate_kind is None:
+        gate_kind = GATE_SCALAR if gate.dim() == 3 else GATE_CHANNEL
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("gate", gate), ("beta", beta)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    if dO.dtype != torch.float32 or tuple(dO.shape) != (B, T, H, dv):
+        raise ValueError("dO must be fp32 [%d,%d,%d,%d]" % (B, T, H, dv))
+    varlen = cu_seqlens is not None
+    N = int(cu_seqlens.numel() - 1) if varlen else B
+    if varlen:
+        _check_dev("cu_seqlens", cu_seqlens, device)
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _check_dev(name, t, device)
+            if t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv):
+                raise ValueError("%s must be fp32 [%d,%d,%d,%d]" % (name, N, H, dk, dv))
+    f32 = dict(device=device, dtype=torch.float32)
+    if out is None:
+        out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+               "dv": torch.empty((B, T, H, dv), **f32), "dgate": torch.empty(tuple(gate.shape), **f32),
+               "dbeta": torch.empty((B, T, H), **f32),
+               "dS0": torch.empty((N, H, dk, dv), **f32) if want_dS0 else None}
+    need = bwd_workspace_bytes(B, H, T, dk, dv, N, varlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
+    st = _stream_handle(stream, device)
+    rc = _lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
+                              _ptr(out["dbeta"]), _ptr(out.get("dS0")), B, H, T, dk, dv, _ptr(cu_seqlens),
+                              N if varlen else 0, dt, int(gate_kind), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), ctypes.c_void_p(st) if st else None)
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd")
+    return out
 
 
 def decode_step(q, k, v, gate, beta, S, out: Optional[torch.Tensor] = None, gate_kind: Optional[int] = None,

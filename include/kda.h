@@ -139,6 +139,44 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* gat
                     float* S, float* o, int N, int H, int dk, int dv, int dtype, int gate_kind,
                     void* stream);
 
+/*
+ * Bytes of device workspace kda_chunk_bwd needs for these sizes (0 when the
+ * arguments are invalid). Arguments as for kda_chunk_fwd_workspace_bytes.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int N, int has_cu_seqlens);
+
+/*
+ * Gradient of kda_chunk_fwd. The pages measure forward-plus-backward
+ * training throughput of this family (Complex KDA summary, efficiency) but
+ * print no backward; this is the reverse-mode derivative of the token
+ * recurrence in the header comment, for the loss
+ *   L = sum_t <o_t, dO_t> + sum_seq <S_T, dS_T>,
+ * computed in fp32 from the same inputs (the forward states are recomputed
+ * from q, k, v, gate, beta and S0; nothing from a forward call is reused).
+ *
+ * Inputs: q, k, v, gate, beta, S0, cu_seqlens, N, dtype and gate_kind as for
+ * kda_chunk_fwd; dO [B, T, H, dv] fp32 (required when T > 0); dS_T
+ * [N, H, dk, dv] fp32 or NULL (zero).
+ * Outputs (fp32, written in full, must not alias inputs or each other):
+ *   grad_q, grad_k [B, T, H, dk]   grad_v [B, T, H, dv]
+ *   grad_gate      [B, T, H, dk] (KDA_GATE_CHANNEL) or [B, T, H] (KDA_GATE_SCALAR)
+ *   grad_beta      [B, T, H]
+ *   grad_S0        [N, H, dk, dv], or NULL when not wanted
+ * dO, grad_v, S0, dS_T and grad_S0 must be 16-byte aligned.
+ *
+ * workspace: at least kda_chunk_bwd_workspace_bytes(...) bytes (state
+ * checkpoints every 8 tokens, 4 * dk * dv bytes each per (sequence, head),
+ * plus per-workgroup partial sums), or NULL to take it stream-ordered from
+ * the device's default memory pool.
+ *
+ * Returns KDA_OK or a negative status.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                  const float* S0, const float* dO, const float* dS_T, float* grad_q, float* grad_k,
+                  float* grad_v, float* grad_gate, float* grad_beta, float* grad_S0, int B, int H, int T,
+                  int dk, int dv, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* kda_strerror(int status);
 
