@@ -28,11 +28,12 @@ FLAGS = [
 ]
 
 
-# Per-source additions. The chunk kernels are bound by dependent chains and
-# schedule better for latency (3-6% faster on every forward configuration);
-# the streaming decode kernel loses 17% with that schedule, so it keeps the
-# default.
-EXTRA = {"kda_chunk.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-source additions. The chunk kernels and the backward are bound by
+# dependent chains and schedule better for latency (3-6% faster on every
+# forward configuration, 7% on the backward); the streaming decode kernel
+# loses 17% with that schedule, so it keeps the default.
+ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+EXTRA = {"kda_chunk.hip": ILP, "kda_bwd.hip": ILP}
 
 
 def _compile(src: str) -> str:

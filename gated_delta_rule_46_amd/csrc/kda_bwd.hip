@@ -20,9 +20,9 @@
 // so each wave owns COLS value columns and all dk rows of S and dS: lane l
 // holds rows l + 64 m. A column sum over the rows (pred, du) is then a
 // wave-wide sum (DPP inside rows of 16 lanes, lane swaps across rows), with
-// no barrier; only dq, dk and dalpha (sums over value columns) cross waves,
-// through LDS atomics, and workgroups, through per-workgroup partial sums
-// that a second kernel adds up.
+// no barrier. Only dq, dk and dalpha (sums over value columns) cross waves,
+// through per-wave partial sums in LDS, and workgroups, through
+// per-workgroup partial sums in memory that a second kernel adds up.
 //
 // Pass A runs the forward from S0 and stores S at the start of every
 // SUB-token block (the checkpoints). Pass B walks the blocks backwards:
@@ -75,16 +75,24 @@ struct BwdStage {
     float v[BW_SUB][NC], dO[BW_SUB][NC], b[BW_SUB];
 };
 
-template <int DK, int NC, bool SG>
+// Dynamic LDS of one workgroup: the double-buffered input stage and, also
+// double-buffered by block parity, each wave's per-token partial sums over its
+// own value columns (dq, dk, dalpha per row; dbeta), written with plain
+// stores and added up across the waves when the block is flushed. (LDS
+// atomics from four waves onto the same rows took 40% of the kernel time.)
+template <int DK, int NC, int NWV, bool SG>
 struct BwdLds {
     BwdStage<DK, NC, SG> st[2];
-    float acc[2][BW_SUB][3][DK];   // dq, dk, dalpha partial sums over this workgroup's columns
-    float accb[2][BW_SUB];         // dbeta partial sums
+    float slot[2][NWV][BW_SUB][3][DK];
+    float slotb[2][NWV][BW_SUB];
 };
 
 // One block's inputs, fetched into registers one block ahead, then written
 // to LDS. Element e = tid + NT i of the [SUB][DK] key-side arrays and of the
-// [SUB][NC] value-side arrays; entries past the sequence end are zero.
+// [SUB][NC] value-side arrays. Tokens past the sequence end get gate 1 and
+// zeros everywhere else, which makes them exact no-ops in both directions
+// (S' = S, u = 0; dS, dq, dk, dv and dbeta unchanged or zero), so the token
+// loops run without branches and the compiler can overlap tokens.
 template <class TIn, int DK, int NC, int NT, int RPL, int COLS, bool SG, bool BWD>
 struct BwdFetch {
     static constexpr int KPT = (BW_SUB * DK + NT - 1) / NT;
@@ -106,7 +114,7 @@ struct BwdFetch {
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
             k[i] = ok ? ld_in(K + row * DK + r) : 0.f;
             if (BWD) q[i] = ok ? ld_in(Q + row * DK + r) : 0.f;
-            if (!SG) a[i] = ok ? ld_in(A + row * DK + r) : 0.f;
+            if (!SG) a[i] = ok ? ld_in(A + row * DK + r) : 1.f;
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -121,7 +129,7 @@ struct BwdFetch {
             const bool ok = tid < BW_SUB && t < te;
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
             b = ok ? ld_in(Bt + row) : 0.f;
-            ag = (SG && ok) ? ld_in(A + row) : 0.f;
+            ag = SG ? (ok ? ld_in(A + row) : 1.f) : 0.f;
         }
         if (BWD) {
             const f32x4* c4 = reinterpret_cast<const f32x4*>(ckp);
@@ -162,7 +170,8 @@ chunk_bwd_kernel(BwdParams p) {
     constexpr int RPL = DK >= WAVE ? DK / WAVE : 1;        // state rows per lane
     constexpr int CKF = NT * RPL * COLS;                    // floats per checkpoint slot
     static_assert(COLS % 4 == 0, "float4 column groups");
-    __shared__ BwdLds<DK, NC, SG> L;
+    extern __shared__ __align__(16) unsigned char smem[];
+    BwdLds<DK, NC, NWV, SG>& L = *reinterpret_cast<BwdLds<DK, NC, NWV, SG>*>(smem);
 
     const int tid = threadIdx.x, lane = tid % WAVE;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
@@ -186,12 +195,9 @@ chunk_bwd_kernel(BwdParams p) {
     float* ck = p.ckpt + ((size_t)(h * p.ncg + cg) * p.nblk + base) * CKF + (size_t)tid * RPL * COLS;
     const size_t sbase = (size_t)(s * p.H + h) * DK * p.dv;
 
-    for (int e = tid; e < 2 * SUB * 3 * DK; e += NT) (&L.acc[0][0][0][0])[e] = 0.f;
-    if (tid < 2 * SUB) (&L.accb[0][0])[tid] = 0.f;
-
     bool rv[RPL];
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) rv[m] = lane + WAVE * m < DK;
+    for (int m = 0; m < RPL; ++m) rv[m] = DK >= WAVE || lane < DK;
 
     float S[RPL][COLS];
 #pragma unroll
@@ -224,7 +230,7 @@ chunk_bwd_kernel(BwdParams p) {
                     cp[m * (COLS / 4) + c4] = f32x4{S[m][4 * c4], S[m][4 * c4 + 1], S[m][4 * c4 + 2], S[m][4 * c4 + 3]};
 #pragma unroll
             for (int j = 0; j < SUB; ++j) {
-                if (ts + j < t1) {
+                {
                     float kr[RPL], part[COLS];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
@@ -268,24 +274,27 @@ chunk_bwd_kernel(BwdParams p) {
         }
     }
     const size_t nrk = (size_t)p.rows * DK;
-    auto flush = [&](int fb) {   // partial sums of block fb (its accumulator half) to memory, then zero them
+    auto flush = [&](int fb) {   // the waves' partial sums of block fb, added up, to memory
         const int ts = t0 + fb * SUB;
-        float(*acc)[3][DK] = L.acc[fb & 1];
         for (int e = tid; e < SUB * 3 * DK; e += NT) {
             const int j = e / (3 * DK), rem = e % (3 * DK), qty = rem / DK, i = rem % DK, t = ts + j;
             if (t < t1) {
+                float x = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NWV; ++ww) x += L.slot[fb & 1][ww][j][qty][i];
                 const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-                p.part[((size_t)cg * 3 + qty) * nrk + row * DK + i] = acc[j][qty][i];
+                p.part[((size_t)cg * 3 + qty) * nrk + row * DK + i] = x;
             }
-            acc[j][qty][i] = 0.f;
         }
         if (tid < SUB) {
             const int t = ts + tid;
             if (t < t1) {
+                float x = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NWV; ++ww) x += L.slotb[fb & 1][ww][tid];
                 const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-                p.part[(size_t)p.ncg * 3 * nrk + (size_t)cg * p.rows + row] = L.accb[fb & 1][tid];
+                p.part[(size_t)p.ncg * 3 * nrk + (size_t)cg * p.rows + row] = x;
             }
-            L.accb[fb & 1][tid] = 0.f;
         }
     };
     {
@@ -312,7 +321,7 @@ chunk_bwd_kernel(BwdParams p) {
                 for (int m = 0; m < RPL; ++m)
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) Sh[j][m][c] = Sb[m][c];
-                if (j + 1 < SUB && ts + j + 1 < t1) {
+                if (j + 1 < SUB) {
                     float kr[RPL], part[COLS];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
@@ -339,10 +348,10 @@ chunk_bwd_kernel(BwdParams p) {
                 }
             }
 
-            float(*acc)[3][DK] = L.acc[blk & 1];
+            float(*slot)[3][DK] = L.slot[blk & 1][w];
 #pragma unroll
             for (int j = SUB - 1; j >= 0; --j) {
-                if (ts + j < t1) {
+                {
                     float kr[RPL], qr[RPL], ar[RPL], oo[COLS], vv[COLS];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
@@ -398,13 +407,13 @@ chunk_bwd_kernel(BwdParams p) {
                         }
                         if (rv[m]) {
                             const int r = lane + WAVE * m;
-                            atomicAdd(&acc[j][0][r], gq);
-                            atomicAdd(&acc[j][1][r], gk);
-                            atomicAdd(&acc[j][2][r], ga);
+                            slot[j][0][r] = gq;
+                            slot[j][1][r] = gk;
+                            slot[j][2][r] = ga;
                         }
                     }
-                    if (lane == 0) {
-                        atomicAdd(&L.accb[blk & 1][j], dbt);
+                    if (lane == 0) L.slotb[blk & 1][w][j] = dbt;
+                    if (lane == 0 && ts + j < t1) {
                         const size_t row = ((size_t)b0 * p.T + ts + j) * p.H + h;
                         f32x4* dvp = reinterpret_cast<f32x4*>(p.dv_out + row * p.dv + c0);
 #pragma unroll
@@ -464,28 +473,30 @@ chunk_bwd_reduce_kernel(const float* __restrict__ part, long rows, int dk, int n
     }
 }
 
-int bwd_waves(int dv) { return dv >= 32 ? 4 : 2; }
-constexpr int BW_COLS = 8;
+constexpr int BW_COLS = 4;   // value columns per wave
+constexpr int BW_WAVES = 4;  // waves per workgroup: 16 value columns (dv >= 16 always)
+int bwd_waves(int) { return BW_WAVES; }
 
 template <class TIn, int DK, int NWV, bool SG>
 hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p) {
-    hipLaunchKernelGGL((chunk_bwd_kernel<TIn, DK, NWV, BW_COLS, SG>), dim3(a.N * a.H * p.ncg), dim3(NWV * WAVE), 0,
-                       a.stream, p);
+    constexpr size_t bytes = sizeof(BwdLds<DK, NWV * BW_COLS, NWV, SG>);
+    static_assert(bytes <= 160 * 1024, "backward LDS");
+    auto kern = chunk_bwd_kernel<TIn, DK, NWV, BW_COLS, SG>;
+    if (bytes > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.N * a.H * p.ncg), dim3(NWV * WAVE), bytes, a.stream, p);
     return hipGetLastError();
-}
-
-template <class TIn, int DK, bool SG>
-hipError_t launch_bwd_w(const BwdArgs& a, const BwdParams& p) {
-    return bwd_waves(a.dv) == 4 ? launch_bwd_t<TIn, DK, 4, SG>(a, p) : launch_bwd_t<TIn, DK, 2, SG>(a, p);
 }
 
 template <class TIn, bool SG>
 hipError_t launch_bwd_dk(const BwdArgs& a, const BwdParams& p) {
     switch (a.dk) {
-        case 16: return launch_bwd_w<TIn, 16, SG>(a, p);
-        case 32: return launch_bwd_w<TIn, 32, SG>(a, p);
-        case 64: return launch_bwd_w<TIn, 64, SG>(a, p);
-        default: return launch_bwd_w<TIn, 128, SG>(a, p);
+        case 16: return launch_bwd_t<TIn, 16, BW_WAVES, SG>(a, p);
+        case 32: return launch_bwd_t<TIn, 32, BW_WAVES, SG>(a, p);
+        case 64: return launch_bwd_t<TIn, 64, BW_WAVES, SG>(a, p);
+        default: return launch_bwd_t<TIn, 128, BW_WAVES, SG>(a, p);
     }
 }
 
