@@ -37,6 +37,8 @@ namespace kda {
 namespace {
 
 constexpr int BW_SUB = 8;   // tokens per checkpoint interval
+constexpr int BW_OOB = (int)0x80000000;   // buffer offset past any range used here: the store is dropped
+
 
 // Sum over the 64 lanes, the same bits in every lane: DPP add steps inside
 // each row of 16 lanes (swap neighbours, swap pairs, mirror halves of 8,
@@ -63,6 +65,7 @@ struct BwdParams {
     const void *q, *k, *v, *gate, *beta;
     const float *S0, *dO, *dST;
     float *dv_out, *dS0, *ckpt, *part;
+    float* pred;   // S'^T k of every token from pass A, [B*T*H][dv]
     const int32_t* cu;
     int H, T, dv, ncg;
     long nblk;   // checkpoint slots per (head, column group)
@@ -72,7 +75,7 @@ struct BwdParams {
 template <int DK, int NC, bool SG>
 struct BwdStage {
     float k[BW_SUB][DK], q[BW_SUB][DK], a[BW_SUB][SG ? 1 : DK];
-    float v[BW_SUB][NC], dO[BW_SUB][NC], b[BW_SUB];
+    float v[BW_SUB][NC], dO[BW_SUB][NC], pred[BW_SUB][NC], b[BW_SUB];
 };
 
 // Dynamic LDS of one workgroup: the double-buffered input stage and, also
@@ -85,7 +88,17 @@ struct BwdLds {
     BwdStage<DK, NC, SG> st[2];
     float slot[2][NWV][BW_SUB][3][DK];
     float slotb[2][NWV][BW_SUB];
+    float vout[2][BW_SUB][NC];   // per-token wave-uniform results: pred (pass A), dv (pass B)
+    float junk[4 * WAVE];        // target of the lanes that do not store a wave-uniform value
 };
+
+// Buffer resource over the SUB tokens starting at token `tok0` (flat token
+// index b * T + t) of a [tokens][H][width] float array, so that per-element
+// offsets stay small and tokens past the end of a sequence can be dropped
+// with an out-of-range offset instead of a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(float* base, size_t tok0, int H, int width) {
+    return make_rsrc(base + tok0 * H * width, (uint32_t)(BW_SUB * H * width * 4));
+}
 
 // One block's inputs, fetched into registers one block ahead, then written
 // to LDS. Element e = tid + NT i of the [SUB][DK] key-side arrays and of the
@@ -93,11 +106,21 @@ struct BwdLds {
 // zeros everywhere else, which makes them exact no-ops in both directions
 // (S' = S, u = 0; dS, dq, dk, dv and dbeta unchanged or zero), so the token
 // loops run without branches and the compiler can overlap tokens.
+// Inputs stay in their storage type between the load and the LDS store (the
+// next block), so that nothing reads the loaded registers early and forces a
+// wait for the memory latency inside the token loop.
+__device__ __forceinline__ float in_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+__device__ __forceinline__ float in_f32(float x) { return x; }
+template <class TIn> __device__ __forceinline__ TIn in_one();
+template <> __device__ __forceinline__ uint16_t in_one<uint16_t>() { return 0x3F80; }   // bf16 1.0
+template <> __device__ __forceinline__ float in_one<float>() { return 1.f; }
+
 template <class TIn, int DK, int NC, int NT, int RPL, int COLS, bool SG, bool BWD>
 struct BwdFetch {
     static constexpr int KPT = (BW_SUB * DK + NT - 1) / NT;
     static constexpr int VPT = (BW_SUB * NC + NT - 1) / NT;
-    float k[KPT], q[BWD ? KPT : 1], a[SG ? 1 : KPT], v[VPT], dO[BWD ? VPT : 1], b, ag;
+    TIn k[KPT], q[BWD ? KPT : 1], a[SG ? 1 : KPT], v[VPT], b, ag;
+    float dO[BWD ? VPT : 1], pr[BWD ? VPT : 1];
     f32x4 ck[BWD ? RPL * COLS / 4 : 1];   // this lane's part of the block's checkpoint
 
     __device__ __forceinline__ void fetch(const BwdParams& p, int tid, int b0, int h, int ts, int te, int cw0,
@@ -112,24 +135,25 @@ struct BwdFetch {
             const int e = tid + NT * i, j = e / DK, r = e % DK, t = ts + j;
             const bool ok = e < BW_SUB * DK && t < te;
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-            k[i] = ok ? ld_in(K + row * DK + r) : 0.f;
-            if (BWD) q[i] = ok ? ld_in(Q + row * DK + r) : 0.f;
-            if (!SG) a[i] = ok ? ld_in(A + row * DK + r) : 1.f;
+            k[i] = ok ? K[row * DK + r] : TIn(0);
+            if (BWD) q[i] = ok ? Q[row * DK + r] : TIn(0);
+            if (!SG) a[i] = ok ? A[row * DK + r] : in_one<TIn>();
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int e = tid + NT * i, j = e / NC, c = e % NC, t = ts + j;
             const bool ok = e < BW_SUB * NC && t < te;
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-            v[i] = ok ? ld_in(V + row * p.dv + cw0 + c) : 0.f;
+            v[i] = ok ? V[row * p.dv + cw0 + c] : TIn(0);
             if (BWD) dO[i] = ok ? p.dO[row * p.dv + cw0 + c] : 0.f;
+            if (BWD) pr[i] = ok ? p.pred[row * p.dv + cw0 + c] : 0.f;
         }
         {
             const int t = ts + tid;
             const bool ok = tid < BW_SUB && t < te;
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-            b = ok ? ld_in(Bt + row) : 0.f;
-            ag = SG ? (ok ? ld_in(A + row) : 1.f) : 0.f;
+            b = ok ? Bt[row] : TIn(0);
+            ag = SG ? (ok ? A[row] : in_one<TIn>()) : TIn(0);
         }
         if (BWD) {
             const f32x4* c4 = reinterpret_cast<const f32x4*>(ckp);
@@ -143,22 +167,23 @@ struct BwdFetch {
         for (int i = 0; i < KPT; ++i) {
             const int e = tid + NT * i;
             if (e < BW_SUB * DK) {
-                (&s.k[0][0])[e] = k[i];
-                if (BWD) (&s.q[0][0])[e] = q[i];
-                if (!SG) (&s.a[0][0])[e] = a[i];
+                (&s.k[0][0])[e] = in_f32(k[i]);
+                if (BWD) (&s.q[0][0])[e] = in_f32(q[i]);
+                if (!SG) (&s.a[0][0])[e] = in_f32(a[i]);
             }
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int e = tid + NT * i;
             if (e < BW_SUB * NC) {
-                (&s.v[0][0])[e] = v[i];
+                (&s.v[0][0])[e] = in_f32(v[i]);
                 if (BWD) (&s.dO[0][0])[e] = dO[i];
+                if (BWD) (&s.pred[0][0])[e] = pr[i];
             }
         }
         if (tid < BW_SUB) {
-            s.b[tid] = b;
-            if (SG) s.a[tid][0] = ag;
+            s.b[tid] = in_f32(b);
+            if (SG) s.a[tid][0] = in_f32(ag);
         }
     }
 };
@@ -212,6 +237,18 @@ chunk_bwd_kernel(BwdParams p) {
         }
     }
 
+    // Wave-uniform per-token results of block fb, from LDS to memory (pass A: pred)
+    auto flush_vout = [&](int fb, float* dst) {
+        const int ts = t0 + fb * SUB;
+        const __amdgpu_buffer_rsrc_t r = block_rsrc(dst, (size_t)b0 * p.T + ts, p.H, p.dv);
+        for (int e = tid; e < SUB * NC; e += NT) {
+            const int j = e / NC, c = e % NC;
+            const int off = ts + j < t1 ? ((j * p.H + h) * p.dv + cw0 + c) * 4 : BW_OOB;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L.vout[fb & 1][j][c]), r, off, 0, 0);
+        }
+    };
+    auto flush_pred = [&](int fb) { flush_vout(fb, p.pred); };
+
     // ------------------------------------------------ pass A: forward, checkpoints
     {
         BwdFetch<TIn, DK, NC, NT, RPL, COLS, SG, false> f;
@@ -221,6 +258,7 @@ chunk_bwd_kernel(BwdParams p) {
             f.store(st, tid);
             __syncthreads();
             const int ts = t0 + blk * SUB;
+            if (blk > 0) flush_pred(blk - 1);
             if (blk + 1 < nb) f.fetch(p, tid, b0, h, ts + SUB, t1, cw0, nullptr);
             f32x4* cp = reinterpret_cast<f32x4*>(ck + (size_t)blk * CKF);
 #pragma unroll
@@ -247,6 +285,9 @@ chunk_bwd_kernel(BwdParams p) {
                         for (int m = 0; m < RPL; ++m) x = fmaf(S[m][c], kr[m], x);
                         part[c] = wave_allsum(x);
                     }
+                    static_assert(COLS == 4, "one 16-byte LDS store of pred per wave and token");
+                    *reinterpret_cast<f32x4*>(lane == 0 ? &L.vout[blk & 1][j][w * COLS] : &L.junk[4 * lane]) =
+                        f32x4{part[0], part[1], part[2], part[3]};
                     const float bt = st.b[j];
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
@@ -259,6 +300,8 @@ chunk_bwd_kernel(BwdParams p) {
         }
     }
     __syncthreads();
+    if (nb > 0) flush_pred(nb - 1);
+    __syncthreads();   // pass B reads pred written by other threads
 
     // ------------------------------------------------ pass B: adjoint, blocks in reverse
     float dS[RPL][COLS];
@@ -274,27 +317,31 @@ chunk_bwd_kernel(BwdParams p) {
         }
     }
     const size_t nrk = (size_t)p.rows * DK;
-    auto flush = [&](int fb) {   // the waves' partial sums of block fb, added up, to memory
+    auto flush = [&](int fb) {   // block fb: dv, and the waves' partial sums added up, to memory
         const int ts = t0 + fb * SUB;
-        for (int e = tid; e < SUB * 3 * DK; e += NT) {
-            const int j = e / (3 * DK), rem = e % (3 * DK), qty = rem / DK, i = rem % DK, t = ts + j;
-            if (t < t1) {
+        const size_t tok0 = (size_t)b0 * p.T + ts;
+        flush_vout(fb, p.dv_out);
+#pragma unroll
+        for (int qty = 0; qty < 3; ++qty) {
+            const __amdgpu_buffer_rsrc_t r = block_rsrc(p.part + ((size_t)cg * 3 + qty) * nrk, tok0, p.H, DK);
+#pragma unroll
+            for (int i = 0; i < (SUB * DK + NT - 1) / NT; ++i) {
+                const int e = tid + NT * i, j = e / DK, ii = e % DK, jj = j < SUB ? j : SUB - 1;
                 float x = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < NWV; ++ww) x += L.slot[fb & 1][ww][j][qty][i];
-                const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-                p.part[((size_t)cg * 3 + qty) * nrk + row * DK + i] = x;
+                for (int ww = 0; ww < NWV; ++ww) x += L.slot[fb & 1][ww][jj][qty][ii];
+                const int off = e < SUB * DK && ts + j < t1 ? ((j * p.H + h) * DK + ii) * 4 : BW_OOB;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
             }
         }
-        if (tid < SUB) {
-            const int t = ts + tid;
-            if (t < t1) {
-                float x = 0.f;
+        {
+            const __amdgpu_buffer_rsrc_t r =
+                block_rsrc(p.part + (size_t)p.ncg * 3 * nrk + (size_t)cg * p.rows, tok0, p.H, 1);
+            float x = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < NWV; ++ww) x += L.slotb[fb & 1][ww][tid];
-                const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-                p.part[(size_t)p.ncg * 3 * nrk + (size_t)cg * p.rows + row] = x;
-            }
+            for (int ww = 0; ww < NWV; ++ww) x += L.slotb[fb & 1][ww][tid < SUB ? tid : 0];
+            const int off = tid < SUB && ts + tid < t1 ? (tid * p.H + h) * 4 : BW_OOB;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
         }
     };
     {
@@ -321,8 +368,8 @@ chunk_bwd_kernel(BwdParams p) {
                 for (int m = 0; m < RPL; ++m)
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) Sh[j][m][c] = Sb[m][c];
-                if (j + 1 < SUB) {
-                    float kr[RPL], part[COLS];
+                if (j + 1 < SUB) {   // pred from pass A: the same values, no reduction
+                    float kr[RPL];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
                         const int r = rv[m] ? lane + WAVE * m : 0;
@@ -331,17 +378,10 @@ chunk_bwd_kernel(BwdParams p) {
 #pragma unroll
                         for (int c = 0; c < COLS; ++c) Sb[m][c] *= a;
                     }
-#pragma unroll
-                    for (int c = 0; c < COLS; ++c) {
-                        float x = 0.f;
-#pragma unroll
-                        for (int m = 0; m < RPL; ++m) x = fmaf(Sb[m][c], kr[m], x);
-                        part[c] = wave_allsum(x);
-                    }
                     const float bt = st.b[j];
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
-                        const float u = bt * (st.v[j][w * COLS + c] - part[c]);
+                        const float u = bt * (st.v[j][w * COLS + c] - st.pred[j][w * COLS + c]);
 #pragma unroll
                         for (int m = 0; m < RPL; ++m) Sb[m][c] = fmaf(kr[m], u, Sb[m][c]);
                     }
@@ -376,13 +416,10 @@ chunk_bwd_kernel(BwdParams p) {
                         }
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
-                        float x = 0.f, y = 0.f;
+                        float y = 0.f;
 #pragma unroll
-                        for (int m = 0; m < RPL; ++m) {
-                            x = fmaf(Sp[m][c], kr[m], x);
-                            y = fmaf(dS[m][c], kr[m], y);
-                        }
-                        pred[c] = wave_allsum(x);
+                        for (int m = 0; m < RPL; ++m) y = fmaf(dS[m][c], kr[m], y);
+                        pred[c] = st.pred[j][w * COLS + c];
                         du[c] = wave_allsum(y);
                     }
                     float u[COLS], dpred[COLS], dbt = 0.f;
@@ -412,15 +449,11 @@ chunk_bwd_kernel(BwdParams p) {
                             slot[j][2][r] = ga;
                         }
                     }
-                    if (lane == 0) L.slotb[blk & 1][w][j] = dbt;
-                    if (lane == 0 && ts + j < t1) {
-                        const size_t row = ((size_t)b0 * p.T + ts + j) * p.H + h;
-                        f32x4* dvp = reinterpret_cast<f32x4*>(p.dv_out + row * p.dv + c0);
-#pragma unroll
-                        for (int c4 = 0; c4 < COLS / 4; ++c4)
-                            dvp[c4] = f32x4{bt * du[4 * c4], bt * du[4 * c4 + 1], bt * du[4 * c4 + 2],
-                                            bt * du[4 * c4 + 3]};
-                    }
+                    // wave-uniform values, stored by lane 0 without a branch (the other
+                    // lanes write a junk area): dbeta and dv, flushed with the block
+                    (lane == 0 ? &L.slotb[blk & 1][w][j] : &L.junk[lane])[0] = dbt;
+                    *reinterpret_cast<f32x4*>(lane == 0 ? &L.vout[blk & 1][j][w * COLS] : &L.junk[4 * lane]) =
+                        f32x4{bt * du[0], bt * du[1], bt * du[2], bt * du[3]};
                 }
             }
         }
@@ -511,13 +544,17 @@ size_t bwd_ckpt_bytes(int H, long slots, int dk, int dv) {
     return align256((size_t)H * slots * dv * WAVE * rpl * sizeof(float));
 }
 
+size_t bwd_part_bytes(int B, int H, int T, int dk, int dv) {
+    const int ncg = dv / (bwd_waves(dv) * BW_COLS);
+    const size_t rows = (size_t)B * T * H;
+    return align256(((size_t)ncg * 3 * rows * dk + (size_t)ncg * rows) * sizeof(float));
+}
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N) {
-    const int ncg = dv / (bwd_waves(dv) * BW_COLS);
-    const size_t rows = (size_t)B * T * H;
-    const size_t part = ((size_t)ncg * 3 * rows * dk + (size_t)ncg * rows) * sizeof(float);
-    return bwd_ckpt_bytes(H, bwd_slots(B, T, varlen, N), dk, dv) + align256(part);
+    const size_t pred = align256((size_t)B * T * H * dv * sizeof(float));
+    return bwd_ckpt_bytes(H, bwd_slots(B, T, varlen, N), dk, dv) + bwd_part_bytes(B, H, T, dk, dv) + pred;
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {
@@ -543,6 +580,8 @@ hipError_t launch_chunk_bwd(const BwdArgs& a) {
     char* ws = static_cast<char*>(a.workspace);
     p.ckpt = reinterpret_cast<float*>(ws);
     p.part = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv));
+    p.pred = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv) +
+                                      bwd_part_bytes(a.B, a.H, a.T, a.dk, a.dv));
     hipError_t e = a.bf16 ? (a.scalar_gate ? launch_bwd_dk<uint16_t, true>(a, p) : launch_bwd_dk<uint16_t, false>(a, p))
                           : (a.scalar_gate ? launch_bwd_dk<float, true>(a, p) : launch_bwd_dk<float, false>(a, p));
     if (e != hipSuccess || p.rows == 0) return e;
