@@ -40,25 +40,38 @@ constexpr int BW_SUB = 8;   // tokens per checkpoint interval
 constexpr int BW_OOB = (int)0x80000000;   // buffer offset past any range used here: the store is dropped
 
 
-// Sum over the 64 lanes, the same bits in every lane: DPP add steps inside
-// each row of 16 lanes (swap neighbours, swap pairs, mirror halves of 8,
-// mirror the row), then the lane swaps across rows. Every step adds a value
-// to its partner's in both lanes, so all lanes round identically.
+// The four column sums of a wave (x[c] summed over the 64 lanes), returned
+// in every lane (wave-uniform), with a reduce-scatter instead of four full
+// reductions: swapping with the neighbour lane and then with the lane two
+// away, each lane keeps half of what it has and adds its partner's copy of
+// that half, until it holds one column (column 0, 2, 1, 3 in lanes 0, 1, 2, 3
+// of every quad); row rotations by 4 and 8 then sum the four quads of each
+// row of 16 lanes, two lane swaps sum the four rows, and lanes 0..3 hold the
+// totals, which readlane makes scalars.
 template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ float dpp_of(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_allsum(float v) {
-    v = dpp_add<0xB1>(v);
-    v = dpp_add<0x4E>(v);
-    v = dpp_add<0x141>(v);
-    v = dpp_add<0x140>(v);
-    const uint32_t u = __float_as_uint(v);
+__device__ __forceinline__ void wave_sum4(const float (&x)[4], float (&out)[4], int lane) {
+    const bool odd = lane & 1, hi = lane & 2;
+    const float k0 = odd ? x[2] : x[0], k1 = odd ? x[3] : x[1];
+    const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
+    const float n0 = k0 + dpp_of<0xB1>(s0), n1 = k1 + dpp_of<0xB1>(s1);   // quad_perm [1,0,3,2]
+    const float kk = hi ? n1 : n0, ss = hi ? n0 : n1;
+    float m = kk + dpp_of<0x4E>(ss);                                      // quad_perm [2,3,0,1]
+    m += dpp_of<0x124>(m);                                                // row_ror:4
+    m += dpp_of<0x128>(m);                                                // row_ror:8
+    const uint32_t u = __float_as_uint(m);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const uint32_t u2 = __float_as_uint(v);
+    m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t u2 = __float_as_uint(m);
     const auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    m = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    const int mi = __float_as_int(m);
+    out[0] = __int_as_float(__builtin_amdgcn_readlane(mi, 0));
+    out[1] = __int_as_float(__builtin_amdgcn_readlane(mi, 2));
+    out[2] = __int_as_float(__builtin_amdgcn_readlane(mi, 1));
+    out[3] = __int_as_float(__builtin_amdgcn_readlane(mi, 3));
 }
 
 struct BwdParams {
@@ -278,12 +291,15 @@ chunk_bwd_kernel(BwdParams p) {
 #pragma unroll
                         for (int c = 0; c < COLS; ++c) S[m][c] *= a;
                     }
+                    {
+                        float x[COLS];
 #pragma unroll
-                    for (int c = 0; c < COLS; ++c) {
-                        float x = 0.f;
+                        for (int c = 0; c < COLS; ++c) {
+                            x[c] = 0.f;
 #pragma unroll
-                        for (int m = 0; m < RPL; ++m) x = fmaf(S[m][c], kr[m], x);
-                        part[c] = wave_allsum(x);
+                            for (int m = 0; m < RPL; ++m) x[c] = fmaf(S[m][c], kr[m], x[c]);
+                        }
+                        wave_sum4(x, part, lane);
                     }
                     static_assert(COLS == 4, "one 16-byte LDS store of pred per wave and token");
                     *reinterpret_cast<f32x4*>(lane == 0 ? &L.vout[blk & 1][j][w * COLS] : &L.junk[4 * lane]) =
@@ -414,13 +430,16 @@ chunk_bwd_kernel(BwdParams p) {
                             Sp[m][c] = ar[m] * Sh[j][m][c];
                             dS[m][c] = fmaf(qr[m], oo[c], dS[m][c]);
                         }
+                    {
+                        float y[COLS];
 #pragma unroll
-                    for (int c = 0; c < COLS; ++c) {
-                        float y = 0.f;
+                        for (int c = 0; c < COLS; ++c) {
+                            y[c] = 0.f;
 #pragma unroll
-                        for (int m = 0; m < RPL; ++m) y = fmaf(dS[m][c], kr[m], y);
-                        pred[c] = st.pred[j][w * COLS + c];
-                        du[c] = wave_allsum(y);
+                            for (int m = 0; m < RPL; ++m) y[c] = fmaf(dS[m][c], kr[m], y[c]);
+                            pred[c] = st.pred[j][w * COLS + c];
+                        }
+                        wave_sum4(y, du, lane);
                     }
                     float u[COLS], dpred[COLS], dbt = 0.f;
 #pragma unroll
