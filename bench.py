@@ -9,6 +9,8 @@ T=8192, dk=dv=128, bf16 inputs, fp32 state, chunk 64): 16,384 tokens. Two
 seeded input sets alternate so the 256 MB last-level cache cannot hold the
 whole working set. The decode step (N=256 sequences, H=32, d=128, fp32 state
 of 512 MiB updated in place) is timed as one block of 128 consecutive steps.
+The backward (kda_chunk_bwd, gradients of every input for given dO and
+dS_T) is timed on the same forward workload.
 Timing uses HIP events recorded on the stream the kernels run on. Prints one
 JSON line.
 """
@@ -27,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tokens/s KDA chunk fwd (H=16,d=128,T=8192) + decode GB/s, % roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
 def fwd_bytes_per_head_token(dk: int, dv: int, scalar_gate: bool, in_bytes: int = 2) -> int:
@@ -43,29 +46,50 @@ def fwd_flops_per_head_token(dk: int, dv: int, C: int = 64) -> int:
     return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
 
 
+def bwd_bytes_per_head_token(dk: int, dv: int, in_bytes: int = 2) -> int:
+    """Compulsory HBM bytes of the backward per (token, head): q, k, v, gate,
+    beta read in the input dtype, dO read in fp32, dq, dk, dgate, dv, dbeta
+    written in fp32."""
+    return in_bytes * (3 * dk + dv + 1) + 4 * dv + 4 * (3 * dk + dv + 1)
+
+
+def bwd_flops_per_head_token(dk: int, dv: int) -> int:
+    """fp32 flops of the token-form adjoint per (token, head): the forward
+    step that rebuilds the state (gate scale, S'^T k, rank-one update: 5 per
+    state element) and the adjoint step (18 per state element: S', q dO^T,
+    dS^T k, S_t dO, dS u, S' dpred, dS', dalpha, Diag(alpha) dS')."""
+    return 23 * dk * dv
+
+
 def decode_bytes_per_head_step(dk: int, dv: int, in_bytes: int = 2) -> int:
     return 8 * dk * dv + in_bytes * (3 * dk + dv + 1) + 4 * dv
 
 
-def measured_traffic():
-    """HBM bytes per forward call and per decode step from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None for each when the
-    kernel sources have changed since the counters were taken."""
+def _traffic_record(name: str) -> dict:
+    """A committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or {} when the
+    kernel sources it names have changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_ckda_fwd_decode.txt")
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None, None
+        return {}
     for rel, digest in rec.get("sources_sha256", {}).items():
         try:
             with open(os.path.join(ROOT, rel), "rb") as f:
                 if hashlib.sha256(f.read()).hexdigest() != digest:
-                    return None, None
+                    return {}
         except OSError:
-            return None, None
-    return rec.get("forward_bytes_per_call"), rec.get("decode_bytes_per_step")
+            return {}
+    return rec
+
+
+def measured_traffic():
+    """Measured HBM bytes per forward call, per decode step and per backward
+    call (None where the profiled sources no longer match)."""
+    fd = _traffic_record("hbm_traffic_ckda_fwd_decode.txt")
+    bw = _traffic_record("hbm_traffic_ckda_bwd.txt")
+    return fd.get("forward_bytes_per_call"), fd.get("decode_bytes_per_step"), bw.get("backward_bytes_per_call")
 
 
 def time_region(fn, iters: int, stream):
@@ -89,6 +113,8 @@ def main(argv=None) -> int:
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--bwd-steps", type=int, default=5)
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the gated delta-rule path here is single-GPU "
@@ -133,7 +159,7 @@ def main(argv=None) -> int:
     ms_state = time_region(lambda i: fwd(0, kda.STAGE_STATE), args.steps, stream)
     print("[bench] prep %.3f ms, state %.3f ms" % (ms_prep, ms_state), file=sys.stderr, flush=True)
 
-    traffic_fwd, traffic_dec = measured_traffic()
+    traffic_fwd, traffic_dec, traffic_bwd = measured_traffic()
     head_tokens = tokens * H
     alg_bytes = head_tokens * fwd_bytes_per_head_token(dk, dv, False) + B * H * dk * dv * 4
     alg_flops = head_tokens * fwd_flops_per_head_token(dk, dv)
@@ -186,6 +212,53 @@ def main(argv=None) -> int:
         print("[bench] decode %.4f ms/step, %.1f GB/s" % (per, gbs), file=sys.stderr, flush=True)
         del S, steps
 
+    # ---------------------------------------------------------------- backward
+    backward = None
+    if not args.no_backward:
+        print("[bench] backward inputs", file=sys.stderr, flush=True)
+        wb = inputs.ckda_fwd(seed=0)
+        dO_c, dST_c = inputs.cotangents(wb, seed=0)
+        bt = [t.to(dev) for t in (wb.q, wb.k, wb.v, wb.gate, wb.beta, dO_c)]
+        dST = dST_c.to(dev)
+        wsb_b = kda.bwd_workspace_bytes(B, H, T, dk, dv)
+        ws_b = torch.empty(wsb_b, device=dev, dtype=torch.uint8)
+        gout = kda.chunk_bwd(*bt, dS_T=dST, workspace=ws_b)
+
+        def bwd(i):
+            kda.chunk_bwd(*bt, dS_T=dST, workspace=ws_b, out=gout)
+
+        bwd(0)
+        ms_b = time_region(bwd, args.bwd_steps, stream)
+        bflops = tokens * H * bwd_flops_per_head_token(dk, dv)
+        bbytes = tokens * H * bwd_bytes_per_head_token(dk, dv) + 3 * B * H * dk * dv * 4
+        tf = bflops / (ms_b * 1e-3) / 1e12
+        gbs_b = bbytes / (ms_b * 1e-3) / 1e9
+        backward = {
+            "workload": "ckda_bwd_b2_h16_t8192_d128",
+            "ms_per_call": round(ms_b, 4),
+            "tokens_per_s": round(tokens / (ms_b * 1e-3), 1),
+            "calls": args.bwd_steps,
+            "roofline": {"bound": "alu", "achieved": round(tf, 3), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic_bwd,
+                         "kernel": "kda_chunk_bwd: chunk_bwd_kernel then chunk_bwd_reduce_kernel",
+                         "flops_per_launch": bflops, "hbm_bytes_algorithmic": bbytes,
+                         "hbm_frac_algorithmic": round(gbs_b / HBM_PEAK_GBS, 4)},
+            "workspace_bytes": wsb_b,
+        }
+        print("[bench] backward %.3f ms/call" % ms_b, file=sys.stderr, flush=True)
+        if not args.no_cpu_baseline:
+            import oracle
+            Ts = 2048
+            sl = lambda t: t[:1, :Ts].contiguous()  # noqa: E731
+            t0 = time.time()
+            oracle.bwd(sl(wb.q), sl(wb.k), sl(wb.v), sl(wb.gate), sl(wb.beta), sl(dO_c), None, dST_c[:1], None, 0)
+            dt = time.time() - t0
+            backward["cpu_baseline"] = {
+                "value": round(Ts / dt, 1), "unit": "tokens/s", "cores": min(oracle.threads(), H), "kind": "oracle",
+                "sample": "first 2048 tokens of sequence 0, all 16 heads, fp64 reverse-mode token recurrence, "
+                          "%.2f s" % dt}
+        del bt, ws_b, gout
+
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -223,6 +296,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode": decode,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
     return 0
