@@ -213,7 +213,10 @@ chunk_bwd_kernel(BwdParams p) {
 
     const int tid = threadIdx.x, lane = tid % WAVE;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
-    const int cg = blockIdx.x % p.ncg, pair = blockIdx.x / p.ncg;
+    // the column groups of one (sequence, head) run on one XCD and share its L2
+    // for the inputs they all read
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int cg = item % p.ncg, pair = item / p.ncg;
     const int s = pair / p.H, h = pair % p.H;
     int t0, t1, b0;
     long base;
