@@ -9,5 +9,7 @@ the HIP kernels.
   gradient (``bwd``).
 * ``dense`` -- a second, independent formulation for tiny inputs: explicit
   dense transition matrices and their products.
+* ``gauge`` -- the gauge transform of Complex KDA onto positive gates
+  (cumulative gate signs folded into q and k), in numpy.
 """
 from .recurrence import build, bwd, fwd, decode_step, fwd_heads, threads  # noqa: F401

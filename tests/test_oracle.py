@@ -421,3 +421,42 @@ def test_pins_catch_planted_mistakes():
     for m in ("delta_then_gate", "read_before_gate", "sign", "no_beta"):
         bad = variant(m)(S0, k, np.zeros(d), alpha, 1.3)
         assert np.abs(bad - good).max() > 1e-3, m
+
+
+@pytest.mark.parametrize("gate_kind", [0, 1])
+def test_gauge_fold_reproduces_direct_run(gate_kind):
+    """oracle.gauge.fold, fed to the forward oracle with the final state's rows
+    flipped by c_T, reproduces the direct Complex KDA run (the gauge identity
+    of the Complex KDA summary, method step 5), also per packed sequence, with
+    exact zero and -1 gates and an empty sequence."""
+    from oracle import gauge
+    rng = np.random.default_rng(21 + gate_kind)
+    lengths = [9, 0, 14, 5]
+    T, H, dk, dv = sum(lengths), 2, 5, 3
+    q = rng.standard_normal((1, T, H, dk))
+    k = rng.standard_normal((1, T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, T, H, dv))
+    a = rng.uniform(-1, 1, (1, T, H, dk) if gate_kind == 0 else (1, T, H))
+    a.reshape(-1)[[3, 17]] = 0.0
+    a.reshape(-1)[[5, 11]] = -1.0
+    b = rng.uniform(0, 2, (1, T, H))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    S0 = rng.standard_normal((len(lengths), H, dk, dv))
+    o1, S1 = oracle.fwd(_t(q), _t(k), _t(v), _t(a), _t(b), _t(S0), cu, gate_kind)
+    qf, kf, af, cT = gauge.fold(_t(q), _t(k), _t(a), cu, gate_kind)
+    assert (af.numpy() >= 0).all()
+    o2, S2 = oracle.fwd(qf, kf, _t(v), af, _t(b), _t(S0), cu, gate_kind)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    flip = cT.astype(np.float64)[..., None]           # [nseq, H, gdim, 1]
+    np.testing.assert_allclose(S1, flip * S2, atol=1e-12)
+    # an exclusive product (c_{t-1}) in place of the inclusive one breaks it
+    c_excl = np.ones_like(a)
+    for s_ in range(len(lengths)):
+        t0, t1 = cu[s_], cu[s_ + 1]
+        if t1 > t0:
+            sg = np.where(a[0, t0:t1] < 0, -1.0, 1.0)
+            c_excl[0, t0:t1] = np.concatenate([np.ones_like(sg[:1]), np.cumprod(sg, axis=0)[:-1]])
+    ce = c_excl if gate_kind == 0 else c_excl[..., None]
+    o3, _ = oracle.fwd(_t(q * ce), _t(k * ce), _t(v), _t(np.abs(a)), _t(b), _t(S0), cu, gate_kind)
+    assert np.abs(o3 - o1).max() > 1e-3
