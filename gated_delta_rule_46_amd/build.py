@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkda.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_bwd.hip", "kda_gauge.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -159,6 +159,140 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
     return hip_status(e);
 }
 
+size_t kda_gauge_fold_workspace_bytes(int B, int H, int T, int dk, int N, int has_cu, int gate_kind) {
+    if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk)) return 0;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return 0;
+    if (has_cu && (B != 1 || N <= 0)) return 0;
+    return kda::gauge_fold_workspace_bytes(H, T, has_cu ? N : B, gate_kind == KDA_GATE_SCALAR ? 1 : dk);
+}
+
+int kda_gauge_fold(const void* q, const void* k, const void* gate, void* q_out, void* k_out, void* gate_out,
+                   int8_t* sign_T, int B, int H, int T, int dk, const int32_t* cu_seqlens, int N, int dtype,
+                   int gate_kind, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B <= 0 || H <= 0 || T < 0) return KDA_EINVAL;
+    if (!size_ok(dk)) return KDA_ENOTSUP;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ENOTSUP;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return KDA_ENOTSUP;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen) {
+        if (B != 1 || N <= 0) return KDA_EINVAL;
+    } else {
+        if (N != 0 && N != B) return KDA_EINVAL;
+        N = B;
+    }
+    const bool need_data = T > 0;
+    if (need_data && (!q || !k || !gate || !q_out || !k_out || !gate_out)) return KDA_EINVAL;
+    const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (need_data && (!aligned(q, es) || !aligned(k, es) || !aligned(gate, es) || !aligned(q_out, es) ||
+                      !aligned(k_out, es) || !aligned(gate_out, es)))
+        return KDA_EALIGN;
+    if ((workspace && !aligned(workspace)) || (varlen && !aligned(cu_seqlens, 4))) return KDA_EALIGN;
+    const size_t need = kda::gauge_fold_workspace_bytes(H, T, N, gate_kind == KDA_GATE_SCALAR ? 1 : dk);
+    if (workspace && workspace_bytes < need) return KDA_EINVAL;
+    if (!need_data && !sign_T) return KDA_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    bool owned = false;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, need, st);   // need >= 256
+        if (e != hipSuccess) return hip_status(e);
+        owned = true;
+    }
+    kda::GaugeArgs a{q, k, gate, q_out, k_out, gate_out, B, H, T, dk, cu_seqlens, N, dtype == KDA_BF16,
+                     gate_kind == KDA_GATE_SCALAR, ws, st};
+    hipError_t e = kda::launch_gauge_fold(a, sign_T);
+    if (owned) {
+        hipError_t f = hipFreeAsync(ws, st);
+        if (e == hipSuccess) e = f;
+    }
+    return hip_status(e);
+}
+
+namespace {
+// Offsets in the gauge route's workspace: the folded q, k and gate, c_T, the
+// fold's scratch, then the forward's own workspace (from off[5]).
+void gauge_route_parts(int B, int H, int T, int dk, int N, bool bf16, bool sg, size_t* off) {
+    const size_t es = bf16 ? 2 : 4, gdim = sg ? 1 : (size_t)dk;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t qb = al((size_t)B * T * H * dk * es), gb = al((size_t)B * T * H * gdim * es);
+    off[0] = 0;                  // q~
+    off[1] = off[0] + qb;        // k~
+    off[2] = off[1] + qb;        // alpha~
+    off[3] = off[2] + gb;        // c_T [N][H][gdim]
+    off[4] = off[3] + al((size_t)N * H * gdim);                                   // fold scratch
+    off[5] = off[4] + al(kda::gauge_fold_workspace_bytes(H, T, N, (int)gdim));     // forward workspace
+}
+}  // namespace
+
+size_t kda_chunk_fwd_gauge_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int N, int has_cu,
+                                           int dtype, int gate_kind) {
+    if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return 0;
+    if (has_cu && (B != 1 || N <= 0)) return 0;
+    const bool varlen = has_cu != 0;
+    size_t off[6];
+    gauge_route_parts(B, H, T, dk, varlen ? N : B, dtype == KDA_BF16, gate_kind == KDA_GATE_SCALAR, off);
+    return off[5] + kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, varlen ? N : B, dtype == KDA_BF16);
+}
+
+int kda_chunk_fwd_gauge(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                        const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
+                        const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (B <= 0 || H <= 0 || T < 0) return KDA_EINVAL;
+    if (!size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return KDA_ENOTSUP;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ENOTSUP;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return KDA_ENOTSUP;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen) {
+        if (B != 1 || N <= 0) return KDA_EINVAL;
+    } else {
+        if (N != 0 && N != B) return KDA_EINVAL;
+        N = B;
+    }
+    const bool need_data = T > 0;
+    if (need_data && (!q || !k || !v || !gate || !beta || !o)) return KDA_EINVAL;
+    const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (need_data && (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(gate) || !aligned(beta, es) ||
+                      !aligned(o, 4)))
+        return KDA_EALIGN;
+    if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) || (workspace && !aligned(workspace))) return KDA_EALIGN;
+    if (varlen && !aligned(cu_seqlens, 4)) return KDA_EALIGN;
+    const bool sg = gate_kind == KDA_GATE_SCALAR;
+    size_t off[6];
+    gauge_route_parts(B, H, T, dk, N, dtype == KDA_BF16, sg, off);
+    const size_t fwd_ws = kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, N, dtype == KDA_BF16);
+    const size_t need = off[5] + fwd_ws;
+    if (workspace && workspace_bytes < need) return KDA_EINVAL;
+    if (!need_data && !S_T) return KDA_OK;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    bool owned = false;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, need, st);
+        if (e != hipSuccess) return hip_status(e);
+        owned = true;
+    }
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    int8_t* sign = reinterpret_cast<int8_t*>(w + off[3]);
+    kda::GaugeArgs g{q, k, gate, w + off[0], w + off[1], w + off[2], B, H, T, dk, cu_seqlens, N, dtype == KDA_BF16,
+                     sg, w + off[4], st};
+    hipError_t e = kda::launch_gauge_fold(g, sign);
+    if (e == hipSuccess) {
+        kda::ChunkArgs a{w + off[0], w + off[1], v, w + off[2], beta, S0, o, S_T, B, H, T, dk, dv, chunk, cu_seqlens,
+                         N, dtype == KDA_BF16, sg, w + off[5], st, KDA_STAGE_ALL};
+        e = kda::launch_chunk_fwd(a);
+    }
+    if (e == hipSuccess && S_T) e = kda::launch_gauge_state_flip(S_T, sign, N, H, dk, dv, sg, st);
+    if (owned) {
+        hipError_t f = hipFreeAsync(ws, st);
+        if (e == hipSuccess) e = f;
+    }
+    return hip_status(e);
+}
+
 int kda_decode_step(const void* q, const void* k, const void* v, const void* gate, const void* beta,
                     float* S, float* o, int N, int H, int dk, int dv, int dtype, int gate_kind, void* stream) {
     if (N <= 0 || H <= 0) return KDA_EINVAL;

@@ -42,6 +42,17 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
+struct GaugeArgs {
+    const void *q, *k, *gate;
+    void *q_out, *k_out, *gate_out;
+    int B, H, T, dk;
+    const int32_t* cu_seqlens;
+    int N;
+    bool bf16, scalar_gate;
+    void* workspace;   // gauge_fold_workspace_bytes(...) bytes: segment parities
+    hipStream_t stream;
+};
+
 // Bytes of intermediates one (chunk, head) pair occupies in the workspace.
 size_t chunk_block_bytes(int dk, int dv, int chunk, bool bf16);
 // Upper bound on the number of chunks over all sequences.
@@ -51,6 +62,13 @@ size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, boo
 
 // Workspace bytes of one backward call (checkpoints and partial sums).
 size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N);
+
+// Gauge fold: workspace bytes (segment parities), the fold (c_T into sign_dev
+// when it is not null), and the row flip of a final state by c_T.
+size_t gauge_fold_workspace_bytes(int H, int T, int N, int gdim);
+hipError_t launch_gauge_fold(const GaugeArgs& a, int8_t* sign_dev);
+hipError_t launch_gauge_state_flip(float* S, const int8_t* sign, int N, int H, int dk, int dv, bool scalar_gate,
+                                   hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);

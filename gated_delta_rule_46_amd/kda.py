@@ -22,7 +22,9 @@ GATE_CHANNEL, GATE_SCALAR = 0, 1
 STAGE_PREP, STAGE_STATE, STAGE_ALL = 1, 2, 3
 
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd",
-           "kda_chunk_bwd_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error", "kda_version")
+           "kda_chunk_bwd_workspace_bytes", "kda_gauge_fold", "kda_gauge_fold_workspace_bytes", "kda_chunk_fwd_gauge",
+           "kda_chunk_fwd_gauge_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error",
+           "kda_version")
 
 
 class KDAError(RuntimeError):
@@ -55,6 +57,14 @@ def _lib():
         lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
         lib.kda_chunk_bwd_workspace_bytes.restype = sz
         lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 7
+        lib.kda_gauge_fold.restype = i
+        lib.kda_gauge_fold.argtypes = [vp] * 7 + [i] * 4 + [vp, i, i, i, vp, sz, vp]
+        lib.kda_gauge_fold_workspace_bytes.restype = sz
+        lib.kda_gauge_fold_workspace_bytes.argtypes = [i] * 7
+        lib.kda_chunk_fwd_gauge.restype = i
+        lib.kda_chunk_fwd_gauge.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
+        lib.kda_chunk_fwd_gauge_workspace_bytes.restype = sz
+        lib.kda_chunk_fwd_gauge_workspace_bytes.argtypes = [i] * 10
         lib.kda_decode_step.restype = i
         lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.kda_strerror.restype = ctypes.c_char_p
@@ -212,6 +222,63 @@ def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_bwd")
     return out
+
+
+def gauge_fold(q, k, gate, cu_seqlens=None, gate_kind: Optional[int] = None, stream=None):
+    """Gauge fold: returns (q~, k~, gate~, c_T) with c_T int8 [N,H,dk] or
+    [N,H]. Inputs as for chunk_fwd."""
+    B, T, H, dk = q.shape
+    device = q.device
+    for name, t in (("q", q), ("k", k), ("gate", gate)):
+        _check_dev(name, t, device)
+    if gate_kind is None:
+        gate_kind = GATE_SCALAR if gate.dim() == 3 else GATE_CHANNEL
+    dt = _dtype_code(q)
+    varlen = cu_seqlens is not None
+    N = int(cu_seqlens.numel() - 1) if varlen else B
+    qo, ko, go = torch.empty_like(q), torch.empty_like(k), torch.empty_like(gate)
+    sign = torch.empty((N, H, dk) if gate_kind == GATE_CHANNEL else (N, H), device=device, dtype=torch.int8)
+    need = int(_lib().kda_gauge_fold_workspace_bytes(B, H, T, dk, N, int(varlen), int(gate_kind)))
+    ws = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
+    st = _stream_handle(stream, device)
+    rc = _lib().kda_gauge_fold(_ptr(q), _ptr(k), _ptr(gate), _ptr(qo), _ptr(ko), _ptr(go), _ptr(sign), B, H, T, dk,
+                               _ptr(cu_seqlens), N if varlen else 0, dt, int(gate_kind), _ptr(ws), need,
+                               ctypes.c_void_p(st) if st else None)
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_gauge_fold")
+    return qo, ko, go, sign
+
+
+def chunk_fwd_gauge(q, k, v, gate, beta, S0=None, cu_seqlens=None, chunk: int = 64, gate_kind: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """chunk_fwd through the gauge transform (kda_chunk_fwd_gauge). Same
+    arguments and results as chunk_fwd."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    device = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta)):
+        _check_dev(name, t, device)
+    if gate_kind is None:
+        gate_kind = GATE_SCALAR if gate.dim() == 3 else GATE_CHANNEL
+    dt = _dtype_code(q)
+    varlen = cu_seqlens is not None
+    N = int(cu_seqlens.numel() - 1) if varlen else B
+    if out is None:
+        out = torch.empty((B, T, H, dv), device=device, dtype=torch.float32)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), device=device, dtype=torch.float32)
+    need = int(_lib().kda_chunk_fwd_gauge_workspace_bytes(B, H, T, dk, dv, chunk, N, int(varlen), dt,
+                                                          int(gate_kind)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
+    st = _stream_handle(stream, device)
+    rc = _lib().kda_chunk_fwd_gauge(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_T),
+                                    B, H, T, dk, dv, chunk, _ptr(cu_seqlens), N if varlen else 0, dt, int(gate_kind),
+                                    _ptr(workspace), workspace.numel(), ctypes.c_void_p(st) if st else None)
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_gauge")
+    return out, S_T
 
 
 def decode_step(q, k, v, gate, beta, S, out: Optional[torch.Tensor] = None, gate_kind: Optional[int] = None,

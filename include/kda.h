@@ -177,6 +177,43 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
                   int dk, int dv, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Gauge transform of Complex KDA onto positive gates (Complex KDA summary,
+ * method step 5: the cumulative gate signs are absorbed into queries and
+ * keys). Per sequence, head and key channel (per sequence and head for the
+ * scalar gate), with s_t = -1 where gate_t < 0 and +1 otherwise (zero and
+ * -0.0 included) and c_t = s_1 ... s_t:
+ *   q_out_t = c_t q_t,  k_out_t = c_t k_t,  gate_out_t = |gate_t|
+ * Running the recurrence on the outputs gives the same o as on the inputs,
+ * and a final state whose rows differ by c_T: S_T = Diag(c_T) S~_T.
+ * Every output value is an input value with its sign changed or cleared
+ * (bit-exact in both dtypes). Layouts, N, cu_seqlens, dtype and gate_kind as
+ * for kda_chunk_fwd; outputs have the input layouts and dtype and must not
+ * alias the inputs. sign_T: device int8 [N, H, dk] (channel gate) or [N, H]
+ * (scalar gate) receiving c_T (+1 / -1), or NULL. workspace: at least
+ * kda_gauge_fold_workspace_bytes(...) bytes, or NULL (stream-ordered pool).
+ * Returns KDA_OK or a negative status.
+ */
+size_t kda_gauge_fold_workspace_bytes(int B, int H, int T, int dk, int N, int has_cu_seqlens, int gate_kind);
+int kda_gauge_fold(const void* q, const void* k, const void* gate, void* q_out, void* k_out, void* gate_out,
+                   int8_t* sign_T, int B, int H, int T, int dk, const int32_t* cu_seqlens, int N, int dtype,
+                   int gate_kind, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd computed through the gauge transform: kda_gauge_fold into
+ * the workspace, the chunkwise forward on the folded (positive-gate)
+ * inputs, then S_T's rows multiplied by c_T. Same arguments, results and
+ * tolerances as kda_chunk_fwd; the workspace is
+ * kda_chunk_fwd_gauge_workspace_bytes(...) bytes (the folded q, k and gate
+ * plus the forward's own workspace), or NULL.
+ */
+size_t kda_chunk_fwd_gauge_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int N,
+                                           int has_cu_seqlens, int dtype, int gate_kind);
+int kda_chunk_fwd_gauge(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                        const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
+                        const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* kda_strerror(int status);
 
