@@ -114,6 +114,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-gauge", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -178,6 +179,25 @@ def main(argv=None) -> int:
         "mfma_frac_algorithmic": round(alg_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_ms": {"chunk_prep_kernel": round(ms_prep, 4), "chunk_state_slice_kernel": round(ms_state, 4)},
     }
+    # the same workload through the gauge route (signs folded into q and k,
+    # positive-gate forward, S_T rows flipped back)
+    gauge = None
+    if not args.no_gauge:
+        wsg = torch.empty(kda.fwd_gauge_workspace_bytes(B, H, T, dk, dv, C), device=dev, dtype=torch.uint8)
+
+        def fwd_g(i):
+            q, k, v, g, b = sets[i % 2]
+            kda.chunk_fwd_gauge(q, k, v, g, b, chunk=C, gate_kind=0, out=o, S_T=ST, workspace=wsg)
+
+        for i in range(args.warmup):
+            fwd_g(i)
+        ms_g = time_region(fwd_g, args.steps, stream)
+        ms_d = time_region(fwd, args.steps, stream)   # direct route again, same box, same moment
+        gauge = {"workload": "ckda_fwd_b2_h16_t8192_d128_chunk64", "ms_per_call": round(ms_g, 4),
+                 "tokens_per_s": round(tokens / (ms_g * 1e-3), 1), "direct_ms_per_call": round(ms_d, 4),
+                 "throughput_vs_direct": round(ms_d / ms_g, 4)}
+        print("[bench] gauge route %.3f ms/step (direct %.3f)" % (ms_g, ms_d), file=sys.stderr, flush=True)
+        del wsg
     del sets, ws, o
 
     # ---------------------------------------------------------------- decode
@@ -297,6 +317,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "decode": decode,
         "backward": backward,
+        "gauge_route": gauge,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -183,8 +183,9 @@ int kda_gauge_fold(const void* q, const void* k, const void* gate, void* q_out, 
     const bool need_data = T > 0;
     if (need_data && (!q || !k || !gate || !q_out || !k_out || !gate_out)) return KDA_EINVAL;
     const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
-    if (need_data && (!aligned(q, es) || !aligned(k, es) || !aligned(gate, es) || !aligned(q_out, es) ||
-                      !aligned(k_out, es) || !aligned(gate_out, es)))
+    const uintptr_t ga = gate_kind == KDA_GATE_SCALAR ? es : 16;   // channel gates are read 8 channels at a time
+    if (need_data && (!aligned(q) || !aligned(k) || !aligned(gate, ga) || !aligned(q_out) || !aligned(k_out) ||
+                      !aligned(gate_out, ga)))
         return KDA_EALIGN;
     if ((workspace && !aligned(workspace)) || (varlen && !aligned(cu_seqlens, 4))) return KDA_EALIGN;
     const size_t need = kda::gauge_fold_workspace_bytes(H, T, N, gate_kind == KDA_GATE_SCALAR ? 1 : dk);

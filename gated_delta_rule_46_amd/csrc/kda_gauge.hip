@@ -11,7 +11,7 @@
 // bit flipped or cleared, so the fold is exact in any precision.
 //
 // The sign products are a prefix XOR of sign bits along the sequence, done
-// in three launches over (sequence, head, 256-token segment): the parity of
+// in three launches over (sequence, head, 32-token segment): the parity of
 // each segment; an exclusive scan over the segments; the fold itself, each
 // segment starting from its prefix.
 #include "kda_common.h"
@@ -20,8 +20,9 @@
 namespace kda {
 namespace {
 
-constexpr int G_SEG = 256;   // tokens per segment
-constexpr int G_NT = 128;    // threads per block: one key channel each
+constexpr int G_SEG = 32;    // tokens per segment
+constexpr int G_UN = 8;      // tokens whose loads are issued together
+constexpr int G_NT = 64;     // threads per block (one wave)
 
 struct GaugeParams {
     const void *q, *k, *gate;
@@ -55,19 +56,72 @@ __device__ __forceinline__ void seq_bounds(const GaugeParams& p, int s, int& b0,
     }
 }
 
+// Thread layout of the parity and fold kernels: each thread owns 8
+// consecutive key channels of one (sequence, head) -- 16-byte accesses for
+// bf16 -- and the dk / 8 threads of a head are adjacent lanes, so a wave
+// reads several heads' contiguous channel rows of one token at once.
+constexpr int G_CPT = 8;
+
 template <class TIn>
-__global__ void __launch_bounds__(G_NT) gauge_parity_kernel(GaugeParams p) {
+struct Lane8 {
     using U = typename Bits<TIn>::U;
-    const int sh = blockIdx.x, g = blockIdx.y, ch = threadIdx.x;
-    const int s = sh / p.H, h = sh % p.H;
+    static constexpr int NV = (int)(G_CPT * sizeof(U)) / 16;   // 16-byte pieces
+    uint4 v[NV];
+    __device__ __forceinline__ void load(const U* p) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = reinterpret_cast<const uint4*>(p)[i];
+    }
+    __device__ __forceinline__ void store(U* p) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) reinterpret_cast<uint4*>(p)[i] = v[i];
+    }
+    __device__ __forceinline__ U get(int c) const { return reinterpret_cast<const U*>(v)[c]; }
+    __device__ __forceinline__ void set(int c, U x) { reinterpret_cast<U*>(v)[c] = x; }
+};
+
+// (sequence, head) and first channel of this thread; false past the last head
+__device__ __forceinline__ bool gauge_lane(const GaugeParams& p, int nsh, int& sh, int& c0) {
+    const int tph = p.dk / G_CPT;                      // threads per head
+    const int hpb = G_NT / tph;                        // heads per block
+    sh = blockIdx.x * hpb + threadIdx.x / tph;
+    c0 = (threadIdx.x % tph) * G_CPT;
+    return sh < nsh;
+}
+
+template <class TIn>
+__global__ void __launch_bounds__(G_NT) gauge_parity_kernel(GaugeParams p, int nsh) {
+    using U = typename Bits<TIn>::U;
+    int sh, c0;
+    if (!gauge_lane(p, nsh, sh, c0)) return;
+    const bool sg = p.gdim == 1;
+    if (sg && c0 != 0) return;
+    const int g = blockIdx.y, s = sh / p.H, h = sh % p.H;
     int b0, t0, len;
     seq_bounds(p, s, b0, t0, len);
-    if (ch >= p.gdim) return;
     const int ta = g * G_SEG, tb = min(len, ta + G_SEG);
-    const U* A = (const U*)p.gate;
-    uint32_t x = 0;
-    for (int t = ta; t < tb; ++t) x ^= is_neg<TIn>(A[(((size_t)b0 * p.T + t0 + t) * p.H + h) * p.gdim + ch]);
-    p.par[((size_t)sh * p.nseg + g) * p.gdim + ch] = (uint8_t)x;
+    const U* __restrict__ A = (const U*)p.gate;
+    uint32_t x = 0;   // bit c: parity of channel c0 + c (bit 0 only for the scalar gate)
+    for (int t = ta; t < tb; t += G_UN) {
+        Lane8<TIn> a[G_UN];
+#pragma unroll
+        for (int u = 0; u < G_UN; ++u) {
+            const size_t row = ((size_t)b0 * p.T + t0 + t + u) * p.H + h;
+            if (t + u < tb) {
+                if (sg) a[u].set(0, A[row]);
+                else a[u].load(A + row * p.dk + c0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < Lane8<TIn>::NV; ++i) a[u].v[i] = uint4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < G_UN; ++u)
+#pragma unroll
+            for (int c = 0; c < (sg ? 1 : G_CPT); ++c) x ^= (uint32_t)is_neg<TIn>(a[u].get(c)) << c;
+    }
+    uint8_t* dst = p.par + ((size_t)sh * p.nseg + g) * p.gdim + c0;
+#pragma unroll
+    for (int c = 0; c < (sg ? 1 : G_CPT); ++c) dst[c] = (uint8_t)((x >> c) & 1u);
 }
 
 // Exclusive prefix over the segments of each (sequence, head, channel), in
@@ -76,44 +130,79 @@ __global__ void __launch_bounds__(256) gauge_scan_kernel(GaugeParams p, int rows
     const int r = blockIdx.x * 256 + threadIdx.x;   // (sequence, head) * gdim + channel
     if (r >= rows) return;
     const int sh = r / p.gdim, ch = r % p.gdim;
+    uint8_t* __restrict__ base = p.par + (size_t)sh * p.nseg * p.gdim + ch;
     uint32_t acc = 0;
-    for (int g = 0; g < p.nseg; ++g) {
-        uint8_t* x = p.par + ((size_t)sh * p.nseg + g) * p.gdim + ch;
-        const uint32_t v = *x;
-        *x = (uint8_t)acc;
-        acc ^= v;
+    for (int g0 = 0; g0 < p.nseg; g0 += 32) {   // 32 loads in flight, then the scan
+        uint32_t v[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) v[u] = g0 + u < p.nseg ? base[(size_t)(g0 + u) * p.gdim] : 0u;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+            if (g0 + u < p.nseg) base[(size_t)(g0 + u) * p.gdim] = (uint8_t)acc;
+            acc ^= v[u];
+        }
     }
     if (p.sign) p.sign[r] = acc ? (int8_t)-1 : (int8_t)1;
 }
 
 template <class TIn>
-__global__ void __launch_bounds__(G_NT) gauge_apply_kernel(GaugeParams p) {
+__global__ void __launch_bounds__(G_NT) gauge_apply_kernel(GaugeParams p, int nsh) {
     using U = typename Bits<TIn>::U;
-    const int sh = blockIdx.x, g = blockIdx.y, ch = threadIdx.x;
-    const int s = sh / p.H, h = sh % p.H;
+    int sh, c0;
+    if (!gauge_lane(p, nsh, sh, c0)) return;
+    const int g = blockIdx.y, s = sh / p.H, h = sh % p.H;
     int b0, t0, len;
     seq_bounds(p, s, b0, t0, len);
-    if (ch >= p.dk) return;
     const int ta = g * G_SEG, tb = min(len, ta + G_SEG);
     if (ta >= tb) return;
     const bool sg = p.gdim == 1;
-    const int gc = sg ? 0 : ch;   // this thread's gate channel
-    uint32_t par = p.par[((size_t)sh * p.nseg + g) * p.gdim + gc];
-    const U* A = (const U*)p.gate;
-    const U* Q = (const U*)p.q;
-    const U* K = (const U*)p.k;
-    U* Ao = (U*)p.go;
-    U* Qo = (U*)p.qo;
-    U* Ko = (U*)p.ko;
-#pragma unroll 4
-    for (int t = ta; t < tb; ++t) {
-        const size_t row = ((size_t)b0 * p.T + t0 + t) * p.H + h;
-        const U a = A[row * p.gdim + gc];
-        par ^= is_neg<TIn>(a);
-        const U flip = par ? Bits<TIn>::SIGN : (U)0;
-        Qo[row * p.dk + ch] = (U)(Q[row * p.dk + ch] ^ flip);
-        Ko[row * p.dk + ch] = (U)(K[row * p.dk + ch] ^ flip);
-        if (!sg || ch == 0) Ao[row * p.gdim + gc] = (U)(a & (U)~Bits<TIn>::SIGN);
+    const uint8_t* pre = p.par + ((size_t)sh * p.nseg + g) * p.gdim;
+    uint32_t par = 0;   // bit c: running parity of channel c0 + c (all bits equal for the scalar gate)
+#pragma unroll
+    for (int c = 0; c < G_CPT; ++c) par |= (uint32_t)(pre[sg ? 0 : c0 + c] & 1u) << c;
+    const U* __restrict__ A = (const U*)p.gate;
+    const U* __restrict__ Q = (const U*)p.q;
+    const U* __restrict__ K = (const U*)p.k;
+    U* __restrict__ Ao = (U*)p.go;
+    U* __restrict__ Qo = (U*)p.qo;
+    U* __restrict__ Ko = (U*)p.ko;
+    for (int t = ta; t < tb; t += G_UN) {
+        Lane8<TIn> a[G_UN], qv[G_UN], kv[G_UN];
+        U as[G_UN];
+#pragma unroll
+        for (int u = 0; u < G_UN; ++u) {
+            if (t + u >= tb) continue;
+            const size_t row = ((size_t)b0 * p.T + t0 + t + u) * p.H + h;
+            if (sg) as[u] = A[row];
+            else a[u].load(A + row * p.dk + c0);
+            qv[u].load(Q + row * p.dk + c0);
+            kv[u].load(K + row * p.dk + c0);
+        }
+#pragma unroll
+        for (int u = 0; u < G_UN; ++u) {
+            if (t + u >= tb) break;
+            const size_t row = ((size_t)b0 * p.T + t0 + t + u) * p.H + h;
+            if (sg) {
+                par ^= is_neg<TIn>(as[u]) ? 0xFFu : 0u;
+                if (c0 == 0) Ao[row] = (U)(as[u] & (U)~Bits<TIn>::SIGN);
+            } else {
+#pragma unroll
+                for (int c = 0; c < G_CPT; ++c) {
+                    const U x = a[u].get(c);
+                    par ^= (uint32_t)is_neg<TIn>(x) << c;
+                    a[u].set(c, (U)(x & (U)~Bits<TIn>::SIGN));
+                }
+                a[u].store(Ao + row * p.dk + c0);
+            }
+#pragma unroll
+            for (int c = 0; c < G_CPT; ++c) {
+                const U flip = ((par >> c) & 1u) ? Bits<TIn>::SIGN : (U)0;
+                qv[u].set(c, (U)(qv[u].get(c) ^ flip));
+                kv[u].set(c, (U)(kv[u].get(c) ^ flip));
+            }
+            qv[u].store(Qo + row * p.dk + c0);
+            kv[u].store(Ko + row * p.dk + c0);
+        }
     }
 }
 
@@ -154,10 +243,11 @@ hipError_t launch_gauge_fold(const GaugeArgs& a, int8_t* sign_dev) {
     p.dk = a.dk;
     p.gdim = a.scalar_gate ? 1 : a.dk;
     p.nseg = gauge_segments(a.T);
-    const dim3 grid((unsigned)(a.N * a.H), (unsigned)p.nseg);
+    const int nsh = a.N * a.H, hpb = G_NT / (a.dk / G_CPT);
+    const dim3 grid((unsigned)((nsh + hpb - 1) / hpb), (unsigned)p.nseg);
     if (p.nseg > 0) {
-        if (a.bf16) hipLaunchKernelGGL(gauge_parity_kernel<uint16_t>, grid, dim3(G_NT), 0, a.stream, p);
-        else hipLaunchKernelGGL(gauge_parity_kernel<float>, grid, dim3(G_NT), 0, a.stream, p);
+        if (a.bf16) hipLaunchKernelGGL(gauge_parity_kernel<uint16_t>, grid, dim3(G_NT), 0, a.stream, p, nsh);
+        else hipLaunchKernelGGL(gauge_parity_kernel<float>, grid, dim3(G_NT), 0, a.stream, p, nsh);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -166,8 +256,8 @@ hipError_t launch_gauge_fold(const GaugeArgs& a, int8_t* sign_dev) {
     hipLaunchKernelGGL(gauge_scan_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, a.stream, p, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nseg == 0) return e;
-    if (a.bf16) hipLaunchKernelGGL(gauge_apply_kernel<uint16_t>, grid, dim3(G_NT), 0, a.stream, p);
-    else hipLaunchKernelGGL(gauge_apply_kernel<float>, grid, dim3(G_NT), 0, a.stream, p);
+    if (a.bf16) hipLaunchKernelGGL(gauge_apply_kernel<uint16_t>, grid, dim3(G_NT), 0, a.stream, p, nsh);
+    else hipLaunchKernelGGL(gauge_apply_kernel<float>, grid, dim3(G_NT), 0, a.stream, p, nsh);
     return hipGetLastError();
 }
 

@@ -249,6 +249,13 @@ def gauge_fold(q, k, gate, cu_seqlens=None, gate_kind: Optional[int] = None, str
     return qo, ko, go, sign
 
 
+def fwd_gauge_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int, N: int = 0, varlen: bool = False,
+                              dtype: torch.dtype = torch.bfloat16, gate_kind: int = GATE_CHANNEL) -> int:
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(_lib().kda_chunk_fwd_gauge_workspace_bytes(B, H, T, dk, dv, chunk, N if varlen else B, int(varlen), code,
+                                                          int(gate_kind)))
+
+
 def chunk_fwd_gauge(q, k, v, gate, beta, S0=None, cu_seqlens=None, chunk: int = 64, gate_kind: Optional[int] = None,
                     out: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None):
@@ -268,8 +275,7 @@ def chunk_fwd_gauge(q, k, v, gate, beta, S0=None, cu_seqlens=None, chunk: int = 
         out = torch.empty((B, T, H, dv), device=device, dtype=torch.float32)
     if S_T is None:
         S_T = torch.empty((N, H, dk, dv), device=device, dtype=torch.float32)
-    need = int(_lib().kda_chunk_fwd_gauge_workspace_bytes(B, H, T, dk, dv, chunk, N, int(varlen), dt,
-                                                          int(gate_kind)))
+    need = fwd_gauge_workspace_bytes(B, H, T, dk, dv, chunk, N, varlen, q.dtype, gate_kind)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
     st = _stream_handle(stream, device)

@@ -189,7 +189,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
  * Every output value is an input value with its sign changed or cleared
  * (bit-exact in both dtypes). Layouts, N, cu_seqlens, dtype and gate_kind as
  * for kda_chunk_fwd; outputs have the input layouts and dtype and must not
- * alias the inputs. sign_T: device int8 [N, H, dk] (channel gate) or [N, H]
+ * alias the inputs. q, k, their outputs and (channel gate) gate and gate_out
+ * must be 16-byte aligned. sign_T: device int8 [N, H, dk] (channel gate) or [N, H]
  * (scalar gate) receiving c_T (+1 / -1), or NULL. workspace: at least
  * kda_gauge_fold_workspace_bytes(...) bytes, or NULL (stream-ordered pool).
  * Returns KDA_OK or a negative status.
