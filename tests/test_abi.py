@@ -98,3 +98,61 @@ def test_workspace_bytes(lib):
     v = f(1, 2, 100, 16, 16, 16, N=5, varlen=True)
     assert v >= f(1, 2, 100, 16, 16, 16)
     assert f(2, 2, 100, 16, 16, 16, N=5, varlen=True) == 0           # varlen needs B == 1
+
+
+def test_bwd_validation(lib):
+    def bwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, S0=None, dO=FAKE, dST=None, gq=FAKE, gk=FAKE,
+                 gv=FAKE, gg=FAKE, gb=FAKE, gS0=None, B=1, H=2, T=8, dk=16, dv=16, cu=None, N=0,
+                 dtype=kda.KDA_BF16, gate_kind=0, ws=FAKE, wsb=0, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_bwd(*a.values())
+    assert bwd(B=0) == kda.KDA_EINVAL
+    assert bwd(dk=24) == kda.KDA_ENOTSUP
+    assert bwd(dv=8) == kda.KDA_ENOTSUP
+    assert bwd(dtype=5) == kda.KDA_ENOTSUP
+    assert bwd(gate_kind=3) == kda.KDA_ENOTSUP
+    assert bwd(dO=None) == kda.KDA_EINVAL
+    assert bwd(gq=None) == kda.KDA_EINVAL
+    assert bwd(dO=FAKE + 4) == kda.KDA_EALIGN                         # dO is read 16 bytes at a time
+    assert bwd(gv=FAKE + 8) == kda.KDA_EALIGN
+    assert bwd(gS0=FAKE + 4) == kda.KDA_EALIGN
+    assert bwd(q=FAKE + 1) == kda.KDA_EALIGN
+    assert bwd(wsb=1) == kda.KDA_EINVAL                               # workspace too small
+    assert bwd(cu=FAKE, B=2, N=2) == kda.KDA_EINVAL
+    assert bwd(N=4) == kda.KDA_EINVAL
+    assert kda.bwd_workspace_bytes(1, 2, 64, 24, 16) == 0
+    w = kda.bwd_workspace_bytes(1, 2, 64, 16, 16)
+    assert w > 0 and w % 256 == 0
+    assert kda.bwd_workspace_bytes(1, 2, 65, 16, 16) > w              # one more checkpoint and token
+    assert kda.bwd_workspace_bytes(2, 2, 64, 16, 16, N=2, varlen=True) == 0
+
+
+def test_gauge_validation(lib):
+    def fold(**kw):
+        a = dict(q=FAKE, k=FAKE, gate=FAKE, qo=FAKE, ko=FAKE, go=FAKE, sign=None, B=1, H=2, T=8, dk=16, cu=None,
+                 N=0, dtype=kda.KDA_BF16, gate_kind=0, ws=FAKE, wsb=0, stream=None)
+        a.update(kw)
+        return lib.kda_gauge_fold(*a.values())
+    assert fold(B=0) == kda.KDA_EINVAL
+    assert fold(dk=12) == kda.KDA_ENOTSUP
+    assert fold(gate_kind=2) == kda.KDA_ENOTSUP
+    assert fold(qo=None) == kda.KDA_EINVAL
+    assert fold(q=FAKE + 2) == kda.KDA_EALIGN                         # read 8 channels (16 bytes) at a time
+    assert fold(go=FAKE + 2) == kda.KDA_EALIGN                        # channel gate likewise
+    assert fold(wsb=1) == kda.KDA_EINVAL
+    args = ("q", "k", "v", "gate", "beta", "S0", "o", "S_T", "B", "H", "T", "dk", "dv", "chunk", "cu", "N", "dtype",
+            "gate_kind", "ws", "wsb", "stream")
+
+    def route(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, S0=None, o=FAKE, S_T=None, B=1, H=2, T=8,
+                 dk=16, dv=16, chunk=16, cu=None, N=0, dtype=kda.KDA_BF16, gate_kind=0, ws=FAKE, wsb=0,
+                 stream=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_gauge(*[a[x] for x in args])
+    assert route(B=0) == kda.KDA_EINVAL
+    assert route(chunk=8) == kda.KDA_ENOTSUP
+    assert route(o=None) == kda.KDA_EINVAL
+    assert route(q=FAKE + 2) == kda.KDA_EALIGN
+    assert route(wsb=1) == kda.KDA_EINVAL
+    assert kda.fwd_gauge_workspace_bytes(1, 2, 64, 16, 16, 16) > kda.workspace_bytes(1, 2, 64, 16, 16, 16)
