@@ -83,7 +83,7 @@ struct Lane8 {
 __device__ __forceinline__ bool gauge_lane(const GaugeParams& p, int nsh, int& sh, int& c0) {
     const int tph = p.dk / G_CPT;                      // threads per head
     const int hpb = G_NT / tph;                        // heads per block
-    sh = blockIdx.x * hpb + threadIdx.x / tph;
+    sh = blockIdx.y * hpb + threadIdx.x / tph;
     c0 = (threadIdx.x % tph) * G_CPT;
     return sh < nsh;
 }
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(G_NT) gauge_parity_kernel(GaugeParams p, int n
     if (!gauge_lane(p, nsh, sh, c0)) return;
     const bool sg = p.gdim == 1;
     if (sg && c0 != 0) return;
-    const int g = blockIdx.y, s = sh / p.H, h = sh % p.H;
+    const int g = blockIdx.x, s = sh / p.H, h = sh % p.H;
     int b0, t0, len;
     seq_bounds(p, s, b0, t0, len);
     const int ta = g * G_SEG, tb = min(len, ta + G_SEG);
@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(G_NT) gauge_apply_kernel(GaugeParams p, int ns
     using U = typename Bits<TIn>::U;
     int sh, c0;
     if (!gauge_lane(p, nsh, sh, c0)) return;
-    const int g = blockIdx.y, s = sh / p.H, h = sh % p.H;
+    const int g = blockIdx.x, s = sh / p.H, h = sh % p.H;
     int b0, t0, len;
     seq_bounds(p, s, b0, t0, len);
     const int ta = g * G_SEG, tb = min(len, ta + G_SEG);
@@ -244,7 +244,8 @@ hipError_t launch_gauge_fold(const GaugeArgs& a, int8_t* sign_dev) {
     p.gdim = a.scalar_gate ? 1 : a.dk;
     p.nseg = gauge_segments(a.T);
     const int nsh = a.N * a.H, hpb = G_NT / (a.dk / G_CPT);
-    const dim3 grid((unsigned)((nsh + hpb - 1) / hpb), (unsigned)p.nseg);
+    // segments along x (long sequences), groups of heads along y
+    const dim3 grid((unsigned)p.nseg, (unsigned)((nsh + hpb - 1) / hpb));
     if (p.nseg > 0) {
         if (a.bf16) hipLaunchKernelGGL(gauge_parity_kernel<uint16_t>, grid, dim3(G_NT), 0, a.stream, p, nsh);
         else hipLaunchKernelGGL(gauge_parity_kernel<float>, grid, dim3(G_NT), 0, a.stream, p, nsh);
