@@ -105,11 +105,42 @@ def time_region(fn, iters: int, stream):
     return start.elapsed_time(end) / iters   # ms per call
 
 
+def per_call_ms(fn, iters: int, stream):
+    """Median and minimum of single-call durations (events around each call),
+    measured after the bracketed region."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2], t[0]
+
+
+def gpu_clock():
+    """The GPU clock line of rocm-smi, or None where it is not available."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for line in r.stdout.splitlines():
+        if "sclk" in line.lower():
+            return " ".join(line.split())
+    return None
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # After the device has idled, calls run about 15% slower for the first
+    # ~20 ms of sustained work (the clock ramps up); the default warm-up covers
+    # that, and the timed calls span about 60 ms.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -155,9 +186,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ms = time_region(fwd, args.steps, stream)
     print("[bench] forward %.3f ms/step" % ms, file=sys.stderr, flush=True)
-    ms_prep = time_region(lambda i: fwd(i, kda.STAGE_PREP), args.steps, stream)
+    ms_med, ms_min = per_call_ms(fwd, args.steps, stream)
+    ms_prep = time_region(lambda i: fwd(i, kda.STAGE_PREP), min(args.steps, 50), stream)
     fwd(0, kda.STAGE_PREP)
-    ms_state = time_region(lambda i: fwd(0, kda.STAGE_STATE), args.steps, stream)
+    ms_state = time_region(lambda i: fwd(0, kda.STAGE_STATE), min(args.steps, 50), stream)
     print("[bench] prep %.3f ms, state %.3f ms" % (ms_prep, ms_state), file=sys.stderr, flush=True)
 
     traffic_fwd, traffic_dec, traffic_bwd = measured_traffic()
@@ -178,6 +210,7 @@ def main(argv=None) -> int:
         "launch_ms": round(ms, 4),
         "mfma_frac_algorithmic": round(alg_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_ms": {"chunk_prep_kernel": round(ms_prep, 4), "chunk_state_slice_kernel": round(ms_state, 4)},
+        "per_call_ms": {"median": round(ms_med, 4), "min": round(ms_min, 4)},
     }
     # the same workload through the gauge route (signs folded into q and k,
     # positive-gate forward, S_T rows flipped back)
@@ -213,9 +246,9 @@ def main(argv=None) -> int:
             q, k, v, g, b = steps[i % len(steps)]
             kda.decode_step(q, k, v, g, b, S, out=od, gate_kind=0)
 
-        for i in range(4):
-            dec(i)
         n_dec = args.decode_steps
+        for i in range(n_dec):   # one untimed block: the clock ramps up again after the host-side input generation
+            dec(i)
         ms_block = time_region(lambda i: [dec(j) for j in range(n_dec)], 1, stream)
         per = ms_block / n_dec
         dbytes = dw.N * dw.H * decode_bytes_per_head_step(dw.dk, dw.dv)
@@ -247,7 +280,8 @@ def main(argv=None) -> int:
         def bwd(i):
             kda.chunk_bwd(*bt, dS_T=dST, workspace=ws_b, out=gout)
 
-        bwd(0)
+        for i in range(5):   # about 35 ms: the clock ramps up again after the host-side input generation
+            bwd(i)
         ms_b = time_region(bwd, args.bwd_steps, stream)
         bflops = tokens * H * bwd_flops_per_head_token(dk, dv)
         bbytes = tokens * H * bwd_bytes_per_head_token(dk, dv) + 3 * B * H * dk * dv * 4
@@ -268,15 +302,25 @@ def main(argv=None) -> int:
         print("[bench] backward %.3f ms/call" % ms_b, file=sys.stderr, flush=True)
         if not args.no_cpu_baseline:
             import oracle
+            # the oracle keeps every state of a sequence (dk*dv doubles per
+            # token), so the sample is the first 2048 tokens of each sequence
             Ts = 2048
-            sl = lambda t: t[:1, :Ts].contiguous()  # noqa: E731
+            sl = lambda t: t[:, :Ts].contiguous()  # noqa: E731
+            bs = [sl(x) for x in (wb.q, wb.k, wb.v, wb.gate, wb.beta, dO_c)]
             t0 = time.time()
-            oracle.bwd(sl(wb.q), sl(wb.k), sl(wb.v), sl(wb.gate), sl(wb.beta), sl(dO_c), None, dST_c[:1], None, 0)
-            dt = time.time() - t0
+            reps = 0
+            while True:
+                oracle.bwd(*bs, None, dST_c, None, 0)
+                reps += 1
+                if time.time() - t0 > 10.0:
+                    break
+            dt = (time.time() - t0) / reps
             backward["cpu_baseline"] = {
-                "value": round(Ts / dt, 1), "unit": "tokens/s", "cores": min(oracle.threads(), H), "kind": "oracle",
-                "sample": "first 2048 tokens of sequence 0, all 16 heads, fp64 reverse-mode token recurrence, "
-                          "%.2f s" % dt}
+                "value": round(B * Ts / dt, 1), "unit": "tokens/s", "cores": min(oracle.threads(), B * H),
+                "kind": "oracle",
+                "sample": "first 2048 tokens of both sequences, all 16 heads, fp64 reverse-mode token recurrence, "
+                          "%d pass(es), %.2f s each" % (reps, dt)}
+            print("[bench] backward oracle %.2f s per pass" % dt, file=sys.stderr, flush=True)
         del bt, ws_b, gout
 
     # ---------------------------------------------------------------- CPU oracle
@@ -289,7 +333,7 @@ def main(argv=None) -> int:
         while True:
             oracle.fwd(w0.q, w0.k, w0.v, w0.gate, w0.beta, None, None, 0)
             reps += 1
-            if time.time() - t0 > 8.0:
+            if time.time() - t0 > 10.0:
                 break
         dt = (time.time() - t0) / reps
         cpu = {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": min(oracle.threads(), B * H),
@@ -318,6 +362,7 @@ def main(argv=None) -> int:
         "decode": decode,
         "backward": backward,
         "gauge_route": gauge,
+        "gpu_clock": gpu_clock(),
     }
     print(json.dumps(line), flush=True)
     return 0
