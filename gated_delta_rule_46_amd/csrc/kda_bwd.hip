@@ -25,11 +25,14 @@
 // per-workgroup partial sums in memory that a second kernel adds up.
 //
 // Pass A runs the forward from S0 and stores S at the start of every
-// SUB-token block (the checkpoints). Pass B walks the blocks backwards:
-// reload the checkpoint, replay the block forward keeping the SUB states
-// S_{t-1} in registers, then the adjoint over the block. Each block's
-// inputs are staged in LDS once, fetched one block ahead; one barrier per
-// block. All arithmetic is fp32 (inputs converted exactly).
+// SUB-token block (the checkpoints) and the residual e = v - pred of every
+// token. Pass B walks the blocks backwards: reload the checkpoint, replay the
+// block forward with u = beta e (no reductions) keeping the SUB states
+// S_{t-1} in registers, then the adjoint over the block. The adjoint takes
+// S_t from the replay (the next block's checkpoint for the block's last
+// token), and dk's S' dpred term as -Diag(alpha) (S_{t-1} dv), so S' is never
+// formed. Each block's inputs are staged in LDS once, fetched one block ahead;
+// one barrier per block. All arithmetic is fp32 (inputs converted exactly).
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -78,7 +81,7 @@ struct BwdParams {
     const void *q, *k, *v, *gate, *beta;
     const float *S0, *dO, *dST;
     float *dv_out, *dS0, *ckpt, *part;
-    float* pred;   // S'^T k of every token from pass A, [B*T*H][dv]
+    float* resid;   // e = v - S'^T k of every token from pass A, [B*T*H][dv]
     const int32_t* cu;
     int H, T, dv, ncg;
     long nblk;   // checkpoint slots per (head, column group)
@@ -88,7 +91,7 @@ struct BwdParams {
 template <int DK, int NC, bool SG>
 struct BwdStage {
     float k[BW_SUB][DK], q[BW_SUB][DK], a[BW_SUB][SG ? 1 : DK];
-    float v[BW_SUB][NC], dO[BW_SUB][NC], pred[BW_SUB][NC], b[BW_SUB];
+    float v[BW_SUB][NC], dO[BW_SUB][NC], e[BW_SUB][NC], b[BW_SUB];
 };
 
 // Dynamic LDS of one workgroup: the double-buffered input stage and, also
@@ -101,8 +104,11 @@ struct BwdLds {
     BwdStage<DK, NC, SG> st[2];
     float slot[2][NWV][BW_SUB][3][DK];
     float slotb[2][NWV][BW_SUB];
-    float vout[2][BW_SUB][NC];   // per-token wave-uniform results: pred (pass A), dv (pass B)
-    float junk[4 * WAVE];        // target of the lanes that do not store a wave-uniform value
+    float vout[2][BW_SUB][NC];   // per-token wave-uniform results: e (pass A), dv (pass B)
+    // target of the lanes that do not store a wave-uniform value: lane l
+    // writes 4 floats at 4 l + j NC for token j (the stride of vout), so one
+    // base address per block serves every token
+    float junk[4 * WAVE + BW_SUB * NC];
 };
 
 // Buffer resource over the SUB tokens starting at token `tok0` (flat token
@@ -132,7 +138,7 @@ template <class TIn, int DK, int NC, int NT, int RPL, int COLS, bool SG, bool BW
 struct BwdFetch {
     static constexpr int KPT = (BW_SUB * DK + NT - 1) / NT;
     static constexpr int VPT = (BW_SUB * NC + NT - 1) / NT;
-    TIn k[KPT], q[BWD ? KPT : 1], a[SG ? 1 : KPT], v[VPT], b, ag;
+    TIn k[KPT], q[BWD ? KPT : 1], a[SG ? 1 : KPT], v[BWD ? 1 : VPT], b, ag;
     float dO[BWD ? VPT : 1], pr[BWD ? VPT : 1];
     f32x4 ck[BWD ? RPL * COLS / 4 : 1];   // this lane's part of the block's checkpoint
 
@@ -157,9 +163,9 @@ struct BwdFetch {
             const int e = tid + NT * i, j = e / NC, c = e % NC, t = ts + j;
             const bool ok = e < BW_SUB * NC && t < te;
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-            v[i] = ok ? V[row * p.dv + cw0 + c] : TIn(0);
+            if (!BWD) v[i] = ok ? V[row * p.dv + cw0 + c] : TIn(0);
             if (BWD) dO[i] = ok ? p.dO[row * p.dv + cw0 + c] : 0.f;
-            if (BWD) pr[i] = ok ? p.pred[row * p.dv + cw0 + c] : 0.f;
+            if (BWD) pr[i] = ok ? p.resid[row * p.dv + cw0 + c] : 0.f;
         }
         {
             const int t = ts + tid;
@@ -189,9 +195,9 @@ struct BwdFetch {
         for (int i = 0; i < VPT; ++i) {
             const int e = tid + NT * i;
             if (e < BW_SUB * NC) {
-                (&s.v[0][0])[e] = in_f32(v[i]);
+                if (!BWD) (&s.v[0][0])[e] = in_f32(v[i]);
                 if (BWD) (&s.dO[0][0])[e] = dO[i];
-                if (BWD) (&s.pred[0][0])[e] = pr[i];
+                if (BWD) (&s.e[0][0])[e] = pr[i];
             }
         }
         if (tid < BW_SUB) {
@@ -253,7 +259,7 @@ chunk_bwd_kernel(BwdParams p) {
         }
     }
 
-    // Wave-uniform per-token results of block fb, from LDS to memory (pass A: pred)
+    // Wave-uniform per-token results of block fb, from LDS to memory (pass A: e)
     auto flush_vout = [&](int fb, float* dst) {
         const int ts = t0 + fb * SUB;
         const __amdgpu_buffer_rsrc_t r = block_rsrc(dst, (size_t)b0 * p.T + ts, p.H, p.dv);
@@ -263,7 +269,7 @@ chunk_bwd_kernel(BwdParams p) {
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L.vout[fb & 1][j][c]), r, off, 0, 0);
         }
     };
-    auto flush_pred = [&](int fb) { flush_vout(fb, p.pred); };
+    auto flush_resid = [&](int fb) { flush_vout(fb, p.resid); };
 
     // ------------------------------------------------ pass A: forward, checkpoints
     {
@@ -274,9 +280,10 @@ chunk_bwd_kernel(BwdParams p) {
             f.store(st, tid);
             __syncthreads();
             const int ts = t0 + blk * SUB;
-            if (blk > 0) flush_pred(blk - 1);
+            if (blk > 0) flush_resid(blk - 1);
             if (blk + 1 < nb) f.fetch(p, tid, b0, h, ts + SUB, t1, cw0, nullptr);
             f32x4* cp = reinterpret_cast<f32x4*>(ck + (size_t)blk * CKF);
+            float* vb = lane == 0 ? &L.vout[blk & 1][0][w * COLS] : &L.junk[4 * lane];
 #pragma unroll
             for (int m = 0; m < RPL; ++m)
 #pragma unroll
@@ -304,13 +311,15 @@ chunk_bwd_kernel(BwdParams p) {
                         }
                         wave_sum4(x, part, lane);
                     }
-                    static_assert(COLS == 4, "one 16-byte LDS store of pred per wave and token");
-                    *reinterpret_cast<f32x4*>(lane == 0 ? &L.vout[blk & 1][j][w * COLS] : &L.junk[4 * lane]) =
-                        f32x4{part[0], part[1], part[2], part[3]};
+                    static_assert(COLS == 4, "one 16-byte LDS store of e per wave and token");
+                    float e[COLS];
+#pragma unroll
+                    for (int c = 0; c < COLS; ++c) e[c] = st.v[j][w * COLS + c] - part[c];
+                    *reinterpret_cast<f32x4*>(vb + j * NC) = f32x4{e[0], e[1], e[2], e[3]};
                     const float bt = st.b[j];
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
-                        const float u = bt * (st.v[j][w * COLS + c] - part[c]);
+                        const float u = bt * e[c];
 #pragma unroll
                         for (int m = 0; m < RPL; ++m) S[m][c] = fmaf(kr[m], u, S[m][c]);
                     }
@@ -319,8 +328,8 @@ chunk_bwd_kernel(BwdParams p) {
         }
     }
     __syncthreads();
-    if (nb > 0) flush_pred(nb - 1);
-    __syncthreads();   // pass B reads pred written by other threads
+    if (nb > 0) flush_resid(nb - 1);
+    __syncthreads();   // pass B reads e written by other threads
 
     // ------------------------------------------------ pass B: adjoint, blocks in reverse
     float dS[RPL][COLS];
@@ -335,6 +344,14 @@ chunk_bwd_kernel(BwdParams p) {
             for (int c = 0; c < 4; ++c) dS[m][4 * c4 + c] = x[c];
         }
     }
+    // S after the last token of the block being processed: pass A's final
+    // state for the last block (padding tokens are exact no-ops), then each
+    // block's checkpoint for the block before it
+    float Sn[RPL][COLS];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m)
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) Sn[m][c] = S[m][c];
     const size_t nrk = (size_t)p.rows * DK;
     auto flush = [&](int fb) {   // block fb: dv, and the waves' partial sums added up, to memory
         const int ts = t0 + fb * SUB;
@@ -379,15 +396,15 @@ chunk_bwd_kernel(BwdParams p) {
             const int ts = t0 + blk * SUB;
             if (blk > 0) f.fetch(p, tid, b0, h, ts - SUB, t1, cw0, ck + (size_t)(blk - 1) * CKF);
 
-            // replay the block forward, keeping S_{t-1} for every token
-            float Sh[SUB][RPL][COLS];
+            // replay the block forward, keeping S_{t-1} and u for every token
+            float Sh[SUB][RPL][COLS], uh[SUB][COLS];
 #pragma unroll
             for (int j = 0; j < SUB; ++j) {
 #pragma unroll
                 for (int m = 0; m < RPL; ++m)
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) Sh[j][m][c] = Sb[m][c];
-                if (j + 1 < SUB) {   // pred from pass A: the same values, no reduction
+                if (j + 1 < SUB) {   // e from pass A: the same values, no reduction
                     float kr[RPL];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
@@ -400,7 +417,8 @@ chunk_bwd_kernel(BwdParams p) {
                     const float bt = st.b[j];
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
-                        const float u = bt * (st.v[j][w * COLS + c] - st.pred[j][w * COLS + c]);
+                        const float u = bt * st.e[j][w * COLS + c];
+                        uh[j][c] = u;
 #pragma unroll
                         for (int m = 0; m < RPL; ++m) Sb[m][c] = fmaf(kr[m], u, Sb[m][c]);
                     }
@@ -408,10 +426,12 @@ chunk_bwd_kernel(BwdParams p) {
             }
 
             float(*slot)[3][DK] = L.slot[blk & 1][w];
+            float* vb = lane == 0 ? &L.vout[blk & 1][0][w * COLS] : &L.junk[4 * lane];
+            float* bb = lane == 0 ? &L.slotb[blk & 1][w][0] : &L.junk[lane];
 #pragma unroll
             for (int j = SUB - 1; j >= 0; --j) {
                 {
-                    float kr[RPL], qr[RPL], ar[RPL], oo[COLS], vv[COLS];
+                    float kr[RPL], qr[RPL], ar[RPL], oo[COLS], ee[COLS];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
                         const int r = rv[m] ? lane + WAVE * m : 0;
@@ -422,17 +442,14 @@ chunk_bwd_kernel(BwdParams p) {
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
                         oo[c] = st.dO[j][w * COLS + c];
-                        vv[c] = st.v[j][w * COLS + c];
+                        ee[c] = st.e[j][w * COLS + c];
                     }
                     const float bt = st.b[j];
-                    float Sp[RPL][COLS], pred[COLS], du[COLS];
+                    float du[COLS];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m)
 #pragma unroll
-                        for (int c = 0; c < COLS; ++c) {
-                            Sp[m][c] = ar[m] * Sh[j][m][c];
-                            dS[m][c] = fmaf(qr[m], oo[c], dS[m][c]);
-                        }
+                        for (int c = 0; c < COLS; ++c) dS[m][c] = fmaf(qr[m], oo[c], dS[m][c]);
                     {
                         float y[COLS];
 #pragma unroll
@@ -440,30 +457,33 @@ chunk_bwd_kernel(BwdParams p) {
                             y[c] = 0.f;
 #pragma unroll
                             for (int m = 0; m < RPL; ++m) y[c] = fmaf(dS[m][c], kr[m], y[c]);
-                            pred[c] = st.pred[j][w * COLS + c];
                         }
                         wave_sum4(y, du, lane);
                     }
-                    float u[COLS], dpred[COLS], dbt = 0.f;
+                    // u = beta e; dv = beta du; dpred = -dv
+                    float u[COLS], dvv[COLS], dbt = 0.f;
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
-                        const float e = vv[c] - pred[c];
-                        u[c] = bt * e;
-                        dpred[c] = -bt * du[c];
-                        dbt = fmaf(du[c], e, dbt);
+                        u[c] = j + 1 < SUB ? uh[j + 1 < SUB ? j : 0][c] : bt * ee[c];
+                        dvv[c] = bt * du[c];
+                        dbt = fmaf(du[c], ee[c], dbt);
                     }
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
-                        float gq = 0.f, gk = 0.f, ga = 0.f;
+                        float St[COLS];   // S_t
+#pragma unroll
+                        for (int c = 0; c < COLS; ++c) St[c] = j + 1 < SUB ? Sh[j + 1 < SUB ? j + 1 : 0][m][c] : Sn[m][c];
+                        float gq = 0.f, gk = 0.f, gs = 0.f, ga = 0.f;
 #pragma unroll
                         for (int c = 0; c < COLS; ++c) {
-                            gq = fmaf(fmaf(kr[m], u[c], Sp[m][c]), oo[c], gq);
+                            gq = fmaf(St[c], oo[c], gq);
                             gk = fmaf(dS[m][c], u[c], gk);
-                            gk = fmaf(Sp[m][c], dpred[c], gk);
-                            const float dsp = fmaf(kr[m], dpred[c], dS[m][c]);
+                            gs = fmaf(Sh[j][m][c], dvv[c], gs);
+                            const float dsp = fmaf(-kr[m], dvv[c], dS[m][c]);   // dS' = dS + k dpred^T
                             ga = fmaf(dsp, Sh[j][m][c], ga);
                             dS[m][c] = ar[m] * dsp;
                         }
+                        gk = fmaf(-ar[m], gs, gk);   // + S' dpred
                         if (rv[m]) {
                             const int r = lane + WAVE * m;
                             slot[j][0][r] = gq;
@@ -473,11 +493,14 @@ chunk_bwd_kernel(BwdParams p) {
                     }
                     // wave-uniform values, stored by lane 0 without a branch (the other
                     // lanes write a junk area): dbeta and dv, flushed with the block
-                    (lane == 0 ? &L.slotb[blk & 1][w][j] : &L.junk[lane])[0] = dbt;
-                    *reinterpret_cast<f32x4*>(lane == 0 ? &L.vout[blk & 1][j][w * COLS] : &L.junk[4 * lane]) =
-                        f32x4{bt * du[0], bt * du[1], bt * du[2], bt * du[3]};
+                    bb[j] = dbt;
+                    *reinterpret_cast<f32x4*>(vb + j * NC) = f32x4{dvv[0], dvv[1], dvv[2], dvv[3]};
                 }
             }
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int c = 0; c < COLS; ++c) Sn[m][c] = Sh[0][m][c];
         }
     }
     __syncthreads();
@@ -575,8 +598,8 @@ size_t bwd_part_bytes(int B, int H, int T, int dk, int dv) {
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N) {
-    const size_t pred = align256((size_t)B * T * H * dv * sizeof(float));
-    return bwd_ckpt_bytes(H, bwd_slots(B, T, varlen, N), dk, dv) + bwd_part_bytes(B, H, T, dk, dv) + pred;
+    const size_t resid = align256((size_t)B * T * H * dv * sizeof(float));
+    return bwd_ckpt_bytes(H, bwd_slots(B, T, varlen, N), dk, dv) + bwd_part_bytes(B, H, T, dk, dv) + resid;
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {
@@ -602,7 +625,7 @@ hipError_t launch_chunk_bwd(const BwdArgs& a) {
     char* ws = static_cast<char*>(a.workspace);
     p.ckpt = reinterpret_cast<float*>(ws);
     p.part = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv));
-    p.pred = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv) +
+    p.resid = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv) +
                                       bwd_part_bytes(a.B, a.H, a.T, a.dk, a.dv));
     hipError_t e = a.bf16 ? (a.scalar_gate ? launch_bwd_dk<uint16_t, true>(a, p) : launch_bwd_dk<uint16_t, false>(a, p))
                           : (a.scalar_gate ? launch_bwd_dk<float, true>(a, p) : launch_bwd_dk<float, false>(a, p));

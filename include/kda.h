@@ -166,7 +166,7 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int N,
  *
  * workspace: at least kda_chunk_bwd_workspace_bytes(...) bytes (state
  * checkpoints every 8 tokens, 4 * dk * dv bytes each per (sequence, head),
- * plus per-workgroup partial sums), or NULL to take it stream-ordered from
+ * the per-token residual v - S'^T k, plus per-workgroup partial sums), or NULL to take it stream-ordered from
  * the device's default memory pool.
  *
  * Returns KDA_OK or a negative status.
