@@ -318,6 +318,54 @@ def test_deterministic(kda):
 
 # ------------------------------------------------------------------ decode
 
+def _norm_keeping_gates(rng, gshape, bshape):
+    """|alpha| = 1 with random signs, and beta = 2 (a reflection) for half the
+    tokens, U(0, 2) otherwise: the state norm stays near its start instead of
+    decaying, so growth from a wrong sign or term would show."""
+    g = np.where(rng.random(gshape) < 0.5, -1.0, 1.0)
+    b = np.where(rng.random(bshape) < 0.5, 2.0, 2.0 * rng.random(bshape))
+    return torch.tensor(g, dtype=torch.float32), torch.tensor(b, dtype=torch.float32)
+
+
+def test_no_write_state_norm_nonincreasing(kda):
+    """With v = 0 every token maps S to A_t S, A_t = (I - beta k k^T) Diag(alpha);
+    with unit k, beta in [0, 2] and |alpha| <= 1 the spectral norm of A_t is at
+    most 1 (Complex KDA summary, stability of the transition), so the
+    Frobenius norm of the state never grows: checked after every decode step
+    and, through the chunked forward, at prefix lengths that cross chunk
+    boundaries. fp32 inputs (k unit to fp32 rounding); the slack covers fp32
+    rounding only."""
+    rng = np.random.default_rng(61)
+    # decode: 48 steps in place from a random state
+    dw = inputs.ckda_decode(seed=6, N=4, H=2, d=64, n_steps=48, s_std=1.0, dtype=torch.float32)
+    S = dw.S.cuda()
+    n0 = torch.linalg.matrix_norm(dw.S.double())
+    prev = n0
+    for st in dw.steps:
+        g, b = _norm_keeping_gates(rng, tuple(st["gate"].shape), tuple(st["beta"].shape))
+        v0 = torch.zeros_like(st["v"])
+        kda.decode_step(st["q"].cuda(), st["k"].cuda(), v0.cuda(), g.cuda(), b.cuda(), S)
+        torch.cuda.synchronize()
+        n = torch.linalg.matrix_norm(S.cpu().double())
+        assert bool((n <= prev * (1 + 1e-5)).all()), float((n / prev).max())
+        prev = n
+    print("decode: norm ratio after 48 steps %.3f..%.3f" % (float((prev / n0).min()), float((prev / n0).max())))
+    # chunked forward: S_T of growing prefixes
+    w = inputs.make_forward("nowrite", B=2, H=2, T=200, dk=64, dv=32, chunk=64, dtype=torch.float32,
+                            gate="ckda", s0_std=1.0, seed=16)
+    g, b = _norm_keeping_gates(rng, tuple(w.gate.shape), tuple(w.beta.shape))
+    w = dataclasses.replace(w, v=torch.zeros_like(w.v), gate=g, beta=b)
+    n0 = prev = torch.linalg.matrix_norm(w.S0.double())
+    for T in (30, 64, 100, 128, 170, 200):
+        wp = dataclasses.replace(w, q=w.q[:, :T].contiguous(), k=w.k[:, :T].contiguous(), v=w.v[:, :T].contiguous(),
+                                 gate=w.gate[:, :T].contiguous(), beta=w.beta[:, :T].contiguous(), T=T)
+        _, ST = gpu_fwd(kda, wp)
+        n = torch.linalg.matrix_norm(ST.double())
+        assert bool((n <= prev * (1 + 1e-4)).all()), (T, float((n / prev).max()))
+        prev = n
+    print("forward: norm ratio after 200 tokens %.3f..%.3f" % (float((prev / n0).min()), float((prev / n0).max())))
+
+
 @pytest.mark.parametrize("dtype,dk,dv,gk", [(torch.bfloat16, 128, 128, 0), (torch.float32, 64, 32, 0),
                                             (torch.bfloat16, 16, 64, 1), (torch.float32, 32, 128, 1)])
 def test_decode_parity(kda, dtype, dk, dv, gk):
