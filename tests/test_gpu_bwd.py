@@ -67,6 +67,7 @@ CASES = [
     ("gdn", torch.float32, 16, 128, 17),
     ("ckda", torch.float32, 128, 16, 9),
     ("kda", torch.bfloat16, 64, 128, 8),
+    ("ckda", torch.float32, 64, 64, 3),   # shorter than one checkpoint block
 ]
 
 
