@@ -2090,23 +2090,26 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
     __syncthreads();
 
     uint32_t sink = 0;
+    // first touch of chunk cg+2: this slice's share of the shared operands'
+    // lines (so that the slices of the (sequence, head) find them in L2) and
+    // its own U~ lines; the lane's line offset within a block is fixed
+    const bool toucher = q * 64 < (int)((L::BYTES / 128 + nsl - 1) / nsl + L::USL / 128);   // wave has lines
+    int toff = (int)p.blk_bytes;   // past the descriptor: no access, value 0
+    {
+        constexpr int L0 = (int)(L::BYTES / 128), LU = (int)(L::USL / 128);
+        const int per = (L0 + nsl - 1) / nsl;
+        const int i = q * 64 + lane;
+        if (i < per && sl * per + i < L0) toff = (sl * per + i) * 128;
+        else if (i >= per && i < per + LU) toff = (int)(L::BYTES + (size_t)sl * L::USL) + (i - per) * 128;
+    }
     for (int cg = cs; cg < ce; ++cg) {
         const long t0 = bos + (long)(cg - cs) * C;
         const int n = (int)min((long)C, eos - t0);
-        // first touch of chunk cg+2: this slice's share of the shared operands'
-        // lines (so that the slices of the (sequence, head) find them in L2)
-        // and its own U~ lines. Issued before the loads below and consumed at
-        // the end of the iteration: waiting for it then does not wait for them.
+        // Issued before the loads below and consumed at the end of the
+        // iteration: waiting for it then does not wait for them.
         uint32_t tch = 0;
-        if (q * 64 < (int)((L::BYTES / 128 + nsl - 1) / nsl + L::USL / 128)) {   // waves with lines to touch
-            constexpr int L0 = (int)(L::BYTES / 128), LU = (int)(L::USL / 128);
-            const int per = (L0 + nsl - 1) / nsl;
-            const int i = q * 64 + lane;
-            int off = (int)p.blk_bytes;   // past the descriptor: no access, value 0
-            if (cg + 2 < ce) {
-                if (i < per && sl * per + i < L0) off = (sl * per + i) * 128;
-                else if (i >= per && i < per + LU) off = (int)(L::BYTES + (size_t)sl * L::USL) + (i - per) * 128;
-            }
+        if (toucher) {
+            const int off = cg + 2 < ce ? toff : (int)p.blk_bytes;
             const __amdgpu_buffer_rsrc_t rt = make_rsrc(gblock(cg + 2 < ce ? cg + 2 : cg), (uint32_t)p.blk_bytes);
             tch = __builtin_amdgcn_raw_buffer_load_b32(rt, off, 0, 0);
         }
