@@ -147,6 +147,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-gauge", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--no-ratio", action="store_true", help="skip the Complex KDA / KDA throughput ratio")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the gated delta-rule path here is single-GPU "
@@ -323,6 +324,55 @@ def main(argv=None) -> int:
             print("[bench] backward oracle %.2f s per pass" % dt, file=sys.stderr, flush=True)
         del bt, ws_b, gout
 
+    # ------------------------------------------------- Complex KDA against KDA
+    # The pages compare forward-plus-backward kernel throughput of Complex KDA
+    # with KDA's at 16 heads, dk = dv = 128, bf16, 32k tokens per step (Complex
+    # KDA summary, efficiency). Same shape here (B=4, T=8192), the KDA gate
+    # recipe (a ~ N(3, 1)) against the Complex KDA one, measured alternately.
+    ratio = None
+    if not args.no_ratio:
+        print("[bench] ratio inputs", file=sys.stderr, flush=True)
+        Br, Tr = 4, 8192
+        runs = {}
+        for name, w in (("kda", inputs.make_forward("kda_b4_h16_t8192", B=Br, H=H, T=Tr, dk=dk, dv=dv, chunk=C,
+                                                     gate="kda", gate_mu=3.0, seed=1)),
+                        ("ckda", inputs.ckda_fwd(seed=1, B=Br, H=H, T=Tr))):
+            dO_r, dST_r = inputs.cotangents(w, seed=1)
+            t = [x.to(dev) for x in (w.q, w.k, w.v, w.gate, w.beta)]
+            runs[name] = (t, dO_r.to(dev), dST_r.to(dev))
+        ws_f = torch.empty(kda.workspace_bytes(Br, H, Tr, dk, dv, C), device=dev, dtype=torch.uint8)
+        ws_r = torch.empty(kda.bwd_workspace_bytes(Br, H, Tr, dk, dv), device=dev, dtype=torch.uint8)
+        o_r = torch.empty((Br, Tr, H, dv), device=dev, dtype=torch.float32)
+        ST_r = torch.empty((Br, H, dk, dv), device=dev, dtype=torch.float32)
+        g_r = kda.chunk_bwd(*runs["kda"][0], runs["kda"][1], dS_T=runs["kda"][2], workspace=ws_r)
+        times = {"kda": [[], []], "ckda": [[], []]}
+        for rep_i in range(2):
+            for name in (("kda", "ckda") if rep_i == 0 else ("ckda", "kda")):
+                t, dO_r, dST_r = runs[name]
+
+                def f_r(i):
+                    kda.chunk_fwd(*t, chunk=C, gate_kind=0, out=o_r, S_T=ST_r, workspace=ws_f)
+
+                def b_r(i):
+                    kda.chunk_bwd(*t, dO_r, dS_T=dST_r, workspace=ws_r, out=g_r)
+
+                for i in range(args.warmup):
+                    f_r(i)
+                times[name][0].append(time_region(f_r, 50, stream))
+                for i in range(2):
+                    b_r(i)
+                times[name][1].append(time_region(b_r, 3, stream))
+        fk, bk = (sum(x) / len(x) for x in times["kda"])
+        fc, bc = (sum(x) / len(x) for x in times["ckda"])
+        ratio = {"workload": "b4_h16_t8192_d128 bf16, 32,768 tokens per step",
+                 "kda_ms": {"forward": round(fk, 4), "backward": round(bk, 4)},
+                 "ckda_ms": {"forward": round(fc, 4), "backward": round(bc, 4)},
+                 "forward_ratio": round(fk / fc, 4), "forward_backward_ratio": round((fk + bk) / (fc + bc), 4),
+                 "pages": "96-97% forward+backward on H100, BF16, their kernels"}
+        print("[bench] Complex KDA / KDA throughput: forward %.3f, forward+backward %.3f"
+              % (fk / fc, (fk + bk) / (fc + bc)), file=sys.stderr, flush=True)
+        del runs, ws_f, ws_r, o_r, ST_r, g_r
+
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -362,6 +412,7 @@ def main(argv=None) -> int:
         "decode": decode,
         "backward": backward,
         "gauge_route": gauge,
+        "ckda_vs_kda": ratio,
         "gpu_clock": gpu_clock(),
     }
     print(json.dumps(line), flush=True)
