@@ -10,7 +10,9 @@ seeded input sets alternate so the 256 MB last-level cache cannot hold the
 whole working set. The decode step (N=256 sequences, H=32, d=128, fp32 state
 of 512 MiB updated in place) is timed as one block of 128 consecutive steps.
 The backward (kda_chunk_bwd, gradients of every input for given dO and
-dS_T) is timed on the same forward workload.
+dS_T) is timed on the same forward workload. Forward and backward are also
+timed at 32k tokens per step (B=4, H=16, T=8192) with the KDA and the Complex
+KDA gate recipes, for the throughput ratio of the two.
 Timing uses HIP events recorded on the stream the kernels run on. Prints one
 JSON line.
 """
