@@ -153,7 +153,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the gated delta-rule path here is single-GPU "
-              "(independent (sequence, head) scans shard without communication; see DESIGN.md). "
+              "(independent (sequence, head) scans shard over GPUs without communication). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
