@@ -1,8 +1,13 @@
 """Seeded randomized parity sweep: forward, backward and gauge route over
 random shapes (every supported dk, dv and chunk), both input dtypes, all gate
 kinds, fixed-length and packed sequences with ragged lengths, against the
-fp64 oracle with the same metrics and bars as the dedicated tests."""
+fp64 oracle with the same metrics and bars as the dedicated tests.
+
+A second generator draws longer sequences (up to 2,000 tokens), more heads
+(up to 8) and packed batches of up to 8 sequences; KDA_SWEEP_LARGE sets how
+many of those cases run (default 40)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -58,6 +63,26 @@ def random_case(seed):
     return w
 
 
+def random_large_case(seed):
+    rng = np.random.default_rng(50000 + seed)
+    dk = int(rng.choice([16, 32, 64, 128]))
+    dv = int(rng.choice([16, 32, 64, 128]))
+    chunk = int(rng.choice([16, 32, 64]))
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    gate = str(rng.choice(["kda", "ckda", "gdn"]))
+    H = int(rng.integers(1, 9))
+    if rng.random() < 0.4:
+        lengths = [int(x) for x in rng.integers(0, 700, size=int(rng.integers(1, 9)))]
+        if sum(lengths) == 0:
+            lengths[0] = 7
+        return inputs.make_forward("large%d" % seed, B=1, H=H, T=0, dk=dk, dv=dv, chunk=chunk, dtype=dtype,
+                                   gate=gate, gate_mu=float(rng.uniform(1, 4)), seed=seed, lengths=lengths,
+                                   s0_std=float(rng.choice([0.0, 0.3])))
+    return inputs.make_forward("large%d" % seed, B=int(rng.integers(1, 4)), H=H, T=int(rng.integers(1, 2000)),
+                               dk=dk, dv=dv, chunk=chunk, dtype=dtype, gate=gate, gate_mu=float(rng.uniform(1, 4)),
+                               seed=seed, s0_std=float(rng.choice([0.0, 0.3])))
+
+
 def dev(t):
     return None if t is None else t.cuda()
 
@@ -96,6 +121,31 @@ def test_gauge_route_sweep(kda, seed):
           flush=True)
     o, ST = kda.chunk_fwd_gauge(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), S0=dev(w.S0),
                                 cu_seqlens=dev(w.cu_seqlens), chunk=w.chunk, gate_kind=w.gate_kind)
+    torch.cuda.synchronize()
+    ro, rS = oracle.fwd(w.q, w.k, w.v, w.gate, w.beta, w.S0, w.cu_seqlens, w.gate_kind)
+    tol = FWD_TOL[w.q.dtype]
+    assert err(o, ro) <= tol and err(ST, rS) <= tol, (err(o, ro), err(ST, rS))
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("KDA_SWEEP_LARGE", "40"))))
+def test_large_sweep(kda, seed):
+    """Forward (three cases in five), backward and gauge route on the larger shapes."""
+    w = random_large_case(seed)
+    kind = ("fwd", "fwd", "fwd", "bwd", "gauge")[seed % 5]
+    print("case", kind, w.name, "B", w.B, "H", w.H, "T", w.T, "dk", w.dk, "dv", w.dv, "chunk", w.chunk, w.q.dtype,
+          "gate kind", w.gate_kind, "varlen", w.cu_seqlens is not None, flush=True)
+    if kind == "bwd":
+        dO, dST = inputs.cotangents(w, seed=seed, with_dS_T=seed % 2 == 0)
+        g = kda.chunk_bwd(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), dev(dO), S0=dev(w.S0),
+                          dS_T=dev(dST), cu_seqlens=dev(w.cu_seqlens), gate_kind=w.gate_kind)
+        torch.cuda.synchronize()
+        r = oracle.bwd(w.q, w.k, w.v, w.gate, w.beta, dO, w.S0, dST, w.cu_seqlens, w.gate_kind)
+        errs = {n: err(g[n], r[n]) for n in NAMES}
+        assert max(errs.values()) <= 1e-4, errs
+        return
+    fn = kda.chunk_fwd if kind == "fwd" else kda.chunk_fwd_gauge
+    o, ST = fn(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), S0=dev(w.S0), cu_seqlens=dev(w.cu_seqlens),
+               chunk=w.chunk, gate_kind=w.gate_kind)
     torch.cuda.synchronize()
     ro, rS = oracle.fwd(w.q, w.k, w.v, w.gate, w.beta, w.S0, w.cu_seqlens, w.gate_kind)
     tol = FWD_TOL[w.q.dtype]
