@@ -5,7 +5,8 @@ fp64 oracle with the same metrics and bars as the dedicated tests.
 
 A second generator draws longer sequences (up to 2,000 tokens), more heads
 (up to 8) and packed batches of up to 8 sequences; KDA_SWEEP_LARGE sets how
-many of those cases run (default 40)."""
+many of those cases run (default 40). The decode step is swept on random
+shapes too, several steps in place."""
 import math
 import os
 
@@ -150,3 +151,28 @@ def test_large_sweep(kda, seed):
     ro, rS = oracle.fwd(w.q, w.k, w.v, w.gate, w.beta, w.S0, w.cu_seqlens, w.gate_kind)
     tol = FWD_TOL[w.q.dtype]
     assert err(o, ro) <= tol and err(ST, rS) <= tol, (err(o, ro), err(ST, rS))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_sweep(kda, seed):
+    """Decode steps in place on random N, H, dk, dv, dtype and gate kind, against
+    the oracle's step applied to the same fp64 state."""
+    rng = np.random.default_rng(7000 + seed)
+    dk = int(rng.choice([16, 32, 64, 128]))
+    dv = int(rng.choice([16, 32, 64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    gate = str(rng.choice(["kda", "ckda", "gdn"]))
+    gk = 1 if gate == "gdn" else 0
+    N, H, steps = int(rng.integers(1, 41)), int(rng.integers(1, 9)), int(rng.integers(3, 9))
+    print("case decode", seed, "N", N, "H", H, "dk", dk, "dv", dv, dtype, gate, "steps", steps, flush=True)
+    S = torch.from_numpy(rng.normal(0, 0.3, (N, H, dk, dv))).float()
+    Sd = S.cuda()
+    Sr = S.double().numpy().copy()
+    for st in range(steps):
+        w = inputs.make_forward("dec", B=N, H=H, T=1, dk=dk, dv=dv, dtype=dtype, gate=gate, seed=100 * seed + st)
+        q, k, v, g, b = (t[:, 0].contiguous() for t in (w.q, w.k, w.v, w.gate, w.beta))
+        o = kda.decode_step(q.cuda(), k.cuda(), v.cuda(), g.cuda(), b.cuda(), Sd, gate_kind=gk)
+        ro = oracle.decode_step(q, k, v, g, b, Sr, gate_kind=gk)
+        torch.cuda.synchronize()
+        assert err(o, ro) < (1e-5 if dtype == torch.float32 else 1e-3)
+    assert err(Sd, Sr) < 1e-5
