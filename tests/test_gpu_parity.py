@@ -327,6 +327,36 @@ def _norm_keeping_gates(rng, gshape, bshape):
     return torch.tensor(g, dtype=torch.float32), torch.tensor(b, dtype=torch.float32)
 
 
+def test_side_stream_bit_identical(kda):
+    """Every call enqueues on the stream it is given: forward, backward and
+    decode launched on a second stream (default priority, workspace taken
+    from the device pool on that stream) give the default stream's results
+    bit for bit."""
+    w = inputs.make_forward("stream", B=2, H=3, T=150, dk=128, dv=64, chunk=64, dtype=torch.bfloat16, gate="ckda",
+                            s0_std=0.3, seed=21)
+    q, k, v, g, b, s0, _ = to_dev(w)
+    dO, dST = (t.cuda() for t in inputs.cotangents(w, seed=21))
+    o1, S1 = kda.chunk_fwd(q, k, v, g, b, S0=s0, chunk=64)
+    g1 = kda.chunk_bwd(q, k, v, g, b, dO, S0=s0, dS_T=dST)
+    Sd1 = s0.clone()
+    od1 = kda.decode_step(q[:, 0].contiguous(), k[:, 0].contiguous(), v[:, 0].contiguous(), g[:, 0].contiguous(),
+                          b[:, 0].contiguous(), Sd1)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        o2, S2 = kda.chunk_fwd(q, k, v, g, b, S0=s0, chunk=64, stream=side)
+        g2 = kda.chunk_bwd(q, k, v, g, b, dO, S0=s0, dS_T=dST, stream=side)
+        Sd2 = s0.clone()
+        od2 = kda.decode_step(q[:, 0].contiguous(), k[:, 0].contiguous(), v[:, 0].contiguous(),
+                              g[:, 0].contiguous(), b[:, 0].contiguous(), Sd2, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
+    assert torch.equal(od1, od2) and torch.equal(Sd1, Sd2)
+
+
 def test_no_write_state_norm_nonincreasing(kda):
     """With v = 0 every token maps S to A_t S, A_t = (I - beta k k^T) Diag(alpha);
     with unit k, beta in [0, 2] and |alpha| <= 1 the spectral norm of A_t is at
