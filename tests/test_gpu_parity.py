@@ -357,6 +357,57 @@ def test_side_stream_bit_identical(kda):
     assert torch.equal(od1, od2) and torch.equal(Sd1, Sd2)
 
 
+def test_graph_replay_matches_eager(kda):
+    """The forward (caller-supplied workspace) and a decode step enqueue kernels
+    only, so a caller can capture them in a graph: three replays, each on new
+    inputs copied into the captured buffers and with eager calls in between,
+    each equal bit for bit to an eager call on the same inputs."""
+    B, H, T, dk, dv = 2, 2, 200, 128, 64
+
+    def make(seed):
+        w = inputs.make_forward("graph", B=B, H=H, T=T, dk=dk, dv=dv, chunk=64, dtype=torch.bfloat16, gate="ckda",
+                                s0_std=0.3, seed=seed)
+        return [t.cuda() for t in (w.q, w.k, w.v, w.gate, w.beta, w.S0)]
+
+    static = make(30)
+    ws = torch.empty(kda.workspace_bytes(B, H, T, dk, dv, 64), device="cuda", dtype=torch.uint8)
+    o = torch.empty((B, T, H, dv), device="cuda")
+    ST = torch.empty((B, H, dk, dv), device="cuda")
+    Sd = torch.empty((B, H, dk, dv), device="cuda")
+    od = torch.empty((B, H, dv), device="cuda")
+
+    def step():
+        q, k, v, g, b, s0 = static
+        kda.chunk_fwd(q, k, v, g, b, S0=s0, chunk=64, out=o, S_T=ST, workspace=ws)
+        Sd.copy_(ST)
+        kda.decode_step(q[:, 0].contiguous(), k[:, 0].contiguous(), v[:, 0].contiguous(), g[:, 0].contiguous(),
+                        b[:, 0].contiguous(), Sd, out=od)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        new = make(31 + rep)
+        for dst, src in zip(static, new):
+            dst.copy_(src)
+        q, k, v, g, b, s0 = new
+        o_e, ST_e = kda.chunk_fwd(q, k, v, g, b, S0=s0, chunk=64)   # eager, own workspace
+        Sd_e = ST_e.clone()
+        od_e = kda.decode_step(q[:, 0].contiguous(), k[:, 0].contiguous(), v[:, 0].contiguous(),
+                               g[:, 0].contiguous(), b[:, 0].contiguous(), Sd_e)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e) and torch.equal(ST, ST_e), rep
+        assert torch.equal(od, od_e) and torch.equal(Sd, Sd_e), rep
+
+
 def test_no_write_state_norm_nonincreasing(kda):
     """With v = 0 every token maps S to A_t S, A_t = (I - beta k k^T) Diag(alpha);
     with unit k, beta in [0, 2] and |alpha| <= 1 the spectral norm of A_t is at
