@@ -150,6 +150,134 @@ int kda_oracle_decode(const double *q, const double *k, const double *v, const d
 }
 
 /*
+ * Decoupled erase and write gates (Gated DeltaNet-2 blurb: the delta rule's
+ * update split into a channel-wise erase gate and a channel-wise write gate).
+ * The pages give no formula; the reading taken here keeps the update rank
+ * one along k and replaces the scalar beta in its two roles:
+ *
+ *   S_t = (I - k_t (e_t o k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t o v_t)^T
+ *
+ * with the erase gate e_t in R^{dk} (per key channel: how much each channel
+ * of the key takes part in reading out what is erased) and the write gate
+ * w_t in R^{dv} (per value channel: how much of v is written). In delta form,
+ * gate first:
+ *
+ *   S'   = Diag(alpha_t) S_{t-1}
+ *   pred = S'^T (e_t o k_t)
+ *   S_t  = S' + k_t (w_t o v_t - pred)^T
+ *   o_t  = S_t^T q_t
+ *
+ * With e_t = beta_t 1 and w_t = beta_t 1 this is the recurrence above.
+ * Layouts: erase [B,T,H,dk], write [B,T,H,dv]; the rest as for
+ * kda_oracle_fwd.
+ */
+static void erase_write_step(double *S, const double *q, const double *k, const double *v,
+                             const double *alpha, int alpha_stride, const double *erase,
+                             const double *write, double *o, double *pred, int dk, int dv)
+{
+    int i, j;
+    for (i = 0; i < dk; ++i) {
+        double a = alpha[i * alpha_stride];
+        for (j = 0; j < dv; ++j)
+            S[i * dv + j] *= a;
+    }
+    for (j = 0; j < dv; ++j)
+        pred[j] = 0.0;
+    for (i = 0; i < dk; ++i) {
+        double ek = erase[i] * k[i];
+        for (j = 0; j < dv; ++j)
+            pred[j] += S[i * dv + j] * ek;
+    }
+    for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j)
+            S[i * dv + j] += k[i] * (write[j] * v[j] - pred[j]);
+    if (o) {
+        for (j = 0; j < dv; ++j)
+            o[j] = 0.0;
+        for (i = 0; i < dk; ++i)
+            for (j = 0; j < dv; ++j)
+                o[j] += S[i * dv + j] * q[i];
+    }
+}
+
+int kda_oracle_fwd_ew(const double *q, const double *k, const double *v, const double *gate,
+                      const double *erase, const double *write, const double *S0, double *o,
+                      double *S_T, int B, int H, int T, int dk, int dv, const int32_t *cu_seqlens,
+                      int nseq, int gate_kind)
+{
+    if (!q || !k || !v || !gate || !erase || !write || !o || B <= 0 || H <= 0 || T < 0 || dk <= 0 ||
+        dv <= 0)
+        return -1;
+    if (gate_kind != GATE_CHANNEL && gate_kind != GATE_SCALAR)
+        return -1;
+    if (cu_seqlens) {
+        if (B != 1 || nseq <= 0 || cu_seqlens[0] != 0 || cu_seqlens[nseq] != T)
+            return -1;
+    } else {
+        nseq = B;
+    }
+    const int gdim = gate_kind == GATE_CHANNEL ? dk : 1;
+    const int astride = gate_kind == GATE_CHANNEL ? 1 : 0;
+    long pairs = (long)nseq * H;
+    long p;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (p = 0; p < pairs; ++p) {
+        int s = (int)(p / H), h = (int)(p % H);
+        long t0, t1, b, t;
+        if (cu_seqlens) {
+            b = 0;
+            t0 = cu_seqlens[s];
+            t1 = cu_seqlens[s + 1];
+        } else {
+            b = s;
+            t0 = 0;
+            t1 = T;
+        }
+        double *S = (double *)malloc(sizeof(double) * (size_t)dk * dv);
+        double *pred = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (S0)
+            memcpy(S, S0 + ((size_t)s * H + h) * dk * dv, sizeof(double) * (size_t)dk * dv);
+        else
+            memset(S, 0, sizeof(double) * (size_t)dk * dv);
+        for (t = t0; t < t1; ++t) {
+            size_t row = ((size_t)b * T + t) * H + h;
+            erase_write_step(S, q + row * dk, k + row * dk, v + row * dv, gate + row * gdim, astride,
+                             erase + row * dk, write + row * dv, o + row * dv, pred, dk, dv);
+        }
+        if (S_T)
+            memcpy(S_T + ((size_t)s * H + h) * dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        free(S);
+        free(pred);
+    }
+    return 0;
+}
+
+/* One decode step with erase and write gates: erase [N,H,dk], write [N,H,dv]. */
+int kda_oracle_decode_ew(const double *q, const double *k, const double *v, const double *gate,
+                         const double *erase, const double *write, double *S, double *o, int N, int H,
+                         int dk, int dv, int gate_kind)
+{
+    if (!q || !k || !v || !gate || !erase || !write || !S || !o || N <= 0 || H <= 0 || dk <= 0 ||
+        dv <= 0)
+        return -1;
+    if (gate_kind != GATE_CHANNEL && gate_kind != GATE_SCALAR)
+        return -1;
+    const int gdim = gate_kind == GATE_CHANNEL ? dk : 1;
+    const int astride = gate_kind == GATE_CHANNEL ? 1 : 0;
+    long pairs = (long)N * H;
+    long p;
+#pragma omp parallel for schedule(static)
+    for (p = 0; p < pairs; ++p) {
+        double *pred = (double *)malloc(sizeof(double) * (size_t)dv);
+        erase_write_step(S + (size_t)p * dk * dv, q + (size_t)p * dk, k + (size_t)p * dk,
+                         v + (size_t)p * dv, gate + (size_t)p * gdim, astride, erase + (size_t)p * dk,
+                         write + (size_t)p * dv, o + (size_t)p * dv, pred, dk, dv);
+        free(pred);
+    }
+    return 0;
+}
+
+/*
  * Reverse-mode gradient of the forward above (the chain rule applied to the
  * delta form, token by token, last token first). With the loss
  *   L = sum_t <o_t, dO_t> + <S_T, dS_T>

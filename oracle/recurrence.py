@@ -16,7 +16,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
-_LIB = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIB names a prebuilt copy (the sanitizer build); build() then
+# leaves it alone unless forced.
+_LIB = os.environ.get("KDA_ORACLE_LIB") or os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -43,6 +45,10 @@ def _load():
         lib.kda_oracle_fwd.argtypes = [_dp] * 7 + [_dp] + [ctypes.c_int] * 5 + [_ip] + [ctypes.c_int] * 2
         lib.kda_oracle_decode.restype = ctypes.c_int
         lib.kda_oracle_decode.argtypes = [_dp] * 7 + [ctypes.c_int] * 5
+        lib.kda_oracle_fwd_ew.restype = ctypes.c_int
+        lib.kda_oracle_fwd_ew.argtypes = [_dp] * 9 + [ctypes.c_int] * 5 + [_ip] + [ctypes.c_int] * 2
+        lib.kda_oracle_decode_ew.restype = ctypes.c_int
+        lib.kda_oracle_decode_ew.argtypes = [_dp] * 8 + [ctypes.c_int] * 5
         lib.kda_oracle_bwd.restype = ctypes.c_int
         lib.kda_oracle_bwd.argtypes = [_dp] * 14 + [ctypes.c_int] * 5 + [_ip] + [ctypes.c_int] * 2
         _lib = lib
@@ -149,4 +155,51 @@ def decode_step(q, k, v, gate, beta, S: np.ndarray, gate_kind: int = 0) -> np.nd
                                N, H, dk, dv, int(gate_kind))
     if rc != 0:
         raise ValueError("kda_oracle_decode rejected its arguments")
+    return o
+
+
+def fwd_ew(q, k, v, gate, erase, write, S0=None, cu_seqlens=None, gate_kind: int = 0):
+    """The recurrence with decoupled erase and write gates (Gated DeltaNet-2
+    blurb; reading in kda_oracle.c):
+        S_t = (I - k_t (e_t o k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t o v_t)^T.
+    erase [B,T,H,dk], write [B,T,H,dv]; everything else as for ``fwd``.
+    Returns (o, S_T) as fp64 numpy."""
+    lib = _load()
+    q, k, v, gate, erase, write = (_f64(t) for t in (q, k, v, gate, erase, write))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    cu = None
+    nseq = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if isinstance(cu_seqlens, torch.Tensor)
+                                             else cu_seqlens), dtype=np.int32)
+        nseq = cu.size - 1
+    if erase.shape != k.shape or write.shape != v.shape:
+        raise ValueError("erase must be shaped like k and write like v")
+    s0 = None if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((nseq, H, dk, dv))
+    rc = lib.kda_oracle_fwd_ew(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(erase), _ptr(write),
+                               None if s0 is None else _ptr(s0), _ptr(o), _ptr(ST), B, H, T, dk, dv,
+                               None if cu is None else cu.ctypes.data_as(_ip), nseq, int(gate_kind))
+    if rc != 0:
+        raise ValueError("kda_oracle_fwd_ew rejected its arguments")
+    return o, ST
+
+
+def decode_step_ew(q, k, v, gate, erase, write, S: np.ndarray, gate_kind: int = 0) -> np.ndarray:
+    """One decode step with erase [N,H,dk] and write [N,H,dv] gates; ``S``
+    (fp64 numpy [N,H,dk,dv]) is updated in place. Returns o [N,H,dv]."""
+    lib = _load()
+    q, k, v, gate, erase, write = (_f64(t) for t in (q, k, v, gate, erase, write))
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if erase.shape != k.shape or write.shape != v.shape:
+        raise ValueError("erase must be shaped like k and write like v")
+    o = np.zeros((N, H, dv))
+    rc = lib.kda_oracle_decode_ew(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(erase), _ptr(write), _ptr(S),
+                                  _ptr(o), N, H, dk, dv, int(gate_kind))
+    if rc != 0:
+        raise ValueError("kda_oracle_decode_ew rejected its arguments")
     return o
