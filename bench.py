@@ -7,12 +7,20 @@ on one MI355X, with roofline fractions and the fp64 CPU oracle as baseline.
 A step is one kda_chunk_fwd call over the Complex KDA workload (B=2, H=16,
 T=8192, dk=dv=128, bf16 inputs, fp32 state, chunk 64): 16,384 tokens. Two
 seeded input sets alternate so the 256 MB last-level cache cannot hold the
-whole working set. The decode step (N=256 sequences, H=32, d=128, fp32 state
-of 512 MiB updated in place) is timed as one block of 128 consecutive steps.
-The backward (kda_chunk_bwd, gradients of every input for given dO and
-dS_T) is timed on the same forward workload. Forward and backward are also
-timed at 32k tokens per step (B=4, H=16, T=8192) with the KDA and the Complex
-KDA gate recipes, for the throughput ratio of the two.
+whole working set. The other forward workloads are timed the same way and
+reported under "configs": KDA (B=4, H=16, T=4096), GDN with eight packed
+sequences (H=32, T=110,440; one input set, its 2.7 GB of inputs dwarf the
+cache) and the tiny fp32 case. The forward workloads run back to back with
+no host work in between, the headline last, so that its W warm-up calls and
+K timed calls run at the clock the device holds under sustained work (after
+an idle period the clock needs about 20 ms of load to ramp up). The GPU
+clock is read from sysfs while the timed calls are still executing.
+The decode step (N=256 sequences, H=32, d=128, fp32 state of 512 MiB updated
+in place) is timed as one block of 128 consecutive steps. The backward
+(kda_chunk_bwd, gradients of every input for given dO and dS_T) is timed on
+the same forward workload. Forward and backward are also timed at 32k tokens
+per step (B=4, H=16, T=8192) with the KDA and the Complex KDA gate recipes,
+for the throughput ratio of the two.
 Timing uses HIP events recorded on the stream the kernels run on. Prints one
 JSON line.
 """
@@ -135,6 +143,104 @@ def gpu_clock():
     return None
 
 
+def sclk_now():
+    """The active shader-clock level of the first GPU in sysfs (the line the
+    driver marks with '*', e.g. '1: 2400Mhz'), or None where unreadable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return line.strip().rstrip("*").strip()
+        except OSError:
+            continue
+    return None
+
+
+def timed_with_clock(fn, iters: int, stream):
+    """time_region, plus the shader clock read after the calls are enqueued
+    and before the device has finished them (so, during the timed work)."""
+    import torch
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    end.record(stream)
+    clk = sclk_now()
+    busy = not end.query()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters, clk if busy else None
+
+
+def walker_name(bf16: bool, dk: int, chunk: int, slices: int, cus: int) -> str:
+    """The state kernel kda_chunk_fwd launches for a shape (same rule as the
+    library's dispatcher)."""
+    if not bf16:
+        return "chunk_state_kernel"
+    if dk == 128 and chunk == 64:
+        return "chunk_state_slice_kernel" if slices <= cus else "chunk_state_quad_kernel"
+    if chunk == 64 and dk >= 64:
+        return "chunk_state_pair_kernel"
+    return "chunk_state_kernel"
+
+
+def forward_leg(kda, name, sets, w, warmup, steps, stream, dev, with_clock=False):
+    """Warm-up, then `steps` timed kda_chunk_fwd calls rotating over the input
+    sets; the prep and state launches timed on their own. Returns the
+    measurements and the (call, stage) closures."""
+    import torch
+    B, H, T, dk, dv, C = w.B, w.H, w.T, w.dk, w.dv, w.chunk
+    N = w.n_seqs
+    varlen = w.cu_seqlens is not None
+    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+    ST = torch.empty((N, H, dk, dv), device=dev, dtype=torch.float32)
+    ws = torch.empty(kda.workspace_bytes(B, H, T, dk, dv, C, N, varlen, w.dtype), device=dev, dtype=torch.uint8)
+
+    def fwd(i, stage=kda.STAGE_ALL):
+        q, k, v, g, b, cu = sets[i % len(sets)]
+        kda.chunk_fwd(q, k, v, g, b, cu_seqlens=cu, chunk=C, gate_kind=w.gate_kind, out=o, S_T=ST, workspace=ws,
+                      stage=stage)
+
+    for i in range(warmup):
+        fwd(i)
+    if with_clock:
+        ms, clk = timed_with_clock(fwd, steps, stream)
+    else:
+        ms, clk = time_region(fwd, steps, stream), None
+    ms_med, ms_min = per_call_ms(fwd, min(steps, 200), stream)
+    ms_prep = time_region(lambda i: fwd(i, kda.STAGE_PREP), min(steps, 50), stream)
+    fwd(0, kda.STAGE_PREP)
+    ms_state = time_region(lambda i: fwd(0, kda.STAGE_STATE), min(steps, 50), stream)
+    status = kda.fwd_status(ws)
+    tokens = B * T
+    head_tokens = tokens * H
+    in_bytes = 2 if w.dtype == torch.bfloat16 else 4
+    alg_bytes = head_tokens * fwd_bytes_per_head_token(dk, dv, w.gate_kind == 1, in_bytes) + N * H * dk * dv * 4
+    alg_flops = head_tokens * fwd_flops_per_head_token(dk, dv)
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    walker = walker_name(w.dtype == torch.bfloat16, dk, C, N * H * (dv // 16), cus)
+    rec = {
+        "workload": name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C, "sequences": N,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "input_sets": len(sets),
+        "ms_per_call": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+        "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": alg_bytes},
+        "mfma_frac_algorithmic": round(alg_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernels_ms": {"chunk_prep_kernel": round(ms_prep, 4), walker: round(ms_state, 4)},
+        "per_call_ms": {"median": round(ms_med, 4), "min": round(ms_min, 4)},
+        "status": kda.strerror(status),
+    }
+    if with_clock:
+        rec["sclk_during_timed_calls"] = clk
+    print("[bench] %s %.4f ms/call (prep %.4f, state %.4f), %.1f M tokens/s"
+          % (name, ms, ms_prep, ms_state, tokens / (ms * 1e-3) / 1e6), file=sys.stderr, flush=True)
+    return rec, fwd, (o, ST, ws)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +256,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-gauge", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-ratio", action="store_true", help="skip the Complex KDA / KDA throughput ratio")
+    ap.add_argument("--no-configs", action="store_true", help="time the headline forward workload only")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the gated delta-rule path here is single-GPU "
@@ -168,37 +275,42 @@ def main(argv=None) -> int:
 
     # ---------------------------------------------------------------- forward
     print("[bench] generating inputs", file=sys.stderr, flush=True)
-    sets = []
-    for seed in (0, 1):
-        w = inputs.ckda_fwd(seed=seed)
-        sets.append(tuple(t.to(dev) for t in (w.q, w.k, w.v, w.gate, w.beta)))
+
+    def dev_set(w):
+        return tuple(None if t is None else t.to(dev) for t in (w.q, w.k, w.v, w.gate, w.beta, w.cu_seqlens))
+
+    w3 = [inputs.ckda_fwd(seed=s_) for s_ in (0, 1)]
+    sets = [dev_set(x) for x in w3]
+    w = w3[0]
+    others = {}
+    if not args.no_configs:
+        w2 = [inputs.kda_fwd(seed=s_) for s_ in (0, 1)]
+        w1 = [inputs.tiny_kda(seed=s_) for s_ in (0, 1)]
+        w4 = inputs.gdn_varlen(seed=0)
+        others = {"kda_fwd_b4_h16_t4096_d128_chunk64": (w2[0], [dev_set(x) for x in w2]),
+                  "gdn_varlen_h32_t110440_d128_chunk64": (w4, [dev_set(w4)]),
+                  "tiny_kda_fp32_b1_h1_t64_d16_chunk16": (w1[0], [dev_set(x) for x in w1])}
+        del w2, w1, w4
     B, H, T, dk, dv, C = w.B, w.H, w.T, w.dk, w.dv, w.chunk
     tokens = B * T
-    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
-    ST = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
-    wsb = kda.workspace_bytes(B, H, T, dk, dv, C)
-    ws = torch.empty(wsb, device=dev, dtype=torch.uint8)
 
-    def fwd(i, stage=kda.STAGE_ALL):
-        q, k, v, g, b = sets[i % 2]
-        kda.chunk_fwd(q, k, v, g, b, chunk=C, gate_kind=0, out=o, S_T=ST, workspace=ws, stage=stage)
-
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        fwd(i)
-    torch.cuda.synchronize()
-    ms = time_region(fwd, args.steps, stream)
-    print("[bench] forward %.3f ms/step" % ms, file=sys.stderr, flush=True)
-    ms_med, ms_min = per_call_ms(fwd, args.steps, stream)
-    ms_prep = time_region(lambda i: fwd(i, kda.STAGE_PREP), min(args.steps, 50), stream)
-    fwd(0, kda.STAGE_PREP)
-    ms_state = time_region(lambda i: fwd(0, kda.STAGE_STATE), min(args.steps, 50), stream)
-    print("[bench] prep %.3f ms, state %.3f ms" % (ms_prep, ms_state), file=sys.stderr, flush=True)
+    # the other forward workloads first, then the headline, with no idle gap
+    configs = {}
+    print("[bench] forward", file=sys.stderr, flush=True)
+    for name, (wx, sx) in others.items():
+        rec, _, bufs = forward_leg(kda, name, sx, wx, args.warmup, args.steps, stream, dev)
+        configs[name] = rec
+        del bufs
+    head, fwd, (o, ST, ws) = forward_leg(kda, "ckda_fwd_b2_h16_t8192_d128_chunk64", sets, w, args.warmup, args.steps,
+                                         stream, dev, with_clock=True)
+    others.clear()
+    ms = head["ms_per_call"]
+    ms_prep = head["kernels_ms"]["chunk_prep_kernel"]
+    ms_state = [v_ for k_, v_ in head["kernels_ms"].items() if k_ != "chunk_prep_kernel"][0]
 
     traffic_fwd, traffic_dec, traffic_bwd = measured_traffic()
     head_tokens = tokens * H
-    alg_bytes = head_tokens * fwd_bytes_per_head_token(dk, dv, False) + B * H * dk * dv * 4
-    alg_flops = head_tokens * fwd_flops_per_head_token(dk, dv)
+    alg_bytes = head["hbm"]["bytes_per_launch"]
     tok_s = tokens / (ms * 1e-3)
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
     roofline = {
@@ -211,9 +323,9 @@ def main(argv=None) -> int:
         "kernel": "kda_chunk_fwd: chunk_prep_kernel then chunk_state_slice_kernel (one call, one stream)",
         "bytes_per_launch": alg_bytes,
         "launch_ms": round(ms, 4),
-        "mfma_frac_algorithmic": round(alg_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "kernels_ms": {"chunk_prep_kernel": round(ms_prep, 4), "chunk_state_slice_kernel": round(ms_state, 4)},
-        "per_call_ms": {"median": round(ms_med, 4), "min": round(ms_min, 4)},
+        "mfma_frac_algorithmic": head["mfma_frac_algorithmic"],
+        "kernels_ms": head["kernels_ms"],
+        "per_call_ms": head["per_call_ms"],
     }
     # the same workload through the gauge route (signs folded into q and k,
     # positive-gate forward, S_T rows flipped back)
@@ -222,7 +334,7 @@ def main(argv=None) -> int:
         wsg = torch.empty(kda.fwd_gauge_workspace_bytes(B, H, T, dk, dv, C), device=dev, dtype=torch.uint8)
 
         def fwd_g(i):
-            q, k, v, g, b = sets[i % 2]
+            q, k, v, g, b, _ = sets[i % 2]
             kda.chunk_fwd_gauge(q, k, v, g, b, chunk=C, gate_kind=0, out=o, S_T=ST, workspace=wsg)
 
         for i in range(args.warmup):
@@ -411,11 +523,14 @@ def main(argv=None) -> int:
                    "chunk": C, "tokens_per_step": tokens, "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "status": head["status"],
+        "sclk_during_timed_calls": head.get("sclk_during_timed_calls"),
+        "configs": configs,
         "decode": decode,
         "backward": backward,
         "gauge_route": gauge,
         "ckda_vs_kda": ratio,
-        "gpu_clock": gpu_clock(),
+        "gpu_clock_after_run": gpu_clock(),
     }
     print(json.dumps(line), flush=True)
     return 0

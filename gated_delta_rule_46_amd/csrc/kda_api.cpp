@@ -1,7 +1,7 @@
 // C ABI: argument validation (before any HIP call) and dispatch.
 #include "../../include/kda.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include "kda_launch.h"
 
@@ -21,37 +21,13 @@ int hip_status(hipError_t e) {
 
 }  // namespace
 
-extern "C" {
+namespace kda {
 
-int kda_version(void) { return 100; }
-
-const char* kda_strerror(int status) {
-    switch (status) {
-        case KDA_OK: return "success";
-        case KDA_EINVAL: return "invalid argument";
-        case KDA_ENOTSUP: return "unsupported size, chunk, dtype or gate kind";
-        case KDA_EALIGN: return "pointer misaligned for its element type, or a 16-byte-aligned buffer is not";
-        case KDA_EHIP: return "HIP runtime error";
-        default: return "unknown status";
-    }
-}
-
-int kda_last_hip_error(void) { return g_last_hip; }
-
-size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int N, int has_cu,
-                                     int dtype) {
-    if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return 0;
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
-    if (has_cu && (B != 1 || N <= 0)) return 0;
-    return kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, has_cu != 0, has_cu ? N : B, dtype == KDA_BF16);
-}
-
-int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const void* gate,
-                        const void* beta, const float* S0, float* o, float* S_T, int B, int H, int T, int dk,
-                        int dv, int chunk, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+int validate_chunk_fwd(int stage, const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                       const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
+                       const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* stream, ChunkArgs* args,
+                       size_t* need) {
     if (stage != KDA_STAGE_ALL && stage != KDA_STAGE_PREP && stage != KDA_STAGE_STATE) return KDA_EINVAL;
-    if (stage != KDA_STAGE_ALL && !workspace) return KDA_EINVAL;
     if (B <= 0 || H <= 0 || T < 0) return KDA_EINVAL;
     if (!size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return KDA_ENOTSUP;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ENOTSUP;
@@ -69,29 +45,61 @@ int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, 
     if (need_data && (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(gate) || !aligned(beta, es) ||
                       !aligned(o, 4)))
         return KDA_EALIGN;
-    if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) || (workspace && !aligned(workspace))) return KDA_EALIGN;
+    if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4))) return KDA_EALIGN;
     if (varlen && !aligned(cu_seqlens, 4)) return KDA_EALIGN;
-    const size_t need = kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, N, dtype == KDA_BF16);
-    if (workspace && workspace_bytes < need) return KDA_EINVAL;
-    if (!need_data && !S_T) return KDA_OK;
-    if (stage == KDA_STAGE_PREP && !need_data) return KDA_OK;
+    *need = chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, N, dtype == KDA_BF16);
+    *args = ChunkArgs{q, k, v, gate, beta, S0, o, S_T, B, H, T, dk, dv, chunk, cu_seqlens, N, dtype == KDA_BF16,
+                      gate_kind == KDA_GATE_SCALAR, nullptr, reinterpret_cast<hipStream_t>(stream), stage};
+    return KDA_OK;
+}
 
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    void* ws = workspace;
-    bool owned = false;
-    if (!ws && need > 0) {
-        hipError_t e = hipMallocAsync(&ws, need, st);
-        if (e != hipSuccess) return hip_status(e);
-        owned = true;
+int hip_to_status(hipError_t e) { return hip_status(e); }
+
+}  // namespace kda
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char* kda_strerror(int status) {
+    switch (status) {
+        case KDA_OK: return "success";
+        case KDA_EINVAL: return "invalid argument";
+        case KDA_ENOTSUP: return "unsupported size, chunk, dtype or gate kind";
+        case KDA_EALIGN: return "pointer misaligned for its element type, or a 16-byte-aligned buffer is not";
+        case KDA_EHIP: return "HIP runtime error";
+        case KDA_EWAIT: return "a bounded wait in the forward's state pass expired; o and S_T were not written";
+        default: return "unknown status";
     }
-    kda::ChunkArgs a{q, k, v, gate, beta, S0, o, S_T, B, H, T, dk, dv, chunk, cu_seqlens, N,
-                     dtype == KDA_BF16, gate_kind == KDA_GATE_SCALAR, ws, st, stage};
-    hipError_t e = kda::launch_chunk_fwd(a);
-    if (owned) {
-        hipError_t f = hipFreeAsync(ws, st);
-        if (e == hipSuccess) e = f;
-    }
-    return hip_status(e);
+}
+
+int kda_last_hip_error(void) { return g_last_hip; }
+
+int kda_chunk_fwd_status(uint32_t status_word) { return status_word == 0u ? KDA_OK : KDA_EWAIT; }
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int N, int has_cu,
+                                     int dtype) {
+    if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk) || !size_ok(dv) || !chunk_ok(chunk)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (has_cu && (B != 1 || N <= 0)) return 0;
+    return kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, has_cu != 0, has_cu ? N : B, dtype == KDA_BF16);
+}
+
+int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const void* gate,
+                        const void* beta, const float* S0, float* o, float* S_T, int B, int H, int T, int dk,
+                        int dv, int chunk, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    kda::ChunkArgs a;
+    size_t need = 0;
+    const int st = kda::validate_chunk_fwd(stage, q, k, v, gate, beta, S0, o, S_T, B, H, T, dk, dv, chunk, cu_seqlens,
+                                           N, dtype, gate_kind, stream, &a, &need);
+    if (st != KDA_OK) return st;
+    if (workspace && !aligned(workspace)) return KDA_EALIGN;
+    if (!workspace || workspace_bytes < need) return KDA_EINVAL;
+    if (T == 0 && !S_T) return KDA_OK;
+    if (stage == KDA_STAGE_PREP && T == 0) return KDA_OK;
+    a.workspace = workspace;
+    return hip_status(kda::launch_chunk_fwd(a));
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate, const void* beta,
@@ -138,25 +146,13 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
         return KDA_EALIGN;
     if (varlen && !aligned(cu_seqlens, 4)) return KDA_EALIGN;
     const size_t need = kda::bwd_workspace_bytes(B, H, T, dk, dv, varlen, N);
-    if (workspace && workspace_bytes < need) return KDA_EINVAL;
+    if (!workspace || workspace_bytes < need) return KDA_EINVAL;
     if (!need_data && !grad_S0) return KDA_OK;
 
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    void* ws = workspace;
-    bool owned = false;
-    if (!ws && need > 0) {
-        hipError_t e = hipMallocAsync(&ws, need, st);
-        if (e != hipSuccess) return hip_status(e);
-        owned = true;
-    }
     kda::BwdArgs a{q, k, v, gate, beta, S0, dO, dS_T, grad_q, grad_k, grad_v, grad_gate, grad_beta, grad_S0,
-                   B, H, T, dk, dv, cu_seqlens, N, dtype == KDA_BF16, gate_kind == KDA_GATE_SCALAR, ws, st};
-    hipError_t e = kda::launch_chunk_bwd(a);
-    if (owned) {
-        hipError_t f = hipFreeAsync(ws, st);
-        if (e == hipSuccess) e = f;
-    }
-    return hip_status(e);
+                   B, H, T, dk, dv, cu_seqlens, N, dtype == KDA_BF16, gate_kind == KDA_GATE_SCALAR, workspace,
+                   reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(kda::launch_chunk_bwd(a));
 }
 
 size_t kda_gauge_fold_workspace_bytes(int B, int H, int T, int dk, int N, int has_cu, int gate_kind) {
@@ -189,39 +185,29 @@ int kda_gauge_fold(const void* q, const void* k, const void* gate, void* q_out, 
         return KDA_EALIGN;
     if ((workspace && !aligned(workspace)) || (varlen && !aligned(cu_seqlens, 4))) return KDA_EALIGN;
     const size_t need = kda::gauge_fold_workspace_bytes(H, T, N, gate_kind == KDA_GATE_SCALAR ? 1 : dk);
-    if (workspace && workspace_bytes < need) return KDA_EINVAL;
+    if (!workspace || workspace_bytes < need) return KDA_EINVAL;
     if (!need_data && !sign_T) return KDA_OK;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    void* ws = workspace;
-    bool owned = false;
-    if (!ws) {
-        hipError_t e = hipMallocAsync(&ws, need, st);   // need >= 256
-        if (e != hipSuccess) return hip_status(e);
-        owned = true;
-    }
     kda::GaugeArgs a{q, k, gate, q_out, k_out, gate_out, B, H, T, dk, cu_seqlens, N, dtype == KDA_BF16,
-                     gate_kind == KDA_GATE_SCALAR, ws, st};
-    hipError_t e = kda::launch_gauge_fold(a, sign_T);
-    if (owned) {
-        hipError_t f = hipFreeAsync(ws, st);
-        if (e == hipSuccess) e = f;
-    }
-    return hip_status(e);
+                     gate_kind == KDA_GATE_SCALAR, workspace, reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(kda::launch_gauge_fold(a, sign_T));
 }
 
 namespace {
-// Offsets in the gauge route's workspace: the folded q, k and gate, c_T, the
-// fold's scratch, then the forward's own workspace (from off[5]).
-void gauge_route_parts(int B, int H, int T, int dk, int N, bool bf16, bool sg, size_t* off) {
+// Offsets in the gauge route's workspace: the forward's own workspace first
+// (so that its status word sits at offset 0, as for kda_chunk_fwd), then the
+// folded q, k and gate, c_T and the fold's scratch; off[6] is the total.
+void gauge_route_parts(int B, int H, int T, int dk, int dv, int chunk, bool varlen, int N, bool bf16, bool sg,
+                       size_t* off) {
     const size_t es = bf16 ? 2 : 4, gdim = sg ? 1 : (size_t)dk;
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t qb = al((size_t)B * T * H * dk * es), gb = al((size_t)B * T * H * gdim * es);
-    off[0] = 0;                  // q~
-    off[1] = off[0] + qb;        // k~
-    off[2] = off[1] + qb;        // alpha~
-    off[3] = off[2] + gb;        // c_T [N][H][gdim]
-    off[4] = off[3] + al((size_t)N * H * gdim);                                   // fold scratch
-    off[5] = off[4] + al(kda::gauge_fold_workspace_bytes(H, T, N, (int)gdim));     // forward workspace
+    off[5] = 0;                                                                      // forward workspace
+    off[0] = al(kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, N, bf16));   // q~
+    off[1] = off[0] + qb;                                                            // k~
+    off[2] = off[1] + qb;                                                            // alpha~
+    off[3] = off[2] + gb;                                                            // c_T [N][H][gdim]
+    off[4] = off[3] + al((size_t)N * H * gdim);                                      // fold scratch
+    off[6] = off[4] + al(kda::gauge_fold_workspace_bytes(H, T, N, (int)gdim));
 }
 }  // namespace
 
@@ -232,9 +218,10 @@ size_t kda_chunk_fwd_gauge_workspace_bytes(int B, int H, int T, int dk, int dv, 
     if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return 0;
     if (has_cu && (B != 1 || N <= 0)) return 0;
     const bool varlen = has_cu != 0;
-    size_t off[6];
-    gauge_route_parts(B, H, T, dk, varlen ? N : B, dtype == KDA_BF16, gate_kind == KDA_GATE_SCALAR, off);
-    return off[5] + kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, varlen ? N : B, dtype == KDA_BF16);
+    size_t off[7];
+    gauge_route_parts(B, H, T, dk, dv, chunk, varlen, varlen ? N : B, dtype == KDA_BF16,
+                      gate_kind == KDA_GATE_SCALAR, off);
+    return off[6];
 }
 
 int kda_chunk_fwd_gauge(const void* q, const void* k, const void* v, const void* gate, const void* beta,
@@ -261,22 +248,14 @@ int kda_chunk_fwd_gauge(const void* q, const void* k, const void* v, const void*
     if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) || (workspace && !aligned(workspace))) return KDA_EALIGN;
     if (varlen && !aligned(cu_seqlens, 4)) return KDA_EALIGN;
     const bool sg = gate_kind == KDA_GATE_SCALAR;
-    size_t off[6];
-    gauge_route_parts(B, H, T, dk, N, dtype == KDA_BF16, sg, off);
-    const size_t fwd_ws = kda::chunk_workspace_bytes(B, H, T, dk, dv, chunk, varlen, N, dtype == KDA_BF16);
-    const size_t need = off[5] + fwd_ws;
-    if (workspace && workspace_bytes < need) return KDA_EINVAL;
+    size_t off[7];
+    gauge_route_parts(B, H, T, dk, dv, chunk, varlen, N, dtype == KDA_BF16, sg, off);
+    const size_t need = off[6];
+    if (!workspace || workspace_bytes < need) return KDA_EINVAL;
     if (!need_data && !S_T) return KDA_OK;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    void* ws = workspace;
-    bool owned = false;
-    if (!ws) {
-        hipError_t e = hipMallocAsync(&ws, need, st);
-        if (e != hipSuccess) return hip_status(e);
-        owned = true;
-    }
-    unsigned char* w = static_cast<unsigned char*>(ws);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
     int8_t* sign = reinterpret_cast<int8_t*>(w + off[3]);
     kda::GaugeArgs g{q, k, gate, w + off[0], w + off[1], w + off[2], B, H, T, dk, cu_seqlens, N, dtype == KDA_BF16,
                      sg, w + off[4], st};
@@ -287,10 +266,6 @@ int kda_chunk_fwd_gauge(const void* q, const void* k, const void* v, const void*
         e = kda::launch_chunk_fwd(a);
     }
     if (e == hipSuccess && S_T) e = kda::launch_gauge_state_flip(S_T, sign, N, H, dk, dv, sg, st);
-    if (owned) {
-        hipError_t f = hipFreeAsync(ws, st);
-        if (e == hipSuccess) e = f;
-    }
     return hip_status(e);
 }
 

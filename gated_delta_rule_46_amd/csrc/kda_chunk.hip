@@ -45,7 +45,6 @@
 // stays fp32. The triangular inverse runs in fp32. The one term that dominates
 // an output -- the current token's own update, P_rr u_r -- is applied in fp32.
 // With fp32 inputs every contraction runs on fp32 MFMA instead.
-#include <mutex>
 #include <type_traits>
 
 #include "kda_common.h"
@@ -356,7 +355,8 @@ struct PrepLds {
     static constexpr size_t RGN = al(RED + 32 * 4);                     // reused region
     // staged value rows (value width up to 128)
     static constexpr size_t VST = RGN;
-    static constexpr size_t END_V = VST + ((size_t)C * 128 * sizeof(TIn) + 1023) / 1024 * 1024;
+    static constexpr size_t WST = VST + ((size_t)C * 128 * sizeof(TIn) + 1023) / 1024 * 1024;   // write gates
+    static constexpr size_t END_V = WST + ((size_t)C * 128 * sizeof(TIn) + 1023) / 1024 * 1024;
     // Gamma o Q and K_end^T tiles
     static constexpr size_t QGT = RGN;
     static constexpr size_t KET = QGT + (size_t)NBK * KSD * TILE;
@@ -379,6 +379,8 @@ struct PrepLds {
 
 struct PrepParams {
     const void *q, *k, *v, *gate, *beta;
+    const void *erase, *write;   // erase [.., dk] and write [.., dv] gates (erase/write form only)
+    unsigned* status;   // cleared by the first workgroup
     unsigned char* ws;
     size_t blk_bytes;
     ChunkMap map;
@@ -394,7 +396,13 @@ __device__ __forceinline__ bool sep_at(int r, int j, int hh) {
 }
 
 // One (chunk, head) item of the prep work on the four waves of a workgroup.
-template <class TIn, int DK, int C, bool SG, bool F32M>
+// EW: decoupled erase and write gates, S_t = (I - k (e o k)^T) Diag(alpha) S
+// + k (w o v)^T. The chunk identities keep their form with beta = 1, the
+// read key e o k in place of k wherever a row of A or of W = T (Gamma o K) is
+// formed (the rows r that read the state), k itself wherever a column of A
+// or P or a row of K_end is (the direction the state is written along), and
+// w o v in place of v.
+template <class TIn, int DK, int C, bool SG, bool F32M, bool EW>
 __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     using L = Lay<DK, C, F32M>;
     using SM = PrepLds<TIn, DK, C, F32M>;
@@ -430,19 +438,25 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     const TIn* gg = (const TIn*)p.gate;
     const TIn* gb = (const TIn*)p.beta;
 
-    // value rows of the chunk -> LDS, asynchronously and first, so that their
-    // latency overlaps that of the gate loads; rows past the chunk end fall
-    // outside the descriptor and arrive as zeros
+    // value rows of the chunk (and write-gate rows) -> LDS, asynchronously
+    // and first, so that their latency overlaps that of the gate loads; rows
+    // past the chunk end fall outside the descriptor and arrive as zeros
     {
         const int rby = DV * (int)sizeof(TIn);            // bytes of one value row
         const int lpr = rby / 16, rpi = 64 / lpr;          // lanes per row, rows per instruction
         const uint32_t rowb = (uint32_t)H * (uint32_t)rby;
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(gv + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * rowb + (uint32_t)rby);
         const int ni = (C * rby + 1023) / 1024;
-        for (int u = w; u < ni; u += 4) {
-            const uint32_t voff = (uint32_t)(u * rpi + lane / lpr) * rowb + (uint32_t)(lane % lpr) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, (__attribute__((address_space(3))) void*)(smem + SM::VST + (size_t)u * 1024), 16, voff, 0, 0, 0);
+#pragma unroll
+        for (int src = 0; src < (EW ? 2 : 1); ++src) {
+            const TIn* base = src == 0 ? gv : (const TIn*)p.write;
+            const size_t dst = src == 0 ? SM::VST : SM::WST;
+            const __amdgpu_buffer_rsrc_t rv =
+                make_rsrc(base + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * rowb + (uint32_t)rby);
+            for (int u = w; u < ni; u += 4) {
+                const uint32_t voff = (uint32_t)(u * rpi + lane / lpr) * rowb + (uint32_t)(lane % lpr) * 16;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, (__attribute__((address_space(3))) void*)(smem + dst + (size_t)u * 1024), 16, voff, 0, 0, 0);
+            }
         }
     }
 
@@ -450,8 +464,8 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     const bool gate_lane = (w < NBK) && (lane < ACT);
     const int b = w;
     const int c0 = lane * CPL;
-    Gx<TIn, CPL> kk, qq, aa;
-    float mk = 0.f, mq = 0.f;
+    Gx<TIn, CPL> kk, qq, aa, ee;
+    float mk = 0.f, mq = 0.f, me = 0.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         const int tl = 16 * b + t;
@@ -461,18 +475,25 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
             qq.load(gq + row * DK + c0, t);
             if constexpr (SG) aa.fill_from(gg + row, t);
             else aa.load(gg + row * DK + c0, t);
+            if constexpr (EW) ee.load((const TIn*)p.erase + row * DK + c0, t);
         } else {
             kk.fill(t, 0.f);
             qq.fill(t, 0.f);
             aa.fill(t, 1.f);
+            if constexpr (EW) ee.fill(t, 0.f);
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             mk = fmaxf(mk, fabsf(kk.get(t, j)));
             mq = fmaxf(mq, fabsf(qq.get(t, j)));
+            if constexpr (EW) me = fmaxf(me, fabsf(kk.get(t, j) * ee.get(t, j)));
         }
     }
-    if (tid < C) s_beta[tid] = tid < n ? ld_in(gb + (size_t)(t0 + tid) * H + h) : 0.f;
+    if constexpr (EW) {
+        if (tid < C) s_beta[tid] = tid < n ? 1.f : 0.f;
+    } else {
+        if (tid < C) s_beta[tid] = tid < n ? ld_in(gb + (size_t)(t0 + tid) * H + h) : 0.f;
+    }
 
     if (gate_lane) {
 #pragma unroll
@@ -485,10 +506,12 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     }
     mk = wave_max(mk);
     mq = wave_max(mq);
+    if constexpr (EW) me = wave_max(me);
     if (lane == 0) { s_red[w] = mk; s_red[4 + w] = mq; }
+    if (EW && lane == 0) s_red[24 + w] = me;
     wait_vm_all();
     __syncthreads();
-    float sK = 1.f, sQ = 1.f, iK = 1.f, iQ = 1.f;
+    float sK = 1.f, sQ = 1.f, iK = 1.f, iQ = 1.f, sE = 1.f, iE = 1.f;
     if constexpr (!F32M) {
         const float m1 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
         const float m2 = fmaxf(fmaxf(s_red[4], s_red[5]), fmaxf(s_red[6], s_red[7]));
@@ -496,9 +519,15 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
         iK = pow2_inv_scale_for(m1);
         sQ = pow2_scale_for(m2);
         iQ = pow2_inv_scale_for(m2);
+        if constexpr (EW) {
+            const float m3 = fmaxf(fmaxf(s_red[24], s_red[25]), fmaxf(s_red[26], s_red[27]));
+            sE = pow2_scale_for(m3);
+            iE = pow2_inv_scale_for(m3);
+        }
     }
     // scaled operand values for every later phase: k * sK, q * sQ, alpha
-    Hx<TIn, CPL> hk, hq, ha;
+    // (and the read key (e o k) * sE, rounded once to the operand format)
+    Hx<TIn, CPL> hk, hq, ha, hke;
 #pragma unroll
     for (int t = 0; t < 16; ++t)
 #pragma unroll
@@ -506,7 +535,10 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
             hk.set(t, j, kk.get(t, j) * sK);
             hq.set(t, j, qq.get(t, j) * sQ);
             ha.set(t, j, aa.get(t, j));
+            if constexpr (EW) hke.set(t, j, kk.get(t, j) * ee.get(t, j) * sE);
         }
+    // row side of A and of W: the read key (e o k) in the erase/write form
+    auto hr_mul = [&](int t, int j, float f) { return EW ? hke.mul(t, j, f) : hk.mul(t, j, f); };
 
     // ---- value fragments (B operand over tokens), kept in registers until
     // U~ = T V: wave w owns value slices w and w + 4, one scale per column
@@ -538,9 +570,14 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
                         const int cc = ok ? 16 * sl + 4 * (li % 4) : 0;
                         const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) v4s*)(smem + SM::VST + (size_t)(row * DV + cc) * sizeof(TIn)));
+                        v4s rw = r;
+                        if constexpr (EW)
+                            rw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) v4s*)(smem + SM::WST + (size_t)(row * DV + cc) * sizeof(TIn)));
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const float v = ok ? bf16_bits_to_f32((uint16_t)r[j]) : 0.f;
+                            float v = ok ? bf16_bits_to_f32((uint16_t)r[j]) : 0.f;
+                            if constexpr (EW) v *= ok ? bf16_bits_to_f32((uint16_t)rw[j]) : 0.f;
                             x[ks][4 * hf + j] = v;
                             mv = fmaxf(mv, fabsf(v));
                         }
@@ -551,7 +588,11 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
 #pragma unroll
                     for (int pp = 0; pp < 8; ++pp) {
                         const int t = 32 * ks + kpos(lg, pp);
-                        const float v = (sl < DV / 16 && t < C) ? ld_in(vst + t * DV + col) : 0.f;
+                        float v = (sl < DV / 16 && t < C) ? ld_in(vst + t * DV + col) : 0.f;
+                        if constexpr (EW) {
+                            const TIn* wst = reinterpret_cast<const TIn*>(smem + SM::WST);
+                            v *= (sl < DV / 16 && t < C) ? ld_in(wst + t * DV + col) : 0.f;
+                        }
                         x[ks][pp] = v;
                         mv = fmaxf(mv, fabsf(v));
                     }
@@ -572,6 +613,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     hk.opaque();
     hq.opaque();
     ha.opaque();
+    if constexpr (EW) hke.opaque();
     if (gate_lane) {
         float pre[CPL], suf[CPL];
 #pragma unroll
@@ -639,6 +681,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
         hk.opaque();
         hq.opaque();
         ha.opaque();
+        if constexpr (EW) hke.opaque();
         if (gate_lane) {
             const int gs = (b / (2 * hb)) * 2 * hb, midb = gs + hb;
             const bool right = b >= midb;
@@ -659,7 +702,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
 #pragma unroll
                     for (int j = 0; j < CPL; ++j) {
                         f[j] = ha.mul(t, j, f[j]);
-                        x[j] = hk.mul(t, j, f[j]);
+                        x[j] = hr_mul(t, j, f[j]);
                         y[j] = hq.mul(t, j, f[j]);
                     }
                     st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
@@ -723,6 +766,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
             hk.opaque();
             hq.opaque();
             ha.opaque();
+            if constexpr (EW) hke.opaque();
             if (lane < ACT) {
                 if (hh > 0) {
 #pragma unroll
@@ -736,7 +780,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
 #pragma unroll
                             for (int j = 0; j < CPL; ++j) {
                                 f[j] = ha.mul(t, j, f[j]);
-                                x[j] = hk.mul(t, j, f[j]);
+                                x[j] = hr_mul(t, j, f[j]);
                                 y[j] = hq.mul(t, j, f[j]);
                             }
                             st_vals<TM, CPL>(SM::XT + stage_off<TM, KSD>(16 * b + t, c0), x);
@@ -805,7 +849,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     __syncthreads();   // the inverse arrays overlay the level tiles
 
     // ---- A = Diag(beta) A' into LDS (fp32, row-major); largest |P| below the diagonal
-    const float invKK = iK * iK, invQK = iQ * iK;
+    const float invKK = iK * (EW ? iE : iK), invQK = iQ * iK;
     float mp = 0.f;
     {
         auto put_a = [&](int R, int J, const f32x4& t) {
@@ -952,6 +996,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     // ---- (Gamma o K)^T tiles (rows channels, K over tokens) for W
     hk.opaque();
     ha.opaque();
+    if constexpr (EW) hke.opaque();
     if (gate_lane) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -961,7 +1006,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 r = ha.mul(t, j, r);
-                gk[t] = hk.mul(t, j, r);
+                gk[t] = hr_mul(t, j, r);
             }
 #pragma unroll
             for (int u = 0; u < 16; u += 4) {
@@ -1022,7 +1067,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     constexpr int NWI = (RB * KSD + 3) / 4;
     f32x4 wt[NWI][2];
     float mw = 0.f;
-    const float invKT = iK * iT;
+    const float invKT = (EW ? iE : iK) * iT;
 #pragma unroll
     for (int j = 0; j < NWI; ++j) {
         wt[j][0] = zero4();
@@ -1080,9 +1125,10 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     }
 }
 
-template <class TIn, int DK, int C, bool SG, bool F32M>
-__global__ void __launch_bounds__(256, F32M ? 1 : 3) chunk_prep_kernel(PrepParams p) {
-    prep_item<TIn, DK, C, SG, F32M>(p, xcd_remap(blockIdx.x, gridDim.x));
+template <class TIn, int DK, int C, bool SG, bool F32M, bool EW>
+__global__ void __launch_bounds__(256, F32M ? 1 : (EW ? 2 : 3)) chunk_prep_kernel(PrepParams p) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0u;
+    prep_item<TIn, DK, C, SG, F32M, EW>(p, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // ------------------------------------------------------------------ state kernel
@@ -1109,7 +1155,21 @@ struct StateParams {
     size_t blk_bytes;
     ChunkMap map;
     int H, DV, NSG;   // NSG: workgroups per (sequence, head)
+    unsigned* status; // the call's status word: a wave whose bounded wait expired sets STATUS_WAIT_EXPIRED
 };
+
+// Bounded LDS flag waits inside one workgroup. Every wave of the workgroup is
+// resident and posts its flag once per chunk, so a wait ends long before the
+// bound; should it ever expire, the wave stops storing outputs (o through a
+// zero-size descriptor, S_T skipped) and raises the status word instead of
+// writing values computed from stale operands.
+constexpr int WAIT_POLLS = 1 << 24;
+constexpr unsigned STATUS_WAIT_EXPIRED = 1u;
+
+__device__ __forceinline__ void raise_status(unsigned* status, int expired) {
+    if (expired && (threadIdx.x % 64) == 0) __hip_atomic_fetch_or(status, STATUS_WAIT_EXPIRED, __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // NW compute waves per workgroup, each owning SPW 16-column slices of the
 // state; NW copy waves alongside.
@@ -1180,6 +1240,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
     const int hs = item / p.NSG;
     const int H = p.H, DV = p.DV;
     const int h = hs % H, s = hs / H;
+    constexpr int expired = 0;   // this walker has no flag waits
     // waves 0..NW-1 compute SPW 16-column slices each; waves NW..2NW-1 stream
     // the next chunk's block into the other LDS buffer meanwhile
     const int lane = threadIdx.x % 64;
@@ -1358,7 +1419,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
         // Rows past the chunk end fall outside the store descriptor and are dropped.
         {
             const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
+                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, expired ? 0u : (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
             f32x4 pu[SPW][RB];
 #pragma unroll
             for (int j = 0; j < SPW; ++j)
@@ -1500,6 +1561,7 @@ __global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams 
 
     const uint32_t xs = (uint32_t)(SM::XCH + (size_t)sl * SM::XSL);   // this slice's exchange area
     const uint32_t lfr = (uint32_t)lane * 16;
+    int expired = 0;   // wave-uniform: set when a bounded wait ran out
 
     // own state rows 16 (CH hf + c) + 4 lg + e of column col
     f32x4 S[CH];
@@ -1619,7 +1681,9 @@ __global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams 
             extern __shared__ __align__(16) unsigned char smem[];
             typedef __attribute__((address_space(3))) const volatile int lds_flag_t;
             lds_flag_t* flag = (lds_flag_t*)(smem + xs + SM::X_F + 4 * (1 - hf));
-            for (int spin = 0; *flag != cg && spin < (1 << 24); ++spin) __builtin_amdgcn_s_sleep(1);
+            int spin = 0;
+            for (; *flag != cg && spin < WAIT_POLLS; ++spin) __builtin_amdgcn_s_sleep(1);
+            expired |= __builtin_amdgcn_readfirstlane(spin >= WAIT_POLLS ? 1 : 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         const F ufx = lds_ld<F>(xs + (uint32_t)(SM::X_U + (size_t)(1 - hf) * 1024) + lfr);
@@ -1629,7 +1693,7 @@ __global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams 
         // fp32); rows past the chunk end fall outside the store descriptor
         {
             const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
+                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, expired ? 0u : (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
             const uint32_t ovoff = (uint32_t)(4 * lg) * orow + (uint32_t)col * 4;
             const float po = iP * iUo, px = iP * iUx;
 #pragma unroll
@@ -1665,7 +1729,8 @@ __global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams 
         __syncthreads();
     }
 
-    if (!copier && p.S_T) {
+    if (!copier) raise_status(p.status, expired);
+    if (!copier && p.S_T && !expired) {
 #pragma unroll
         for (int c = 0; c < CH; ++c)
 #pragma unroll
@@ -1738,6 +1803,7 @@ __device__ __forceinline__ void quad_walk(const StateParams& p, int item) {
 
     const uint32_t xs = (uint32_t)(SM::XCH + (size_t)sl * SM::XSL);   // this slice's exchange area
     const uint32_t lfr = (uint32_t)lane * 16;
+    int expired = 0;   // wave-uniform: set when a bounded wait ran out
 
     // own state rows 16 (2q + c) + 4 lg + e of column col
     f32x4 S[2];
@@ -1860,10 +1926,12 @@ __device__ __forceinline__ void quad_walk(const StateParams& p, int item) {
             extern __shared__ __align__(16) unsigned char smem[];
             typedef __attribute__((address_space(3))) const volatile int lds_flag_t;
             lds_flag_t* flags = (lds_flag_t*)(smem + xs + SM::X_F);
-            for (int spin = 0; spin < (1 << 24); ++spin) {
+            int spin = 0;
+            for (; spin < WAIT_POLLS; ++spin) {
                 if (flags[0] == cg && flags[1] == cg && flags[2] == cg && flags[3] == cg) break;
                 __builtin_amdgcn_s_sleep(1);
             }
+            expired |= __builtin_amdgcn_readfirstlane(spin >= WAIT_POLLS ? 1 : 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         f32x4 u[4];
@@ -1889,7 +1957,7 @@ __device__ __forceinline__ void quad_walk(const StateParams& p, int item) {
         // descriptor
         {
             const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
+                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, expired ? 0u : (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
             const uint32_t ovoff = (uint32_t)(4 * lg) * orow + (uint32_t)col * 4;
             f32x4 o4 = ov;
 #pragma unroll
@@ -1927,7 +1995,10 @@ __device__ __forceinline__ void quad_walk(const StateParams& p, int item) {
         // keep the L2 touches alive: a store that no real input triggers
         // (H is positive for every launch)
         if (sink == 0x9e3779b9u && p.H < 0) p.o[0] = 0.f;
-    } else if (p.S_T) {
+    } else {
+        raise_status(p.status, expired);
+    }
+    if (!copier && p.S_T && !expired) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -2054,6 +2125,7 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         ce = p.map.cstart[s + 1];
     }
     const uint32_t lfr = (uint32_t)lane * 16;
+    int expired = 0;   // wave-uniform: set when a bounded wait ran out
 
     // own state rows 16 (2q + c) + 4 lg + e of column col
     f32x4 S[2];
@@ -2159,10 +2231,12 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
             lds_flag_t* fl = (lds_flag_t*)(smem + SM::X_F);
             // all four flags read before one wait (not one round trip each);
             // no sleep: the waits are short
-            for (int spin = 0; spin < (1 << 24); ++spin) {
+            int spin = 0;
+            for (; spin < WAIT_POLLS; ++spin) {
                 const int f0 = fl[0], f1 = fl[1], f2 = fl[2], f3 = fl[3];
                 if ((f0 == cg) & (f1 == cg) & (f2 == cg) & (f3 == cg)) break;
             }
+            expired |= __builtin_amdgcn_readfirstlane(spin >= WAIT_POLLS ? 1 : 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         f32x4 u[4];
@@ -2182,7 +2256,7 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
         // ---- O += P U for token rows rb = q, diagonal in fp32
         {
             const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
+                make_rsrc(p.o + ((size_t)t0 * H + h) * DV, expired ? 0u : (uint32_t)(n - 1) * orow + (uint32_t)DV * 4);
             const uint32_t ovoff = (uint32_t)(4 * lg) * orow + (uint32_t)col * 4;
             f32x4 o4 = ov;
 #pragma unroll
@@ -2218,7 +2292,8 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
     }
     // keep the L2 touches alive: a store that no real input triggers
     if (sink == 0x9e3779b9u && p.H < 0) p.o[0] = 0.f;
-    if (p.S_T) {
+    raise_status(p.status, expired);
+    if (p.S_T && !expired) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -2263,22 +2338,26 @@ long chunk_count_bound(int B, int T, int chunk, bool varlen, int N) {
 
 static size_t index_bytes(bool varlen, int N) { return varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0; }
 
+// Workspace: a 256-byte header whose first word is the call's status, the
+// chunk index of packed sequences, then one block per (chunk, head).
+constexpr size_t STATUS_BYTES = 256;
+
 size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, bool varlen, int N, bool bf16) {
-    return index_bytes(varlen, N) + (size_t)chunk_count_bound(B, T, chunk, varlen, N) * H * chunk_block_bytes(dk, dv, chunk, bf16);
+    return STATUS_BYTES + index_bytes(varlen, N) +
+           (size_t)chunk_count_bound(B, T, chunk, varlen, N) * H * chunk_block_bytes(dk, dv, chunk, bf16);
 }
 
+__global__ void __launch_bounds__(64) status_clear_kernel(unsigned* status) {
+    if (threadIdx.x == 0) *status = 0u;
+}
+
+// Compute units of the current device, queried on every call (a device
+// attribute read; no state is kept between calls).
 static int device_cus() {
-    static std::mutex mu;
-    static int per_dev[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    if (per_dev[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        per_dev[dev] = n;
-    }
-    return per_dev[dev];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
 }
 
 template <class K>
@@ -2287,18 +2366,29 @@ static hipError_t allow_lds(K kern, size_t bytes) {
     return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <class TIn, int DK, int C, bool SG>
+template <class TIn, int DK, int C, bool SG, bool EW>
 static hipError_t launch_prep_t(const ChunkArgs& a, const ChunkMap& map, unsigned char* blocks, long nchunks) {
     constexpr bool F32M = std::is_same<TIn, float>::value;
     using SM = PrepLds<TIn, DK, C, F32M>;
     static_assert(SM::BYTES <= 160 * 1024, "prep LDS");
-    auto kern = chunk_prep_kernel<TIn, DK, C, SG, F32M>;
+    auto kern = chunk_prep_kernel<TIn, DK, C, SG, F32M, EW>;
     hipError_t e = allow_lds(kern, SM::BYTES);
     if (e != hipSuccess) return e;
-    PrepParams pp{a.q, a.k, a.v, a.gate, a.beta, blocks, chunk_block_bytes(DK, a.dv, C, !F32M), map, a.H, a.dv};
+    PrepParams pp{a.q, a.k, a.v, a.gate, a.beta, a.erase, a.write, (unsigned*)a.workspace, blocks,
+                  chunk_block_bytes(DK, a.dv, C, !F32M), map, a.H, a.dv};
     const long grid = nchunks * a.H;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), SM::BYTES, a.stream, pp);
     return hipGetLastError();
+}
+
+template <class TIn, int DK, int C>
+static hipError_t launch_prep(const ChunkArgs& a, const ChunkMap& map, unsigned char* blocks, long nchunks) {
+    if (a.erase) {
+        return a.scalar_gate ? launch_prep_t<TIn, DK, C, true, true>(a, map, blocks, nchunks)
+                             : launch_prep_t<TIn, DK, C, false, true>(a, map, blocks, nchunks);
+    }
+    return a.scalar_gate ? launch_prep_t<TIn, DK, C, true, false>(a, map, blocks, nchunks)
+                         : launch_prep_t<TIn, DK, C, false, false>(a, map, blocks, nchunks);
 }
 
 template <class TIn, int DK, int C, int NW, int SPW>
@@ -2310,7 +2400,8 @@ static hipError_t launch_state_w(const ChunkArgs& a, const ChunkMap& map, const 
     hipError_t e = allow_lds(kern, SM::BYTES);
     if (e != hipSuccess) return e;
     const int nsg = a.dv / 16 / SM::NSL;
-    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(DK, a.dv, C, !F32M), map, a.H, a.dv, nsg};
+    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(DK, a.dv, C, !F32M), map, a.H, a.dv, nsg,
+                   (unsigned*)a.workspace};
     const long grid = (long)nsg * a.H * a.N;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(128 * NW), SM::BYTES, a.stream, sp);
     return hipGetLastError();
@@ -2324,7 +2415,8 @@ static hipError_t launch_state_pair(const ChunkArgs& a, const ChunkMap& map, con
     hipError_t e = allow_lds(kern, SM::BYTES);
     if (e != hipSuccess) return e;
     const int nsg = a.dv / 16 / NP;
-    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(DK, a.dv, C, true), map, a.H, a.dv, nsg};
+    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(DK, a.dv, C, true), map, a.H, a.dv, nsg,
+                   (unsigned*)a.workspace};
     const long grid = (long)nsg * a.H * a.N;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(192 * NP), SM::BYTES, a.stream, sp);
     return hipGetLastError();
@@ -2338,7 +2430,8 @@ static hipError_t launch_state_quad(const ChunkArgs& a, const ChunkMap& map, con
     hipError_t e = allow_lds(kern, SM::BYTES);
     if (e != hipSuccess) return e;
     const int nsg = a.dv / 16 / NS;
-    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(128, a.dv, 64, true), map, a.H, a.dv, nsg};
+    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(128, a.dv, 64, true), map, a.H, a.dv, nsg,
+                   (unsigned*)a.workspace};
     const long grid = (long)nsg * a.H * a.N;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(384 * NS), SM::BYTES, a.stream, sp);
     return hipGetLastError();
@@ -2346,7 +2439,8 @@ static hipError_t launch_state_quad(const ChunkArgs& a, const ChunkMap& map, con
 
 static hipError_t launch_state_slice(const ChunkArgs& a, const ChunkMap& map, const unsigned char* blocks) {
     const int nsl = a.dv / 16;
-    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(128, a.dv, 64, true), map, a.H, a.dv, nsl};
+    StateParams sp{a.S0, a.o, a.S_T, blocks, chunk_block_bytes(128, a.dv, 64, true), map, a.H, a.dv, nsl,
+                   (unsigned*)a.workspace};
     const long grid = (long)nsl * a.H * a.N;
     hipLaunchKernelGGL(chunk_state_slice_kernel, dim3((unsigned)grid), dim3(256), SliceLds::BYTES, a.stream, sp);
     return hipGetLastError();
@@ -2384,20 +2478,25 @@ static hipError_t launch_pair(const ChunkArgs& a) {
     unsigned char* ws = (unsigned char*)a.workspace;
     const size_t ib = index_bytes(varlen, a.N);
     const int NC = (a.T + C - 1) / C;
-    ChunkMap map{a.cu_seqlens, varlen ? (const int32_t*)ws : nullptr, a.T, a.N, NC, 0, NC};
-    unsigned char* blocks = ws + ib;
+    int32_t* cidx = (int32_t*)(ws + STATUS_BYTES);
+    ChunkMap map{a.cu_seqlens, varlen ? cidx : nullptr, a.T, a.N, NC, 0, NC};
+    unsigned char* blocks = ws + STATUS_BYTES + ib;
     const long nch = chunk_count_bound(a.B, a.T, C, varlen, a.N);
     if (a.stages & 1) {
         if (varlen) {
-            hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, (int32_t*)ws, a.N, C);
+            hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, cidx, a.N, C);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
+        // the prep's first workgroup clears the status word; without chunks a kernel of its own does
+        hipError_t e;
         if (nch > 0) {
-            hipError_t e = a.scalar_gate ? launch_prep_t<TIn, DK, C, true>(a, map, blocks, nch)
-                                         : launch_prep_t<TIn, DK, C, false>(a, map, blocks, nch);
-            if (e != hipSuccess) return e;
+            e = launch_prep<TIn, DK, C>(a, map, blocks, nch);
+        } else {
+            hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, a.stream, (unsigned*)a.workspace);
+            e = hipGetLastError();
         }
+        if (e != hipSuccess) return e;
     }
     if (a.stages & 2) return launch_state_t<TIn, DK, C>(a, map, blocks);
     return hipSuccess;

@@ -1,7 +1,7 @@
 // Host-side launch descriptors shared by the C-ABI and the kernel files.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -14,6 +14,8 @@ struct DecodeArgs {
     int N, H, dk, dv;
     bool bf16, scalar_gate;
     hipStream_t stream;
+    const void* erase = nullptr;   // erase [N, H, dk] and write [N, H, dv] gates, or none
+    const void* write = nullptr;
 };
 
 struct ChunkArgs {
@@ -28,6 +30,10 @@ struct ChunkArgs {
     void* workspace;
     hipStream_t stream;
     int stages;                 // bit 0: index + prep kernels, bit 1: state kernel
+    // decoupled erase [.., dk] and write [.., dv] gates in the input dtype
+    // (both set, beta unused) or none (both null)
+    const void* erase = nullptr;
+    const void* write = nullptr;
 };
 
 struct BwdArgs {
@@ -69,6 +75,16 @@ size_t gauge_fold_workspace_bytes(int H, int T, int N, int gdim);
 hipError_t launch_gauge_fold(const GaugeArgs& a, int8_t* sign_dev);
 hipError_t launch_gauge_state_flip(float* S, const int8_t* sign, int N, int H, int dk, int dv, bool scalar_gate,
                                    hipStream_t stream);
+
+// Argument checks of kda_chunk_fwd_stage, everything but the workspace (no HIP
+// call): KDA_OK with the launch descriptor (workspace left null) and the
+// workspace bytes the call needs, or a negative status.
+int validate_chunk_fwd(int stage, const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                       const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
+                       const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* stream, ChunkArgs* args,
+                       size_t* need);
+// hipError_t -> KDA status (KDA_EHIP records the code for kda_last_hip_error).
+int hip_to_status(hipError_t e);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);

@@ -109,6 +109,18 @@ def ckda_gate_beta(rng, gshape, bshape, signs: np.ndarray):
     return gate, beta
 
 
+def signed_zero_gates(gate: torch.Tensor, seed: int, frac: float = 0.03) -> torch.Tensor:
+    """A copy of ``gate`` with about ``frac`` of its elements replaced, in
+    equal parts, by -0.0, +0.0 and -1.0 (a stress mix of both zero signs and
+    exact sign flips; any dtype with signed zeros)."""
+    u = torch.from_numpy(np.random.default_rng(seed + 104729).random(size=tuple(gate.shape)))
+    out = gate.clone()
+    out[u < frac] = -1.0
+    out[u < 2.0 * frac / 3.0] = 0.0
+    out[u < frac / 3.0] = -0.0
+    return out
+
+
 def spread_signs(rng, H: int, dk: int) -> np.ndarray:
     return np.where(rng.random(size=(H, dk)) < 0.5, -1.0, 1.0)
 

@@ -13,9 +13,11 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkda.so")
+# KDA_LIB names another build of the same library (the sanitizer build of the
+# host-side validation code loads that way); default: the in-tree libkda.so.
+LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(_HERE, "libkda.so")
 
-KDA_OK, KDA_EINVAL, KDA_ENOTSUP, KDA_EALIGN, KDA_EHIP = 0, -1, -2, -3, -4
+KDA_OK, KDA_EINVAL, KDA_ENOTSUP, KDA_EALIGN, KDA_EHIP, KDA_EWAIT = 0, -1, -2, -3, -4, -5
 KDA_F32, KDA_BF16 = 0, 1
 GATE_CHANNEL, GATE_SCALAR = 0, 1
 
@@ -24,7 +26,7 @@ STAGE_PREP, STAGE_STATE, STAGE_ALL = 1, 2, 3
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd",
            "kda_chunk_bwd_workspace_bytes", "kda_gauge_fold", "kda_gauge_fold_workspace_bytes", "kda_chunk_fwd_gauge",
            "kda_chunk_fwd_gauge_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error",
-           "kda_version")
+           "kda_version", "kda_chunk_fwd_status")
 
 
 class KDAError(RuntimeError):
@@ -73,6 +75,8 @@ def _lib():
         lib.kda_last_hip_error.argtypes = []
         lib.kda_version.restype = i
         lib.kda_version.argtypes = []
+        lib.kda_chunk_fwd_status.restype = i
+        lib.kda_chunk_fwd_status.argtypes = [ctypes.c_uint32]
         _L = lib
     return _L
 
@@ -113,6 +117,76 @@ def _check_dev(name: str, t: torch.Tensor, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _check_shape(name: str, t: torch.Tensor, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _gate_kind(gate: torch.Tensor, lead: int, gate_kind: Optional[int]) -> int:
+    """Gate kind from the gate's rank (lead = number of leading dims before
+    dk), checked against an explicit gate_kind."""
+    by_rank = {lead + 1: GATE_CHANNEL, lead: GATE_SCALAR}
+    if gate.dim() not in by_rank:
+        raise ValueError("gate has %d dims, expected %d (channel) or %d (scalar)" % (gate.dim(), lead + 1, lead))
+    kind = by_rank[gate.dim()]
+    if gate_kind is not None and int(gate_kind) != kind:
+        raise ValueError("gate of rank %d does not match gate_kind %d" % (gate.dim(), gate_kind))
+    return kind
+
+
+def _check_seq_inputs(q, k, v, gate, beta, gate_kind):
+    """Shapes of a whole-sequence call: q, k [B,T,H,dk], v [B,T,H,dv], gate
+    [B,T,H,dk] or [B,T,H], beta [B,T,H]; one dtype. Returns (B, T, H, dk, dv,
+    gate_kind)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk], got %s" % (tuple(q.shape),))
+    B, T, H, dk = q.shape
+    if v.dim() != 4:
+        raise ValueError("v must be [B,T,H,dv], got %s" % (tuple(v.shape),))
+    dv = v.shape[-1]
+    _check_shape("k", k, (B, T, H, dk))
+    _check_shape("v", v, (B, T, H, dv))
+    gate_kind = _gate_kind(gate, 3, gate_kind)
+    _check_shape("gate", gate, (B, T, H, dk) if gate_kind == GATE_CHANNEL else (B, T, H))
+    _check_shape("beta", beta, (B, T, H))
+    for name, t in (("k", k), ("v", v), ("gate", gate), ("beta", beta)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    return B, T, H, dk, dv, gate_kind
+
+
+def _check_varlen(cu_seqlens, B, device):
+    if cu_seqlens is None:
+        return False, B
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
+    if B != 1:
+        raise ValueError("packed sequences (cu_seqlens) need B = 1, got %d" % B)
+    _check_dev("cu_seqlens", cu_seqlens, device)
+    return True, int(cu_seqlens.numel() - 1)
+
+
+def _check_state(name, t, N, H, dk, dv, device):
+    if t is None:
+        return
+    if t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv):
+        raise ValueError("%s must be fp32 [%d,%d,%d,%d]" % (name, N, H, dk, dv))
+    _check_dev(name, t, device)
+
+
+def status_from_word(word: int) -> int:
+    """KDA_OK or KDA_EWAIT for the status word a forward left in its workspace."""
+    return int(_lib().kda_chunk_fwd_status(ctypes.c_uint32(int(word) & 0xFFFFFFFF)))
+
+
+def fwd_status(workspace: torch.Tensor) -> int:
+    """Read the status word of the last forward that used ``workspace`` (waits
+    for the device) and map it; KDA_OK means every state-pass wait completed."""
+    torch.cuda.synchronize(workspace.device)
+    word = int(workspace[:4].cpu().view(torch.int32).item())
+    return status_from_word(word)
+
+
 def workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int, N: int = 0,
                     varlen: bool = False, dtype: torch.dtype = torch.bfloat16) -> int:
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
@@ -126,43 +200,43 @@ def chunk_fwd(q, k, v, gate, beta, S0=None, cu_seqlens=None, chunk: int = 64, ga
     """Chunkwise forward. q, k [B,T,H,dk]; v [B,T,H,dv]; gate [B,T,H,dk] or
     [B,T,H]; beta [B,T,H]; S0 [N,H,dk,dv] fp32 or None; cu_seqlens int32 [N+1]
     on the device (B must be 1) or None. Returns (o fp32 [B,T,H,dv], S_T)."""
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    B, T, H, dk, dv, gate_kind = _check_seq_inputs(q, k, v, gate, beta, gate_kind)
+    N = B if cu_seqlens is None else int(cu_seqlens.numel() - 1)
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed sequences (cu_seqlens) need B = 1, got %d" % B)
+    if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (N, H, dk, dv)):
+        raise ValueError("S0 must be fp32 [%d,%d,%d,%d]" % (N, H, dk, dv))
     device = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta)):
         _check_dev(name, t, device)
-    if gate_kind is None:
-        gate_kind = GATE_SCALAR if gate.dim() == 3 else GATE_CHANNEL
     dt = _dtype_code(q)
-    for name, t in (("k", k), ("v", v), ("gate", gate), ("beta", beta)):
-        if t.dtype != q.dtype:
-            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
-    varlen = cu_seqlens is not None
-    N = int(cu_seqlens.numel() - 1) if varlen else B
-    if varlen:
-        _check_dev("cu_seqlens", cu_seqlens, device)
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-    if S0 is not None:
-        _check_dev("S0", S0, device)
-        if S0.dtype != torch.float32 or tuple(S0.shape) != (N, H, dk, dv):
-            raise ValueError("S0 must be fp32 [%d,%d,%d,%d]" % (N, H, dk, dv))
+    varlen, N = _check_varlen(cu_seqlens, B, device)
+    _check_state("S0", S0, N, H, dk, dv, device)
     if out is None:
         out = torch.empty((B, T, H, dv), device=device, dtype=torch.float32)
+    else:
+        _check_dev("out", out, device)
+        if out.dtype != torch.float32:
+            raise TypeError("out must be fp32")
+        _check_shape("out", out, (B, T, H, dv))
     if S_T is None and state_out:
         S_T = torch.empty((N, H, dk, dv), device=device, dtype=torch.float32)
+    _check_state("S_T", S_T, N, H, dk, dv, device)
     need = workspace_bytes(B, H, T, dk, dv, chunk, N, varlen, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
     st = _stream_handle(stream, device)
-    rc = _lib().kda_chunk_fwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0), _ptr(out),
-                              _ptr(S_T), B, H, T, dk, dv, chunk, _ptr(cu_seqlens), N if varlen else 0, dt,
-                              int(gate_kind), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                              ctypes.c_void_p(st) if st else None)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_T), B, H, T, dk, dv, chunk,
+            _ptr(cu_seqlens), N if varlen else 0, dt, int(gate_kind), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(st) if st else None)
+    if stage == STAGE_ALL:
+        rc, where = _lib().kda_chunk_fwd(*args), "kda_chunk_fwd"
+    else:
+        rc, where = _lib().kda_chunk_fwd_stage(int(stage), *args), "kda_chunk_fwd_stage"
     if rc != KDA_OK:
-        raise KDAError(rc, "kda_chunk_fwd_stage")
+        raise KDAError(rc, where)
     return out, S_T
 
 
@@ -178,30 +252,22 @@ def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate
     a dict of fp32 tensors dq, dk, dv, dgate, dbeta (input layouts) and dS0
     ([N,H,dk,dv], or None when not wanted). ``out`` may supply that dict's
     tensors to write into."""
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    B, T, H, dk, dv, gate_kind = _check_seq_inputs(q, k, v, gate, beta, gate_kind)
+    if dO.dtype != torch.float32 or tuple(dO.shape) != (B, T, H, dv):
+        raise ValueError("dO must be fp32 [%d,%d,%d,%d]" % (B, T, H, dv))
+    N = B if cu_seqlens is None else int(cu_seqlens.numel() - 1)
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed sequences (cu_seqlens) need B = 1, got %d" % B)
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv)):
+            raise ValueError("%s must be fp32 [%d,%d,%d,%d]" % (name, N, H, dk, dv))
     device = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta), ("dO", dO)):
         _check_dev(name, t, device)
-    if gate_kind is None:
-        gate_kind = GATE_SCALAR if gate.dim() == 3 else GATE_CHANNEL
     dt = _dtype_code(q)
-    for name, t in (("k", k), ("v", v), ("gate", gate), ("beta", beta)):
-        if t.dtype != q.dtype:
-            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
-    if dO.dtype != torch.float32 or tuple(dO.shape) != (B, T, H, dv):
-        raise ValueError("dO must be fp32 [%d,%d,%d,%d]" % (B, T, H, dv))
-    varlen = cu_seqlens is not None
-    N = int(cu_seqlens.numel() - 1) if varlen else B
-    if varlen:
-        _check_dev("cu_seqlens", cu_seqlens, device)
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-    for name, t in (("S0", S0), ("dS_T", dS_T)):
-        if t is not None:
-            _check_dev(name, t, device)
-            if t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv):
-                raise ValueError("%s must be fp32 [%d,%d,%d,%d]" % (name, N, H, dk, dv))
+    varlen, N = _check_varlen(cu_seqlens, B, device)
+    _check_state("S0", S0, N, H, dk, dv, device)
+    _check_state("dS_T", dS_T, N, H, dk, dv, device)
     f32 = dict(device=device, dtype=torch.float32)
     if out is None:
         out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
@@ -227,15 +293,20 @@ def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate
 def gauge_fold(q, k, gate, cu_seqlens=None, gate_kind: Optional[int] = None, stream=None):
     """Gauge fold: returns (q~, k~, gate~, c_T) with c_T int8 [N,H,dk] or
     [N,H]. Inputs as for chunk_fwd."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk], got %s" % (tuple(q.shape),))
     B, T, H, dk = q.shape
+    _check_shape("k", k, (B, T, H, dk))
+    gate_kind = _gate_kind(gate, 3, gate_kind)
+    _check_shape("gate", gate, (B, T, H, dk) if gate_kind == GATE_CHANNEL else (B, T, H))
+    for name, t in (("k", k), ("gate", gate)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
     device = q.device
     for name, t in (("q", q), ("k", k), ("gate", gate)):
         _check_dev(name, t, device)
-    if gate_kind is None:
-        gate_kind = GATE_SCALAR if gate.dim() == 3 else GATE_CHANNEL
     dt = _dtype_code(q)
-    varlen = cu_seqlens is not None
-    N = int(cu_seqlens.numel() - 1) if varlen else B
+    varlen, N = _check_varlen(cu_seqlens, B, device)
     qo, ko, go = torch.empty_like(q), torch.empty_like(k), torch.empty_like(gate)
     sign = torch.empty((N, H, dk) if gate_kind == GATE_CHANNEL else (N, H), device=device, dtype=torch.int8)
     need = int(_lib().kda_gauge_fold_workspace_bytes(B, H, T, dk, N, int(varlen), int(gate_kind)))
@@ -261,23 +332,31 @@ def chunk_fwd_gauge(q, k, v, gate, beta, S0=None, cu_seqlens=None, chunk: int = 
                     workspace: Optional[torch.Tensor] = None, stream=None):
     """chunk_fwd through the gauge transform (kda_chunk_fwd_gauge). Same
     arguments and results as chunk_fwd."""
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    B, T, H, dk, dv, gate_kind = _check_seq_inputs(q, k, v, gate, beta, gate_kind)
+    N = B if cu_seqlens is None else int(cu_seqlens.numel() - 1)
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed sequences (cu_seqlens) need B = 1, got %d" % B)
+    if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (N, H, dk, dv)):
+        raise ValueError("S0 must be fp32 [%d,%d,%d,%d]" % (N, H, dk, dv))
     device = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta)):
         _check_dev(name, t, device)
-    if gate_kind is None:
-        gate_kind = GATE_SCALAR if gate.dim() == 3 else GATE_CHANNEL
     dt = _dtype_code(q)
-    varlen = cu_seqlens is not None
-    N = int(cu_seqlens.numel() - 1) if varlen else B
+    varlen, N = _check_varlen(cu_seqlens, B, device)
+    _check_state("S0", S0, N, H, dk, dv, device)
     if out is None:
         out = torch.empty((B, T, H, dv), device=device, dtype=torch.float32)
+    else:
+        _check_dev("out", out, device)
+        _check_shape("out", out, (B, T, H, dv))
     if S_T is None:
         S_T = torch.empty((N, H, dk, dv), device=device, dtype=torch.float32)
+    _check_state("S_T", S_T, N, H, dk, dv, device)
     need = fwd_gauge_workspace_bytes(B, H, T, dk, dv, chunk, N, varlen, q.dtype, gate_kind)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
     st = _stream_handle(stream, device)
     rc = _lib().kda_chunk_fwd_gauge(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_T),
                                     B, H, T, dk, dv, chunk, _ptr(cu_seqlens), N if varlen else 0, dt, int(gate_kind),
@@ -291,18 +370,29 @@ def decode_step(q, k, v, gate, beta, S, out: Optional[torch.Tensor] = None, gate
                 stream=None) -> torch.Tensor:
     """One decode step, S [N,H,dk,dv] fp32 updated in place. q, k [N,H,dk];
     v [N,H,dv]; gate [N,H,dk] or [N,H]; beta [N,H]. Returns o fp32 [N,H,dv]."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [N,H,dk] and v [N,H,dv]")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _check_shape("k", k, (N, H, dk))
+    _check_shape("v", v, (N, H, dv))
+    gate_kind = _gate_kind(gate, 2, gate_kind)
+    _check_shape("gate", gate, (N, H, dk) if gate_kind == GATE_CHANNEL else (N, H))
+    _check_shape("beta", beta, (N, H))
+    for name, t in (("k", k), ("v", v), ("gate", gate), ("beta", beta)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError("S must be fp32 [%d,%d,%d,%d]" % (N, H, dk, dv))
     device = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta), ("S", S)):
         _check_dev(name, t, device)
-    if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
-        raise ValueError("S must be fp32 [%d,%d,%d,%d]" % (N, H, dk, dv))
-    if gate_kind is None:
-        gate_kind = GATE_SCALAR if gate.dim() == 2 else GATE_CHANNEL
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty((N, H, dv), device=device, dtype=torch.float32)
+    else:
+        _check_dev("out", out, device)
+        _check_shape("out", out, (N, H, dv))
     st = _stream_handle(stream, device)
     rc = _lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S), _ptr(out),
                                 N, H, dk, dv, dt, int(gate_kind), ctypes.c_void_p(st) if st else None)

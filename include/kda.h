@@ -31,9 +31,13 @@
  *    validation fails. Device-side contents (cu_seqlens offsets, NaN/Inf in
  *    inputs) are not checked: NaN/Inf propagate.
  *  - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}.
- *  - Calls are re-entrant; the library keeps no mutable global state. Two
- *    calls may run concurrently on different streams if they do not share
- *    output or workspace buffers.
+ *  - The library never allocates, frees or synchronises device memory in a
+ *    compute call: every call that needs scratch space takes a caller-owned
+ *    workspace, and a NULL workspace (or a short one) is KDA_EINVAL.
+ *  - Calls are re-entrant and keep no state between calls (the compute-unit
+ *    count that picks a state walker is queried from the runtime on each
+ *    call). Two calls may run concurrently on different streams if they do
+ *    not share output or workspace buffers.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -51,6 +55,7 @@ extern "C" {
 #define KDA_ENOTSUP (-2) /* dk, dv, chunk, dtype or gate_kind outside the supported set */
 #define KDA_EALIGN (-3)  /* a pointer violates the alignment rules above */
 #define KDA_EHIP (-4)    /* a HIP call failed; see kda_last_hip_error() */
+#define KDA_EWAIT (-5)   /* from kda_chunk_fwd_status: a bounded wait in the state pass expired */
 
 /* dtype */
 #define KDA_F32 0
@@ -92,9 +97,14 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
  * agree across chunk sizes up to rounding. T need not be a multiple of it.
  *
  * workspace: device memory of at least kda_chunk_fwd_workspace_bytes(...)
- * bytes, owned by the caller and not read before it is written. If workspace
- * is NULL the library takes it stream-ordered from the device's default memory
- * pool (hipMallocAsync) and returns it the same way (hipFreeAsync).
+ * bytes, owned by the caller and not read before it is written (required:
+ * NULL or too small is KDA_EINVAL). Its first 4 bytes receive the call's
+ * status word once the call's kernels have run: 0 when every bounded wait in
+ * the state pass completed. The state pass's waves trade operands through LDS
+ * with bounded waits that cannot expire while all waves of a workgroup run;
+ * if one ever did, that wave stores neither o nor S_T and sets the status
+ * word. The caller may read the word after synchronising with `stream` and
+ * map it with kda_chunk_fwd_status().
  *
  * Returns KDA_OK or a negative status.
  */
@@ -102,6 +112,13 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate,
                   const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
                   const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * Maps the status word a forward left in the first 4 bytes of its workspace
+ * (read by the caller after the call completed) to KDA_OK (0) or KDA_EWAIT.
+ * Host-only; touches no device.
+ */
+int kda_chunk_fwd_status(uint32_t status_word);
 
 /* stage for kda_chunk_fwd_stage */
 #define KDA_STAGE_PREP 1  /* in-chunk work: gate products, gated Gram, UT inverse -> workspace */
@@ -112,9 +129,9 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate,
  * kda_chunk_fwd split into its two launches, for callers that schedule or
  * time them separately. Arguments as for kda_chunk_fwd. KDA_STAGE_STATE
  * consumes a workspace that a KDA_STAGE_PREP call with identical arguments
- * filled earlier on the same stream (or with ordering the caller provides);
- * both partial stages require a caller-provided workspace (KDA_EINVAL when it
- * is NULL). KDA_STAGE_PREP writes neither o nor S_T.
+ * filled earlier on the same stream (or with ordering the caller provides).
+ * KDA_STAGE_PREP writes neither o nor S_T and clears the status word;
+ * KDA_STAGE_STATE only ever sets it.
  */
 int kda_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const void* gate,
                         const void* beta, const float* S0, float* o, float* S_T, int B, int H, int T, int dk,
@@ -166,8 +183,8 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int N,
  *
  * workspace: at least kda_chunk_bwd_workspace_bytes(...) bytes (state
  * checkpoints every 8 tokens, 4 * dk * dv bytes each per (sequence, head),
- * the per-token residual v - S'^T k, plus per-workgroup partial sums), or NULL to take it stream-ordered from
- * the device's default memory pool.
+ * the per-token residual v - S'^T k, plus per-workgroup partial sums);
+ * required (NULL is KDA_EINVAL).
  *
  * Returns KDA_OK or a negative status.
  */
@@ -192,7 +209,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
  * alias the inputs. q, k, their outputs and (channel gate) gate and gate_out
  * must be 16-byte aligned. sign_T: device int8 [N, H, dk] (channel gate) or [N, H]
  * (scalar gate) receiving c_T (+1 / -1), or NULL. workspace: at least
- * kda_gauge_fold_workspace_bytes(...) bytes, or NULL (stream-ordered pool).
+ * kda_gauge_fold_workspace_bytes(...) bytes (required).
  * Returns KDA_OK or a negative status.
  */
 size_t kda_gauge_fold_workspace_bytes(int B, int H, int T, int dk, int N, int has_cu_seqlens, int gate_kind);
@@ -204,9 +221,10 @@ int kda_gauge_fold(const void* q, const void* k, const void* gate, void* q_out, 
  * kda_chunk_fwd computed through the gauge transform: kda_gauge_fold into
  * the workspace, the chunkwise forward on the folded (positive-gate)
  * inputs, then S_T's rows multiplied by c_T. Same arguments, results and
- * tolerances as kda_chunk_fwd; the workspace is
- * kda_chunk_fwd_gauge_workspace_bytes(...) bytes (the folded q, k and gate
- * plus the forward's own workspace), or NULL.
+ * tolerances as kda_chunk_fwd; the workspace (required) is
+ * kda_chunk_fwd_gauge_workspace_bytes(...) bytes: the forward's own
+ * workspace first (so its status word is again the first 4 bytes), then the
+ * folded q, k and gate and the fold's scratch.
  */
 size_t kda_chunk_fwd_gauge_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int N,
                                            int has_cu_seqlens, int dtype, int gate_kind);

@@ -10,6 +10,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "sanitize: host code rebuilt with AddressSanitizer/UBSan (CPU only)")
 
 
 @pytest.fixture(scope="session", autouse=True)

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert lib.kda_version() == 100
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert kda.strerror(code)
     assert kda.strerror(-99) == "unknown status"
     assert lib.kda_last_hip_error() == 0
@@ -92,7 +92,9 @@ def test_workspace_bytes(lib):
     assert f(1, 2, 64, 24, 16, 16) == 0
     a = f(1, 2, 64, 16, 16, 16)
     assert a > 0 and a % 256 == 0
-    assert f(2, 2, 64, 16, 16, 16) == 2 * a
+    hdr = f(1, 2, 0, 16, 16, 16)                                     # status header only
+    assert hdr == 256
+    assert f(2, 2, 64, 16, 16, 16) - hdr == 2 * (a - hdr)
     assert f(1, 2, 65, 16, 16, 16) > a                                # ragged tail adds a chunk
     assert f(1, 16, 8192, 128, 128, 64) > f(1, 16, 8192, 128, 128, 64, dtype=None) * 0  # defined
     v = f(1, 2, 100, 16, 16, 16, N=5, varlen=True)
@@ -156,3 +158,94 @@ def test_gauge_validation(lib):
     assert route(q=FAKE + 2) == kda.KDA_EALIGN
     assert route(wsb=1) == kda.KDA_EINVAL
     assert kda.fwd_gauge_workspace_bytes(1, 2, 64, 16, 16, 16) > kda.workspace_bytes(1, 2, 64, 16, 16, 16)
+
+
+def test_null_workspace_rejected(lib):
+    """The library never allocates: a NULL workspace is an argument error for
+    every call that needs scratch space, caught before any HIP call."""
+    assert chunk(lib, ws=None, wsb=0) == kda.KDA_EINVAL
+    assert chunk(lib, ws=None, wsb=1 << 30) == kda.KDA_EINVAL
+    assert chunk(lib, ws=None, T=0, S_T=FAKE) == kda.KDA_EINVAL
+    assert lib.kda_chunk_bwd(*([FAKE] * 5 + [None, FAKE, None] + [FAKE] * 5 + [None, 1, 2, 8, 16, 16, None, 0,
+                                                                                  kda.KDA_BF16, 0, None, 0, None])) \
+        == kda.KDA_EINVAL
+    assert lib.kda_gauge_fold(*([FAKE] * 6 + [None, 1, 2, 8, 16, None, 0, kda.KDA_BF16, 0, None, 0, None])) \
+        == kda.KDA_EINVAL
+    assert lib.kda_chunk_fwd_gauge(*([FAKE] * 5 + [None, FAKE, None, 1, 2, 8, 16, 16, 16, None, 0, kda.KDA_BF16, 0,
+                                                   None, 0, None])) == kda.KDA_EINVAL
+
+
+def test_status_word_mapping(lib):
+    """The forward's status word (first 4 bytes of its workspace) maps to
+    KDA_OK when zero and to KDA_EWAIT when a state-pass wait expired."""
+    assert lib.kda_chunk_fwd_status(0) == kda.KDA_OK
+    assert kda.status_from_word(0) == kda.KDA_OK
+    for word in (1, 3, 0x80000001, 0xFFFFFFFF):
+        assert kda.status_from_word(word) == kda.KDA_EWAIT
+    assert "wait" in kda.strerror(kda.KDA_EWAIT)
+
+
+def _cpu_inputs(B=1, T=8, H=2, dk=16, dv=16, scalar=False):
+    import torch
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)  # noqa: E731
+    return dict(q=z(B, T, H, dk), k=z(B, T, H, dk), v=z(B, T, H, dv),
+                gate=z(B, T, H) if scalar else z(B, T, H, dk), beta=z(B, T, H))
+
+
+def test_binding_rejects_mismatched_shapes(lib):
+    """The Python binding checks every tensor's full shape (and the gate's
+    rank against gate_kind) before it touches a device: a short v, a wrong
+    gate rank or a mismatched S0 would otherwise let a kernel read past an
+    allocation."""
+    import torch
+    base = _cpu_inputs()
+    bad = [
+        dict(k=torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16)),
+        dict(v=torch.zeros(1, 7, 2, 16, dtype=torch.bfloat16)),
+        dict(gate=torch.zeros(1, 8, 2, 8, dtype=torch.bfloat16)),
+        dict(gate=torch.zeros(1, 8, 2, 16, 1, dtype=torch.bfloat16)),
+        dict(beta=torch.zeros(1, 8, 3, dtype=torch.bfloat16)),
+        dict(beta=torch.zeros(1, 8, 2, 1, dtype=torch.bfloat16)),
+    ]
+    for change in bad:
+        a = dict(base, **change)
+        with pytest.raises(ValueError):
+            kda.chunk_fwd(**a)
+        with pytest.raises(ValueError):
+            kda.chunk_fwd_gauge(**a)
+        with pytest.raises(ValueError):
+            kda.chunk_bwd(**a, dO=torch.zeros(1, 8, 2, 16))
+    # scalar gate passed with the channel kind, channel gate with the scalar kind
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(**_cpu_inputs(scalar=True), gate_kind=kda.GATE_CHANNEL)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(**base, gate_kind=kda.GATE_SCALAR)
+    with pytest.raises(ValueError):
+        kda.gauge_fold(base["q"], base["k"], base["gate"], gate_kind=kda.GATE_SCALAR)
+    with pytest.raises(ValueError):
+        kda.gauge_fold(base["q"], base["k"][:, :4].contiguous(), base["gate"])
+    # states
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(**base, S0=torch.zeros(1, 2, 16, 8))
+    with pytest.raises(ValueError):
+        kda.chunk_fwd_gauge(**base, S0=torch.zeros(2, 2, 16, 16))
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(**base, S0=torch.zeros(1, 2, 16, 16, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        kda.chunk_bwd(**base, dO=torch.zeros(1, 8, 2, 8))
+    with pytest.raises(ValueError):
+        kda.chunk_bwd(**base, dO=torch.zeros(1, 8, 2, 16), dS_T=torch.zeros(1, 2, 8, 16))
+    # varlen needs B = 1
+    b2 = _cpu_inputs(B=2)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(**b2, cu_seqlens=torch.tensor([0, 4, 8], dtype=torch.int32))
+    # decode
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)  # noqa: E731
+    S = torch.zeros(3, 2, 16, 16)
+    dec = dict(q=z(3, 2, 16), k=z(3, 2, 16), v=z(3, 2, 16), gate=z(3, 2, 16), beta=z(3, 2), S=S)
+    for change in (dict(k=z(3, 2, 32)), dict(v=z(2, 2, 16)), dict(gate=z(3, 2, 8)), dict(beta=z(3, 1)),
+                   dict(S=torch.zeros(3, 2, 16, 32)), dict(gate=z(3, 2, 16, 1))):
+        with pytest.raises(ValueError):
+            kda.decode_step(**dict(dec, **change))
+    with pytest.raises(ValueError):
+        kda.decode_step(**dict(dec, gate=z(3, 2)), gate_kind=kda.GATE_CHANNEL)

@@ -39,22 +39,33 @@ def bits(t):
 
 
 FOLD_CASES = [
-    ("ckda", torch.bfloat16, 128, 700, None),
-    ("ckda", torch.float32, 64, 300, None),
-    ("gdn", torch.bfloat16, 32, 513, None),
-    ("ckda", torch.bfloat16, 16, 0, [260, 0, 1, 255, 40]),
+    ("ckda", torch.bfloat16, 128, 700, None, False),
+    ("ckda", torch.float32, 64, 300, None, False),
+    ("gdn", torch.bfloat16, 32, 513, None, False),
+    ("ckda", torch.bfloat16, 16, 0, [260, 0, 1, 255, 40], False),
+    # -0.0, +0.0 and -1.0 gates mixed in: -0.0 counts as positive (no sign
+    # flip), its folded gate is +0.0, and c_T matches bit for bit
+    ("ckda", torch.bfloat16, 128, 400, None, True),
+    ("ckda", torch.float32, 32, 0, [100, 1, 0, 77], True),
+    ("gdn", torch.bfloat16, 64, 333, None, True),
+    ("gdn", torch.float32, 16, 129, None, True),
 ]
 
 
-@pytest.mark.parametrize("gate,dtype,dk,T,lengths", FOLD_CASES)
-def test_fold_bit_exact(kda, gate, dtype, dk, T, lengths):
+@pytest.mark.parametrize("gate,dtype,dk,T,lengths,szero", FOLD_CASES)
+def test_fold_bit_exact(kda, gate, dtype, dk, T, lengths, szero):
     w = inputs.make_forward("fold", B=1 if lengths else 2, H=3, T=T, dk=dk, dv=16, dtype=dtype, gate=gate,
                             lengths=lengths, seed=T + dk)
     if gate == "gdn":   # make the scalar gates signed: flip every third token's sign
         g = w.gate.clone()
         g[:, ::3] = -g[:, ::3]
         w.gate = g
-    print("case", gate, dtype, "dk", dk, "T", w.T, "lengths", lengths, flush=True)
+    if szero:
+        w.gate = inputs.signed_zero_gates(w.gate, seed=T, frac=0.06 if gate == "ckda" else 0.3)
+        negz = (w.gate.view(torch.int16 if dtype == torch.bfloat16 else torch.int32) ==
+                (-32768 if dtype == torch.bfloat16 else -2 ** 31))
+        assert int(negz.sum()) > 0
+    print("case", gate, dtype, "dk", dk, "T", w.T, "lengths", lengths, "signed zeros", szero, flush=True)
     d = lambda t: None if t is None else t.cuda()  # noqa: E731
     qo, ko, go, sign = kda.gauge_fold(d(w.q), d(w.k), d(w.gate), cu_seqlens=d(w.cu_seqlens), gate_kind=w.gate_kind)
     torch.cuda.synchronize()
@@ -63,6 +74,8 @@ def test_fold_bit_exact(kda, gate, dtype, dk, T, lengths):
     np.testing.assert_array_equal(bits(ko), bits(rk))
     np.testing.assert_array_equal(bits(go), bits(rg))
     np.testing.assert_array_equal(sign.cpu().numpy().reshape(rc.shape), rc)
+    if szero:   # every folded gate is non-negative, -0.0 included (it becomes +0.0)
+        assert not bool(torch.signbit(go.cpu()).any())
 
 
 ROUTE_CASES = [
@@ -101,16 +114,17 @@ def test_gauge_route_varlen_scalar(kda):
     assert err(o, ro) <= 1e-4 and err(ST, rS) <= 1e-4
 
 
-def test_gauge_route_full_size_sampled_heads(kda):
-    """The Complex KDA workload through the gauge route; the oracle runs heads
-    2 and 11 directly over all 8192 tokens."""
+def test_gauge_route_full_size_every_head(kda):
+    """The Complex KDA workload (with -0.0 gates mixed in) through the gauge
+    route; the oracle runs every (sequence, head) pair directly over all 8192
+    tokens, and each head is checked on its own."""
     w = inputs.ckda_fwd(seed=0)
+    w.gate = inputs.signed_zero_gates(w.gate, seed=5, frac=0.015)
     d = lambda t: t.cuda()  # noqa: E731
     o, ST = kda.chunk_fwd_gauge(d(w.q), d(w.k), d(w.v), d(w.gate), d(w.beta), chunk=64)
     torch.cuda.synchronize()
-    heads = [2, 11]
-    ro, rS = oracle.fwd_heads(w.q, w.k, w.v, w.gate, w.beta, heads)
-    eo = err(o[:, :, heads], ro)
-    eS = err(ST[:, heads], rS)
-    print("  full size err o %.2e S %.2e" % (eo, eS), flush=True)
-    assert eo <= 2e-2 and eS <= 2e-2
+    ro, rS = oracle.fwd(w.q, w.k, w.v, w.gate, w.beta)
+    eo, eS = err(o, ro), err(ST, rS)
+    worst = max(max(err(o[:, :, h], ro[:, :, h]), err(ST[:, h], rS[:, h])) for h in range(w.H))
+    print("  full size err o %.2e S %.2e worst head %.2e" % (eo, eS, worst), flush=True)
+    assert eo <= 2e-2 and eS <= 2e-2 and worst <= 2e-2
