@@ -69,6 +69,7 @@ const char* kda_strerror(int status) {
         case KDA_EALIGN: return "pointer misaligned for its element type, or a 16-byte-aligned buffer is not";
         case KDA_EHIP: return "HIP runtime error";
         case KDA_EWAIT: return "a bounded wait in the forward's state pass expired; o and S_T were not written";
+        case KDA_ESCRATCH: return "the call needs more scratch than the library's fixed array (KDA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

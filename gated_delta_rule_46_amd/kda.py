@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # host-side validation code loads that way); default: the in-tree libkda.so.
 LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(_HERE, "libkda.so")
 
-KDA_OK, KDA_EINVAL, KDA_ENOTSUP, KDA_EALIGN, KDA_EHIP, KDA_EWAIT = 0, -1, -2, -3, -4, -5
+KDA_OK, KDA_EINVAL, KDA_ENOTSUP, KDA_EALIGN, KDA_EHIP, KDA_EWAIT, KDA_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 128 << 20
 KDA_F32, KDA_BF16 = 0, 1
 GATE_CHANNEL, GATE_SCALAR = 0, 1
 
@@ -26,7 +27,7 @@ STAGE_PREP, STAGE_STATE, STAGE_ALL = 1, 2, 3
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd",
            "kda_chunk_bwd_workspace_bytes", "kda_gauge_fold", "kda_gauge_fold_workspace_bytes", "kda_chunk_fwd_gauge",
            "kda_chunk_fwd_gauge_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error",
-           "kda_version", "kda_chunk_fwd_status")
+           "kda_version", "kda_chunk_fwd_status", "kda_chunk_fwd_noalloc")
 
 
 class KDAError(RuntimeError):
@@ -77,6 +78,8 @@ def _lib():
         lib.kda_version.argtypes = []
         lib.kda_chunk_fwd_status.restype = i
         lib.kda_chunk_fwd_status.argtypes = [ctypes.c_uint32]
+        lib.kda_chunk_fwd_noalloc.restype = i
+        lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp]
         _L = lib
     return _L
 

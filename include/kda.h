@@ -56,6 +56,7 @@ extern "C" {
 #define KDA_EALIGN (-3)  /* a pointer violates the alignment rules above */
 #define KDA_EHIP (-4)    /* a HIP call failed; see kda_last_hip_error() */
 #define KDA_EWAIT (-5)   /* from kda_chunk_fwd_status: a bounded wait in the state pass expired */
+#define KDA_ESCRATCH (-6) /* kda_chunk_fwd_noalloc: the call needs more than KDA_NOALLOC_SCRATCH_BYTES */
 
 /* dtype */
 #define KDA_F32 0
@@ -112,6 +113,26 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate,
                   const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
                   const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory (work recorded
+ * under graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results minus the workspace, which here
+ * is a fixed device array of KDA_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held until the process ends. A call whose workspace would
+ * exceed it (kda_chunk_fwd_workspace_bytes(...) > KDA_NOALLOC_SCRATCH_BYTES;
+ * about 1,770 (chunk, head) blocks at dk = dv = 128, chunk 64, e.g. H = 16
+ * and T = 7,000) returns KDA_ESCRATCH before any HIP call. The call allocates
+ * nothing; the first call with a device current looks up the array's address
+ * on that device. All calls on one GPU share the array, which keeps the last
+ * call's contents (its status word included): calls that overlap on one GPU
+ * (concurrent streams, or host threads) race and must be ordered by the
+ * caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                          const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv, int chunk,
+                          const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* stream);
 
 /*
  * Maps the status word a forward left in the first 4 bytes of its workspace

@@ -67,7 +67,7 @@ def test_oracle_under_sanitizers(sandir):
 
 def test_abi_validation_under_sanitizers(sandir):
     objs = [os.path.join(ROOT, "gated_delta_rule_46_amd", "_build", f + ".o")
-            for f in ("kda_decode", "kda_chunk", "kda_bwd", "kda_gauge")]
+            for f in ("kda_decode", "kda_chunk", "kda_bwd", "kda_gauge", "kda_noalloc")]
     if not all(os.path.exists(o) for o in objs):
         from gated_delta_rule_46_amd import build
         build.build()
