@@ -111,6 +111,45 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* gate,
                                N, dtype, gate_kind, workspace, workspace_bytes, stream);
 }
 
+int kda_chunk_fwd_ew(const void* q, const void* k, const void* v, const void* gate, const void* erase,
+                     const void* write, const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv,
+                     int chunk, const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    kda::ChunkArgs a;
+    size_t need = 0;
+    // erase stands in for beta in the shared checks (beta is not an input of this form)
+    const int st = kda::validate_chunk_fwd(KDA_STAGE_ALL, q, k, v, gate, erase, S0, o, S_T, B, H, T, dk, dv, chunk,
+                                           cu_seqlens, N, dtype, gate_kind, stream, &a, &need);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!erase || !write)) return KDA_EINVAL;
+    if (T > 0 && (!aligned(erase) || !aligned(write))) return KDA_EALIGN;
+    if (workspace && !aligned(workspace)) return KDA_EALIGN;
+    if (!workspace || workspace_bytes < need) return KDA_EINVAL;
+    if (T == 0 && !S_T) return KDA_OK;
+    a.beta = nullptr;
+    a.erase = erase;
+    a.write = write;
+    a.workspace = workspace;
+    return hip_status(kda::launch_chunk_fwd(a));
+}
+
+int kda_decode_step_ew(const void* q, const void* k, const void* v, const void* gate, const void* erase,
+                       const void* write, float* S, float* o, int N, int H, int dk, int dv, int dtype, int gate_kind,
+                       void* stream) {
+    if (N <= 0 || H <= 0) return KDA_EINVAL;
+    if (!size_ok(dk) || !size_ok(dv)) return KDA_ENOTSUP;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ENOTSUP;
+    if (gate_kind != KDA_GATE_CHANNEL && gate_kind != KDA_GATE_SCALAR) return KDA_ENOTSUP;
+    if (!q || !k || !v || !gate || !erase || !write || !S || !o) return KDA_EINVAL;
+    const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(gate, es) || !aligned(erase, es) ||
+        !aligned(write, es) || !aligned(S) || !aligned(o))
+        return KDA_EALIGN;
+    kda::DecodeArgs a{q, k, v, gate, nullptr, S, o, N, H, dk, dv, dtype == KDA_BF16,
+                      gate_kind == KDA_GATE_SCALAR, reinterpret_cast<hipStream_t>(stream), erase, write};
+    return hip_status(kda::launch_decode(a));
+}
+
 size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int N, int has_cu) {
     if (B <= 0 || H <= 0 || T < 0 || !size_ok(dk) || !size_ok(dv)) return 0;
     if (has_cu && (B != 1 || N <= 0)) return 0;

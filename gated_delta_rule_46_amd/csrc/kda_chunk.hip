@@ -339,7 +339,7 @@ __host__ __device__ constexpr int tf_index(int rb, int s) {
     return n + s;
 }
 
-template <class TIn, int DK, int C, bool F32M>
+template <class TIn, int DK, int C, bool F32M, bool EW = false>
 struct PrepLds {
     using TM = typename Lay<DK, C, F32M>::TM;
     static constexpr int NBK = C / 16, KSD = (DK + 31) / 32, KSC = (C + 31) / 32, CB = DK / 16;
@@ -356,7 +356,7 @@ struct PrepLds {
     // staged value rows (value width up to 128)
     static constexpr size_t VST = RGN;
     static constexpr size_t WST = VST + ((size_t)C * 128 * sizeof(TIn) + 1023) / 1024 * 1024;   // write gates
-    static constexpr size_t END_V = WST + ((size_t)C * 128 * sizeof(TIn) + 1023) / 1024 * 1024;
+    static constexpr size_t END_V = WST + (EW ? ((size_t)C * 128 * sizeof(TIn) + 1023) / 1024 * 1024 : 0);
     // Gamma o Q and K_end^T tiles
     static constexpr size_t QGT = RGN;
     static constexpr size_t KET = QGT + (size_t)NBK * KSD * TILE;
@@ -405,7 +405,7 @@ __device__ __forceinline__ bool sep_at(int r, int j, int hh) {
 template <class TIn, int DK, int C, bool SG, bool F32M, bool EW>
 __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     using L = Lay<DK, C, F32M>;
-    using SM = PrepLds<TIn, DK, C, F32M>;
+    using SM = PrepLds<TIn, DK, C, F32M, EW>;
     using TM = typename L::TM;
     using F = typename FragOf<TM>::type;
     constexpr int RB = L::RB, CB = L::CB, KSD = L::KSD, KSC = L::KSC;
@@ -2369,7 +2369,7 @@ static hipError_t allow_lds(K kern, size_t bytes) {
 template <class TIn, int DK, int C, bool SG, bool EW>
 static hipError_t launch_prep_t(const ChunkArgs& a, const ChunkMap& map, unsigned char* blocks, long nchunks) {
     constexpr bool F32M = std::is_same<TIn, float>::value;
-    using SM = PrepLds<TIn, DK, C, F32M>;
+    using SM = PrepLds<TIn, DK, C, F32M, EW>;
     static_assert(SM::BYTES <= 160 * 1024, "prep LDS");
     auto kern = chunk_prep_kernel<TIn, DK, C, SG, F32M, EW>;
     hipError_t e = allow_lds(kern, SM::BYTES);

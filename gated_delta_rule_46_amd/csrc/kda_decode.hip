@@ -7,6 +7,10 @@
 //   u    = beta (v - pred)
 //   S    = S' + k u^T                          (delta form, CyFA blog post 2.2)
 //   o    = S^T q = y + (k . q) u               (readout after the update)
+// With decoupled erase and write gates (Gated DeltaNet-2 blurb; erase e per
+// key channel, write w per value channel) the same kernel reads the state
+// with the key e o k and writes w o v:
+//   pred = S'^T (e o k),  u = w o v - pred,  S = S' + k u^T,  o = y + (k . q) u.
 // The state is streamed once in and once out with 128-bit accesses; the step
 // is bound by HBM bandwidth (about 0.87 flop per byte at dk = dv = 128).
 // 512 threads per (sequence, head), plain loads and nontemporal stores:
@@ -17,11 +21,11 @@
 
 namespace kda {
 
-template <class TIn, int DK, int DV, bool SCALAR_GATE>
+template <class TIn, int DK, int DV, bool SCALAR_GATE, bool EW>
 __global__ void __launch_bounds__(512)
 decode_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-                   const TIn* __restrict__ gate, const TIn* __restrict__ beta,
-                   float* __restrict__ S, float* __restrict__ o, int NH) {
+                   const TIn* __restrict__ gate, const TIn* __restrict__ beta, const TIn* __restrict__ erase,
+                   const TIn* __restrict__ write, float* __restrict__ S, float* __restrict__ o, int NH) {
     constexpr int CG = DV / 4;                                   // float4 columns per row
     constexpr int NT = (DK * DV / 4) < 512 ? (DK * DV / 4) : 512;
     constexpr int RG = NT / CG;                                  // row groups
@@ -30,6 +34,7 @@ decode_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     static_assert(NT % WAVE == 0 && DK % RG == 0, "decode tiling");
 
     __shared__ float s_a[DK], s_k[DK], s_q[DK], s_v[DV];
+    __shared__ float s_ke[EW ? DK : 1];   // read key e o k (erase/write form)
     __shared__ float s_red[NW][2][DV];
     __shared__ float s_kq[NW];
 
@@ -46,9 +51,10 @@ decode_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
         s_k[t] = kv;
         s_q[t] = qv;
         s_a[t] = SCALAR_GATE ? ld_in(gate + pair) : ld_in(gate + kb + t);
+        if constexpr (EW) s_ke[t] = ld_in(erase + kb + t) * kv;
         kq_part = kv * qv;
     }
-    if (t < DV) s_v[t] = ld_in(v + vb + t);
+    if (t < DV) s_v[t] = EW ? ld_in(write + vb + t) * ld_in(v + vb + t) : ld_in(v + vb + t);
     kq_part = wave_sum(kq_part);
     if (lane == 0) s_kq[w] = kq_part;
 
@@ -62,7 +68,7 @@ decode_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int r = rg + RG * m;
-        const float a = s_a[r], kr = s_k[r], qr = s_q[r];
+        const float a = s_a[r], kr = EW ? s_ke[r] : s_k[r], qr = s_q[r];
         sv[m] *= a;
         pr += sv[m] * kr;
         yy += sv[m] * qr;
@@ -87,14 +93,14 @@ decode_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     float kqs = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) kqs += s_kq[ww];
-    const float bt = ld_in(beta + pair);
+    const float bt = EW ? 1.f : ld_in(beta + pair);
     float u[4], yv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float p = 0.f, y = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) { p += s_red[ww][0][4 * cg + j]; y += s_red[ww][1][4 * cg + j]; }
-        u[j] = bt * (s_v[4 * cg + j] - p);
+        u[j] = EW ? s_v[4 * cg + j] - p : bt * (s_v[4 * cg + j] - p);
         yv[j] = y;
     }
 #pragma unroll
@@ -117,9 +123,15 @@ template <class TIn, int DK, int DV, bool SG>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     constexpr int NT = (DK * DV / 4) < 512 ? (DK * DV / 4) : 512;
     const int NH = a.N * a.H;
-    hipLaunchKernelGGL((decode_step_kernel<TIn, DK, DV, SG>), dim3(NH), dim3(NT), 0, a.stream,
-                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.gate,
-                       (const TIn*)a.beta, a.S, a.o, NH);
+    if (a.erase) {
+        hipLaunchKernelGGL((decode_step_kernel<TIn, DK, DV, SG, true>), dim3(NH), dim3(NT), 0, a.stream,
+                           (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.gate, (const TIn*)nullptr,
+                           (const TIn*)a.erase, (const TIn*)a.write, a.S, a.o, NH);
+    } else {
+        hipLaunchKernelGGL((decode_step_kernel<TIn, DK, DV, SG, false>), dim3(NH), dim3(NT), 0, a.stream,
+                           (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.gate,
+                           (const TIn*)a.beta, (const TIn*)nullptr, (const TIn*)nullptr, a.S, a.o, NH);
+    }
     return hipGetLastError();
 }
 

@@ -162,6 +162,46 @@ def make_forward(name: str, *, B: int, H: int, T: int, dk: int, dv: int, chunk: 
                     _round(beta, dtype), S0, cu, B, H, T, dk, dv, chunk, gate_kind)
 
 
+@dataclasses.dataclass
+class EraseWriteWorkload:
+    """Forward inputs with decoupled erase [B,T,H,dk] and write [B,T,H,dv]
+    gates in place of beta."""
+    w: Workload
+    erase: torch.Tensor
+    write: torch.Tensor
+
+
+def erase_write_gates(w: Workload, seed: int, erase: str = "bimodal"):
+    """Erase and write gates for workload ``w`` (a generator of their own,
+    seeded with seed + 15485863): erase e = 2 sigmoid(b) per (token, head,
+    key channel) with b a 50/50 mixture of N(+2, 1) and N(-2, 1) ("bimodal",
+    the Complex KDA beta recipe applied per channel, with about 1% of the
+    values exactly 2.0 and 1% exactly 0.0), or e = sigmoid(N(0, 1))
+    ("sigmoid"); write w = sigmoid(N(0, 1)) per (token, head, value channel)."""
+    rng = np.random.default_rng(seed + 15485863)
+    es = (w.B, w.T, w.H, w.dk)
+    if erase == "bimodal":
+        comp = rng.random(size=es) < 0.5
+        e = 2.0 * _sigmoid(rng.normal(0.0, 1.0, size=es) + np.where(comp, 2.0, -2.0))
+        m = rng.random(size=es)
+        e = np.where(m < 0.01, 2.0, np.where(m < 0.02, 0.0, e))
+    elif erase == "sigmoid":
+        e = _sigmoid(rng.standard_normal(es))
+    else:
+        raise ValueError(erase)
+    wr = _sigmoid(rng.standard_normal((w.B, w.T, w.H, w.dv)))
+    return EraseWriteWorkload(w, _round(e, w.dtype), _round(wr, w.dtype))
+
+
+def gdn2_ckda_fwd(seed: int = 0, B: int = 2, H: int = 16, T: int = 8192) -> EraseWriteWorkload:
+    """Erase/write gates combined with Complex KDA's signed gates (the pages'
+    future-work combination) at the Complex KDA workload's shape: B=2, H=16,
+    T=8192, d=128, bf16, chunk 64; alpha by the Complex KDA recipe, erase
+    bimodal in [0, 2], write sigmoid."""
+    w = make_forward("gdn2_ckda_b2_h16_t8192", B=B, H=H, T=T, dk=128, dv=128, chunk=64, gate="ckda", seed=seed)
+    return erase_write_gates(w, seed)
+
+
 def cotangents(w: Workload, seed: int = 0, with_dS_T: bool = True):
     """Output gradients for a backward call on ``w``: dO [B,T,H,dv] and dS_T
     [N,H,dk,dv] (or None), fp32 CPU tensors."""

@@ -27,7 +27,8 @@ STAGE_PREP, STAGE_STATE, STAGE_ALL = 1, 2, 3
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd",
            "kda_chunk_bwd_workspace_bytes", "kda_gauge_fold", "kda_gauge_fold_workspace_bytes", "kda_chunk_fwd_gauge",
            "kda_chunk_fwd_gauge_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error",
-           "kda_version", "kda_chunk_fwd_status", "kda_chunk_fwd_noalloc")
+           "kda_version", "kda_chunk_fwd_status", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_ew",
+           "kda_decode_step_ew")
 
 
 class KDAError(RuntimeError):
@@ -78,6 +79,10 @@ def _lib():
         lib.kda_version.argtypes = []
         lib.kda_chunk_fwd_status.restype = i
         lib.kda_chunk_fwd_status.argtypes = [ctypes.c_uint32]
+        lib.kda_chunk_fwd_ew.restype = i
+        lib.kda_chunk_fwd_ew.argtypes = [vp] * 9 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
+        lib.kda_decode_step_ew.restype = i
+        lib.kda_decode_step_ew.argtypes = [vp] * 8 + [i] * 6 + [vp]
         lib.kda_chunk_fwd_noalloc.restype = i
         lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp]
         _L = lib
@@ -401,4 +406,88 @@ def decode_step(q, k, v, gate, beta, S, out: Optional[torch.Tensor] = None, gate
                                 N, H, dk, dv, dt, int(gate_kind), ctypes.c_void_p(st) if st else None)
     if rc != KDA_OK:
         raise KDAError(rc, "kda_decode_step")
+    return out
+
+
+def chunk_fwd_ew(q, k, v, gate, erase, write, S0=None, cu_seqlens=None, chunk: int = 64,
+                 gate_kind: Optional[int] = None, out: Optional[torch.Tensor] = None, state_out: bool = True,
+                 S_T: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise forward with decoupled erase and write gates
+    (kda_chunk_fwd_ew): S_t = (I - k (e o k)^T) Diag(alpha) S + k (w o v)^T.
+    erase [B,T,H,dk], write [B,T,H,dv] in the inputs' dtype; everything else as
+    for chunk_fwd (the erase gate takes beta's place in the shape checks)."""
+    B, T, H, dk, dv, gate_kind = _check_seq_inputs(q, k, v, gate, erase[..., 0], gate_kind)
+    _check_shape("erase", erase, (B, T, H, dk))
+    _check_shape("write", write, (B, T, H, dv))
+    for name, t in (("erase", erase), ("write", write)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    N = B if cu_seqlens is None else int(cu_seqlens.numel() - 1)
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed sequences (cu_seqlens) need B = 1, got %d" % B)
+    if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (N, H, dk, dv)):
+        raise ValueError("S0 must be fp32 [%d,%d,%d,%d]" % (N, H, dk, dv))
+    device = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("erase", erase), ("write", write)):
+        _check_dev(name, t, device)
+    dt = _dtype_code(q)
+    varlen, N = _check_varlen(cu_seqlens, B, device)
+    _check_state("S0", S0, N, H, dk, dv, device)
+    if out is None:
+        out = torch.empty((B, T, H, dv), device=device, dtype=torch.float32)
+    else:
+        _check_dev("out", out, device)
+        _check_shape("out", out, (B, T, H, dv))
+    if S_T is None and state_out:
+        S_T = torch.empty((N, H, dk, dv), device=device, dtype=torch.float32)
+    _check_state("S_T", S_T, N, H, dk, dv, device)
+    need = workspace_bytes(B, H, T, dk, dv, chunk, N, varlen, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
+    st = _stream_handle(stream, device)
+    rc = _lib().kda_chunk_fwd_ew(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(erase), _ptr(write), _ptr(S0), _ptr(out),
+                                 _ptr(S_T), B, H, T, dk, dv, chunk, _ptr(cu_seqlens), N if varlen else 0, dt,
+                                 int(gate_kind), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 ctypes.c_void_p(st) if st else None)
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_ew")
+    return out, S_T
+
+
+def decode_step_ew(q, k, v, gate, erase, write, S, out: Optional[torch.Tensor] = None,
+                   gate_kind: Optional[int] = None, stream=None) -> torch.Tensor:
+    """One decode step with erase [N,H,dk] and write [N,H,dv] gates
+    (kda_decode_step_ew); S [N,H,dk,dv] fp32 updated in place."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [N,H,dk] and v [N,H,dv]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check_shape("k", k, (N, H, dk))
+    _check_shape("v", v, (N, H, dv))
+    _check_shape("erase", erase, (N, H, dk))
+    _check_shape("write", write, (N, H, dv))
+    gate_kind = _gate_kind(gate, 2, gate_kind)
+    _check_shape("gate", gate, (N, H, dk) if gate_kind == GATE_CHANNEL else (N, H))
+    for name, t in (("k", k), ("v", v), ("gate", gate), ("erase", erase), ("write", write)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError("S must be fp32 [%d,%d,%d,%d]" % (N, H, dk, dv))
+    device = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("erase", erase), ("write", write), ("S", S)):
+        _check_dev(name, t, device)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((N, H, dv), device=device, dtype=torch.float32)
+    else:
+        _check_dev("out", out, device)
+        _check_shape("out", out, (N, H, dv))
+    st = _stream_handle(stream, device)
+    rc = _lib().kda_decode_step_ew(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(erase), _ptr(write), _ptr(S),
+                                   _ptr(out), N, H, dk, dv, dt, int(gate_kind), ctypes.c_void_p(st) if st else None)
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_decode_step_ew")
     return out

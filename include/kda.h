@@ -178,6 +178,36 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* gat
                     void* stream);
 
 /*
+ * Decoupled erase and write gates (Gated DeltaNet-2 blurb: the delta rule's
+ * memory update split into a channel-wise erase gate and a channel-wise
+ * write gate; the pages name combining them with Complex KDA's gates as
+ * future work, Complex KDA summary). The pages give no formula; the form
+ * implemented keeps the update rank one along k and gives beta's two roles to
+ * two gates:
+ *   S_t = (I - k_t (e_t o k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t o v_t)^T
+ *   o_t = S_t^T q_t
+ * with the erase gate e_t in R^{dk} (per key channel) and the write gate w_t
+ * in R^{dv} (per value channel); e_t = w_t = beta_t (every channel) gives the
+ * recurrence at the top of this header. Any alpha the forward takes is
+ * allowed (channel or scalar gate, signs and zeros included).
+ *
+ * kda_chunk_fwd_ew: the chunkwise forward of that form. Arguments as for
+ * kda_chunk_fwd, with beta replaced by
+ *   erase [B, T, H, dk] and write [B, T, H, dv] in the input dtype,
+ * both 16-byte aligned; the workspace is kda_chunk_fwd_workspace_bytes(...)
+ * bytes (same status word). kda_decode_step_ew: one decode step of it, as
+ * kda_decode_step with erase [N, H, dk] and write [N, H, dv].
+ * Returns KDA_OK or a negative status.
+ */
+int kda_chunk_fwd_ew(const void* q, const void* k, const void* v, const void* gate, const void* erase,
+                     const void* write, const float* S0, float* o, float* S_T, int B, int H, int T, int dk, int dv,
+                     int chunk, const int32_t* cu_seqlens, int N, int dtype, int gate_kind, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int kda_decode_step_ew(const void* q, const void* k, const void* v, const void* gate, const void* erase,
+                       const void* write, float* S, float* o, int N, int H, int dk, int dv, int dtype, int gate_kind,
+                       void* stream);
+
+/*
  * Bytes of device workspace kda_chunk_bwd needs for these sizes (0 when the
  * arguments are invalid). Arguments as for kda_chunk_fwd_workspace_bytes.
  */

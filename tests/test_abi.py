@@ -249,3 +249,35 @@ def test_binding_rejects_mismatched_shapes(lib):
             kda.decode_step(**dict(dec, **change))
     with pytest.raises(ValueError):
         kda.decode_step(**dict(dec, gate=z(3, 2)), gate_kind=kda.GATE_CHANNEL)
+
+
+def test_erase_write_validation(lib):
+    args = ("q", "k", "v", "gate", "erase", "write", "S0", "o", "S_T", "B", "H", "T", "dk", "dv", "chunk", "cu", "N",
+            "dtype", "gate_kind", "ws", "wsb", "stream")
+
+    def fwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, erase=FAKE, write=FAKE, S0=None, o=FAKE, S_T=None, B=1, H=2, T=8,
+                 dk=16, dv=16, chunk=16, cu=None, N=0, dtype=kda.KDA_BF16, gate_kind=0, ws=FAKE, wsb=1 << 30,
+                 stream=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_ew(*[a[x] for x in args])
+    assert fwd(B=0) == kda.KDA_EINVAL
+    assert fwd(dk=48) == kda.KDA_ENOTSUP
+    assert fwd(erase=None) == kda.KDA_EINVAL
+    assert fwd(write=None) == kda.KDA_EINVAL
+    assert fwd(erase=FAKE + 4) == kda.KDA_EALIGN
+    assert fwd(write=FAKE + 2) == kda.KDA_EALIGN
+    assert fwd(ws=None) == kda.KDA_EINVAL
+    assert fwd(wsb=1) == kda.KDA_EINVAL
+
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, erase=FAKE, write=FAKE, S=FAKE, o=FAKE, N=2, H=2, dk=16, dv=16,
+                 dtype=kda.KDA_BF16, gate_kind=0, stream=None)
+        a.update(kw)
+        return lib.kda_decode_step_ew(*a.values())
+    assert dec(N=0) == kda.KDA_EINVAL
+    assert dec(erase=None) == kda.KDA_EINVAL
+    assert dec(write=None) == kda.KDA_EINVAL
+    assert dec(erase=FAKE + 1) == kda.KDA_EALIGN
+    assert dec(S=FAKE + 4) == kda.KDA_EALIGN
+    assert dec(gate_kind=5) == kda.KDA_ENOTSUP

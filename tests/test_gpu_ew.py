@@ -1,0 +1,162 @@
+"""GPU parity of the erase/write-gate forward and decode (kda_chunk_fwd_ew,
+kda_decode_step_ew) against the oracle's erase/write recurrence
+(oracle.fwd_ew / decode_step_ew, pinned in test_oracle_ew.py).
+
+Same metric and bars as the forward: err = max|x_gpu - x_ref| / rms(x_ref),
+1e-4 with fp32 inputs, 2e-2 with bf16 inputs (fp32 state)."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_46_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_46_amd import kda as m
+    m.library()
+    return m
+
+
+def err(x, ref):
+    x = x.detach().double().cpu().numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    d = float(np.max(np.abs(x - ref)))
+    return d / rms if rms > 0 else d
+
+
+def run_gpu(kda, x, chunk=None):
+    w = x.w
+    d = lambda t: None if t is None else t.cuda()  # noqa: E731
+    need = kda.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, chunk or w.chunk, w.n_seqs, w.cu_seqlens is not None,
+                               w.dtype)
+    ws = torch.full((max(need, 1),), 0xA5, dtype=torch.uint8, device="cuda")
+    o, ST = kda.chunk_fwd_ew(d(w.q), d(w.k), d(w.v), d(w.gate), d(x.erase), d(x.write), S0=d(w.S0),
+                             cu_seqlens=d(w.cu_seqlens), chunk=chunk or w.chunk, gate_kind=w.gate_kind, workspace=ws)
+    assert kda.fwd_status(ws) == kda.KDA_OK
+    return o.cpu(), ST.cpu()
+
+
+def check(kda, x, chunk=None):
+    w = x.w
+    print("case", w.name, "B", w.B, "H", w.H, "T", w.T, "dk", w.dk, "dv", w.dv, "chunk", chunk or w.chunk,
+          "dtype", w.dtype, flush=True)
+    o, ST = run_gpu(kda, x, chunk)
+    ro, rS = oracle.fwd_ew(w.q, w.k, w.v, w.gate, x.erase, x.write, w.S0, w.cu_seqlens, w.gate_kind)
+    eo, eS = err(o, ro), err(ST, rS)
+    print("  err o %.2e S %.2e" % (eo, eS), flush=True)
+    assert np.isfinite(o.numpy()).all() and np.isfinite(ST.numpy()).all()
+    assert eo <= TOL[w.dtype] and eS <= TOL[w.dtype], (eo, eS)
+    return o, ST
+
+
+CASES = [
+    # gate, dtype, dk, dv, chunk, T, erase recipe
+    ("ckda", torch.bfloat16, 128, 128, 64, 300, "bimodal"),
+    ("kda", torch.bfloat16, 128, 64, 64, 129, "sigmoid"),
+    ("gdn", torch.bfloat16, 128, 128, 64, 200, "bimodal"),
+    ("kda", torch.bfloat16, 64, 64, 64, 150, "sigmoid"),
+    ("ckda", torch.bfloat16, 128, 32, 32, 97, "bimodal"),
+    ("gdn", torch.bfloat16, 16, 32, 16, 40, "sigmoid"),
+    ("ckda", torch.float32, 128, 128, 64, 150, "bimodal"),
+    ("kda", torch.float32, 32, 16, 16, 77, "sigmoid"),
+    ("gdn", torch.float32, 64, 128, 32, 65, "bimodal"),
+    ("ckda", torch.float32, 16, 64, 64, 1, "bimodal"),
+]
+
+
+@pytest.mark.parametrize("gate,dtype,dk,dv,chunk,T,erase", CASES)
+def test_ew_small_parity(kda, gate, dtype, dk, dv, chunk, T, erase):
+    w = inputs.make_forward("ew_%s" % gate, B=2, H=3, T=T, dk=dk, dv=dv, chunk=chunk, dtype=dtype, gate=gate,
+                            seed=T + dk + dv, s0_std=0.3)
+    check(kda, inputs.erase_write_gates(w, seed=T, erase=erase))
+
+
+def test_ew_varlen_and_signed_zero_gates(kda):
+    w = inputs.make_forward("ew_varlen", B=1, H=2, T=0, dk=128, dv=128, chunk=64, gate="ckda", seed=3,
+                            lengths=[300, 0, 1, 129, 64], s0_std=0.2)
+    w = dataclasses.replace(w, gate=inputs.signed_zero_gates(w.gate, seed=2))
+    check(kda, inputs.erase_write_gates(w, seed=5))
+
+
+def test_ew_chunk_sizes_agree(kda):
+    w = inputs.make_forward("ew_chunks", B=2, H=2, T=170, dk=64, dv=64, chunk=64, dtype=torch.float32, gate="ckda",
+                            seed=8, s0_std=0.2)
+    x = inputs.erase_write_gates(w, seed=8)
+    outs = [run_gpu(kda, x, chunk=c) for c in (16, 32, 64)]
+    for o, S in outs[1:]:
+        assert err(o, outs[0][0].double().numpy()) < 1e-5 and err(S, outs[0][1].double().numpy()) < 1e-5
+
+
+def test_ew_reduces_to_the_gated_delta_rule(kda):
+    """erase = write = beta on every channel: the erase/write forward and the
+    plain forward both match the plain oracle at the bar."""
+    w = inputs.make_forward("ew_red", B=2, H=4, T=260, dk=128, dv=128, chunk=64, gate="ckda", seed=21, s0_std=0.2)
+    e = w.beta[..., None].expand(*w.beta.shape, w.dk).contiguous()
+    wr = w.beta[..., None].expand(*w.beta.shape, w.dv).contiguous()
+    o_ew, S_ew = run_gpu(kda, inputs.EraseWriteWorkload(w, e, wr))
+    ro, rS = oracle.fwd(w.q, w.k, w.v, w.gate, w.beta, w.S0, None, w.gate_kind)
+    assert err(o_ew, ro) <= 2e-2 and err(S_ew, rS) <= 2e-2
+
+
+def test_ew_full_size_every_head(kda):
+    """Erase/write gates with Complex KDA's signed gates at the Complex KDA
+    workload's shape (B=2, H=16, T=8192, d=128, bf16, chunk 64), every
+    (sequence, head) against the oracle."""
+    x = inputs.gdn2_ckda_fwd()
+    o, ST = check(kda, x)
+    ro, rS = oracle.fwd_ew(x.w.q, x.w.k, x.w.v, x.w.gate, x.erase, x.write)
+    worst = max(max(err(o[:, :, h], ro[:, :, h]), err(ST[:, h], rS[:, h])) for h in range(x.w.H))
+    print("  worst head %.3e" % worst, flush=True)
+    assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,dk,dv,gk", [(torch.bfloat16, 128, 128, 0), (torch.float32, 64, 32, 0),
+                                            (torch.bfloat16, 32, 64, 1), (torch.float32, 128, 16, 1)])
+def test_ew_decode_parity(kda, dtype, dk, dv, gk):
+    N, H, steps = 6, 3, 6
+    rng = np.random.default_rng(dk + 3 * dv)
+    S = torch.from_numpy(rng.normal(0, 0.3, (N, H, dk, dv))).float()
+    Sd, Sr = S.cuda(), S.double().numpy().copy()
+    for st in range(steps):
+        w = inputs.make_forward("dew", B=N, H=H, T=1, dk=dk, dv=dv, dtype=dtype, gate="gdn" if gk else "ckda",
+                                seed=60 + st)
+        x = inputs.erase_write_gates(w, seed=st)
+        q, k, v, g, e, wr = (t[:, 0].contiguous() for t in (w.q, w.k, w.v, w.gate, x.erase, x.write))
+        o = kda.decode_step_ew(q.cuda(), k.cuda(), v.cuda(), g.cuda(), e.cuda(), wr.cuda(), Sd, gate_kind=gk)
+        ro = oracle.decode_step_ew(q, k, v, g, e, wr, Sr, gate_kind=gk)
+        torch.cuda.synchronize()
+        assert err(o.cpu(), ro) < TOL[dtype] / 20
+    assert err(Sd.cpu(), Sr) < TOL[dtype] / 20
+
+
+def test_ew_decode_after_prefill(kda):
+    """prefill(T) through kda_chunk_fwd_ew, then decode_step_ew steps, equals
+    one erase/write forward over T + steps tokens."""
+    w = inputs.make_forward("pfew", B=3, H=2, T=70, dk=64, dv=64, chunk=32, dtype=torch.float32, gate="ckda",
+                            s0_std=0.2, seed=15)
+    x = inputs.erase_write_gates(w, seed=15)
+    o_full, S_full = run_gpu(kda, x)
+    pre = 66
+    sl = lambda t: t[:, :pre].contiguous()  # noqa: E731
+    wp = dataclasses.replace(w, q=sl(w.q), k=sl(w.k), v=sl(w.v), gate=sl(w.gate), beta=sl(w.beta), T=pre)
+    _, S = run_gpu(kda, inputs.EraseWriteWorkload(wp, sl(x.erase), sl(x.write)))
+    S = S.cuda()
+    for t in range(pre, 70):
+        o = kda.decode_step_ew(*(z[:, t].contiguous().cuda() for z in (w.q, w.k, w.v, w.gate, x.erase, x.write)), S)
+        torch.cuda.synchronize()
+        assert err(o.cpu(), o_full[:, t].double().numpy()) < 1e-4
+    assert err(S.cpu(), S_full.double().numpy()) < 1e-4
