@@ -1,0 +1,1149 @@
+// Chunkwise backward of the gated delta rule (KDA / Complex KDA / GDN): the
+// gradient of L = sum_t <o_t, dO_t> + sum_seq <S_T, dS_T> with respect to q,
+// k, v, the gate alpha, beta and S0, chunk by chunk with fp32 MFMA
+// contractions (the pages name a chunkwise WY algorithm with gate-aware
+// backpropagation for this family: Gated DeltaNet-2 blurb; they print no
+// formulas, so the adjoint below is derived from the chunk identities).
+//
+// Chunk identities (C = 64 tokens entering with state S; per key channel
+// rel(r, j) = prod_{j < tau <= r} alpha_tau, Gamma_r = prod_{tau <= r} alpha_tau
+// inside the chunk, gamma = Gamma_{C-1}):
+//   G_rj = sum_i k_ri rel_i(r,j) k_ji  (j < r),   P_rj = sum_i q_ri rel_i(r,j) k_ji  (j <= r)
+//   X = (I + Diag(beta) G)^{-1},  W = X (beta o Gamma o K),  U~ = X (beta o V)
+//   U = U~ - W S,  O = (Gamma o Q) S + P U,  S_next = Diag(gamma) S + K_end^T U
+// (K_end[j] = rel(C-1, j) o k_j). With dS' = dL/dS_next:
+//   dU = P^T dO + K_end dS'              dS = Diag(gamma) dS' + (Gamma o Q)^T dO - W^T dU
+//   d(Gamma o Q) = dO S^T   dP = dO U^T   dK_end = U dS'^T   dW = -dU S^T   dgamma = rowsum(S o dS')
+//   dX = dU (beta o V)^T + dW (beta o Gamma o K)^T,   dV = beta o (X^T dU),  d(Gamma o K) = beta o (X^T dW)
+//   dA = -X^T dX X^T (strictly lower part),  dG = Diag(beta) dA
+//   dbeta_r = rowsum(V o X^T dU)_r + rowsum(Gamma o K o X^T dW)_r + sum_j dA_rj G_rj
+// and through the gated Gram matrices and the prefix/suffix products to q, k
+// and alpha. Every pair (r > j) of a chunk is separated at one level of a
+// binary split (halves of 32, 16, 8, 4, 2, 1 tokens); at that level
+// rel(r, j) = pre_r o suf_j with pre_r = prod_{m < tau <= r} alpha_tau and
+// suf_j = prod_{j < tau <= m} alpha_tau (m the last token of the left half),
+// so each level's Gram terms are plain matrix products of scaled rows, and the
+// gate gradient of a product of consecutive gates is a prefix product times a
+// reverse scan: d/dalpha_tau sum_{r >= tau} c_r prod_{m<sigma<=r} alpha_sigma
+// = (prod_{m<sigma<tau} alpha_sigma) R_tau with R_tau = c_tau + alpha_{tau+1} R_{tau+1}.
+// Nothing is divided, so exact zero and negative gates have their ordinary
+// derivatives.
+//
+// Kernels (one stream, in order):
+//   1. cb_prep_kernel       (chunk, head) parallel: G, P, X, W, K_end, Gamma o Q, gamma
+//   2. cb_state_kernel      sequential per (sequence, head, 16 value columns): S at every chunk start
+//   3. cb_adjoint_kernel    sequential backwards: dS' at every chunk end; dS0
+//   4. cb_grad_state_kernel (chunk, head) parallel: dv; d(Gamma o Q), dK_end, dP, dX, d(Gamma o K), dgamma, beta parts
+//   5. cb_grad_gate_kernel  (chunk, head) parallel: dA, dG, dq, dk, dalpha, dbeta
+// All operands fp32; products on v_mfma_f32_16x16x4f32 with fp32 accumulation.
+#include "kda_common.h"
+#include "kda_launch.h"
+#include "kda_chunkmap.h"
+
+namespace kda {
+namespace cb {
+
+constexpr int C = 64;          // chunk length
+constexpr int LC = C + 4;      // LDS row stride (floats) of C x C matrices
+constexpr int LS = 16 + 4;     // LDS row stride of 16-column slices
+
+// Workspace regions, per (chunk, head), in floats.
+template <int DK>
+struct PrepLay {
+    static constexpr size_t X = 0, G = (size_t)C * C, P = 2 * (size_t)C * C, W = 3 * (size_t)C * C;
+    static constexpr size_t KE = W + (size_t)C * DK, QG = KE + (size_t)C * DK, GAM = QG + (size_t)C * DK;
+    static constexpr size_t FLOATS = (GAM + DK + 63) / 64 * 64;
+};
+constexpr size_t EXT_FLOATS = (size_t)C * C + 2 * C;   // dX, beta part
+
+// ---------------------------------------------------------------- 16x16x4 fp32 tiles
+// lane l = 16 g + i. Within a 16-deep K block, step s of lane group g takes K
+// index 4 g + s for both operands (any order works as long as A and B agree):
+//   A operand a[s] = A(i, 4g + s),  B operand b[s] = B(4g + s, i),
+//   D tile: lane holds D(4g + e, i), e = 0..3.
+// A D tile is then itself the B operand of the next product over its rows.
+
+__device__ __forceinline__ f32x4 mm4(const f32x4& a, const f32x4& b, f32x4 c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ int lane_i() { return threadIdx.x & 15; }
+__device__ __forceinline__ int lane_g() { return (threadIdx.x >> 4) & 3; }
+
+// A operand from row-major M: rows r0.., K columns k0..k0+15
+__device__ __forceinline__ f32x4 ldA(const float* M, int ld, int r0, int k0) {
+    return *reinterpret_cast<const f32x4*>(M + (r0 + lane_i()) * ld + k0 + 4 * lane_g());
+}
+// A operand of M^T: A(i, kk) = M[k0 + kk][r0 + i]
+__device__ __forceinline__ f32x4 ldAT(const float* M, int ld, int r0, int k0) {
+    const int i = lane_i(), g = lane_g();
+    f32x4 a;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = M[(k0 + 4 * g + s) * ld + r0 + i];
+    return a;
+}
+// B operand from row-major M: B(kk, j) = M[k0 + kk][c0 + j]
+__device__ __forceinline__ f32x4 ldB(const float* M, int ld, int k0, int c0) {
+    const int i = lane_i(), g = lane_g();
+    f32x4 b;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = M[(k0 + 4 * g + s) * ld + c0 + i];
+    return b;
+}
+// B operand of M^T: B(kk, j) = M[c0 + j][k0 + kk]
+__device__ __forceinline__ f32x4 ldBT(const float* M, int ld, int k0, int c0) {
+    return *reinterpret_cast<const f32x4*>(M + (c0 + lane_i()) * ld + k0 + 4 * lane_g());
+}
+// D tile into row-major M at (r0, c0)
+__device__ __forceinline__ void stD(float* M, int ld, int r0, int c0, const f32x4& d) {
+    const int i = lane_i(), g = lane_g();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M[(r0 + 4 * g + e) * ld + c0 + i] = d[e];
+}
+__device__ __forceinline__ f32x4 ldD(const float* M, int ld, int r0, int c0) {
+    const int i = lane_i(), g = lane_g();
+    f32x4 d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = M[(r0 + 4 * g + e) * ld + c0 + i];
+    return d;
+}
+
+// Is local pair (r, j) of a 16-token tile separated at the in-tile level of
+// half width h (8, 4, 2, 1)?
+__device__ __forceinline__ bool sep_in(int r, int j, int h) {
+    const int w = 2 * h;
+    return (r / w == j / w) && (r % w >= h) && (j % w < h);
+}
+
+// Binary-split levels of a 64-token chunk: half widths 32, 16 (between 16-token
+// tiles) and 8, 4, 2, 1 (inside tiles).
+__device__ __forceinline__ int level_half(int L) { return 32 >> L; }
+
+// The lower 16x16 tiles (R >= J) of a C x C matrix, in a fixed order.
+__device__ __forceinline__ void lower_tile(int idx, int& R, int& J) {
+    R = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
+    J = idx - (R * (R + 1)) / 2;
+}
+
+// Is lower tile (R, J) active at between-tile level L (0: halves of 32, 1: halves of 16)?
+__device__ __forceinline__ bool tile_at_level(int R, int J, int L) {
+    if (L == 0) return R >= 2 && J <= 1;
+    if (L == 1) return (R == 1 && J == 0) || (R == 3 && J == 2);
+    return R == J;
+}
+
+struct Params {
+    const void *q, *k, *v, *gate, *beta;
+    const float *S0, *dO, *dST;
+    float *gq, *gk, *gv, *gg, *gb, *gS0;
+    float* prep;   // PrepLay per (chunk, head)
+    float* ck;     // S and dS' per (chunk, head): 2 * dk * dv floats
+    float* ext;    // EXT_FLOATS per (chunk, head)
+    ChunkMap map;
+    int H, DV;
+};
+
+template <class TIn>
+__device__ __forceinline__ float gate_at(const Params& p, size_t row, int DK, int c, bool sg) {
+    const TIn* g = (const TIn*)p.gate;
+    return sg ? ld_in(g + row) : ld_in(g + row * DK + c);
+}
+
+// ================================================================ 1. prep
+// One workgroup (4 waves) per (chunk, head). Pass 1 over blocks of 32 key
+// channels accumulates the gated Gram matrices G and P level by level; then
+// X = (I + Diag(beta) G)^{-1} (16x16 diagonal blocks by forward substitution,
+// the rest by block products); pass 2 forms W, K_end, Gamma o Q and gamma.
+template <int DK>
+struct PrepSmem {
+    static constexpr int CB = 32, LB = CB + 4;
+    static constexpr size_t K = 0, Q = K + (size_t)C * LB, A = Q + (size_t)C * LB;
+    static constexpr size_t XK = A + (size_t)C * LB, XQ = XK + (size_t)C * LB;
+    static constexpr size_t G = XQ + (size_t)C * LB, P = G + (size_t)C * LC, XI = P + (size_t)C * LC;
+    static constexpr size_t BETA = XI + (size_t)C * LC;
+    static constexpr size_t FLOATS = BETA + C;
+    static constexpr size_t BYTES = FLOATS * 4;
+};
+
+template <class TIn, int DK, bool SG>
+__global__ void __launch_bounds__(256) cb_prep_kernel(Params p) {
+    using SM = PrepSmem<DK>;
+    using PL = PrepLay<DK>;
+    constexpr int CB = SM::CB, LB = SM::LB;
+    extern __shared__ __align__(16) float sm[];
+    float *sK = sm + SM::K, *sQ = sm + SM::Q, *sA = sm + SM::A, *sXK = sm + SM::XK, *sXQ = sm + SM::XQ;
+    float *sG = sm + SM::G, *sP = sm + SM::P, *sX = sm + SM::XI, *sBeta = sm + SM::BETA;
+
+    const int H = p.H;
+    const int item = blockIdx.x;
+    const int h = item % H, gidx = launch_chunk(p.map, item / H);
+    long t0;
+    int n;
+    if (!resolve_chunk(p.map, gidx, C, t0, n)) return;
+    const int tid = threadIdx.x, w = tid / WAVE;
+    float* out = p.prep + ((size_t)gidx * H + h) * PL::FLOATS;
+    const TIn* gk = (const TIn*)p.k;
+    const TIn* gq = (const TIn*)p.q;
+
+    if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
+
+    auto load_block = [&](int cb) {
+        for (int x = tid; x < C * CB; x += 256) {
+            const int r = x / CB, c = x % CB, ch = cb * CB + c;
+            float kv = 0.f, qv = 0.f, av = 1.f;
+            if (r < n) {
+                const size_t row = (size_t)(t0 + r) * H + h;
+                kv = ld_in(gk + row * DK + ch);
+                qv = ld_in(gq + row * DK + ch);
+                av = gate_at<TIn>(p, row, DK, ch, SG);
+            }
+            sK[r * LB + c] = kv;
+            sQ[r * LB + c] = qv;
+            sA[r * LB + c] = av;
+        }
+    };
+
+    // ---- pass 1: G and P, lower tiles; wave w owns tiles w, w + 4, w + 8
+    f32x4 accG[3], accP[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) { accG[u] = zero4(); accP[u] = zero4(); }
+    for (int cb = 0; cb < DK / CB; ++cb) {
+        __syncthreads();
+        load_block(cb);
+        __syncthreads();
+        for (int L = 0; L < 7; ++L) {
+            // stage: right rows k o pre and q o pre, left rows k o suf (L = 6: raw k, q)
+            {
+                const int c = tid % CB, part = tid / CB;
+                if (L == 6) {
+                    for (int r = part; r < C; r += 256 / CB) {
+                        sXK[r * LB + c] = sK[r * LB + c];
+                        sXQ[r * LB + c] = sQ[r * LB + c];
+                    }
+                } else {
+                    const int hw = level_half(L), ng = C / (2 * hw);
+                    for (int gi = part; gi < ng; gi += 256 / CB) {
+                        const int s0 = gi * 2 * hw, m = s0 + hw - 1;
+                        float f = 1.f;
+                        for (int r = m + 1; r < s0 + 2 * hw; ++r) {
+                            f *= sA[r * LB + c];
+                            sXK[r * LB + c] = sK[r * LB + c] * f;
+                            sXQ[r * LB + c] = sQ[r * LB + c] * f;
+                        }
+                        f = 1.f;
+                        for (int j = m; j >= s0; --j) {
+                            sXK[j * LB + c] = sK[j * LB + c] * f;
+                            f *= sA[j * LB + c];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int idx = w + 4 * u;
+                if (idx >= 10) continue;
+                int R, J;
+                lower_tile(idx, R, J);
+                if (L < 6 && !tile_at_level(R, J, L < 2 ? L : 2)) continue;
+                if (L == 6 && R != J) continue;
+                f32x4 tg = zero4(), tp = zero4();
+#pragma unroll
+                for (int kb = 0; kb < CB / 16; ++kb) {
+                    const f32x4 bj = ldBT(sXK, LB, 16 * kb, 16 * J);
+                    if (L < 6) tg = mm4(ldA(sXK, LB, 16 * R, 16 * kb), bj, tg);
+                    tp = mm4(ldA(sXQ, LB, 16 * R, 16 * kb), bj, tp);
+                }
+                if (L >= 2) {
+                    const int hw = L < 6 ? level_half(L) : 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * lane_g() + e, j = lane_i();
+                        const bool keep = L < 6 ? sep_in(r, j, hw) : (r == j);
+                        tg[e] = keep ? tg[e] : 0.f;
+                        tp[e] = keep ? tp[e] : 0.f;
+                    }
+                }
+                if (L < 6) accG[u] += tg;
+                accP[u] += tp;
+            }
+            __syncthreads();
+        }
+    }
+    // ---- G and P to LDS (upper tiles zero) and out
+    for (int x = tid; x < C * C; x += 256) {
+        const int r = x / C, c = x % C;
+        if ((r / 16) < (c / 16)) { sG[r * LC + c] = 0.f; sP[r * LC + c] = 0.f; }
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int idx = w + 4 * u;
+        if (idx >= 10) continue;
+        int R, J;
+        lower_tile(idx, R, J);
+        stD(sG, LC, 16 * R, 16 * J, accG[u]);
+        stD(sP, LC, 16 * R, 16 * J, accP[u]);
+    }
+    __syncthreads();
+    for (int x = tid; x < C * C; x += 256) {
+        const int r = x / C, c = x % C;
+        out[PL::G + x] = sG[r * LC + c];
+        out[PL::P + x] = sP[r * LC + c];
+        sX[r * LC + c] = 0.f;
+    }
+    __syncthreads();
+    // ---- X = (I + A)^{-1}, A = Diag(beta) G: diagonal 16x16 blocks (wave b,
+    // lanes 0..15 = columns) by forward substitution
+    {
+        const int b = w, c = tid % WAVE;
+        if (c < 16) {
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) acc += sG[(16 * b + r) * LC + 16 * b + m] * x[m];
+                const float br = sBeta[16 * b + r];
+                x[r] = r == c ? 1.f : (r > c ? -br * acc : 0.f);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sX[(16 * b + r) * LC + 16 * b + c] = x[r];
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance: X_RJ = -X_RR sum_{J <= M < R} A_RM X_MJ
+    for (int d = 1; d < 4; ++d) {
+        if (w < 4 - d) {
+            const int J = w, R = w + d;
+            const float br = sBeta[16 * R + lane_i()];
+            f32x4 y = zero4();
+            for (int M = J; M < R; ++M) y = mm4(ldA(sG, LC, 16 * R, 16 * M) * br, ldB(sX, LC, 16 * M, 16 * J), y);
+            const f32x4 xr = mm4(ldA(sX, LC, 16 * R, 16 * R), y, zero4());
+            stD(sX, LC, 16 * R, 16 * J, -xr);
+        }
+        __syncthreads();
+    }
+    for (int x = tid; x < C * C; x += 256) out[PL::X + x] = sX[(x / C) * LC + x % C];
+
+    // ---- pass 2: W = X (beta o Gamma o K), K_end, Gamma o Q, gamma
+    for (int cb = 0; cb < DK / CB; ++cb) {
+        __syncthreads();
+        load_block(cb);
+        __syncthreads();
+        if (tid < CB) {
+            const int c = tid;
+            float gm = 1.f;
+            for (int r = 0; r < C; ++r) {
+                gm *= sA[r * LB + c];
+                sXQ[r * LB + c] = gm * sQ[r * LB + c];                   // Gamma o Q
+                sXK[r * LB + c] = sBeta[r] * gm * sK[r * LB + c];         // beta o Gamma o K
+            }
+            out[PL::GAM + cb * CB + c] = gm;
+            float f = 1.f;
+            for (int j = C - 1; j >= 0; --j) {
+                const float kv = sK[j * LB + c];
+                sK[j * LB + c] = kv * f;                                 // K_end
+                f *= sA[j * LB + c];
+            }
+        }
+        __syncthreads();
+        // W tiles: 4 token tiles x CB/16 channel tiles, two per wave
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tt = w + 4 * u, R = tt % 4, cc = tt / 4;
+            f32x4 acc = zero4();
+            for (int J = 0; J <= R; ++J) acc = mm4(ldA(sX, LC, 16 * R, 16 * J), ldB(sXK, LB, 16 * J, 16 * cc), acc);
+            const int i = lane_i(), g = lane_g();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[PL::W + (size_t)(16 * R + 4 * g + e) * DK + cb * CB + 16 * cc + i] = acc[e];
+        }
+        for (int x = tid; x < C * CB; x += 256) {
+            const int r = x / CB, c = x % CB;
+            out[PL::KE + (size_t)r * DK + cb * CB + c] = sK[r * LB + c];
+            out[PL::QG + (size_t)r * DK + cb * CB + c] = sXQ[r * LB + c];
+        }
+    }
+}
+
+// ================================================================ 2. states at chunk starts
+// One workgroup (4 waves) per (sequence, head, 16 value columns). Wave q keeps
+// state rows q dk/4 .. (q+1) dk/4 - 1 of the slice as D tiles. Per chunk:
+// store S; partial W S over own rows (to LDS); U = X (beta o V) - W S for
+// token tile q; S <- Diag(gamma) S + K_end^T U for own rows.
+template <int DK>
+struct WalkSmem {
+    static constexpr int LK = DK + 4;
+    static constexpr size_t M1 = 0, M2 = M1 + (size_t)C * LK, M3 = M2 + (size_t)C * LK;
+    static constexpr size_t SQ = M3 + (size_t)C * LK;           // C x C (X or P)
+    static constexpr size_t VS = SQ + (size_t)C * LC;            // C x 16 slice (v or dO)
+    static constexpr size_t BETA = VS + (size_t)C * LS;
+    static constexpr size_t GAM = BETA + C;
+    static constexpr size_t PART = GAM + DK;                     // [4 waves][4 tiles][64 lanes][4]
+    static constexpr size_t UT = PART + 4 * 4 * 256;             // [4 tiles][64 lanes][4]
+    static constexpr size_t FLOATS = UT + 4 * 256;
+    static constexpr size_t BYTES = FLOATS * 4;
+};
+
+__device__ __forceinline__ void seq_range(const ChunkMap& m, int s, int C_, long& bos, long& eos, int& cs, int& ce) {
+    if (m.cu == nullptr) {
+        bos = (long)s * m.T;
+        eos = (long)(s + 1) * m.T;
+        cs = s * m.NC;
+        ce = (s + 1) * m.NC;
+    } else {
+        bos = m.cu[s];
+        eos = m.cu[s + 1];
+        cs = m.cstart[s];
+        ce = m.cstart[s + 1];
+    }
+}
+
+template <class TIn, int DK>
+__global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
+    using SM = WalkSmem<DK>;
+    using PL = PrepLay<DK>;
+    constexpr int LK = SM::LK, RW = DK / 4, RT = RW / 16;
+    extern __shared__ __align__(16) float sm[];
+    float *sW = sm + SM::M1, *sKE = sm + SM::M2, *sX = sm + SM::SQ, *sV = sm + SM::VS;
+    float *sBeta = sm + SM::BETA, *sGam = sm + SM::GAM, *sPart = sm + SM::PART, *sU = sm + SM::UT;
+
+    const int H = p.H, DV = p.DV, NSL = DV / 16;
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
+    const int tid = threadIdx.x, q = tid / WAVE, lane = tid % WAVE;
+    const int i = lane_i(), g = lane_g();
+    long bos, eos;
+    int cs, ce;
+    seq_range(p.map, s, C, bos, eos, cs, ce);
+
+    f32x4 S[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = q * RW + 16 * rt + 4 * g + e;
+            S[rt][e] = p.S0 ? p.S0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
+        }
+    for (int gi = cs; gi < ce; ++gi) {
+        const long t0 = bos + (long)(gi - cs) * C;
+        const int n = (int)min((long)C, eos - t0);
+        const size_t base = (size_t)gi * H + h;
+        float* ckS = p.ck + base * 2 * DK * DV;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ckS[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * sl + i] = S[rt][e];
+        const float* pb = p.prep + base * PL::FLOATS;
+        for (int x = tid; x < C * DK; x += 256) {
+            const int r = x / DK, c = x % DK;
+            sW[r * LK + c] = pb[PL::W + x];
+            sKE[r * LK + c] = pb[PL::KE + x];
+        }
+        for (int x = tid; x < C * C; x += 256) sX[(x / C) * LC + x % C] = pb[PL::X + x];
+        for (int x = tid; x < C * 16; x += 256) {
+            const int r = x / 16, c = x % 16;
+            sV[r * LS + c] = r < n ? ld_in((const TIn*)p.v + ((size_t)(t0 + r) * H + h) * DV + 16 * sl + c) : 0.f;
+        }
+        if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
+        if (tid < DK) sGam[tid] = pb[PL::GAM + tid];
+        __syncthreads();
+        // partial W S over own rows, every token tile
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acc = mm4(ldA(sW, LK, 16 * t, q * RW + 16 * rt), S[rt], acc);
+            *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
+        }
+        __syncthreads();
+        // U tile q = X (beta o V) - W S
+        {
+            f32x4 acc = zero4();
+            for (int kb = 0; kb <= q; ++kb) {
+                f32x4 b = ldB(sV, LS, 16 * kb, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) b[e] *= sBeta[16 * kb + 4 * g + e];
+                acc = mm4(ldA(sX, LC, 16 * q, 16 * kb), b, acc);
+            }
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) acc -= *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
+            *reinterpret_cast<f32x4*>(sU + (q * 64 + lane) * 4) = acc;
+        }
+        __syncthreads();
+        // own rows: S <- Diag(gamma) S + K_end^T U
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mm4(ldAT(sKE, LK, q * RW + 16 * rt, 16 * kb), *reinterpret_cast<const f32x4*>(sU + (kb * 64 + lane) * 4), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[rt][e] = sGam[q * RW + 16 * rt + 4 * g + e] * S[rt][e] + acc[e];
+        }
+        __syncthreads();
+    }
+}
+
+// ================================================================ 3. adjoint at chunk ends
+// Same layout, chunks in reverse: store dS'; partial K_end dS' over own rows;
+// dU = P^T dO + K_end dS' for token tile q; dS = Diag(gamma) dS' +
+// (Gamma o Q)^T dO - W^T dU for own rows.
+template <int DK>
+__global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
+    using SM = WalkSmem<DK>;
+    using PL = PrepLay<DK>;
+    constexpr int LK = SM::LK, RW = DK / 4, RT = RW / 16;
+    extern __shared__ __align__(16) float sm[];
+    float *sKE = sm + SM::M1, *sQG = sm + SM::M2, *sW = sm + SM::M3, *sP = sm + SM::SQ, *sdO = sm + SM::VS;
+    float *sGam = sm + SM::GAM, *sPart = sm + SM::PART, *sdU = sm + SM::UT;
+
+    const int H = p.H, DV = p.DV, NSL = DV / 16;
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
+    const int tid = threadIdx.x, q = tid / WAVE, lane = tid % WAVE;
+    const int i = lane_i(), g = lane_g();
+    long bos, eos;
+    int cs, ce;
+    seq_range(p.map, s, C, bos, eos, cs, ce);
+
+    f32x4 D[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = q * RW + 16 * rt + 4 * g + e;
+            D[rt][e] = p.dST ? p.dST[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
+        }
+    for (int gi = ce - 1; gi >= cs; --gi) {
+        const long t0 = bos + (long)(gi - cs) * C;
+        const int n = (int)min((long)C, eos - t0);
+        const size_t base = (size_t)gi * H + h;
+        float* ckD = p.ck + base * 2 * DK * DV + (size_t)DK * DV;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ckD[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * sl + i] = D[rt][e];
+        const float* pb = p.prep + base * PL::FLOATS;
+        for (int x = tid; x < C * DK; x += 256) {
+            const int r = x / DK, c = x % DK;
+            sKE[r * LK + c] = pb[PL::KE + x];
+            sQG[r * LK + c] = pb[PL::QG + x];
+            sW[r * LK + c] = pb[PL::W + x];
+        }
+        for (int x = tid; x < C * C; x += 256) sP[(x / C) * LC + x % C] = pb[PL::P + x];
+        for (int x = tid; x < C * 16; x += 256) {
+            const int r = x / 16, c = x % 16;
+            sdO[r * LS + c] = r < n ? p.dO[((size_t)(t0 + r) * H + h) * DV + 16 * sl + c] : 0.f;
+        }
+        if (tid < DK) sGam[tid] = pb[PL::GAM + tid];
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acc = mm4(ldA(sKE, LK, 16 * t, q * RW + 16 * rt), D[rt], acc);
+            *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
+        }
+        __syncthreads();
+        {
+            f32x4 acc = zero4();
+            for (int kb = q; kb < 4; ++kb) acc = mm4(ldAT(sP, LC, 16 * q, 16 * kb), ldB(sdO, LS, 16 * kb, 0), acc);
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) acc += *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
+            *reinterpret_cast<f32x4*>(sdU + (q * 64 + lane) * 4) = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r0 = q * RW + 16 * rt;
+            f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                a1 = mm4(ldAT(sQG, LK, r0, 16 * kb), ldB(sdO, LS, 16 * kb, 0), a1);
+                a2 = mm4(ldAT(sW, LK, r0, 16 * kb), *reinterpret_cast<const f32x4*>(sdU + (kb * 64 + lane) * 4), a2);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) D[rt][e] = sGam[r0 + 4 * g + e] * D[rt][e] + a1[e] - a2[e];
+        }
+        __syncthreads();
+    }
+    if (p.gS0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = q * RW + 16 * rt + 4 * g + e;
+                p.gS0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] = D[rt][e];
+            }
+    }
+}
+
+// ================================================================ 4. state-side gradients
+// One workgroup (8 waves) per (chunk, head), streaming the value columns in
+// slices of 16: U and dU of the slice, dv, and running sums of d(Gamma o Q),
+// dW, dK_end, dP and dX (tiles owned by waves). Then dX += dW (beta o Gamma o
+// K)^T and Y = X^T dW. Outputs replace the prep block's W (d(Gamma o K) =
+// beta o Y), K_end (dK_end), Gamma o Q (its gradient), P (dP) and gamma
+// (dgamma); dX and the beta terms go to the extra block.
+template <int DK>
+struct GradSmem {
+    static constexpr int LK = DK + 4;
+    static constexpr size_t X = 0, P = X + (size_t)C * LC, W = P + (size_t)C * LC, KE = W + (size_t)C * LK;
+    static constexpr size_t S = KE + (size_t)C * LK, D = S + (size_t)DK * LS;
+    static constexpr size_t DO = D + (size_t)DK * LS, V = DO + (size_t)C * LS, U = V + (size_t)C * LS;
+    static constexpr size_t DU = U + (size_t)C * LS, BETA = DU + (size_t)C * LS, DG = BETA + C, DB = DG + DK;
+    static constexpr size_t FLOATS = DB + 4 * C;
+    static constexpr size_t BYTES = FLOATS * 4;
+};
+
+template <class TIn, int DK, bool SG>
+__global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
+    using SM = GradSmem<DK>;
+    using PL = PrepLay<DK>;
+    constexpr int LK = SM::LK, NCT = DK / 16;
+    constexpr int NT1 = 12 * NCT, NTILE = NT1 + 20, NPW = (NTILE + 7) / 8;
+    extern __shared__ __align__(16) float sm[];
+    float *sX = sm + SM::X, *sP = sm + SM::P, *sW = sm + SM::W, *sKE = sm + SM::KE, *sS = sm + SM::S, *sD = sm + SM::D;
+    float *sdO = sm + SM::DO, *sV = sm + SM::V, *sU = sm + SM::U, *sdU = sm + SM::DU, *sBeta = sm + SM::BETA;
+    float *sdg = sm + SM::DG, *sdb = sm + SM::DB;   // sdb: [4][C] beta parts (fixed-order sums)
+
+    const int H = p.H, DV = p.DV;
+    const int item = blockIdx.x;
+    const int h = item % H, gidx = launch_chunk(p.map, item / H);
+    long t0;
+    int n;
+    if (!resolve_chunk(p.map, gidx, C, t0, n)) return;
+    const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
+    const int i = lane_i(), g = lane_g();
+    const size_t base = (size_t)gidx * H + h;
+    float* pb = p.prep + base * PL::FLOATS;
+    const float* ckS = p.ck + base * 2 * DK * DV;
+    const float* ckD = ckS + (size_t)DK * DV;
+    float* ex = p.ext + base * EXT_FLOATS;
+
+    for (int x = tid; x < C * C; x += 512) {
+        sX[(x / C) * LC + x % C] = pb[PL::X + x];
+        sP[(x / C) * LC + x % C] = pb[PL::P + x];
+    }
+    for (int x = tid; x < C * DK; x += 512) {
+        sW[(x / DK) * LK + x % DK] = pb[PL::W + x];
+        sKE[(x / DK) * LK + x % DK] = pb[PL::KE + x];
+    }
+    if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
+    if (tid < DK) sdg[tid] = 0.f;
+    if (tid < 4 * C) sdb[tid] = 0.f;
+
+    f32x4 acc[NPW];
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) acc[u] = zero4();
+
+    for (int b = 0; b < DV / 16; ++b) {
+        __syncthreads();
+        for (int x = tid; x < DK * 16; x += 512) {
+            const int r = x / 16, c = x % 16;
+            sS[r * LS + c] = ckS[(size_t)r * DV + 16 * b + c];
+            sD[r * LS + c] = ckD[(size_t)r * DV + 16 * b + c];
+        }
+        for (int x = tid; x < C * 16; x += 512) {
+            const int r = x / 16, c = x % 16;
+            const size_t row = (size_t)(t0 + r) * H + h;
+            sdO[r * LS + c] = r < n ? p.dO[row * DV + 16 * b + c] : 0.f;
+            sV[r * LS + c] = r < n ? ld_in((const TIn*)p.v + row * DV + 16 * b + c) : 0.f;
+        }
+        __syncthreads();
+        if (w < 4) {   // U tile t = X (beta o V) - W S
+            const int t = w;
+            f32x4 a = zero4();
+            for (int kb = 0; kb <= t; ++kb) {
+                f32x4 bv = ldB(sV, LS, 16 * kb, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] *= sBeta[16 * kb + 4 * g + e];
+                a = mm4(ldA(sX, LC, 16 * t, 16 * kb), bv, a);
+            }
+            f32x4 ws = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NCT; ++kb) ws = mm4(ldA(sW, LK, 16 * t, 16 * kb), ldB(sS, LS, 16 * kb, 0), ws);
+            stD(sU, LS, 16 * t, 0, a - ws);
+        } else {       // dU tile t = P^T dO + K_end dS'
+            const int t = w - 4;
+            f32x4 a = zero4();
+            for (int kb = t; kb < 4; ++kb) a = mm4(ldAT(sP, LC, 16 * t, 16 * kb), ldB(sdO, LS, 16 * kb, 0), a);
+#pragma unroll
+            for (int kb = 0; kb < NCT; ++kb) a = mm4(ldA(sKE, LK, 16 * t, 16 * kb), ldB(sD, LS, 16 * kb, 0), a);
+            stD(sdU, LS, 16 * t, 0, a);
+        }
+        if (tid < DK) {
+            float sacc = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) sacc += sS[tid * LS + c] * sD[tid * LS + c];
+            sdg[tid] += sacc;
+        }
+        __syncthreads();
+        if (w < 4) {   // dv = beta o (X^T dU); beta part rowsum(V o X^T dU)
+            const int t = w;
+            f32x4 a = zero4();
+            for (int kb = t; kb < 4; ++kb) a = mm4(ldAT(sX, LC, 16 * t, 16 * kb), ldB(sdU, LS, 16 * kb, 0), a);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * t + 4 * g + e;
+                if (r < n) p.gv[((size_t)(t0 + r) * H + h) * DV + 16 * b + i] = sBeta[r] * a[e];
+                float rs = a[e] * sV[r * LS + i];
+                rs += __shfl_xor(rs, 1, 16);
+                rs += __shfl_xor(rs, 2, 16);
+                rs += __shfl_xor(rs, 4, 16);
+                rs += __shfl_xor(rs, 8, 16);
+                if (i == 0) sdb[r] += rs;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int idx = w + 8 * u;
+            if (idx >= NTILE) continue;
+            if (idx < NT1) {
+                const int kind = idx / (4 * NCT), rem = idx % (4 * NCT), t = rem / NCT, c = rem % NCT;
+                if (kind == 0) acc[u] = mm4(ldA(sdO, LS, 16 * t, 0), ldBT(sS, LS, 0, 16 * c), acc[u]);
+                else if (kind == 1) acc[u] = mm4(-ldA(sdU, LS, 16 * t, 0), ldBT(sS, LS, 0, 16 * c), acc[u]);
+                else acc[u] = mm4(ldA(sU, LS, 16 * t, 0), ldBT(sD, LS, 0, 16 * c), acc[u]);
+            } else if (idx < NT1 + 10) {
+                int R, J;
+                lower_tile(idx - NT1, R, J);
+                acc[u] = mm4(ldA(sdO, LS, 16 * R, 0), ldBT(sU, LS, 0, 16 * J), acc[u]);
+            } else {
+                int R, J;
+                lower_tile(idx - NT1 - 10, R, J);
+                f32x4 bv = ldBT(sV, LS, 0, 16 * J) * sBeta[16 * J + i];
+                acc[u] = mm4(ldA(sdU, LS, 16 * R, 0), bv, acc[u]);
+            }
+        }
+    }
+    __syncthreads();
+    // ---- write d(Gamma o Q), dK_end, dP; dW to LDS (replacing W); Gamma o K into sKE
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+        const int idx = w + 8 * u;
+        if (idx >= NTILE) continue;
+        if (idx < NT1) {
+            const int kind = idx / (4 * NCT), rem = idx % (4 * NCT), t = rem / NCT, c = rem % NCT;
+            if (kind == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pb[PL::QG + (size_t)(16 * t + 4 * g + e) * DK + 16 * c + i] = acc[u][e];
+            } else if (kind == 1) {
+                stD(sW, LK, 16 * t, 16 * c, acc[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pb[PL::KE + (size_t)(16 * t + 4 * g + e) * DK + 16 * c + i] = acc[u][e];
+            }
+        } else if (idx < NT1 + 10) {
+            int R, J;
+            lower_tile(idx - NT1, R, J);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pb[PL::P + (size_t)(16 * R + 4 * g + e) * C + 16 * J + i] = acc[u][e];
+        }
+    }
+    if (tid < DK) {   // Gamma o K (unscaled), one channel per thread
+        float gm = 1.f;
+        for (int r = 0; r < C; ++r) {
+            float kv = 0.f, av = 1.f;
+            if (r < n) {
+                const size_t row = (size_t)(t0 + r) * H + h;
+                kv = ld_in((const TIn*)p.k + row * DK + tid);
+                av = gate_at<TIn>(p, row, DK, tid, SG);
+            }
+            gm *= av;
+            sKE[r * LK + tid] = gm * kv;
+        }
+        pb[PL::GAM + tid] = sdg[tid];
+    }
+    __syncthreads();
+    // ---- dX += dW (beta o Gamma o K)^T (tiles already owned), then dX out
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+        const int idx = w + 8 * u;
+        if (idx < NT1 + 10 || idx >= NTILE) continue;
+        int R, J;
+        lower_tile(idx - NT1 - 10, R, J);
+        f32x4 a = acc[u];
+#pragma unroll
+        for (int kb = 0; kb < NCT; ++kb) {
+            const f32x4 bk = ldBT(sKE, LK, 16 * kb, 16 * J) * sBeta[16 * J + i];
+            a = mm4(ldA(sW, LK, 16 * R, 16 * kb), bk, a);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ex[(size_t)(16 * R + 4 * g + e) * C + 16 * J + i] = a[e];
+    }
+    // ---- Y = X^T dW: d(Gamma o K) = beta o Y; beta part rowsum(Gamma o K o Y).
+    // Wave w: token tile t = w % 4, channel tiles half (w / 4); each half's
+    // row sums go to their own slot, added in a fixed order.
+    {
+        const int t = w % 4, half = w / 4;
+        for (int c = half * (NCT / 2); c < (half + 1) * (NCT / 2); ++c) {
+            f32x4 a = zero4();
+            for (int kb = t; kb < 4; ++kb) a = mm4(ldAT(sX, LC, 16 * t, 16 * kb), ldB(sW, LK, 16 * kb, 16 * c), a);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * t + 4 * g + e;
+                pb[PL::W + (size_t)r * DK + 16 * c + i] = sBeta[r] * a[e];
+                float rs = a[e] * sKE[r * LK + 16 * c + i];
+                rs += __shfl_xor(rs, 1, 16);
+                rs += __shfl_xor(rs, 2, 16);
+                rs += __shfl_xor(rs, 4, 16);
+                rs += __shfl_xor(rs, 8, 16);
+                if (i == 0) sdb[(1 + half) * C + r] += rs;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < C) ex[(size_t)C * C + tid] = sdb[tid] + sdb[C + tid] + sdb[2 * C + tid];
+}
+
+// ================================================================ 5. gate-side gradients
+// One workgroup (4 waves) per (chunk, head): dA = -X^T dX X^T (strictly
+// lower), dG = Diag(beta) dA, then, per block of 16 key channels, dq, dk and
+// the gate gradient from Gamma o Q, Gamma o K, K_end, gamma and, level by
+// level of the binary split, the gated Gram matrices.
+template <int DK>
+struct GateSmem {
+    static constexpr int LB = 16 + 4;
+    static constexpr size_t X = 0, G = X + (size_t)C * LC, DX = G + (size_t)C * LC, DP = DX + (size_t)C * LC;
+    static constexpr size_t T = DP + (size_t)C * LC;
+    static constexpr size_t K = T + (size_t)C * LC, Q = K + (size_t)C * LB, A = Q + (size_t)C * LB;
+    static constexpr size_t XK = A + (size_t)C * LB, XQ = XK + (size_t)C * LB, PS = XQ + (size_t)C * LB;
+    static constexpr size_t YZ = PS + (size_t)C * LB, YP = YZ + (size_t)C * LB;
+    static constexpr size_t DQ = YP + (size_t)C * LB, DKK = DQ + (size_t)C * LB, DA = DKK + (size_t)C * LB;
+    static constexpr size_t BETA = DA + (size_t)C * LB, DB = BETA + C, DAT = DB + 4 * C;
+    static constexpr size_t FLOATS = DAT + C;
+    static constexpr size_t BYTES = FLOATS * 4;
+};
+
+template <class TIn, int DK, bool SG>
+__global__ void __launch_bounds__(256) cb_grad_gate_kernel(Params p) {
+    using SM = GateSmem<DK>;
+    using PL = PrepLay<DK>;
+    constexpr int LB = SM::LB;
+    extern __shared__ __align__(16) float sm[];
+    float *sX = sm + SM::X, *sG = sm + SM::G, *sdX = sm + SM::DX, *sdP = sm + SM::DP, *sT = sm + SM::T;
+    float *sK = sm + SM::K, *sQ = sm + SM::Q, *sA = sm + SM::A, *sXK = sm + SM::XK, *sXQ = sm + SM::XQ;
+    float *sPS = sm + SM::PS, *sYZ = sm + SM::YZ, *sYP = sm + SM::YP, *sdq = sm + SM::DQ, *sdk = sm + SM::DKK;
+    float *sda = sm + SM::DA, *sBeta = sm + SM::BETA, *sdb = sm + SM::DB, *sdat = sm + SM::DAT;
+
+    const int H = p.H;
+    const int item = blockIdx.x;
+    const int h = item % H, gidx = launch_chunk(p.map, item / H);
+    long t0;
+    int n;
+    if (!resolve_chunk(p.map, gidx, C, t0, n)) return;
+    const int tid = threadIdx.x, w = tid / WAVE;
+    const int i = lane_i(), g = lane_g();
+    const size_t base = (size_t)gidx * H + h;
+    const float* pb = p.prep + base * PL::FLOATS;
+    const float* ex = p.ext + base * EXT_FLOATS;
+
+    for (int x = tid; x < C * C; x += 256) {
+        const int r = x / C, c = x % C;
+        const bool low = (r / 16) >= (c / 16);
+        sX[r * LC + c] = pb[PL::X + x];
+        sG[r * LC + c] = pb[PL::G + x];
+        sdX[r * LC + c] = low ? ex[x] : 0.f;
+        sdP[r * LC + c] = low ? pb[PL::P + x] : 0.f;
+    }
+    if (tid < C) {
+        sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
+        sdb[tid] = ex[(size_t)C * C + tid];
+        sdat[tid] = 0.f;
+    }
+    __syncthreads();
+    // ---- T = dX X^T (full tiles)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int tt = w + 4 * u, R = tt / 4, J = tt % 4;
+        f32x4 a = zero4();
+        for (int kb = 0; kb <= min(R, J); ++kb) a = mm4(ldA(sdX, LC, 16 * R, 16 * kb), ldBT(sX, LC, 16 * kb, 16 * J), a);
+        stD(sT, LC, 16 * R, 16 * J, a);
+    }
+    __syncthreads();
+    // ---- dA = -X^T T (strictly lower), dG = Diag(beta) dA into sdX; wave R
+    // owns row tile R (every J <= R), so the beta part of each row is one sum
+    {
+        const int R = w;
+        float rowpart[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int J = 0; J <= R; ++J) {
+            f32x4 a = zero4();
+            for (int kb = R; kb < 4; ++kb) a = mm4(ldAT(sX, LC, 16 * R, 16 * kb), ldB(sT, LC, 16 * kb, 16 * J), a);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * g + e, c = 16 * J + i;
+                const float da = r > c ? -a[e] : 0.f;
+                rowpart[e] += da * sG[r * LC + c];
+                a[e] = sBeta[r] * da;
+            }
+            stD(sdX, LC, 16 * R, 16 * J, a);
+        }
+        for (int J = R + 1; J < 4; ++J) stD(sdX, LC, 16 * R, 16 * J, zero4());
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float rs = rowpart[e];
+            rs += __shfl_xor(rs, 1, 16);
+            rs += __shfl_xor(rs, 2, 16);
+            rs += __shfl_xor(rs, 4, 16);
+            rs += __shfl_xor(rs, 8, 16);
+            if (i == 0) sdb[C + 16 * R + 4 * g + e] = rs;
+        }
+    }
+    __syncthreads();
+    float* sdG = sdX;
+
+    // ---- per block of 16 key channels
+    const TIn* gk = (const TIn*)p.k;
+    const TIn* gq = (const TIn*)p.q;
+    for (int cb = 0; cb < DK / 16; ++cb) {
+        for (int x = tid; x < C * 16; x += 256) {
+            const int r = x / 16, c = x % 16, ch = 16 * cb + c;
+            float kv = 0.f, qv = 0.f, av = 1.f;
+            if (r < n) {
+                const size_t row = (size_t)(t0 + r) * H + h;
+                kv = ld_in(gk + row * DK + ch);
+                qv = ld_in(gq + row * DK + ch);
+                av = gate_at<TIn>(p, row, DK, ch, SG);
+            }
+            sK[r * LB + c] = kv;
+            sQ[r * LB + c] = qv;
+            sA[r * LB + c] = av;
+        }
+        __syncthreads();
+        // Gamma o Q, Gamma o K, K_end and gamma terms; the diagonal of P
+        if (tid < 16) {
+            const int c = tid, ch = 16 * cb + c;
+            float gm = 1.f;
+            for (int r = 0; r < C; ++r) {
+                gm *= sA[r * LB + c];
+                const float dqg = pb[PL::QG + (size_t)r * DK + ch], dgk = pb[PL::W + (size_t)r * DK + ch];
+                const float kv = sK[r * LB + c], qv = sQ[r * LB + c], dpd = sdP[r * LC + r];
+                sdq[r * LB + c] = dqg * gm + dpd * kv;
+                sdk[r * LB + c] = dgk * gm + dpd * qv;
+                sYZ[r * LB + c] = dqg * qv + dgk * kv;   // dGamma_r
+                sPS[r * LB + c] = gm;                    // Gamma_r
+            }
+            sYZ[(C - 1) * LB + c] += pb[PL::GAM + ch];   // dgamma
+            float R = 0.f;
+            for (int tau = C - 1; tau >= 0; --tau) {
+                R = sYZ[tau * LB + c] + (tau + 1 < C ? sA[(tau + 1) * LB + c] * R : 0.f);
+                sda[tau * LB + c] = (tau > 0 ? sPS[(tau - 1) * LB + c] : 1.f) * R;
+            }
+            float f = 1.f;
+            for (int j = C - 1; j >= 0; --j) {
+                const float dke = pb[PL::KE + (size_t)j * DK + ch];
+                sdk[j * LB + c] += dke * f;
+                sYP[j * LB + c] = dke * sK[j * LB + c];  // drel_end
+                sPS[j * LB + c] = f;                     // rel_end
+                f *= sA[j * LB + c];
+            }
+            float Lr = 0.f;
+            for (int tau = 0; tau < C; ++tau) {
+                sda[tau * LB + c] += sPS[tau * LB + c] * Lr;
+                Lr = sYP[tau * LB + c] + sA[tau * LB + c] * Lr;
+            }
+        }
+        __syncthreads();
+        for (int L = 0; L < 6; ++L) {
+            const int hw = level_half(L), ng = C / (2 * hw);
+            const int c = tid % 16, part = tid / 16;
+            // stage right rows k o pre, q o pre (pre in PS), left rows k o suf (suf in PS)
+            for (int gi = part; gi < ng; gi += 16) {
+                const int s0 = gi * 2 * hw, m = s0 + hw - 1;
+                float f = 1.f;
+                for (int r = m + 1; r < s0 + 2 * hw; ++r) {
+                    f *= sA[r * LB + c];
+                    sXK[r * LB + c] = sK[r * LB + c] * f;
+                    sXQ[r * LB + c] = sQ[r * LB + c] * f;
+                    sPS[r * LB + c] = f;
+                }
+                f = 1.f;
+                for (int j = m; j >= s0; --j) {
+                    sXK[j * LB + c] = sK[j * LB + c] * f;
+                    sPS[j * LB + c] = f;
+                    f *= sA[j * LB + c];
+                }
+            }
+            __syncthreads();
+            // products of the level: Y_G, Y_P (right row tiles) and Z (left row tiles)
+            if (L < 2) {
+                // outputs: 0..(NR-1) Y tiles, then Z tiles; pairs from tile_at_level
+                for (int o = w; o < 6; o += 4) {
+                    // L = 0: Y rows {2, 3} from J {0, 1}; Z rows {0, 1} from R {2, 3}
+                    // L = 1: Y rows {1, 3} from J {0, 2}; Z rows {0, 2} from R {1, 3}
+                    const int kind = o % 3;   // 0: Y_G, 1: Y_P, 2: Z
+                    const int which = o / 3;
+                    if (kind < 2) {
+                        const int R = L == 0 ? 2 + which : 1 + 2 * which;
+                        f32x4 a = zero4();
+                        for (int J = 0; J < R; ++J) {
+                            if (!tile_at_level(R, J, L)) continue;
+                            a = mm4(ldA(kind == 0 ? sdG : sdP, LC, 16 * R, 16 * J), ldB(sXK, LB, 16 * J, 0), a);
+                        }
+                        stD(kind == 0 ? sYZ : sYP, LB, 16 * R, 0, a);
+                    } else {
+                        const int J = L == 0 ? which : 2 * which;
+                        f32x4 a = zero4();
+                        for (int R = J + 1; R < 4; ++R) {
+                            if (!tile_at_level(R, J, L)) continue;
+                            a = mm4(ldAT(sdG, LC, 16 * J, 16 * R), ldB(sXK, LB, 16 * R, 0), a);
+                            a = mm4(ldAT(sdP, LC, 16 * J, 16 * R), ldB(sXQ, LB, 16 * R, 0), a);
+                        }
+                        stD(sYZ, LB, 16 * J, 0, a);
+                    }
+                }
+            } else {
+                // in-tile level: tile b = w; Y_G + Z into YZ, Y_P into YP
+                const int b = w;
+                f32x4 ag, ap, bgT, bpT;
+                ag = ldA(sdG, LC, 16 * b, 16 * b);
+                ap = ldA(sdP, LC, 16 * b, 16 * b);
+                bgT = ldAT(sdG, LC, 16 * b, 16 * b);
+                bpT = ldAT(sdP, LC, 16 * b, 16 * b);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const bool ky = sep_in(i, 4 * g + s, hw);   // A(i, k) = dG[r = i][j = k]
+                    const bool kz = sep_in(4 * g + s, i, hw);   // A(i, k) = dG[r = k][j = i]
+                    ag[s] = ky ? ag[s] : 0.f;
+                    ap[s] = ky ? ap[s] : 0.f;
+                    bgT[s] = kz ? bgT[s] : 0.f;
+                    bpT[s] = kz ? bpT[s] : 0.f;
+                }
+                const f32x4 xk = ldB(sXK, LB, 16 * b, 0), xq = ldB(sXQ, LB, 16 * b, 0);
+                f32x4 yz = mm4(ag, xk, zero4());
+                yz = mm4(bgT, xk, yz);
+                yz = mm4(bpT, xq, yz);
+                stD(sYZ, LB, 16 * b, 0, yz);
+                stD(sYP, LB, 16 * b, 0, mm4(ap, xk, zero4()));
+            }
+            __syncthreads();
+            // accumulate dq, dk and the gate gradient of this level
+            for (int gi = part; gi < ng; gi += 16) {
+                const int s0 = gi * 2 * hw, m = s0 + hw - 1, e1 = s0 + 2 * hw;
+                float R = 0.f;
+                for (int tau = e1 - 1; tau > m; --tau) {
+                    const float yz = sYZ[tau * LB + c], yp = sYP[tau * LB + c], pre = sPS[tau * LB + c];
+                    sdk[tau * LB + c] += pre * yz;
+                    sdq[tau * LB + c] += pre * yp;
+                    const float dpre = sK[tau * LB + c] * yz + sQ[tau * LB + c] * yp;
+                    R = dpre + (tau + 1 < e1 ? sA[(tau + 1) * LB + c] * R : 0.f);
+                    sda[tau * LB + c] += (tau - 1 > m ? sPS[(tau - 1) * LB + c] : 1.f) * R;
+                }
+                float Lf = 0.f;
+                for (int tau = s0; tau <= m; ++tau) {
+                    const float yz = sYZ[tau * LB + c], suf = sPS[tau * LB + c];
+                    sdk[tau * LB + c] += suf * yz;
+                    sda[tau * LB + c] += suf * Lf;
+                    Lf = sK[tau * LB + c] * yz + sA[tau * LB + c] * Lf;
+                }
+            }
+            __syncthreads();
+        }
+        // outputs of this channel block
+        for (int x = tid; x < C * 16; x += 256) {
+            const int r = x / 16, c = x % 16, ch = 16 * cb + c;
+            if (r < n) {
+                const size_t row = (size_t)(t0 + r) * H + h;
+                p.gq[row * DK + ch] = sdq[r * LB + c];
+                p.gk[row * DK + ch] = sdk[r * LB + c];
+                if (!SG) p.gg[row * DK + ch] = sda[r * LB + c];
+            }
+        }
+        if (SG && tid < C) {
+            float sacc = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) sacc += sda[tid * LB + c];
+            sdat[tid] += sacc;
+        }
+        __syncthreads();
+    }
+    if (tid < n) {
+        const size_t row = (size_t)(t0 + tid) * H + h;
+        p.gb[row] = sdb[tid] + sdb[C + tid];
+        if (SG) p.gg[row] = sdat[tid];
+    }
+}
+
+}  // namespace cb
+
+// ================================================================ host side
+
+size_t cbwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N) {
+    const long nch = chunk_count_bound(B, T, cb::C, varlen, N);
+    const size_t ib = varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0;
+    const size_t prep = (dk == 64 ? cb::PrepLay<64>::FLOATS : cb::PrepLay<128>::FLOATS);
+    const size_t per = prep + 2 * (size_t)dk * dv + cb::EXT_FLOATS;
+    return ib + (size_t)nch * H * per * 4;
+}
+
+template <class K>
+static hipError_t cb_allow_lds(K kern, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <class TIn, int DK, bool SG>
+static hipError_t launch_cbwd_t(const BwdArgs& a) {
+    using namespace cb;
+    static_assert(PrepSmem<DK>::BYTES <= 160 * 1024 && WalkSmem<DK>::BYTES <= 160 * 1024 &&
+                      GradSmem<DK>::BYTES <= 160 * 1024 && GateSmem<DK>::BYTES <= 160 * 1024,
+                  "chunkwise backward LDS");
+    const bool varlen = a.cu_seqlens != nullptr;
+    const int N = a.N;
+    unsigned char* ws = (unsigned char*)a.workspace;
+    const size_t ib = varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0;
+    const long nch = chunk_count_bound(a.B, a.T, C, varlen, N);
+    const int NC = (a.T + C - 1) / C;
+    int32_t* cstart = (int32_t*)ws;
+    ChunkMap map{a.cu_seqlens, varlen ? cstart : nullptr, a.T, N, NC, 0, NC};
+    float* prep = (float*)(ws + ib);
+    float* ck = prep + (size_t)nch * a.H * PrepLay<DK>::FLOATS;
+    float* ext = ck + (size_t)nch * a.H * 2 * DK * a.dv;
+    Params p{a.q, a.k, a.v, a.gate, a.beta, a.S0, a.dO, a.dST, a.g_q, a.g_k, a.g_v, a.g_gate, a.g_beta, a.g_S0,
+             prep, ck, ext, map, a.H, a.dv};
+    hipError_t e;
+    if (varlen) {
+        e = launch_chunk_index(a.cu_seqlens, cstart, N, C, a.stream);
+        if (e != hipSuccess) return e;
+    }
+    const unsigned items = (unsigned)(nch * a.H);
+    const unsigned walkers = (unsigned)((long)N * a.H * (a.dv / 16));
+    if (items > 0) {
+        auto k1 = cb_prep_kernel<TIn, DK, SG>;
+        if ((e = cb_allow_lds(k1, PrepSmem<DK>::BYTES)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k1, dim3(items), dim3(256), PrepSmem<DK>::BYTES, a.stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto k2 = cb_state_kernel<TIn, DK>;
+        if ((e = cb_allow_lds(k2, WalkSmem<DK>::BYTES)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k2, dim3(walkers), dim3(256), WalkSmem<DK>::BYTES, a.stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    auto k3 = cb_adjoint_kernel<DK>;
+    if ((e = cb_allow_lds(k3, WalkSmem<DK>::BYTES)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k3, dim3(walkers), dim3(256), WalkSmem<DK>::BYTES, a.stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (items > 0) {
+        auto k4 = cb_grad_state_kernel<TIn, DK, SG>;
+        if ((e = cb_allow_lds(k4, GradSmem<DK>::BYTES)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k4, dim3(items), dim3(512), GradSmem<DK>::BYTES, a.stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto k5 = cb_grad_gate_kernel<TIn, DK, SG>;
+        if ((e = cb_allow_lds(k5, GateSmem<DK>::BYTES)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k5, dim3(items), dim3(256), GateSmem<DK>::BYTES, a.stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_cbwd(const BwdArgs& a) {
+    const bool sg = a.scalar_gate;
+    if (a.dk == 64) {
+        if (a.bf16) return sg ? launch_cbwd_t<uint16_t, 64, true>(a) : launch_cbwd_t<uint16_t, 64, false>(a);
+        return sg ? launch_cbwd_t<float, 64, true>(a) : launch_cbwd_t<float, 64, false>(a);
+    }
+    if (a.bf16) return sg ? launch_cbwd_t<uint16_t, 128, true>(a) : launch_cbwd_t<uint16_t, 128, false>(a);
+    return sg ? launch_cbwd_t<float, 128, true>(a) : launch_cbwd_t<float, 128, false>(a);
+}
+
+}  // namespace kda

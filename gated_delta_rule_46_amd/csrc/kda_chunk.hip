@@ -132,42 +132,11 @@ __device__ __forceinline__ float colsum4(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// ------------------------------------------------------------------ chunk addressing
+}  // namespace kda
 
-struct ChunkMap {
-    const int32_t* cu;      // null when every sequence has length T
-    const int32_t* cstart;  // first chunk of each sequence (N+1), varlen only
-    int T, N, NC;           // NC: chunks per sequence when not varlen
-    int c0, c1;             // not varlen: this launch covers chunks [c0, c1) of every sequence
-};
+#include "kda_chunkmap.h"
 
-// Workgroup-local chunk number -> global chunk index.
-__device__ __forceinline__ int launch_chunk(const ChunkMap& m, int li) {
-    if (m.cu != nullptr) return li;
-    const int ns = m.c1 - m.c0;
-    return (li / ns) * m.NC + m.c0 + li % ns;
-}
-
-// Chunk g -> first token (flattened over batch and time) and token count.
-__device__ __forceinline__ bool resolve_chunk(const ChunkMap& m, int g, int C, long& t0, int& n) {
-    if (m.cu == nullptr) {
-        const int s = g / m.NC, c = g % m.NC;
-        t0 = (long)s * m.T + (long)c * C;
-        n = min(C, m.T - c * C);
-        return true;
-    }
-    if (g >= m.cstart[m.N]) return false;
-    int lo = 0, hi = m.N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (m.cstart[mid] <= g) lo = mid; else hi = mid - 1;
-    }
-    const int c = g - m.cstart[lo];
-    const int len = m.cu[lo + 1] - m.cu[lo];
-    t0 = (long)m.cu[lo] + (long)c * C;
-    n = min(C, len - c * C);
-    return true;
-}
+namespace kda {
 
 // cstart[s] = sum over earlier sequences of ceil(len / C); one workgroup.
 __global__ void __launch_bounds__(256) chunk_index_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ cstart,
@@ -197,6 +166,11 @@ __global__ void __launch_bounds__(256) chunk_index_kernel(const int32_t* __restr
         __syncthreads();
     }
     if (threadIdx.x == 0) cstart[0] = 0;
+}
+
+hipError_t launch_chunk_index(const int32_t* cu, int32_t* cstart, int N, int C, hipStream_t stream) {
+    hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, stream, cu, cstart, N, C);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ prep kernel

@@ -86,8 +86,14 @@ int validate_chunk_fwd(int stage, const void* q, const void* k, const void* v, c
 // hipError_t -> KDA status (KDA_EHIP records the code for kda_last_hip_error).
 int hip_to_status(hipError_t e);
 
+// Per-sequence first chunk index (cstart, N+1 entries) of packed sequences.
+hipError_t launch_chunk_index(const int32_t* cu, int32_t* cstart, int N, int C, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+// Chunkwise backward (dk 64 or 128): workspace bytes and launch.
+size_t cbwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N);
+hipError_t launch_cbwd(const BwdArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 
 }  // namespace kda

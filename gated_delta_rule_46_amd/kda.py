@@ -28,7 +28,7 @@ EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_byte
            "kda_chunk_bwd_workspace_bytes", "kda_gauge_fold", "kda_gauge_fold_workspace_bytes", "kda_chunk_fwd_gauge",
            "kda_chunk_fwd_gauge_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error",
            "kda_version", "kda_chunk_fwd_status", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_ew",
-           "kda_decode_step_ew")
+           "kda_decode_step_ew", "kda_chunk_bwd_cw", "kda_chunk_bwd_cw_workspace_bytes")
 
 
 class KDAError(RuntimeError):
@@ -59,6 +59,10 @@ def _lib():
         lib.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 9
         lib.kda_chunk_bwd.restype = i
         lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
+        lib.kda_chunk_bwd_cw.restype = i
+        lib.kda_chunk_bwd_cw.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
+        lib.kda_chunk_bwd_cw_workspace_bytes.restype = sz
+        lib.kda_chunk_bwd_cw_workspace_bytes.argtypes = [i] * 7
         lib.kda_chunk_bwd_workspace_bytes.restype = sz
         lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 7
         lib.kda_gauge_fold.restype = i
@@ -252,9 +256,13 @@ def bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, N: int = 0, va
     return int(_lib().kda_chunk_bwd_workspace_bytes(B, H, T, dk, dv, N, int(varlen)))
 
 
+def bwd_cw_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, N: int = 0, varlen: bool = False) -> int:
+    return int(_lib().kda_chunk_bwd_cw_workspace_bytes(B, H, T, dk, dv, N, int(varlen)))
+
+
 def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate_kind: Optional[int] = None,
               want_dS0: bool = True, out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-              stream=None) -> dict:
+              stream=None, chunked: bool = False) -> dict:
     """Gradient of chunk_fwd for L = sum(o * dO) + sum(S_T * dS_T). Inputs as
     for chunk_fwd; dO fp32 [B,T,H,dv]; dS_T fp32 [N,H,dk,dv] or None. Returns
     a dict of fp32 tensors dq, dk, dv, dgate, dbeta (input layouts) and dS0
@@ -282,19 +290,20 @@ def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate
                "dv": torch.empty((B, T, H, dv), **f32), "dgate": torch.empty(tuple(gate.shape), **f32),
                "dbeta": torch.empty((B, T, H), **f32),
                "dS0": torch.empty((N, H, dk, dv), **f32) if want_dS0 else None}
-    need = bwd_workspace_bytes(B, H, T, dk, dv, N, varlen)
+    need = (bwd_cw_workspace_bytes if chunked else bwd_workspace_bytes)(B, H, T, dk, dv, N, varlen)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
     st = _stream_handle(stream, device)
-    rc = _lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+    fn = _lib().kda_chunk_bwd_cw if chunked else _lib().kda_chunk_bwd
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
                               _ptr(out["dbeta"]), _ptr(out.get("dS0")), B, H, T, dk, dv, _ptr(cu_seqlens),
                               N if varlen else 0, dt, int(gate_kind), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), ctypes.c_void_p(st) if st else None)
     if rc != KDA_OK:
-        raise KDAError(rc, "kda_chunk_bwd")
+        raise KDAError(rc, "kda_chunk_bwd_cw" if chunked else "kda_chunk_bwd")
     return out
 
 

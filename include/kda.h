@@ -246,6 +246,29 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same gradient as kda_chunk_bwd (same arguments, outputs and layouts),
+ * computed chunk by chunk (the pages' chunkwise algorithm with gate-aware
+ * backpropagation for this family; Gated DeltaNet-2 blurb): per 64-token
+ * chunk the gated Gram matrices, the UT inverse X = (I + Diag(beta) G)^{-1} and
+ * W = X (beta o Gamma o K) in fp32; the state at every chunk start by a
+ * forward walk over the chunks and the adjoint at every chunk end by a
+ * reverse walk; then every chunk's gradients in parallel, all contractions on
+ * fp32 MFMA. The gate gradient uses products of gates only, so exact zero and
+ * negative gates have their ordinary derivatives. Supported: dk 64 or 128
+ * (KDA_ENOTSUP otherwise), dv in {16, 32, 64, 128}, both dtypes and gate kinds,
+ * packed sequences. Element alignment suffices for every pointer (workspace:
+ * 16 bytes). workspace: kda_chunk_bwd_cw_workspace_bytes(...) bytes (per
+ * (chunk, head) the chunk's fp32 matrices, the state and adjoint at its
+ * boundaries and the gradient intermediates); required.
+ */
+size_t kda_chunk_bwd_cw_workspace_bytes(int B, int H, int T, int dk, int dv, int N, int has_cu_seqlens);
+int kda_chunk_bwd_cw(const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                     const float* S0, const float* dO, const float* dS_T, float* grad_q, float* grad_k,
+                     float* grad_v, float* grad_gate, float* grad_beta, float* grad_S0, int B, int H, int T,
+                     int dk, int dv, const int32_t* cu_seqlens, int N, int dtype, int gate_kind,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Gauge transform of Complex KDA onto positive gates (Complex KDA summary,
  * method step 5: the cumulative gate signs are absorbed into queries and
  * keys). Per sequence, head and key channel (per sequence and head for the

@@ -1,0 +1,140 @@
+"""GPU parity of the chunkwise backward (kda_chunk_bwd_cw) against the
+oracle's gradient, with the token-form backward's metric and bar (fp32
+arithmetic on the exact input values: 1e-4 for both input dtypes)."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_46_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dgate", "dbeta", "dS0")
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_46_amd import kda as m
+    m.library()
+    return m
+
+
+def err(x, ref):
+    x = x.detach().double().cpu().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = math.sqrt(float(np.mean(ref * ref))) if ref.size else 0.0
+    d = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    return d / rms if rms > 0 else d
+
+
+def gpu_bwd(kda, w, dO, dST):
+    d = lambda t: None if t is None else t.cuda()  # noqa: E731
+    g = kda.chunk_bwd(d(w.q), d(w.k), d(w.v), d(w.gate), d(w.beta), d(dO), S0=d(w.S0), dS_T=d(dST),
+                      cu_seqlens=d(w.cu_seqlens), gate_kind=w.gate_kind, chunked=True)
+    torch.cuda.synchronize()
+    return {n: (None if g[n] is None else g[n].cpu()) for n in NAMES}
+
+
+def check(kda, w, with_dS_T=True, tol=1e-4):
+    print("case", w.name, "B", w.B, "H", w.H, "T", w.T, "dk", w.dk, "dv", w.dv, "dtype", w.q.dtype, flush=True)
+    dO, dST = inputs.cotangents(w, seed=w.T + w.dk, with_dS_T=with_dS_T)
+    g = gpu_bwd(kda, w, dO, dST)
+    r = oracle.bwd(w.q, w.k, w.v, w.gate, w.beta, dO, w.S0, dST, w.cu_seqlens, w.gate_kind)
+    errs = {n: err(g[n], r[n]) for n in NAMES}
+    print("  errors", {n: "%.2e" % e for n, e in errs.items()}, flush=True)
+    for n in NAMES:
+        assert errs[n] <= tol, (n, errs)
+    return g, r
+
+
+CASES = [
+    ("ckda", torch.bfloat16, 128, 128, 77),
+    ("kda", torch.float32, 64, 32, 130),
+    ("gdn", torch.bfloat16, 128, 64, 65),
+    ("ckda", torch.float32, 128, 16, 200),
+    ("kda", torch.bfloat16, 64, 128, 8),
+    ("gdn", torch.float32, 64, 64, 129),
+]
+
+
+@pytest.mark.parametrize("gate,dtype,dk,dv,T", CASES)
+def test_cbwd_small_parity(kda, gate, dtype, dk, dv, T):
+    w = inputs.make_forward("cbwd_%s" % gate, B=2, H=3, T=T, dk=dk, dv=dv, dtype=dtype, gate=gate, gate_mu=2.0,
+                            seed=T + dv, s0_std=0.3)
+    check(kda, w)
+
+
+def test_cbwd_varlen_empty_and_signed_zeros(kda):
+    w = inputs.make_forward("cbwd_varlen", B=1, H=2, T=0, dk=64, dv=64, dtype=torch.float32, gate="ckda",
+                            lengths=[37, 0, 1, 150, 64], s0_std=0.2, seed=6)
+    w = dataclasses.replace(w, gate=inputs.signed_zero_gates(w.gate, seed=4))
+    g, r = check(kda, w)
+    dO, dST = inputs.cotangents(w, seed=w.T + w.dk)
+    np.testing.assert_array_equal(g["dS0"][1].numpy(), dST[1].numpy())
+
+
+def test_cbwd_no_state_inputs(kda):
+    w = inputs.make_forward("cbwd_nostate", B=1, H=2, T=100, dk=128, dv=32, dtype=torch.bfloat16, gate="ckda", seed=9)
+    check(kda, w, with_dS_T=False)
+
+
+def test_cbwd_zero_tokens(kda):
+    w = inputs.make_forward("cbwd_t0", B=2, H=2, T=0, dk=64, dv=32, dtype=torch.float32, gate="kda", seed=2,
+                            s0_std=0.1)
+    dO, dST = inputs.cotangents(w, seed=1)
+    g = gpu_bwd(kda, w, dO, dST)
+    np.testing.assert_array_equal(g["dS0"].numpy(), dST.numpy())
+
+
+def test_cbwd_full_size_every_pair(kda):
+    """The Complex KDA workload (B=2, H=16, T=8192, d=128, bf16); the oracle
+    recomputes every (sequence, head) pair, each checked on its own."""
+    w = inputs.ckda_fwd(seed=0)
+    print("case full ckda B2 H16 T8192, every pair", flush=True)
+    dO, dST = inputs.cotangents(w, seed=0)
+    g = gpu_bwd(kda, w, dO, dST)
+    r = oracle.bwd(w.q, w.k, w.v, w.gate, w.beta, dO, None, dST, None, w.gate_kind)
+    errs = {n: err(g[n], r[n]) for n in NAMES}
+    worst = {n: 0.0 for n in NAMES}
+    for b in range(w.B):
+        for h in range(w.H):
+            for n in NAMES:
+                x = g[n][b, h] if n == "dS0" else g[n][b, :, h]
+                ref = r[n][b, h] if n == "dS0" else r[n][b, :, h]
+                worst[n] = max(worst[n], err(x, ref))
+    print("  global", {n: "%.2e" % e for n, e in errs.items()}, flush=True)
+    print("  worst pair", {n: "%.2e" % e for n, e in worst.items()}, flush=True)
+    for n in NAMES:
+        assert errs[n] <= 1e-3 and worst[n] <= 1e-3, (n, errs, worst)
+
+
+def test_cbwd_full_size_gdn_varlen(kda):
+    """GDN scalar gate, eight packed sequences, H=32, T=110,440 (the varlen
+    workload) with dS_T; every (sequence, head) pair against the oracle."""
+    w = inputs.gdn_varlen()
+    print("case full gdn varlen H32 T110440", flush=True)
+    dO, dST = inputs.cotangents(w, seed=0)
+    g = gpu_bwd(kda, w, dO, dST)
+    r = oracle.bwd(w.q, w.k, w.v, w.gate, w.beta, dO, None, dST, w.cu_seqlens, w.gate_kind)
+    errs = {n: err(g[n], r[n]) for n in NAMES}
+    cu = w.cu_seqlens.tolist()
+    worst = {n: 0.0 for n in NAMES}
+    for s in range(w.n_seqs):
+        a, z = cu[s], cu[s + 1]
+        for h in range(w.H):
+            for n in NAMES:
+                if n == "dS0":
+                    x, ref = g[n][s, h], r[n][s, h]
+                else:
+                    x, ref = g[n][0, a:z, h], r[n][0, a:z, h]
+                worst[n] = max(worst[n], err(x, ref))
+    print("  global", {n: "%.2e" % e for n, e in errs.items()}, flush=True)
+    print("  worst pair", {n: "%.2e" % e for n, e in worst.items()}, flush=True)
+    for n in NAMES:
+        assert errs[n] <= 1e-3 and worst[n] <= 1e-3, (n, errs, worst)
