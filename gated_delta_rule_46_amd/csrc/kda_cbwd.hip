@@ -370,22 +370,17 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(Params p) {
 // One workgroup (4 waves) per (sequence, head, 16 value columns). Wave q keeps
 // state rows q dk/4 .. (q+1) dk/4 - 1 of the slice as D tiles. Per chunk:
 // store S; partial W S over own rows (to LDS); U = X (beta o V) - W S for
-// token tile q; S <- Diag(gamma) S + K_end^T U for own rows.
+// token tile q; S <- Diag(gamma) S + K_end^T U for own rows. The chunk's
+// operands go from global memory straight into registers, one chunk ahead.
 template <int DK>
 struct WalkSmem {
-    static constexpr int LK = DK + 4;
-    static constexpr size_t M1 = 0, M2 = M1 + (size_t)C * LK, M3 = M2 + (size_t)C * LK;
-    static constexpr size_t SQ = M3 + (size_t)C * LK;           // C x C (X or P)
-    static constexpr size_t VS = SQ + (size_t)C * LC;            // C x 16 slice (v or dO)
-    static constexpr size_t BETA = VS + (size_t)C * LS;
-    static constexpr size_t GAM = BETA + C;
-    static constexpr size_t PART = GAM + DK;                     // [4 waves][4 tiles][64 lanes][4]
-    static constexpr size_t UT = PART + 4 * 4 * 256;             // [4 tiles][64 lanes][4]
+    static constexpr size_t PART = 0;                 // [4 waves][4 tiles][64 lanes][4]
+    static constexpr size_t UT = PART + 4 * 4 * 256;  // [4 tiles][64 lanes][4]
     static constexpr size_t FLOATS = UT + 4 * 256;
     static constexpr size_t BYTES = FLOATS * 4;
 };
 
-__device__ __forceinline__ void seq_range(const ChunkMap& m, int s, int C_, long& bos, long& eos, int& cs, int& ce) {
+__device__ __forceinline__ void seq_range(const ChunkMap& m, int s, long& bos, long& eos, int& cs, int& ce) {
     if (m.cu == nullptr) {
         bos = (long)s * m.T;
         eos = (long)(s + 1) * m.T;
@@ -399,14 +394,64 @@ __device__ __forceinline__ void seq_range(const ChunkMap& m, int s, int C_, long
     }
 }
 
+// Operands of one chunk for the forward walk (wave q, own rows q dk/4..).
+template <int DK>
+struct StateOps {
+    static constexpr int RT = DK / 64;
+    f32x4 w[4][RT];    // W[16t + i][own channels]: A operand over own channels
+    f32x4 x[4];        // X[16q + i][16kb..]: A operand over tokens
+    f32x4 v[4];        // beta o V (K = tokens): B operand
+    f32x4 ke[RT][4];   // K_end^T[own rows][16kb..]: A operand over tokens
+    f32x4 gm[RT];      // gamma of own rows
+};
+
+template <class TIn, int DK>
+__device__ __forceinline__ void load_state_ops(StateOps<DK>& o, const Params& p, int gi, int cs, long bos, long eos,
+                                               int h, int sl, int q) {
+    using PL = PrepLay<DK>;
+    constexpr int RW = DK / 4, RT = DK / 64;
+    const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
+    const long t0 = bos + (long)(gi - cs) * C;
+    const int n = (int)min((long)C, eos - t0);
+    const float* pb = p.prep + ((size_t)gi * H + h) * PL::FLOATS;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            o.w[t][rt] = *reinterpret_cast<const f32x4*>(pb + PL::W + (size_t)(16 * t + i) * DK + q * RW + 16 * rt + 4 * g);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        o.x[kb] = kb <= q ? *reinterpret_cast<const f32x4*>(pb + PL::X + (size_t)(16 * q + i) * C + 16 * kb + 4 * g) : zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int tok = 16 * kb + 4 * g + s;
+            float val = 0.f;
+            if (tok < n) {
+                const size_t row = (size_t)(t0 + tok) * H + h;
+                val = ld_in((const TIn*)p.beta + row) * ld_in((const TIn*)p.v + row * DV + 16 * sl + i);
+            }
+            o.v[kb][s] = val;
+        }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) o.ke[rt][kb][s] = pb[PL::KE + (size_t)(16 * kb + 4 * g + s) * DK + q * RW + 16 * rt + i];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.gm[rt][e] = pb[PL::GAM + q * RW + 16 * rt + 4 * g + e];
+}
+
 template <class TIn, int DK>
 __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
     using SM = WalkSmem<DK>;
-    using PL = PrepLay<DK>;
-    constexpr int LK = SM::LK, RW = DK / 4, RT = RW / 16;
+    constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
-    float *sW = sm + SM::M1, *sKE = sm + SM::M2, *sX = sm + SM::SQ, *sV = sm + SM::VS;
-    float *sBeta = sm + SM::BETA, *sGam = sm + SM::GAM, *sPart = sm + SM::PART, *sU = sm + SM::UT;
+    float *sPart = sm + SM::PART, *sU = sm + SM::UT;
 
     const int H = p.H, DV = p.DV, NSL = DV / 16;
     const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -415,7 +460,7 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
     const int i = lane_i(), g = lane_g();
     long bos, eos;
     int cs, ce;
-    seq_range(p.map, s, C, bos, eos, cs, ce);
+    seq_range(p.map, s, bos, eos, cs, ce);
 
     f32x4 S[RT];
 #pragma unroll
@@ -425,47 +470,30 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
             const int row = q * RW + 16 * rt + 4 * g + e;
             S[rt][e] = p.S0 ? p.S0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
         }
+    StateOps<DK> cur, nxt;
+    if (cs < ce) load_state_ops<TIn, DK>(cur, p, cs, cs, bos, eos, h, sl, q);
     for (int gi = cs; gi < ce; ++gi) {
-        const long t0 = bos + (long)(gi - cs) * C;
-        const int n = (int)min((long)C, eos - t0);
-        const size_t base = (size_t)gi * H + h;
-        float* ckS = p.ck + base * 2 * DK * DV;
+        if (gi + 1 < ce) load_state_ops<TIn, DK>(nxt, p, gi + 1, cs, bos, eos, h, sl, q);
+        float* ckS = p.ck + ((size_t)gi * H + h) * 2 * DK * DV;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) ckS[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * sl + i] = S[rt][e];
-        const float* pb = p.prep + base * PL::FLOATS;
-        for (int x = tid; x < C * DK; x += 256) {
-            const int r = x / DK, c = x % DK;
-            sW[r * LK + c] = pb[PL::W + x];
-            sKE[r * LK + c] = pb[PL::KE + x];
-        }
-        for (int x = tid; x < C * C; x += 256) sX[(x / C) * LC + x % C] = pb[PL::X + x];
-        for (int x = tid; x < C * 16; x += 256) {
-            const int r = x / 16, c = x % 16;
-            sV[r * LS + c] = r < n ? ld_in((const TIn*)p.v + ((size_t)(t0 + r) * H + h) * DV + 16 * sl + c) : 0.f;
-        }
-        if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
-        if (tid < DK) sGam[tid] = pb[PL::GAM + tid];
-        __syncthreads();
         // partial W S over own rows, every token tile
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc = mm4(ldA(sW, LK, 16 * t, q * RW + 16 * rt), S[rt], acc);
+            for (int rt = 0; rt < RT; ++rt) acc = mm4(cur.w[t][rt], S[rt], acc);
             *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
         }
         __syncthreads();
         // U tile q = X (beta o V) - W S
         {
             f32x4 acc = zero4();
-            for (int kb = 0; kb <= q; ++kb) {
-                f32x4 b = ldB(sV, LS, 16 * kb, 0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) b[e] *= sBeta[16 * kb + 4 * g + e];
-                acc = mm4(ldA(sX, LC, 16 * q, 16 * kb), b, acc);
-            }
+            for (int kb = 0; kb < 4; ++kb)
+                if (kb <= q) acc = mm4(cur.x[kb], cur.v[kb], acc);
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) acc -= *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
             *reinterpret_cast<f32x4*>(sU + (q * 64 + lane) * 4) = acc;
@@ -476,27 +504,73 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                acc = mm4(ldAT(sKE, LK, q * RW + 16 * rt, 16 * kb), *reinterpret_cast<const f32x4*>(sU + (kb * 64 + lane) * 4), acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[rt][e] = sGam[q * RW + 16 * rt + 4 * g + e] * S[rt][e] + acc[e];
+            for (int kb = 0; kb < 4; ++kb) acc = mm4(cur.ke[rt][kb], *reinterpret_cast<const f32x4*>(sU + (kb * 64 + lane) * 4), acc);
+            S[rt] = cur.gm[rt] * S[rt] + acc;
         }
-        __syncthreads();
+        cur = nxt;
     }
 }
 
 // ================================================================ 3. adjoint at chunk ends
 // Same layout, chunks in reverse: store dS'; partial K_end dS' over own rows;
 // dU = P^T dO + K_end dS' for token tile q; dS = Diag(gamma) dS' +
-// (Gamma o Q)^T dO - W^T dU for own rows.
+// (Gamma o Q)^T dO - W^T dU for own rows. Operands straight into registers,
+// one chunk ahead.
+template <int DK>
+struct AdjOps {
+    static constexpr int RT = DK / 64;
+    f32x4 ke[4][RT];   // K_end[16t + i][own channels]: A operand over own channels
+    f32x4 pt[4];       // P^T[16q + i][16kb..] = P[16kb + ..][16q + i]: A operand over tokens
+    f32x4 d[4];        // dO (K = tokens): B operand
+    f32x4 qg[RT][4];   // (Gamma o Q)^T[own rows][16kb..]
+    f32x4 wt[RT][4];   // W^T[own rows][16kb..]
+    f32x4 gm[RT];
+};
+
+template <int DK>
+__device__ __forceinline__ void load_adj_ops(AdjOps<DK>& o, const Params& p, int gi, int cs, long bos, long eos, int h,
+                                             int sl, int q) {
+    using PL = PrepLay<DK>;
+    constexpr int RW = DK / 4, RT = DK / 64;
+    const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
+    const long t0 = bos + (long)(gi - cs) * C;
+    const int n = (int)min((long)C, eos - t0);
+    const float* pb = p.prep + ((size_t)gi * H + h) * PL::FLOATS;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            o.ke[t][rt] = *reinterpret_cast<const f32x4*>(pb + PL::KE + (size_t)(16 * t + i) * DK + q * RW + 16 * rt + 4 * g);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            o.pt[kb][s] = kb >= q ? pb[PL::P + (size_t)(16 * kb + 4 * g + s) * C + 16 * q + i] : 0.f;
+            const int tok = 16 * kb + 4 * g + s;
+            o.d[kb][s] = tok < n ? p.dO[((size_t)(t0 + tok) * H + h) * DV + 16 * sl + i] : 0.f;
+        }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const size_t off = (size_t)(16 * kb + 4 * g + s) * DK + q * RW + 16 * rt + i;
+                o.qg[rt][kb][s] = pb[PL::QG + off];
+                o.wt[rt][kb][s] = pb[PL::W + off];
+            }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.gm[rt][e] = pb[PL::GAM + q * RW + 16 * rt + 4 * g + e];
+}
+
 template <int DK>
 __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
     using SM = WalkSmem<DK>;
-    using PL = PrepLay<DK>;
-    constexpr int LK = SM::LK, RW = DK / 4, RT = RW / 16;
+    constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
-    float *sKE = sm + SM::M1, *sQG = sm + SM::M2, *sW = sm + SM::M3, *sP = sm + SM::SQ, *sdO = sm + SM::VS;
-    float *sGam = sm + SM::GAM, *sPart = sm + SM::PART, *sdU = sm + SM::UT;
+    float *sPart = sm + SM::PART, *sdU = sm + SM::UT;
 
     const int H = p.H, DV = p.DV, NSL = DV / 16;
     const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -505,7 +579,7 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
     const int i = lane_i(), g = lane_g();
     long bos, eos;
     int cs, ce;
-    seq_range(p.map, s, C, bos, eos, cs, ce);
+    seq_range(p.map, s, bos, eos, cs, ce);
 
     f32x4 D[RT];
 #pragma unroll
@@ -515,40 +589,28 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
             const int row = q * RW + 16 * rt + 4 * g + e;
             D[rt][e] = p.dST ? p.dST[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
         }
+    AdjOps<DK> cur, nxt;
+    if (cs < ce) load_adj_ops<DK>(cur, p, ce - 1, cs, bos, eos, h, sl, q);
     for (int gi = ce - 1; gi >= cs; --gi) {
-        const long t0 = bos + (long)(gi - cs) * C;
-        const int n = (int)min((long)C, eos - t0);
-        const size_t base = (size_t)gi * H + h;
-        float* ckD = p.ck + base * 2 * DK * DV + (size_t)DK * DV;
+        if (gi - 1 >= cs) load_adj_ops<DK>(nxt, p, gi - 1, cs, bos, eos, h, sl, q);
+        float* ckD = p.ck + ((size_t)gi * H + h) * 2 * DK * DV + (size_t)DK * DV;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) ckD[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * sl + i] = D[rt][e];
-        const float* pb = p.prep + base * PL::FLOATS;
-        for (int x = tid; x < C * DK; x += 256) {
-            const int r = x / DK, c = x % DK;
-            sKE[r * LK + c] = pb[PL::KE + x];
-            sQG[r * LK + c] = pb[PL::QG + x];
-            sW[r * LK + c] = pb[PL::W + x];
-        }
-        for (int x = tid; x < C * C; x += 256) sP[(x / C) * LC + x % C] = pb[PL::P + x];
-        for (int x = tid; x < C * 16; x += 256) {
-            const int r = x / 16, c = x % 16;
-            sdO[r * LS + c] = r < n ? p.dO[((size_t)(t0 + r) * H + h) * DV + 16 * sl + c] : 0.f;
-        }
-        if (tid < DK) sGam[tid] = pb[PL::GAM + tid];
-        __syncthreads();
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc = mm4(ldA(sKE, LK, 16 * t, q * RW + 16 * rt), D[rt], acc);
+            for (int rt = 0; rt < RT; ++rt) acc = mm4(cur.ke[t][rt], D[rt], acc);
             *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
         }
         __syncthreads();
         {
             f32x4 acc = zero4();
-            for (int kb = q; kb < 4; ++kb) acc = mm4(ldAT(sP, LC, 16 * q, 16 * kb), ldB(sdO, LS, 16 * kb, 0), acc);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                if (kb >= q) acc = mm4(cur.pt[kb], cur.d[kb], acc);
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) acc += *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
             *reinterpret_cast<f32x4*>(sdU + (q * 64 + lane) * 4) = acc;
@@ -556,17 +618,15 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
         __syncthreads();
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const int r0 = q * RW + 16 * rt;
             f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                a1 = mm4(ldAT(sQG, LK, r0, 16 * kb), ldB(sdO, LS, 16 * kb, 0), a1);
-                a2 = mm4(ldAT(sW, LK, r0, 16 * kb), *reinterpret_cast<const f32x4*>(sdU + (kb * 64 + lane) * 4), a2);
+                a1 = mm4(cur.qg[rt][kb], cur.d[kb], a1);
+                a2 = mm4(cur.wt[rt][kb], *reinterpret_cast<const f32x4*>(sdU + (kb * 64 + lane) * 4), a2);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) D[rt][e] = sGam[r0 + 4 * g + e] * D[rt][e] + a1[e] - a2[e];
+            D[rt] = cur.gm[rt] * D[rt] + a1 - a2;
         }
-        __syncthreads();
+        cur = nxt;
     }
     if (p.gS0) {
 #pragma unroll
@@ -595,6 +655,7 @@ struct GradSmem {
     static constexpr size_t DU = U + (size_t)C * LS, BETA = DU + (size_t)C * LS, DG = BETA + C, DB = DG + DK;
     static constexpr size_t FLOATS = DB + 4 * C;
     static constexpr size_t BYTES = FLOATS * 4;
+    static_assert(BETA - S >= (size_t)C * DK, "alpha staging fits the value-slice buffers");
 };
 
 template <class TIn, int DK, bool SG>
@@ -622,13 +683,15 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     const float* ckD = ckS + (size_t)DK * DV;
     float* ex = p.ext + base * EXT_FLOATS;
 
-    for (int x = tid; x < C * C; x += 512) {
-        sX[(x / C) * LC + x % C] = pb[PL::X + x];
-        sP[(x / C) * LC + x % C] = pb[PL::P + x];
+    for (int x = tid; x < C * C / 4; x += 512) {
+        const int r = x / (C / 4), c = 4 * (x % (C / 4));
+        *reinterpret_cast<f32x4*>(sX + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::X + 4 * x);
+        *reinterpret_cast<f32x4*>(sP + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::P + 4 * x);
     }
-    for (int x = tid; x < C * DK; x += 512) {
-        sW[(x / DK) * LK + x % DK] = pb[PL::W + x];
-        sKE[(x / DK) * LK + x % DK] = pb[PL::KE + x];
+    for (int x = tid; x < C * DK / 4; x += 512) {
+        const int r = x / (DK / 4), c = 4 * (x % (DK / 4));
+        *reinterpret_cast<f32x4*>(sW + r * LK + c) = *reinterpret_cast<const f32x4*>(pb + PL::W + 4 * x);
+        *reinterpret_cast<f32x4*>(sKE + r * LK + c) = *reinterpret_cast<const f32x4*>(pb + PL::KE + 4 * x);
     }
     if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
     if (tid < DK) sdg[tid] = 0.f;
@@ -640,10 +703,10 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
 
     for (int b = 0; b < DV / 16; ++b) {
         __syncthreads();
-        for (int x = tid; x < DK * 16; x += 512) {
-            const int r = x / 16, c = x % 16;
-            sS[r * LS + c] = ckS[(size_t)r * DV + 16 * b + c];
-            sD[r * LS + c] = ckD[(size_t)r * DV + 16 * b + c];
+        for (int x = tid; x < DK * 4; x += 512) {
+            const int r = x / 4, c = 4 * (x % 4);
+            *reinterpret_cast<f32x4*>(sS + r * LS + c) = *reinterpret_cast<const f32x4*>(ckS + (size_t)r * DV + 16 * b + c);
+            *reinterpret_cast<f32x4*>(sD + r * LS + c) = *reinterpret_cast<const f32x4*>(ckD + (size_t)r * DV + 16 * b + c);
         }
         for (int x = tid; x < C * 16; x += 512) {
             const int r = x / 16, c = x % 16;
@@ -741,19 +804,29 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
             for (int e = 0; e < 4; ++e) pb[PL::P + (size_t)(16 * R + 4 * g + e) * C + 16 * J + i] = acc[u][e];
         }
     }
-    if (tid < DK) {   // Gamma o K (unscaled), one channel per thread
-        float gm = 1.f;
-        for (int r = 0; r < C; ++r) {
+    {   // k into sKE, alpha into the (now free) value-slice buffers, then Gamma o K in place
+        float* sAl = sm + SM::S;   // C x DK floats fit in S .. DU
+        for (int x = tid; x < C * DK; x += 512) {
+            const int r = x / DK, c = x % DK;
             float kv = 0.f, av = 1.f;
             if (r < n) {
                 const size_t row = (size_t)(t0 + r) * H + h;
-                kv = ld_in((const TIn*)p.k + row * DK + tid);
-                av = gate_at<TIn>(p, row, DK, tid, SG);
+                kv = ld_in((const TIn*)p.k + row * DK + c);
+                av = gate_at<TIn>(p, row, DK, c, SG);
             }
-            gm *= av;
-            sKE[r * LK + tid] = gm * kv;
+            sKE[r * LK + c] = kv;
+            sAl[x] = av;
         }
-        pb[PL::GAM + tid] = sdg[tid];
+        __syncthreads();
+        if (tid < DK) {
+            float gm = 1.f;
+#pragma unroll 16
+            for (int r = 0; r < C; ++r) {
+                gm *= sAl[r * DK + tid];
+                sKE[r * LK + tid] *= gm;
+            }
+            pb[PL::GAM + tid] = sdg[tid];
+        }
     }
     __syncthreads();
     // ---- dX += dW (beta o Gamma o K)^T (tiles already owned), then dX out
@@ -798,34 +871,254 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
 }
 
 // ================================================================ 5. gate-side gradients
-// One workgroup (4 waves) per (chunk, head): dA = -X^T dX X^T (strictly
-// lower), dG = Diag(beta) dA, then, per block of 16 key channels, dq, dk and
-// the gate gradient from Gamma o Q, Gamma o K, K_end, gamma and, level by
-// level of the binary split, the gated Gram matrices.
+// One workgroup (4 waves) per (chunk, head). First dA = -X^T dX X^T (strictly
+// lower) and dG = Diag(beta) dA on MFMA; then, per block of 32 key channels,
+// dq, dk and the gate gradient from Gamma o Q, Gamma o K, K_end, gamma and,
+// level by level of the binary split, the gated Gram matrices.
+//
+// In the channel phase thread (c, part) owns channel c of the block and the
+// 8 rows 8 part .. 8 part + 7 of the chunk, in registers. Every gate scan
+// (prefix products, the reverse and forward affine scans of the adjoint) runs
+// as a local scan over those 8 rows plus a carry composed from the summaries
+// of the other row parts, exchanged through a small LDS table; only the
+// operands and results of the level products go through LDS. The C x C
+// buffers of the first phase are reused for the channel phase, which keeps
+// the workgroup under 80 KB of LDS (two per compute unit).
 template <int DK>
 struct GateSmem {
-    static constexpr int LB = 16 + 4;
-    static constexpr size_t X = 0, G = X + (size_t)C * LC, DX = G + (size_t)C * LC, DP = DX + (size_t)C * LC;
-    static constexpr size_t T = DP + (size_t)C * LC;
-    static constexpr size_t K = T + (size_t)C * LC, Q = K + (size_t)C * LB, A = Q + (size_t)C * LB;
-    static constexpr size_t XK = A + (size_t)C * LB, XQ = XK + (size_t)C * LB, PS = XQ + (size_t)C * LB;
-    static constexpr size_t YZ = PS + (size_t)C * LB, YP = YZ + (size_t)C * LB;
-    static constexpr size_t DQ = YP + (size_t)C * LB, DKK = DQ + (size_t)C * LB, DA = DKK + (size_t)C * LB;
-    static constexpr size_t BETA = DA + (size_t)C * LB, DB = BETA + C, DAT = DB + 4 * C;
+    static constexpr int CB = 32, LB = CB + 4, NP = 8;
+    // channel phase: carry tables [part][channel], the level operands XK, XQ
+    // and products YZ, YP, dP, dG -- everything a thread addresses per row
+    // sits below 64 KB, in reach of one base register
+    static constexpr size_t CM = 0, CL = CM + NP * CB, CR = CL + NP * CB, CV = CR + NP * CB;
+    static constexpr size_t XK = CV + NP * CB, XQ = XK + (size_t)C * LB, YZ = XQ + (size_t)C * LB;
+    static constexpr size_t YP = YZ + (size_t)C * LB, DP = YP + (size_t)C * LB, DG = DP + (size_t)C * LC;
+    // phase 1: X, G and T = dX X^T below dG (dX is held in the dG buffer)
+    static constexpr size_t X = 0, G = X + (size_t)C * LC, T = G + (size_t)C * LC;
+    static_assert(T + (size_t)C * LC <= DG, "phase-1 buffers overlap dG");
+    static constexpr size_t BETA = DG + (size_t)C * LC, DB = BETA + C, DAT = DB + 2 * C;
     static constexpr size_t FLOATS = DAT + C;
     static constexpr size_t BYTES = FLOATS * 4;
+    static_assert(DG * 4 <= 65536, "per-row arrays beyond the ds offset range");
 };
 
+// Products of level L (half width 32 >> L) for the two 16-channel column
+// tiles of the block: Y_G = dG_L XK and Y_P = dP_L XK on right row tiles,
+// Z = dG_L^T XK + dP_L^T XQ on left row tiles (Y_G + Z share YZ).
+template <int L, int LB>
+__device__ __forceinline__ void gate_products(int w, const float* sdG, const float* sdP, const float* sXK,
+                                             const float* sXQ, float* sYZ, float* sYP) {
+    constexpr int HW = 32 >> L;
+    const int i = lane_i(), g = lane_g();
+    if constexpr (L < 2) {
+        // L = 0: Y rows {2, 3} from J {0, 1}; Z rows {0, 1} from R {2, 3}
+        // L = 1: Y rows {1, 3} from J {0, 2}; Z rows {0, 2} from R {1, 3}
+        for (int job = w; job < 12; job += 4) {
+            const int o = job / 2, ct = job % 2, kind = o % 3, which = o / 3;   // kind 0: Y_G, 1: Y_P, 2: Z
+            if (kind < 2) {
+                const int R = L == 0 ? 2 + which : 1 + 2 * which;
+                const float* M = kind == 0 ? sdG : sdP;
+                f32x4 a = zero4();
+                for (int J = 0; J < R; ++J) {
+                    if (!tile_at_level(R, J, L)) continue;
+                    a = mm4(ldA(M, LC, 16 * R, 16 * J), ldB(sXK, LB, 16 * J, 16 * ct), a);
+                }
+                stD(kind == 0 ? sYZ : sYP, LB, 16 * R, 16 * ct, a);
+            } else {
+                const int J = L == 0 ? which : 2 * which;
+                f32x4 a = zero4();
+                for (int R = J + 1; R < 4; ++R) {
+                    if (!tile_at_level(R, J, L)) continue;
+                    a = mm4(ldAT(sdG, LC, 16 * J, 16 * R), ldB(sXK, LB, 16 * R, 16 * ct), a);
+                    a = mm4(ldAT(sdP, LC, 16 * J, 16 * R), ldB(sXQ, LB, 16 * R, 16 * ct), a);
+                }
+                stD(sYZ, LB, 16 * J, 16 * ct, a);
+            }
+        }
+    } else {
+        // in-tile level: wave w owns diagonal tile w
+        const int b = w;
+        f32x4 ag = ldA(sdG, LC, 16 * b, 16 * b), ap = ldA(sdP, LC, 16 * b, 16 * b);
+        f32x4 bgT = ldAT(sdG, LC, 16 * b, 16 * b), bpT = ldAT(sdP, LC, 16 * b, 16 * b);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bool ky = sep_in(i, 4 * g + s, HW);   // A(i, k) = dG[r = i][j = k]
+            const bool kz = sep_in(4 * g + s, i, HW);   // A(i, k) = dG[r = k][j = i]
+            ag[s] = ky ? ag[s] : 0.f;
+            ap[s] = ky ? ap[s] : 0.f;
+            bgT[s] = kz ? bgT[s] : 0.f;
+            bpT[s] = kz ? bpT[s] : 0.f;
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const f32x4 xk = ldB(sXK, LB, 16 * b, 16 * ct), xq = ldB(sXQ, LB, 16 * b, 16 * ct);
+            f32x4 yz = mm4(ag, xk, zero4());
+            yz = mm4(bgT, xk, yz);
+            yz = mm4(bpT, xq, yz);
+            stD(sYZ, LB, 16 * b, 16 * ct, yz);
+            stD(sYP, LB, 16 * b, 16 * ct, mm4(ap, xk, zero4()));
+        }
+    }
+}
+
+// Registers of thread (c, part) in the channel phase: gates a, keys k and
+// queries q of its 8 rows and the gradients accumulated for them.
+struct GateRegs {
+    float a[8], k[8], q[8], dq[8], dk[8], da[8];
+};
+
+// Inclusive prefix (lp) and exclusive suffix (ml) products of a thread's 8 gates.
+__device__ __forceinline__ void local_products(const float* a, float* lp, float* ml) {
+    float f = 1.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        f *= a[j];
+        lp[j] = f;
+    }
+    f = 1.f;
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+        ml[j] = f;
+        f *= a[j];
+    }
+}
+
+// One level of the binary split, half width HW = 32 >> L. Right rows of a
+// group (its second half) carry pre = product of the gates from the middle
+// up to the row, left rows suf = product of the gates after the row up to
+// the middle. With HW >= 8 a half is a whole number of row parts and pre/suf
+// come from the part products in CM; with HW >= 16 the adjoint scans of a
+// half also cross row parts and take a carry through the CV table.
+template <int L, int LB, int CB>
+__device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, float* sXK, float* sXQ, float* sYZ,
+                                          float* sYP, float* sCV, const float* sCM, const float* sdG,
+                                          const float* sdP) {
+    constexpr int HW = 32 >> L;
+    const int r0 = 8 * part;
+    float ps[8];
+    float lp[8], ml[8];
+    local_products(x.a, lp, ml);
+    bool rt = false;    // HW >= 8: this part lies in a right half
+    float sp = 1.f;     // HW >= 8: product of the gates of the earlier parts of the same half
+    int hlo = 0, hhi = 0;
+    if constexpr (HW >= 8) {
+        constexpr int SPS = HW / 8;
+        hlo = part / SPS * SPS;
+        hhi = hlo + SPS;
+        rt = (part / SPS) & 1;
+        float ss = 1.f;
+        for (int qq = hlo; qq < part; ++qq) sp *= sCM[qq * CB + c];
+        for (int qq = part + 1; qq < hhi; ++qq) ss *= sCM[qq * CB + c];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ps[j] = rt ? sp * lp[j] : ml[j] * ss;
+    } else {
+#pragma unroll
+        for (int s0 = 0; s0 < 8; s0 += 2 * HW) {
+            float f = 1.f;
+#pragma unroll
+            for (int u = 0; u < HW; ++u) {
+                f *= x.a[s0 + HW + u];
+                ps[s0 + HW + u] = f;
+            }
+            f = 1.f;
+#pragma unroll
+            for (int u = 0; u < HW; ++u) {
+                ps[s0 + HW - 1 - u] = f;
+                f *= x.a[s0 + HW - 1 - u];
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        sXK[(r0 + j) * LB + c] = x.k[j] * ps[j];
+        sXQ[(r0 + j) * LB + c] = x.q[j] * ps[j];
+    }
+    __syncthreads();
+    gate_products<L, LB>(w, sdG, sdP, sXK, sXQ, sYZ, sYP);
+    __syncthreads();
+    float yz[8], yp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        yz[j] = sYZ[(r0 + j) * LB + c];
+        yp[j] = sYP[(r0 + j) * LB + c];
+    }
+    if constexpr (HW >= 8) {
+        constexpr int SPS = HW / 8;
+        float loc[8];   // right: reverse scan R without carry; left: forward scan L before each row
+        float summary;
+        if (rt) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                x.dk[j] += ps[j] * yz[j];
+                x.dq[j] += ps[j] * yp[j];
+                loc[j] = x.k[j] * yz[j] + x.q[j] * yp[j];   // dpre
+            }
+#pragma unroll
+            for (int j = 6; j >= 0; --j) loc[j] += x.a[j + 1] * loc[j + 1];
+            summary = x.a[0] * loc[0];
+        } else {
+            float Lv = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                x.dk[j] += ps[j] * yz[j];
+                loc[j] = Lv;
+                Lv = x.k[j] * yz[j] + x.a[j] * Lv;
+            }
+            summary = Lv;
+        }
+        float carry = 0.f;
+        if constexpr (SPS > 1) {
+            sCV[part * CB + c] = summary;
+            __syncthreads();
+            if (rt) {
+                for (int qq = hhi - 1; qq > part; --qq) carry = sCV[qq * CB + c] + sCM[qq * CB + c] * carry;
+            } else {
+                for (int qq = hlo; qq < part; ++qq) carry = sCV[qq * CB + c] + sCM[qq * CB + c] * carry;
+            }
+        }
+        if (rt) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x.da[j] += (j > 0 ? ps[j - 1] : sp) * (loc[j] + ml[j] * carry);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x.da[j] += ps[j] * (loc[j] + (j > 0 ? lp[j - 1] : 1.f) * carry);
+        }
+    } else {
+#pragma unroll
+        for (int s0 = 0; s0 < 8; s0 += 2 * HW) {
+            float R = 0.f;
+#pragma unroll
+            for (int u = HW - 1; u >= 0; --u) {
+                const int j = s0 + HW + u;
+                x.dk[j] += ps[j] * yz[j];
+                x.dq[j] += ps[j] * yp[j];
+                const float dpre = x.k[j] * yz[j] + x.q[j] * yp[j];
+                R = u < HW - 1 ? dpre + x.a[j + 1] * R : dpre;
+                x.da[j] += (u > 0 ? ps[j - 1] : 1.f) * R;
+            }
+            float Lv = 0.f;
+#pragma unroll
+            for (int u = 0; u < HW; ++u) {
+                const int j = s0 + u;
+                x.dk[j] += ps[j] * yz[j];
+                x.da[j] += ps[j] * Lv;
+                Lv = x.k[j] * yz[j] + x.a[j] * Lv;
+            }
+        }
+    }
+}
+
 template <class TIn, int DK, bool SG>
-__global__ void __launch_bounds__(256) cb_grad_gate_kernel(Params p) {
+__global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
     using SM = GateSmem<DK>;
     using PL = PrepLay<DK>;
-    constexpr int LB = SM::LB;
+    constexpr int CB = SM::CB, LB = SM::LB, NP = SM::NP;
+    static_assert(CB * NP == 256 && NP * 8 == C && DK % CB == 0, "gate-side thread layout");
     extern __shared__ __align__(16) float sm[];
-    float *sX = sm + SM::X, *sG = sm + SM::G, *sdX = sm + SM::DX, *sdP = sm + SM::DP, *sT = sm + SM::T;
-    float *sK = sm + SM::K, *sQ = sm + SM::Q, *sA = sm + SM::A, *sXK = sm + SM::XK, *sXQ = sm + SM::XQ;
-    float *sPS = sm + SM::PS, *sYZ = sm + SM::YZ, *sYP = sm + SM::YP, *sdq = sm + SM::DQ, *sdk = sm + SM::DKK;
-    float *sda = sm + SM::DA, *sBeta = sm + SM::BETA, *sdb = sm + SM::DB, *sdat = sm + SM::DAT;
+    float *sdG = sm + SM::DG, *sX = sm + SM::X, *sG = sm + SM::G, *sT = sm + SM::T, *sdP = sm + SM::DP;
+    float *sXK = sm + SM::XK, *sXQ = sm + SM::XQ, *sYZ = sm + SM::YZ, *sYP = sm + SM::YP;
+    float *sCM = sm + SM::CM, *sCL = sm + SM::CL, *sCR = sm + SM::CR, *sCV = sm + SM::CV;
+    float *sBeta = sm + SM::BETA, *sdb = sm + SM::DB, *sdat = sm + SM::DAT;
 
     const int H = p.H;
     const int item = blockIdx.x;
@@ -839,18 +1132,17 @@ __global__ void __launch_bounds__(256) cb_grad_gate_kernel(Params p) {
     const float* pb = p.prep + base * PL::FLOATS;
     const float* ex = p.ext + base * EXT_FLOATS;
 
-    for (int x = tid; x < C * C; x += 256) {
-        const int r = x / C, c = x % C;
+    // dX into the dG buffer (replaced by dG below), X, G
+    for (int x = tid; x < C * C / 4; x += 256) {
+        const int r = x / (C / 4), c = 4 * (x % (C / 4));
         const bool low = (r / 16) >= (c / 16);
-        sX[r * LC + c] = pb[PL::X + x];
-        sG[r * LC + c] = pb[PL::G + x];
-        sdX[r * LC + c] = low ? ex[x] : 0.f;
-        sdP[r * LC + c] = low ? pb[PL::P + x] : 0.f;
+        *reinterpret_cast<f32x4*>(sX + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::X + 4 * x);
+        *reinterpret_cast<f32x4*>(sG + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::G + 4 * x);
+        *reinterpret_cast<f32x4*>(sdG + r * LC + c) = low ? *reinterpret_cast<const f32x4*>(ex + 4 * x) : zero4();
     }
     if (tid < C) {
         sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
         sdb[tid] = ex[(size_t)C * C + tid];
-        sdat[tid] = 0.f;
     }
     __syncthreads();
     // ---- T = dX X^T (full tiles)
@@ -858,12 +1150,12 @@ __global__ void __launch_bounds__(256) cb_grad_gate_kernel(Params p) {
     for (int u = 0; u < 4; ++u) {
         const int tt = w + 4 * u, R = tt / 4, J = tt % 4;
         f32x4 a = zero4();
-        for (int kb = 0; kb <= min(R, J); ++kb) a = mm4(ldA(sdX, LC, 16 * R, 16 * kb), ldBT(sX, LC, 16 * kb, 16 * J), a);
+        for (int kb = 0; kb <= min(R, J); ++kb) a = mm4(ldA(sdG, LC, 16 * R, 16 * kb), ldBT(sX, LC, 16 * kb, 16 * J), a);
         stD(sT, LC, 16 * R, 16 * J, a);
     }
     __syncthreads();
-    // ---- dA = -X^T T (strictly lower), dG = Diag(beta) dA into sdX; wave R
-    // owns row tile R (every J <= R), so the beta part of each row is one sum
+    // ---- dA = -X^T T (strictly lower), dG = Diag(beta) dA; wave R owns row
+    // tile R (every J <= R), so the beta part of each row is one sum
     {
         const int R = w;
         float rowpart[4] = {0.f, 0.f, 0.f, 0.f};
@@ -877,9 +1169,9 @@ __global__ void __launch_bounds__(256) cb_grad_gate_kernel(Params p) {
                 rowpart[e] += da * sG[r * LC + c];
                 a[e] = sBeta[r] * da;
             }
-            stD(sdX, LC, 16 * R, 16 * J, a);
+            stD(sdG, LC, 16 * R, 16 * J, a);
         }
-        for (int J = R + 1; J < 4; ++J) stD(sdX, LC, 16 * R, 16 * J, zero4());
+        for (int J = R + 1; J < 4; ++J) stD(sdG, LC, 16 * R, 16 * J, zero4());
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float rs = rowpart[e];
@@ -890,178 +1182,135 @@ __global__ void __launch_bounds__(256) cb_grad_gate_kernel(Params p) {
             if (i == 0) sdb[C + 16 * R + 4 * g + e] = rs;
         }
     }
-    __syncthreads();
-    float* sdG = sdX;
-
-    // ---- per block of 16 key channels
-    const TIn* gk = (const TIn*)p.k;
-    const TIn* gq = (const TIn*)p.q;
-    for (int cb = 0; cb < DK / 16; ++cb) {
-        for (int x = tid; x < C * 16; x += 256) {
-            const int r = x / 16, c = x % 16, ch = 16 * cb + c;
-            float kv = 0.f, qv = 0.f, av = 1.f;
-            if (r < n) {
-                const size_t row = (size_t)(t0 + r) * H + h;
-                kv = ld_in(gk + row * DK + ch);
-                qv = ld_in(gq + row * DK + ch);
-                av = gate_at<TIn>(p, row, DK, ch, SG);
-            }
-            sK[r * LB + c] = kv;
-            sQ[r * LB + c] = qv;
-            sA[r * LB + c] = av;
-        }
-        __syncthreads();
-        // Gamma o Q, Gamma o K, K_end and gamma terms; the diagonal of P
-        if (tid < 16) {
-            const int c = tid, ch = 16 * cb + c;
-            float gm = 1.f;
-            for (int r = 0; r < C; ++r) {
-                gm *= sA[r * LB + c];
-                const float dqg = pb[PL::QG + (size_t)r * DK + ch], dgk = pb[PL::W + (size_t)r * DK + ch];
-                const float kv = sK[r * LB + c], qv = sQ[r * LB + c], dpd = sdP[r * LC + r];
-                sdq[r * LB + c] = dqg * gm + dpd * kv;
-                sdk[r * LB + c] = dgk * gm + dpd * qv;
-                sYZ[r * LB + c] = dqg * qv + dgk * kv;   // dGamma_r
-                sPS[r * LB + c] = gm;                    // Gamma_r
-            }
-            sYZ[(C - 1) * LB + c] += pb[PL::GAM + ch];   // dgamma
-            float R = 0.f;
-            for (int tau = C - 1; tau >= 0; --tau) {
-                R = sYZ[tau * LB + c] + (tau + 1 < C ? sA[(tau + 1) * LB + c] * R : 0.f);
-                sda[tau * LB + c] = (tau > 0 ? sPS[(tau - 1) * LB + c] : 1.f) * R;
-            }
-            float f = 1.f;
-            for (int j = C - 1; j >= 0; --j) {
-                const float dke = pb[PL::KE + (size_t)j * DK + ch];
-                sdk[j * LB + c] += dke * f;
-                sYP[j * LB + c] = dke * sK[j * LB + c];  // drel_end
-                sPS[j * LB + c] = f;                     // rel_end
-                f *= sA[j * LB + c];
-            }
-            float Lr = 0.f;
-            for (int tau = 0; tau < C; ++tau) {
-                sda[tau * LB + c] += sPS[tau * LB + c] * Lr;
-                Lr = sYP[tau * LB + c] + sA[tau * LB + c] * Lr;
-            }
-        }
-        __syncthreads();
-        for (int L = 0; L < 6; ++L) {
-            const int hw = level_half(L), ng = C / (2 * hw);
-            const int c = tid % 16, part = tid / 16;
-            // stage right rows k o pre, q o pre (pre in PS), left rows k o suf (suf in PS)
-            for (int gi = part; gi < ng; gi += 16) {
-                const int s0 = gi * 2 * hw, m = s0 + hw - 1;
-                float f = 1.f;
-                for (int r = m + 1; r < s0 + 2 * hw; ++r) {
-                    f *= sA[r * LB + c];
-                    sXK[r * LB + c] = sK[r * LB + c] * f;
-                    sXQ[r * LB + c] = sQ[r * LB + c] * f;
-                    sPS[r * LB + c] = f;
-                }
-                f = 1.f;
-                for (int j = m; j >= s0; --j) {
-                    sXK[j * LB + c] = sK[j * LB + c] * f;
-                    sPS[j * LB + c] = f;
-                    f *= sA[j * LB + c];
-                }
-            }
-            __syncthreads();
-            // products of the level: Y_G, Y_P (right row tiles) and Z (left row tiles)
-            if (L < 2) {
-                // outputs: 0..(NR-1) Y tiles, then Z tiles; pairs from tile_at_level
-                for (int o = w; o < 6; o += 4) {
-                    // L = 0: Y rows {2, 3} from J {0, 1}; Z rows {0, 1} from R {2, 3}
-                    // L = 1: Y rows {1, 3} from J {0, 2}; Z rows {0, 2} from R {1, 3}
-                    const int kind = o % 3;   // 0: Y_G, 1: Y_P, 2: Z
-                    const int which = o / 3;
-                    if (kind < 2) {
-                        const int R = L == 0 ? 2 + which : 1 + 2 * which;
-                        f32x4 a = zero4();
-                        for (int J = 0; J < R; ++J) {
-                            if (!tile_at_level(R, J, L)) continue;
-                            a = mm4(ldA(kind == 0 ? sdG : sdP, LC, 16 * R, 16 * J), ldB(sXK, LB, 16 * J, 0), a);
-                        }
-                        stD(kind == 0 ? sYZ : sYP, LB, 16 * R, 0, a);
-                    } else {
-                        const int J = L == 0 ? which : 2 * which;
-                        f32x4 a = zero4();
-                        for (int R = J + 1; R < 4; ++R) {
-                            if (!tile_at_level(R, J, L)) continue;
-                            a = mm4(ldAT(sdG, LC, 16 * J, 16 * R), ldB(sXK, LB, 16 * R, 0), a);
-                            a = mm4(ldAT(sdP, LC, 16 * J, 16 * R), ldB(sXQ, LB, 16 * R, 0), a);
-                        }
-                        stD(sYZ, LB, 16 * J, 0, a);
-                    }
-                }
-            } else {
-                // in-tile level: tile b = w; Y_G + Z into YZ, Y_P into YP
-                const int b = w;
-                f32x4 ag, ap, bgT, bpT;
-                ag = ldA(sdG, LC, 16 * b, 16 * b);
-                ap = ldA(sdP, LC, 16 * b, 16 * b);
-                bgT = ldAT(sdG, LC, 16 * b, 16 * b);
-                bpT = ldAT(sdP, LC, 16 * b, 16 * b);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bool ky = sep_in(i, 4 * g + s, hw);   // A(i, k) = dG[r = i][j = k]
-                    const bool kz = sep_in(4 * g + s, i, hw);   // A(i, k) = dG[r = k][j = i]
-                    ag[s] = ky ? ag[s] : 0.f;
-                    ap[s] = ky ? ap[s] : 0.f;
-                    bgT[s] = kz ? bgT[s] : 0.f;
-                    bpT[s] = kz ? bpT[s] : 0.f;
-                }
-                const f32x4 xk = ldB(sXK, LB, 16 * b, 0), xq = ldB(sXQ, LB, 16 * b, 0);
-                f32x4 yz = mm4(ag, xk, zero4());
-                yz = mm4(bgT, xk, yz);
-                yz = mm4(bpT, xq, yz);
-                stD(sYZ, LB, 16 * b, 0, yz);
-                stD(sYP, LB, 16 * b, 0, mm4(ap, xk, zero4()));
-            }
-            __syncthreads();
-            // accumulate dq, dk and the gate gradient of this level
-            for (int gi = part; gi < ng; gi += 16) {
-                const int s0 = gi * 2 * hw, m = s0 + hw - 1, e1 = s0 + 2 * hw;
-                float R = 0.f;
-                for (int tau = e1 - 1; tau > m; --tau) {
-                    const float yz = sYZ[tau * LB + c], yp = sYP[tau * LB + c], pre = sPS[tau * LB + c];
-                    sdk[tau * LB + c] += pre * yz;
-                    sdq[tau * LB + c] += pre * yp;
-                    const float dpre = sK[tau * LB + c] * yz + sQ[tau * LB + c] * yp;
-                    R = dpre + (tau + 1 < e1 ? sA[(tau + 1) * LB + c] * R : 0.f);
-                    sda[tau * LB + c] += (tau - 1 > m ? sPS[(tau - 1) * LB + c] : 1.f) * R;
-                }
-                float Lf = 0.f;
-                for (int tau = s0; tau <= m; ++tau) {
-                    const float yz = sYZ[tau * LB + c], suf = sPS[tau * LB + c];
-                    sdk[tau * LB + c] += suf * yz;
-                    sda[tau * LB + c] += suf * Lf;
-                    Lf = sK[tau * LB + c] * yz + sA[tau * LB + c] * Lf;
-                }
-            }
-            __syncthreads();
-        }
-        // outputs of this channel block
-        for (int x = tid; x < C * 16; x += 256) {
-            const int r = x / 16, c = x % 16, ch = 16 * cb + c;
-            if (r < n) {
-                const size_t row = (size_t)(t0 + r) * H + h;
-                p.gq[row * DK + ch] = sdq[r * LB + c];
-                p.gk[row * DK + ch] = sdk[r * LB + c];
-                if (!SG) p.gg[row * DK + ch] = sda[r * LB + c];
-            }
-        }
-        if (SG && tid < C) {
-            float sacc = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) sacc += sda[tid * LB + c];
-            sdat[tid] += sacc;
-        }
-        __syncthreads();
+    __syncthreads();   // X, G and T are dead from here on
+    for (int x = tid; x < C * C / 4; x += 256) {
+        const int r = x / (C / 4), c = 4 * (x % (C / 4));
+        const bool low = (r / 16) >= (c / 16);
+        *reinterpret_cast<f32x4*>(sdP + r * LC + c) =
+            low ? *reinterpret_cast<const f32x4*>(pb + PL::P + 4 * x) : zero4();
     }
+
+    // ---- per block of 32 key channels. Addresses: a uniform base at the
+    // chunk's first row plus a 32-bit offset per thread and row.
+    const size_t rowbase = (size_t)t0 * H + h;
+    const TIn* gk = (const TIn*)p.k + rowbase * DK;
+    const TIn* gq = (const TIn*)p.q + rowbase * DK;
+    const TIn* ga = (const TIn*)p.gate + rowbase * (SG ? 1 : DK);
+    float* oq = p.gq + rowbase * DK;
+    float* ok = p.gk + rowbase * DK;
+    float* oa = p.gg + rowbase * (SG ? 1 : DK);
+    const unsigned rs = (unsigned)H * DK;   // row stride of q, k and per-channel gates
+#pragma unroll 1
+    for (int cb = 0; cb < DK / CB; ++cb) {
+        // the row and channel indices are re-derived in every block: kept
+        // opaque to the compiler, the per-row offsets are not hoisted out of
+        // the loop and held in registers across it
+        int c = tid % CB, part = tid / CB;
+        asm volatile("" : "+v"(c), "+v"(part));
+        const int r0 = 8 * part;
+        const int ch = CB * cb + c;
+        GateRegs x;
+        float dqg[8], dgk[8], dke[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = r0 + j;
+            x.k[j] = 0.f;
+            x.q[j] = 0.f;
+            x.a[j] = 1.f;
+            dqg[j] = dgk[j] = dke[j] = 0.f;
+            if (r < n) {
+                const unsigned o = (unsigned)r * rs + ch;
+                x.k[j] = ld_in(gk + o);
+                x.q[j] = ld_in(gq + o);
+                x.a[j] = SG ? ld_in(ga + (unsigned)r * H) : ld_in(ga + o);
+                const unsigned off = (unsigned)r * DK + ch;
+                dqg[j] = pb[PL::QG + off];
+                dgk[j] = pb[PL::W + off];
+                dke[j] = pb[PL::KE + off];
+            }
+        }
+        // local products, and the local forward scan of drel_end = dK_end o k
+        float lp[8], ml[8];
+        local_products(x.a, lp, ml);
+        float Ll[8], Lend = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            Ll[j] = Lend;
+            Lend = dke[j] * x.k[j] + x.a[j] * Lend;
+        }
+        sCM[part * CB + c] = lp[7];
+        sCL[part * CB + c] = Lend;
+        __syncthreads();
+        float pfx = 1.f, sfx = 1.f, Lin = 0.f;
+        for (int qq = 0; qq < part; ++qq) {
+            const float m = sCM[qq * CB + c];
+            pfx *= m;
+            Lin = sCL[qq * CB + c] + m * Lin;
+        }
+        for (int qq = part + 1; qq < NP; ++qq) sfx *= sCM[qq * CB + c];
+        // Gamma o Q, Gamma o K and the diagonal of P; dGamma into a reverse scan
+        float gm[8], Rl[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = r0 + j;
+            gm[j] = pfx * lp[j];
+            const float dpd = sdP[r * LC + r];
+            x.dq[j] = dqg[j] * gm[j] + dpd * x.k[j];
+            x.dk[j] = dgk[j] * gm[j] + dpd * x.q[j];
+            Rl[j] = dqg[j] * x.q[j] + dgk[j] * x.k[j];   // dGamma_r
+        }
+        if (part == NP - 1) Rl[7] += pb[PL::GAM + ch];   // dgamma
+#pragma unroll
+        for (int j = 6; j >= 0; --j) Rl[j] += x.a[j + 1] * Rl[j + 1];
+        sCR[part * CB + c] = x.a[0] * Rl[0];
+        // K_end: rel_end = product of the gates after the row
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f = ml[j] * sfx;
+            x.dk[j] += dke[j] * f;
+            x.da[j] = f * (Ll[j] + (j > 0 ? lp[j - 1] : 1.f) * Lin);
+        }
+        __syncthreads();
+        float Cin = 0.f;
+        for (int qq = NP - 1; qq > part; --qq) Cin = sCR[qq * CB + c] + sCM[qq * CB + c] * Cin;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x.da[j] += (j > 0 ? gm[j - 1] : pfx) * (Rl[j] + ml[j] * Cin);
+
+        gate_level<0, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
+        gate_level<1, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
+        gate_level<2, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
+        gate_level<3, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
+        gate_level<4, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
+        gate_level<5, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = r0 + j;
+            if (r < n) {
+                const unsigned o = (unsigned)r * rs + ch;
+                oq[o] = x.dq[j];
+                ok[o] = x.dk[j];
+                if (!SG) oa[o] = x.da[j];
+            }
+        }
+        if (SG) {
+            // scalar gate: the gate gradient of a row is the sum over its
+            // channels -- over the 32 lanes of the row part, then the blocks
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float v = x.da[j];
+                v += __shfl_xor(v, 1, 32);
+                v += __shfl_xor(v, 2, 32);
+                v += __shfl_xor(v, 4, 32);
+                v += __shfl_xor(v, 8, 32);
+                v += __shfl_xor(v, 16, 32);
+                if (c == 0) sdat[r0 + j] = (cb == 0 ? 0.f : sdat[r0 + j]) + v;
+            }
+        }
+    }
+    if (SG) __syncthreads();
     if (tid < n) {
-        const size_t row = (size_t)(t0 + tid) * H + h;
-        p.gb[row] = sdb[tid] + sdb[C + tid];
-        if (SG) p.gg[row] = sdat[tid];
+        p.gb[(size_t)(t0 + tid) * H + h] = sdb[tid] + sdb[C + tid];
+        if (SG) oa[(unsigned)tid * H] = sdat[tid];
     }
 }
 
