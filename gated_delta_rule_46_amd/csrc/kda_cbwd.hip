@@ -150,29 +150,153 @@ __device__ __forceinline__ float gate_at(const Params& p, size_t row, int DK, in
     return sg ? ld_in(g + row) : ld_in(g + row * DK + c);
 }
 
+// Inclusive prefix (lp) and exclusive suffix (ml) products of a thread's 8 gates.
+__device__ __forceinline__ void local_products(const float* a, float* lp, float* ml) {
+    float f = 1.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        f *= a[j];
+        lp[j] = f;
+    }
+    f = 1.f;
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+        ml[j] = f;
+        f *= a[j];
+    }
+}
+
 // ================================================================ 1. prep
 // One workgroup (4 waves) per (chunk, head). Pass 1 over blocks of 32 key
 // channels accumulates the gated Gram matrices G and P level by level; then
 // X = (I + Diag(beta) G)^{-1} (16x16 diagonal blocks by forward substitution,
 // the rest by block products); pass 2 forms W, K_end, Gamma o Q and gamma.
+// Thread (c, part) holds channel c of the block on the 8 rows 8 part ..
+// 8 part + 7 in registers; gate products that span several row parts come
+// from the part products exchanged through the CM table.
 template <int DK>
 struct PrepSmem {
-    static constexpr int CB = 32, LB = CB + 4;
-    static constexpr size_t K = 0, Q = K + (size_t)C * LB, A = Q + (size_t)C * LB;
-    static constexpr size_t XK = A + (size_t)C * LB, XQ = XK + (size_t)C * LB;
+    static constexpr int CB = 32, LB = CB + 4, NP = 8;
+    static constexpr size_t CM = 0, XK = CM + NP * CB, XQ = XK + (size_t)C * LB;
     static constexpr size_t G = XQ + (size_t)C * LB, P = G + (size_t)C * LC, XI = P + (size_t)C * LC;
     static constexpr size_t BETA = XI + (size_t)C * LC;
     static constexpr size_t FLOATS = BETA + C;
     static constexpr size_t BYTES = FLOATS * 4;
 };
 
+// Gates, keys and queries of rows r0 .. r0 + 7 on one channel; rows past the
+// chunk's n tokens are zero keys and queries with unit gates.
+template <class TIn, bool SG>
+__device__ __forceinline__ void load_rows(const TIn* gk, const TIn* gq, const TIn* ga, unsigned rs, int H, int n,
+                                          int r0, int ch, float* a, float* k, float* q) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = r0 + j;
+        k[j] = 0.f;
+        q[j] = 0.f;
+        a[j] = 1.f;
+        if (r < n) {
+            const unsigned o = (unsigned)r * rs + ch;
+            k[j] = ld_in(gk + o);
+            q[j] = ld_in(gq + o);
+            a[j] = SG ? ld_in(ga + (unsigned)r * H) : ld_in(ga + o);
+        }
+    }
+}
+
+// pre (right rows) / suf (left rows) of level L for a thread's 8 rows; L = 6
+// is the diagonal level (no gates).
+template <int L, int CB>
+__device__ __forceinline__ void level_weights(const float* a, const float* lp, const float* ml, int c, int part,
+                                              const float* sCM, float* ps) {
+    if constexpr (L == 6) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ps[j] = 1.f;
+    } else {
+        constexpr int HW = 32 >> L;
+        if constexpr (HW >= 8) {
+            constexpr int SPS = HW / 8;
+            const int hlo = part / SPS * SPS, hhi = hlo + SPS;
+            const bool rt = (part / SPS) & 1;
+            float sp = 1.f, ss = 1.f;
+            for (int qq = hlo; qq < part; ++qq) sp *= sCM[qq * CB + c];
+            for (int qq = part + 1; qq < hhi; ++qq) ss *= sCM[qq * CB + c];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ps[j] = rt ? sp * lp[j] : ml[j] * ss;
+        } else {
+#pragma unroll
+            for (int s0 = 0; s0 < 8; s0 += 2 * HW) {
+                float f = 1.f;
+#pragma unroll
+                for (int u = 0; u < HW; ++u) {
+                    f *= a[s0 + HW + u];
+                    ps[s0 + HW + u] = f;
+                }
+                f = 1.f;
+#pragma unroll
+                for (int u = 0; u < HW; ++u) {
+                    ps[s0 + HW - 1 - u] = f;
+                    f *= a[s0 + HW - 1 - u];
+                }
+            }
+        }
+    }
+}
+
+// Stage level L (k o w, q o w into XK, XQ), then add its tiles of G and P:
+// wave w owns lower tiles w, w + 4, w + 8.
+template <int L, int LB, int CB>
+__device__ __forceinline__ void prep_level(const float* a, const float* k, const float* q, const float* lp,
+                                          const float* ml, int c, int part, int w, const float* sCM, float* sXK,
+                                          float* sXQ, f32x4* accG, f32x4* accP) {
+    float ps[8];
+    level_weights<L, CB>(a, lp, ml, c, part, sCM, ps);
+    const int r0 = 8 * part;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        sXK[(r0 + j) * LB + c] = k[j] * ps[j];
+        sXQ[(r0 + j) * LB + c] = q[j] * ps[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int idx = w + 4 * u;
+        if (idx >= 10) continue;
+        int R, J;
+        lower_tile(idx, R, J);
+        if (L < 6 && !tile_at_level(R, J, L < 2 ? L : 2)) continue;
+        if (L == 6 && R != J) continue;
+        f32x4 tg = zero4(), tp = zero4();
+#pragma unroll
+        for (int kb = 0; kb < CB / 16; ++kb) {
+            const f32x4 bj = ldBT(sXK, LB, 16 * kb, 16 * J);
+            if (L < 6) tg = mm4(ldA(sXK, LB, 16 * R, 16 * kb), bj, tg);
+            tp = mm4(ldA(sXQ, LB, 16 * R, 16 * kb), bj, tp);
+        }
+        if (L >= 2) {
+            constexpr int hw = L < 6 ? (32 >> L) : 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lane_g() + e, j = lane_i();
+                const bool keep = L < 6 ? sep_in(r, j, hw) : (r == j);
+                tg[e] = keep ? tg[e] : 0.f;
+                tp[e] = keep ? tp[e] : 0.f;
+            }
+        }
+        if (L < 6) accG[u] += tg;
+        accP[u] += tp;
+    }
+    __syncthreads();
+}
+
 template <class TIn, int DK, bool SG>
-__global__ void __launch_bounds__(256) cb_prep_kernel(Params p) {
+__global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
     using SM = PrepSmem<DK>;
     using PL = PrepLay<DK>;
-    constexpr int CB = SM::CB, LB = SM::LB;
+    constexpr int CB = SM::CB, LB = SM::LB, NP = SM::NP;
+    static_assert(CB * NP == 256 && NP * 8 == C && DK % CB == 0, "prep thread layout");
     extern __shared__ __align__(16) float sm[];
-    float *sK = sm + SM::K, *sQ = sm + SM::Q, *sA = sm + SM::A, *sXK = sm + SM::XK, *sXQ = sm + SM::XQ;
+    float *sCM = sm + SM::CM, *sXK = sm + SM::XK, *sXQ = sm + SM::XQ;
     float *sG = sm + SM::G, *sP = sm + SM::P, *sX = sm + SM::XI, *sBeta = sm + SM::BETA;
 
     const int H = p.H;
@@ -183,93 +307,37 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(Params p) {
     if (!resolve_chunk(p.map, gidx, C, t0, n)) return;
     const int tid = threadIdx.x, w = tid / WAVE;
     float* out = p.prep + ((size_t)gidx * H + h) * PL::FLOATS;
-    const TIn* gk = (const TIn*)p.k;
-    const TIn* gq = (const TIn*)p.q;
+    const size_t rowbase = (size_t)t0 * H + h;
+    const TIn* gk = (const TIn*)p.k + rowbase * DK;
+    const TIn* gq = (const TIn*)p.q + rowbase * DK;
+    const TIn* ga = (const TIn*)p.gate + rowbase * (SG ? 1 : DK);
+    const unsigned rs = (unsigned)H * DK;
 
     if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
-
-    auto load_block = [&](int cb) {
-        for (int x = tid; x < C * CB; x += 256) {
-            const int r = x / CB, c = x % CB, ch = cb * CB + c;
-            float kv = 0.f, qv = 0.f, av = 1.f;
-            if (r < n) {
-                const size_t row = (size_t)(t0 + r) * H + h;
-                kv = ld_in(gk + row * DK + ch);
-                qv = ld_in(gq + row * DK + ch);
-                av = gate_at<TIn>(p, row, DK, ch, SG);
-            }
-            sK[r * LB + c] = kv;
-            sQ[r * LB + c] = qv;
-            sA[r * LB + c] = av;
-        }
-    };
 
     // ---- pass 1: G and P, lower tiles; wave w owns tiles w, w + 4, w + 8
     f32x4 accG[3], accP[3];
 #pragma unroll
     for (int u = 0; u < 3; ++u) { accG[u] = zero4(); accP[u] = zero4(); }
+#pragma unroll 1
     for (int cb = 0; cb < DK / CB; ++cb) {
+        // row and channel indices opaque to the compiler, so that per-row
+        // offsets are re-derived per block rather than held across the loop
+        int c = tid % CB, part = tid / CB;
+        asm volatile("" : "+v"(c), "+v"(part));
+        const int ch = CB * cb + c;
+        float a[8], k[8], q[8], lp[8], ml[8];
+        load_rows<TIn, SG>(gk, gq, ga, rs, H, n, 8 * part, ch, a, k, q);
+        local_products(a, lp, ml);
+        sCM[part * CB + c] = lp[7];   // the last reader of CM passed a barrier since
         __syncthreads();
-        load_block(cb);
-        __syncthreads();
-        for (int L = 0; L < 7; ++L) {
-            // stage: right rows k o pre and q o pre, left rows k o suf (L = 6: raw k, q)
-            {
-                const int c = tid % CB, part = tid / CB;
-                if (L == 6) {
-                    for (int r = part; r < C; r += 256 / CB) {
-                        sXK[r * LB + c] = sK[r * LB + c];
-                        sXQ[r * LB + c] = sQ[r * LB + c];
-                    }
-                } else {
-                    const int hw = level_half(L), ng = C / (2 * hw);
-                    for (int gi = part; gi < ng; gi += 256 / CB) {
-                        const int s0 = gi * 2 * hw, m = s0 + hw - 1;
-                        float f = 1.f;
-                        for (int r = m + 1; r < s0 + 2 * hw; ++r) {
-                            f *= sA[r * LB + c];
-                            sXK[r * LB + c] = sK[r * LB + c] * f;
-                            sXQ[r * LB + c] = sQ[r * LB + c] * f;
-                        }
-                        f = 1.f;
-                        for (int j = m; j >= s0; --j) {
-                            sXK[j * LB + c] = sK[j * LB + c] * f;
-                            f *= sA[j * LB + c];
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const int idx = w + 4 * u;
-                if (idx >= 10) continue;
-                int R, J;
-                lower_tile(idx, R, J);
-                if (L < 6 && !tile_at_level(R, J, L < 2 ? L : 2)) continue;
-                if (L == 6 && R != J) continue;
-                f32x4 tg = zero4(), tp = zero4();
-#pragma unroll
-                for (int kb = 0; kb < CB / 16; ++kb) {
-                    const f32x4 bj = ldBT(sXK, LB, 16 * kb, 16 * J);
-                    if (L < 6) tg = mm4(ldA(sXK, LB, 16 * R, 16 * kb), bj, tg);
-                    tp = mm4(ldA(sXQ, LB, 16 * R, 16 * kb), bj, tp);
-                }
-                if (L >= 2) {
-                    const int hw = L < 6 ? level_half(L) : 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * lane_g() + e, j = lane_i();
-                        const bool keep = L < 6 ? sep_in(r, j, hw) : (r == j);
-                        tg[e] = keep ? tg[e] : 0.f;
-                        tp[e] = keep ? tp[e] : 0.f;
-                    }
-                }
-                if (L < 6) accG[u] += tg;
-                accP[u] += tp;
-            }
-            __syncthreads();
-        }
+        prep_level<0, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
+        prep_level<1, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
+        prep_level<2, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
+        prep_level<3, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
+        prep_level<4, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
+        prep_level<5, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
+        prep_level<6, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
     }
     // ---- G and P to LDS (upper tiles zero) and out
     for (int x = tid; x < C * C; x += 256) {
@@ -327,26 +395,29 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(Params p) {
     for (int x = tid; x < C * C; x += 256) out[PL::X + x] = sX[(x / C) * LC + x % C];
 
     // ---- pass 2: W = X (beta o Gamma o K), K_end, Gamma o Q, gamma
+#pragma unroll 1
     for (int cb = 0; cb < DK / CB; ++cb) {
+        int c = tid % CB, part = tid / CB;
+        asm volatile("" : "+v"(c), "+v"(part));
+        const int r0 = 8 * part, ch = CB * cb + c;
+        float a[8], k[8], q[8], lp[8], ml[8];
+        load_rows<TIn, SG>(gk, gq, ga, rs, H, n, r0, ch, a, k, q);
+        local_products(a, lp, ml);
+        __syncthreads();   // CM and XK of the previous block are read
+        sCM[part * CB + c] = lp[7];
         __syncthreads();
-        load_block(cb);
-        __syncthreads();
-        if (tid < CB) {
-            const int c = tid;
-            float gm = 1.f;
-            for (int r = 0; r < C; ++r) {
-                gm *= sA[r * LB + c];
-                sXQ[r * LB + c] = gm * sQ[r * LB + c];                   // Gamma o Q
-                sXK[r * LB + c] = sBeta[r] * gm * sK[r * LB + c];         // beta o Gamma o K
-            }
-            out[PL::GAM + cb * CB + c] = gm;
-            float f = 1.f;
-            for (int j = C - 1; j >= 0; --j) {
-                const float kv = sK[j * LB + c];
-                sK[j * LB + c] = kv * f;                                 // K_end
-                f *= sA[j * LB + c];
-            }
+        float pfx = 1.f, sfx = 1.f;
+        for (int qq = 0; qq < part; ++qq) pfx *= sCM[qq * CB + c];
+        for (int qq = part + 1; qq < NP; ++qq) sfx *= sCM[qq * CB + c];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = r0 + j;
+            const float gm = pfx * lp[j];
+            out[PL::QG + (unsigned)r * DK + ch] = gm * q[j];             // Gamma o Q
+            out[PL::KE + (unsigned)r * DK + ch] = k[j] * (ml[j] * sfx);  // K_end
+            sXK[r * LB + c] = sBeta[r] * gm * k[j];                      // beta o Gamma o K
         }
+        if (part == NP - 1) out[PL::GAM + ch] = pfx * lp[7];
         __syncthreads();
         // W tiles: 4 token tiles x CB/16 channel tiles, two per wave
 #pragma unroll
@@ -357,11 +428,6 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(Params p) {
             const int i = lane_i(), g = lane_g();
 #pragma unroll
             for (int e = 0; e < 4; ++e) out[PL::W + (size_t)(16 * R + 4 * g + e) * DK + cb * CB + 16 * cc + i] = acc[e];
-        }
-        for (int x = tid; x < C * CB; x += 256) {
-            const int r = x / CB, c = x % CB;
-            out[PL::KE + (size_t)r * DK + cb * CB + c] = sK[r * LB + c];
-            out[PL::QG + (size_t)r * DK + cb * CB + c] = sXQ[r * LB + c];
         }
     }
 }
@@ -966,22 +1032,6 @@ __device__ __forceinline__ void gate_products(int w, const float* sdG, const flo
 struct GateRegs {
     float a[8], k[8], q[8], dq[8], dk[8], da[8];
 };
-
-// Inclusive prefix (lp) and exclusive suffix (ml) products of a thread's 8 gates.
-__device__ __forceinline__ void local_products(const float* a, float* lp, float* ml) {
-    float f = 1.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        f *= a[j];
-        lp[j] = f;
-    }
-    f = 1.f;
-#pragma unroll
-    for (int j = 7; j >= 0; --j) {
-        ml[j] = f;
-        f *= a[j];
-    }
-}
 
 // One level of the binary split, half width HW = 32 >> L. Right rows of a
 // group (its second half) carry pre = product of the gates from the middle
