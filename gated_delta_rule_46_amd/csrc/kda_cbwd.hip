@@ -185,22 +185,22 @@ struct PrepSmem {
 };
 
 // Gates, keys and queries of rows r0 .. r0 + 7 on one channel; rows past the
-// chunk's n tokens are zero keys and queries with unit gates.
+// chunk's n >= 1 tokens are zero keys and queries with unit gates. The loads
+// read row min(r, n - 1) unconditionally and the padding is selected after:
+// straight-line loads are all issued before the first wait, where a load in
+// a branch followed by a conversion waits once per row.
 template <class TIn, bool SG>
 __device__ __forceinline__ void load_rows(const TIn* gk, const TIn* gq, const TIn* ga, unsigned rs, int H, int n,
                                           int r0, int ch, float* a, float* k, float* q) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int r = r0 + j;
-        k[j] = 0.f;
-        q[j] = 0.f;
-        a[j] = 1.f;
-        if (r < n) {
-            const unsigned o = (unsigned)r * rs + ch;
-            k[j] = ld_in(gk + o);
-            q[j] = ld_in(gq + o);
-            a[j] = SG ? ld_in(ga + (unsigned)r * H) : ld_in(ga + o);
-        }
+        const int r = r0 + j, rc = min(r, n - 1);
+        const unsigned o = (unsigned)rc * rs + ch;
+        const float kv = ld_in(gk + o), qv = ld_in(gq + o);
+        const float av = SG ? ld_in(ga + (unsigned)rc * H) : ld_in(ga + o);
+        k[j] = r < n ? kv : 0.f;
+        q[j] = r < n ? qv : 0.f;
+        a[j] = r < n ? av : 1.f;
     }
 }
 
@@ -460,46 +460,63 @@ __device__ __forceinline__ void seq_range(const ChunkMap& m, int s, long& bos, l
     }
 }
 
-// Operands of one chunk for the forward walk (wave q, own rows q dk/4..).
+// Operands of one chunk for the forward walk (wave q, own rows q dk/4..), in
+// the groups in which they are reloaded for the next chunk: each group right
+// after its last use in the current one, so that one register set suffices
+// and the loads spread over the step.
 template <int DK>
 struct StateOps {
     static constexpr int RT = DK / 64;
-    f32x4 w[4][RT];    // W[16t + i][own channels]: A operand over own channels
-    f32x4 x[4];        // X[16q + i][16kb..]: A operand over tokens
-    f32x4 v[4];        // beta o V (K = tokens): B operand
-    f32x4 ke[RT][4];   // K_end^T[own rows][16kb..]: A operand over tokens
-    f32x4 gm[RT];      // gamma of own rows
+    f32x4 w[4][RT];    // group 0: W[16t + i][own channels], A operand over own channels
+    f32x4 x[4];        // group 1: X[16q + i][16kb..], A operand over tokens
+    f32x4 v[4];        //          beta o V (K = tokens), B operand
+    f32x4 ke[RT][4];   // group 2: K_end^T[own rows][16kb..], A operand over tokens
+    f32x4 gm[RT];      //          gamma of own rows
 };
 
-template <class TIn, int DK>
-__device__ __forceinline__ void load_state_ops(StateOps<DK>& o, const Params& p, int gi, int cs, long bos, long eos,
-                                               int h, int sl, int q) {
+// Where chunk gi starts and how many tokens it has.
+__device__ __forceinline__ void chunk_span(int gi, int cs, long bos, long eos, long& t0, int& n) {
+    t0 = bos + (long)(gi - cs) * C;
+    n = (int)min((long)C, eos - t0);
+}
+
+template <int DK>
+__device__ __forceinline__ void state_load0(StateOps<DK>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
-    const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
-    const long t0 = bos + (long)(gi - cs) * C;
-    const int n = (int)min((long)C, eos - t0);
-    const float* pb = p.prep + ((size_t)gi * H + h) * PL::FLOATS;
+    const int i = lane_i(), g = lane_g();
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
             o.w[t][rt] = *reinterpret_cast<const f32x4*>(pb + PL::W + (size_t)(16 * t + i) * DK + q * RW + 16 * rt + 4 * g);
+}
+
+template <class TIn, int DK>
+__device__ __forceinline__ void state_load1(StateOps<DK>& o, const Params& p, const float* pb, long t0, int n, int h,
+                                            int sl, int q) {
+    using PL = PrepLay<DK>;
+    const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
         o.x[kb] = kb <= q ? *reinterpret_cast<const f32x4*>(pb + PL::X + (size_t)(16 * q + i) * C + 16 * kb + 4 * g) : zero4();
+    // rows clamped to the chunk's last token, padding selected after the loads
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int tok = 16 * kb + 4 * g + s;
-            float val = 0.f;
-            if (tok < n) {
-                const size_t row = (size_t)(t0 + tok) * H + h;
-                val = ld_in((const TIn*)p.beta + row) * ld_in((const TIn*)p.v + row * DV + 16 * sl + i);
-            }
-            o.v[kb][s] = val;
+            const size_t row = (size_t)(t0 + min(tok, n - 1)) * H + h;
+            const float bv = ld_in((const TIn*)p.beta + row), vv = ld_in((const TIn*)p.v + row * DV + 16 * sl + i);
+            o.v[kb][s] = tok < n ? bv * vv : 0.f;
         }
+}
+
+template <int DK>
+__device__ __forceinline__ void state_load2(StateOps<DK>& o, const float* pb, int q) {
+    using PL = PrepLay<DK>;
+    constexpr int RW = DK / 4, RT = DK / 64;
+    const int i = lane_i(), g = lane_g();
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -507,14 +524,28 @@ __device__ __forceinline__ void load_state_ops(StateOps<DK>& o, const Params& p,
 #pragma unroll
             for (int s = 0; s < 4; ++s) o.ke[rt][kb][s] = pb[PL::KE + (size_t)(16 * kb + 4 * g + s) * DK + q * RW + 16 * rt + i];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o.gm[rt][e] = pb[PL::GAM + q * RW + 16 * rt + 4 * g + e];
+    for (int rt = 0; rt < RT; ++rt) o.gm[rt] = *reinterpret_cast<const f32x4*>(pb + PL::GAM + q * RW + 16 * rt + 4 * g);
+}
+
+// First touch of a chunk two steps ahead: the slices of one (sequence,
+// head) run on one XCD and split the 128-byte lines of the per-chunk blocks
+// they all read between them (so that the reloads one step ahead find them in
+// L2); a slice touches the lines of its own value columns itself. The value
+// is only folded into a sink, so nothing waits for it until the step ends.
+// The two spans are [a0, a0 + na) and [b0, b0 + nb) in floats of the block.
+__device__ __forceinline__ uint32_t touch_lines(const float* blk, size_t a0, size_t na, size_t b0, size_t nb, int sl,
+                                                int nsl, int tid) {
+    const size_t la = na / 32, lb = nb / 32;   // 32 floats per line
+    const size_t li = (size_t)sl + (size_t)nsl * tid;
+    if (li < la) return __float_as_uint(blk[a0 + 32 * li]);
+    if (li < la + lb) return __float_as_uint(blk[b0 + 32 * (li - la)]);
+    return 0u;
 }
 
 template <class TIn, int DK>
 __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
     using SM = WalkSmem<DK>;
+    using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
     float *sPart = sm + SM::PART, *sU = sm + SM::UT;
@@ -527,6 +558,7 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
     long bos, eos;
     int cs, ce;
     seq_range(p.map, s, bos, eos, cs, ce);
+    auto block = [&](int gi) { return p.prep + ((size_t)gi * H + h) * PL::FLOATS; };
 
     f32x4 S[RT];
 #pragma unroll
@@ -536,10 +568,25 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
             const int row = q * RW + 16 * rt + 4 * g + e;
             S[rt][e] = p.S0 ? p.S0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
         }
-    StateOps<DK> cur, nxt;
-    if (cs < ce) load_state_ops<TIn, DK>(cur, p, cs, cs, bos, eos, h, sl, q);
+    StateOps<DK> op;
+    if (cs < ce) {
+        long t0;
+        int n;
+        chunk_span(cs, cs, bos, eos, t0, n);
+        state_load0<DK>(op, block(cs), q);
+        state_load1<TIn, DK>(op, p, block(cs), t0, n, h, sl, q);
+        state_load2<DK>(op, block(cs), q);
+    }
+    uint32_t sink = 0;
     for (int gi = cs; gi < ce; ++gi) {
-        if (gi + 1 < ce) load_state_ops<TIn, DK>(nxt, p, gi + 1, cs, bos, eos, h, sl, q);
+        // X, W and K_end of chunk gi + 2 (W and K_end are adjacent)
+        const uint32_t tch =
+            gi + 2 < ce ? touch_lines(block(gi + 2), PL::X, (size_t)C * C, PL::W, 2 * (size_t)C * DK, sl, NSL, tid) : 0u;
+        const bool more = gi + 1 < ce;
+        const float* pn = block(more ? gi + 1 : gi);
+        long tn;
+        int nn;
+        chunk_span(more ? gi + 1 : gi, cs, bos, eos, tn, nn);
         float* ckS = p.ck + ((size_t)gi * H + h) * 2 * DK * DV;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -550,70 +597,90 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
         for (int t = 0; t < 4; ++t) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc = mm4(cur.w[t][rt], S[rt], acc);
+            for (int rt = 0; rt < RT; ++rt) acc = mm4(op.w[t][rt], S[rt], acc);
             *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
         }
+        if (more) state_load0<DK>(op, pn, q);
         __syncthreads();
         // U tile q = X (beta o V) - W S
         {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                if (kb <= q) acc = mm4(cur.x[kb], cur.v[kb], acc);
+                if (kb <= q) acc = mm4(op.x[kb], op.v[kb], acc);
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) acc -= *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
             *reinterpret_cast<f32x4*>(sU + (q * 64 + lane) * 4) = acc;
         }
+        if (more) state_load1<TIn, DK>(op, p, pn, tn, nn, h, sl, q);
         __syncthreads();
         // own rows: S <- Diag(gamma) S + K_end^T U
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) acc = mm4(cur.ke[rt][kb], *reinterpret_cast<const f32x4*>(sU + (kb * 64 + lane) * 4), acc);
-            S[rt] = cur.gm[rt] * S[rt] + acc;
+            for (int kb = 0; kb < 4; ++kb) acc = mm4(op.ke[rt][kb], *reinterpret_cast<const f32x4*>(sU + (kb * 64 + lane) * 4), acc);
+            S[rt] = op.gm[rt] * S[rt] + acc;
         }
-        cur = nxt;
+        if (more) state_load2<DK>(op, pn, q);
+        sink ^= tch;
     }
+    // keep the L2 touches alive: a store that no real input triggers
+    if (sink == 0x9e3779b9u && p.H < 0) p.ck[0] = 0.f;
 }
 
 // ================================================================ 3. adjoint at chunk ends
 // Same layout, chunks in reverse: store dS'; partial K_end dS' over own rows;
 // dU = P^T dO + K_end dS' for token tile q; dS = Diag(gamma) dS' +
 // (Gamma o Q)^T dO - W^T dU for own rows. Operands straight into registers,
-// one chunk ahead.
+// each group reloaded for the previous chunk right after its last use, and
+// the lines of the chunk two steps back touched first.
 template <int DK>
 struct AdjOps {
     static constexpr int RT = DK / 64;
-    f32x4 ke[4][RT];   // K_end[16t + i][own channels]: A operand over own channels
-    f32x4 pt[4];       // P^T[16q + i][16kb..] = P[16kb + ..][16q + i]: A operand over tokens
-    f32x4 d[4];        // dO (K = tokens): B operand
-    f32x4 qg[RT][4];   // (Gamma o Q)^T[own rows][16kb..]
-    f32x4 wt[RT][4];   // W^T[own rows][16kb..]
+    f32x4 ke[4][RT];   // group 0: K_end[16t + i][own channels], A operand over own channels
+    f32x4 pt[4];       // group 1: P^T[16q + i][16kb..] = P[16kb + ..][16q + i], A operand over tokens
+    f32x4 d[4];        // group 2: dO (K = tokens), B operand
+    f32x4 qg[RT][4];   //          (Gamma o Q)^T[own rows][16kb..]
+    f32x4 wt[RT][4];   //          W^T[own rows][16kb..]
     f32x4 gm[RT];
 };
 
 template <int DK>
-__device__ __forceinline__ void load_adj_ops(AdjOps<DK>& o, const Params& p, int gi, int cs, long bos, long eos, int h,
-                                             int sl, int q) {
+__device__ __forceinline__ void adj_load0(AdjOps<DK>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
-    const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
-    const long t0 = bos + (long)(gi - cs) * C;
-    const int n = (int)min((long)C, eos - t0);
-    const float* pb = p.prep + ((size_t)gi * H + h) * PL::FLOATS;
+    const int i = lane_i(), g = lane_g();
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
             o.ke[t][rt] = *reinterpret_cast<const f32x4*>(pb + PL::KE + (size_t)(16 * t + i) * DK + q * RW + 16 * rt + 4 * g);
+}
+
+template <int DK>
+__device__ __forceinline__ void adj_load1(AdjOps<DK>& o, const float* pb, int q) {
+    using PL = PrepLay<DK>;
+    const int i = lane_i(), g = lane_g();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) o.pt[kb][s] = kb >= q ? pb[PL::P + (size_t)(16 * kb + 4 * g + s) * C + 16 * q + i] : 0.f;
+}
+
+template <int DK>
+__device__ __forceinline__ void adj_load2(AdjOps<DK>& o, const Params& p, const float* pb, long t0, int n, int h,
+                                          int sl, int q) {
+    using PL = PrepLay<DK>;
+    constexpr int RW = DK / 4, RT = DK / 64;
+    const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            o.pt[kb][s] = kb >= q ? pb[PL::P + (size_t)(16 * kb + 4 * g + s) * C + 16 * q + i] : 0.f;
             const int tok = 16 * kb + 4 * g + s;
-            o.d[kb][s] = tok < n ? p.dO[((size_t)(t0 + tok) * H + h) * DV + 16 * sl + i] : 0.f;
+            const float dv = p.dO[((size_t)(t0 + min(tok, n - 1)) * H + h) * DV + 16 * sl + i];
+            o.d[kb][s] = tok < n ? dv : 0.f;
         }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -626,14 +693,13 @@ __device__ __forceinline__ void load_adj_ops(AdjOps<DK>& o, const Params& p, int
                 o.wt[rt][kb][s] = pb[PL::W + off];
             }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o.gm[rt][e] = pb[PL::GAM + q * RW + 16 * rt + 4 * g + e];
+    for (int rt = 0; rt < RT; ++rt) o.gm[rt] = *reinterpret_cast<const f32x4*>(pb + PL::GAM + q * RW + 16 * rt + 4 * g);
 }
 
 template <int DK>
 __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
     using SM = WalkSmem<DK>;
+    using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
     float *sPart = sm + SM::PART, *sdU = sm + SM::UT;
@@ -646,6 +712,7 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
     long bos, eos;
     int cs, ce;
     seq_range(p.map, s, bos, eos, cs, ce);
+    auto block = [&](int gi) { return p.prep + ((size_t)gi * H + h) * PL::FLOATS; };
 
     f32x4 D[RT];
 #pragma unroll
@@ -655,10 +722,25 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
             const int row = q * RW + 16 * rt + 4 * g + e;
             D[rt][e] = p.dST ? p.dST[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
         }
-    AdjOps<DK> cur, nxt;
-    if (cs < ce) load_adj_ops<DK>(cur, p, ce - 1, cs, bos, eos, h, sl, q);
+    AdjOps<DK> op;
+    if (cs < ce) {
+        long t0;
+        int n;
+        chunk_span(ce - 1, cs, bos, eos, t0, n);
+        adj_load0<DK>(op, block(ce - 1), q);
+        adj_load1<DK>(op, block(ce - 1), q);
+        adj_load2<DK>(op, p, block(ce - 1), t0, n, h, sl, q);
+    }
+    uint32_t sink = 0;
     for (int gi = ce - 1; gi >= cs; --gi) {
-        if (gi - 1 >= cs) load_adj_ops<DK>(nxt, p, gi - 1, cs, bos, eos, h, sl, q);
+        // P and W, K_end, Gamma o Q of chunk gi - 2 (the last three are adjacent)
+        const uint32_t tch =
+            gi - 2 >= cs ? touch_lines(block(gi - 2), PL::P, (size_t)C * C, PL::W, 3 * (size_t)C * DK, sl, NSL, tid) : 0u;
+        const bool more = gi - 1 >= cs;
+        const float* pn = block(more ? gi - 1 : gi);
+        long tn;
+        int nn;
+        chunk_span(more ? gi - 1 : gi, cs, bos, eos, tn, nn);
         float* ckD = p.ck + ((size_t)gi * H + h) * 2 * DK * DV + (size_t)DK * DV;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -668,32 +750,36 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
         for (int t = 0; t < 4; ++t) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc = mm4(cur.ke[t][rt], D[rt], acc);
+            for (int rt = 0; rt < RT; ++rt) acc = mm4(op.ke[t][rt], D[rt], acc);
             *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
         }
+        if (more) adj_load0<DK>(op, pn, q);
         __syncthreads();
         {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                if (kb >= q) acc = mm4(cur.pt[kb], cur.d[kb], acc);
+                if (kb >= q) acc = mm4(op.pt[kb], op.d[kb], acc);
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) acc += *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
             *reinterpret_cast<f32x4*>(sdU + (q * 64 + lane) * 4) = acc;
         }
+        if (more) adj_load1<DK>(op, pn, q);
         __syncthreads();
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                a1 = mm4(cur.qg[rt][kb], cur.d[kb], a1);
-                a2 = mm4(cur.wt[rt][kb], *reinterpret_cast<const f32x4*>(sdU + (kb * 64 + lane) * 4), a2);
+                a1 = mm4(op.qg[rt][kb], op.d[kb], a1);
+                a2 = mm4(op.wt[rt][kb], *reinterpret_cast<const f32x4*>(sdU + (kb * 64 + lane) * 4), a2);
             }
-            D[rt] = cur.gm[rt] * D[rt] + a1 - a2;
+            D[rt] = op.gm[rt] * D[rt] + a1 - a2;
         }
-        cur = nxt;
+        if (more) adj_load2<DK>(op, p, pn, tn, nn, h, sl, q);
+        sink ^= tch;
     }
+    if (sink == 0x9e3779b9u && p.H < 0) p.ck[0] = 0.f;
     if (p.gS0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -767,19 +853,41 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
 #pragma unroll
     for (int u = 0; u < NPW; ++u) acc[u] = zero4();
 
+    // The value-column block b + 1 (S, dS', dO, V) is fetched into registers
+    // while block b computes, and written to LDS at the start of its turn.
+    static_assert(DK * 4 <= 512 && C * 16 == 2 * 512, "value-block staging");
+    const int sr = tid / 4, sc = 4 * (tid % 4);
+    f32x4 nS = zero4(), nD = zero4();
+    float nO[2], nV[2];
+    auto fetch_block = [&](int b) {
+        if (tid < DK * 4) {
+            nS = *reinterpret_cast<const f32x4*>(ckS + (size_t)sr * DV + 16 * b + sc);
+            nD = *reinterpret_cast<const f32x4*>(ckD + (size_t)sr * DV + 16 * b + sc);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int x = tid + 512 * u, r = x / 16, c = x % 16;
+            const size_t row = (size_t)(t0 + min(r, n - 1)) * H + h;
+            const float ov = p.dO[row * DV + 16 * b + c], vv = ld_in((const TIn*)p.v + row * DV + 16 * b + c);
+            nO[u] = r < n ? ov : 0.f;
+            nV[u] = r < n ? vv : 0.f;
+        }
+    };
+    fetch_block(0);
+
     for (int b = 0; b < DV / 16; ++b) {
         __syncthreads();
-        for (int x = tid; x < DK * 4; x += 512) {
-            const int r = x / 4, c = 4 * (x % 4);
-            *reinterpret_cast<f32x4*>(sS + r * LS + c) = *reinterpret_cast<const f32x4*>(ckS + (size_t)r * DV + 16 * b + c);
-            *reinterpret_cast<f32x4*>(sD + r * LS + c) = *reinterpret_cast<const f32x4*>(ckD + (size_t)r * DV + 16 * b + c);
+        if (tid < DK * 4) {
+            *reinterpret_cast<f32x4*>(sS + sr * LS + sc) = nS;
+            *reinterpret_cast<f32x4*>(sD + sr * LS + sc) = nD;
         }
-        for (int x = tid; x < C * 16; x += 512) {
-            const int r = x / 16, c = x % 16;
-            const size_t row = (size_t)(t0 + r) * H + h;
-            sdO[r * LS + c] = r < n ? p.dO[row * DV + 16 * b + c] : 0.f;
-            sV[r * LS + c] = r < n ? ld_in((const TIn*)p.v + row * DV + 16 * b + c) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int x = tid + 512 * u, r = x / 16, c = x % 16;
+            sdO[r * LS + c] = nO[u];
+            sV[r * LS + c] = nV[u];
         }
+        if (b + 1 < DV / 16) fetch_block(b + 1);
         __syncthreads();
         if (w < 4) {   // U tile t = X (beta o V) - W S
             const int t = w;
@@ -872,16 +980,21 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     }
     {   // k into sKE, alpha into the (now free) value-slice buffers, then Gamma o K in place
         float* sAl = sm + SM::S;   // C x DK floats fit in S .. DU
-        for (int x = tid; x < C * DK; x += 512) {
-            const int r = x / DK, c = x % DK;
-            float kv = 0.f, av = 1.f;
-            if (r < n) {
-                const size_t row = (size_t)(t0 + r) * H + h;
-                kv = ld_in((const TIn*)p.k + row * DK + c);
-                av = gate_at<TIn>(p, row, DK, c, SG);
-            }
-            sKE[r * LK + c] = kv;
-            sAl[x] = av;
+        constexpr int KPT = C * DK / 512;
+        float nK[KPT], nA[KPT];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int x = tid + 512 * u, r = x / DK, c = x % DK;
+            const size_t row = (size_t)(t0 + min(r, n - 1)) * H + h;
+            const float kv = ld_in((const TIn*)p.k + row * DK + c), av = gate_at<TIn>(p, row, DK, c, SG);
+            nK[u] = r < n ? kv : 0.f;
+            nA[u] = r < n ? av : 1.f;
+        }
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int x = tid + 512 * u, r = x / DK, c = x % DK;
+            sKE[r * LK + c] = nK[u];
+            sAl[x] = nA[u];
         }
         __syncthreads();
         if (tid < DK) {
@@ -1261,23 +1374,15 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
         const int ch = CB * cb + c;
         GateRegs x;
         float dqg[8], dgk[8], dke[8];
+        load_rows<TIn, SG>(gk, gq, ga, rs, H, n, r0, ch, x.a, x.k, x.q);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = r0 + j;
-            x.k[j] = 0.f;
-            x.q[j] = 0.f;
-            x.a[j] = 1.f;
-            dqg[j] = dgk[j] = dke[j] = 0.f;
-            if (r < n) {
-                const unsigned o = (unsigned)r * rs + ch;
-                x.k[j] = ld_in(gk + o);
-                x.q[j] = ld_in(gq + o);
-                x.a[j] = SG ? ld_in(ga + (unsigned)r * H) : ld_in(ga + o);
-                const unsigned off = (unsigned)r * DK + ch;
-                dqg[j] = pb[PL::QG + off];
-                dgk[j] = pb[PL::W + off];
-                dke[j] = pb[PL::KE + off];
-            }
+            const unsigned off = (unsigned)r * DK + ch;   // every row of the block is written
+            const float v0 = pb[PL::QG + off], v1 = pb[PL::W + off], v2 = pb[PL::KE + off];
+            dqg[j] = r < n ? v0 : 0.f;
+            dgk[j] = r < n ? v1 : 0.f;
+            dke[j] = r < n ? v2 : 0.f;
         }
         // local products, and the local forward scan of drel_end = dK_end o k
         float lp[8], ml[8];

@@ -246,7 +246,13 @@ struct Gx {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) v[t][j] = x;
     }
-    __device__ __forceinline__ void fill_from(const float* p, int t) { fill(t, *p); }
+    // one value for every channel: fill_from only loads, widen (after all the
+    // loads are issued) copies it to the other channels
+    __device__ __forceinline__ void fill_from(const float* p, int t) { v[t][0] = *p; }
+    __device__ __forceinline__ void widen(int t) {
+#pragma unroll
+        for (int j = 1; j < CPL; ++j) v[t][j] = v[t][0];
+    }
 };
 template <int CPL>
 struct Gx<uint16_t, CPL> {
@@ -262,9 +268,9 @@ struct Gx<uint16_t, CPL> {
         const uint32_t b = __float_as_uint(x) >> 16;
         w[t] = CPL == 2 ? (b | (b << 16)) : b;
     }
-    __device__ __forceinline__ void fill_from(const uint16_t* p, int t) {
-        const uint32_t b = *p;
-        w[t] = CPL == 2 ? (b | (b << 16)) : b;
+    __device__ __forceinline__ void fill_from(const uint16_t* p, int t) { w[t] = *p; }
+    __device__ __forceinline__ void widen(int t) {
+        if constexpr (CPL == 2) w[t] = w[t] | (w[t] << 16);
     }
 };
 
@@ -440,21 +446,29 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
     const int c0 = lane * CPL;
     Gx<TIn, CPL> kk, qq, aa, ee;
     float mk = 0.f, mq = 0.f, me = 0.f;
+    // Rows past the chunk end read row n - 1 (n >= 1) and are replaced after
+    // the loads: no branch or use of a loaded value between two loads, so all
+    // 16 rows are in flight together.
+    if (gate_lane) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const int tl = 16 * b + t;
-        if (gate_lane && tl < n) {
-            const size_t row = (size_t)(t0 + tl) * H + h;
+        for (int t = 0; t < 16; ++t) {
+            const size_t row = (size_t)(t0 + min(16 * b + t, n - 1)) * H + h;
             kk.load(gk + row * DK + c0, t);
             qq.load(gq + row * DK + c0, t);
             if constexpr (SG) aa.fill_from(gg + row, t);
             else aa.load(gg + row * DK + c0, t);
             if constexpr (EW) ee.load((const TIn*)p.erase + row * DK + c0, t);
-        } else {
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        if (!gate_lane || 16 * b + t >= n) {
             kk.fill(t, 0.f);
             qq.fill(t, 0.f);
             aa.fill(t, 1.f);
             if constexpr (EW) ee.fill(t, 0.f);
+        } else if constexpr (SG) {
+            aa.widen(t);
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
