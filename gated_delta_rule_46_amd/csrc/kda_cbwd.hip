@@ -807,7 +807,7 @@ struct GradSmem {
     static constexpr size_t DU = U + (size_t)C * LS, BETA = DU + (size_t)C * LS, DG = BETA + C, DB = DG + DK;
     static constexpr size_t FLOATS = DB + 4 * C;
     static constexpr size_t BYTES = FLOATS * 4;
-    static_assert(BETA - S >= (size_t)C * DK, "alpha staging fits the value-slice buffers");
+    static_assert(BETA - S >= 512, "the gate part products fit the value-block buffers");
 };
 
 template <class TIn, int DK, bool SG>
@@ -978,34 +978,35 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
             for (int e = 0; e < 4; ++e) pb[PL::P + (size_t)(16 * R + 4 * g + e) * C + 16 * J + i] = acc[u][e];
         }
     }
-    {   // k into sKE, alpha into the (now free) value-slice buffers, then Gamma o K in place
-        float* sAl = sm + SM::S;   // C x DK floats fit in S .. DU
-        constexpr int KPT = C * DK / 512;
-        float nK[KPT], nA[KPT];
+    {   // Gamma o K into sKE. Thread (c, part) holds the RPP consecutive rows
+        // part RPP .. of channel c in registers; the product of the gates
+        // before its rows comes from the other parts' products (LDS table in
+        // the now free value-block buffers).
+        constexpr int NPART = 512 / DK, RPP = C / NPART;
+        float* sPP = sm + SM::S;   // [NPART][DK]
+        const int c = tid % DK, part = tid / DK;
+        float kr[RPP], lp[RPP];
+        float f = 1.f;
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int x = tid + 512 * u, r = x / DK, c = x % DK;
+        for (int j = 0; j < RPP; ++j) {
+            const int r = part * RPP + j;
             const size_t row = (size_t)(t0 + min(r, n - 1)) * H + h;
             const float kv = ld_in((const TIn*)p.k + row * DK + c), av = gate_at<TIn>(p, row, DK, c, SG);
-            nK[u] = r < n ? kv : 0.f;
-            nA[u] = r < n ? av : 1.f;
+            kr[j] = r < n ? kv : 0.f;
+            lp[j] = r < n ? av : 1.f;
         }
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int x = tid + 512 * u, r = x / DK, c = x % DK;
-            sKE[r * LK + c] = nK[u];
-            sAl[x] = nA[u];
+        for (int j = 0; j < RPP; ++j) {
+            f *= lp[j];
+            lp[j] = f;
         }
+        sPP[part * DK + c] = f;
+        if (tid < DK) pb[PL::GAM + tid] = sdg[tid];
         __syncthreads();
-        if (tid < DK) {
-            float gm = 1.f;
-#pragma unroll 16
-            for (int r = 0; r < C; ++r) {
-                gm *= sAl[r * DK + tid];
-                sKE[r * LK + tid] *= gm;
-            }
-            pb[PL::GAM + tid] = sdg[tid];
-        }
+        float pfx = 1.f;
+        for (int qq = 0; qq < part; ++qq) pfx *= sPP[qq * DK + c];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) sKE[(part * RPP + j) * LK + c] = kr[j] * (pfx * lp[j]);
     }
     __syncthreads();
     // ---- dX += dW (beta o Gamma o K)^T (tiles already owned), then dX out
