@@ -40,6 +40,7 @@ METRIC = "tokens/s KDA chunk fwd (H=16,d=128,T=8192) + decode GB/s, % roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
 def fwd_bytes_per_head_token(dk: int, dv: int, scalar_gate: bool, in_bytes: int = 2) -> int:
@@ -69,6 +70,22 @@ def bwd_flops_per_head_token(dk: int, dv: int) -> int:
     state element) and the adjoint step (18 per state element: S', q dO^T,
     dS^T k, S_t dO, dS u, S' dpred, dS', dalpha, Diag(alpha) dS')."""
     return 23 * dk * dv
+
+
+def cbwd_flops_per_head_chunk(dk: int, dv: int, C: int = 64) -> int:
+    """Algorithmic fp32 matrix flops of the chunkwise backward per (chunk,
+    head), each contraction counted once (2 flops per multiply-add) and a
+    lower-triangular C x C operand at half:
+      C x dk x dv, 8 of them: W S and K_end^T U (forward state step),
+        K_end dS', (Gamma Q)^T dO and W^T dU (adjoint step), dO S^T, dU S^T
+        and U dS'^T (gradients);
+      lower C x C by dv columns, 5: X(beta V), P^T dO, dO U^T, dU (beta V)^T,
+        X^T dU;
+      lower C x C by dk columns, 8: the gated Gram matrices G and P,
+        W = X(beta Gamma K), dW (beta Gamma K)^T, X^T dW and the three level
+        products of the gate side;
+      C^3 / 3 multiply-adds, 3: the inverse X, dX X^T and X^T T."""
+    return 16 * C * dk * dv + 5 * C * C * dv + 8 * C * C * dk + 2 * C ** 3
 
 
 def decode_bytes_per_head_step(dk: int, dv: int, in_bytes: int = 2) -> int:
@@ -388,33 +405,43 @@ def main(argv=None) -> int:
         dO_c, dST_c = inputs.cotangents(wb, seed=0)
         bt = [t.to(dev) for t in (wb.q, wb.k, wb.v, wb.gate, wb.beta, dO_c)]
         dST = dST_c.to(dev)
-        wsb_b = kda.bwd_workspace_bytes(B, H, T, dk, dv)
-        ws_b = torch.empty(wsb_b, device=dev, dtype=torch.uint8)
-        gout = kda.chunk_bwd(*bt, dS_T=dST, workspace=ws_b)
-
-        def bwd(i):
-            kda.chunk_bwd(*bt, dS_T=dST, workspace=ws_b, out=gout)
-
-        for i in range(5):   # about 35 ms: the clock ramps up again after the host-side input generation
-            bwd(i)
-        ms_b = time_region(bwd, args.bwd_steps, stream)
-        bflops = tokens * H * bwd_flops_per_head_token(dk, dv)
         bbytes = tokens * H * bwd_bytes_per_head_token(dk, dv) + 3 * B * H * dk * dv * 4
+        legs = {}
+        for form, chunked in (("chunkwise", True), ("token", False)):
+            wsb = (kda.bwd_cw_workspace_bytes if chunked else kda.bwd_workspace_bytes)(B, H, T, dk, dv)
+            ws_b = torch.empty(wsb, device=dev, dtype=torch.uint8)
+            gout = kda.chunk_bwd(*bt, dS_T=dST, workspace=ws_b, chunked=chunked)
+
+            def bwd(i):
+                kda.chunk_bwd(*bt, dS_T=dST, workspace=ws_b, out=gout, chunked=chunked)
+
+            for i in range(5):   # the clock ramps up again after the host-side input generation
+                bwd(i)
+            legs[form] = (time_region(bwd, args.bwd_steps, stream), wsb)
+            print("[bench] backward (%s) %.3f ms/call" % (form, legs[form][0]), file=sys.stderr, flush=True)
+            del ws_b, gout
+        ms_b, wsb_b = legs["chunkwise"]
+        ms_t, wsb_t = legs["token"]
+        bflops = B * H * ((T + 63) // 64) * cbwd_flops_per_head_chunk(dk, dv, 64)   # its chunk is 64
         tf = bflops / (ms_b * 1e-3) / 1e12
         gbs_b = bbytes / (ms_b * 1e-3) / 1e9
+        tflops = tokens * H * bwd_flops_per_head_token(dk, dv)
         backward = {
             "workload": "ckda_bwd_b2_h16_t8192_d128",
             "ms_per_call": round(ms_b, 4),
             "tokens_per_s": round(tokens / (ms_b * 1e-3), 1),
             "calls": args.bwd_steps,
-            "roofline": {"bound": "alu", "achieved": round(tf, 3), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic_bwd,
-                         "kernel": "kda_chunk_bwd: chunk_bwd_kernel then chunk_bwd_reduce_kernel",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": traffic_bwd,
+                         "kernel": "kda_chunk_bwd_cw: cb_prep, cb_state, cb_adjoint, cb_grad_state, cb_grad_gate "
+                                   "(fp32 MFMA, one stream)",
                          "flops_per_launch": bflops, "hbm_bytes_algorithmic": bbytes,
                          "hbm_frac_algorithmic": round(gbs_b / HBM_PEAK_GBS, 4)},
             "workspace_bytes": wsb_b,
+            "token_form": {"ms_per_call": round(ms_t, 4), "workspace_bytes": wsb_t,
+                           "kernel": "kda_chunk_bwd: chunk_bwd_kernel then chunk_bwd_reduce_kernel",
+                           "alu_frac": round(tflops / (ms_t * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4)},
         }
-        print("[bench] backward %.3f ms/call" % ms_b, file=sys.stderr, flush=True)
         if not args.no_cpu_baseline:
             import oracle
             # the oracle keeps every state of a sequence (dk*dv doubles per
@@ -436,7 +463,7 @@ def main(argv=None) -> int:
                 "sample": "first 2048 tokens of both sequences, all 16 heads, fp64 reverse-mode token recurrence, "
                           "%d pass(es), %.2f s each" % (reps, dt)}
             print("[bench] backward oracle %.2f s per pass" % dt, file=sys.stderr, flush=True)
-        del bt, ws_b, gout
+        del bt
 
     # ------------------------------------------------- Complex KDA against KDA
     # The pages compare forward-plus-backward kernel throughput of Complex KDA
@@ -455,10 +482,10 @@ def main(argv=None) -> int:
             t = [x.to(dev) for x in (w.q, w.k, w.v, w.gate, w.beta)]
             runs[name] = (t, dO_r.to(dev), dST_r.to(dev))
         ws_f = torch.empty(kda.workspace_bytes(Br, H, Tr, dk, dv, C), device=dev, dtype=torch.uint8)
-        ws_r = torch.empty(kda.bwd_workspace_bytes(Br, H, Tr, dk, dv), device=dev, dtype=torch.uint8)
+        ws_r = torch.empty(kda.bwd_cw_workspace_bytes(Br, H, Tr, dk, dv), device=dev, dtype=torch.uint8)
         o_r = torch.empty((Br, Tr, H, dv), device=dev, dtype=torch.float32)
         ST_r = torch.empty((Br, H, dk, dv), device=dev, dtype=torch.float32)
-        g_r = kda.chunk_bwd(*runs["kda"][0], runs["kda"][1], dS_T=runs["kda"][2], workspace=ws_r)
+        g_r = kda.chunk_bwd(*runs["kda"][0], runs["kda"][1], dS_T=runs["kda"][2], workspace=ws_r, chunked=True)
         times = {"kda": [[], []], "ckda": [[], []]}
         for rep_i in range(2):
             for name in (("kda", "ckda") if rep_i == 0 else ("ckda", "kda")):
@@ -468,7 +495,7 @@ def main(argv=None) -> int:
                     kda.chunk_fwd(*t, chunk=C, gate_kind=0, out=o_r, S_T=ST_r, workspace=ws_f)
 
                 def b_r(i):
-                    kda.chunk_bwd(*t, dO_r, dS_T=dST_r, workspace=ws_r, out=g_r)
+                    kda.chunk_bwd(*t, dO_r, dS_T=dST_r, workspace=ws_r, out=g_r, chunked=True)
 
                 for i in range(args.warmup):
                     f_r(i)

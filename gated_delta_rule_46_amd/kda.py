@@ -262,13 +262,17 @@ def bwd_cw_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, N: int = 0,
 
 def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate_kind: Optional[int] = None,
               want_dS0: bool = True, out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-              stream=None, chunked: bool = False) -> dict:
+              stream=None, chunked: Optional[bool] = None) -> dict:
     """Gradient of chunk_fwd for L = sum(o * dO) + sum(S_T * dS_T). Inputs as
     for chunk_fwd; dO fp32 [B,T,H,dv]; dS_T fp32 [N,H,dk,dv] or None. Returns
     a dict of fp32 tensors dq, dk, dv, dgate, dbeta (input layouts) and dS0
     ([N,H,dk,dv], or None when not wanted). ``out`` may supply that dict's
-    tensors to write into."""
+    tensors to write into. ``chunked`` picks kda_chunk_bwd_cw (True) or the
+    token-form kda_chunk_bwd (False); None takes the chunkwise form where it
+    applies (dk = 64 or 128) and the token form elsewhere."""
     B, T, H, dk, dv, gate_kind = _check_seq_inputs(q, k, v, gate, beta, gate_kind)
+    if chunked is None:
+        chunked = dk in (64, 128)
     if dO.dtype != torch.float32 or tuple(dO.shape) != (B, T, H, dv):
         raise ValueError("dO must be fp32 [%d,%d,%d,%d]" % (B, T, H, dv))
     N = B if cu_seqlens is None else int(cu_seqlens.numel() - 1)

@@ -1,10 +1,12 @@
 """A short, fixed workload to run under rocprofv3.
 
-    python -m gated_delta_rule_46_amd.profile_run [--fwd 3] [--bwd 2] [--decode 8] [--copy-mib 256]
+    python -m gated_delta_rule_46_amd.profile_run [--fwd 3] [--bwd 2] [--bwd-token 0] [--decode 8]
+                                                  [--copy-mib 256]
 
 Runs, on cuda:0 and with seeded synthetic inputs: --fwd forward calls on the
 Complex KDA workload (B=2, H=16, T=8192, d=128, bf16, chunk 64), --bwd
-backward calls on the same workload, --decode decode steps on the decode
+chunkwise backward calls (kda_chunk_bwd_cw) and --bwd-token token-form
+backward calls (kda_chunk_bwd) on the same workload, --decode decode steps on the decode
 workload (N=256, H=32, d=128, fp32 state in place), and --copy-mib MiB of
 plain device-to-device copy (one read and one write of that many bytes per
 call, three calls), whose counter readings calibrate FETCH_SIZE and
@@ -21,6 +23,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--fwd", type=int, default=3)
     ap.add_argument("--bwd", type=int, default=2)
+    ap.add_argument("--bwd-token", type=int, default=0)
     ap.add_argument("--decode", type=int, default=8)
     ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args(argv)
@@ -43,17 +46,20 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print("forward calls: %d" % args.fwd, flush=True)
         del q, k, v, g, b, ws, o, ST
-    if args.bwd > 0:
+    for calls, chunked in ((args.bwd, True), (args.bwd_token, False)):
+        if calls <= 0:
+            continue
         w = inputs.ckda_fwd(seed=0)
         dO, dST = inputs.cotangents(w, seed=0)
         t = [x.to(dev) for x in (w.q, w.k, w.v, w.gate, w.beta, dO)]
         dST = dST.to(dev)
-        ws = torch.empty(kda.bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), device=dev, dtype=torch.uint8)
-        g = kda.chunk_bwd(*t, dS_T=dST, workspace=ws)
-        for _ in range(args.bwd - 1):
-            kda.chunk_bwd(*t, dS_T=dST, workspace=ws, out=g)
+        need = (kda.bwd_cw_workspace_bytes if chunked else kda.bwd_workspace_bytes)(w.B, w.H, w.T, w.dk, w.dv)
+        ws = torch.empty(need, device=dev, dtype=torch.uint8)
+        g = kda.chunk_bwd(*t, dS_T=dST, workspace=ws, chunked=chunked)
+        for _ in range(calls - 1):
+            kda.chunk_bwd(*t, dS_T=dST, workspace=ws, out=g, chunked=chunked)
         torch.cuda.synchronize()
-        print("backward calls: %d" % args.bwd, flush=True)
+        print("%s backward calls: %d" % ("chunkwise" if chunked else "token-form", calls), flush=True)
         del t, dST, ws, g
     if args.decode > 0:
         dw = inputs.ckda_decode(n_steps=min(args.decode, 16))

@@ -1,5 +1,6 @@
-"""GPU parity of the backward (kda_chunk_bwd through the C ABI) against the
-fp64 oracle's gradient (``oracle.bwd``).
+"""GPU parity of the token-form backward (kda_chunk_bwd through the C ABI)
+against the fp64 oracle's gradient (``oracle.bwd``); the chunkwise form
+(kda_chunk_bwd_cw) has its own file.
 
 Metric per gradient: err = max|g_gpu - g_ref| / rms(g_ref). The backward
 computes in fp32 from the exact input values (bf16 inputs are converted
@@ -41,7 +42,7 @@ def err(x, ref):
 def gpu_bwd(kda, w, dO, dST):
     d = lambda t: None if t is None else t.cuda()  # noqa: E731
     g = kda.chunk_bwd(d(w.q), d(w.k), d(w.v), d(w.gate), d(w.beta), d(dO), S0=d(w.S0), dS_T=d(dST),
-                      cu_seqlens=d(w.cu_seqlens), gate_kind=w.gate_kind)
+                      cu_seqlens=d(w.cu_seqlens), gate_kind=w.gate_kind, chunked=False)
     torch.cuda.synchronize()
     return {n: (None if g[n] is None else g[n].cpu()) for n in NAMES}
 

@@ -107,12 +107,14 @@ def test_backward_sweep(kda, seed):
     print("case", w.name, "B", w.B, "H", w.H, "T", w.T, "dk", w.dk, "dv", w.dv, w.q.dtype, "gate kind", w.gate_kind,
           "varlen", w.cu_seqlens is not None, flush=True)
     dO, dST = inputs.cotangents(w, seed=seed, with_dS_T=seed % 3 != 0)
-    g = kda.chunk_bwd(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), dev(dO), S0=dev(w.S0), dS_T=dev(dST),
-                      cu_seqlens=dev(w.cu_seqlens), gate_kind=w.gate_kind)
-    torch.cuda.synchronize()
     r = oracle.bwd(w.q, w.k, w.v, w.gate, w.beta, dO, w.S0, dST, w.cu_seqlens, w.gate_kind)
-    errs = {n: err(g[n], r[n]) for n in NAMES}
-    assert max(errs.values()) <= 1e-4, errs
+    # the token form everywhere, the chunkwise form where it applies (dk 64, 128)
+    for chunked in (False, True) if w.dk in (64, 128) else (False,):
+        g = kda.chunk_bwd(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), dev(dO), S0=dev(w.S0),
+                          dS_T=dev(dST), cu_seqlens=dev(w.cu_seqlens), gate_kind=w.gate_kind, chunked=chunked)
+        torch.cuda.synchronize()
+        errs = {n: err(g[n], r[n]) for n in NAMES}
+        assert max(errs.values()) <= 1e-4, (chunked, errs)
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -137,12 +139,13 @@ def test_large_sweep(kda, seed):
           "gate kind", w.gate_kind, "varlen", w.cu_seqlens is not None, flush=True)
     if kind == "bwd":
         dO, dST = inputs.cotangents(w, seed=seed, with_dS_T=seed % 2 == 0)
-        g = kda.chunk_bwd(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), dev(dO), S0=dev(w.S0),
-                          dS_T=dev(dST), cu_seqlens=dev(w.cu_seqlens), gate_kind=w.gate_kind)
-        torch.cuda.synchronize()
         r = oracle.bwd(w.q, w.k, w.v, w.gate, w.beta, dO, w.S0, dST, w.cu_seqlens, w.gate_kind)
-        errs = {n: err(g[n], r[n]) for n in NAMES}
-        assert max(errs.values()) <= 1e-4, errs
+        for chunked in (False, True) if w.dk in (64, 128) else (False,):
+            g = kda.chunk_bwd(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), dev(dO), S0=dev(w.S0),
+                              dS_T=dev(dST), cu_seqlens=dev(w.cu_seqlens), gate_kind=w.gate_kind, chunked=chunked)
+            torch.cuda.synchronize()
+            errs = {n: err(g[n], r[n]) for n in NAMES}
+            assert max(errs.values()) <= 1e-4, (chunked, errs)
         return
     fn = kda.chunk_fwd if kind == "fwd" else kda.chunk_fwd_gauge
     o, ST = fn(dev(w.q), dev(w.k), dev(w.v), dev(w.gate), dev(w.beta), S0=dev(w.S0), cu_seqlens=dev(w.cu_seqlens),
