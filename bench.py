@@ -92,31 +92,32 @@ def decode_bytes_per_head_step(dk: int, dv: int, in_bytes: int = 2) -> int:
     return 8 * dk * dv + in_bytes * (3 * dk + dv + 1) + 4 * dv
 
 
-def _traffic_record(name: str) -> dict:
-    """A committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or {} when the
-    kernel sources it names have changed since the counters were taken."""
+def measured_traffic():
+    """Measured HBM bytes per forward call, per decode step and per
+    chunkwise-backward call, from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (profiles/hbm_traffic_ckda.txt); None for a group whose
+    kernel sources have changed since its counters were taken."""
     import hashlib
     try:
-        with open(os.path.join(ROOT, "profiles", name)) as f:
-            rec = json.load(f)
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic_ckda.txt")) as f:
+            groups = json.load(f).get("groups", {})
     except (OSError, ValueError):
-        return {}
-    for rel, digest in rec.get("sources_sha256", {}).items():
-        try:
-            with open(os.path.join(ROOT, rel), "rb") as f:
-                if hashlib.sha256(f.read()).hexdigest() != digest:
-                    return {}
-        except OSError:
-            return {}
-    return rec
+        return None, None, None
 
+    def get(name, key):
+        g = groups.get(name)
+        if not g:
+            return None
+        for rel, digest in g.get("sources_sha256", {}).items():
+            try:
+                with open(os.path.join(ROOT, rel), "rb") as f:
+                    if hashlib.sha256(f.read()).hexdigest() != digest:
+                        return None
+            except OSError:
+                return None
+        return g.get(key)
 
-def measured_traffic():
-    """Measured HBM bytes per forward call, per decode step and per backward
-    call (None where the profiled sources no longer match)."""
-    fd = _traffic_record("hbm_traffic_ckda_fwd_decode.txt")
-    bw = _traffic_record("hbm_traffic_ckda_bwd.txt")
-    return fd.get("forward_bytes_per_call"), fd.get("decode_bytes_per_step"), bw.get("backward_bytes_per_call")
+    return (get("forward", "bytes_per_call"), get("decode", "bytes_per_step"), get("backward", "bytes_per_call"))
 
 
 def time_region(fn, iters: int, stream):
