@@ -31,8 +31,8 @@
 //
 // Kernels (one stream, in order):
 //   1. cb_prep_kernel       (chunk, head) parallel: G, P, X, W, K_end, Gamma o Q, gamma
-//   2. cb_state_kernel      sequential per (sequence, head, 16 value columns): S at every chunk start
-//   3. cb_adjoint_kernel    sequential backwards: dS' at every chunk end; dS0
+//   2. cb_walk_kernel       two sequential walks in one launch, per (sequence, head, 16 value columns):
+//                           forward, S at every chunk start; backward, dS' at every chunk end and dS0
 //   4. cb_grad_state_kernel (chunk, head) parallel: dv; d(Gamma o Q), dK_end, dP, dX, d(Gamma o K), dgamma, beta parts
 //   5. cb_grad_gate_kernel  (chunk, head) parallel: dA, dG, dq, dk, dalpha, dbeta
 // All operands fp32; products on v_mfma_f32_16x16x4f32 with fp32 accumulation.
@@ -433,16 +433,19 @@ __global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
 }
 
 // ================================================================ 2. states at chunk starts
-// One workgroup (4 waves) per (sequence, head, 16 value columns). Wave q keeps
-// state rows q dk/4 .. (q+1) dk/4 - 1 of the slice as D tiles. Per chunk:
-// store S; partial W S over own rows (to LDS); U = X (beta o V) - W S for
-// token tile q; S <- Diag(gamma) S + K_end^T U for own rows. The chunk's
-// operands go from global memory straight into registers, one chunk ahead.
-template <int DK>
+// One workgroup (4 waves) per (sequence, head, slice of 16 CT value columns).
+// Wave q keeps state rows q dk/4 .. (q+1) dk/4 - 1 of the slice as D tiles
+// (CT column tiles). Per chunk: store S; partial W S over own rows (to LDS);
+// U = X (beta o V) - W S for token tile q; S <- Diag(gamma) S + K_end^T U for
+// own rows. The chunk's operands go from global memory straight into
+// registers, one chunk ahead. The A operands (W, X, K_end^T) are the same for
+// every column tile: a slice of two tiles reads them once for both, which
+// halves what the slices of one (sequence, head) read from L2 per step.
+template <int DK, int CT>
 struct WalkSmem {
-    static constexpr size_t PART = 0;                 // [4 waves][4 tiles][64 lanes][4]
-    static constexpr size_t UT = PART + 4 * 4 * 256;  // [4 tiles][64 lanes][4]
-    static constexpr size_t FLOATS = UT + 4 * 256;
+    static constexpr size_t PART = 0;                      // [4 waves][4 tiles][CT][64 lanes][4]
+    static constexpr size_t UT = PART + 4 * 4 * CT * 256;  // [4 tiles][CT][64 lanes][4]
+    static constexpr size_t FLOATS = UT + 4 * CT * 256;
     static constexpr size_t BYTES = FLOATS * 4;
 };
 
@@ -464,14 +467,14 @@ __device__ __forceinline__ void seq_range(const ChunkMap& m, int s, long& bos, l
 // the groups in which they are reloaded for the next chunk: each group right
 // after its last use in the current one, so that one register set suffices
 // and the loads spread over the step.
-template <int DK>
+template <int DK, int CT>
 struct StateOps {
     static constexpr int RT = DK / 64;
-    f32x4 w[4][RT];    // group 0: W[16t + i][own channels], A operand over own channels
-    f32x4 x[4];        // group 1: X[16q + i][16kb..], A operand over tokens
-    f32x4 v[4];        //          beta o V (K = tokens), B operand
-    f32x4 ke[RT][4];   // group 2: K_end^T[own rows][16kb..], A operand over tokens
-    f32x4 gm[RT];      //          gamma of own rows
+    f32x4 w[4][RT];      // group 0: W[16t + i][own channels], A operand over own channels
+    f32x4 x[4];          // group 1: X[16q + i][16kb..], A operand over tokens
+    f32x4 v[CT][4];      //          beta o V (K = tokens) per column tile, B operand
+    f32x4 ke[RT][4];     // group 2: K_end^T[own rows][16kb..], A operand over tokens
+    f32x4 gm[RT];        //          gamma of own rows
 };
 
 // Where chunk gi starts and how many tokens it has.
@@ -480,8 +483,8 @@ __device__ __forceinline__ void chunk_span(int gi, int cs, long bos, long eos, l
     n = (int)min((long)C, eos - t0);
 }
 
-template <int DK>
-__device__ __forceinline__ void state_load0(StateOps<DK>& o, const float* pb, int q) {
+template <int DK, int CT>
+__device__ __forceinline__ void state_load0(StateOps<DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     const int i = lane_i(), g = lane_g();
@@ -492,9 +495,9 @@ __device__ __forceinline__ void state_load0(StateOps<DK>& o, const float* pb, in
             o.w[t][rt] = *reinterpret_cast<const f32x4*>(pb + PL::W + (size_t)(16 * t + i) * DK + q * RW + 16 * rt + 4 * g);
 }
 
-template <class TIn, int DK>
-__device__ __forceinline__ void state_load1(StateOps<DK>& o, const Params& p, const float* pb, long t0, int n, int h,
-                                            int sl, int q) {
+template <class TIn, int DK, int CT>
+__device__ __forceinline__ void state_load1(StateOps<DK, CT>& o, const Params& p, const float* pb, long t0, int n,
+                                            int h, int sl, int q) {
     using PL = PrepLay<DK>;
     const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
 #pragma unroll
@@ -507,13 +510,17 @@ __device__ __forceinline__ void state_load1(StateOps<DK>& o, const Params& p, co
         for (int s = 0; s < 4; ++s) {
             const int tok = 16 * kb + 4 * g + s;
             const size_t row = (size_t)(t0 + min(tok, n - 1)) * H + h;
-            const float bv = ld_in((const TIn*)p.beta + row), vv = ld_in((const TIn*)p.v + row * DV + 16 * sl + i);
-            o.v[kb][s] = tok < n ? bv * vv : 0.f;
+            const float bv = ld_in((const TIn*)p.beta + row);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const float vv = ld_in((const TIn*)p.v + row * DV + 16 * (CT * sl + ct) + i);
+                o.v[ct][kb][s] = tok < n ? bv * vv : 0.f;
+            }
         }
 }
 
-template <int DK>
-__device__ __forceinline__ void state_load2(StateOps<DK>& o, const float* pb, int q) {
+template <int DK, int CT>
+__device__ __forceinline__ void state_load2(StateOps<DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     const int i = lane_i(), g = lane_g();
@@ -530,9 +537,9 @@ __device__ __forceinline__ void state_load2(StateOps<DK>& o, const float* pb, in
 // First touch of a chunk two steps ahead: the slices of one (sequence,
 // head) run on one XCD and split the 128-byte lines of the per-chunk blocks
 // they all read between them (so that the reloads one step ahead find them in
-// L2); a slice touches the lines of its own value columns itself. The value
-// is only folded into a sink, so nothing waits for it until the step ends.
-// The two spans are [a0, a0 + na) and [b0, b0 + nb) in floats of the block.
+// L2). The value is only folded into a sink, so nothing waits for it until
+// the step ends. The two spans are [a0, a0 + na) and [b0, b0 + nb) in floats
+// of the block.
 __device__ __forceinline__ uint32_t touch_lines(const float* blk, size_t a0, size_t na, size_t b0, size_t nb, int sl,
                                                 int nsl, int tid) {
     const size_t la = na / 32, lb = nb / 32;   // 32 floats per line
@@ -542,16 +549,15 @@ __device__ __forceinline__ uint32_t touch_lines(const float* blk, size_t a0, siz
     return 0u;
 }
 
-template <class TIn, int DK>
-__global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
-    using SM = WalkSmem<DK>;
+template <class TIn, int DK, int CT>
+__device__ __forceinline__ void state_walk(const Params& p, int item) {
+    using SM = WalkSmem<DK, CT>;
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
     float *sPart = sm + SM::PART, *sU = sm + SM::UT;
 
-    const int H = p.H, DV = p.DV, NSL = DV / 16;
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int H = p.H, DV = p.DV, NSL = DV / (16 * CT);
     const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
     const int tid = threadIdx.x, q = tid / WAVE, lane = tid % WAVE;
     const int i = lane_i(), g = lane_g();
@@ -560,22 +566,25 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
     seq_range(p.map, s, bos, eos, cs, ce);
     auto block = [&](int gi) { return p.prep + ((size_t)gi * H + h) * PL::FLOATS; };
 
-    f32x4 S[RT];
+    f32x4 S[CT][RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = q * RW + 16 * rt + 4 * g + e;
-            S[rt][e] = p.S0 ? p.S0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
-        }
-    StateOps<DK> op;
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = q * RW + 16 * rt + 4 * g + e;
+                S[ct][rt][e] =
+                    p.S0 ? p.S0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * (CT * sl + ct) + i] : 0.f;
+            }
+    StateOps<DK, CT> op;
     if (cs < ce) {
         long t0;
         int n;
         chunk_span(cs, cs, bos, eos, t0, n);
-        state_load0<DK>(op, block(cs), q);
-        state_load1<TIn, DK>(op, p, block(cs), t0, n, h, sl, q);
-        state_load2<DK>(op, block(cs), q);
+        state_load0<DK, CT>(op, block(cs), q);
+        state_load1<TIn, DK, CT>(op, p, block(cs), t0, n, h, sl, q);
+        state_load2<DK, CT>(op, block(cs), q);
     }
     uint32_t sink = 0;
     for (int gi = cs; gi < ce; ++gi) {
@@ -589,40 +598,50 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
         chunk_span(more ? gi + 1 : gi, cs, bos, eos, tn, nn);
         float* ckS = p.ck + ((size_t)gi * H + h) * 2 * DK * DV;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ckS[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * sl + i] = S[rt][e];
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ckS[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * (CT * sl + ct) + i] = S[ct][rt][e];
         // partial W S over own rows, every token tile
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = zero4();
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc = mm4(op.w[t][rt], S[rt], acc);
-            *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
-        }
-        if (more) state_load0<DK>(op, pn, q);
+            for (int ct = 0; ct < CT; ++ct) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) acc = mm4(op.w[t][rt], S[ct][rt], acc);
+                *reinterpret_cast<f32x4*>(sPart + (((q * 4 + t) * CT + ct) * 64 + lane) * 4) = acc;
+            }
+        if (more) state_load0<DK, CT>(op, pn, q);
         __syncthreads();
         // U tile q = X (beta o V) - W S
-        {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                if (kb <= q) acc = mm4(op.x[kb], op.v[kb], acc);
+                if (kb <= q) acc = mm4(op.x[kb], op.v[ct][kb], acc);
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) acc -= *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
-            *reinterpret_cast<f32x4*>(sU + (q * 64 + lane) * 4) = acc;
+            for (int w2 = 0; w2 < 4; ++w2)
+                acc -= *reinterpret_cast<const f32x4*>(sPart + (((w2 * 4 + q) * CT + ct) * 64 + lane) * 4);
+            *reinterpret_cast<f32x4*>(sU + ((q * CT + ct) * 64 + lane) * 4) = acc;
         }
-        if (more) state_load1<TIn, DK>(op, p, pn, tn, nn, h, sl, q);
+        if (more) state_load1<TIn, DK, CT>(op, p, pn, tn, nn, h, sl, q);
         __syncthreads();
         // own rows: S <- Diag(gamma) S + K_end^T U
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            f32x4 acc = zero4();
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) acc = mm4(op.ke[rt][kb], *reinterpret_cast<const f32x4*>(sU + (kb * 64 + lane) * 4), acc);
-            S[rt] = op.gm[rt] * S[rt] + acc;
-        }
-        if (more) state_load2<DK>(op, pn, q);
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    acc = mm4(op.ke[rt][kb], *reinterpret_cast<const f32x4*>(sU + ((kb * CT + ct) * 64 + lane) * 4), acc);
+                S[ct][rt] = op.gm[rt] * S[ct][rt] + acc;
+            }
+        if (more) state_load2<DK, CT>(op, pn, q);
         sink ^= tch;
     }
     // keep the L2 touches alive: a store that no real input triggers
@@ -635,19 +654,19 @@ __global__ void __launch_bounds__(256) cb_state_kernel(Params p) {
 // (Gamma o Q)^T dO - W^T dU for own rows. Operands straight into registers,
 // each group reloaded for the previous chunk right after its last use, and
 // the lines of the chunk two steps back touched first.
-template <int DK>
+template <int DK, int CT>
 struct AdjOps {
     static constexpr int RT = DK / 64;
     f32x4 ke[4][RT];   // group 0: K_end[16t + i][own channels], A operand over own channels
     f32x4 pt[4];       // group 1: P^T[16q + i][16kb..] = P[16kb + ..][16q + i], A operand over tokens
-    f32x4 d[4];        // group 2: dO (K = tokens), B operand
+    f32x4 d[CT][4];    // group 2: dO (K = tokens) per column tile, B operand
     f32x4 qg[RT][4];   //          (Gamma o Q)^T[own rows][16kb..]
     f32x4 wt[RT][4];   //          W^T[own rows][16kb..]
     f32x4 gm[RT];
 };
 
-template <int DK>
-__device__ __forceinline__ void adj_load0(AdjOps<DK>& o, const float* pb, int q) {
+template <int DK, int CT>
+__device__ __forceinline__ void adj_load0(AdjOps<DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     const int i = lane_i(), g = lane_g();
@@ -658,8 +677,8 @@ __device__ __forceinline__ void adj_load0(AdjOps<DK>& o, const float* pb, int q)
             o.ke[t][rt] = *reinterpret_cast<const f32x4*>(pb + PL::KE + (size_t)(16 * t + i) * DK + q * RW + 16 * rt + 4 * g);
 }
 
-template <int DK>
-__device__ __forceinline__ void adj_load1(AdjOps<DK>& o, const float* pb, int q) {
+template <int DK, int CT>
+__device__ __forceinline__ void adj_load1(AdjOps<DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     const int i = lane_i(), g = lane_g();
 #pragma unroll
@@ -668,8 +687,8 @@ __device__ __forceinline__ void adj_load1(AdjOps<DK>& o, const float* pb, int q)
         for (int s = 0; s < 4; ++s) o.pt[kb][s] = kb >= q ? pb[PL::P + (size_t)(16 * kb + 4 * g + s) * C + 16 * q + i] : 0.f;
 }
 
-template <int DK>
-__device__ __forceinline__ void adj_load2(AdjOps<DK>& o, const Params& p, const float* pb, long t0, int n, int h,
+template <int DK, int CT>
+__device__ __forceinline__ void adj_load2(AdjOps<DK, CT>& o, const Params& p, const float* pb, long t0, int n, int h,
                                           int sl, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
@@ -679,8 +698,11 @@ __device__ __forceinline__ void adj_load2(AdjOps<DK>& o, const Params& p, const 
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int tok = 16 * kb + 4 * g + s;
-            const float dv = p.dO[((size_t)(t0 + min(tok, n - 1)) * H + h) * DV + 16 * sl + i];
-            o.d[kb][s] = tok < n ? dv : 0.f;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const float dv = p.dO[((size_t)(t0 + min(tok, n - 1)) * H + h) * DV + 16 * (CT * sl + ct) + i];
+                o.d[ct][kb][s] = tok < n ? dv : 0.f;
+            }
         }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -696,16 +718,15 @@ __device__ __forceinline__ void adj_load2(AdjOps<DK>& o, const Params& p, const 
     for (int rt = 0; rt < RT; ++rt) o.gm[rt] = *reinterpret_cast<const f32x4*>(pb + PL::GAM + q * RW + 16 * rt + 4 * g);
 }
 
-template <int DK>
-__global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
-    using SM = WalkSmem<DK>;
+template <int DK, int CT>
+__device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
+    using SM = WalkSmem<DK, CT>;
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
     float *sPart = sm + SM::PART, *sdU = sm + SM::UT;
 
-    const int H = p.H, DV = p.DV, NSL = DV / 16;
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int H = p.H, DV = p.DV, NSL = DV / (16 * CT);
     const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
     const int tid = threadIdx.x, q = tid / WAVE, lane = tid % WAVE;
     const int i = lane_i(), g = lane_g();
@@ -713,23 +734,26 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
     int cs, ce;
     seq_range(p.map, s, bos, eos, cs, ce);
     auto block = [&](int gi) { return p.prep + ((size_t)gi * H + h) * PL::FLOATS; };
+    auto col = [&](int ct) { return 16 * (CT * sl + ct) + i; };
 
-    f32x4 D[RT];
+    f32x4 D[CT][RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = q * RW + 16 * rt + 4 * g + e;
-            D[rt][e] = p.dST ? p.dST[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] : 0.f;
-        }
-    AdjOps<DK> op;
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = q * RW + 16 * rt + 4 * g + e;
+                D[ct][rt][e] = p.dST ? p.dST[((size_t)s * H + h) * DK * DV + (size_t)row * DV + col(ct)] : 0.f;
+            }
+    AdjOps<DK, CT> op;
     if (cs < ce) {
         long t0;
         int n;
         chunk_span(ce - 1, cs, bos, eos, t0, n);
-        adj_load0<DK>(op, block(ce - 1), q);
-        adj_load1<DK>(op, block(ce - 1), q);
-        adj_load2<DK>(op, p, block(ce - 1), t0, n, h, sl, q);
+        adj_load0<DK, CT>(op, block(ce - 1), q);
+        adj_load1<DK, CT>(op, block(ce - 1), q);
+        adj_load2<DK, CT>(op, p, block(ce - 1), t0, n, h, sl, q);
     }
     uint32_t sink = 0;
     for (int gi = ce - 1; gi >= cs; --gi) {
@@ -743,52 +767,75 @@ __global__ void __launch_bounds__(256) cb_adjoint_kernel(Params p) {
         chunk_span(more ? gi - 1 : gi, cs, bos, eos, tn, nn);
         float* ckD = p.ck + ((size_t)gi * H + h) * 2 * DK * DV + (size_t)DK * DV;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ckD[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * sl + i] = D[rt][e];
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = zero4();
+                for (int e = 0; e < 4; ++e) ckD[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + col(ct)] = D[ct][rt][e];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc = mm4(op.ke[t][rt], D[rt], acc);
-            *reinterpret_cast<f32x4*>(sPart + ((q * 4 + t) * 64 + lane) * 4) = acc;
-        }
-        if (more) adj_load0<DK>(op, pn, q);
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) acc = mm4(op.ke[t][rt], D[ct][rt], acc);
+                *reinterpret_cast<f32x4*>(sPart + (((q * 4 + t) * CT + ct) * 64 + lane) * 4) = acc;
+            }
+        if (more) adj_load0<DK, CT>(op, pn, q);
         __syncthreads();
-        {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                if (kb >= q) acc = mm4(op.pt[kb], op.d[kb], acc);
+                if (kb >= q) acc = mm4(op.pt[kb], op.d[ct][kb], acc);
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) acc += *reinterpret_cast<const f32x4*>(sPart + ((w2 * 4 + q) * 64 + lane) * 4);
-            *reinterpret_cast<f32x4*>(sdU + (q * 64 + lane) * 4) = acc;
+            for (int w2 = 0; w2 < 4; ++w2)
+                acc += *reinterpret_cast<const f32x4*>(sPart + (((w2 * 4 + q) * CT + ct) * 64 + lane) * 4);
+            *reinterpret_cast<f32x4*>(sdU + ((q * CT + ct) * 64 + lane) * 4) = acc;
         }
-        if (more) adj_load1<DK>(op, pn, q);
+        if (more) adj_load1<DK, CT>(op, pn, q);
         __syncthreads();
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            f32x4 a1 = zero4(), a2 = zero4();
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                a1 = mm4(op.qg[rt][kb], op.d[kb], a1);
-                a2 = mm4(op.wt[rt][kb], *reinterpret_cast<const f32x4*>(sdU + (kb * 64 + lane) * 4), a2);
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    a1 = mm4(op.qg[rt][kb], op.d[ct][kb], a1);
+                    a2 = mm4(op.wt[rt][kb], *reinterpret_cast<const f32x4*>(sdU + ((kb * CT + ct) * 64 + lane) * 4), a2);
+                }
+                D[ct][rt] = op.gm[rt] * D[ct][rt] + a1 - a2;
             }
-            D[rt] = op.gm[rt] * D[rt] + a1 - a2;
-        }
-        if (more) adj_load2<DK>(op, p, pn, tn, nn, h, sl, q);
+        if (more) adj_load2<DK, CT>(op, p, pn, tn, nn, h, sl, q);
         sink ^= tch;
     }
     if (sink == 0x9e3779b9u && p.H < 0) p.ck[0] = 0.f;
     if (p.gS0) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = q * RW + 16 * rt + 4 * g + e;
-                p.gS0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * sl + i] = D[rt][e];
-            }
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = q * RW + 16 * rt + 4 * g + e;
+                    p.gS0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + col(ct)] = D[ct][rt][e];
+                }
     }
+}
+
+// The two walks read only the prep's blocks, dO and dS_T, not each other's
+// results: one launch runs both, its first nstate workgroups walking the state
+// forward and the rest the adjoint backward. With slices of two column tiles
+// (dv >= 32) there are half as many walkers, one per CU for both walks
+// together; within each half the slices of one (sequence, head) stay on one
+// XCD.
+template <class TIn, int DK, int CT>
+__global__ void __launch_bounds__(256) cb_walk_kernel(Params p, int nstate) {
+    const int b = blockIdx.x;
+    if (b < nstate) state_walk<TIn, DK, CT>(p, xcd_remap(b, nstate));
+    else adjoint_walk<DK, CT>(p, xcd_remap(b - nstate, (int)gridDim.x - nstate));
 }
 
 // ================================================================ 4. state-side gradients
@@ -1491,7 +1538,7 @@ static hipError_t cb_allow_lds(K kern, size_t bytes) {
 template <class TIn, int DK, bool SG>
 static hipError_t launch_cbwd_t(const BwdArgs& a) {
     using namespace cb;
-    static_assert(PrepSmem<DK>::BYTES <= 160 * 1024 && WalkSmem<DK>::BYTES <= 160 * 1024 &&
+    static_assert(PrepSmem<DK>::BYTES <= 160 * 1024 && WalkSmem<DK, 2>::BYTES <= 160 * 1024 &&
                       GradSmem<DK>::BYTES <= 160 * 1024 && GateSmem<DK>::BYTES <= 160 * 1024,
                   "chunkwise backward LDS");
     const bool varlen = a.cu_seqlens != nullptr;
@@ -1513,20 +1560,27 @@ static hipError_t launch_cbwd_t(const BwdArgs& a) {
         if (e != hipSuccess) return e;
     }
     const unsigned items = (unsigned)(nch * a.H);
-    const unsigned walkers = (unsigned)((long)N * a.H * (a.dv / 16));
+    const int CTW = a.dv % 32 == 0 ? 2 : 1;   // column tiles per walker slice
+    const unsigned walkers = (unsigned)((long)N * a.H * (a.dv / (16 * CTW)));
     if (items > 0) {
         auto k1 = cb_prep_kernel<TIn, DK, SG>;
         if ((e = cb_allow_lds(k1, PrepSmem<DK>::BYTES)) != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(items), dim3(256), PrepSmem<DK>::BYTES, a.stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        auto k2 = cb_state_kernel<TIn, DK>;
-        if ((e = cb_allow_lds(k2, WalkSmem<DK>::BYTES)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k2, dim3(walkers), dim3(256), WalkSmem<DK>::BYTES, a.stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    auto k3 = cb_adjoint_kernel<DK>;
-    if ((e = cb_allow_lds(k3, WalkSmem<DK>::BYTES)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k3, dim3(walkers), dim3(256), WalkSmem<DK>::BYTES, a.stream, p);
+    // both walks in one launch (the state walk only when there are chunks;
+    // the adjoint half also writes dS0 = dS_T for empty sequences)
+    const int nstate = items > 0 ? (int)walkers : 0;
+    constexpr size_t WB1 = WalkSmem<DK, 1>::BYTES, WB2 = WalkSmem<DK, 2>::BYTES;
+    if (CTW == 2) {
+        auto k23 = cb_walk_kernel<TIn, DK, 2>;
+        if ((e = cb_allow_lds(k23, WB2)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k23, dim3((unsigned)nstate + walkers), dim3(256), WB2, a.stream, p, nstate);
+    } else {
+        auto k23 = cb_walk_kernel<TIn, DK, 1>;
+        if ((e = cb_allow_lds(k23, WB1)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k23, dim3((unsigned)nstate + walkers), dim3(256), WB1, a.stream, p, nstate);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (items > 0) {
         auto k4 = cb_grad_state_kernel<TIn, DK, SG>;
