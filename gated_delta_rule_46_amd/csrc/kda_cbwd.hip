@@ -47,14 +47,19 @@ constexpr int C = 64;          // chunk length
 constexpr int LC = C + 4;      // LDS row stride (floats) of C x C matrices
 constexpr int LS = 16 + 4;     // LDS row stride of 16-column slices
 
-// Workspace regions, per (chunk, head), in floats.
+// Workspace regions, per (chunk, head), in floats. XP holds two triangular
+// C x C matrices in one: X = (I + A)^{-1} below the diagonal (its diagonal is
+// 1 and not stored), P on and below it in transposed position, i.e.
+//   XP[r][c] = X[r][c] (r > c),  XP[r][r] = P[r][r],  XP[c][r] = P[r][c] (r > c);
+// the gradient pass then replaces it by dP and dA the same way (dP on and
+// below the diagonal, dA transposed above it). The chunk's state and adjoint
+// follow per (chunk, head) in a second region (2 dk dv floats).
 template <int DK>
 struct PrepLay {
-    static constexpr size_t X = 0, G = (size_t)C * C, P = 2 * (size_t)C * C, W = 3 * (size_t)C * C;
+    static constexpr size_t XP = 0, W = (size_t)C * C;
     static constexpr size_t KE = W + (size_t)C * DK, QG = KE + (size_t)C * DK, GAM = QG + (size_t)C * DK;
     static constexpr size_t FLOATS = (GAM + DK + 63) / 64 * 64;
 };
-constexpr size_t EXT_FLOATS = (size_t)C * C + 2 * C;   // dX, beta part
 
 // ---------------------------------------------------------------- 16x16x4 fp32 tiles
 // lane l = 16 g + i. Within a 16-deep K block, step s of lane group g takes K
@@ -139,7 +144,6 @@ struct Params {
     float *gq, *gk, *gv, *gg, *gb, *gS0;
     float* prep;   // PrepLay per (chunk, head)
     float* ck;     // S and dS' per (chunk, head): 2 * dk * dv floats
-    float* ext;    // EXT_FLOATS per (chunk, head)
     ChunkMap map;
     int H, DV;
 };
@@ -354,12 +358,7 @@ __global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
         stD(sP, LC, 16 * R, 16 * J, accP[u]);
     }
     __syncthreads();
-    for (int x = tid; x < C * C; x += 256) {
-        const int r = x / C, c = x % C;
-        out[PL::G + x] = sG[r * LC + c];
-        out[PL::P + x] = sP[r * LC + c];
-        sX[r * LC + c] = 0.f;
-    }
+    for (int x = tid; x < C * C; x += 256) sX[(x / C) * LC + x % C] = 0.f;
     __syncthreads();
     // ---- X = (I + A)^{-1}, A = Diag(beta) G: diagonal 16x16 blocks (wave b,
     // lanes 0..15 = columns) by forward substitution
@@ -392,7 +391,11 @@ __global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
         }
         __syncthreads();
     }
-    for (int x = tid; x < C * C; x += 256) out[PL::X + x] = sX[(x / C) * LC + x % C];
+    // X below the diagonal, P on and (transposed) above it
+    for (int x = tid; x < C * C; x += 256) {
+        const int r = x / C, c = x % C;
+        out[PL::XP + x] = r > c ? sX[r * LC + c] : sP[c * LC + r];
+    }
 
     // ---- pass 2: W = X (beta o Gamma o K), K_end, Gamma o Q, gamma
 #pragma unroll 1
@@ -500,9 +503,19 @@ __device__ __forceinline__ void state_load1(StateOps<DK, CT>& o, const Params& p
                                             int h, int sl, int q) {
     using PL = PrepLay<DK>;
     const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
+    // X row tile q from the packed XP: tiles left of the diagonal as stored;
+    // the diagonal tile with its unit diagonal restored and P's part above it
+    // cleared
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-        o.x[kb] = kb <= q ? *reinterpret_cast<const f32x4*>(pb + PL::X + (size_t)(16 * q + i) * C + 16 * kb + 4 * g) : zero4();
+    for (int kb = 0; kb < 4; ++kb) {
+        f32x4 xv = kb <= q ? *reinterpret_cast<const f32x4*>(pb + PL::XP + (size_t)(16 * q + i) * C + 16 * kb + 4 * g)
+                           : zero4();
+        if (kb == q) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xv[s] = 4 * g + s < i ? xv[s] : (4 * g + s == i ? 1.f : 0.f);
+        }
+        o.x[kb] = xv;
+    }
     // rows clamped to the chunk's last token, padding selected after the loads
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -588,9 +601,9 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
     }
     uint32_t sink = 0;
     for (int gi = cs; gi < ce; ++gi) {
-        // X, W and K_end of chunk gi + 2 (W and K_end are adjacent)
+        // XP, W and K_end of chunk gi + 2 (W and K_end are adjacent)
         const uint32_t tch =
-            gi + 2 < ce ? touch_lines(block(gi + 2), PL::X, (size_t)C * C, PL::W, 2 * (size_t)C * DK, sl, NSL, tid) : 0u;
+            gi + 2 < ce ? touch_lines(block(gi + 2), PL::XP, (size_t)C * C, PL::W, 2 * (size_t)C * DK, sl, NSL, tid) : 0u;
         const bool more = gi + 1 < ce;
         const float* pn = block(more ? gi + 1 : gi);
         long tn;
@@ -681,10 +694,19 @@ template <int DK, int CT>
 __device__ __forceinline__ void adj_load1(AdjOps<DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     const int i = lane_i(), g = lane_g();
+    // P^T[16q + i][16kb + 4g + s] = P[16kb + 4g + s][16q + i] sits in the
+    // packed XP at [16q + i][16kb + 4g + s] on and above the diagonal; below
+    // it (X's part) P is zero
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+        f32x4 pv = kb >= q ? *reinterpret_cast<const f32x4*>(pb + PL::XP + (size_t)(16 * q + i) * C + 16 * kb + 4 * g)
+                           : zero4();
+        if (kb == q) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) o.pt[kb][s] = kb >= q ? pb[PL::P + (size_t)(16 * kb + 4 * g + s) * C + 16 * q + i] : 0.f;
+            for (int s = 0; s < 4; ++s) pv[s] = 4 * g + s >= i ? pv[s] : 0.f;
+        }
+        o.pt[kb] = pv;
+    }
 }
 
 template <int DK, int CT>
@@ -757,9 +779,9 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
     }
     uint32_t sink = 0;
     for (int gi = ce - 1; gi >= cs; --gi) {
-        // P and W, K_end, Gamma o Q of chunk gi - 2 (the last three are adjacent)
+        // XP and W, K_end, Gamma o Q of chunk gi - 2 (the last three are adjacent)
         const uint32_t tch =
-            gi - 2 >= cs ? touch_lines(block(gi - 2), PL::P, (size_t)C * C, PL::W, 3 * (size_t)C * DK, sl, NSL, tid) : 0u;
+            gi - 2 >= cs ? touch_lines(block(gi - 2), PL::XP, (size_t)C * C, PL::W, 3 * (size_t)C * DK, sl, NSL, tid) : 0u;
         const bool more = gi - 1 >= cs;
         const float* pn = block(more ? gi - 1 : gi);
         long tn;
@@ -854,7 +876,7 @@ struct GradSmem {
     static constexpr size_t DU = U + (size_t)C * LS, BETA = DU + (size_t)C * LS, DG = BETA + C, DB = DG + DK;
     static constexpr size_t FLOATS = DB + 4 * C;
     static constexpr size_t BYTES = FLOATS * 4;
-    static_assert(BETA - S >= 512, "the gate part products fit the value-block buffers");
+    static_assert(BETA - S >= (size_t)C * LC, "dX (and before it the gate part products) fit the value-block buffers");
 };
 
 template <class TIn, int DK, bool SG>
@@ -878,14 +900,21 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     const int i = lane_i(), g = lane_g();
     const size_t base = (size_t)gidx * H + h;
     float* pb = p.prep + base * PL::FLOATS;
-    const float* ckS = p.ck + base * 2 * DK * DV;
+    float* ckS = p.ck + base * 2 * DK * DV;   // read by the value blocks; then the beta parts go here
     const float* ckD = ckS + (size_t)DK * DV;
-    float* ex = p.ext + base * EXT_FLOATS;
 
+    // X (unit diagonal) and P out of the packed XP: element [r][c] of XP is
+    // X[r][c] below the diagonal and P[c][r] on and above it
     for (int x = tid; x < C * C / 4; x += 512) {
         const int r = x / (C / 4), c = 4 * (x % (C / 4));
-        *reinterpret_cast<f32x4*>(sX + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::X + 4 * x);
-        *reinterpret_cast<f32x4*>(sP + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::P + 4 * x);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(pb + PL::XP + 4 * x);
+        f32x4 xv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xv[e] = c + e < r ? v[e] : (c + e == r ? 1.f : 0.f);
+            sP[(c + e) * LC + r] = c + e >= r ? v[e] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(sX + r * LC + c) = xv;
     }
     for (int x = tid; x < C * DK / 4; x += 512) {
         const int r = x / (DK / 4), c = 4 * (x % (DK / 4));
@@ -1019,10 +1048,14 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
                 for (int e = 0; e < 4; ++e) pb[PL::KE + (size_t)(16 * t + 4 * g + e) * DK + 16 * c + i] = acc[u][e];
             }
         } else if (idx < NT1 + 10) {
+            // dP on and below the diagonal of the packed slot (dA^T goes above)
             int R, J;
             lower_tile(idx - NT1, R, J);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pb[PL::P + (size_t)(16 * R + 4 * g + e) * C + 16 * J + i] = acc[u][e];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * g + e, c = 16 * J + i;
+                if (r >= c) pb[PL::XP + (size_t)r * C + c] = acc[u][e];
+            }
         }
     }
     {   // Gamma o K into sKE. Thread (c, part) holds the RPP consecutive rows
@@ -1056,7 +1089,10 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
         for (int j = 0; j < RPP; ++j) sKE[(part * RPP + j) * LK + c] = kr[j] * (pfx * lp[j]);
     }
     __syncthreads();
-    // ---- dX += dW (beta o Gamma o K)^T (tiles already owned), then dX out
+    // ---- dX += dW (beta o Gamma o K)^T (tiles already owned), into LDS (the
+    // value-block buffers are free now; T below goes where P was)
+    float* sDX = sm + SM::S;
+    float* sT = sP;
 #pragma unroll
     for (int u = 0; u < NPW; ++u) {
         const int idx = w + 8 * u;
@@ -1069,8 +1105,7 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
             const f32x4 bk = ldBT(sKE, LK, 16 * kb, 16 * J) * sBeta[16 * J + i];
             a = mm4(ldA(sW, LK, 16 * R, 16 * kb), bk, a);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ex[(size_t)(16 * R + 4 * g + e) * C + 16 * J + i] = a[e];
+        stD(sDX, LC, 16 * R, 16 * J, a);
     }
     // ---- Y = X^T dW: d(Gamma o K) = beta o Y; beta part rowsum(Gamma o K o Y).
     // Wave w: token tile t = w % 4, channel tiles half (w / 4); each half's
@@ -1094,46 +1129,73 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
         }
     }
     __syncthreads();
-    if (tid < C) ex[(size_t)C * C + tid] = sdb[tid] + sdb[C + tid] + sdb[2 * C + tid];
+    // ---- dA = -X^T dX X^T (strictly lower): T = dX X^T (tiles below and on
+    // the diagonal of dX are read), then dA = -X^T T, written transposed
+    // above the diagonal of the packed slot. The beta parts go to the chunk's
+    // state area, whose last reader was this workgroup's value-block loop.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tt = w + 8 * u, R = tt / 4, J = tt % 4;
+        f32x4 a = zero4();
+        for (int kb = 0; kb <= min(R, J); ++kb) a = mm4(ldA(sDX, LC, 16 * R, 16 * kb), ldBT(sX, LC, 16 * kb, 16 * J), a);
+        stD(sT, LC, 16 * R, 16 * J, a);
+    }
+    if (tid < C) ckS[tid] = sdb[tid] + sdb[C + tid] + sdb[2 * C + tid];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int idx = w + 8 * u;
+        if (idx >= 10) continue;
+        int R, J;
+        lower_tile(idx, R, J);
+        f32x4 a = zero4();
+        for (int kb = R; kb < 4; ++kb) a = mm4(ldAT(sX, LC, 16 * R, 16 * kb), ldB(sT, LC, 16 * kb, 16 * J), a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * R + 4 * g + e, c = 16 * J + i;
+            if (r > c) pb[PL::XP + (size_t)c * C + r] = -a[e];
+        }
+    }
 }
 
 // ================================================================ 5. gate-side gradients
-// One workgroup (4 waves) per (chunk, head). First dA = -X^T dX X^T (strictly
-// lower) and dG = Diag(beta) dA on MFMA; then, per block of 32 key channels,
+// One workgroup (4 waves) per (chunk, head): per block of 32 key channels,
 // dq, dk and the gate gradient from Gamma o Q, Gamma o K, K_end, gamma and,
-// level by level of the binary split, the gated Gram matrices.
+// level by level of the binary split, the gated Gram matrices G and P, whose
+// gradients are dG = Diag(beta) dA and dP (dA and dP come packed from the
+// state-side pass). The level products take dA itself: Y = dA_L XK on the
+// right rows (times beta there where dG is meant), Z = dA_L^T (beta o XK) +
+// dP_L^T XQ on the left rows (the right rows of XK staged times beta). The
+// same Y gives the last part of dbeta, rowsum(dA o G) = sum over levels and
+// channels of k o pre o Y.
 //
-// In the channel phase thread (c, part) owns channel c of the block and the
-// 8 rows 8 part .. 8 part + 7 of the chunk, in registers. Every gate scan
-// (prefix products, the reverse and forward affine scans of the adjoint) runs
-// as a local scan over those 8 rows plus a carry composed from the summaries
-// of the other row parts, exchanged through a small LDS table; only the
-// operands and results of the level products go through LDS. The C x C
-// buffers of the first phase are reused for the channel phase, which keeps
-// the workgroup under 80 KB of LDS (two per compute unit).
+// Thread (c, part) owns channel c of the block and the 8 rows 8 part ..
+// 8 part + 7 of the chunk, in registers. Every gate scan (prefix products,
+// the reverse and forward affine scans of the adjoint) runs as a local scan
+// over those 8 rows plus a carry composed from the summaries of the other row
+// parts, exchanged through a small LDS table; only the operands and results
+// of the level products go through LDS.
 template <int DK>
 struct GateSmem {
     static constexpr int CB = 32, LB = CB + 4, NP = 8;
-    // channel phase: carry tables [part][channel], the level operands XK, XQ
-    // and products YZ, YP, dP, dG -- everything a thread addresses per row
-    // sits below 64 KB, in reach of one base register
+    // carry tables [part][channel], the level operands XK, XQ and products
+    // YZ, YP, dP, dA -- everything a thread addresses per row sits below
+    // 64 KB, in reach of one base register
     static constexpr size_t CM = 0, CL = CM + NP * CB, CR = CL + NP * CB, CV = CR + NP * CB;
     static constexpr size_t XK = CV + NP * CB, XQ = XK + (size_t)C * LB, YZ = XQ + (size_t)C * LB;
-    static constexpr size_t YP = YZ + (size_t)C * LB, DP = YP + (size_t)C * LB, DG = DP + (size_t)C * LC;
-    // phase 1: X, G and T = dX X^T below dG (dX is held in the dG buffer)
-    static constexpr size_t X = 0, G = X + (size_t)C * LC, T = G + (size_t)C * LC;
-    static_assert(T + (size_t)C * LC <= DG, "phase-1 buffers overlap dG");
-    static constexpr size_t BETA = DG + (size_t)C * LC, DB = BETA + C, DAT = DB + 2 * C;
+    static constexpr size_t YP = YZ + (size_t)C * LB, DP = YP + (size_t)C * LB, DA = DP + (size_t)C * LC;
+    static constexpr size_t BETA = DA + (size_t)C * LC, DB = BETA + C, RP = DB + C, DAT = RP + C;
     static constexpr size_t FLOATS = DAT + C;
     static constexpr size_t BYTES = FLOATS * 4;
-    static_assert(DG * 4 <= 65536, "per-row arrays beyond the ds offset range");
+    static_assert(DA * 4 <= 65536, "per-row arrays beyond the ds offset range");
 };
 
 // Products of level L (half width 32 >> L) for the two 16-channel column
-// tiles of the block: Y_G = dG_L XK and Y_P = dP_L XK on right row tiles,
-// Z = dG_L^T XK + dP_L^T XQ on left row tiles (Y_G + Z share YZ).
+// tiles of the block: Y = dA_L XK and Y_P = dP_L XK on right row tiles,
+// Z = dA_L^T XK + dP_L^T XQ on left row tiles (Y and Z share YZ; XK's right
+// rows carry beta, so Z is the dG term).
 template <int L, int LB>
-__device__ __forceinline__ void gate_products(int w, const float* sdG, const float* sdP, const float* sXK,
+__device__ __forceinline__ void gate_products(int w, const float* sdA, const float* sdP, const float* sXK,
                                              const float* sXQ, float* sYZ, float* sYP) {
     constexpr int HW = 32 >> L;
     const int i = lane_i(), g = lane_g();
@@ -1144,7 +1206,7 @@ __device__ __forceinline__ void gate_products(int w, const float* sdG, const flo
             const int o = job / 2, ct = job % 2, kind = o % 3, which = o / 3;   // kind 0: Y_G, 1: Y_P, 2: Z
             if (kind < 2) {
                 const int R = L == 0 ? 2 + which : 1 + 2 * which;
-                const float* M = kind == 0 ? sdG : sdP;
+                const float* M = kind == 0 ? sdA : sdP;
                 f32x4 a = zero4();
                 for (int J = 0; J < R; ++J) {
                     if (!tile_at_level(R, J, L)) continue;
@@ -1156,7 +1218,7 @@ __device__ __forceinline__ void gate_products(int w, const float* sdG, const flo
                 f32x4 a = zero4();
                 for (int R = J + 1; R < 4; ++R) {
                     if (!tile_at_level(R, J, L)) continue;
-                    a = mm4(ldAT(sdG, LC, 16 * J, 16 * R), ldB(sXK, LB, 16 * R, 16 * ct), a);
+                    a = mm4(ldAT(sdA, LC, 16 * J, 16 * R), ldB(sXK, LB, 16 * R, 16 * ct), a);
                     a = mm4(ldAT(sdP, LC, 16 * J, 16 * R), ldB(sXQ, LB, 16 * R, 16 * ct), a);
                 }
                 stD(sYZ, LB, 16 * J, 16 * ct, a);
@@ -1165,8 +1227,8 @@ __device__ __forceinline__ void gate_products(int w, const float* sdG, const flo
     } else {
         // in-tile level: wave w owns diagonal tile w
         const int b = w;
-        f32x4 ag = ldA(sdG, LC, 16 * b, 16 * b), ap = ldA(sdP, LC, 16 * b, 16 * b);
-        f32x4 bgT = ldAT(sdG, LC, 16 * b, 16 * b), bpT = ldAT(sdP, LC, 16 * b, 16 * b);
+        f32x4 ag = ldA(sdA, LC, 16 * b, 16 * b), ap = ldA(sdP, LC, 16 * b, 16 * b);
+        f32x4 bgT = ldAT(sdA, LC, 16 * b, 16 * b), bpT = ldAT(sdP, LC, 16 * b, 16 * b);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const bool ky = sep_in(i, 4 * g + s, HW);   // A(i, k) = dG[r = i][j = k]
@@ -1188,10 +1250,11 @@ __device__ __forceinline__ void gate_products(int w, const float* sdG, const flo
     }
 }
 
-// Registers of thread (c, part) in the channel phase: gates a, keys k and
-// queries q of its 8 rows and the gradients accumulated for them.
+// Registers of thread (c, part) in the channel phase: gates a, keys k,
+// queries q and beta of its 8 rows, the gradients accumulated for them, and
+// the block's share of rowsum(dA o G) per row.
 struct GateRegs {
-    float a[8], k[8], q[8], dq[8], dk[8], da[8];
+    float a[8], k[8], q[8], b[8], dq[8], dk[8], da[8], rp[8];
 };
 
 // One level of the binary split, half width HW = 32 >> L. Right rows of a
@@ -1202,11 +1265,12 @@ struct GateRegs {
 // half also cross row parts and take a carry through the CV table.
 template <int L, int LB, int CB>
 __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, float* sXK, float* sXQ, float* sYZ,
-                                          float* sYP, float* sCV, const float* sCM, const float* sdG,
+                                          float* sYP, float* sCV, const float* sCM, const float* sdA,
                                           const float* sdP) {
     constexpr int HW = 32 >> L;
     const int r0 = 8 * part;
     float ps[8];
+    bool right[8];
     float lp[8], ml[8];
     local_products(x.a, lp, ml);
     bool rt = false;    // HW >= 8: this part lies in a right half
@@ -1221,7 +1285,10 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
         for (int qq = hlo; qq < part; ++qq) sp *= sCM[qq * CB + c];
         for (int qq = part + 1; qq < hhi; ++qq) ss *= sCM[qq * CB + c];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ps[j] = rt ? sp * lp[j] : ml[j] * ss;
+        for (int j = 0; j < 8; ++j) {
+            ps[j] = rt ? sp * lp[j] : ml[j] * ss;
+            right[j] = rt;
+        }
     } else {
 #pragma unroll
         for (int s0 = 0; s0 < 8; s0 += 2 * HW) {
@@ -1230,22 +1297,25 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
             for (int u = 0; u < HW; ++u) {
                 f *= x.a[s0 + HW + u];
                 ps[s0 + HW + u] = f;
+                right[s0 + HW + u] = true;
             }
             f = 1.f;
 #pragma unroll
             for (int u = 0; u < HW; ++u) {
                 ps[s0 + HW - 1 - u] = f;
+                right[s0 + HW - 1 - u] = false;
                 f *= x.a[s0 + HW - 1 - u];
             }
         }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        sXK[(r0 + j) * LB + c] = x.k[j] * ps[j];
+        const float kw = x.k[j] * ps[j];
+        sXK[(r0 + j) * LB + c] = right[j] ? x.b[j] * kw : kw;
         sXQ[(r0 + j) * LB + c] = x.q[j] * ps[j];
     }
     __syncthreads();
-    gate_products<L, LB>(w, sdG, sdP, sXK, sXQ, sYZ, sYP);
+    gate_products<L, LB>(w, sdA, sdP, sXK, sXQ, sYZ, sYP);
     __syncthreads();
     float yz[8], yp[8];
 #pragma unroll
@@ -1260,9 +1330,11 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
         if (rt) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                x.dk[j] += ps[j] * yz[j];
+                const float yg = x.b[j] * yz[j];   // the dG term of the row
+                x.rp[j] += x.k[j] * ps[j] * yz[j];
+                x.dk[j] += ps[j] * yg;
                 x.dq[j] += ps[j] * yp[j];
-                loc[j] = x.k[j] * yz[j] + x.q[j] * yp[j];   // dpre
+                loc[j] = x.k[j] * yg + x.q[j] * yp[j];   // dpre
             }
 #pragma unroll
             for (int j = 6; j >= 0; --j) loc[j] += x.a[j + 1] * loc[j + 1];
@@ -1301,9 +1373,11 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
 #pragma unroll
             for (int u = HW - 1; u >= 0; --u) {
                 const int j = s0 + HW + u;
-                x.dk[j] += ps[j] * yz[j];
+                const float yg = x.b[j] * yz[j];
+                x.rp[j] += x.k[j] * ps[j] * yz[j];
+                x.dk[j] += ps[j] * yg;
                 x.dq[j] += ps[j] * yp[j];
-                const float dpre = x.k[j] * yz[j] + x.q[j] * yp[j];
+                const float dpre = x.k[j] * yg + x.q[j] * yp[j];
                 R = u < HW - 1 ? dpre + x.a[j + 1] * R : dpre;
                 x.da[j] += (u > 0 ? ps[j - 1] : 1.f) * R;
             }
@@ -1326,83 +1400,43 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
     constexpr int CB = SM::CB, LB = SM::LB, NP = SM::NP;
     static_assert(CB * NP == 256 && NP * 8 == C && DK % CB == 0, "gate-side thread layout");
     extern __shared__ __align__(16) float sm[];
-    float *sdG = sm + SM::DG, *sX = sm + SM::X, *sG = sm + SM::G, *sT = sm + SM::T, *sdP = sm + SM::DP;
+    float *sdA = sm + SM::DA, *sdP = sm + SM::DP;
     float *sXK = sm + SM::XK, *sXQ = sm + SM::XQ, *sYZ = sm + SM::YZ, *sYP = sm + SM::YP;
     float *sCM = sm + SM::CM, *sCL = sm + SM::CL, *sCR = sm + SM::CR, *sCV = sm + SM::CV;
-    float *sBeta = sm + SM::BETA, *sdb = sm + SM::DB, *sdat = sm + SM::DAT;
+    float *sBeta = sm + SM::BETA, *sdb = sm + SM::DB, *sRP = sm + SM::RP, *sdat = sm + SM::DAT;
 
-    const int H = p.H;
+    const int H = p.H, DV = p.DV;
     const int item = blockIdx.x;
     const int h = item % H, gidx = launch_chunk(p.map, item / H);
     long t0;
     int n;
     if (!resolve_chunk(p.map, gidx, C, t0, n)) return;
-    const int tid = threadIdx.x, w = tid / WAVE;
-    const int i = lane_i(), g = lane_g();
+    const int tid = threadIdx.x;
     const size_t base = (size_t)gidx * H + h;
     const float* pb = p.prep + base * PL::FLOATS;
-    const float* ex = p.ext + base * EXT_FLOATS;
+    const float* ckS = p.ck + base * 2 * DK * DV;   // beta parts from the state-side pass
 
-    // dX into the dG buffer (replaced by dG below), X, G
+    // dP (on and below the diagonal of the packed slot) and dA (transposed
+    // above it)
     for (int x = tid; x < C * C / 4; x += 256) {
         const int r = x / (C / 4), c = 4 * (x % (C / 4));
-        const bool low = (r / 16) >= (c / 16);
-        *reinterpret_cast<f32x4*>(sX + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::X + 4 * x);
-        *reinterpret_cast<f32x4*>(sG + r * LC + c) = *reinterpret_cast<const f32x4*>(pb + PL::G + 4 * x);
-        *reinterpret_cast<f32x4*>(sdG + r * LC + c) = low ? *reinterpret_cast<const f32x4*>(ex + 4 * x) : zero4();
+        const f32x4 v = *reinterpret_cast<const f32x4*>(pb + PL::XP + 4 * x);
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pv[e] = c + e <= r ? v[e] : 0.f;
+            sdA[(c + e) * LC + r] = c + e > r ? v[e] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(sdP + r * LC + c) = pv;
     }
     if (tid < C) {
         sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
-        sdb[tid] = ex[(size_t)C * C + tid];
-    }
-    __syncthreads();
-    // ---- T = dX X^T (full tiles)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int tt = w + 4 * u, R = tt / 4, J = tt % 4;
-        f32x4 a = zero4();
-        for (int kb = 0; kb <= min(R, J); ++kb) a = mm4(ldA(sdG, LC, 16 * R, 16 * kb), ldBT(sX, LC, 16 * kb, 16 * J), a);
-        stD(sT, LC, 16 * R, 16 * J, a);
-    }
-    __syncthreads();
-    // ---- dA = -X^T T (strictly lower), dG = Diag(beta) dA; wave R owns row
-    // tile R (every J <= R), so the beta part of each row is one sum
-    {
-        const int R = w;
-        float rowpart[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int J = 0; J <= R; ++J) {
-            f32x4 a = zero4();
-            for (int kb = R; kb < 4; ++kb) a = mm4(ldAT(sX, LC, 16 * R, 16 * kb), ldB(sT, LC, 16 * kb, 16 * J), a);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * R + 4 * g + e, c = 16 * J + i;
-                const float da = r > c ? -a[e] : 0.f;
-                rowpart[e] += da * sG[r * LC + c];
-                a[e] = sBeta[r] * da;
-            }
-            stD(sdG, LC, 16 * R, 16 * J, a);
-        }
-        for (int J = R + 1; J < 4; ++J) stD(sdG, LC, 16 * R, 16 * J, zero4());
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float rs = rowpart[e];
-            rs += __shfl_xor(rs, 1, 16);
-            rs += __shfl_xor(rs, 2, 16);
-            rs += __shfl_xor(rs, 4, 16);
-            rs += __shfl_xor(rs, 8, 16);
-            if (i == 0) sdb[C + 16 * R + 4 * g + e] = rs;
-        }
-    }
-    __syncthreads();   // X, G and T are dead from here on
-    for (int x = tid; x < C * C / 4; x += 256) {
-        const int r = x / (C / 4), c = 4 * (x % (C / 4));
-        const bool low = (r / 16) >= (c / 16);
-        *reinterpret_cast<f32x4*>(sdP + r * LC + c) =
-            low ? *reinterpret_cast<const f32x4*>(pb + PL::P + 4 * x) : zero4();
+        sdb[tid] = ckS[tid];
     }
 
     // ---- per block of 32 key channels. Addresses: a uniform base at the
     // chunk's first row plus a 32-bit offset per thread and row.
+    const int w = tid / WAVE;
     const size_t rowbase = (size_t)t0 * H + h;
     const TIn* gk = (const TIn*)p.k + rowbase * DK;
     const TIn* gq = (const TIn*)p.q + rowbase * DK;
@@ -1431,6 +1465,7 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
             dqg[j] = r < n ? v0 : 0.f;
             dgk[j] = r < n ? v1 : 0.f;
             dke[j] = r < n ? v2 : 0.f;
+            x.rp[j] = 0.f;
         }
         // local products, and the local forward scan of drel_end = dK_end o k
         float lp[8], ml[8];
@@ -1444,6 +1479,8 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
         sCM[part * CB + c] = lp[7];
         sCL[part * CB + c] = Lend;
         __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x.b[j] = sBeta[r0 + j];
         float pfx = 1.f, sfx = 1.f, Lin = 0.f;
         for (int qq = 0; qq < part; ++qq) {
             const float m = sCM[qq * CB + c];
@@ -1479,12 +1516,12 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x.da[j] += (j > 0 ? gm[j - 1] : pfx) * (Rl[j] + ml[j] * Cin);
 
-        gate_level<0, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
-        gate_level<1, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
-        gate_level<2, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
-        gate_level<3, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
-        gate_level<4, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
-        gate_level<5, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdG, sdP);
+        gate_level<0, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
+        gate_level<1, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
+        gate_level<2, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
+        gate_level<3, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
+        gate_level<4, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
+        gate_level<5, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = r0 + j;
@@ -1495,24 +1532,27 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
                 if (!SG) oa[o] = x.da[j];
             }
         }
-        if (SG) {
-            // scalar gate: the gate gradient of a row is the sum over its
-            // channels -- over the 32 lanes of the row part, then the blocks
+        // per-row sums over the 32 channels of the row part (lanes 0-31 or
+        // 32-63 of the wave), then over the blocks: rowsum(dA o G) and, for a
+        // scalar gate, its gradient
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v = x.da[j];
-                v += __shfl_xor(v, 1, 32);
-                v += __shfl_xor(v, 2, 32);
-                v += __shfl_xor(v, 4, 32);
-                v += __shfl_xor(v, 8, 32);
-                v += __shfl_xor(v, 16, 32);
-                if (c == 0) sdat[r0 + j] = (cb == 0 ? 0.f : sdat[r0 + j]) + v;
+        for (int j = 0; j < 8; ++j) {
+            float v = x.rp[j];
+            float d = SG ? x.da[j] : 0.f;
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) {
+                v += __shfl_xor(v, o, 32);
+                if (SG) d += __shfl_xor(d, o, 32);
+            }
+            if (c == 0) {
+                sRP[r0 + j] = (cb == 0 ? 0.f : sRP[r0 + j]) + v;
+                if (SG) sdat[r0 + j] = (cb == 0 ? 0.f : sdat[r0 + j]) + d;
             }
         }
     }
-    if (SG) __syncthreads();
+    __syncthreads();
     if (tid < n) {
-        p.gb[(size_t)(t0 + tid) * H + h] = sdb[tid] + sdb[C + tid];
+        p.gb[(size_t)(t0 + tid) * H + h] = sdb[tid] + sRP[tid];
         if (SG) oa[(unsigned)tid * H] = sdat[tid];
     }
 }
@@ -1525,7 +1565,7 @@ size_t cbwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, in
     const long nch = chunk_count_bound(B, T, cb::C, varlen, N);
     const size_t ib = varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0;
     const size_t prep = (dk == 64 ? cb::PrepLay<64>::FLOATS : cb::PrepLay<128>::FLOATS);
-    const size_t per = prep + 2 * (size_t)dk * dv + cb::EXT_FLOATS;
+    const size_t per = prep + 2 * (size_t)dk * dv;
     return ib + (size_t)nch * H * per * 4;
 }
 
@@ -1551,9 +1591,8 @@ static hipError_t launch_cbwd_t(const BwdArgs& a) {
     ChunkMap map{a.cu_seqlens, varlen ? cstart : nullptr, a.T, N, NC, 0, NC};
     float* prep = (float*)(ws + ib);
     float* ck = prep + (size_t)nch * a.H * PrepLay<DK>::FLOATS;
-    float* ext = ck + (size_t)nch * a.H * 2 * DK * a.dv;
     Params p{a.q, a.k, a.v, a.gate, a.beta, a.S0, a.dO, a.dST, a.g_q, a.g_k, a.g_v, a.g_gate, a.g_beta, a.g_S0,
-             prep, ck, ext, map, a.H, a.dv};
+             prep, ck, map, a.H, a.dv};
     hipError_t e;
     if (varlen) {
         e = launch_chunk_index(a.cu_seqlens, cstart, N, C, a.stream);
