@@ -434,8 +434,8 @@ def main(argv=None) -> int:
             "calls": args.bwd_steps,
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": traffic_bwd,
-                         "kernel": "kda_chunk_bwd_cw: cb_prep, cb_state, cb_adjoint, cb_grad_state, cb_grad_gate "
-                                   "(fp32 MFMA, one stream)",
+                         "kernel": "kda_chunk_bwd_cw: cb_prep, cb_walk (state and adjoint walks), cb_grad_state, "
+                                   "cb_grad_gate (fp32 MFMA, one stream)",
                          "flops_per_launch": bflops, "hbm_bytes_algorithmic": bbytes,
                          "hbm_frac_algorithmic": round(gbs_b / HBM_PEAK_GBS, 4)},
             "workspace_bytes": wsb_b,

@@ -44,8 +44,8 @@ GROUPS = {
                             "gated_delta_rule_46_amd/csrc/kda_chunkmap.h"]},
     "decode": {"match": ("decode_step_kernel",), "per": "step",
                "sources": ["gated_delta_rule_46_amd/csrc/kda_decode.hip", "gated_delta_rule_46_amd/csrc/kda_common.h"]},
-    "backward": {"match": ("cb_prep_kernel", "cb_state_kernel", "cb_adjoint_kernel", "cb_grad_state_kernel",
-                           "cb_grad_gate_kernel"), "per": "call",
+    "backward": {"match": ("cb_prep_kernel", "cb_walk_kernel", "cb_grad_state_kernel", "cb_grad_gate_kernel",
+                           "chunk_index_kernel"), "per": "call",
                  "sources": ["gated_delta_rule_46_amd/csrc/kda_cbwd.hip", "gated_delta_rule_46_amd/csrc/kda_common.h",
                              "gated_delta_rule_46_amd/csrc/kda_chunkmap.h"]},
     "backward_token": {"match": ("chunk_bwd_kernel", "chunk_bwd_reduce_kernel"), "per": "call",
