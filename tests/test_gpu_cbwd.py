@@ -138,3 +138,54 @@ def test_cbwd_full_size_gdn_varlen(kda):
     print("  worst pair", {n: "%.2e" % e for n, e in worst.items()}, flush=True)
     for n in NAMES:
         assert errs[n] <= 1e-3 and worst[n] <= 1e-3, (n, errs, worst)
+
+
+def test_cbwd_graph_replay_matches_eager(kda):
+    """The chunkwise backward with a caller-supplied workspace and output dict
+    enqueues kernels only, so a caller can capture it in a graph: packed
+    sequences (the chunk-index kernel runs inside the graph), three replays,
+    each on new inputs and a new split of the same total length copied into
+    the captured buffers, with eager calls in between, each equal bit for bit
+    to an eager call on the same inputs."""
+    H, dk, dv = 2, 128, 64
+    splits = ([37, 0, 150, 64], [64, 64, 1, 122], [0, 200, 50, 1], [100, 51, 99, 1])
+
+    def make(seed, lengths):
+        w = inputs.make_forward("graph_bwd", B=1, H=H, T=0, dk=dk, dv=dv, dtype=torch.bfloat16, gate="ckda",
+                                lengths=lengths, s0_std=0.3, seed=seed)
+        dO, dST = inputs.cotangents(w, seed=seed)
+        return [t.cuda() for t in (w.q, w.k, w.v, w.gate, w.beta, dO, w.S0, dST, w.cu_seqlens)]
+
+    static = make(40, splits[0])
+    T, N = static[0].shape[1], static[8].numel() - 1
+    ws = torch.empty(kda.bwd_cw_workspace_bytes(1, H, T, dk, dv, N, True), device="cuda", dtype=torch.uint8)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    g = {"dq": torch.empty((1, T, H, dk), **f32), "dk": torch.empty((1, T, H, dk), **f32),
+         "dv": torch.empty((1, T, H, dv), **f32), "dgate": torch.empty((1, T, H, dk), **f32),
+         "dbeta": torch.empty((1, T, H), **f32), "dS0": torch.empty((N, H, dk, dv), **f32)}
+
+    def step():
+        q, k, v, gt, b, dO, s0, dst, cu = static
+        kda.chunk_bwd(q, k, v, gt, b, dO, S0=s0, dS_T=dst, cu_seqlens=cu, workspace=ws, out=g, chunked=True)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        print("replay", rep, "lengths", splits[rep + 1], flush=True)
+        new = make(41 + rep, splits[rep + 1])
+        for dst, src in zip(static, new):
+            dst.copy_(src)
+        q, k, v, gt, b, dO, s0, dst, cu = new
+        e = kda.chunk_bwd(q, k, v, gt, b, dO, S0=s0, dS_T=dst, cu_seqlens=cu, chunked=True)   # eager
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in NAMES:
+            assert torch.equal(g[n], e[n]), (rep, n)
