@@ -154,6 +154,10 @@ __device__ __forceinline__ float gate_at(const Params& p, size_t row, int DK, in
     return sg ? ld_in(g + row) : ld_in(g + row * DK + c);
 }
 
+// An input element already loaded (bf16 bits or fp32) as fp32.
+__device__ __forceinline__ float cvt_in(uint16_t b) { return bf16_bits_to_f32(b); }
+__device__ __forceinline__ float cvt_in(float v) { return v; }
+
 // Inclusive prefix (lp) and exclusive suffix (ml) products of a thread's 8 gates.
 __device__ __forceinline__ void local_products(const float* a, float* lp, float* ml) {
     float f = 1.f;
@@ -879,14 +883,38 @@ struct GradSmem {
     static_assert(BETA - S >= (size_t)C * LC, "dX (and before it the gate part products) fit the value-block buffers");
 };
 
+// Operands of the value-loop tile in slot idx (slots 0 .. 12 dk/16 - 1: three
+// kinds of dk/16 x 4 tiles, d(Gamma o Q), dU S^T, dK_end; then ten lower
+// tiles of dP and ten of dX), as float offsets into the workgroup's LDS of
+// the first A row and the first B^T row (both read with the same lane
+// offset); jb is the first beta row of a dX tile (B = (beta o V)^T), else -1.
+template <int DK>
+__device__ __forceinline__ void tile_operands(int idx, int& oa, int& ob, int& jb) {
+    using SM = GradSmem<DK>;
+    constexpr int NCT = DK / 16, NT1 = 12 * NCT;
+    jb = -1;
+    if (idx < NT1) {
+        const int kind = idx / (4 * NCT), rem = idx % (4 * NCT), t = rem / NCT, c = rem % NCT;
+        oa = (int)(kind == 0 ? SM::DO : kind == 1 ? SM::DU : SM::U) + 16 * t * LS;
+        ob = (int)(kind == 2 ? SM::D : SM::S) + 16 * c * LS;
+    } else {
+        const bool dx = idx >= NT1 + 10;
+        int R, J;
+        lower_tile(dx ? idx - NT1 - 10 : idx - NT1, R, J);
+        oa = (int)(dx ? SM::DU : SM::DO) + 16 * R * LS;
+        ob = (int)(dx ? SM::V : SM::U) + 16 * J * LS;
+        if (dx) jb = 16 * J;
+    }
+}
+
 template <class TIn, int DK, bool SG>
 __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     using SM = GradSmem<DK>;
     using PL = PrepLay<DK>;
     constexpr int LK = SM::LK, NCT = DK / 16;
-    constexpr int NT1 = 12 * NCT, NTILE = NT1 + 20, NPW = (NTILE + 7) / 8;
+    constexpr int NT1 = 12 * NCT, NTILE = NT1 + 20, NPW = (NTILE + 7) / 8, UX = (NT1 + 10) / 8;
     extern __shared__ __align__(16) float sm[];
-    float *sX = sm + SM::X, *sP = sm + SM::P, *sW = sm + SM::W, *sKE = sm + SM::KE, *sS = sm + SM::S, *sD = sm + SM::D;
+    float *sX = sm + SM::X, *sPT = sm + SM::P, *sW = sm + SM::W, *sKE = sm + SM::KE, *sS = sm + SM::S, *sD = sm + SM::D;
     float *sdO = sm + SM::DO, *sV = sm + SM::V, *sU = sm + SM::U, *sdU = sm + SM::DU, *sBeta = sm + SM::BETA;
     float *sdg = sm + SM::DG, *sdb = sm + SM::DB;   // sdb: [4][C] beta parts (fixed-order sums)
 
@@ -896,45 +924,37 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     long t0;
     int n;
     if (!resolve_chunk(p.map, gidx, C, t0, n)) return;
-    const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / WAVE), lane = tid % WAVE;
     const int i = lane_i(), g = lane_g();
     const size_t base = (size_t)gidx * H + h;
     float* pb = p.prep + base * PL::FLOATS;
     float* ckS = p.ck + base * 2 * DK * DV;   // read by the value blocks; then the beta parts go here
     const float* ckD = ckS + (size_t)DK * DV;
 
-    // X (unit diagonal) and P out of the packed XP: element [r][c] of XP is
-    // X[r][c] below the diagonal and P[c][r] on and above it
-    for (int x = tid; x < C * C / 4; x += 512) {
-        const int r = x / (C / 4), c = 4 * (x % (C / 4));
-        const f32x4 v = *reinterpret_cast<const f32x4*>(pb + PL::XP + 4 * x);
-        f32x4 xv;
+    // Every load of the prologue (the packed XP, W, K_end, beta and the first
+    // value block) is issued before the first LDS store, so their latencies
+    // overlap.
+    constexpr int NXP = C * C / 4 / 512, NWK = C * DK / 4 / 512;
+    static_assert(NXP * 512 * 4 == C * C && NWK * 512 * 4 == C * DK, "prologue tiling");
+    f32x4 lxp[NXP], lw[NWK], lke[NWK];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            xv[e] = c + e < r ? v[e] : (c + e == r ? 1.f : 0.f);
-            sP[(c + e) * LC + r] = c + e >= r ? v[e] : 0.f;
-        }
-        *reinterpret_cast<f32x4*>(sX + r * LC + c) = xv;
-    }
-    for (int x = tid; x < C * DK / 4; x += 512) {
-        const int r = x / (DK / 4), c = 4 * (x % (DK / 4));
-        *reinterpret_cast<f32x4*>(sW + r * LK + c) = *reinterpret_cast<const f32x4*>(pb + PL::W + 4 * x);
-        *reinterpret_cast<f32x4*>(sKE + r * LK + c) = *reinterpret_cast<const f32x4*>(pb + PL::KE + 4 * x);
-    }
-    if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
-    if (tid < DK) sdg[tid] = 0.f;
-    if (tid < 4 * C) sdb[tid] = 0.f;
-
-    f32x4 acc[NPW];
+    for (int j = 0; j < NXP; ++j) lxp[j] = *reinterpret_cast<const f32x4*>(pb + PL::XP + 4 * (tid + 512 * j));
 #pragma unroll
-    for (int u = 0; u < NPW; ++u) acc[u] = zero4();
+    for (int j = 0; j < NWK; ++j) {
+        lw[j] = *reinterpret_cast<const f32x4*>(pb + PL::W + 4 * (tid + 512 * j));
+        lke[j] = *reinterpret_cast<const f32x4*>(pb + PL::KE + 4 * (tid + 512 * j));
+    }
+    const TIn lbeta = ((const TIn*)p.beta)[(size_t)(t0 + min(tid % C, n - 1)) * H + h];
 
     // The value-column block b + 1 (S, dS', dO, V) is fetched into registers
-    // while block b computes, and written to LDS at the start of its turn.
+    // while block b computes and written to LDS at the start of its turn.
+    // Rows past the chunk end read row n - 1 and are zeroed only when staged,
+    // so that nothing waits for these loads before then.
     static_assert(DK * 4 <= 512 && C * 16 == 2 * 512, "value-block staging");
     const int sr = tid / 4, sc = 4 * (tid % 4);
     f32x4 nS = zero4(), nD = zero4();
-    float nO[2], nV[2];
+    float nO[2];
+    TIn nV[2];
     auto fetch_block = [&](int b) {
         if (tid < DK * 4) {
             nS = *reinterpret_cast<const f32x4*>(ckS + (size_t)sr * DV + 16 * b + sc);
@@ -944,12 +964,40 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
         for (int u = 0; u < 2; ++u) {
             const int x = tid + 512 * u, r = x / 16, c = x % 16;
             const size_t row = (size_t)(t0 + min(r, n - 1)) * H + h;
-            const float ov = p.dO[row * DV + 16 * b + c], vv = ld_in((const TIn*)p.v + row * DV + 16 * b + c);
-            nO[u] = r < n ? ov : 0.f;
-            nV[u] = r < n ? vv : 0.f;
+            nO[u] = p.dO[row * DV + 16 * b + c];
+            nV[u] = ((const TIn*)p.v)[row * DV + 16 * b + c];
         }
     };
     fetch_block(0);
+
+    // X (unit diagonal, zero above) and P^T (zero below the diagonal) out of
+    // the packed XP: element [r][c] of XP is X[r][c] below the diagonal and
+    // P[c][r] = P^T[r][c] on and above it
+#pragma unroll
+    for (int j = 0; j < NXP; ++j) {
+        const int x = tid + 512 * j, r = x / (C / 4), c = 4 * (x % (C / 4));
+        f32x4 xv, pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xv[e] = c + e < r ? lxp[j][e] : (c + e == r ? 1.f : 0.f);
+            pv[e] = c + e >= r ? lxp[j][e] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(sX + r * LC + c) = xv;
+        *reinterpret_cast<f32x4*>(sPT + r * LC + c) = pv;
+    }
+#pragma unroll
+    for (int j = 0; j < NWK; ++j) {
+        const int x = tid + 512 * j, r = x / (DK / 4), c = 4 * (x % (DK / 4));
+        *reinterpret_cast<f32x4*>(sW + r * LK + c) = lw[j];
+        *reinterpret_cast<f32x4*>(sKE + r * LK + c) = lke[j];
+    }
+    if (tid < C) sBeta[tid] = tid < n ? cvt_in(lbeta) : 0.f;
+    if (tid < DK) sdg[tid] = 0.f;
+    if (tid < 4 * C) sdb[tid] = 0.f;
+
+    f32x4 acc[NPW];
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) acc[u] = zero4();
 
     for (int b = 0; b < DV / 16; ++b) {
         __syncthreads();
@@ -960,31 +1008,32 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int x = tid + 512 * u, r = x / 16, c = x % 16;
-            sdO[r * LS + c] = nO[u];
-            sV[r * LS + c] = nV[u];
+            sdO[r * LS + c] = r < n ? nO[u] : 0.f;
+            sV[r * LS + c] = r < n ? cvt_in(nV[u]) : 0.f;
         }
         if (b + 1 < DV / 16) fetch_block(b + 1);
         __syncthreads();
-        if (w < 4) {   // U tile t = X (beta o V) - W S
-            const int t = w;
-            f32x4 a = zero4();
-            for (int kb = 0; kb <= t; ++kb) {
-                f32x4 bv = ldB(sV, LS, 16 * kb, 0);
+        {   // waves 0-3: U tile t = X (beta o V) - W S; waves 4-7: dU tile t =
+            // P^T dO + K_end dS'. Same shape, no branch: the C x C factor runs
+            // over all four token blocks (X is zero above its diagonal, P^T
+            // below), and the channel sum is split over two accumulators.
+            const bool isU = w < 4;
+            const int t = w & 3;
+            const float *A1 = isU ? sX : sPT, *B1 = isU ? sV : sdO, *A2 = isU ? sW : sKE, *B2 = isU ? sS : sD;
+            f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] *= sBeta[16 * kb + 4 * g + e];
-                a = mm4(ldA(sX, LC, 16 * t, 16 * kb), bv, a);
+            for (int kb = 0; kb < 4; ++kb) {
+                f32x4 bv = ldB(B1, LS, 16 * kb, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] *= isU ? sBeta[16 * kb + 4 * g + e] : 1.f;
+                a1 = mm4(ldA(A1, LC, 16 * t, 16 * kb), bv, a1);
             }
-            f32x4 ws = zero4();
 #pragma unroll
-            for (int kb = 0; kb < NCT; ++kb) ws = mm4(ldA(sW, LK, 16 * t, 16 * kb), ldB(sS, LS, 16 * kb, 0), ws);
-            stD(sU, LS, 16 * t, 0, a - ws);
-        } else {       // dU tile t = P^T dO + K_end dS'
-            const int t = w - 4;
-            f32x4 a = zero4();
-            for (int kb = t; kb < 4; ++kb) a = mm4(ldAT(sP, LC, 16 * t, 16 * kb), ldB(sdO, LS, 16 * kb, 0), a);
-#pragma unroll
-            for (int kb = 0; kb < NCT; ++kb) a = mm4(ldA(sKE, LK, 16 * t, 16 * kb), ldB(sD, LS, 16 * kb, 0), a);
-            stD(sdU, LS, 16 * t, 0, a);
+            for (int kb = 0; kb < NCT; kb += 2) {
+                a2 = mm4(ldA(A2, LK, 16 * t, 16 * kb), ldB(B2, LS, 16 * kb, 0), a2);
+                a3 = mm4(ldA(A2, LK, 16 * t, 16 * kb + 16), ldB(B2, LS, 16 * kb + 16, 0), a3);
+            }
+            stD(isU ? sU : sdU, LS, 16 * t, 0, a1 + (isU ? -1.f : 1.f) * (a2 + a3));
         }
         if (tid < DK) {
             float sacc = 0.f;
@@ -995,8 +1044,13 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
         __syncthreads();
         if (w < 4) {   // dv = beta o (X^T dU); beta part rowsum(V o X^T dU)
             const int t = w;
-            f32x4 a = zero4();
-            for (int kb = t; kb < 4; ++kb) a = mm4(ldAT(sX, LC, 16 * t, 16 * kb), ldB(sdU, LS, 16 * kb, 0), a);
+            f32x4 a = zero4(), a2 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; kb += 2) {   // X^T is zero below its diagonal
+                a = mm4(ldAT(sX, LC, 16 * t, 16 * kb), ldB(sdU, LS, 16 * kb, 0), a);
+                a2 = mm4(ldAT(sX, LC, 16 * t, 16 * kb + 16), ldB(sdU, LS, 16 * kb + 16, 0), a2);
+            }
+            a += a2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * t + 4 * g + e;
@@ -1009,28 +1063,34 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
                 if (i == 0) sdb[r] += rs;
             }
         }
+        // The owned tiles, one operand pattern for all (A rows and B^T rows
+        // at a tile offset, the same lane offset), so that the products of
+        // different tiles interleave: d(Gamma o Q) += dO S^T, dU S^T (dW is
+        // its negative), dK_end += U dS'^T, dP += dO U^T, dX += dU (beta o V)^T.
+        const int lo = i * LS + 4 * g;
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
-            const int idx = w + 8 * u;
-            if (idx >= NTILE) continue;
-            if (idx < NT1) {
-                const int kind = idx / (4 * NCT), rem = idx % (4 * NCT), t = rem / NCT, c = rem % NCT;
-                if (kind == 0) acc[u] = mm4(ldA(sdO, LS, 16 * t, 0), ldBT(sS, LS, 0, 16 * c), acc[u]);
-                else if (kind == 1) acc[u] = mm4(-ldA(sdU, LS, 16 * t, 0), ldBT(sS, LS, 0, 16 * c), acc[u]);
-                else acc[u] = mm4(ldA(sU, LS, 16 * t, 0), ldBT(sD, LS, 0, 16 * c), acc[u]);
-            } else if (idx < NT1 + 10) {
-                int R, J;
-                lower_tile(idx - NT1, R, J);
-                acc[u] = mm4(ldA(sdO, LS, 16 * R, 0), ldBT(sU, LS, 0, 16 * J), acc[u]);
-            } else {
-                int R, J;
-                lower_tile(idx - NT1 - 10, R, J);
-                f32x4 bv = ldBT(sV, LS, 0, 16 * J) * sBeta[16 * J + i];
-                acc[u] = mm4(ldA(sdU, LS, 16 * R, 0), bv, acc[u]);
-            }
+            if (u == NPW - 1 && w + 8 * u >= NTILE) continue;
+            int oa, ob, jb;
+            tile_operands<DK>(w + 8 * u, oa, ob, jb);
+            f32x4 bv = *reinterpret_cast<const f32x4*>(sm + ob + lo);
+            if (u >= UX) bv *= jb >= 0 ? sBeta[max(jb, 0) + i] : 1.f;   // no dX tile below slot 8 UX
+            acc[u] = mm4(*reinterpret_cast<const f32x4*>(sm + oa + lo), bv, acc[u]);
         }
     }
     __syncthreads();
+    // The keys and gates behind Gamma o K are loaded before the tiles are
+    // written out, so that their latency overlaps the stores. Thread
+    // (c, part) takes the RPP consecutive rows part RPP .. of channel c.
+    constexpr int NPART = 512 / DK, RPP = C / NPART;
+    const int kc = tid % DK, part = tid / DK;
+    TIn kraw[RPP], araw[RPP];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const size_t row = (size_t)(t0 + min(part * RPP + j, n - 1)) * H + h;
+        kraw[j] = ((const TIn*)p.k)[row * DK + kc];
+        araw[j] = ((const TIn*)p.gate)[SG ? row : row * DK + kc];
+    }
     // ---- write d(Gamma o Q), dK_end, dP; dW to LDS (replacing W); Gamma o K into sKE
 #pragma unroll
     for (int u = 0; u < NPW; ++u) {
@@ -1042,7 +1102,7 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) pb[PL::QG + (size_t)(16 * t + 4 * g + e) * DK + 16 * c + i] = acc[u][e];
             } else if (kind == 1) {
-                stD(sW, LK, 16 * t, 16 * c, acc[u]);
+                stD(sW, LK, 16 * t, 16 * c, -acc[u]);   // dW = -dU S^T
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) pb[PL::KE + (size_t)(16 * t + 4 * g + e) * DK + 16 * c + i] = acc[u][e];
@@ -1058,22 +1118,18 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
             }
         }
     }
-    {   // Gamma o K into sKE. Thread (c, part) holds the RPP consecutive rows
-        // part RPP .. of channel c in registers; the product of the gates
-        // before its rows comes from the other parts' products (LDS table in
-        // the now free value-block buffers).
-        constexpr int NPART = 512 / DK, RPP = C / NPART;
+    {   // Gamma o K into sKE. Thread (c, part) holds its rows in registers;
+        // the product of the gates before them comes from the other parts'
+        // products (LDS table in the now free value-block buffers).
         float* sPP = sm + SM::S;   // [NPART][DK]
-        const int c = tid % DK, part = tid / DK;
+        const int c = kc;
         float kr[RPP], lp[RPP];
         float f = 1.f;
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = part * RPP + j;
-            const size_t row = (size_t)(t0 + min(r, n - 1)) * H + h;
-            const float kv = ld_in((const TIn*)p.k + row * DK + c), av = gate_at<TIn>(p, row, DK, c, SG);
-            kr[j] = r < n ? kv : 0.f;
-            lp[j] = r < n ? av : 1.f;
+            kr[j] = r < n ? cvt_in(kraw[j]) : 0.f;
+            lp[j] = r < n ? cvt_in(araw[j]) : 1.f;
         }
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
@@ -1092,40 +1148,54 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     // ---- dX += dW (beta o Gamma o K)^T (tiles already owned), into LDS (the
     // value-block buffers are free now; T below goes where P was)
     float* sDX = sm + SM::S;
-    float* sT = sP;
+    float* sT = sPT;
 #pragma unroll
     for (int u = 0; u < NPW; ++u) {
         const int idx = w + 8 * u;
         if (idx < NT1 + 10 || idx >= NTILE) continue;
         int R, J;
         lower_tile(idx - NT1 - 10, R, J);
-        f32x4 a = acc[u];
+        f32x4 a = acc[u], a2 = zero4();
+        const float bj = sBeta[16 * J + i];
 #pragma unroll
-        for (int kb = 0; kb < NCT; ++kb) {
-            const f32x4 bk = ldBT(sKE, LK, 16 * kb, 16 * J) * sBeta[16 * J + i];
-            a = mm4(ldA(sW, LK, 16 * R, 16 * kb), bk, a);
+        for (int kb = 0; kb < NCT; kb += 2) {
+            a = mm4(ldA(sW, LK, 16 * R, 16 * kb), ldBT(sKE, LK, 16 * kb, 16 * J) * bj, a);
+            a2 = mm4(ldA(sW, LK, 16 * R, 16 * kb + 16), ldBT(sKE, LK, 16 * kb + 16, 16 * J) * bj, a2);
         }
-        stD(sDX, LC, 16 * R, 16 * J, a);
+        stD(sDX, LC, 16 * R, 16 * J, a + a2);
     }
     // ---- Y = X^T dW: d(Gamma o K) = beta o Y; beta part rowsum(Gamma o K o Y).
-    // Wave w: token tile t = w % 4, channel tiles half (w / 4); each half's
-    // row sums go to their own slot, added in a fixed order.
+    // Waves 0-3 take token tile t = w and the first half of the channel
+    // tiles, waves 4-7 t = 7 - w and the second half, so that the two waves
+    // of a SIMD share five token-block steps; the half's channel tiles are
+    // independent products on one X^T operand. Each half's row sums go to
+    // their own slot, added in a fixed order.
     {
-        const int t = w % 4, half = w / 4;
-        for (int c = half * (NCT / 2); c < (half + 1) * (NCT / 2); ++c) {
-            f32x4 a = zero4();
-            for (int kb = t; kb < 4; ++kb) a = mm4(ldAT(sX, LC, 16 * t, 16 * kb), ldB(sW, LK, 16 * kb, 16 * c), a);
+        constexpr int NH = NCT / 2;
+        const int half = w / 4, t = half ? 7 - w : w;
+        f32x4 ya[NH];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * t + 4 * g + e;
-                pb[PL::W + (size_t)r * DK + 16 * c + i] = sBeta[r] * a[e];
-                float rs = a[e] * sKE[r * LK + 16 * c + i];
-                rs += __shfl_xor(rs, 1, 16);
-                rs += __shfl_xor(rs, 2, 16);
-                rs += __shfl_xor(rs, 4, 16);
-                rs += __shfl_xor(rs, 8, 16);
-                if (i == 0) sdb[(1 + half) * C + r] += rs;
+        for (int cc = 0; cc < NH; ++cc) ya[cc] = zero4();
+        for (int kb = t; kb < 4; ++kb) {
+            const f32x4 xa = ldAT(sX, LC, 16 * t, 16 * kb);
+#pragma unroll
+            for (int cc = 0; cc < NH; ++cc) ya[cc] = mm4(xa, ldB(sW, LK, 16 * kb, 16 * (half * NH + cc)), ya[cc]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * t + 4 * g + e;
+            float rs = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < NH; ++cc) {
+                const int c = half * NH + cc;
+                pb[PL::W + (size_t)r * DK + 16 * c + i] = sBeta[r] * ya[cc][e];
+                rs += ya[cc][e] * sKE[r * LK + 16 * c + i];
             }
+            rs += __shfl_xor(rs, 1, 16);
+            rs += __shfl_xor(rs, 2, 16);
+            rs += __shfl_xor(rs, 4, 16);
+            rs += __shfl_xor(rs, 8, 16);
+            if (i == 0) sdb[(1 + half) * C + r] += rs;
         }
     }
     __syncthreads();
