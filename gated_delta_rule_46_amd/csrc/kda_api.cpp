@@ -223,7 +223,7 @@ int kda_chunk_bwd_cw(const void* q, const void* k, const void* v, const void* ga
         return KDA_EINVAL;
     const uintptr_t es = dtype == KDA_BF16 ? 2 : 4;
     if (need_data && (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(gate, es) ||
-                      !aligned(beta, es) || !aligned(dO, 4) || !aligned(grad_q, 4) || !aligned(grad_k, 4) ||
+                      !aligned(beta, es) || !aligned(dO) || !aligned(grad_q, 4) || !aligned(grad_k, 4) ||
                       !aligned(grad_v, 4) || !aligned(grad_gate, 4) || !aligned(grad_beta, 4)))
         return KDA_EALIGN;
     if ((S0 && !aligned(S0, 4)) || (dS_T && !aligned(dS_T, 4)) || (grad_S0 && !aligned(grad_S0, 4)) ||

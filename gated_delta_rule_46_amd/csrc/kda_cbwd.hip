@@ -52,8 +52,11 @@ constexpr int LS = 16 + 4;     // LDS row stride of 16-column slices
 // 1 and not stored), P on and below it in transposed position, i.e.
 //   XP[r][c] = X[r][c] (r > c),  XP[r][r] = P[r][r],  XP[c][r] = P[r][c] (r > c);
 // the gradient pass then replaces it by dP and dA the same way (dP on and
-// below the diagonal, dA transposed above it). The chunk's state and adjoint
-// follow per (chunk, head) in a second region (2 dk dv floats).
+// below the diagonal, dA transposed above it). W and K_end are row-major
+// (C x dk), Gamma o Q is stored transposed (dk x C: its only reader takes it
+// as an operand over tokens), and the state-side pass puts d(Gamma o Q) in
+// its place row-major. The chunk's state and adjoint follow per (chunk, head)
+// in a second region (2 dk dv floats).
 template <int DK>
 struct PrepLay {
     static constexpr size_t XP = 0, W = (size_t)C * C;
@@ -416,14 +419,17 @@ __global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
         float pfx = 1.f, sfx = 1.f;
         for (int qq = 0; qq < part; ++qq) pfx *= sCM[qq * CB + c];
         for (int qq = part + 1; qq < NP; ++qq) sfx *= sCM[qq * CB + c];
+        f32x4 qv[2];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = r0 + j;
             const float gm = pfx * lp[j];
-            out[PL::QG + (unsigned)r * DK + ch] = gm * q[j];             // Gamma o Q
+            qv[j / 4][j % 4] = gm * q[j];                                // (Gamma o Q)^T, 8 rows in a run
             out[PL::KE + (unsigned)r * DK + ch] = k[j] * (ml[j] * sfx);  // K_end
             sXK[r * LB + c] = sBeta[r] * gm * k[j];                      // beta o Gamma o K
         }
+        *reinterpret_cast<f32x4*>(out + PL::QG + (unsigned)ch * C + r0) = qv[0];
+        *reinterpret_cast<f32x4*>(out + PL::QG + (unsigned)ch * C + r0 + 4) = qv[1];
         if (part == NP - 1) out[PL::GAM + ch] = pfx * lp[7];
         __syncthreads();
         // W tiles: 4 token tiles x CB/16 channel tiles, two per wave
@@ -452,7 +458,13 @@ template <int DK, int CT>
 struct WalkSmem {
     static constexpr size_t PART = 0;                      // [4 waves][4 tiles][CT][64 lanes][4]
     static constexpr size_t UT = PART + 4 * 4 * CT * 256;  // [4 tiles][CT][64 lanes][4]
-    static constexpr size_t FLOATS = UT + 4 * CT * 256;
+    // the adjoint walk's dO rows of two chunks, [2][C][LD]; LD = 4 (mod 8)
+    // keeps the column reads of lane groups 0 and 1 on different banks
+    static constexpr int LD = 16 * CT + 4;
+    static constexpr size_t DO = UT + 4 * CT * 256;
+    // gamma of two chunks, [2][DK]
+    static constexpr size_t GB = DO + 2 * (size_t)C * LD;
+    static constexpr size_t FLOATS = GB + 2 * (size_t)DK;
     static constexpr size_t BYTES = FLOATS * 4;
 };
 
@@ -474,14 +486,14 @@ __device__ __forceinline__ void seq_range(const ChunkMap& m, int s, long& bos, l
 // the groups in which they are reloaded for the next chunk: each group right
 // after its last use in the current one, so that one register set suffices
 // and the loads spread over the step.
-template <int DK, int CT>
+template <class TIn, int DK, int CT>
 struct StateOps {
     static constexpr int RT = DK / 64;
     f32x4 w[4][RT];      // group 0: W[16t + i][own channels], A operand over own channels
     f32x4 x[4];          // group 1: X[16q + i][16kb..], A operand over tokens
-    f32x4 v[CT][4];      //          beta o V (K = tokens) per column tile, B operand
+    TIn v[CT][4][4];     //          V and beta as loaded (rows clamped to the chunk's last
+    TIn b[4][4];         //          token); beta o V, padding zeroed, is formed where used
     f32x4 ke[RT][4];     // group 2: K_end^T[own rows][16kb..], A operand over tokens
-    f32x4 gm[RT];        //          gamma of own rows
 };
 
 // Where chunk gi starts and how many tokens it has.
@@ -490,8 +502,8 @@ __device__ __forceinline__ void chunk_span(int gi, int cs, long bos, long eos, l
     n = (int)min((long)C, eos - t0);
 }
 
-template <int DK, int CT>
-__device__ __forceinline__ void state_load0(StateOps<DK, CT>& o, const float* pb, int q) {
+template <class TIn, int DK, int CT>
+__device__ __forceinline__ void state_load0(StateOps<TIn, DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     const int i = lane_i(), g = lane_g();
@@ -503,41 +515,57 @@ __device__ __forceinline__ void state_load0(StateOps<DK, CT>& o, const float* pb
 }
 
 template <class TIn, int DK, int CT>
-__device__ __forceinline__ void state_load1(StateOps<DK, CT>& o, const Params& p, const float* pb, long t0, int n,
+__device__ __forceinline__ void state_load1(StateOps<TIn, DK, CT>& o, const Params& p, const float* pb, long t0, int n,
                                             int h, int sl, int q) {
     using PL = PrepLay<DK>;
     const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
-    // X row tile q from the packed XP: tiles left of the diagonal as stored;
-    // the diagonal tile with its unit diagonal restored and P's part above it
-    // cleared
+    // X row tile q from the packed XP, as stored: the tiles left of the
+    // diagonal are X's; the diagonal tile gets its unit diagonal and loses
+    // P's part above it where it is used (state_x), not here, so that nothing
+    // waits for the loads
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        f32x4 xv = kb <= q ? *reinterpret_cast<const f32x4*>(pb + PL::XP + (size_t)(16 * q + i) * C + 16 * kb + 4 * g)
-                           : zero4();
-        if (kb == q) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) xv[s] = 4 * g + s < i ? xv[s] : (4 * g + s == i ? 1.f : 0.f);
-        }
-        o.x[kb] = xv;
-    }
-    // rows clamped to the chunk's last token, padding selected after the loads
+    for (int kb = 0; kb < 4; ++kb)
+        o.x[kb] = kb <= q ? *reinterpret_cast<const f32x4*>(pb + PL::XP + (size_t)(16 * q + i) * C + 16 * kb + 4 * g)
+                          : zero4();
+    // rows clamped to the chunk's last token; nothing here uses the values,
+    // so no wait follows the loads
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int tok = 16 * kb + 4 * g + s;
-            const size_t row = (size_t)(t0 + min(tok, n - 1)) * H + h;
-            const float bv = ld_in((const TIn*)p.beta + row);
+            const size_t row = (size_t)(t0 + min(16 * kb + 4 * g + s, n - 1)) * H + h;
+            o.b[kb][s] = ((const TIn*)p.beta)[row];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const float vv = ld_in((const TIn*)p.v + row * DV + 16 * (CT * sl + ct) + i);
-                o.v[ct][kb][s] = tok < n ? bv * vv : 0.f;
-            }
+            for (int ct = 0; ct < CT; ++ct) o.v[ct][kb][s] = ((const TIn*)p.v)[row * DV + 16 * (CT * sl + ct) + i];
         }
 }
 
-template <int DK, int CT>
-__device__ __forceinline__ void state_load2(StateOps<DK, CT>& o, const float* pb, int q) {
+// X tile (q, kb) as an A operand: the diagonal tile with its unit diagonal
+// restored and P's part above it cleared
+template <class TIn, int DK, int CT>
+__device__ __forceinline__ f32x4 state_x(const StateOps<TIn, DK, CT>& o, int kb, int q) {
+    f32x4 xv = o.x[kb];
+    if (kb == q) {
+        const int i = lane_i(), g = lane_g();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xv[s] = 4 * g + s < i ? xv[s] : (4 * g + s == i ? 1.f : 0.f);
+    }
+    return xv;
+}
+
+// beta o V of token block kb, column tile ct, as a B operand (zero past the
+// chunk's n tokens)
+template <class TIn, int DK, int CT>
+__device__ __forceinline__ f32x4 state_bv(const StateOps<TIn, DK, CT>& o, int ct, int kb, int n) {
+    const int g = lane_g();
+    f32x4 r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r[s] = 16 * kb + 4 * g + s < n ? cvt_in(o.b[kb][s]) * cvt_in(o.v[ct][kb][s]) : 0.f;
+    return r;
+}
+
+template <class TIn, int DK, int CT>
+__device__ __forceinline__ void state_load2(StateOps<TIn, DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     const int i = lane_i(), g = lane_g();
@@ -547,8 +575,6 @@ __device__ __forceinline__ void state_load2(StateOps<DK, CT>& o, const float* pb
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int s = 0; s < 4; ++s) o.ke[rt][kb][s] = pb[PL::KE + (size_t)(16 * kb + 4 * g + s) * DK + q * RW + 16 * rt + i];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) o.gm[rt] = *reinterpret_cast<const f32x4*>(pb + PL::GAM + q * RW + 16 * rt + 4 * g);
 }
 
 // First touch of a chunk two steps ahead: the slices of one (sequence,
@@ -572,7 +598,7 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
-    float *sPart = sm + SM::PART, *sU = sm + SM::UT;
+    float *sPart = sm + SM::PART, *sU = sm + SM::UT, *sG = sm + SM::GB;
 
     const int H = p.H, DV = p.DV, NSL = DV / (16 * CT);
     const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
@@ -582,6 +608,16 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
     int cs, ce;
     seq_range(p.map, s, bos, eos, cs, ce);
     auto block = [&](int gi) { return p.prep + ((size_t)gi * H + h) * PL::FLOATS; };
+    // gamma of a chunk: loaded a step ahead by the first DK / 4 threads and
+    // staged in LDS at the end of the step (no loaded register is carried
+    // over the loop, which would make the step wait for its last loads)
+    f32x4 lg = zero4();
+    auto load_g = [&](const float* pb) {
+        if (tid < DK / 4) lg = *reinterpret_cast<const f32x4*>(pb + PL::GAM + 4 * tid);
+    };
+    auto stage_g = [&](int gi) {
+        if (tid < DK / 4) *reinterpret_cast<f32x4*>(sG + (gi & 1) * DK + 4 * tid) = lg;
+    };
 
     f32x4 S[CT][RT];
 #pragma unroll
@@ -594,25 +630,32 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
                 S[ct][rt][e] =
                     p.S0 ? p.S0[((size_t)s * H + h) * DK * DV + (size_t)row * DV + 16 * (CT * sl + ct) + i] : 0.f;
             }
-    StateOps<DK, CT> op;
+    StateOps<TIn, DK, CT> op;
     if (cs < ce) {
         long t0;
         int n;
         chunk_span(cs, cs, bos, eos, t0, n);
-        state_load0<DK, CT>(op, block(cs), q);
+        state_load0<TIn, DK, CT>(op, block(cs), q);
         state_load1<TIn, DK, CT>(op, p, block(cs), t0, n, h, sl, q);
-        state_load2<DK, CT>(op, block(cs), q);
+        state_load2<TIn, DK, CT>(op, block(cs), q);
+        load_g(block(cs));
+        stage_g(cs);
     }
     uint32_t sink = 0;
+    // every prologue load done before the loop, so that the loop's waits
+    // count only its own loads
+    __builtin_amdgcn_s_waitcnt(0);
     for (int gi = cs; gi < ce; ++gi) {
         // XP, W and K_end of chunk gi + 2 (W and K_end are adjacent)
         const uint32_t tch =
             gi + 2 < ce ? touch_lines(block(gi + 2), PL::XP, (size_t)C * C, PL::W, 2 * (size_t)C * DK, sl, NSL, tid) : 0u;
         const bool more = gi + 1 < ce;
         const float* pn = block(more ? gi + 1 : gi);
-        long tn;
-        int nn;
+        long tc, tn;
+        int nc, nn;
+        chunk_span(gi, cs, bos, eos, tc, nc);
         chunk_span(more ? gi + 1 : gi, cs, bos, eos, tn, nn);
+        if (more) load_g(pn);   // staged at the end of this step
         float* ckS = p.ck + ((size_t)gi * H + h) * 2 * DK * DV;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -631,7 +674,7 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
                 for (int rt = 0; rt < RT; ++rt) acc = mm4(op.w[t][rt], S[ct][rt], acc);
                 *reinterpret_cast<f32x4*>(sPart + (((q * 4 + t) * CT + ct) * 64 + lane) * 4) = acc;
             }
-        if (more) state_load0<DK, CT>(op, pn, q);
+        if (more) state_load0<TIn, DK, CT>(op, pn, q);
         __syncthreads();
         // U tile q = X (beta o V) - W S
 #pragma unroll
@@ -639,7 +682,7 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                if (kb <= q) acc = mm4(op.x[kb], op.v[ct][kb], acc);
+                if (kb <= q) acc = mm4(state_x(op, kb, q), state_bv(op, ct, kb, nc), acc);
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2)
                 acc -= *reinterpret_cast<const f32x4*>(sPart + (((w2 * 4 + q) * CT + ct) * 64 + lane) * 4);
@@ -656,9 +699,13 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
                     acc = mm4(op.ke[rt][kb], *reinterpret_cast<const f32x4*>(sU + ((kb * CT + ct) * 64 + lane) * 4), acc);
-                S[ct][rt] = op.gm[rt] * S[ct][rt] + acc;
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(sG + (gi & 1) * DK + q * RW + 16 * rt + 4 * g);
+                S[ct][rt] = gm * S[ct][rt] + acc;
             }
-        if (more) state_load2<DK, CT>(op, pn, q);
+        if (more) {
+            state_load2<TIn, DK, CT>(op, pn, q);
+            stage_g(gi + 1);   // read after the next step's first barrier
+        }
         sink ^= tch;
     }
     // keep the L2 touches alive: a store that no real input triggers
@@ -676,10 +723,9 @@ struct AdjOps {
     static constexpr int RT = DK / 64;
     f32x4 ke[4][RT];   // group 0: K_end[16t + i][own channels], A operand over own channels
     f32x4 pt[4];       // group 1: P^T[16q + i][16kb..] = P[16kb + ..][16q + i], A operand over tokens
-    f32x4 d[CT][4];    // group 2: dO (K = tokens) per column tile, B operand
-    f32x4 qg[RT][4];   //          (Gamma o Q)^T[own rows][16kb..]
+    f32x4 d[CT][4];    // dO (K = tokens) per column tile, B operand, read from LDS
+    f32x4 qg[RT][4];   // group 2: (Gamma o Q)^T[own rows][16kb..]
     f32x4 wt[RT][4];   //          W^T[own rows][16kb..]
-    f32x4 gm[RT];
 };
 
 template <int DK, int CT>
@@ -700,48 +746,39 @@ __device__ __forceinline__ void adj_load1(AdjOps<DK, CT>& o, const float* pb, in
     const int i = lane_i(), g = lane_g();
     // P^T[16q + i][16kb + 4g + s] = P[16kb + 4g + s][16q + i] sits in the
     // packed XP at [16q + i][16kb + 4g + s] on and above the diagonal; below
-    // it (X's part) P is zero
+    // it (X's part) P is zero, which the diagonal tile gets where it is used
+    // (adj_pt), not here, so that nothing waits for the loads
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        f32x4 pv = kb >= q ? *reinterpret_cast<const f32x4*>(pb + PL::XP + (size_t)(16 * q + i) * C + 16 * kb + 4 * g)
+    for (int kb = 0; kb < 4; ++kb)
+        o.pt[kb] = kb >= q ? *reinterpret_cast<const f32x4*>(pb + PL::XP + (size_t)(16 * q + i) * C + 16 * kb + 4 * g)
                            : zero4();
-        if (kb == q) {
+}
+
+// P^T tile (q, kb) as an A operand, X's part of the diagonal tile cleared
+template <int DK, int CT>
+__device__ __forceinline__ f32x4 adj_pt(const AdjOps<DK, CT>& o, int kb, int q) {
+    f32x4 pv = o.pt[kb];
+    if (kb == q) {
+        const int i = lane_i(), g = lane_g();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) pv[s] = 4 * g + s >= i ? pv[s] : 0.f;
-        }
-        o.pt[kb] = pv;
+        for (int s = 0; s < 4; ++s) pv[s] = 4 * g + s >= i ? pv[s] : 0.f;
     }
+    return pv;
 }
 
 template <int DK, int CT>
-__device__ __forceinline__ void adj_load2(AdjOps<DK, CT>& o, const Params& p, const float* pb, long t0, int n, int h,
-                                          int sl, int q) {
+__device__ __forceinline__ void adj_load2(AdjOps<DK, CT>& o, const float* pb, int q) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
-    const int H = p.H, DV = p.DV, i = lane_i(), g = lane_g();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int tok = 16 * kb + 4 * g + s;
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const float dv = p.dO[((size_t)(t0 + min(tok, n - 1)) * H + h) * DV + 16 * (CT * sl + ct) + i];
-                o.d[ct][kb][s] = tok < n ? dv : 0.f;
-            }
-        }
+    const int i = lane_i(), g = lane_g();
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
+            o.qg[rt][kb] = *reinterpret_cast<const f32x4*>(pb + PL::QG + (size_t)(q * RW + 16 * rt + i) * C + 16 * kb + 4 * g);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const size_t off = (size_t)(16 * kb + 4 * g + s) * DK + q * RW + 16 * rt + i;
-                o.qg[rt][kb][s] = pb[PL::QG + off];
-                o.wt[rt][kb][s] = pb[PL::W + off];
-            }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) o.gm[rt] = *reinterpret_cast<const f32x4*>(pb + PL::GAM + q * RW + 16 * rt + 4 * g);
+            for (int s = 0; s < 4; ++s) o.wt[rt][kb][s] = pb[PL::W + (size_t)(16 * kb + 4 * g + s) * DK + q * RW + 16 * rt + i];
+        }
 }
 
 template <int DK, int CT>
@@ -750,7 +787,7 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
-    float *sPart = sm + SM::PART, *sdU = sm + SM::UT;
+    float *sPart = sm + SM::PART, *sdU = sm + SM::UT, *sDO = sm + SM::DO, *sG = sm + SM::GB;
 
     const int H = p.H, DV = p.DV, NSL = DV / (16 * CT);
     const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
@@ -761,6 +798,33 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
     seq_range(p.map, s, bos, eos, cs, ce);
     auto block = [&](int gi) { return p.prep + ((size_t)gi * H + h) * PL::FLOATS; };
     auto col = [&](int ct) { return 16 * (CT * sl + ct) + i; };
+
+    // dO rows of a chunk for this slice (four consecutive columns per thread,
+    // NDO quads) and gamma (first DK / 4 threads): loaded a step ahead and
+    // staged in LDS at the end of the step (padding rows zeroed then), so that
+    // the column reads of the B operands come from LDS instead of one global
+    // load per element, and no loaded register is carried over the loop
+    // (which would make the step wait for its last loads).
+    constexpr int QPR = 4 * CT, NDO = C * QPR / 256;
+    static_assert(NDO * 256 == C * QPR, "dO staging");
+    f32x4 ldo[NDO], lg = zero4();
+    auto load_do = [&](const float* pb, long t0, int n) {
+#pragma unroll
+        for (int u = 0; u < NDO; ++u) {
+            const int x = tid + 256 * u, r = x / QPR, c4 = 4 * (x % QPR);
+            ldo[u] = *reinterpret_cast<const f32x4*>(p.dO + ((size_t)(t0 + min(r, n - 1)) * H + h) * DV + 16 * CT * sl + c4);
+        }
+        if (tid < DK / 4) lg = *reinterpret_cast<const f32x4*>(pb + PL::GAM + 4 * tid);
+    };
+    auto stage_do = [&](int gi, int n) {
+        float* dst = sDO + (size_t)(gi & 1) * C * SM::LD;
+#pragma unroll
+        for (int u = 0; u < NDO; ++u) {
+            const int x = tid + 256 * u, r = x / QPR, c4 = 4 * (x % QPR);
+            *reinterpret_cast<f32x4*>(dst + r * SM::LD + c4) = r < n ? ldo[u] : zero4();
+        }
+        if (tid < DK / 4) *reinterpret_cast<f32x4*>(sG + (gi & 1) * DK + 4 * tid) = lg;
+    };
 
     f32x4 D[CT][RT];
 #pragma unroll
@@ -779,9 +843,14 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
         chunk_span(ce - 1, cs, bos, eos, t0, n);
         adj_load0<DK, CT>(op, block(ce - 1), q);
         adj_load1<DK, CT>(op, block(ce - 1), q);
-        adj_load2<DK, CT>(op, p, block(ce - 1), t0, n, h, sl, q);
+        adj_load2<DK, CT>(op, block(ce - 1), q);
+        load_do(block(ce - 1), t0, n);
+        stage_do(ce - 1, n);
     }
     uint32_t sink = 0;
+    // every prologue load done before the loop, so that the loop's waits
+    // count only its own loads
+    __builtin_amdgcn_s_waitcnt(0);
     for (int gi = ce - 1; gi >= cs; --gi) {
         // XP and W, K_end, Gamma o Q of chunk gi - 2 (the last three are adjacent)
         const uint32_t tch =
@@ -791,6 +860,7 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
         long tn;
         int nn;
         chunk_span(more ? gi - 1 : gi, cs, bos, eos, tn, nn);
+        if (more) load_do(pn, tn, nn);   // staged at the end of this step
         float* ckD = p.ck + ((size_t)gi * H + h) * 2 * DK * DV + (size_t)DK * DV;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -809,12 +879,19 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
             }
         if (more) adj_load0<DK, CT>(op, pn, q);
         __syncthreads();
+        {   // this chunk's dO (staged by the previous step) as B operands
+            const float* src = sDO + (size_t)(gi & 1) * C * SM::LD;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) op.d[ct][kb] = ldB(src, SM::LD, 16 * kb, 16 * ct);
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                if (kb >= q) acc = mm4(op.pt[kb], op.d[ct][kb], acc);
+                if (kb >= q) acc = mm4(adj_pt(op, kb, q), op.d[ct][kb], acc);
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2)
                 acc += *reinterpret_cast<const f32x4*>(sPart + (((w2 * 4 + q) * CT + ct) * 64 + lane) * 4);
@@ -832,9 +909,13 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
                     a1 = mm4(op.qg[rt][kb], op.d[ct][kb], a1);
                     a2 = mm4(op.wt[rt][kb], *reinterpret_cast<const f32x4*>(sdU + ((kb * CT + ct) * 64 + lane) * 4), a2);
                 }
-                D[ct][rt] = op.gm[rt] * D[ct][rt] + a1 - a2;
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(sG + (gi & 1) * DK + q * RW + 16 * rt + 4 * g);
+                D[ct][rt] = gm * D[ct][rt] + a1 - a2;
             }
-        if (more) adj_load2<DK, CT>(op, p, pn, tn, nn, h, sl, q);
+        if (more) {
+            adj_load2<DK, CT>(op, pn, q);
+            stage_do(gi - 1, nn);   // read after the next step's first barrier
+        }
         sink ^= tch;
     }
     if (sink == 0x9e3779b9u && p.H < 0) p.ck[0] = 0.f;

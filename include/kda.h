@@ -256,8 +256,9 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
  * fp32 MFMA. The gate gradient uses products of gates only, so exact zero and
  * negative gates have their ordinary derivatives. Supported: dk 64 or 128
  * (KDA_ENOTSUP otherwise), dv in {16, 32, 64, 128}, both dtypes and gate kinds,
- * packed sequences. Element alignment suffices for every pointer (workspace:
- * 16 bytes). workspace: kda_chunk_bwd_cw_workspace_bytes(...) bytes (per
+ * packed sequences. dO and the workspace must be 16-byte aligned (dO rows are
+ * read four values at a time); element alignment suffices for every other
+ * pointer. workspace: kda_chunk_bwd_cw_workspace_bytes(...) bytes (per
  * (chunk, head) the chunk's fp32 matrices, the state and adjoint at its
  * boundaries and the gradient intermediates); required.
  */

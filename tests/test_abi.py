@@ -130,6 +130,33 @@ def test_bwd_validation(lib):
     assert kda.bwd_workspace_bytes(2, 2, 64, 16, 16, N=2, varlen=True) == 0
 
 
+def test_bwd_cw_validation(lib):
+    def bwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, S0=None, dO=FAKE, dST=None, gq=FAKE, gk=FAKE,
+                 gv=FAKE, gg=FAKE, gb=FAKE, gS0=None, B=1, H=2, T=8, dk=64, dv=16, cu=None, N=0,
+                 dtype=kda.KDA_BF16, gate_kind=0, ws=FAKE, wsb=0, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_bwd_cw(*a.values())
+    assert bwd(B=0) == kda.KDA_EINVAL
+    assert bwd(dk=32) == kda.KDA_ENOTSUP                              # dk 64 or 128 only
+    assert bwd(dv=8) == kda.KDA_ENOTSUP
+    assert bwd(dtype=5) == kda.KDA_ENOTSUP
+    assert bwd(gate_kind=3) == kda.KDA_ENOTSUP
+    assert bwd(dO=None) == kda.KDA_EINVAL
+    assert bwd(gq=None) == kda.KDA_EINVAL
+    assert bwd(dO=FAKE + 4) == kda.KDA_EALIGN                         # dO rows are read 16 bytes at a time
+    assert bwd(gv=FAKE + 2) == kda.KDA_EALIGN
+    assert bwd(q=FAKE + 1) == kda.KDA_EALIGN
+    assert bwd(ws=FAKE + 8) == kda.KDA_EALIGN
+    assert bwd(wsb=1) == kda.KDA_EINVAL                               # workspace too small
+    assert bwd(ws=None) == kda.KDA_EINVAL                             # the library never allocates
+    assert bwd(cu=FAKE, B=2, N=2) == kda.KDA_EINVAL
+    assert bwd(N=4) == kda.KDA_EINVAL
+    w = kda.bwd_cw_workspace_bytes(1, 2, 64, 64, 16)
+    assert w > 0 and kda.bwd_cw_workspace_bytes(1, 2, 65, 64, 16) > w  # one more chunk
+    assert kda.bwd_cw_workspace_bytes(1, 2, 64, 32, 16) == 0
+
+
 def test_gauge_validation(lib):
     def fold(**kw):
         a = dict(q=FAKE, k=FAKE, gate=FAKE, qo=FAKE, ko=FAKE, go=FAKE, sign=None, B=1, H=2, T=8, dk=16, cu=None,
