@@ -464,7 +464,11 @@ struct WalkSmem {
     static constexpr size_t DO = UT + 4 * CT * 256;
     // gamma of two chunks, [2][DK]
     static constexpr size_t GB = DO + 2 * (size_t)C * LD;
-    static constexpr size_t FLOATS = GB + 2 * (size_t)DK;
+    // the walker's state (or adjoint) at the chunk boundary, [DK][LD], on its
+    // way to the chunk's checkpoint: written as D tiles, stored to memory as
+    // whole 16-byte row pieces
+    static constexpr size_t CK = GB + 2 * (size_t)DK;
+    static constexpr size_t FLOATS = CK + (size_t)DK * LD;
     static constexpr size_t BYTES = FLOATS * 4;
 };
 
@@ -598,7 +602,9 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
-    float *sPart = sm + SM::PART, *sU = sm + SM::UT, *sG = sm + SM::GB;
+    float *sPart = sm + SM::PART, *sU = sm + SM::UT, *sG = sm + SM::GB, *sCK = sm + SM::CK;
+    constexpr int QPR = 4 * CT, NCK = DK * QPR / 256;
+    static_assert(NCK * 256 == DK * QPR, "checkpoint staging");
 
     const int H = p.H, DV = p.DV, NSL = DV / (16 * CT);
     const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
@@ -657,13 +663,13 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
         chunk_span(more ? gi + 1 : gi, cs, bos, eos, tn, nn);
         if (more) load_g(pn);   // staged at the end of this step
         float* ckS = p.ck + ((size_t)gi * H + h) * 2 * DK * DV;
+        // S to LDS now, to its checkpoint after the barrier (16-byte row pieces)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ckS[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + 16 * (CT * sl + ct) + i] = S[ct][rt][e];
+                for (int e = 0; e < 4; ++e) sCK[(q * RW + 16 * rt + 4 * g + e) * SM::LD + 16 * ct + i] = S[ct][rt][e];
         // partial W S over own rows, every token tile
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -676,6 +682,12 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
             }
         if (more) state_load0<TIn, DK, CT>(op, pn, q);
         __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NCK; ++u) {
+            const int x = tid + 256 * u, r = x / QPR, c4 = 4 * (x % QPR);
+            *reinterpret_cast<f32x4*>(ckS + (size_t)r * DV + 16 * CT * sl + c4) =
+                *reinterpret_cast<const f32x4*>(sCK + r * SM::LD + c4);
+        }
         // U tile q = X (beta o V) - W S
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -787,7 +799,7 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
     using PL = PrepLay<DK>;
     constexpr int RW = DK / 4, RT = DK / 64;
     extern __shared__ __align__(16) float sm[];
-    float *sPart = sm + SM::PART, *sdU = sm + SM::UT, *sDO = sm + SM::DO, *sG = sm + SM::GB;
+    float *sPart = sm + SM::PART, *sdU = sm + SM::UT, *sDO = sm + SM::DO, *sG = sm + SM::GB, *sCK = sm + SM::CK;
 
     const int H = p.H, DV = p.DV, NSL = DV / (16 * CT);
     const int sl = item % NSL, hs = item / NSL, h = hs % H, s = hs / H;
@@ -805,8 +817,8 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
     // the column reads of the B operands come from LDS instead of one global
     // load per element, and no loaded register is carried over the loop
     // (which would make the step wait for its last loads).
-    constexpr int QPR = 4 * CT, NDO = C * QPR / 256;
-    static_assert(NDO * 256 == C * QPR, "dO staging");
+    constexpr int QPR = 4 * CT, NDO = C * QPR / 256, NCK = DK * QPR / 256;
+    static_assert(NDO * 256 == C * QPR && NCK * 256 == DK * QPR, "dO and checkpoint staging");
     f32x4 ldo[NDO], lg = zero4();
     auto load_do = [&](const float* pb, long t0, int n) {
 #pragma unroll
@@ -862,12 +874,13 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
         chunk_span(more ? gi - 1 : gi, cs, bos, eos, tn, nn);
         if (more) load_do(pn, tn, nn);   // staged at the end of this step
         float* ckD = p.ck + ((size_t)gi * H + h) * 2 * DK * DV + (size_t)DK * DV;
+        // dS' to LDS now, to its checkpoint after the barrier (16-byte row pieces)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ckD[(size_t)(q * RW + 16 * rt + 4 * g + e) * DV + col(ct)] = D[ct][rt][e];
+                for (int e = 0; e < 4; ++e) sCK[(q * RW + 16 * rt + 4 * g + e) * SM::LD + 16 * ct + i] = D[ct][rt][e];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -879,6 +892,12 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
             }
         if (more) adj_load0<DK, CT>(op, pn, q);
         __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NCK; ++u) {
+            const int x = tid + 256 * u, r = x / QPR, c4 = 4 * (x % QPR);
+            *reinterpret_cast<f32x4*>(ckD + (size_t)r * DV + 16 * CT * sl + c4) =
+                *reinterpret_cast<const f32x4*>(sCK + r * SM::LD + c4);
+        }
         {   // this chunk's dO (staged by the previous step) as B operands
             const float* src = sDO + (size_t)(gi & 1) * C * SM::LD;
 #pragma unroll
