@@ -178,22 +178,37 @@ __device__ __forceinline__ void local_products(const float* a, float* lp, float*
 }
 
 // ================================================================ 1. prep
-// One workgroup (4 waves) per (chunk, head). Pass 1 over blocks of 32 key
-// channels accumulates the gated Gram matrices G and P level by level; then
-// X = (I + Diag(beta) G)^{-1} (16x16 diagonal blocks by forward substitution,
-// the rest by block products); pass 2 forms W, K_end, Gamma o Q and gamma.
-// Thread (c, part) holds channel c of the block on the 8 rows 8 part ..
-// 8 part + 7 in registers; gate products that span several row parts come
-// from the part products exchanged through the CM table.
+// One workgroup (4 waves) per (chunk, head), four per CU. Pass 1 over blocks
+// of 32 key channels accumulates the gated Gram matrices G and P level by
+// level; then X = (I + Diag(beta) G)^{-1} (16x16 diagonal blocks by forward
+// substitution, the rest by block products); pass 2 forms W, K_end, Gamma o Q
+// and gamma. Thread (c, part) holds channel c of the block on the 8 rows
+// 8 part .. 8 part + 7 in registers; gate products that span several row
+// parts come from the part products exchanged through the CM table. The
+// staging area of pass 1 (XK, XQ) holds G once pass 1 is done and the staged
+// beta o Gamma o K of pass 2 once X is formed; P goes from the accumulators
+// straight to the workspace.
 template <int DK>
 struct PrepSmem {
     static constexpr int CB = 32, LB = CB + 4, NP = 8;
-    static constexpr size_t CM = 0, XK = CM + NP * CB, XQ = XK + (size_t)C * LB;
-    static constexpr size_t G = XQ + (size_t)C * LB, P = G + (size_t)C * LC, XI = P + (size_t)C * LC;
-    static constexpr size_t BETA = XI + (size_t)C * LC;
-    static constexpr size_t FLOATS = BETA + C;
+    static constexpr size_t CM = 0, BETA = CM + NP * CB, XK = BETA + C, XQ = XK + (size_t)C * LB, G = XK;
+    static constexpr size_t XI = XK + (2 * (size_t)C * LB > (size_t)C * LC ? 2 * (size_t)C * LB : (size_t)C * LC);
+    static constexpr size_t FLOATS = XI + (size_t)C * LC;
     static constexpr size_t BYTES = FLOATS * 4;
+    static_assert(XK % 4 == 0 && XI % 4 == 0, "16-byte operand reads");
 };
+
+// The lower 16x16 tiles a prep wave accumulates: slot 0 its diagonal tile
+// (w, w), which takes the in-tile levels; slot 1 one of the four tiles split
+// at the half-32 level; slot 2 (waves 0 and 1) one of the two split at the
+// half-16 level. Every level but the half-16 one has one tile per wave.
+__device__ __forceinline__ bool prep_tile(int w, int u, int& R, int& J) {
+    if (u == 0) { R = w; J = w; return true; }
+    if (u == 1) { R = 2 + (w >> 1); J = w & 1; return true; }
+    R = w == 0 ? 3 : 1;
+    J = w == 0 ? 2 : 0;
+    return w < 2;
+}
 
 // Gates, keys and queries of rows r0 .. r0 + 7 on one channel; rows past the
 // chunk's n >= 1 tokens are zero keys and queries with unit gates. The loads
@@ -254,8 +269,8 @@ __device__ __forceinline__ void level_weights(const float* a, const float* lp, c
     }
 }
 
-// Stage level L (k o w, q o w into XK, XQ), then add its tiles of G and P:
-// wave w owns lower tiles w, w + 4, w + 8.
+// Stage level L (k o w, q o w into XK, XQ), then add its tile of G and P to
+// the wave's slot for that level.
 template <int L, int LB, int CB>
 __device__ __forceinline__ void prep_level(const float* a, const float* k, const float* q, const float* lp,
                                           const float* ml, int c, int part, int w, const float* sCM, float* sXK,
@@ -269,14 +284,9 @@ __device__ __forceinline__ void prep_level(const float* a, const float* k, const
         sXQ[(r0 + j) * LB + c] = q[j] * ps[j];
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-        const int idx = w + 4 * u;
-        if (idx >= 10) continue;
-        int R, J;
-        lower_tile(idx, R, J);
-        if (L < 6 && !tile_at_level(R, J, L < 2 ? L : 2)) continue;
-        if (L == 6 && R != J) continue;
+    constexpr int u = L == 0 ? 1 : L == 1 ? 2 : 0;
+    int R, J;
+    if (prep_tile(w, u, R, J)) {
         f32x4 tg = zero4(), tp = zero4();
 #pragma unroll
         for (int kb = 0; kb < CB / 16; ++kb) {
@@ -301,14 +311,14 @@ __device__ __forceinline__ void prep_level(const float* a, const float* k, const
 }
 
 template <class TIn, int DK, bool SG>
-__global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
+__global__ void __launch_bounds__(256, 4) cb_prep_kernel(Params p) {
     using SM = PrepSmem<DK>;
     using PL = PrepLay<DK>;
     constexpr int CB = SM::CB, LB = SM::LB, NP = SM::NP;
     static_assert(CB * NP == 256 && NP * 8 == C && DK % CB == 0, "prep thread layout");
     extern __shared__ __align__(16) float sm[];
     float *sCM = sm + SM::CM, *sXK = sm + SM::XK, *sXQ = sm + SM::XQ;
-    float *sG = sm + SM::G, *sP = sm + SM::P, *sX = sm + SM::XI, *sBeta = sm + SM::BETA;
+    float *sG = sm + SM::G, *sX = sm + SM::XI, *sBeta = sm + SM::BETA;
 
     const int H = p.H;
     const int item = blockIdx.x;
@@ -326,7 +336,7 @@ __global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
 
     if (tid < C) sBeta[tid] = tid < n ? ld_in((const TIn*)p.beta + (size_t)(t0 + tid) * H + h) : 0.f;
 
-    // ---- pass 1: G and P, lower tiles; wave w owns tiles w, w + 4, w + 8
+    // ---- pass 1: G and P, lower tiles, in the wave's three slots
     f32x4 accG[3], accP[3];
 #pragma unroll
     for (int u = 0; u < 3; ++u) { accG[u] = zero4(); accP[u] = zero4(); }
@@ -350,22 +360,25 @@ __global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
         prep_level<5, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
         prep_level<6, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
     }
-    // ---- G and P to LDS (upper tiles zero) and out
-    for (int x = tid; x < C * C; x += 256) {
-        const int r = x / C, c = x % C;
-        if ((r / 16) < (c / 16)) { sG[r * LC + c] = 0.f; sP[r * LC + c] = 0.f; }
-    }
+    // ---- G to LDS (lower tiles: nothing reads the upper ones) and P to the
+    // workspace on and above the diagonal, XP[c][r] = P[r][c]: a lane's four
+    // rows of one column are one 16-byte run (on a diagonal tile, those with
+    // r >= c only)
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-        const int idx = w + 4 * u;
-        if (idx >= 10) continue;
         int R, J;
-        lower_tile(idx, R, J);
+        if (!prep_tile(w, u, R, J)) continue;
         stD(sG, LC, 16 * R, 16 * J, accG[u]);
-        stD(sP, LC, 16 * R, 16 * J, accP[u]);
+        const int i = lane_i(), g = lane_g();
+        float* dst = out + PL::XP + (size_t)(16 * J + i) * C + 16 * R + 4 * g;
+        if (R != J) {
+            *reinterpret_cast<f32x4*>(dst) = accP[u];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * g + e >= i) dst[e] = accP[u][e];
+        }
     }
-    __syncthreads();
-    for (int x = tid; x < C * C; x += 256) sX[(x / C) * LC + x % C] = 0.f;
     __syncthreads();
     // ---- X = (I + A)^{-1}, A = Diag(beta) G: diagonal 16x16 blocks (wave b,
     // lanes 0..15 = columns) by forward substitution
@@ -398,10 +411,10 @@ __global__ void __launch_bounds__(256, 2) cb_prep_kernel(Params p) {
         }
         __syncthreads();
     }
-    // X below the diagonal, P on and (transposed) above it
+    // X strictly below the diagonal (the upper tiles of sX are never written)
     for (int x = tid; x < C * C; x += 256) {
         const int r = x / C, c = x % C;
-        out[PL::XP + x] = r > c ? sX[r * LC + c] : sP[c * LC + r];
+        if (r > c) out[PL::XP + x] = sX[r * LC + c];
     }
 
     // ---- pass 2: W = X (beta o Gamma o K), K_end, Gamma o Q, gamma
