@@ -1356,8 +1356,9 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
 // 8 part + 7 of the chunk, in registers. Every gate scan (prefix products,
 // the reverse and forward affine scans of the adjoint) runs as a local scan
 // over those 8 rows plus a carry composed from the summaries of the other row
-// parts, exchanged through a small LDS table; only the operands and results
-// of the level products go through LDS.
+// parts, exchanged through a small LDS table; besides dA and dP only the
+// operands and results of the level products between row parts go through
+// LDS.
 template <int DK>
 struct GateSmem {
     static constexpr int CB = 32, LB = CB + 4, NP = 8;
@@ -1433,23 +1434,26 @@ __device__ __forceinline__ void gate_products(int w, const float* sdA, const flo
     }
 }
 
-// Registers of thread (c, part) in the channel phase: gates a, keys k,
-// queries q and beta of its 8 rows, the gradients accumulated for them, and
-// the block's share of rowsum(dA o G) per row.
+// Registers of thread (c, part) in the channel phase: gates a, keys k and
+// queries q of its 8 rows (beta is read from LDS where it is used), the
+// gradients accumulated for them, and
+// rowsum(dA o G) per row, summed over the blocks the thread has taken.
 struct GateRegs {
-    float a[8], k[8], q[8], b[8], dq[8], dk[8], da[8], rp[8];
+    float a[8], k[8], q[8], dq[8], dk[8], da[8], rp[8];
 };
 
 // One level of the binary split, half width HW = 32 >> L. Right rows of a
 // group (its second half) carry pre = product of the gates from the middle
 // up to the row, left rows suf = product of the gates after the row up to
 // the middle. With HW >= 8 a half is a whole number of row parts and pre/suf
-// come from the part products in CM; with HW >= 16 the adjoint scans of a
-// half also cross row parts and take a carry through the CV table.
+// come from the part products in CM, and the level's products are MFMA tiles
+// over the staged rows; with HW >= 16 the adjoint scans of a half also cross
+// row parts and take a carry through the CV table. With HW <= 4 every group
+// lies inside one thread's rows and the products are taken in registers.
 template <int L, int LB, int CB>
 __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, float* sXK, float* sXQ, float* sYZ,
                                           float* sYP, float* sCV, const float* sCM, const float* sdA,
-                                          const float* sdP) {
+                                          const float* sdP, const float* sBeta) {
     constexpr int HW = 32 >> L;
     const int r0 = 8 * part;
     float ps[8];
@@ -1491,20 +1495,60 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
             }
         }
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float kw = x.k[j] * ps[j];
-        sXK[(r0 + j) * LB + c] = right[j] ? x.b[j] * kw : kw;
-        sXQ[(r0 + j) * LB + c] = x.q[j] * ps[j];
-    }
-    __syncthreads();
-    gate_products<L, LB>(w, sdA, sdP, sXK, sXQ, sYZ, sYP);
-    __syncthreads();
     float yz[8], yp[8];
+    if constexpr (HW >= 8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        yz[j] = sYZ[(r0 + j) * LB + c];
-        yp[j] = sYP[(r0 + j) * LB + c];
+        for (int j = 0; j < 8; ++j) {
+            const float kw = x.k[j] * ps[j];
+            sXK[(r0 + j) * LB + c] = right[j] ? sBeta[r0 + j] * kw : kw;
+            sXQ[(r0 + j) * LB + c] = x.q[j] * ps[j];
+        }
+        __syncthreads();
+        gate_products<L, LB>(w, sdA, sdP, sXK, sXQ, sYZ, sYP);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            yz[j] = sYZ[(r0 + j) * LB + c];
+            yp[j] = sYP[(r0 + j) * LB + c];
+        }
+    } else {
+        // every group lies inside the thread's 8 rows: the level's products
+        // are sums over at most 4 of its own rows, with the coefficients of
+        // dA and dP read from LDS (the same for all channels of a row part)
+        float xk[8], xq[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float kw = x.k[j] * ps[j];
+            xk[j] = right[j] ? sBeta[r0 + j] * kw : kw;
+            xq[j] = x.q[j] * ps[j];
+        }
+#pragma unroll
+        for (int s0 = 0; s0 < 8; s0 += 2 * HW) {
+#pragma unroll
+            for (int v = 0; v < HW; ++v) {
+                yz[s0 + v] = 0.f;
+                yp[s0 + v] = 0.f;
+            }
+            // right row j: Y = dA_L XK, Y_P = dP_L XK over the left rows; the
+            // same coefficients give the left rows' Z = dA_L^T (beta o XK) +
+            // dP_L^T XQ, accumulated row by row
+#pragma unroll
+            for (int u = 0; u < HW; ++u) {
+                const int j = s0 + HW + u;
+                const float* ra = sdA + (r0 + j) * LC + r0 + s0;
+                const float* rq = sdP + (r0 + j) * LC + r0 + s0;
+                float y = 0.f, y2 = 0.f;
+#pragma unroll
+                for (int v = 0; v < HW; ++v) {
+                    const float ca = ra[v], cq = rq[v];
+                    y += ca * xk[s0 + v];
+                    y2 += cq * xk[s0 + v];
+                    yz[s0 + v] += ca * xk[j] + cq * xq[j];
+                }
+                yz[j] = y;
+                yp[j] = y2;
+            }
+        }
     }
     if constexpr (HW >= 8) {
         constexpr int SPS = HW / 8;
@@ -1513,7 +1557,7 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
         if (rt) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float yg = x.b[j] * yz[j];   // the dG term of the row
+                const float yg = sBeta[r0 + j] * yz[j];   // the dG term of the row
                 x.rp[j] += x.k[j] * ps[j] * yz[j];
                 x.dk[j] += ps[j] * yg;
                 x.dq[j] += ps[j] * yp[j];
@@ -1556,7 +1600,7 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
 #pragma unroll
             for (int u = HW - 1; u >= 0; --u) {
                 const int j = s0 + HW + u;
-                const float yg = x.b[j] * yz[j];
+                const float yg = sBeta[r0 + j] * yz[j];
                 x.rp[j] += x.k[j] * ps[j] * yz[j];
                 x.dk[j] += ps[j] * yg;
                 x.dq[j] += ps[j] * yp[j];
@@ -1628,6 +1672,12 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
     float* ok = p.gk + rowbase * DK;
     float* oa = p.gg + rowbase * (SG ? 1 : DK);
     const unsigned rs = (unsigned)H * DK;   // row stride of q, k and per-channel gates
+    // x.rp and dsa sum over the blocks; their sums over the channels of a
+    // row part are taken once, after the last block
+    GateRegs x;
+    float dsa[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { x.rp[j] = 0.f; dsa[j] = 0.f; }
 #pragma unroll 1
     for (int cb = 0; cb < DK / CB; ++cb) {
         // the row and channel indices are re-derived in every block: kept
@@ -1637,7 +1687,6 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
         asm volatile("" : "+v"(c), "+v"(part));
         const int r0 = 8 * part;
         const int ch = CB * cb + c;
-        GateRegs x;
         float dqg[8], dgk[8], dke[8];
         load_rows<TIn, SG>(gk, gq, ga, rs, H, n, r0, ch, x.a, x.k, x.q);
 #pragma unroll
@@ -1648,7 +1697,6 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
             dqg[j] = r < n ? v0 : 0.f;
             dgk[j] = r < n ? v1 : 0.f;
             dke[j] = r < n ? v2 : 0.f;
-            x.rp[j] = 0.f;
         }
         // local products, and the local forward scan of drel_end = dK_end o k
         float lp[8], ml[8];
@@ -1662,8 +1710,6 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
         sCM[part * CB + c] = lp[7];
         sCL[part * CB + c] = Lend;
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x.b[j] = sBeta[r0 + j];
         float pfx = 1.f, sfx = 1.f, Lin = 0.f;
         for (int qq = 0; qq < part; ++qq) {
             const float m = sCM[qq * CB + c];
@@ -1699,12 +1745,12 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x.da[j] += (j > 0 ? gm[j - 1] : pfx) * (Rl[j] + ml[j] * Cin);
 
-        gate_level<0, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
-        gate_level<1, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
-        gate_level<2, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
-        gate_level<3, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
-        gate_level<4, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
-        gate_level<5, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP);
+        gate_level<0, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
+        gate_level<1, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
+        gate_level<2, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
+        gate_level<3, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
+        gate_level<4, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
+        gate_level<5, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = r0 + j;
@@ -1715,21 +1761,27 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
                 if (!SG) oa[o] = x.da[j];
             }
         }
-        // per-row sums over the 32 channels of the row part (lanes 0-31 or
-        // 32-63 of the wave), then over the blocks: rowsum(dA o G) and, for a
-        // scalar gate, its gradient
+        if (SG) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dsa[j] += x.da[j];
+        }
+    }
+    // per-row sums over the 32 channels of the row part (lanes 0-31 or 32-63
+    // of the wave): rowsum(dA o G) and, for a scalar gate, its gradient
+    {
+        const int c = tid % CB, r0 = 8 * (tid / CB);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float v = x.rp[j];
-            float d = SG ? x.da[j] : 0.f;
+            float d = SG ? dsa[j] : 0.f;
 #pragma unroll
             for (int o = 1; o < 32; o <<= 1) {
                 v += __shfl_xor(v, o, 32);
                 if (SG) d += __shfl_xor(d, o, 32);
             }
             if (c == 0) {
-                sRP[r0 + j] = (cb == 0 ? 0.f : sRP[r0 + j]) + v;
-                if (SG) sdat[r0 + j] = (cb == 0 ? 0.f : sdat[r0 + j]) + d;
+                sRP[r0 + j] = v;
+                if (SG) sdat[r0 + j] = d;
             }
         }
     }
