@@ -1465,9 +1465,12 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
     int hlo = 0, hhi = 0;
     if constexpr (HW >= 8) {
         constexpr int SPS = HW / 8;
-        hlo = part / SPS * SPS;
+        // with halves of two or more row parts both halves of a wave (parts
+        // 2w, 2w + 1) lie in the same half: the branches on rt are uniform
+        const int hf = SPS > 1 ? __builtin_amdgcn_readfirstlane(part / SPS) : part;
+        hlo = hf * SPS;
         hhi = hlo + SPS;
-        rt = (part / SPS) & 1;
+        rt = hf & 1;
         float ss = 1.f;
         for (int qq = hlo; qq < part; ++qq) sp *= sCM[qq * CB + c];
         for (int qq = part + 1; qq < hhi; ++qq) ss *= sCM[qq * CB + c];
@@ -1751,11 +1754,14 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
         gate_level<3, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
         gate_level<4, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
         gate_level<5, LB, CB>(x, c, part, w, sXK, sXQ, sYZ, sYP, sCV, sCM, sdA, sdP, sBeta);
+        // the output offsets are formed here, not held from the loads on
+        int rw = r0, cw = ch;
+        asm volatile("" : "+v"(rw), "+v"(cw));
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int r = r0 + j;
+            const int r = rw + j;
             if (r < n) {
-                const unsigned o = (unsigned)r * rs + ch;
+                const unsigned o = (unsigned)r * rs + cw;
                 oq[o] = x.dq[j];
                 ok[o] = x.dk[j];
                 if (!SG) oa[o] = x.da[j];
