@@ -181,8 +181,8 @@ __device__ __forceinline__ void local_products(const float* a, float* lp, float*
 // One workgroup (4 waves) per (chunk, head), four per CU. Pass 1 over blocks
 // of 32 key channels accumulates the gated Gram matrices G and P level by
 // level; then X = (I + Diag(beta) G)^{-1} (16x16 diagonal blocks by forward
-// substitution, the rest by block products); pass 2 forms W, K_end, Gamma o Q
-// and gamma. Thread (c, part) holds channel c of the block on the 8 rows
+// substitution, the rest by block products); pass 2 forms W. K_end, Gamma o Q
+// and gamma go out in pass 1, from the rows it holds. Thread (c, part) holds channel c of the block on the 8 rows
 // 8 part .. 8 part + 7 in registers; gate products that span several row
 // parts come from the part products exchanged through the CM table. The
 // staging area of pass 1 (XK, XQ) holds G once pass 1 is done and the staged
@@ -215,17 +215,17 @@ __device__ __forceinline__ bool prep_tile(int w, int u, int& R, int& J) {
 // read row min(r, n - 1) unconditionally and the padding is selected after:
 // straight-line loads are all issued before the first wait, where a load in
 // a branch followed by a conversion waits once per row.
-template <class TIn, bool SG>
+template <class TIn, bool SG, bool WQ = true>
 __device__ __forceinline__ void load_rows(const TIn* gk, const TIn* gq, const TIn* ga, unsigned rs, int H, int n,
                                           int r0, int ch, float* a, float* k, float* q) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int r = r0 + j, rc = min(r, n - 1);
         const unsigned o = (unsigned)rc * rs + ch;
-        const float kv = ld_in(gk + o), qv = ld_in(gq + o);
+        const float kv = ld_in(gk + o), qv = WQ ? ld_in(gq + o) : 0.f;
         const float av = SG ? ld_in(ga + (unsigned)rc * H) : ld_in(ga + o);
         k[j] = r < n ? kv : 0.f;
-        q[j] = r < n ? qv : 0.f;
+        if (WQ) q[j] = r < n ? qv : 0.f;
         a[j] = r < n ? av : 1.f;
     }
 }
@@ -352,6 +352,22 @@ __global__ void __launch_bounds__(256, 4) cb_prep_kernel(Params p) {
         local_products(a, lp, ml);
         sCM[part * CB + c] = lp[7];   // the last reader of CM passed a barrier since
         __syncthreads();
+        {
+            // K_end, Gamma o Q (transposed) and gamma of the block's channels
+            const int r0 = 8 * part;
+            float pfx = 1.f, sfx = 1.f;
+            for (int qq = 0; qq < part; ++qq) pfx *= sCM[qq * CB + c];
+            for (int qq = part + 1; qq < NP; ++qq) sfx *= sCM[qq * CB + c];
+            f32x4 qv[2];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                qv[j / 4][j % 4] = (pfx * lp[j]) * q[j];
+                out[PL::KE + (unsigned)(r0 + j) * DK + ch] = k[j] * (ml[j] * sfx);
+            }
+            *reinterpret_cast<f32x4*>(out + PL::QG + (unsigned)ch * C + r0) = qv[0];
+            *reinterpret_cast<f32x4*>(out + PL::QG + (unsigned)ch * C + r0 + 4) = qv[1];
+            if (part == NP - 1) out[PL::GAM + ch] = pfx * lp[7];
+        }
         prep_level<0, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
         prep_level<1, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
         prep_level<2, LB, CB>(a, k, q, lp, ml, c, part, w, sCM, sXK, sXQ, accG, accP);
@@ -417,33 +433,22 @@ __global__ void __launch_bounds__(256, 4) cb_prep_kernel(Params p) {
         if (r > c) out[PL::XP + x] = sX[r * LC + c];
     }
 
-    // ---- pass 2: W = X (beta o Gamma o K), K_end, Gamma o Q, gamma
+    // ---- pass 2: W = X (beta o Gamma o K)
 #pragma unroll 1
     for (int cb = 0; cb < DK / CB; ++cb) {
         int c = tid % CB, part = tid / CB;
         asm volatile("" : "+v"(c), "+v"(part));
         const int r0 = 8 * part, ch = CB * cb + c;
-        float a[8], k[8], q[8], lp[8], ml[8];
-        load_rows<TIn, SG>(gk, gq, ga, rs, H, n, r0, ch, a, k, q);
+        float a[8], k[8], lp[8], ml[8];
+        load_rows<TIn, SG, false>(gk, gq, ga, rs, H, n, r0, ch, a, k, nullptr);
         local_products(a, lp, ml);
         __syncthreads();   // CM and XK of the previous block are read
         sCM[part * CB + c] = lp[7];
         __syncthreads();
-        float pfx = 1.f, sfx = 1.f;
+        float pfx = 1.f;
         for (int qq = 0; qq < part; ++qq) pfx *= sCM[qq * CB + c];
-        for (int qq = part + 1; qq < NP; ++qq) sfx *= sCM[qq * CB + c];
-        f32x4 qv[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = r0 + j;
-            const float gm = pfx * lp[j];
-            qv[j / 4][j % 4] = gm * q[j];                                // (Gamma o Q)^T, 8 rows in a run
-            out[PL::KE + (unsigned)r * DK + ch] = k[j] * (ml[j] * sfx);  // K_end
-            sXK[r * LB + c] = sBeta[r] * gm * k[j];                      // beta o Gamma o K
-        }
-        *reinterpret_cast<f32x4*>(out + PL::QG + (unsigned)ch * C + r0) = qv[0];
-        *reinterpret_cast<f32x4*>(out + PL::QG + (unsigned)ch * C + r0 + 4) = qv[1];
-        if (part == NP - 1) out[PL::GAM + ch] = pfx * lp[7];
+        for (int j = 0; j < 8; ++j) sXK[(r0 + j) * LB + c] = sBeta[r0 + j] * (pfx * lp[j]) * k[j];
         __syncthreads();
         // W tiles: 4 token tiles x CB/16 channel tiles, two per wave
 #pragma unroll
