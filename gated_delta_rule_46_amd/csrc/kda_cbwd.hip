@@ -1362,7 +1362,7 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
 // the reverse and forward affine scans of the adjoint) runs as a local scan
 // over those 8 rows plus a carry composed from the summaries of the other row
 // parts, exchanged through a small LDS table; besides dA and dP only the
-// operands and results of the level products between row parts go through
+// operands and results of the products of the two widest levels go through
 // LDS.
 template <int DK>
 struct GateSmem {
@@ -1386,9 +1386,9 @@ struct GateSmem {
 template <int L, int LB>
 __device__ __forceinline__ void gate_products(int w, const float* sdA, const float* sdP, const float* sXK,
                                              const float* sXQ, float* sYZ, float* sYP) {
-    constexpr int HW = 32 >> L;
+    static_assert(L < 2, "the levels inside a wave's rows are taken in registers");
     const int i = lane_i(), g = lane_g();
-    if constexpr (L < 2) {
+    {
         // L = 0: Y rows {2, 3} from J {0, 1}; Z rows {0, 1} from R {2, 3}
         // L = 1: Y rows {1, 3} from J {0, 2}; Z rows {0, 2} from R {1, 3}
         for (int job = w; job < 12; job += 4) {
@@ -1413,29 +1413,6 @@ __device__ __forceinline__ void gate_products(int w, const float* sdA, const flo
                 stD(sYZ, LB, 16 * J, 16 * ct, a);
             }
         }
-    } else {
-        // in-tile level: wave w owns diagonal tile w
-        const int b = w;
-        f32x4 ag = ldA(sdA, LC, 16 * b, 16 * b), ap = ldA(sdP, LC, 16 * b, 16 * b);
-        f32x4 bgT = ldAT(sdA, LC, 16 * b, 16 * b), bpT = ldAT(sdP, LC, 16 * b, 16 * b);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bool ky = sep_in(i, 4 * g + s, HW);   // A(i, k) = dG[r = i][j = k]
-            const bool kz = sep_in(4 * g + s, i, HW);   // A(i, k) = dG[r = k][j = i]
-            ag[s] = ky ? ag[s] : 0.f;
-            ap[s] = ky ? ap[s] : 0.f;
-            bgT[s] = kz ? bgT[s] : 0.f;
-            bpT[s] = kz ? bpT[s] : 0.f;
-        }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const f32x4 xk = ldB(sXK, LB, 16 * b, 16 * ct), xq = ldB(sXQ, LB, 16 * b, 16 * ct);
-            f32x4 yz = mm4(ag, xk, zero4());
-            yz = mm4(bgT, xk, yz);
-            yz = mm4(bpT, xq, yz);
-            stD(sYZ, LB, 16 * b, 16 * ct, yz);
-            stD(sYP, LB, 16 * b, 16 * ct, mm4(ap, xk, zero4()));
-        }
     }
 }
 
@@ -1451,10 +1428,11 @@ struct GateRegs {
 // group (its second half) carry pre = product of the gates from the middle
 // up to the row, left rows suf = product of the gates after the row up to
 // the middle. With HW >= 8 a half is a whole number of row parts and pre/suf
-// come from the part products in CM, and the level's products are MFMA tiles
-// over the staged rows; with HW >= 16 the adjoint scans of a half also cross
-// row parts and take a carry through the CV table. With HW <= 4 every group
-// lies inside one thread's rows and the products are taken in registers.
+// come from the part products in CM. With HW >= 16 the level's products are
+// MFMA tiles over the rows staged in LDS, and the adjoint scans of a half
+// also cross row parts and take a carry through the CV table. With HW = 8 a
+// group is the two row parts of one wave and with HW <= 4 it lies inside one
+// thread's rows: the products are taken in registers.
 template <int L, int LB, int CB>
 __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, float* sXK, float* sXQ, float* sYZ,
                                           float* sYP, float* sCV, const float* sCM, const float* sdA,
@@ -1504,7 +1482,53 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
         }
     }
     float yz[8], yp[8];
-    if constexpr (HW >= 8) {
+    if constexpr (HW == 8) {
+        // a group is the wave's two row parts (lanes 0-31 its left half,
+        // lanes 32-63 its right half, the same channels): the other half's
+        // operands come over by a lane swap, and the products are taken in
+        // registers with the coefficients of dA and dP read from LDS
+        float xk[8], xq[8], oxk[8], oxq[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float kw = x.k[j] * ps[j];
+            xk[j] = rt ? sBeta[r0 + j] * kw : kw;
+            xq[j] = x.q[j] * ps[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            oxk[j] = __shfl_xor(xk[j], 32);
+            oxq[j] = __shfl_xor(xq[j], 32);
+        }
+        const int gb = r0 & ~15;
+        if (rt) {   // right rows: Y, Y_P over the left rows
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float* ra = sdA + (gb + 8 + u) * LC + gb;
+                const float* rq = sdP + (gb + 8 + u) * LC + gb;
+                float y = 0.f, y2 = 0.f;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    y += ra[v] * oxk[v];
+                    y2 += rq[v] * oxk[v];
+                }
+                yz[u] = y;
+                yp[u] = y2;
+            }
+        } else {    // left rows: Z over the right rows, accumulated row by row
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                yz[v] = 0.f;
+                yp[v] = 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float* ra = sdA + (gb + 8 + u) * LC + gb;
+                const float* rq = sdP + (gb + 8 + u) * LC + gb;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) yz[v] += ra[v] * oxk[u] + rq[v] * oxq[u];
+            }
+        }
+    } else if constexpr (HW >= 16) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float kw = x.k[j] * ps[j];
@@ -1715,6 +1739,7 @@ __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
             Ll[j] = Lend;
             Lend = dke[j] * x.k[j] + x.a[j] * Lend;
         }
+        if (cb > 0) __syncthreads();   // the last carry reads of CM (half-16 level) are done
         sCM[part * CB + c] = lp[7];
         sCL[part * CB + c] = Lend;
         __syncthreads();
