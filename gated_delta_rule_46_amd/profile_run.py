@@ -4,7 +4,9 @@
                                                   [--copy-mib 256]
 
 Runs, on cuda:0 and with seeded synthetic inputs: --fwd forward calls on the
-Complex KDA workload (B=2, H=16, T=8192, d=128, bf16, chunk 64), --bwd
+workload --fwd-workload names (ckda: Complex KDA, B=2, H=16, T=8192, d=128,
+bf16, chunk 64, the default; kda: KDA, B=4, H=16, T=4096; gdn: GDN with eight
+packed sequences, H=32, T=110,440), --bwd
 chunkwise backward calls (kda_chunk_bwd_cw) and --bwd-token token-form
 backward calls (kda_chunk_bwd) on the same workload, --decode decode steps on the decode
 workload (N=256, H=32, d=128, fp32 state in place), and --copy-mib MiB of
@@ -22,6 +24,7 @@ import sys
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--fwd", type=int, default=3)
+    ap.add_argument("--fwd-workload", choices=("ckda", "kda", "gdn"), default="ckda")
     ap.add_argument("--bwd", type=int, default=2)
     ap.add_argument("--bwd-token", type=int, default=0)
     ap.add_argument("--decode", type=int, default=8)
@@ -36,16 +39,20 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     kda.library()
     if args.fwd > 0:
-        w = inputs.ckda_fwd(seed=0)
+        w = {"ckda": inputs.ckda_fwd, "kda": inputs.kda_fwd, "gdn": inputs.gdn_varlen}[args.fwd_workload](seed=0)
         q, k, v, g, b = (t.to(dev) for t in (w.q, w.k, w.v, w.gate, w.beta))
-        ws = torch.empty(kda.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk), device=dev, dtype=torch.uint8)
+        cu = None if w.cu_seqlens is None else w.cu_seqlens.to(dev)
+        N = w.n_seqs
+        ws = torch.empty(kda.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, N, cu is not None, w.dtype),
+                         device=dev, dtype=torch.uint8)
         o = torch.empty((w.B, w.T, w.H, w.dv), device=dev, dtype=torch.float32)
-        ST = torch.empty((w.B, w.H, w.dk, w.dv), device=dev, dtype=torch.float32)
+        ST = torch.empty((N, w.H, w.dk, w.dv), device=dev, dtype=torch.float32)
         for _ in range(args.fwd):
-            kda.chunk_fwd(q, k, v, g, b, chunk=w.chunk, gate_kind=0, out=o, S_T=ST, workspace=ws)
+            kda.chunk_fwd(q, k, v, g, b, cu_seqlens=cu, chunk=w.chunk, gate_kind=w.gate_kind, out=o, S_T=ST,
+                          workspace=ws)
         torch.cuda.synchronize()
-        print("forward calls: %d" % args.fwd, flush=True)
-        del q, k, v, g, b, ws, o, ST
+        print("forward calls: %d (%s)" % (args.fwd, args.fwd_workload), flush=True)
+        del q, k, v, g, b, cu, ws, o, ST
     for calls, chunked in ((args.bwd, True), (args.bwd_token, False)):
         if calls <= 0:
             continue

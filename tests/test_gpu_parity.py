@@ -289,6 +289,18 @@ def test_walkers_agree(kda):
     assert err(o4, ro) <= 2e-2 and err(S4, rS) <= 2e-2
 
 
+@pytest.mark.parametrize("gate,B,H,T,s0", [("ckda", 1, 2, 1611, 0.3), ("kda", 2, 3, 3000, 0.0),
+                                           ("gdn", 1, 4, 1536, 0.2), ("ckda", 3, 1, 4097, 0.1)])
+def test_long_sequences_few_heads(kda, gate, B, H, T, s0):
+    """Long sequences at few heads (bf16, dk = dv = 128, chunk 64: the
+    one-slice walker with far fewer slices than CUs): 24 to 65 chunks, ragged
+    last chunks and exactly 24 chunks, with and without an initial state; o
+    and S_T against the oracle."""
+    w = inputs.make_forward("long", B=B, H=H, T=T, dk=128, dv=128, chunk=64, dtype=torch.bfloat16, gate=gate,
+                            s0_std=s0, seed=T + H)
+    check(kda, w)
+
+
 def test_stage_split_equals_single_call(kda):
     """The forward as one call equals its two stages called one after the
     other (prep into a caller-provided workspace, then the state walk) bit
