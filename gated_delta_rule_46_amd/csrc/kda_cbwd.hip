@@ -1132,15 +1132,17 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
         if (b + 1 < DV / 16) fetch_block(b + 1);
         __syncthreads();
         {   // waves 0-3: U tile t = X (beta o V) - W S; waves 4-7: dU tile t =
-            // P^T dO + K_end dS'. Same shape, no branch: the C x C factor runs
-            // over all four token blocks (X is zero above its diagonal, P^T
-            // below), and the channel sum is split over two accumulators.
+            // P^T dO + K_end dS'. The C x C factor runs over the token blocks
+            // where it is nonzero (X up to its diagonal block, P^T from it on):
+            // waves t and 4 + t share a SIMD and take t + 1 and 4 - t blocks,
+            // five per SIMD. The channel sum is split over two accumulators.
             const bool isU = w < 4;
             const int t = w & 3;
             const float *A1 = isU ? sX : sPT, *B1 = isU ? sV : sdO, *A2 = isU ? sW : sKE, *B2 = isU ? sS : sD;
             f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
+                if (isU ? kb > t : kb < t) continue;   // wave-uniform
                 f32x4 bv = ldB(B1, LS, 16 * kb, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bv[e] *= isU ? sBeta[16 * kb + 4 * g + e] : 1.f;
