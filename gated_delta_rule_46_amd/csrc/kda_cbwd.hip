@@ -147,9 +147,17 @@ struct Params {
     float *gq, *gk, *gv, *gg, *gb, *gS0;
     float* prep;   // PrepLay per (chunk, head)
     float* ck;     // S and dS' per (chunk, head): 2 * dk * dv floats
+    float* ud;     // U and dU per (chunk, head), from the walks: 2 * C * dv floats (ud_tile)
     ChunkMap map;
     int H, DV;
 };
+
+// The 16 x 16 tile (token tile t, column tile c16) of U (k = 0) or dU (k = 1)
+// of (chunk, head) item `base` in D-tile order: lane l = 16 g + i holds rows
+// 16 t + 4 g + e of column 16 c16 + i as four consecutive floats at 4 l.
+__device__ __forceinline__ float* ud_tile(const Params& p, size_t base, int k, int c16, int t) {
+    return p.ud + base * 2 * C * p.DV + (size_t)k * C * p.DV + ((size_t)c16 * 4 + t) * 256;
+}
 
 template <class TIn>
 __device__ __forceinline__ float gate_at(const Params& p, size_t row, int DK, int c, bool sg) {
@@ -717,6 +725,8 @@ __device__ __forceinline__ void state_walk(const Params& p, int item) {
             for (int w2 = 0; w2 < 4; ++w2)
                 acc -= *reinterpret_cast<const f32x4*>(sPart + (((w2 * 4 + q) * CT + ct) * 64 + lane) * 4);
             *reinterpret_cast<f32x4*>(sU + ((q * CT + ct) * 64 + lane) * 4) = acc;
+            // and to the workspace for the state-side gradients
+            *reinterpret_cast<f32x4*>(ud_tile(p, (size_t)gi * H + h, 0, CT * sl + ct, q) + 4 * lane) = acc;
         }
         if (more) state_load1<TIn, DK, CT>(op, p, pn, tn, nn, h, sl, q);
         __syncthreads();
@@ -933,6 +943,7 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
             for (int w2 = 0; w2 < 4; ++w2)
                 acc += *reinterpret_cast<const f32x4*>(sPart + (((w2 * 4 + q) * CT + ct) * 64 + lane) * 4);
             *reinterpret_cast<f32x4*>(sdU + ((q * CT + ct) * 64 + lane) * 4) = acc;
+            *reinterpret_cast<f32x4*>(ud_tile(p, (size_t)gi * H + h, 1, CT * sl + ct, q) + 4 * lane) = acc;
         }
         if (more) adj_load1<DK, CT>(op, pn, q);
         __syncthreads();
@@ -984,8 +995,8 @@ __global__ void __launch_bounds__(256) cb_walk_kernel(Params p, int nstate) {
 
 // ================================================================ 4. state-side gradients
 // One workgroup (8 waves) per (chunk, head), streaming the value columns in
-// slices of 16: U and dU of the slice, dv, and running sums of d(Gamma o Q),
-// dW, dK_end, dP and dX (tiles owned by waves). Then dX += dW (beta o Gamma o
+// slices of 16: U and dU of the slice (as the walks left them), dv, and
+// running sums of d(Gamma o Q), dW, dK_end, dP and dX (tiles owned by waves). Then dX += dW (beta o Gamma o
 // K)^T and Y = X^T dW. Outputs replace the prep block's W (d(Gamma o K) =
 // beta o Y), K_end (dK_end), Gamma o Q (its gradient), P (dP) and gamma
 // (dgamma); dX and the beta terms go to the extra block.
@@ -1049,28 +1060,24 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     float* ckS = p.ck + base * 2 * DK * DV;   // read by the value blocks; then the beta parts go here
     const float* ckD = ckS + (size_t)DK * DV;
 
-    // Every load of the prologue (the packed XP, W, K_end, beta and the first
-    // value block) is issued before the first LDS store, so their latencies
-    // overlap.
-    constexpr int NXP = C * C / 4 / 512, NWK = C * DK / 4 / 512;
-    static_assert(NXP * 512 * 4 == C * C && NWK * 512 * 4 == C * DK, "prologue tiling");
-    f32x4 lxp[NXP], lw[NWK], lke[NWK];
+    // Every load of the prologue (the packed XP, beta and the first value
+    // block) is issued before the first LDS store, so their latencies overlap.
+    constexpr int NXP = C * C / 4 / 512;
+    static_assert(NXP * 512 * 4 == C * C, "prologue tiling");
+    f32x4 lxp[NXP];
 #pragma unroll
     for (int j = 0; j < NXP; ++j) lxp[j] = *reinterpret_cast<const f32x4*>(pb + PL::XP + 4 * (tid + 512 * j));
-#pragma unroll
-    for (int j = 0; j < NWK; ++j) {
-        lw[j] = *reinterpret_cast<const f32x4*>(pb + PL::W + 4 * (tid + 512 * j));
-        lke[j] = *reinterpret_cast<const f32x4*>(pb + PL::KE + 4 * (tid + 512 * j));
-    }
     const TIn lbeta = ((const TIn*)p.beta)[(size_t)(t0 + min(tid % C, n - 1)) * H + h];
 
-    // The value-column block b + 1 (S, dS', dO, V) is fetched into registers
-    // while block b computes and written to LDS at the start of its turn.
-    // Rows past the chunk end read row n - 1 and are zeroed only when staged,
-    // so that nothing waits for these loads before then.
+    // The value-column block b + 1 (S, dS', dO, V, and U and dU from the
+    // walks) is fetched into registers while block b computes and written to
+    // LDS at the start of its turn. Rows past the chunk end read row n - 1
+    // and are zeroed only when staged, so that nothing waits for these loads
+    // before then (U and dU are zero there already).
     static_assert(DK * 4 <= 512 && C * 16 == 2 * 512, "value-block staging");
     const int sr = tid / 4, sc = 4 * (tid % 4);
-    f32x4 nS = zero4(), nD = zero4();
+    const int uk = tid / 256, uf = tid % 256;   // U (uk = 0) or dU, float4 uf of the 64 x 16 block
+    f32x4 nS = zero4(), nD = zero4(), nUD;
     float nO[2];
     TIn nV[2];
     auto fetch_block = [&](int b) {
@@ -1078,6 +1085,7 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
             nS = *reinterpret_cast<const f32x4*>(ckS + (size_t)sr * DV + 16 * b + sc);
             nD = *reinterpret_cast<const f32x4*>(ckD + (size_t)sr * DV + 16 * b + sc);
         }
+        nUD = *reinterpret_cast<const f32x4*>(ud_tile(p, base, uk, b, uf / 64) + 4 * (uf % 64));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int x = tid + 512 * u, r = x / 16, c = x % 16;
@@ -1088,26 +1096,15 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
     };
     fetch_block(0);
 
-    // X (unit diagonal, zero above) and P^T (zero below the diagonal) out of
-    // the packed XP: element [r][c] of XP is X[r][c] below the diagonal and
-    // P[c][r] = P^T[r][c] on and above it
+    // X (unit diagonal, zero above) out of the packed XP: element [r][c] of
+    // XP is X[r][c] below the diagonal
 #pragma unroll
     for (int j = 0; j < NXP; ++j) {
         const int x = tid + 512 * j, r = x / (C / 4), c = 4 * (x % (C / 4));
-        f32x4 xv, pv;
+        f32x4 xv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            xv[e] = c + e < r ? lxp[j][e] : (c + e == r ? 1.f : 0.f);
-            pv[e] = c + e >= r ? lxp[j][e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) xv[e] = c + e < r ? lxp[j][e] : (c + e == r ? 1.f : 0.f);
         *reinterpret_cast<f32x4*>(sX + r * LC + c) = xv;
-        *reinterpret_cast<f32x4*>(sPT + r * LC + c) = pv;
-    }
-#pragma unroll
-    for (int j = 0; j < NWK; ++j) {
-        const int x = tid + 512 * j, r = x / (DK / 4), c = 4 * (x % (DK / 4));
-        *reinterpret_cast<f32x4*>(sW + r * LK + c) = lw[j];
-        *reinterpret_cast<f32x4*>(sKE + r * LK + c) = lke[j];
     }
     if (tid < C) sBeta[tid] = tid < n ? cvt_in(lbeta) : 0.f;
     if (tid < DK) sdg[tid] = 0.f;
@@ -1129,39 +1126,20 @@ __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
             sdO[r * LS + c] = r < n ? nO[u] : 0.f;
             sV[r * LS + c] = r < n ? cvt_in(nV[u]) : 0.f;
         }
+        {
+            float* dst = uk ? sdU : sU;
+            const int t = uf / 64, ln = uf % 64;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(16 * t + 4 * (ln / 16) + e) * LS + ln % 16] = nUD[e];
+        }
         if (b + 1 < DV / 16) fetch_block(b + 1);
         __syncthreads();
-        {   // waves 0-3: U tile t = X (beta o V) - W S; waves 4-7: dU tile t =
-            // P^T dO + K_end dS'. The C x C factor runs over the token blocks
-            // where it is nonzero (X up to its diagonal block, P^T from it on):
-            // waves t and 4 + t share a SIMD and take t + 1 and 4 - t blocks,
-            // five per SIMD. The channel sum is split over two accumulators.
-            const bool isU = w < 4;
-            const int t = w & 3;
-            const float *A1 = isU ? sX : sPT, *B1 = isU ? sV : sdO, *A2 = isU ? sW : sKE, *B2 = isU ? sS : sD;
-            f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (isU ? kb > t : kb < t) continue;   // wave-uniform
-                f32x4 bv = ldB(B1, LS, 16 * kb, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] *= isU ? sBeta[16 * kb + 4 * g + e] : 1.f;
-                a1 = mm4(ldA(A1, LC, 16 * t, 16 * kb), bv, a1);
-            }
-#pragma unroll
-            for (int kb = 0; kb < NCT; kb += 2) {
-                a2 = mm4(ldA(A2, LK, 16 * t, 16 * kb), ldB(B2, LS, 16 * kb, 0), a2);
-                a3 = mm4(ldA(A2, LK, 16 * t, 16 * kb + 16), ldB(B2, LS, 16 * kb + 16, 0), a3);
-            }
-            stD(isU ? sU : sdU, LS, 16 * t, 0, a1 + (isU ? -1.f : 1.f) * (a2 + a3));
-        }
         if (tid < DK) {
             float sacc = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) sacc += sS[tid * LS + c] * sD[tid * LS + c];
             sdg[tid] += sacc;
         }
-        __syncthreads();
         if (w < 4) {   // dv = beta o (X^T dU); beta part rowsum(V o X^T dU)
             const int t = w;
             f32x4 a = zero4(), a2 = zero4();
@@ -1838,7 +1816,7 @@ size_t cbwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, in
     const long nch = chunk_count_bound(B, T, cb::C, varlen, N);
     const size_t ib = varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0;
     const size_t prep = (dk == 64 ? cb::PrepLay<64>::FLOATS : cb::PrepLay<128>::FLOATS);
-    const size_t per = prep + 2 * (size_t)dk * dv;
+    const size_t per = prep + 2 * (size_t)dk * dv + 2 * (size_t)cb::C * dv;
     return ib + (size_t)nch * H * per * 4;
 }
 
@@ -1864,8 +1842,9 @@ static hipError_t launch_cbwd_t(const BwdArgs& a) {
     ChunkMap map{a.cu_seqlens, varlen ? cstart : nullptr, a.T, N, NC, 0, NC};
     float* prep = (float*)(ws + ib);
     float* ck = prep + (size_t)nch * a.H * PrepLay<DK>::FLOATS;
+    float* ud = ck + (size_t)nch * a.H * 2 * DK * a.dv;
     Params p{a.q, a.k, a.v, a.gate, a.beta, a.S0, a.dO, a.dST, a.g_q, a.g_k, a.g_v, a.g_gate, a.g_beta, a.g_S0,
-             prep, ck, map, a.H, a.dv};
+             prep, ck, ud, map, a.H, a.dv};
     hipError_t e;
     if (varlen) {
         e = launch_chunk_index(a.cu_seqlens, cstart, N, C, a.stream);
