@@ -260,7 +260,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
  * read four values at a time); element alignment suffices for every other
  * pointer. workspace: kda_chunk_bwd_cw_workspace_bytes(...) bytes (per
  * (chunk, head) the chunk's fp32 matrices, the state and adjoint at its
- * boundaries and the gradient intermediates); required.
+ * boundaries, the chunk's U and dU, and the gradient intermediates);
+ * required.
  */
 size_t kda_chunk_bwd_cw_workspace_bytes(int B, int H, int T, int dk, int dv, int N, int has_cu_seqlens);
 int kda_chunk_bwd_cw(const void* q, const void* k, const void* v, const void* gate, const void* beta,
