@@ -16,7 +16,9 @@ K timed calls run at the clock the device holds under sustained work (after
 an idle period the clock needs about 20 ms of load to ramp up). The GPU
 clock is read from sysfs while the timed calls are still executing.
 The decode step (N=256 sequences, H=32, d=128, fp32 state of 512 MiB updated
-in place) is timed as one block of 128 consecutive steps. The backward
+in place) is timed as one block of 128 consecutive steps, and set beside a
+plain device copy of the same 512 MiB (read and written) as a practical
+bandwidth ceiling. The backward
 (kda_chunk_bwd, gradients of every input for given dO and dS_T) is timed on
 the same forward workload. Forward and backward are also timed at 32k tokens
 per step (B=4, H=16, T=8192) with the KDA and the Complex KDA gate recipes,
@@ -131,6 +133,24 @@ def time_region(fn, iters: int, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / iters   # ms per call
+
+
+def copy_bandwidth(dev, stream, mib: int = 512, iters: int = 20) -> dict:
+    """Read + write GB/s of a plain device copy of `mib` MiB (the size of the
+    decode state), two ways: hipMemcpy's copy kernel (Tensor.copy_) and torch's
+    vectorized elementwise kernel (a multiply by one). A practical ceiling for
+    streaming kernels on this machine, beside the 8 TB/s peak."""
+    import torch
+    src = torch.ones(mib << 18, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    nbytes = 2 * src.numel() * 4
+    res = {}
+    for name, fn in (("memcpy", lambda i: dst.copy_(src)), ("elementwise", lambda i: torch.mul(src, 1.0, out=dst))):
+        for i in range(5):
+            fn(i)
+        res[name] = round(nbytes / (time_region(fn, iters, stream) * 1e-3) / 1e9, 1)
+    del src, dst
+    return res
 
 
 def per_call_ms(fn, iters: int, stream):
@@ -397,8 +417,12 @@ def main(argv=None) -> int:
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_dec,
                          "kernel": "decode_step_kernel", "bytes_per_launch": dbytes},
         }
-        print("[bench] decode %.4f ms/step, %.1f GB/s" % (per, gbs), file=sys.stderr, flush=True)
         del S, steps
+        copy = copy_bandwidth(dev, stream)
+        decode["roofline"]["copy_gbs"] = copy
+        decode["roofline"]["frac_of_copy"] = round(gbs / max(copy.values()), 4)
+        print("[bench] decode %.4f ms/step, %.1f GB/s (device copy: %s GB/s)" % (per, gbs, copy), file=sys.stderr,
+              flush=True)
 
     # ---------------------------------------------------------------- backward
     backward = None
