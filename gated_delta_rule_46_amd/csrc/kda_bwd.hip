@@ -210,6 +210,7 @@ struct BwdFetch {
 template <class TIn, int DK, int NWV, int COLS, bool SG>
 __global__ void __launch_bounds__(NWV * WAVE)
 chunk_bwd_kernel(BwdParams p) {
+    lds_poison((uint32_t)sizeof(BwdLds<DK, NWV * COLS, NWV, SG>));
     constexpr int NT = NWV * WAVE, NC = NWV * COLS, SUB = BW_SUB;
     constexpr int RPL = DK >= WAVE ? DK / WAVE : 1;        // state rows per lane
     constexpr int CKF = NT * RPL * COLS;                    // floats per checkpoint slot
@@ -525,6 +526,7 @@ __global__ void __launch_bounds__(256)
 chunk_bwd_reduce_kernel(const float* __restrict__ part, long rows, int dk, int ncg, bool sg,
                         float* __restrict__ dq, float* __restrict__ dkg, float* __restrict__ dg,
                         float* __restrict__ db) {
+    lds_poison(0);
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     const long n = rows * dk;
     if (e < n) {

@@ -320,6 +320,7 @@ __device__ __forceinline__ void prep_level(const float* a, const float* k, const
 
 template <class TIn, int DK, bool SG>
 __global__ void __launch_bounds__(256, 4) cb_prep_kernel(Params p) {
+    lds_poison((uint32_t)PrepSmem<DK>::BYTES);
     using SM = PrepSmem<DK>;
     using PL = PrepLay<DK>;
     constexpr int CB = SM::CB, LB = SM::LB, NP = SM::NP;
@@ -988,6 +989,7 @@ __device__ __forceinline__ void adjoint_walk(const Params& p, int item) {
 // XCD.
 template <class TIn, int DK, int CT>
 __global__ void __launch_bounds__(256) cb_walk_kernel(Params p, int nstate) {
+    lds_poison((uint32_t)WalkSmem<DK, CT>::BYTES);
     const int b = blockIdx.x;
     if (b < nstate) state_walk<TIn, DK, CT>(p, xcd_remap(b, nstate));
     else adjoint_walk<DK, CT>(p, xcd_remap(b - nstate, (int)gridDim.x - nstate));
@@ -1038,6 +1040,7 @@ __device__ __forceinline__ void tile_operands(int idx, int& oa, int& ob, int& jb
 
 template <class TIn, int DK, bool SG>
 __global__ void __launch_bounds__(512) cb_grad_state_kernel(Params p) {
+    lds_poison((uint32_t)GradSmem<DK>::BYTES);
     using SM = GradSmem<DK>;
     using PL = PrepLay<DK>;
     constexpr int LK = SM::LK, NCT = DK / 16;
@@ -1634,6 +1637,7 @@ __device__ __forceinline__ void gate_level(GateRegs& x, int c, int part, int w, 
 
 template <class TIn, int DK, bool SG>
 __global__ void __launch_bounds__(256, 2) cb_grad_gate_kernel(Params p) {
+    lds_poison((uint32_t)GateSmem<DK>::BYTES);
     using SM = GateSmem<DK>;
     using PL = PrepLay<DK>;
     constexpr int CB = SM::CB, LB = SM::LB, NP = SM::NP;

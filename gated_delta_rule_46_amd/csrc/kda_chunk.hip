@@ -141,6 +141,7 @@ namespace kda {
 // cstart[s] = sum over earlier sequences of ceil(len / C); one workgroup.
 __global__ void __launch_bounds__(256) chunk_index_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ cstart,
                                                           int N, int C) {
+    lds_poison(0);
     __shared__ int32_t part[256];
     __shared__ int32_t carry;
     if (threadIdx.x == 0) carry = 0;
@@ -1115,6 +1116,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, int item) {
 
 template <class TIn, int DK, int C, bool SG, bool F32M, bool EW>
 __global__ void __launch_bounds__(256, F32M ? 1 : (EW ? 2 : 3)) chunk_prep_kernel(PrepParams p) {
+    lds_poison((uint32_t)PrepLds<TIn, DK, C, F32M, EW>::BYTES);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0u;
     prep_item<TIn, DK, C, SG, F32M, EW>(p, xcd_remap(blockIdx.x, gridDim.x));
 }
@@ -1215,6 +1217,7 @@ __device__ __forceinline__ void touch_chunk(uint32_t (&pf)[NPF], const unsigned 
 
 template <int DK, int C, bool F32M, int NW, int SPW>
 __global__ void __launch_bounds__(128 * NW) chunk_state_kernel(StateParams p) {
+    lds_poison((uint32_t)StateSmem<DK, C, F32M, NW, SPW>::BYTES);
     using L = Lay<DK, C, F32M>;
     using SM = StateSmem<DK, C, F32M, NW, SPW>;
     using TM = typename L::TM;
@@ -1512,6 +1515,7 @@ struct PairSmem {
 
 template <int DK, int C, int NP>
 __global__ void __launch_bounds__(192 * NP) chunk_state_pair_kernel(StateParams p) {
+    lds_poison((uint32_t)PairSmem<DK, C, NP>::BYTES);
     using L = Lay<DK, C, false>;
     using SM = PairSmem<DK, C, NP>;
     using F = f16x8;
@@ -1996,6 +2000,7 @@ __device__ __forceinline__ void quad_walk(const StateParams& p, int item) {
 
 template <int NS>
 __global__ void __launch_bounds__(384 * NS) chunk_state_quad_kernel(StateParams p) {
+    lds_poison((uint32_t)QuadSmem<NS>::BYTES);
     quad_walk<NS>(p, walker_item(blockIdx.x, gridDim.x, p.NSG));
 }
 
@@ -2290,6 +2295,7 @@ __device__ __forceinline__ void slice_walk(const StateParams& p, int item) {
 }
 
 __global__ void __launch_bounds__(256) chunk_state_slice_kernel(StateParams p) {
+    lds_poison((uint32_t)SliceLds::BYTES);
     slice_walk(p, walker_item(blockIdx.x, gridDim.x, p.NSG));
 }
 
@@ -2336,6 +2342,7 @@ size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, boo
 }
 
 __global__ void __launch_bounds__(64) status_clear_kernel(unsigned* status) {
+    lds_poison(0);
     if (threadIdx.x == 0) *status = 0u;
 }
 

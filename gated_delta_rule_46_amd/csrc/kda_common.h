@@ -164,4 +164,22 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
     return x * per + (x < rem ? x : rem) + j;
 }
 
+// ---------------------------------------------------------------- LDS poisoning (debug build)
+// Built with -DKDA_LDS_POISON, every kernel first fills its workgroup's whole
+// LDS allocation (static, then dyn_bytes of dynamic) with 0xFFFFFFFF -- a NaN
+// as fp32 and as each fp16 or bf16 half -- so that a read of LDS the kernel
+// has not written first turns into NaN in its results. Every thread calls it
+// before anything else; in the normal build it does nothing.
+__device__ __forceinline__ void lds_poison(uint32_t dyn_bytes) {
+#ifdef KDA_LDS_POISON
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    const uint32_t total = __builtin_amdgcn_groupstaticsize() + dyn_bytes;
+    const uint32_t nt = blockDim.x * blockDim.y * blockDim.z;
+    for (uint32_t off = 4 * threadIdx.x; off < total; off += 4 * nt) *(lds_u32*)off = 0xFFFFFFFFu;
+    __syncthreads();
+#else
+    (void)dyn_bytes;
+#endif
+}
+
 }  // namespace kda

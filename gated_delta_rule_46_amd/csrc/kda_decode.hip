@@ -26,6 +26,7 @@ __global__ void __launch_bounds__(512)
 decode_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                    const TIn* __restrict__ gate, const TIn* __restrict__ beta, const TIn* __restrict__ erase,
                    const TIn* __restrict__ write, float* __restrict__ S, float* __restrict__ o, int NH) {
+    lds_poison(0);
     constexpr int CG = DV / 4;                                   // float4 columns per row
     constexpr int NT = (DK * DV / 4) < 512 ? (DK * DV / 4) : 512;
     constexpr int RG = NT / CG;                                  // row groups

@@ -90,6 +90,7 @@ __device__ __forceinline__ bool gauge_lane(const GaugeParams& p, int nsh, int& s
 
 template <class TIn>
 __global__ void __launch_bounds__(G_NT) gauge_parity_kernel(GaugeParams p, int nsh) {
+    lds_poison(0);
     using U = typename Bits<TIn>::U;
     int sh, c0;
     if (!gauge_lane(p, nsh, sh, c0)) return;
@@ -127,6 +128,7 @@ __global__ void __launch_bounds__(G_NT) gauge_parity_kernel(GaugeParams p, int n
 // Exclusive prefix over the segments of each (sequence, head, channel), in
 // place; c_T from the total.
 __global__ void __launch_bounds__(256) gauge_scan_kernel(GaugeParams p, int rows) {
+    lds_poison(0);
     const int r = blockIdx.x * 256 + threadIdx.x;   // (sequence, head) * gdim + channel
     if (r >= rows) return;
     const int sh = r / p.gdim, ch = r % p.gdim;
@@ -147,6 +149,7 @@ __global__ void __launch_bounds__(256) gauge_scan_kernel(GaugeParams p, int rows
 
 template <class TIn>
 __global__ void __launch_bounds__(G_NT) gauge_apply_kernel(GaugeParams p, int nsh) {
+    lds_poison(0);
     using U = typename Bits<TIn>::U;
     int sh, c0;
     if (!gauge_lane(p, nsh, sh, c0)) return;
@@ -210,6 +213,7 @@ __global__ void __launch_bounds__(G_NT) gauge_apply_kernel(GaugeParams p, int ns
 // one per (sequence, head) for the scalar gate).
 __global__ void __launch_bounds__(256) gauge_state_flip_kernel(float* __restrict__ S, const int8_t* __restrict__ sign,
                                                                long rows, int dk, int dv, int gdim) {
+    lds_poison(0);
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     if (e >= rows * dv) return;
     const long r = e / dv;   // (sequence, head) * dk + channel

@@ -7,6 +7,7 @@ module fails loudly when the library has not been built.
 from __future__ import annotations
 
 import ctypes
+import contextlib
 import os
 from typing import Optional, Tuple
 
@@ -43,54 +44,72 @@ class KDAError(RuntimeError):
 _L = None
 
 
+def load(path: str):
+    """A ctypes handle on the build of the library at `path`, with the
+    argument and result types of every export set."""
+    if not os.path.exists(path):
+        raise ImportError("%s is not built; run python -m gated_delta_rule_46_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_chunk_fwd_stage.restype = i
+    lib.kda_chunk_fwd_stage.argtypes = [i] + [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 9
+    lib.kda_chunk_bwd.restype = i
+    lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_chunk_bwd_cw.restype = i
+    lib.kda_chunk_bwd_cw.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_chunk_bwd_cw_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_cw_workspace_bytes.argtypes = [i] * 7
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 7
+    lib.kda_gauge_fold.restype = i
+    lib.kda_gauge_fold.argtypes = [vp] * 7 + [i] * 4 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_gauge_fold_workspace_bytes.restype = sz
+    lib.kda_gauge_fold_workspace_bytes.argtypes = [i] * 7
+    lib.kda_chunk_fwd_gauge.restype = i
+    lib.kda_chunk_fwd_gauge.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_chunk_fwd_gauge_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd_gauge_workspace_bytes.argtypes = [i] * 10
+    lib.kda_decode_step.restype = i
+    lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
+    lib.kda_strerror.restype = ctypes.c_char_p
+    lib.kda_strerror.argtypes = [i]
+    lib.kda_last_hip_error.restype = i
+    lib.kda_last_hip_error.argtypes = []
+    lib.kda_version.restype = i
+    lib.kda_version.argtypes = []
+    lib.kda_chunk_fwd_status.restype = i
+    lib.kda_chunk_fwd_status.argtypes = [ctypes.c_uint32]
+    lib.kda_chunk_fwd_ew.restype = i
+    lib.kda_chunk_fwd_ew.argtypes = [vp] * 9 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_decode_step_ew.restype = i
+    lib.kda_decode_step_ew.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    lib.kda_chunk_fwd_noalloc.restype = i
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp]
+    return lib
+
+
 def _lib():
     global _L
     if _L is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError("libkda.so is not built (%s); run python -m gated_delta_rule_46_amd.build"
-                              % LIB_PATH)
-        lib = ctypes.CDLL(LIB_PATH)
-        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-        lib.kda_chunk_fwd.restype = i
-        lib.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
-        lib.kda_chunk_fwd_stage.restype = i
-        lib.kda_chunk_fwd_stage.argtypes = [i] + [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
-        lib.kda_chunk_fwd_workspace_bytes.restype = sz
-        lib.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 9
-        lib.kda_chunk_bwd.restype = i
-        lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
-        lib.kda_chunk_bwd_cw.restype = i
-        lib.kda_chunk_bwd_cw.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
-        lib.kda_chunk_bwd_cw_workspace_bytes.restype = sz
-        lib.kda_chunk_bwd_cw_workspace_bytes.argtypes = [i] * 7
-        lib.kda_chunk_bwd_workspace_bytes.restype = sz
-        lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 7
-        lib.kda_gauge_fold.restype = i
-        lib.kda_gauge_fold.argtypes = [vp] * 7 + [i] * 4 + [vp, i, i, i, vp, sz, vp]
-        lib.kda_gauge_fold_workspace_bytes.restype = sz
-        lib.kda_gauge_fold_workspace_bytes.argtypes = [i] * 7
-        lib.kda_chunk_fwd_gauge.restype = i
-        lib.kda_chunk_fwd_gauge.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
-        lib.kda_chunk_fwd_gauge_workspace_bytes.restype = sz
-        lib.kda_chunk_fwd_gauge_workspace_bytes.argtypes = [i] * 10
-        lib.kda_decode_step.restype = i
-        lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
-        lib.kda_strerror.restype = ctypes.c_char_p
-        lib.kda_strerror.argtypes = [i]
-        lib.kda_last_hip_error.restype = i
-        lib.kda_last_hip_error.argtypes = []
-        lib.kda_version.restype = i
-        lib.kda_version.argtypes = []
-        lib.kda_chunk_fwd_status.restype = i
-        lib.kda_chunk_fwd_status.argtypes = [ctypes.c_uint32]
-        lib.kda_chunk_fwd_ew.restype = i
-        lib.kda_chunk_fwd_ew.argtypes = [vp] * 9 + [i] * 6 + [vp, i, i, i, vp, sz, vp]
-        lib.kda_decode_step_ew.restype = i
-        lib.kda_decode_step_ew.argtypes = [vp] * 8 + [i] * 6 + [vp]
-        lib.kda_chunk_fwd_noalloc.restype = i
-        lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 6 + [vp, i, i, i, vp]
-        _L = lib
+        _L = load(LIB_PATH)
     return _L
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route this module's calls through another build of the library (for
+    instance the LDS-poisoning debug build) inside a with-block."""
+    global _L
+    prev = _lib()
+    _L = load(path)
+    try:
+        yield _L
+    finally:
+        _L = prev
 
 
 def library():
