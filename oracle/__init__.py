@@ -13,4 +13,4 @@ the HIP kernels.
 * ``gauge`` -- the gauge transform of Complex KDA onto positive gates
   (cumulative gate signs folded into q and k), in numpy.
 """
-from .recurrence import build, bwd, fwd, decode_step, decode_step_ew, fwd_ew, fwd_heads, threads  # noqa: F401
+from .recurrence import build, bwd, bwd_ew, fwd, decode_step, decode_step_ew, fwd_ew, fwd_heads, threads  # noqa: F401

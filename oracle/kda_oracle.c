@@ -447,3 +447,169 @@ int kda_oracle_bwd(const double *q, const double *k, const double *v, const doub
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Reverse-mode gradient of kda_oracle_fwd_ew (decoupled erase and write
+ * gates; reading stated above that function). With ke = e o k and
+ * u = w o v - S'^T ke, the adjoint of each forward line, last token first:
+ *
+ *   forward                          adjoint (dS holds dL/dS_t on entry)
+ *   o    = S_t^T q                   dS += q dO^T;   dq = S_t dO
+ *   S_t  = S' + k u^T                du = dS^T k;    dk = dS u;   dS' = dS
+ *   u    = w o v - pred              dw = du o v;    dv = du o w;  dpred = -du
+ *   pred = S'^T ke                   dS' += ke dpred^T;  dke = S' dpred;
+ *                                    de = dke o k;   dk += dke o e
+ *   S'   = Diag(alpha) S_{t-1}       dalpha_i = sum_j dS'_ij S_{t-1,ij};
+ *                                    dS_{t-1} = Diag(alpha) dS'
+ *
+ * Returns dL/dq, dk, dv, dgate, derase [B,T,H,dk], dwrite [B,T,H,dv] and dS0
+ * for L = sum_t <o_t, dO_t> + <S_T, dS_T>; layouts and NULL conventions as
+ * for kda_oracle_bwd. Returns 0, or -1 on a bad argument or failed
+ * allocation.
+ */
+int kda_oracle_bwd_ew(const double *q, const double *k, const double *v, const double *gate,
+                      const double *erase, const double *write, const double *S0, const double *dO,
+                      const double *dS_T, double *dq, double *dk_out, double *dv_out, double *dgate,
+                      double *derase, double *dwrite, double *dS0, int B, int H, int T, int dk, int dv,
+                      const int32_t *cu_seqlens, int nseq, int gate_kind)
+{
+    if (!q || !k || !v || !gate || !erase || !write || !dO || !dq || !dk_out || !dv_out || !dgate ||
+        !derase || !dwrite || B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (gate_kind != GATE_CHANNEL && gate_kind != GATE_SCALAR)
+        return -1;
+    if (cu_seqlens) {
+        if (B != 1 || nseq <= 0 || cu_seqlens[0] != 0 || cu_seqlens[nseq] != T)
+            return -1;
+    } else {
+        nseq = B;
+    }
+    const int gdim = gate_kind == GATE_CHANNEL ? dk : 1;
+    const size_t sd = (size_t)dk * dv;
+    long pairs = (long)nseq * H;
+    long p;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (p = 0; p < pairs; ++p) {
+        int s = (int)(p / H), h = (int)(p % H);
+        long t0, t1, b, t;
+        int i, j;
+        if (cu_seqlens) {
+            b = 0;
+            t0 = cu_seqlens[s];
+            t1 = cu_seqlens[s + 1];
+        } else {
+            b = s;
+            t0 = 0;
+            t1 = T;
+        }
+        const long len = t1 - t0;
+        double *hist = (double *)malloc(sizeof(double) * sd * (size_t)(len > 0 ? len : 1));
+        double *S = (double *)malloc(sizeof(double) * sd);
+        double *Sp = (double *)malloc(sizeof(double) * sd);
+        double *dS = (double *)malloc(sizeof(double) * sd);
+        double *pred = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *du = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!hist || !S || !Sp || !dS || !pred || !u || !du) {
+            failed = 1;
+        } else {
+            /* forward, keeping S_{t-1} before every token */
+            if (S0)
+                memcpy(S, S0 + ((size_t)s * H + h) * sd, sizeof(double) * sd);
+            else
+                memset(S, 0, sizeof(double) * sd);
+            for (t = t0; t < t1; ++t) {
+                size_t row = ((size_t)b * T + t) * H + h;
+                memcpy(hist + (size_t)(t - t0) * sd, S, sizeof(double) * sd);
+                erase_write_step(S, q + row * dk, k + row * dk, v + row * dv, gate + row * gdim,
+                                 gdim == dk ? 1 : 0, erase + row * dk, write + row * dv, NULL, pred, dk, dv);
+            }
+            /* backward */
+            if (dS_T)
+                memcpy(dS, dS_T + ((size_t)s * H + h) * sd, sizeof(double) * sd);
+            else
+                memset(dS, 0, sizeof(double) * sd);
+            for (t = t1 - 1; t >= t0; --t) {
+                size_t row = ((size_t)b * T + t) * H + h;
+                const double *qt = q + row * dk, *kt = k + row * dk, *vt = v + row * dv;
+                const double *et = erase + row * dk, *wt = write + row * dv;
+                const double *ot = dO + row * dv, *at = gate + row * gdim;
+                const double *Sprev = hist + (size_t)(t - t0) * sd;
+                double *dqt = dq + row * dk, *dkt = dk_out + row * dk, *dvt = dv_out + row * dv;
+                double *dat = dgate + row * gdim, *det = derase + row * dk, *dwt = dwrite + row * dv;
+                /* recompute S', pred, u, S_t */
+                for (i = 0; i < dk; ++i) {
+                    double a = at[gdim == dk ? i : 0];
+                    for (j = 0; j < dv; ++j)
+                        Sp[i * dv + j] = a * Sprev[i * dv + j];
+                }
+                for (j = 0; j < dv; ++j) {
+                    double acc = 0.0;
+                    for (i = 0; i < dk; ++i)
+                        acc += Sp[i * dv + j] * (et[i] * kt[i]);
+                    pred[j] = acc;
+                    u[j] = wt[j] * vt[j] - acc;
+                }
+                for (i = 0; i < dk; ++i)
+                    for (j = 0; j < dv; ++j)
+                        S[i * dv + j] = Sp[i * dv + j] + kt[i] * u[j];
+                /* o_t = S_t^T q_t */
+                for (i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (j = 0; j < dv; ++j) {
+                        dS[i * dv + j] += qt[i] * ot[j];
+                        acc += S[i * dv + j] * ot[j];
+                    }
+                    dqt[i] = acc;
+                }
+                /* S_t = S' + k u^T;  u = w o v - pred */
+                for (j = 0; j < dv; ++j) {
+                    double acc = 0.0;
+                    for (i = 0; i < dk; ++i)
+                        acc += dS[i * dv + j] * kt[i];
+                    du[j] = acc;
+                    dwt[j] = acc * vt[j];
+                    dvt[j] = acc * wt[j];
+                }
+                for (i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (j = 0; j < dv; ++j)
+                        acc += dS[i * dv + j] * u[j];
+                    dkt[i] = acc;
+                }
+                /* pred = S'^T ke with dpred = -du; then S' = Diag(alpha) S_{t-1} */
+                if (gdim == 1)
+                    dat[0] = 0.0;
+                for (i = 0; i < dk; ++i) {
+                    double a = at[gdim == dk ? i : 0];
+                    double ke = et[i] * kt[i];
+                    double dke = 0.0, acca = 0.0;
+                    for (j = 0; j < dv; ++j) {
+                        double dpred = -du[j];
+                        double dsp = dS[i * dv + j] + ke * dpred;
+                        dke += Sp[i * dv + j] * dpred;
+                        acca += dsp * Sprev[i * dv + j];
+                        dS[i * dv + j] = a * dsp;
+                    }
+                    det[i] = dke * kt[i];
+                    dkt[i] += dke * et[i];
+                    if (gdim == dk)
+                        dat[i] = acca;
+                    else
+                        dat[0] += acca;
+                }
+            }
+            if (dS0)
+                memcpy(dS0 + ((size_t)s * H + h) * sd, dS, sizeof(double) * sd);
+        }
+        free(hist);
+        free(S);
+        free(Sp);
+        free(dS);
+        free(pred);
+        free(u);
+        free(du);
+    }
+    return failed ? -1 : 0;
+}

@@ -51,6 +51,8 @@ def _load():
         lib.kda_oracle_decode_ew.argtypes = [_dp] * 8 + [ctypes.c_int] * 5
         lib.kda_oracle_bwd.restype = ctypes.c_int
         lib.kda_oracle_bwd.argtypes = [_dp] * 14 + [ctypes.c_int] * 5 + [_ip] + [ctypes.c_int] * 2
+        lib.kda_oracle_bwd_ew.restype = ctypes.c_int
+        lib.kda_oracle_bwd_ew.argtypes = [_dp] * 16 + [ctypes.c_int] * 5 + [_ip] + [ctypes.c_int] * 2
         _lib = lib
     return _lib
 
@@ -203,3 +205,34 @@ def decode_step_ew(q, k, v, gate, erase, write, S: np.ndarray, gate_kind: int = 
     if rc != 0:
         raise ValueError("kda_oracle_decode_ew rejected its arguments")
     return o
+
+
+def bwd_ew(q, k, v, gate, erase, write, dO, S0=None, dS_T=None, cu_seqlens=None, gate_kind: int = 0):
+    """Gradient of L = sum(o * dO) + sum(S_T * dS_T) for ``fwd_ew`` (reverse-mode
+    adjoint of the erase/write token recurrence, fp64). Returns a dict of fp64
+    numpy arrays dq, dk, dv, dgate, derase, dwrite (input layouts) and dS0
+    [nseq,H,dk,dv]."""
+    lib = _load()
+    q, k, v, gate, erase, write, dO = (_f64(t) for t in (q, k, v, gate, erase, write, dO))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if erase.shape != k.shape or write.shape != v.shape:
+        raise ValueError("erase must be shaped like k and write like v")
+    cu = None
+    nseq = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if isinstance(cu_seqlens, torch.Tensor)
+                                             else cu_seqlens), dtype=np.int32)
+        nseq = cu.size - 1
+    s0 = None if S0 is None else _f64(S0)
+    dst = None if dS_T is None else _f64(dS_T)
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v), "dgate": np.zeros_like(gate),
+           "derase": np.zeros_like(erase), "dwrite": np.zeros_like(write), "dS0": np.zeros((nseq, H, dk, dv))}
+    rc = lib.kda_oracle_bwd_ew(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(erase), _ptr(write),
+                               None if s0 is None else _ptr(s0), _ptr(dO), None if dst is None else _ptr(dst),
+                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
+                               _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out["dS0"]), B, H, T, dk, dv,
+                               None if cu is None else cu.ctypes.data_as(_ip), nseq, int(gate_kind))
+    if rc != 0:
+        raise ValueError("kda_oracle_bwd_ew rejected its arguments")
+    return out

@@ -137,3 +137,70 @@ def test_one_token_state_gradient_closed_form():
     np.testing.assert_allclose(g["dS0"][0, 0], right, atol=1e-12)
     planted = a0[:, None] * D
     assert np.abs(planted - right).max() > 1e-3
+
+
+# ------------------------------------------------------------------ erase/write gates (oracle.bwd_ew)
+
+def _ew_inputs(rng, B, T, H, dk, dv, gate_kind, lengths=None):
+    x, dO, dST, cu = _inputs(rng, B, T, H, dk, dv, gate_kind, lengths)
+    B, T = x["q"].shape[:2]
+    x = {n: x[n] for n in ("q", "k", "v", "gate", "S0")}
+    x["erase"] = rng.uniform(-0.5, 2.0, (B, T, H, dk))    # negative, zero-crossing and above-one erase entries
+    x["write"] = rng.uniform(-0.5, 2.0, (B, T, H, dv))
+    x["erase"].reshape(-1)[rng.integers(0, x["erase"].size)] = 0.0
+    return x, dO, dST, cu
+
+
+def _ew_loss(x, dO, dST, cu, gate_kind):
+    o, ST = oracle.fwd_ew(*(torch.from_numpy(x[n]) for n in ("q", "k", "v", "gate", "erase", "write")),
+                          torch.from_numpy(x["S0"]), cu, gate_kind)
+    return float((o * dO).sum() + (ST * dST).sum())
+
+
+@pytest.mark.parametrize("case", CASES, ids=["channel", "scalar", "varlen"])
+def test_erase_write_gradient_equals_finite_differences(case):
+    """Every component of oracle.bwd_ew against central differences of the
+    (separately pinned) oracle.fwd_ew. L is affine in each single q, v, gate,
+    erase, write and S0 entry and quadratic in each k entry (k reads through
+    e o k and writes along k), so central differences are exact up to
+    rounding."""
+    case = dict(case)
+    gk = case["gate_kind"]
+    rng = np.random.default_rng(21 + gk)
+    x, dO, dST, cu = _ew_inputs(rng, case["B"], case["T"], case["H"], case["dk"], case["dv"], gk,
+                                case.get("lengths"))
+    g = oracle.bwd_ew(*(torch.from_numpy(x[n]) for n in ("q", "k", "v", "gate", "erase", "write")),
+                      torch.from_numpy(dO), torch.from_numpy(x["S0"]), torch.from_numpy(dST), cu, gk)
+    h = 1e-5
+    names = {"q": "dq", "k": "dk", "v": "dv", "gate": "dgate", "erase": "derase", "write": "dwrite", "S0": "dS0"}
+    for name, gname in names.items():
+        num = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            keep = x[name][idx]
+            x[name][idx] = keep + h
+            lp = _ew_loss(x, dO, dST, cu, gk)
+            x[name][idx] = keep - h
+            lm = _ew_loss(x, dO, dST, cu, gk)
+            x[name][idx] = keep
+            num[idx] = (lp - lm) / (2 * h)
+        scale = max(1.0, float(np.abs(num).max()))
+        np.testing.assert_allclose(g[gname], num, rtol=0, atol=1e-8 * scale, err_msg=name)
+
+
+def test_erase_write_gradient_reduces_to_beta_form():
+    """With e = beta 1 (every key channel) and w = beta 1 (every value channel)
+    the erase/write recurrence is the beta recurrence, so dq, dk, dv, dgate
+    and dS0 equal oracle.bwd's, and by the chain rule dbeta = sum over
+    channels of derase plus sum over channels of dwrite."""
+    rng = np.random.default_rng(13)
+    x, dO, dST, _ = _inputs(rng, 2, 9, 2, 5, 4, 0)
+    t = {n: torch.from_numpy(x[n]) for n in x}
+    b = t["beta"]
+    e = b[..., None].expand(*b.shape, 5).contiguous()
+    w = b[..., None].expand(*b.shape, 4).contiguous()
+    gb = oracle.bwd(t["q"], t["k"], t["v"], t["gate"], b, torch.from_numpy(dO), t["S0"], torch.from_numpy(dST))
+    ge = oracle.bwd_ew(t["q"], t["k"], t["v"], t["gate"], e, w, torch.from_numpy(dO), t["S0"],
+                       torch.from_numpy(dST))
+    for n in ("dq", "dk", "dv", "dgate", "dS0"):
+        np.testing.assert_allclose(ge[n], gb[n], atol=1e-11, err_msg=n)
+    np.testing.assert_allclose(ge["derase"].sum(-1) + ge["dwrite"].sum(-1), gb["dbeta"], atol=1e-11)
