@@ -15,6 +15,12 @@
 // The pages measure forward-plus-backward throughput of this family (Complex
 // KDA summary, efficiency) without printing the backward; the lines above
 // are the chain rule applied to the forward, nothing more.
+// With decoupled erase and write gates (EW: erase e per key channel, write w
+// per value channel; S_t = S' + k (w o v - S'^T (e o k))^T) the same adjoint
+// reads with ke = e o k and drops beta:
+//   du = dS^T k       dk = dS u + e o dke,   dke = S' dpred,  dpred = -du
+//   dv = w o du       dw = du o v            de = k o dke
+//   dS' = dS + ke dpred^T                    (dalpha, dS as above)
 //
 // Value columns of S never mix (the transition acts on the key side only),
 // so each wave owns COLS value columns and all dk rows of S and dS: lane l
@@ -79,8 +85,10 @@ __device__ __forceinline__ void wave_sum4(const float (&x)[4], float (&out)[4], 
 
 struct BwdParams {
     const void *q, *k, *v, *gate, *beta;
+    const void *erase, *write;   // erase/write form only
     const float *S0, *dO, *dST;
     float *dv_out, *dS0, *ckpt, *part;
+    float* dw_out;               // erase/write form: dL/dwrite
     float* resid;   // e = v - S'^T k of every token from pass A, [B*T*H][dv]
     const int32_t* cu;
     int H, T, dv, ncg;
@@ -88,23 +96,32 @@ struct BwdParams {
     long rows;   // B * T * H
 };
 
-template <int DK, int NC, bool SG>
+template <int DK, int NC, bool SG, bool EW>
 struct BwdStage {
     float k[BW_SUB][DK], q[BW_SUB][DK], a[BW_SUB][SG ? 1 : DK];
     float v[BW_SUB][NC], dO[BW_SUB][NC], e[BW_SUB][NC], b[BW_SUB];
+    float er[BW_SUB][EW ? DK : 1], wr[BW_SUB][EW ? NC : 1];   // erase and write gates
 };
+
+// Partial sums per row kept per wave: dq, dk, dalpha (and de with erase/write gates).
+template <bool EW> constexpr int bwd_nq() { return EW ? 4 : 3; }
 
 // Dynamic LDS of one workgroup: the double-buffered input stage and, also
 // double-buffered by block parity, each wave's per-token partial sums over its
 // own value columns (dq, dk, dalpha per row; dbeta), written with plain
 // stores and added up across the waves when the block is flushed. (LDS
 // atomics from four waves onto the same rows took 40% of the kernel time.)
-template <int DK, int NC, int NWV, bool SG>
+template <int DK, int NC, int NWV, bool SG, bool EW>
 struct BwdLds {
-    BwdStage<DK, NC, SG> st[2];
-    float slot[2][NWV][BW_SUB][3][DK];
+    // partial-sum slots double-buffered by block parity, except for the
+    // erase/write form at dk = 128, whose four slots fit LDS only once (its
+    // block flush then ends with a barrier of its own)
+    static constexpr int NSB = (EW && DK >= 128) ? 1 : 2;
+    BwdStage<DK, NC, SG, EW> st[2];
+    float slot[NSB][NWV][BW_SUB][bwd_nq<EW>()][DK];
     float slotb[2][NWV][BW_SUB];
     float vout[2][BW_SUB][NC];   // per-token wave-uniform results: e (pass A), dv (pass B)
+    float vout2[2][BW_SUB][EW ? NC : 1];   // dw (pass B, erase/write form)
     // target of the lanes that do not store a wave-uniform value: lane l
     // writes 4 floats at 4 l + j NC for token j (the stride of vout), so one
     // base address per block serves every token
@@ -134,11 +151,13 @@ template <class TIn> __device__ __forceinline__ TIn in_one();
 template <> __device__ __forceinline__ uint16_t in_one<uint16_t>() { return 0x3F80; }   // bf16 1.0
 template <> __device__ __forceinline__ float in_one<float>() { return 1.f; }
 
-template <class TIn, int DK, int NC, int NT, int RPL, int COLS, bool SG, bool BWD>
+template <class TIn, int DK, int NC, int NT, int RPL, int COLS, bool SG, bool BWD, bool EW>
 struct BwdFetch {
     static constexpr int KPT = (BW_SUB * DK + NT - 1) / NT;
     static constexpr int VPT = (BW_SUB * NC + NT - 1) / NT;
-    TIn k[KPT], q[BWD ? KPT : 1], a[SG ? 1 : KPT], v[BWD ? 1 : VPT], b, ag;
+    static constexpr bool LV = !BWD || EW;   // v is staged (pass A; pass B of the erase/write form)
+    TIn k[KPT], q[BWD ? KPT : 1], a[SG ? 1 : KPT], v[LV ? VPT : 1], b, ag;
+    TIn er[EW ? KPT : 1], wr[EW ? VPT : 1];
     float dO[BWD ? VPT : 1], pr[BWD ? VPT : 1];
     f32x4 ck[BWD ? RPL * COLS / 4 : 1];   // this lane's part of the block's checkpoint
 
@@ -149,6 +168,8 @@ struct BwdFetch {
         const TIn* A = (const TIn*)p.gate;
         const TIn* V = (const TIn*)p.v;
         const TIn* Bt = (const TIn*)p.beta;
+        const TIn* E = (const TIn*)p.erase;
+        const TIn* W = (const TIn*)p.write;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int e = tid + NT * i, j = e / DK, r = e % DK, t = ts + j;
@@ -157,13 +178,15 @@ struct BwdFetch {
             k[i] = ok ? K[row * DK + r] : TIn(0);
             if (BWD) q[i] = ok ? Q[row * DK + r] : TIn(0);
             if (!SG) a[i] = ok ? A[row * DK + r] : in_one<TIn>();
+            if (EW) er[i] = ok ? E[row * DK + r] : TIn(0);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int e = tid + NT * i, j = e / NC, c = e % NC, t = ts + j;
             const bool ok = e < BW_SUB * NC && t < te;
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-            if (!BWD) v[i] = ok ? V[row * p.dv + cw0 + c] : TIn(0);
+            if (LV) v[i] = ok ? V[row * p.dv + cw0 + c] : TIn(0);
+            if (EW) wr[i] = ok ? W[row * p.dv + cw0 + c] : TIn(0);
             if (BWD) dO[i] = ok ? p.dO[row * p.dv + cw0 + c] : 0.f;
             if (BWD) pr[i] = ok ? p.resid[row * p.dv + cw0 + c] : 0.f;
         }
@@ -171,7 +194,7 @@ struct BwdFetch {
             const int t = ts + tid;
             const bool ok = tid < BW_SUB && t < te;
             const size_t row = ((size_t)b0 * p.T + t) * p.H + h;
-            b = ok ? Bt[row] : TIn(0);
+            b = ok && !EW ? Bt[row] : TIn(0);
             ag = SG ? (ok ? A[row] : in_one<TIn>()) : TIn(0);
         }
         if (BWD) {
@@ -181,7 +204,7 @@ struct BwdFetch {
         }
     }
 
-    __device__ __forceinline__ void store(BwdStage<DK, NC, SG>& s, int tid) const {
+    __device__ __forceinline__ void store(BwdStage<DK, NC, SG, EW>& s, int tid) const {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int e = tid + NT * i;
@@ -189,13 +212,15 @@ struct BwdFetch {
                 (&s.k[0][0])[e] = in_f32(k[i]);
                 if (BWD) (&s.q[0][0])[e] = in_f32(q[i]);
                 if (!SG) (&s.a[0][0])[e] = in_f32(a[i]);
+                if (EW) (&s.er[0][0])[e] = in_f32(er[i]);
             }
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int e = tid + NT * i;
             if (e < BW_SUB * NC) {
-                if (!BWD) (&s.v[0][0])[e] = in_f32(v[i]);
+                if (LV) (&s.v[0][0])[e] = in_f32(v[i]);
+                if (EW) (&s.wr[0][0])[e] = in_f32(wr[i]);
                 if (BWD) (&s.dO[0][0])[e] = dO[i];
                 if (BWD) (&s.e[0][0])[e] = pr[i];
             }
@@ -207,16 +232,16 @@ struct BwdFetch {
     }
 };
 
-template <class TIn, int DK, int NWV, int COLS, bool SG>
+template <class TIn, int DK, int NWV, int COLS, bool SG, bool EW>
 __global__ void __launch_bounds__(NWV * WAVE)
 chunk_bwd_kernel(BwdParams p) {
-    lds_poison((uint32_t)sizeof(BwdLds<DK, NWV * COLS, NWV, SG>));
-    constexpr int NT = NWV * WAVE, NC = NWV * COLS, SUB = BW_SUB;
+    lds_poison((uint32_t)sizeof(BwdLds<DK, NWV * COLS, NWV, SG, EW>));
+    constexpr int NT = NWV * WAVE, NC = NWV * COLS, SUB = BW_SUB, NQ = bwd_nq<EW>();
     constexpr int RPL = DK >= WAVE ? DK / WAVE : 1;        // state rows per lane
     constexpr int CKF = NT * RPL * COLS;                    // floats per checkpoint slot
     static_assert(COLS % 4 == 0, "float4 column groups");
     extern __shared__ __align__(16) unsigned char smem[];
-    BwdLds<DK, NC, NWV, SG>& L = *reinterpret_cast<BwdLds<DK, NC, NWV, SG>*>(smem);
+    BwdLds<DK, NC, NWV, SG, EW>& L = *reinterpret_cast<BwdLds<DK, NC, NWV, SG, EW>*>(smem);
 
     const int tid = threadIdx.x, lane = tid % WAVE;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
@@ -261,23 +286,23 @@ chunk_bwd_kernel(BwdParams p) {
     }
 
     // Wave-uniform per-token results of block fb, from LDS to memory (pass A: e)
-    auto flush_vout = [&](int fb, float* dst) {
+    auto flush_vout = [&](int fb, float* dst, const float (*src)[NC]) {
         const int ts = t0 + fb * SUB;
         const __amdgpu_buffer_rsrc_t r = block_rsrc(dst, (size_t)b0 * p.T + ts, p.H, p.dv);
         for (int e = tid; e < SUB * NC; e += NT) {
             const int j = e / NC, c = e % NC;
             const int off = ts + j < t1 ? ((j * p.H + h) * p.dv + cw0 + c) * 4 : BW_OOB;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L.vout[fb & 1][j][c]), r, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(src[j][c]), r, off, 0, 0);
         }
     };
-    auto flush_resid = [&](int fb) { flush_vout(fb, p.resid); };
+    auto flush_resid = [&](int fb) { flush_vout(fb, p.resid, L.vout[fb & 1]); };
 
     // ------------------------------------------------ pass A: forward, checkpoints
     {
-        BwdFetch<TIn, DK, NC, NT, RPL, COLS, SG, false> f;
+        BwdFetch<TIn, DK, NC, NT, RPL, COLS, SG, false, EW> f;
         if (nb > 0) f.fetch(p, tid, b0, h, t0, t1, cw0, nullptr);
         for (int blk = 0; blk < nb; ++blk) {
-            BwdStage<DK, NC, SG>& st = L.st[blk & 1];
+            BwdStage<DK, NC, SG, EW>& st = L.st[blk & 1];
             f.store(st, tid);
             __syncthreads();
             const int ts = t0 + blk * SUB;
@@ -293,11 +318,12 @@ chunk_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int j = 0; j < SUB; ++j) {
                 {
-                    float kr[RPL], part[COLS];
+                    float kr[RPL], kx[RPL], part[COLS];   // write key k, read key (k, or e o k)
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
                         const int r = rv[m] ? lane + WAVE * m : 0;
                         kr[m] = rv[m] ? st.k[j][r] : 0.f;
+                        kx[m] = EW ? kr[m] * (rv[m] ? st.er[j][r] : 0.f) : kr[m];
                         const float a = SG ? st.a[j][0] : (rv[m] ? st.a[j][r] : 0.f);
 #pragma unroll
                         for (int c = 0; c < COLS; ++c) S[m][c] *= a;
@@ -308,16 +334,19 @@ chunk_bwd_kernel(BwdParams p) {
                         for (int c = 0; c < COLS; ++c) {
                             x[c] = 0.f;
 #pragma unroll
-                            for (int m = 0; m < RPL; ++m) x[c] = fmaf(S[m][c], kr[m], x[c]);
+                            for (int m = 0; m < RPL; ++m) x[c] = fmaf(S[m][c], kx[m], x[c]);
                         }
                         wave_sum4(x, part, lane);
                     }
                     static_assert(COLS == 4, "one 16-byte LDS store of e per wave and token");
                     float e[COLS];
 #pragma unroll
-                    for (int c = 0; c < COLS; ++c) e[c] = st.v[j][w * COLS + c] - part[c];
+                    for (int c = 0; c < COLS; ++c) {
+                        const float vv = st.v[j][w * COLS + c];
+                        e[c] = (EW ? st.wr[j][w * COLS + c] * vv : vv) - part[c];
+                    }
                     *reinterpret_cast<f32x4*>(vb + j * NC) = f32x4{e[0], e[1], e[2], e[3]};
-                    const float bt = st.b[j];
+                    const float bt = EW ? 1.f : st.b[j];
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
                         const float u = bt * e[c];
@@ -354,24 +383,25 @@ chunk_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int c = 0; c < COLS; ++c) Sn[m][c] = S[m][c];
     const size_t nrk = (size_t)p.rows * DK;
-    auto flush = [&](int fb) {   // block fb: dv, and the waves' partial sums added up, to memory
+    auto flush = [&](int fb) {   // block fb: dv (and dw), and the waves' partial sums added up, to memory
         const int ts = t0 + fb * SUB;
         const size_t tok0 = (size_t)b0 * p.T + ts;
-        flush_vout(fb, p.dv_out);
+        flush_vout(fb, p.dv_out, L.vout[fb & 1]);
+        if constexpr (EW) flush_vout(fb, p.dw_out, L.vout2[fb & 1]);
 #pragma unroll
-        for (int qty = 0; qty < 3; ++qty) {
-            const __amdgpu_buffer_rsrc_t r = block_rsrc(p.part + ((size_t)cg * 3 + qty) * nrk, tok0, p.H, DK);
+        for (int qty = 0; qty < NQ; ++qty) {
+            const __amdgpu_buffer_rsrc_t r = block_rsrc(p.part + ((size_t)cg * NQ + qty) * nrk, tok0, p.H, DK);
 #pragma unroll
             for (int i = 0; i < (SUB * DK + NT - 1) / NT; ++i) {
                 const int e = tid + NT * i, j = e / DK, ii = e % DK, jj = j < SUB ? j : SUB - 1;
                 float x = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < NWV; ++ww) x += L.slot[fb & 1][ww][jj][qty][ii];
+                for (int ww = 0; ww < NWV; ++ww) x += L.slot[fb % L.NSB][ww][jj][qty][ii];
                 const int off = e < SUB * DK && ts + j < t1 ? ((j * p.H + h) * DK + ii) * 4 : BW_OOB;
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
             }
         }
-        {
+        if constexpr (!EW) {
             const __amdgpu_buffer_rsrc_t r =
                 block_rsrc(p.part + (size_t)p.ncg * 3 * nrk + (size_t)cg * p.rows, tok0, p.H, 1);
             float x = 0.f;
@@ -382,10 +412,10 @@ chunk_bwd_kernel(BwdParams p) {
         }
     };
     {
-        BwdFetch<TIn, DK, NC, NT, RPL, COLS, SG, true> f;
+        BwdFetch<TIn, DK, NC, NT, RPL, COLS, SG, true, EW> f;
         if (nb > 0) f.fetch(p, tid, b0, h, t0 + (nb - 1) * SUB, t1, cw0, ck + (size_t)(nb - 1) * CKF);
         for (int blk = nb - 1; blk >= 0; --blk) {
-            BwdStage<DK, NC, SG>& st = L.st[blk & 1];
+            BwdStage<DK, NC, SG, EW>& st = L.st[blk & 1];
             f.store(st, tid);
             float Sb[RPL][COLS];
 #pragma unroll
@@ -394,6 +424,7 @@ chunk_bwd_kernel(BwdParams p) {
                 for (int c = 0; c < COLS; ++c) Sb[m][c] = f.ck[m * (COLS / 4) + c / 4][c % 4];
             __syncthreads();
             if (blk + 1 < nb) flush(blk + 1);
+            if constexpr (BwdLds<DK, NC, NWV, SG, EW>::NSB == 1) __syncthreads();   // slot read before rewritten
             const int ts = t0 + blk * SUB;
             if (blk > 0) f.fetch(p, tid, b0, h, ts - SUB, t1, cw0, ck + (size_t)(blk - 1) * CKF);
 
@@ -415,7 +446,7 @@ chunk_bwd_kernel(BwdParams p) {
 #pragma unroll
                         for (int c = 0; c < COLS; ++c) Sb[m][c] *= a;
                     }
-                    const float bt = st.b[j];
+                    const float bt = EW ? 1.f : st.b[j];
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
                         const float u = bt * st.e[j][w * COLS + c];
@@ -426,26 +457,28 @@ chunk_bwd_kernel(BwdParams p) {
                 }
             }
 
-            float(*slot)[3][DK] = L.slot[blk & 1][w];
+            float(*slot)[NQ][DK] = L.slot[blk % L.NSB][w];
             float* vb = lane == 0 ? &L.vout[blk & 1][0][w * COLS] : &L.junk[4 * lane];
+            float* wb = EW && lane == 0 ? &L.vout2[blk & 1][0][w * COLS] : &L.junk[4 * lane];
             float* bb = lane == 0 ? &L.slotb[blk & 1][w][0] : &L.junk[lane];
 #pragma unroll
             for (int j = SUB - 1; j >= 0; --j) {
                 {
-                    float kr[RPL], qr[RPL], ar[RPL], oo[COLS], ee[COLS];
+                    float kr[RPL], qr[RPL], ar[RPL], er[RPL], oo[COLS], ee[COLS];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) {
                         const int r = rv[m] ? lane + WAVE * m : 0;
                         kr[m] = rv[m] ? st.k[j][r] : 0.f;
                         qr[m] = rv[m] ? st.q[j][r] : 0.f;
                         ar[m] = SG ? st.a[j][0] : (rv[m] ? st.a[j][r] : 0.f);
+                        er[m] = EW && rv[m] ? st.er[j][r] : 0.f;
                     }
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
                         oo[c] = st.dO[j][w * COLS + c];
                         ee[c] = st.e[j][w * COLS + c];
                     }
-                    const float bt = st.b[j];
+                    const float bt = EW ? 1.f : st.b[j];
                     float du[COLS];
 #pragma unroll
                     for (int m = 0; m < RPL; ++m)
@@ -461,12 +494,15 @@ chunk_bwd_kernel(BwdParams p) {
                         }
                         wave_sum4(y, du, lane);
                     }
-                    // u = beta e; dv = beta du; dpred = -dv
-                    float u[COLS], dvv[COLS], dbt = 0.f;
+                    // u = beta e; dv = beta du; dpred = -dv. Erase/write form:
+                    // u = e; dv = w o du; dw = du o v; dpred = -du
+                    float u[COLS], dvv[COLS], dpr[COLS], dww[COLS], dbt = 0.f;
 #pragma unroll
                     for (int c = 0; c < COLS; ++c) {
                         u[c] = j + 1 < SUB ? uh[j + 1 < SUB ? j : 0][c] : bt * ee[c];
-                        dvv[c] = bt * du[c];
+                        dvv[c] = (EW ? st.wr[j][w * COLS + c] : bt) * du[c];
+                        dpr[c] = EW ? du[c] : dvv[c];   // -dpred
+                        dww[c] = EW ? du[c] * st.v[j][w * COLS + c] : 0.f;
                         dbt = fmaf(du[c], ee[c], dbt);
                     }
 #pragma unroll
@@ -474,28 +510,31 @@ chunk_bwd_kernel(BwdParams p) {
                         float St[COLS];   // S_t
 #pragma unroll
                         for (int c = 0; c < COLS; ++c) St[c] = j + 1 < SUB ? Sh[j + 1 < SUB ? j + 1 : 0][m][c] : Sn[m][c];
+                        const float kx = EW ? er[m] * kr[m] : kr[m];   // the read key
                         float gq = 0.f, gk = 0.f, gs = 0.f, ga = 0.f;
 #pragma unroll
                         for (int c = 0; c < COLS; ++c) {
                             gq = fmaf(St[c], oo[c], gq);
                             gk = fmaf(dS[m][c], u[c], gk);
-                            gs = fmaf(Sh[j][m][c], dvv[c], gs);
-                            const float dsp = fmaf(-kr[m], dvv[c], dS[m][c]);   // dS' = dS + k dpred^T
+                            gs = fmaf(Sh[j][m][c], dpr[c], gs);
+                            const float dsp = fmaf(-kx, dpr[c], dS[m][c]);   // dS' = dS + kx dpred^T
                             ga = fmaf(dsp, Sh[j][m][c], ga);
                             dS[m][c] = ar[m] * dsp;
                         }
-                        gk = fmaf(-ar[m], gs, gk);   // + S' dpred
+                        const float dke = -ar[m] * gs;   // S' dpred
                         if (rv[m]) {
                             const int r = lane + WAVE * m;
                             slot[j][0][r] = gq;
-                            slot[j][1][r] = gk;
+                            slot[j][1][r] = EW ? fmaf(er[m], dke, gk) : fmaf(-ar[m], gs, gk);
                             slot[j][2][r] = ga;
+                            if constexpr (EW) slot[j][EW ? 3 : 0][r] = kr[m] * dke;
                         }
                     }
                     // wave-uniform values, stored by lane 0 without a branch (the other
                     // lanes write a junk area): dbeta and dv, flushed with the block
                     bb[j] = dbt;
                     *reinterpret_cast<f32x4*>(vb + j * NC) = f32x4{dvv[0], dvv[1], dvv[2], dvv[3]};
+                    if constexpr (EW) *reinterpret_cast<f32x4*>(wb + j * NC) = f32x4{dww[0], dww[1], dww[2], dww[3]};
                 }
             }
 #pragma unroll
@@ -519,35 +558,39 @@ chunk_bwd_kernel(BwdParams p) {
     }
 }
 
-// Sums the per-workgroup partials: dq, dk, dalpha per (token, head, channel)
-// and dbeta per (token, head); the scalar gate's gradient also sums over
-// the channels.
+// Sums the per-workgroup partials: dq, dk, dalpha (and, with nq = 4, de)
+// per (token, head, channel) and dbeta per (token, head) (db null: none, the
+// erase/write form); the scalar gate's gradient also sums over the channels.
 __global__ void __launch_bounds__(256)
-chunk_bwd_reduce_kernel(const float* __restrict__ part, long rows, int dk, int ncg, bool sg,
+chunk_bwd_reduce_kernel(const float* __restrict__ part, long rows, int dk, int ncg, bool sg, int nq,
                         float* __restrict__ dq, float* __restrict__ dkg, float* __restrict__ dg,
-                        float* __restrict__ db) {
+                        float* __restrict__ db, float* __restrict__ de) {
     lds_poison(0);
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     const long n = rows * dk;
     if (e < n) {
-        float a = 0.f, b = 0.f, c = 0.f;
+        float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
         for (int g = 0; g < ncg; ++g) {
-            a += part[(size_t)(3 * g) * n + e];
-            b += part[(size_t)(3 * g + 1) * n + e];
-            if (!sg) c += part[(size_t)(3 * g + 2) * n + e];
+            a += part[(size_t)(nq * g) * n + e];
+            b += part[(size_t)(nq * g + 1) * n + e];
+            if (!sg) c += part[(size_t)(nq * g + 2) * n + e];
+            if (nq > 3) d += part[(size_t)(nq * g + 3) * n + e];
         }
         dq[e] = a;
         dkg[e] = b;
         if (!sg) dg[e] = c;
+        if (nq > 3) de[e] = d;
     }
     if (e < rows) {
-        float x = 0.f;
-        for (int g = 0; g < ncg; ++g) x += part[(size_t)3 * ncg * n + (size_t)g * rows + e];
-        db[e] = x;
+        if (db) {
+            float x = 0.f;
+            for (int g = 0; g < ncg; ++g) x += part[(size_t)nq * ncg * n + (size_t)g * rows + e];
+            db[e] = x;
+        }
         if (sg) {
             float y = 0.f;
             for (int g = 0; g < ncg; ++g)
-                for (int i = 0; i < dk; ++i) y += part[(size_t)(3 * g + 2) * n + (size_t)e * dk + i];
+                for (int i = 0; i < dk; ++i) y += part[(size_t)(nq * g + 2) * n + (size_t)e * dk + i];
             dg[e] = y;
         }
     }
@@ -557,11 +600,11 @@ constexpr int BW_COLS = 4;   // value columns per wave
 constexpr int BW_WAVES = 4;  // waves per workgroup: 16 value columns (dv >= 16 always)
 int bwd_waves(int) { return BW_WAVES; }
 
-template <class TIn, int DK, int NWV, bool SG>
+template <class TIn, int DK, int NWV, bool SG, bool EW>
 hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p) {
-    constexpr size_t bytes = sizeof(BwdLds<DK, NWV * BW_COLS, NWV, SG>);
+    constexpr size_t bytes = sizeof(BwdLds<DK, NWV * BW_COLS, NWV, SG, EW>);
     static_assert(bytes <= 160 * 1024, "backward LDS");
-    auto kern = chunk_bwd_kernel<TIn, DK, NWV, BW_COLS, SG>;
+    auto kern = chunk_bwd_kernel<TIn, DK, NWV, BW_COLS, SG, EW>;
     if (bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
         if (e != hipSuccess) return e;
@@ -570,14 +613,19 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p) {
     return hipGetLastError();
 }
 
-template <class TIn, bool SG>
+template <class TIn, bool SG, bool EW>
 hipError_t launch_bwd_dk(const BwdArgs& a, const BwdParams& p) {
     switch (a.dk) {
-        case 16: return launch_bwd_t<TIn, 16, BW_WAVES, SG>(a, p);
-        case 32: return launch_bwd_t<TIn, 32, BW_WAVES, SG>(a, p);
-        case 64: return launch_bwd_t<TIn, 64, BW_WAVES, SG>(a, p);
-        default: return launch_bwd_t<TIn, 128, BW_WAVES, SG>(a, p);
+        case 16: return launch_bwd_t<TIn, 16, BW_WAVES, SG, EW>(a, p);
+        case 32: return launch_bwd_t<TIn, 32, BW_WAVES, SG, EW>(a, p);
+        case 64: return launch_bwd_t<TIn, 64, BW_WAVES, SG, EW>(a, p);
+        default: return launch_bwd_t<TIn, 128, BW_WAVES, SG, EW>(a, p);
     }
+}
+
+template <class TIn, bool SG>
+hipError_t launch_bwd_ew(const BwdArgs& a, const BwdParams& p) {
+    return a.erase ? launch_bwd_dk<TIn, SG, true>(a, p) : launch_bwd_dk<TIn, SG, false>(a, p);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -591,17 +639,20 @@ size_t bwd_ckpt_bytes(int H, long slots, int dk, int dv) {
     return align256((size_t)H * slots * dv * WAVE * rpl * sizeof(float));
 }
 
-size_t bwd_part_bytes(int B, int H, int T, int dk, int dv) {
+// Per-workgroup partial sums: dq, dk, dalpha [ncg][3][rows][dk] and dbeta
+// [ncg][rows]; the erase/write form keeps dq, dk, dalpha, de [ncg][4][rows][dk].
+size_t bwd_part_bytes(int B, int H, int T, int dk, int dv, bool ew) {
     const int ncg = dv / (bwd_waves(dv) * BW_COLS);
     const size_t rows = (size_t)B * T * H;
-    return align256(((size_t)ncg * 3 * rows * dk + (size_t)ncg * rows) * sizeof(float));
+    return align256((ew ? (size_t)ncg * 4 * rows * dk : (size_t)ncg * 3 * rows * dk + (size_t)ncg * rows) *
+                    sizeof(float));
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N) {
+size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N, bool ew) {
     const size_t resid = align256((size_t)B * T * H * dv * sizeof(float));
-    return bwd_ckpt_bytes(H, bwd_slots(B, T, varlen, N), dk, dv) + bwd_part_bytes(B, H, T, dk, dv) + resid;
+    return bwd_ckpt_bytes(H, bwd_slots(B, T, varlen, N), dk, dv) + bwd_part_bytes(B, H, T, dk, dv, ew) + resid;
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {
@@ -612,6 +663,9 @@ hipError_t launch_chunk_bwd(const BwdArgs& a) {
     p.v = a.v;
     p.gate = a.gate;
     p.beta = a.beta;
+    p.erase = a.erase;
+    p.write = a.write;
+    p.dw_out = a.g_write;
     p.S0 = a.S0;
     p.dO = a.dO;
     p.dST = a.dST;
@@ -626,15 +680,17 @@ hipError_t launch_chunk_bwd(const BwdArgs& a) {
     p.rows = (long)a.B * a.T * a.H;
     char* ws = static_cast<char*>(a.workspace);
     p.ckpt = reinterpret_cast<float*>(ws);
+    const bool ew = a.erase != nullptr;
     p.part = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv));
     p.resid = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(a.H, p.nblk, a.dk, a.dv) +
-                                      bwd_part_bytes(a.B, a.H, a.T, a.dk, a.dv));
-    hipError_t e = a.bf16 ? (a.scalar_gate ? launch_bwd_dk<uint16_t, true>(a, p) : launch_bwd_dk<uint16_t, false>(a, p))
-                          : (a.scalar_gate ? launch_bwd_dk<float, true>(a, p) : launch_bwd_dk<float, false>(a, p));
+                                      bwd_part_bytes(a.B, a.H, a.T, a.dk, a.dv, ew));
+    hipError_t e = a.bf16 ? (a.scalar_gate ? launch_bwd_ew<uint16_t, true>(a, p) : launch_bwd_ew<uint16_t, false>(a, p))
+                          : (a.scalar_gate ? launch_bwd_ew<float, true>(a, p) : launch_bwd_ew<float, false>(a, p));
     if (e != hipSuccess || p.rows == 0) return e;
     const long n = p.rows * a.dk;
     hipLaunchKernelGGL(chunk_bwd_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, p.part,
-                       p.rows, a.dk, p.ncg, a.scalar_gate, a.g_q, a.g_k, a.g_gate, a.g_beta);
+                       p.rows, a.dk, p.ncg, a.scalar_gate, ew ? 4 : 3, a.g_q, a.g_k, a.g_gate,
+                       ew ? nullptr : a.g_beta, ew ? a.g_erase : nullptr);
     return hipGetLastError();
 }
 

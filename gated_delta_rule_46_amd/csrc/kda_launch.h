@@ -46,6 +46,12 @@ struct BwdArgs {
     bool bf16, scalar_gate;
     void* workspace;
     hipStream_t stream;
+    // decoupled erase [.., dk] and write [.., dv] gates in the input dtype
+    // (both set, beta and g_beta unused) with their gradients, or none
+    const void* erase = nullptr;
+    const void* write = nullptr;
+    float* g_erase = nullptr;
+    float* g_write = nullptr;
 };
 
 struct GaugeArgs {
@@ -67,7 +73,7 @@ long chunk_count_bound(int B, int T, int chunk, bool varlen, int N);
 size_t chunk_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, bool varlen, int N, bool bf16);
 
 // Workspace bytes of one backward call (checkpoints and partial sums).
-size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N);
+size_t bwd_workspace_bytes(int B, int H, int T, int dk, int dv, bool varlen, int N, bool ew = false);
 
 // Gauge fold: workspace bytes (segment parities), the fold (c_T into sign_dev
 // when it is not null), and the row flip of a final state by c_T.

@@ -29,7 +29,8 @@ EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace_byte
            "kda_chunk_bwd_workspace_bytes", "kda_gauge_fold", "kda_gauge_fold_workspace_bytes", "kda_chunk_fwd_gauge",
            "kda_chunk_fwd_gauge_workspace_bytes", "kda_decode_step", "kda_strerror", "kda_last_hip_error",
            "kda_version", "kda_chunk_fwd_status", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_ew",
-           "kda_decode_step_ew", "kda_chunk_bwd_cw", "kda_chunk_bwd_cw_workspace_bytes")
+           "kda_decode_step_ew", "kda_chunk_bwd_cw", "kda_chunk_bwd_cw_workspace_bytes", "kda_chunk_bwd_ew",
+           "kda_chunk_bwd_ew_workspace_bytes")
 
 
 class KDAError(RuntimeError):
@@ -63,6 +64,10 @@ def load(path: str):
     lib.kda_chunk_bwd_cw.argtypes = [vp] * 14 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
     lib.kda_chunk_bwd_cw_workspace_bytes.restype = sz
     lib.kda_chunk_bwd_cw_workspace_bytes.argtypes = [i] * 7
+    lib.kda_chunk_bwd_ew.restype = i
+    lib.kda_chunk_bwd_ew.argtypes = [vp] * 16 + [i] * 5 + [vp, i, i, i, vp, sz, vp]
+    lib.kda_chunk_bwd_ew_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_ew_workspace_bytes.argtypes = [i] * 7
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 7
     lib.kda_gauge_fold.restype = i
@@ -327,6 +332,56 @@ def chunk_bwd(q, k, v, gate, beta, dO, S0=None, dS_T=None, cu_seqlens=None, gate
                               workspace.numel() * workspace.element_size(), ctypes.c_void_p(st) if st else None)
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_bwd_cw" if chunked else "kda_chunk_bwd")
+    return out
+
+
+def bwd_ew_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, N: int = 0, varlen: bool = False) -> int:
+    return int(_lib().kda_chunk_bwd_ew_workspace_bytes(B, H, T, dk, dv, N, int(varlen)))
+
+
+def chunk_bwd_ew(q, k, v, gate, erase, write, dO, S0=None, dS_T=None, cu_seqlens=None,
+                 gate_kind: Optional[int] = None, want_dS0: bool = True, out: Optional[dict] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradient of chunk_fwd_ew (kda_chunk_bwd_ew) for L = sum(o * dO) +
+    sum(S_T * dS_T). Inputs as for chunk_fwd_ew, dO and dS_T as for chunk_bwd.
+    Returns a dict of fp32 tensors dq, dk, dv, dgate, derase, dwrite (input
+    layouts) and dS0 ([N,H,dk,dv], or None when not wanted)."""
+    B, T, H, dk, dv, gate_kind = _check_seq_inputs(q, k, v, gate, erase[..., 0], gate_kind)
+    _check_shape("erase", erase, (B, T, H, dk))
+    _check_shape("write", write, (B, T, H, dv))
+    for name, t in (("erase", erase), ("write", write)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    if dO.dtype != torch.float32 or tuple(dO.shape) != (B, T, H, dv):
+        raise ValueError("dO must be fp32 [%d,%d,%d,%d]" % (B, T, H, dv))
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed sequences (cu_seqlens) need B = 1, got %d" % B)
+    device = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("erase", erase), ("write", write), ("dO", dO)):
+        _check_dev(name, t, device)
+    dt = _dtype_code(q)
+    varlen, N = _check_varlen(cu_seqlens, B, device)
+    _check_state("S0", S0, N, H, dk, dv, device)
+    _check_state("dS_T", dS_T, N, H, dk, dv, device)
+    f32 = dict(device=device, dtype=torch.float32)
+    if out is None:
+        out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+               "dv": torch.empty((B, T, H, dv), **f32), "dgate": torch.empty(tuple(gate.shape), **f32),
+               "derase": torch.empty((B, T, H, dk), **f32), "dwrite": torch.empty((B, T, H, dv), **f32),
+               "dS0": torch.empty((N, H, dk, dv), **f32) if want_dS0 else None}
+    need = bwd_ew_workspace_bytes(B, H, T, dk, dv, N, varlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=device, dtype=torch.uint8)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
+    st = _stream_handle(stream, device)
+    rc = _lib().kda_chunk_bwd_ew(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(erase), _ptr(write), _ptr(S0), _ptr(dO),
+                                 _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
+                                 _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out.get("dS0")), B, H, T, dk, dv,
+                                 _ptr(cu_seqlens), N if varlen else 0, dt, int(gate_kind), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), ctypes.c_void_p(st) if st else None)
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd_ew")
     return out
 
 

@@ -246,6 +246,27 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Gradient of kda_chunk_fwd_ew (decoupled erase and write gates; Gated
+ * DeltaNet-2 blurb, and the reading stated at kda_chunk_fwd_ew), by the same
+ * token-recurrence method as kda_chunk_bwd: with the read key ke = e o k and
+ * u = w o v - S'^T ke, the adjoint of each token reads the state with ke,
+ * writes along k, and has no beta. Loss, inputs, dO, dS_T, grad_q, grad_k,
+ * grad_v, grad_gate and grad_S0 as for kda_chunk_bwd (erase and write as for
+ * kda_chunk_fwd_ew, same dtype as q). Outputs in place of grad_beta (fp32,
+ * written in full): grad_erase [B, T, H, dk] and grad_write [B, T, H, dv]
+ * (16-byte aligned). workspace: kda_chunk_bwd_ew_workspace_bytes(...) bytes
+ * (as for kda_chunk_bwd, with one more partial sum per key channel instead of
+ * the partial sums of dbeta); required. Every dk and dv of kda_chunk_fwd.
+ * Returns KDA_OK or a negative status.
+ */
+size_t kda_chunk_bwd_ew_workspace_bytes(int B, int H, int T, int dk, int dv, int N, int has_cu_seqlens);
+int kda_chunk_bwd_ew(const void* q, const void* k, const void* v, const void* gate, const void* erase,
+                     const void* write, const float* S0, const float* dO, const float* dS_T, float* grad_q,
+                     float* grad_k, float* grad_v, float* grad_gate, float* grad_erase, float* grad_write,
+                     float* grad_S0, int B, int H, int T, int dk, int dv, const int32_t* cu_seqlens, int N, int dtype,
+                     int gate_kind, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The same gradient as kda_chunk_bwd (same arguments, outputs and layouts),
  * computed chunk by chunk (the pages' chunkwise algorithm with gate-aware
  * backpropagation for this family; Gated DeltaNet-2 blurb): per 64-token

@@ -1,9 +1,11 @@
-"""GPU parity of the erase/write-gate forward and decode (kda_chunk_fwd_ew,
-kda_decode_step_ew) against the oracle's erase/write recurrence
-(oracle.fwd_ew / decode_step_ew, pinned in test_oracle_ew.py).
+"""GPU parity of the erase/write-gate forward, decode and backward
+(kda_chunk_fwd_ew, kda_decode_step_ew, kda_chunk_bwd_ew) against the oracle's
+erase/write recurrence and its gradient (oracle.fwd_ew / decode_step_ew,
+pinned in test_oracle_ew.py; oracle.bwd_ew, pinned in test_oracle_bwd.py).
 
 Same metric and bars as the forward: err = max|x_gpu - x_ref| / rms(x_ref),
-1e-4 with fp32 inputs, 2e-2 with bf16 inputs (fp32 state)."""
+1e-4 with fp32 inputs, 2e-2 with bf16 inputs (fp32 state); the backward
+1e-4 for both (1e-3 at full size), as for the beta form."""
 import dataclasses
 import math
 
@@ -160,3 +162,97 @@ def test_ew_decode_after_prefill(kda):
         torch.cuda.synchronize()
         assert err(o.cpu(), o_full[:, t].double().numpy()) < 1e-4
     assert err(S.cpu(), S_full.double().numpy()) < 1e-4
+
+
+# ------------------------------------------------------------------ backward (kda_chunk_bwd_ew)
+
+EW_NAMES = ("dq", "dk", "dv", "dgate", "derase", "dwrite", "dS0")
+
+
+def gpu_bwd_ew(kda, x, dO, dST):
+    w = x.w
+    d = lambda t: None if t is None else t.cuda()  # noqa: E731
+    g = kda.chunk_bwd_ew(d(w.q), d(w.k), d(w.v), d(w.gate), d(x.erase), d(x.write), d(dO), S0=d(w.S0),
+                         dS_T=d(dST), cu_seqlens=d(w.cu_seqlens), gate_kind=w.gate_kind)
+    torch.cuda.synchronize()
+    return {n: (None if g[n] is None else g[n].cpu()) for n in EW_NAMES}
+
+
+def check_bwd(kda, x, tol=1e-4, every_pair=False):
+    """Every gradient of the erase/write backward against oracle.bwd_ew
+    (pinned in test_oracle_bwd.py); the backward computes in fp32 from the
+    exact input values, so the bar is 1e-4 for both input dtypes."""
+    w = x.w
+    print("case bwd_ew", w.name, "B", w.B, "H", w.H, "T", w.T, "dk", w.dk, "dv", w.dv, "dtype", w.q.dtype, flush=True)
+    dO, dST = inputs.cotangents(w, seed=w.T + w.dk)
+    g = gpu_bwd_ew(kda, x, dO, dST)
+    r = oracle.bwd_ew(w.q, w.k, w.v, w.gate, x.erase, x.write, dO, w.S0, dST, w.cu_seqlens, w.gate_kind)
+    errs = {n: err(g[n], r[n]) for n in EW_NAMES}
+    print("  errors", {n: "%.2e" % e for n, e in errs.items()}, flush=True)
+    for n in EW_NAMES:
+        assert np.isfinite(g[n].numpy()).all(), n
+        assert errs[n] <= tol, (n, errs)
+    if every_pair:
+        for s_ in range(w.n_seqs):
+            for h in range(w.H):
+                worst = max(err(g[n][s_, :, h], r[n][s_, :, h]) for n in EW_NAMES if n != "dS0")
+                assert worst <= tol and err(g["dS0"][s_, h], r["dS0"][s_, h]) <= tol, (s_, h, worst)
+    return g, r
+
+
+BWD_CASES = [
+    # gate, dtype, dk, dv, T, erase recipe
+    ("ckda", torch.bfloat16, 128, 128, 77, "bimodal"),
+    ("kda", torch.float32, 64, 32, 130, "sigmoid"),
+    ("gdn", torch.bfloat16, 32, 64, 45, "bimodal"),
+    ("ckda", torch.float32, 16, 16, 9, "sigmoid"),
+    ("gdn", torch.float32, 128, 16, 200, "bimodal"),
+]
+
+
+@pytest.mark.parametrize("gate,dtype,dk,dv,T,erase", BWD_CASES)
+def test_ew_bwd_small_parity(kda, gate, dtype, dk, dv, T, erase):
+    w = inputs.make_forward("bwd_ew_%s" % gate, B=2, H=3, T=T, dk=dk, dv=dv, dtype=dtype, gate=gate, gate_mu=2.0,
+                            seed=T + dk + dv, s0_std=0.3)
+    check_bwd(kda, inputs.erase_write_gates(w, seed=T, erase=erase))
+
+
+def test_ew_bwd_varlen_empty_and_signed_zeros(kda):
+    """Packed sequences with an empty and a one-token one, -0.0 / +0.0 / -1.0
+    gates mixed in: the empty sequence passes dS_T to dS0 exactly."""
+    w = inputs.make_forward("bwd_ew_varlen", B=1, H=2, T=0, dk=64, dv=64, dtype=torch.float32, gate="ckda",
+                            lengths=[37, 0, 1, 150], s0_std=0.2, seed=6)
+    w = dataclasses.replace(w, gate=inputs.signed_zero_gates(w.gate, seed=4))
+    x = inputs.erase_write_gates(w, seed=6)
+    g, r = check_bwd(kda, x)
+    dO, dST = inputs.cotangents(w, seed=w.T + w.dk)
+    np.testing.assert_array_equal(g["dS0"][1].numpy(), dST[1].numpy())
+
+
+def test_ew_bwd_reduces_to_the_beta_form(kda):
+    """erase = write = beta on every channel: the erase/write backward and the
+    token-form beta backward on the GPU give the same dq, dk, dv, dgate, dS0,
+    and dbeta = sum of derase over the key channels + sum of dwrite over the
+    value channels."""
+    w = inputs.make_forward("bwd_ew_red", B=2, H=2, T=140, dk=64, dv=32, dtype=torch.float32, gate="ckda", seed=31,
+                            s0_std=0.2)
+    e = w.beta[..., None].expand(*w.beta.shape, w.dk).contiguous()
+    wr = w.beta[..., None].expand(*w.beta.shape, w.dv).contiguous()
+    dO, dST = inputs.cotangents(w, seed=3)
+    g_ew = gpu_bwd_ew(kda, inputs.EraseWriteWorkload(w, e, wr), dO, dST)
+    d = lambda t: None if t is None else t.cuda()  # noqa: E731
+    g_b = kda.chunk_bwd(d(w.q), d(w.k), d(w.v), d(w.gate), d(w.beta), d(dO), S0=d(w.S0), dS_T=d(dST),
+                        gate_kind=w.gate_kind, chunked=False)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dgate", "dS0"):
+        assert err(g_ew[n], g_b[n].cpu().double().numpy()) <= 1e-5, n
+    db = g_ew["derase"].sum(-1) + g_ew["dwrite"].sum(-1)
+    assert err(db, g_b["dbeta"].cpu().double().numpy()) <= 1e-5
+
+
+def test_ew_bwd_full_size_every_pair(kda):
+    """Erase/write gates with Complex KDA's signed gates at the Complex KDA
+    workload's shape (B=2, H=16, T=8192, d=128, bf16): every gradient of every
+    (sequence, head) against the oracle, bar 1e-3 as for the beta form's
+    full-size case (fp32 sums over 8,192 tokens)."""
+    check_bwd(kda, inputs.gdn2_ckda_fwd(), tol=1e-3, every_pair=True)

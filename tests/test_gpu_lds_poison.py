@@ -95,6 +95,12 @@ def test_poisoned_token_backward(kda):
     tok_bwd.check(kda, w)
 
 
+def test_poisoned_erase_write_backward(kda):
+    w = inputs.make_forward("poison_bwd_ew", B=2, H=3, T=70, dk=128, dv=32, dtype=BF16, gate="ckda", seed=8,
+                            s0_std=0.3)
+    ew.check_bwd(kda, inputs.erase_write_gates(w, seed=8))
+
+
 def test_poisoned_gauge_route(kda):
     w = inputs.make_forward("poison_route", B=2, H=2, T=129, dk=128, dv=64, chunk=64, gate="ckda", seed=5,
                             s0_std=0.3)
