@@ -20,7 +20,8 @@ in place) is timed as one block of 128 consecutive steps, and set beside a
 plain device copy of the same 512 MiB (read and written) as a practical
 bandwidth ceiling. The backward
 (kda_chunk_bwd, gradients of every input for given dO and dS_T) is timed on
-the same forward workload. Forward and backward are also timed at 32k tokens
+the same forward workload, in both forms, and so is the erase/write-gate
+backward (kda_chunk_bwd_ew) on that shape. Forward and backward are also timed at 32k tokens
 per step (B=4, H=16, T=8192) with the KDA and the Complex KDA gate recipes,
 for the throughput ratio of the two.
 Timing uses HIP events recorded on the stream the kernels run on. Prints one
@@ -447,6 +448,21 @@ def main(argv=None) -> int:
             legs[form] = (time_region(bwd, args.bwd_steps, stream), wsb)
             print("[bench] backward (%s) %.3f ms/call" % (form, legs[form][0]), file=sys.stderr, flush=True)
             del ws_b, gout
+        # the erase/write form (Gated DeltaNet-2 gates with the Complex KDA gate recipe), token form
+        xe = inputs.gdn2_ckda_fwd(seed=0)
+        et = [t.to(dev) for t in (xe.w.q, xe.w.k, xe.w.v, xe.w.gate, xe.erase, xe.write)]
+        wse = kda.bwd_ew_workspace_bytes(B, H, T, dk, dv)
+        ws_e = torch.empty(wse, device=dev, dtype=torch.uint8)
+        gout = kda.chunk_bwd_ew(*et, bt[5], dS_T=dST, workspace=ws_e)
+
+        def bwd_ew(i):
+            kda.chunk_bwd_ew(*et, bt[5], dS_T=dST, workspace=ws_e, out=gout)
+
+        for i in range(5):
+            bwd_ew(i)
+        ms_e = time_region(bwd_ew, args.bwd_steps, stream)
+        print("[bench] backward (erase/write, token form) %.3f ms/call" % ms_e, file=sys.stderr, flush=True)
+        del ws_e, gout, et, xe
         ms_b, wsb_b = legs["chunkwise"]
         ms_t, wsb_t = legs["token"]
         bflops = B * H * ((T + 63) // 64) * cbwd_flops_per_head_chunk(dk, dv, 64)   # its chunk is 64
@@ -468,6 +484,10 @@ def main(argv=None) -> int:
             "token_form": {"ms_per_call": round(ms_t, 4), "workspace_bytes": wsb_t,
                            "kernel": "kda_chunk_bwd: chunk_bwd_kernel then chunk_bwd_reduce_kernel",
                            "alu_frac": round(tflops / (ms_t * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4)},
+            "erase_write_token_form": {"workload": "gdn2_ckda_bwd_b2_h16_t8192_d128", "ms_per_call": round(ms_e, 4),
+                                       "tokens_per_s": round(tokens / (ms_e * 1e-3), 1), "workspace_bytes": wse,
+                                       "kernel": "kda_chunk_bwd_ew: chunk_bwd_kernel (erase/write) then "
+                                                 "chunk_bwd_reduce_kernel"},
         }
         if not args.no_cpu_baseline:
             import oracle
