@@ -308,3 +308,43 @@ def test_erase_write_validation(lib):
     assert dec(erase=FAKE + 1) == kda.KDA_EALIGN
     assert dec(S=FAKE + 4) == kda.KDA_EALIGN
     assert dec(gate_kind=5) == kda.KDA_ENOTSUP
+
+
+def test_erase_write_bwd_validation(lib):
+    def bwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, erase=FAKE, write=FAKE, S0=None, dO=FAKE, dST=None, gq=FAKE,
+                 gk=FAKE, gv=FAKE, gg=FAKE, ge=FAKE, gw=FAKE, gS0=None, B=1, H=2, T=8, dk=16, dv=16, cu=None, N=0,
+                 dtype=kda.KDA_BF16, gate_kind=0, ws=FAKE, wsb=1 << 30, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_bwd_ew(*a.values())
+    assert bwd(B=0) == kda.KDA_EINVAL
+    assert bwd(dk=24) == kda.KDA_ENOTSUP
+    assert bwd(dtype=5) == kda.KDA_ENOTSUP
+    assert bwd(gate_kind=3) == kda.KDA_ENOTSUP
+    assert bwd(erase=None) == kda.KDA_EINVAL
+    assert bwd(write=None) == kda.KDA_EINVAL
+    assert bwd(ge=None) == kda.KDA_EINVAL
+    assert bwd(gw=None) == kda.KDA_EINVAL
+    assert bwd(erase=FAKE + 1) == kda.KDA_EALIGN
+    assert bwd(gw=FAKE + 4) == kda.KDA_EALIGN                         # grad_write is written 16 bytes at a time
+    assert bwd(dO=FAKE + 4) == kda.KDA_EALIGN
+    assert bwd(ws=None) == kda.KDA_EINVAL                             # the library never allocates
+    assert bwd(wsb=1) == kda.KDA_EINVAL
+    assert bwd(cu=FAKE, B=2, N=2) == kda.KDA_EINVAL
+    # one more per-row partial sum (de) in place of dbeta's: more workspace than the beta form
+    w = kda.bwd_ew_workspace_bytes(1, 2, 64, 16, 16)
+    assert w > kda.bwd_workspace_bytes(1, 2, 64, 16, 16) and w % 256 == 0
+    assert kda.bwd_ew_workspace_bytes(1, 2, 64, 24, 16) == 0
+    assert kda.bwd_ew_workspace_bytes(2, 2, 64, 16, 16, N=2, varlen=True) == 0
+
+
+def test_lds_poison_build_exports_every_declared_symbol():
+    """The LDS-poisoning debug build is the same library: it loads and exports
+    every declared symbol (its GPU test runs the kernels through it)."""
+    from gated_delta_rule_46_amd import build
+    if not os.path.exists(build.POISON_LIB):
+        build.build(poison=True)
+    plib = kda.load(build.POISON_LIB)
+    for n in declared_functions():
+        assert hasattr(plib, n), n
+    assert plib.kda_version() == 100
