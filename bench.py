@@ -24,8 +24,9 @@ the same forward workload, in both forms, and so is the erase/write-gate
 backward (kda_chunk_bwd_ew) on that shape. Forward and backward are also timed at 32k tokens
 per step (B=4, H=16, T=8192) with the KDA and the Complex KDA gate recipes,
 for the throughput ratio of the two.
-Timing uses HIP events recorded on the stream the kernels run on. Prints one
-JSON line.
+Timing uses HIP events recorded on the stream the kernels run on. The fp64
+CPU oracle is timed on the host cores beside the headline, the backward and
+each other forward workload (a bounded sample each). Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -344,6 +345,7 @@ def main(argv=None) -> int:
         del bufs
     head, fwd, (o, ST, ws) = forward_leg(kda, "ckda_fwd_b2_h16_t8192_d128_chunk64", sets, w, args.warmup, args.steps,
                                          stream, dev, with_clock=True)
+    cpu_w = {name: wx for name, (wx, _) in others.items()}   # host copies, for the oracle baselines
     others.clear()
     ms = head["ms_per_call"]
     ms_prep = head["kernels_ms"]["chunk_prep_kernel"]
@@ -579,6 +581,38 @@ def main(argv=None) -> int:
                "sample": "whole Complex KDA workload (B=2, H=16, T=8192, d=128), fp64 token recurrence, "
                          "%d pass(es), %.2f s each" % (reps, dt)}
         print("[bench] oracle %.2f s per pass" % dt, file=sys.stderr, flush=True)
+        # the other forward workloads, each on a bounded sample
+        samples = {
+            "tiny_kda_fp32_b1_h1_t64_d16_chunk16": (None, "whole workload"),
+            "kda_fwd_b4_h16_t4096_d128_chunk64": (None, "whole workload"),
+            "gdn_varlen_h32_t110440_d128_chunk64": (range(4), "heads 0-3 of all 8 sequences"),
+        }
+        for name, (heads, what) in samples.items():
+            if name not in cpu_w:
+                continue
+            wx = cpu_w[name]
+            nh = wx.H if heads is None else len(heads)
+
+            def run(wx=wx, heads=heads):
+                if heads is None:
+                    oracle.fwd(wx.q, wx.k, wx.v, wx.gate, wx.beta, None, wx.cu_seqlens, wx.gate_kind)
+                else:
+                    oracle.fwd_heads(wx.q, wx.k, wx.v, wx.gate, wx.beta, heads, None, wx.cu_seqlens, wx.gate_kind)
+
+            t0 = time.time()
+            reps = 0
+            while reps == 0 or time.time() - t0 < 2.0:
+                run()
+                reps += 1
+            dtx = (time.time() - t0) / reps
+            # tokens/s of the whole workload at the sample's rate per head-token
+            tok_x = wx.B * wx.T
+            configs[name]["cpu_baseline"] = {
+                "value": round(tok_x * nh / wx.H / dtx, 1), "unit": "tokens/s",
+                "cores": min(oracle.threads(), wx.n_seqs * nh), "kind": "oracle",
+                "sample": "%s, fp64 token recurrence, %d pass(es), %.3g s each" % (what, reps, dtx)}
+            print("[bench] oracle %s %.3g s per pass" % (name, dtx), file=sys.stderr, flush=True)
+    cpu_w = None
 
     line = {
         "metric": METRIC,
