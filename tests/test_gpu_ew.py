@@ -256,3 +256,55 @@ def test_ew_bwd_full_size_every_pair(kda):
     (sequence, head) against the oracle, bar 1e-3 as for the beta form's
     full-size case (fp32 sums over 8,192 tokens)."""
     check_bwd(kda, inputs.gdn2_ckda_fwd(), tol=1e-3, every_pair=True)
+
+
+def test_ew_bwd_graph_replay_matches_eager(kda):
+    """The erase/write backward with a caller-supplied workspace and output
+    dict enqueues kernels only, so it can be captured in a graph: packed
+    sequences, three replays on new inputs and a new split of the same total
+    length copied into the captured buffers, eager calls in between, each
+    replay equal bit for bit to an eager call on the same inputs."""
+    H, dk, dv = 2, 64, 32
+    splits = ([37, 0, 150, 64], [64, 64, 1, 122], [0, 200, 50, 1], [100, 51, 99, 1])
+
+    def make(seed, lengths):
+        w = inputs.make_forward("graph_bwd_ew", B=1, H=H, T=0, dk=dk, dv=dv, dtype=torch.bfloat16, gate="ckda",
+                                lengths=lengths, s0_std=0.3, seed=seed)
+        x = inputs.erase_write_gates(w, seed=seed)
+        dO, dST = inputs.cotangents(w, seed=seed)
+        return [t.cuda() for t in (w.q, w.k, w.v, w.gate, x.erase, x.write, dO, w.S0, dST, w.cu_seqlens)]
+
+    static = make(50, splits[0])
+    T, N = static[0].shape[1], static[9].numel() - 1
+    ws = torch.empty(kda.bwd_ew_workspace_bytes(1, H, T, dk, dv, N, True), device="cuda", dtype=torch.uint8)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    g = {"dq": torch.empty((1, T, H, dk), **f32), "dk": torch.empty((1, T, H, dk), **f32),
+         "dv": torch.empty((1, T, H, dv), **f32), "dgate": torch.empty((1, T, H, dk), **f32),
+         "derase": torch.empty((1, T, H, dk), **f32), "dwrite": torch.empty((1, T, H, dv), **f32),
+         "dS0": torch.empty((N, H, dk, dv), **f32)}
+
+    def step():
+        q, k, v, gt, e, wr, dO, s0, dst, cu = static
+        kda.chunk_bwd_ew(q, k, v, gt, e, wr, dO, S0=s0, dS_T=dst, cu_seqlens=cu, workspace=ws, out=g)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        print("replay", rep, "lengths", splits[rep + 1], flush=True)
+        new = make(51 + rep, splits[rep + 1])
+        for dst, src in zip(static, new):
+            dst.copy_(src)
+        q, k, v, gt, e, wr, dO, s0, dst, cu = new
+        ref = kda.chunk_bwd_ew(q, k, v, gt, e, wr, dO, S0=s0, dS_T=dst, cu_seqlens=cu)   # eager
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in EW_NAMES:
+            assert torch.equal(g[n], ref[n]), (rep, n)
