@@ -21,7 +21,8 @@ plain device copy of the same 512 MiB (read and written) as a practical
 bandwidth ceiling. The backward
 (kda_chunk_bwd, gradients of every input for given dO and dS_T) is timed on
 the same forward workload, in both forms, and so is the erase/write-gate
-backward (kda_chunk_bwd_ew) on that shape. Forward and backward are also timed at 32k tokens
+backward (kda_chunk_bwd_ew) on that shape; the erase/write forward
+(kda_chunk_fwd_ew) is timed beside the direct one. Forward and backward are also timed at 32k tokens
 per step (B=4, H=16, T=8192) with the KDA and the Complex KDA gate recipes,
 for the throughput ratio of the two.
 Timing uses HIP events recorded on the stream the kernels run on. The fp64
@@ -389,6 +390,29 @@ def main(argv=None) -> int:
                  "throughput_vs_direct": round(ms_d / ms_g, 4)}
         print("[bench] gauge route %.3f ms/step (direct %.3f)" % (ms_g, ms_d), file=sys.stderr, flush=True)
         del wsg
+    # the erase/write-gate forward (Gated DeltaNet-2 gates with the Complex KDA
+    # gate recipe) on the same shape, two input sets, beside the direct route
+    erase_write = None
+    if not args.no_configs:
+        ew_sets = []
+        for s_ in (0, 1):
+            xe = inputs.gdn2_ckda_fwd(seed=s_)
+            ew_sets.append(tuple(t.to(dev) for t in (xe.w.q, xe.w.k, xe.w.v, xe.w.gate, xe.erase, xe.write)))
+        del xe
+
+        def fwd_e(i):
+            q, k, v, g, e, wr = ew_sets[i % 2]
+            kda.chunk_fwd_ew(q, k, v, g, e, wr, chunk=C, gate_kind=0, out=o, S_T=ST, workspace=ws)
+
+        for i in range(args.warmup):
+            fwd_e(i)
+        ms_e = time_region(fwd_e, args.steps, stream)
+        ms_d = time_region(fwd, args.steps, stream)
+        erase_write = {"workload": "gdn2_ckda_fwd_b2_h16_t8192_d128_chunk64", "ms_per_call": round(ms_e, 4),
+                       "tokens_per_s": round(tokens / (ms_e * 1e-3), 1), "direct_ms_per_call": round(ms_d, 4),
+                       "throughput_vs_direct": round(ms_d / ms_e, 4)}
+        print("[bench] erase/write forward %.4f ms/call (direct %.4f)" % (ms_e, ms_d), file=sys.stderr, flush=True)
+        del ew_sets
     del sets, ws, o
 
     # ---------------------------------------------------------------- decode
@@ -637,6 +661,7 @@ def main(argv=None) -> int:
         "decode": decode,
         "backward": backward,
         "gauge_route": gauge,
+        "erase_write_forward": erase_write,
         "ckda_vs_kda": ratio,
         "gpu_clock_after_run": gpu_clock(),
     }
